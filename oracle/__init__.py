@@ -1,0 +1,110 @@
+"""fp64 CPU oracle for the Mamba-2 SSD recurrence (plain sequential definition).
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, ``__graft_entry__.smoke()`` and the
+benchmark's ``cpu_baseline`` leg may import this package.  It never imports the
+GPU package and the GPU package never imports it; the two share no code.
+
+The arithmetic lives in ``ssd_oracle.c`` (the recurrence written out token by
+token, in float64).  This module only marshals arrays through ctypes:
+
+* ``prefill(x, dt, A, B, C, D, h0=None, cu_seqlens=None)`` -> ``(y, h_out)``
+* ``step(x, dt, A, B, C, D, h)`` -> ``y`` (``h`` updated in place)
+
+Passages followed: COREY, section 3.1 (generic selective SSM update);
+Compiler-First State Space Duality ..., Abstract (diagonal per-head dynamics);
+Mamba-2 SSD fused layer via VGpuWarp, "Lane mapping" (per-channel sweep over
+d_state, one exp per step); Recurrence Scan, "One equation, one packed result"
+(output and carried state both returned and both compared).
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+
+def load(path=None):
+    """Load (building first if absent) the oracle shared library."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        _lib = _bind(ctypes.CDLL(_build.LIB))
+    return _lib
+
+
+def _bind(lib):
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    lib.ssd_ref_prefill.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, P, P, I]
+    lib.ssd_ref_prefill.restype = I
+    lib.ssd_ref_step.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I]
+    lib.ssd_ref_step.restype = I
+    return lib
+
+
+def _f32(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def default_threads():
+    return max(1, len(os.sched_getaffinity(0)))
+
+
+def prefill(x, dt, A, B, C, D, h0=None, cu_seqlens=None, threads=None, lib=None):
+    """Sequential fp64 SSD over packed sequences.
+
+    x [T,H,P], dt [T,H], A [H], B/C [T,G,N], D [H]; h0 [nseq,H,N,P] or None.
+    cu_seqlens: int array [nseq+1] (None = one sequence of length T).
+    A dense batch [b,L,...] may be passed flattened with
+    ``cu_seqlens = arange(b+1)*L``.  Returns (y [T,H,P] f64, h_out [nseq,H,N,P] f64).
+    """
+    lib = lib or load()
+    x, dt, A, B, C, D = (_f32(v) for v in (x, dt, A, B, C, D))
+    T, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    if cu_seqlens is None:
+        cu_seqlens = np.array([0, T], dtype=np.int64)
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    nseq = cu.shape[0] - 1
+    assert cu[0] == 0 and cu[-1] == T
+    assert dt.shape == (T, H) and A.shape == (H,) and D.shape == (H,)
+    assert B.shape == (T, G, N) and C.shape == (T, G, N)
+    h0c = None
+    if h0 is not None:
+        h0c = np.ascontiguousarray(np.asarray(h0, dtype=np.float64))
+        assert h0c.shape == (nseq, H, N, P)
+    y = np.empty((T, H, P), dtype=np.float64)
+    h_out = np.empty((nseq, H, N, P), dtype=np.float64)
+    rc = lib.ssd_ref_prefill(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                             _ptr(h0c), _ptr(cu), nseq, H, P, N, G, _ptr(y), _ptr(h_out),
+                             threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    return y, h_out
+
+
+def step(x, dt, A, B, C, D, h, threads=None, lib=None):
+    """One fp64 decode token.  x [b,H,P], dt [b,H], B/C [b,G,N];
+    h [b,H,N,P] float64, updated in place.  Returns y [b,H,P] f64."""
+    lib = lib or load()
+    x, dt, A, B, C, D = (_f32(v) for v in (x, dt, A, B, C, D))
+    b, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    assert isinstance(h, np.ndarray) and h.dtype == np.float64 and h.flags.c_contiguous
+    assert h.shape == (b, H, N, P)
+    y = np.empty((b, H, P), dtype=np.float64)
+    rc = lib.ssd_ref_step(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                          _ptr(h), _ptr(y), b, H, P, N, G, threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    return y

@@ -1,0 +1,126 @@
+/*
+ * ssd_oracle.c -- plain, slow, fp64 CPU reference for the Mamba-2 SSD recurrence.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg may load this library.  The product path never links it.
+ * It shares no code, header or constant with the GPU library.
+ *
+ * What it computes (one token at a time, per sequence and head):
+ *
+ *   a_t        = exp(dt_t * A_h)
+ *   h_t[n][p]  = a_t * h_{t-1}[n][p] + dt_t * x_t[p] * B_t[n]
+ *   y_t[p]     = sum_n C_t[n] * h_t[n][p] + D_h * x_t[p]
+ *
+ * Passages followed:
+ *  - COREY: Entropy-Guided Runtime Chunk Scheduling for Selective Scan Kernels,
+ *    section 3.1 (Preliminaries): the generic selective SSM update
+ *    h_t = A_t h_{t-1} + B_t x_t, y_t = C_t h_t + D_t x_t.
+ *  - Compiler-First State Space Duality and Portable O(1) Autoregressive Caching
+ *    for Inference, Abstract: SSD has diagonal per-head dynamics, i.e. the state
+ *    transition of head h is the scalar exp(dt*A_h) times the identity.
+ *  - Mamba-2 SSD fused layer via VGpuWarp -- design sketch, "Lane mapping" and
+ *    "S2 RESULT": each (head, head_dim) channel sweeps d_state with one exp per
+ *    step; the state h is an N x P matrix per head.
+ *  - Recurrence Scan (poot docs), "One equation, one packed result": the scan
+ *    returns the output and the carried state, and a CPU oracle is compared on
+ *    every element of both.
+ * Readings where the pages are silent (documented with the build): dt is the
+ * final positive step (softplus already applied by the caller), A_h is the
+ * negative decay rate itself, the input term is dt*x (x) B with no zero-order-hold
+ * factor, D is a per-head scalar skip, head h reads group floor(h*G/H).
+ *
+ * Inputs are float32 (bf16 inputs are upcast exactly before the call); all
+ * arithmetic and the outputs are float64.  Layouts are row-major:
+ *   x [T][H][P], dt [T][H], A [H], B [T][G][N], C [T][G][N], D [H],
+ *   state [nseq][H][N][P], y [T][H][P].
+ * Sequences are packed along T; sequence s covers tokens cu[s] .. cu[s+1]-1.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* Advance one (sequence, head) state by one token and write that token's output. */
+static void ssd_token(double *h, const float *x, double dt, double A,
+                      const float *B, const float *C, double D, double *y,
+                      int P, int N)
+{
+    const double a = exp(dt * A);
+    for (int n = 0; n < N; ++n) {
+        const double bn = (double)B[n];
+        for (int p = 0; p < P; ++p)
+            h[(size_t)n * P + p] = a * h[(size_t)n * P + p] + dt * (double)x[p] * bn;
+    }
+    for (int p = 0; p < P; ++p) {
+        double acc = 0.0;
+        for (int n = 0; n < N; ++n)
+            acc += (double)C[n] * h[(size_t)n * P + p];
+        y[p] = acc + D * (double)x[p];
+    }
+}
+
+/*
+ * Whole-sequence recurrence for every (sequence, head) pair.
+ * h0 may be NULL (zero initial state).  h_out may be NULL (not written).
+ * cu has nseq+1 entries, cu[0] = 0, non-decreasing.
+ * Returns 0, or -1 on an invalid argument.
+ */
+int ssd_ref_prefill(const float *x, const float *dt, const float *A,
+                    const float *B, const float *C, const float *D,
+                    const double *h0, const int64_t *cu, int nseq,
+                    int H, int P, int N, int G,
+                    double *y, double *h_out, int nthreads)
+{
+    if (!x || !dt || !A || !B || !C || !D || !cu || !y) return -1;
+    if (nseq < 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0 || H % G != 0) return -1;
+    for (int s = 0; s < nseq; ++s)
+        if (cu[s + 1] < cu[s]) return -1;
+    const long units = (long)nseq * H;
+    if (nthreads <= 0) nthreads = 1;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+    for (long u = 0; u < units; ++u) {
+        const int s = (int)(u / H), hd = (int)(u % H);
+        const int g = (int)(((long)hd * G) / H);
+        double *h = (double *)malloc(sizeof(double) * (size_t)N * P);
+        if (!h) { bad = 1; continue; }
+        const size_t hoff = ((size_t)s * H + hd) * (size_t)N * P;
+        if (h0) memcpy(h, h0 + hoff, sizeof(double) * (size_t)N * P);
+        else memset(h, 0, sizeof(double) * (size_t)N * P);
+        for (int64_t t = cu[s]; t < cu[s + 1]; ++t) {
+            ssd_token(h, x + ((size_t)t * H + hd) * P, (double)dt[(size_t)t * H + hd],
+                      (double)A[hd], B + ((size_t)t * G + g) * N,
+                      C + ((size_t)t * G + g) * N, (double)D[hd],
+                      y + ((size_t)t * H + hd) * P, P, N);
+        }
+        if (h_out) memcpy(h_out + hoff, h, sizeof(double) * (size_t)N * P);
+        free(h);
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * One decode token for a batch of independent states, updated in place.
+ * x [b][H][P], dt [b][H], B, C [b][G][N], h [b][H][N][P] (float64), y [b][H][P].
+ */
+int ssd_ref_step(const float *x, const float *dt, const float *A,
+                 const float *B, const float *C, const float *D,
+                 double *h, double *y, int batch, int H, int P, int N, int G,
+                 int nthreads)
+{
+    if (!x || !dt || !A || !B || !C || !D || !h || !y) return -1;
+    if (batch < 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0 || H % G != 0) return -1;
+    const long units = (long)batch * H;
+    if (nthreads <= 0) nthreads = 1;
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+    for (long u = 0; u < units; ++u) {
+        const int b = (int)(u / H), hd = (int)(u % H);
+        const int g = (int)(((long)hd * G) / H);
+        ssd_token(h + ((size_t)b * H + hd) * (size_t)N * P,
+                  x + ((size_t)b * H + hd) * P, (double)dt[(size_t)b * H + hd],
+                  (double)A[hd], B + ((size_t)b * G + g) * N,
+                  C + ((size_t)b * G + g) * N, (double)D[hd],
+                  y + ((size_t)b * H + hd) * P, P, N);
+    }
+    return 0;
+}

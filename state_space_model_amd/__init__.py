@@ -1,0 +1,17 @@
+"""MI355X-native Mamba-2 SSD selective scan (chunked prefill + decode step).
+
+The compute runs in the HIP library ``libssd.so`` (built from ``csrc/``);
+``ssd.py`` is the thin ctypes binding over its C ABI (``include/ssd.h``).
+Importing this package does not load the library; ``prefill``/``step``
+load it on first use and raise if it is missing.
+"""
+
+
+def prefill(*args, **kwargs):
+    from . import ssd
+    return ssd.prefill(*args, **kwargs)
+
+
+def step(*args, **kwargs):
+    from . import ssd
+    return ssd.step(*args, **kwargs)

@@ -1,0 +1,16 @@
+"""The fp64 oracle against its pins (CPU only)."""
+import pytest
+
+import oracle
+import oracle_pins
+
+
+class _Orc:
+    prefill = staticmethod(oracle.prefill)
+    step = staticmethod(oracle.step)
+
+
+@pytest.mark.parametrize("name", sorted(oracle_pins.PINS))
+def test_pin(name):
+    ok, detail = oracle_pins.PINS[name](_Orc)
+    assert ok, f"pin {name} failed: {detail}"
