@@ -1,0 +1,142 @@
+/*
+ * ssd.h -- C ABI of libssd.so: the Mamba-2 SSD (state space duality) selective
+ * scan on AMD Instinct MI355X (gfx950).
+ *
+ * The recurrence, per sequence and per head h (head h reads B/C group
+ * g = floor(h*G/H)):
+ *
+ *     a_t       = exp(dt_t * A_h)
+ *     h_t[n][p] = a_t * h_{t-1}[n][p] + dt_t * x_t[p] * B_t[n]
+ *     y_t[p]    = sum_n C_t[n] * h_t[n][p] + D_h * x_t[p]
+ *
+ * Sources: COREY: Entropy-Guided Runtime Chunk Scheduling for Selective Scan
+ * Kernels, section 3.1 (the generic selective SSM update); Compiler-First State
+ * Space Duality and Portable O(1) Autoregressive Caching for Inference,
+ * Abstract (diagonal per-head dynamics, fixed-size chunking, einsum-dominated
+ * compute, O(1) decode cache) and Tables 7-8 (static causal mask inside a
+ * chunk; decay kept in float32); Recurrence Scan (poot docs), "One equation,
+ * one packed result" and "The schedule" (the scan returns the output and the
+ * carried state; a long sequence may be split across launches that hand the
+ * state on; shapes that do not fit are refused before any work); Mamba-2 SSD
+ * fused layer via VGpuWarp, "S2 RESULT" (the decode state stored so that
+ * consecutive lanes touch consecutive addresses).
+ *
+ * Conventions for every entry point:
+ *  - Every array pointer is caller-owned DEVICE memory, row-major, contiguous.
+ *    The library never allocates, frees or retains caller memory.
+ *  - Work is enqueued on `stream` (hipStream_t passed as void*; NULL = the null
+ *    stream) and returns without synchronising.  Device faults surface at the
+ *    caller's next synchronisation.
+ *  - Return value: SSD_OK, or a negative SSD_ERR_* code.  Arguments are checked
+ *    before anything is enqueued; on error nothing is launched and
+ *    ssd_last_error() describes the problem.  No C++ exception crosses the ABI.
+ *  - Preconditions that are NOT checked (values, not shapes): A_h <= 0,
+ *    dt >= 0, all inputs finite.  Under them every exponent is <= 0.
+ *  - dtype selects the element type of x, B and C (float32 or bfloat16).
+ *    dt, A, D, states and y are always float32; decay math is float32 and
+ *    matrix products accumulate in float32.
+ */
+#ifndef SSD_H
+#define SSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype_t;
+
+enum {
+    SSD_OK = 0,
+    SSD_ERR_INVALID_ARG = -1, /* null pointer, negative size, H % G != 0, ... */
+    SSD_ERR_UNSUPPORTED = -2, /* P, N or chunk without a compiled instance    */
+    SSD_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required   */
+    SSD_ERR_HIP = -4          /* a HIP runtime call or launch failed          */
+};
+
+/* Stages of the chunked prefill, for ssd_scan_prefill_stages(). */
+enum {
+    SSD_STAGE_CHUNK_CUMSUM = 1u, /* per-chunk cumulative log-decay s = cumsum(dt*A) */
+    SSD_STAGE_CHUNK_STATE = 2u,  /* per-chunk state S_c = sum_j exp(s_end-s_j) dt_j B_j x_j^T */
+    SSD_STAGE_STATE_PASS = 4u,   /* sequential carry H_c = exp(s_end) H_{c-1} + S_c     */
+    SSD_STAGE_CHUNK_SCAN = 8u,   /* y = intra-chunk (masked C.B^T) x + exp(s) C.H_in + D x */
+    SSD_STAGE_ALL = 15u
+};
+
+/*
+ * Workspace bytes needed by ssd_scan_prefill() for `total_tokens` tokens in
+ * `nseq` sequences (chunking restarts at every sequence start).  Returns 0 for
+ * arguments ssd_scan_prefill() would reject.
+ */
+size_t ssd_scan_prefill_workspace(int64_t total_tokens, int nseq, int H, int P, int N,
+                                  int chunk, ssd_dtype_t dtype);
+
+/*
+ * Chunked SSD prefill over a packed batch of sequences.
+ *
+ *   x        [T][H][P]      dtype       inputs
+ *   dt       [T][H]         float32     step sizes (softplus already applied)
+ *   A        [H]            float32     per-head decay rate (<= 0)
+ *   B, C     [T][G][N]      dtype       input / output projections
+ *   D        [H]            float32     per-head skip
+ *   h0       [nseq][H][N][P] float32    initial states, or NULL for zeros
+ *   y        [T][H][P]      float32     output (must not alias any input)
+ *   h_out    [nseq][H][N][P] float32    final states, or NULL to skip; may be
+ *                                        the same pointer as h0 (read first)
+ *   cu_seqlens  device int32 [nseq+1], cu[0] = 0, non-decreasing, cu[nseq] = T;
+ *            or NULL for a dense batch of nseq sequences of T/nseq tokens each
+ *   chunk    chunk length Q; the result is the same for every supported Q up
+ *            to floating-point reassociation
+ *   workspace / workspace_bytes   device scratch of at least
+ *            ssd_scan_prefill_workspace(...) bytes (256-byte aligned)
+ *
+ * Supported: P in {16,32,64,128}, N in {16,32,64,128}, chunk in
+ * {32,64,128,256,512}, H % G == 0.  T = 0 copies h0 (or zeros) to h_out.
+ * Splitting a sequence at any token and passing h_out of the first part as h0
+ * of the second gives the same result as one call.
+ */
+int ssd_scan_prefill(const void *x, const float *dt, const float *A, const void *B,
+                     const void *C, const float *D, const float *h0, float *y, float *h_out,
+                     const int32_t *cu_seqlens, int nseq, int64_t total_tokens, int H, int P,
+                     int N, int G, int chunk, ssd_dtype_t dtype, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
+/*
+ * The same computation as ssd_scan_prefill(), running only the stages in the
+ * bitmask `stages` (SSD_STAGE_*).  Stages communicate through the workspace,
+ * so running CHUNK_CUMSUM, CHUNK_STATE, STATE_PASS and CHUNK_SCAN in that order,
+ * in one call or in four calls with identical arguments, equals one
+ * ssd_scan_prefill() call.  Used to time and test each stage on its own.
+ */
+int ssd_scan_prefill_stages(unsigned stages, const void *x, const float *dt, const float *A,
+                            const void *B, const void *C, const float *D, const float *h0,
+                            float *y, float *h_out, const int32_t *cu_seqlens, int nseq,
+                            int64_t total_tokens, int H, int P, int N, int G, int chunk,
+                            ssd_dtype_t dtype, void *workspace, size_t workspace_bytes,
+                            void *stream);
+
+/*
+ * One decode token for `batch` independent states, updated in place.
+ *
+ *   x   [batch][H][P]  dtype;  dt [batch][H] float32;  A, D [H] float32
+ *   B,C [batch][G][N]  dtype
+ *   h   [batch][H][N][P] float32, read and overwritten with the new state
+ *       (layout n-major, p fastest: consecutive lanes touch consecutive bytes)
+ *   y   [batch][H][P]  float32 (must not alias any input)
+ *
+ * Supported: P in {16,32,64,128}, N in {1..1024}, H % G == 0.
+ * Equal to ssd_scan_prefill() over one token with h0 = h.
+ */
+int ssd_step(const void *x, const float *dt, const float *A, const void *B, const void *C,
+             const float *D, float *h, float *y, int batch, int H, int P, int N, int G,
+             ssd_dtype_t dtype, void *stream);
+
+/* Message for the last non-zero return on the calling thread ("" if none). */
+const char *ssd_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SSD_H */

@@ -1,0 +1,124 @@
+// ssd_api.hip -- the C ABI of libssd.so (declared in include/ssd.h).
+//
+// Host-side only: argument checks before anything is enqueued (shapes that
+// have no compiled instance are refused up front, as the Recurrence Scan
+// design note's planner refuses a state column that does not fit, "The
+// schedule"), workspace sizing, and dispatch to the kernels on the caller's
+// stream.  No allocation, no synchronisation, no exception across the ABI.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+
+#include "../../include/ssd.h"
+#include "ssd_launch.h"
+
+namespace {
+
+thread_local char g_err[512];
+
+int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+bool pow2_in(int v, int lo, int hi) { return v >= lo && v <= hi && (v & (v - 1)) == 0; }
+
+int check_prefill(const void *x, const float *dt, const float *A, const void *B, const void *C,
+                  const float *D, float *y, int nseq, int64_t T, int H, int P, int N, int G,
+                  int chunk, ssd_dtype_t dtype, const int32_t *cu) {
+  if (dtype != SSD_F32 && dtype != SSD_BF16) return fail(SSD_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (nseq < 1) return fail(SSD_ERR_INVALID_ARG, "nseq must be >= 1 (got %d)", nseq);
+  if (T < 0 || T > INT32_MAX) return fail(SSD_ERR_INVALID_ARG, "total_tokens %lld out of range", (long long)T);
+  if (H < 1 || G < 1) return fail(SSD_ERR_INVALID_ARG, "H and G must be >= 1 (H=%d G=%d)", H, G);
+  if (H % G != 0) return fail(SSD_ERR_INVALID_ARG, "H %% G != 0 (H=%d G=%d)", H, G);
+  if (!pow2_in(P, 16, 128)) return fail(SSD_ERR_UNSUPPORTED, "headdim P=%d not in {16,32,64,128}", P);
+  if (!pow2_in(N, 16, 128)) return fail(SSD_ERR_UNSUPPORTED, "d_state N=%d not in {16,32,64,128}", N);
+  if (!pow2_in(chunk, 32, 512)) return fail(SSD_ERR_UNSUPPORTED, "chunk=%d not in {32,64,128,256,512}", chunk);
+  if (!cu && T % nseq != 0)
+    return fail(SSD_ERR_INVALID_ARG, "dense batch: total_tokens %lld not divisible by nseq %d", (long long)T, nseq);
+  if (T > 0 && (!x || !dt || !B || !C || !y))
+    return fail(SSD_ERR_INVALID_ARG, "null x/dt/B/C/y pointer");
+  if (!A || !D) return fail(SSD_ERR_INVALID_ARG, "null A/D pointer");
+  if ((int64_t)T * H > INT32_MAX * 16LL) return fail(SSD_ERR_UNSUPPORTED, "problem too large");
+  return SSD_OK;
+}
+
+int prefill_impl(unsigned stages, const void *x, const float *dt, const float *A, const void *B,
+                 const void *C, const float *D, const float *h0, float *y, float *h_out,
+                 const int32_t *cu, int nseq, int64_t T, int H, int P, int N, int G, int chunk,
+                 ssd_dtype_t dtype, void *workspace, size_t workspace_bytes, void *stream) {
+  g_err[0] = 0;
+  int rc = check_prefill(x, dt, A, B, C, D, y, nseq, T, H, P, N, G, chunk, dtype, cu);
+  if (rc) return rc;
+  if (stages & ~(unsigned)SSD_STAGE_ALL) return fail(SSD_ERR_INVALID_ARG, "unknown stage bits 0x%x", stages);
+  const ssd::WorkspaceLayout L =
+      ssd::prefill_layout(T, nseq, H, P, N, chunk, dtype == SSD_BF16 ? 2 : 4);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(SSD_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, L.total);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(SSD_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  ssd::PrefillArgs a{x, dt, A, B, C, D, h0, y, h_out, cu, nseq, T, H, P, N, G, chunk,
+                     dtype == SSD_BF16, workspace, stream};
+  hipError_t e = ssd::launch_prefill(a, stages);
+  if (e != hipSuccess) return fail(SSD_ERR_HIP, "HIP error: %s", hipGetErrorString(e));
+  return SSD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ssd_scan_prefill_workspace(int64_t total_tokens, int nseq, int H, int P, int N, int chunk,
+                                  ssd_dtype_t dtype) {
+  if (dtype != SSD_F32 && dtype != SSD_BF16) return 0;
+  if (nseq < 1 || total_tokens < 0 || total_tokens > INT32_MAX || H < 1) return 0;
+  if (!pow2_in(P, 16, 128) || !pow2_in(N, 16, 128) || !pow2_in(chunk, 32, 512)) return 0;
+  return ssd::prefill_layout(total_tokens, nseq, H, P, N, chunk, dtype == SSD_BF16 ? 2 : 4).total;
+}
+
+int ssd_scan_prefill(const void *x, const float *dt, const float *A, const void *B, const void *C,
+                     const float *D, const float *h0, float *y, float *h_out,
+                     const int32_t *cu_seqlens, int nseq, int64_t total_tokens, int H, int P, int N,
+                     int G, int chunk, ssd_dtype_t dtype, void *workspace, size_t workspace_bytes,
+                     void *stream) {
+  return prefill_impl(SSD_STAGE_ALL, x, dt, A, B, C, D, h0, y, h_out, cu_seqlens, nseq,
+                      total_tokens, H, P, N, G, chunk, dtype, workspace, workspace_bytes, stream);
+}
+
+int ssd_scan_prefill_stages(unsigned stages, const void *x, const float *dt, const float *A,
+                            const void *B, const void *C, const float *D, const float *h0,
+                            float *y, float *h_out, const int32_t *cu_seqlens, int nseq,
+                            int64_t total_tokens, int H, int P, int N, int G, int chunk,
+                            ssd_dtype_t dtype, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+  return prefill_impl(stages, x, dt, A, B, C, D, h0, y, h_out, cu_seqlens, nseq, total_tokens, H,
+                      P, N, G, chunk, dtype, workspace, workspace_bytes, stream);
+}
+
+int ssd_step(const void *x, const float *dt, const float *A, const void *B, const void *C,
+             const float *D, float *h, float *y, int batch, int H, int P, int N, int G,
+             ssd_dtype_t dtype, void *stream) {
+  g_err[0] = 0;
+  if (dtype != SSD_F32 && dtype != SSD_BF16) return fail(SSD_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (batch < 0) return fail(SSD_ERR_INVALID_ARG, "batch must be >= 0 (got %d)", batch);
+  if (H < 1 || G < 1 || H % G != 0) return fail(SSD_ERR_INVALID_ARG, "need H >= 1, G >= 1, H %% G == 0 (H=%d G=%d)", H, G);
+  if (!pow2_in(P, 16, 128)) return fail(SSD_ERR_UNSUPPORTED, "headdim P=%d not in {16,32,64,128}", P);
+  if (N < 1 || N > 1024) return fail(SSD_ERR_UNSUPPORTED, "d_state N=%d not in 1..1024", N);
+  if (batch > 65535) return fail(SSD_ERR_UNSUPPORTED, "batch %d > 65535", batch);
+  if (batch > 0 && (!x || !dt || !A || !B || !C || !D || !h || !y))
+    return fail(SSD_ERR_INVALID_ARG, "null pointer argument");
+  ssd::StepArgs a{x, dt, A, B, C, D, h, y, batch, H, P, N, G, dtype == SSD_BF16, stream};
+  hipError_t e = ssd::launch_step(a);
+  if (e != hipSuccess) return fail(SSD_ERR_HIP, "HIP error: %s", hipGetErrorString(e));
+  return SSD_OK;
+}
+
+const char *ssd_last_error(void) { return g_err; }
+
+}  // extern "C"

@@ -1,0 +1,51 @@
+// ssd_launch.h -- internal interface between the C ABI layer and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ssd {
+
+struct PrefillArgs {
+  const void *x;
+  const float *dt, *A;
+  const void *B, *C;
+  const float *D, *h0;
+  float *y, *h_out;
+  const int32_t *cu;
+  int nseq;
+  int64_t T;
+  int H, P, N, G, Q;
+  bool bf16;
+  void *workspace;
+  void *stream;
+};
+
+// Byte offsets of the prefill workspace regions (each 256-byte aligned).
+struct WorkspaceLayout {
+  int64_t nc_max;  // upper bound on the number of chunks: floor((T + nseq*(Q-1)) / Q)
+  size_t info;     // int4 [max(nc_max,1)]       chunk -> {seq, t0, len, index in seq}
+  size_t seq_off;  // int  [nseq+1]              first chunk of each sequence
+  size_t s;        // f32  [nc_max][H][Q]        chunk-local cumsum of dt*A
+  size_t dt;       // f32  [nc_max][H][Q]        dt, chunk-major (0 on padded rows)
+  size_t S;        // f32  [nc_max][H][N][P]     chunk states
+  size_t hin;      // T    [nc_max][H][N][P]     state entering each chunk (operand type)
+  size_t total;
+};
+
+WorkspaceLayout prefill_layout(int64_t T, int nseq, int H, int P, int N, int Q, int elem);
+hipError_t launch_prefill(const PrefillArgs &a, unsigned stages);
+
+struct StepArgs {
+  const void *x;
+  const float *dt, *A;
+  const void *B, *C;
+  const float *D;
+  float *h, *y;
+  int batch, H, P, N, G;
+  bool bf16;
+  void *stream;
+};
+hipError_t launch_step(const StepArgs &a);
+
+}  // namespace ssd

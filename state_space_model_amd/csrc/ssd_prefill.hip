@@ -1,0 +1,529 @@
+// ssd_prefill.hip -- chunked SSD prefill on gfx950: four kernels.
+//
+// Math (per sequence, head h, chunk c of Q tokens; all exponents <= 0):
+//   s_i    = sum_{k<=i} dt_k A_h                         (chunk-local, float32)
+//   S_c    = sum_j exp(s_{Q-1} - s_j) dt_j  B_j x_j^T     (N x P chunk state)
+//   H_c    = exp(s_{Q-1}) H_{c-1} + S_c,   H_{-1} = h0     (state carried across chunks)
+//   y_i    = sum_{j<=i} (C_i . B_j) exp(s_i - s_j) dt_j x_j   (intra-chunk, causal)
+//          + exp(s_i) C_i . H_{c-1}                         (state entering the chunk)
+//          + D_h x_i
+// This is the unrolled recurrence regrouped into fixed-size chunks: the
+// structured-state-space-duality form of Compiler-First State Space Duality
+// and Portable O(1) Autoregressive Caching for Inference (Abstract: diagonal
+// per-head dynamics, fixed-size chunking, einsum-dominated compute), with the
+// static lower-triangular mask of its Table 7 and the float32 decay of its
+// Table 8; chunk-by-chunk state hand-off as in Recurrence Scan ("One equation,
+// one packed result").
+//
+// Kernels (one launch each, all on the caller's stream):
+//   K1 k_chunk_cumsum : grid (nc_max)       chunk map + s, dt per (chunk, head)
+//   K2 k_chunk_state  : grid (nc_max, H)    S_c^T = (w o X)^T B on MFMA, k = tokens
+//   K3 k_state_pass   : grid (NP/1024,H,nseq) sequential H_c over the chunks of a sequence
+//   K4 k_chunk_scan   : grid (nc_max, H)    C.B^T (k = N), mask/decay, Y^T = X^T M^T
+//                                           (k = tokens) and exp(s) H^T C^T (k = N) on MFMA
+// Every padded row of a partial chunk has dt = 0, x = 0, B = 0: it changes
+// nothing (decay 1, no input), so the chunk-end value s_{Q-1} equals
+// s_{len-1}.
+#include "ssd_device.h"
+#include "ssd_launch.h"
+
+namespace ssd {
+
+// ---------------------------------------------------------------- chunk map
+// Chunks restart at every sequence start: chunk k of sequence s covers tokens
+// cu[s] + kQ .. min(cu[s] + (k+1)Q, cu[s+1]) - 1.  info = {seq, t0, len, k}.
+
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int t = __shfl_up(v, off, 64);
+    if (lane >= off) v += t;
+  }
+  return v;
+}
+
+// Block-wide inclusive scan (blockDim.x a multiple of 64, <= 1024).
+__device__ int block_incl_scan(int v, int *sh, int &total) {
+  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  v = wave_incl_scan(v);
+  if ((threadIdx.x & 63) == 63) sh[wave] = v;
+  __syncthreads();
+  int prefix = 0;
+  total = 0;
+  for (int w = 0; w < nw; ++w) {
+    int s = sh[w];
+    if (w < wave) prefix += s;
+    total += s;
+  }
+  __syncthreads();
+  return v + prefix;
+}
+
+__global__ __launch_bounds__(256) void k_chunk_cumsum(const float *__restrict__ dt,
+                                                      const float *__restrict__ A,
+                                                      const int32_t *__restrict__ cu, int nseq,
+                                                      int L_dense, int64_t T, int H, int Q,
+                                                      int nc_max, int4 *__restrict__ info_out,
+                                                      int *__restrict__ seq_off,
+                                                      float *__restrict__ s_out,
+                                                      float *__restrict__ dt_out) {
+  __shared__ int sh_scan[16];
+  __shared__ int4 sh_info;
+  const int c = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (tid == 0) sh_info = make_int4(-1, 0, 0, 0);
+  __syncthreads();
+  if (cu == nullptr) {
+    const int cps = (L_dense + Q - 1) / Q;
+    if (tid == 0 && cps > 0) {
+      const int seq = c / cps, k = c % cps;
+      if (seq < nseq) sh_info = make_int4(seq, seq * L_dense + k * Q, min(Q, L_dense - k * Q), k);
+    }
+    if (blockIdx.x == 0)
+      for (int s = tid; s <= nseq; s += blockDim.x) seq_off[s] = s * cps;
+  } else {
+    int running = 0;
+    for (int base = 0; base < nseq; base += blockDim.x) {
+      const int s = base + tid;
+      int start = 0, len = 0;
+      if (s < nseq) {
+        start = cu[s];
+        len = max(0, cu[s + 1] - start);
+        if (start < 0 || (int64_t)start + len > T) len = 0;  // malformed: no chunks
+      }
+      const int cnt = (len + Q - 1) / Q;
+      int total;
+      const int incl = block_incl_scan(cnt, sh_scan, total);
+      const int excl = incl - cnt;
+      if (cnt > 0 && running + excl <= c && c < running + incl) {
+        const int k = c - running - excl;
+        sh_info = make_int4(s, start + k * Q, min(Q, len - k * Q), k);
+      }
+      if (blockIdx.x == 0 && s < nseq) seq_off[s] = running + excl;
+      running += total;
+    }
+    if (blockIdx.x == 0 && tid == 0) seq_off[nseq] = running;
+  }
+  __syncthreads();
+  const int4 ci = sh_info;
+  if (c >= nc_max) return;
+  if (tid == 0) info_out[c] = ci.x < 0 ? make_int4(0, 0, 0, 0) : ci;
+  if (ci.x < 0 || ci.z <= 0) return;
+
+  // chunk-local inclusive cumsum of dt*A per head; padded rows get dt = 0
+  const int wave = tid >> 6, lane = tid & 63, nw = blockDim.x >> 6;
+  for (int h = wave; h < H; h += nw) {
+    const float a = A[h];
+    float carry = 0.f;
+    float *so = s_out + ((size_t)c * H + h) * Q;
+    float *dto = dt_out + ((size_t)c * H + h) * Q;
+    for (int i0 = 0; i0 < Q; i0 += 64) {
+      const int i = i0 + lane;
+      const float d = (i < ci.z) ? dt[((size_t)ci.y + i) * H + h] : 0.f;
+      float v = d * a;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        float t = __shfl_up(v, off, 64);
+        if (lane >= off) v += t;
+      }
+      v += carry;
+      if (i < Q) {
+        so[i] = v;
+        dto[i] = d;
+      }
+      carry = __shfl(v, 63, 64);
+    }
+  }
+}
+
+// ---------------------------------------------------------- staging helpers
+// Copy rows [r0, r0+nrows) of a token-major operand into an LDS tile
+// (pitch `pitch` elements), optionally scaling row r by scale[r]; rows at or
+// beyond `len`, and columns at or beyond `width`, are zero.
+template <typename T, int WIDTH, int WPAD>
+__device__ __forceinline__ void stage_rows(T *tile, int pitch, const T *__restrict__ src,
+                                           size_t row_stride, int r0, int nrows, int len,
+                                           const float *scale) {
+  typedef typename Vec16<T>::type V;
+  constexpr int VN = Vec16<T>::n;
+  constexpr int VPR = WPAD / VN;  // 16-byte vectors per tile row
+  const int total = nrows * VPR;
+  for (int idx = threadIdx.x; idx < total; idx += blockDim.x) {
+    const int r = idx / VPR, v = idx % VPR;
+    const int row = r0 + r;
+    V val = vzero<V>();
+    if (row < len && v * VN < WIDTH) {
+      val = *reinterpret_cast<const V *>(src + (size_t)row * row_stride + v * VN);
+      if (scale) val = vscale(val, scale[row]);
+    }
+    *reinterpret_cast<V *>(tile + r * pitch + v * VN) = val;
+  }
+}
+
+constexpr int kJP = 128;  // token rows staged in LDS per phase (K2, K4)
+
+// ------------------------------------------------------------ K2 chunk state
+// S_c^T[p][n] = sum_j X'[j][p] B[j][n],  X'[j] = exp(s_end - s_j) dt_j x_j.
+// MFMA 16x16 tiles over (p, n); k = tokens, read from token-major LDS tiles
+// with the transpose read.  Output stored as S[c][h][n][p] (float32).
+template <typename T, int P, int N>
+__global__ __launch_bounds__(256) void k_chunk_state(const T *__restrict__ x, const T *__restrict__ B,
+                                                     const float *__restrict__ s_ws,
+                                                     const float *__restrict__ dt_ws,
+                                                     const int4 *__restrict__ info, int H, int G,
+                                                     int Q, float *__restrict__ S_out) {
+  constexpr int PAD = 16 / sizeof(T);
+  constexpr int XP = P + PAD, BP = N + PAD;
+  constexpr int NPT = P / 16, NNT = N / 16, NT = NPT * NNT, TPW = (NT + 3) / 4;
+  const int c = blockIdx.x, hd = blockIdx.y;
+  const int4 ci = info[c];
+  if (ci.z <= 0) return;
+  const int g = (hd * G) / H;
+  const int JP = Q < kJP ? Q : kJP;
+  extern __shared__ __align__(16) char smem[];
+  T *Xs = reinterpret_cast<T *>(smem);
+  T *Bs = Xs + JP * XP;
+  float *w = reinterpret_cast<float *>(Bs + JP * BP);
+
+  const float *sc = s_ws + ((size_t)c * H + hd) * Q;
+  const float *dtc = dt_ws + ((size_t)c * H + hd) * Q;
+  const float s_end = sc[Q - 1];
+  for (int i = threadIdx.x; i < Q; i += blockDim.x) w[i] = expf(fminf(s_end - sc[i], 0.f)) * dtc[i];
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, grp = lane >> 4;
+  f4 acc[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) acc[t] = zero4();
+
+  const T *xs = x + ((size_t)ci.y * H + hd) * P;
+  const T *bs = B + ((size_t)ci.y * G + g) * N;
+  for (int ph = 0; ph < ci.z; ph += JP) {  // phases past the chunk length add nothing
+    __syncthreads();
+    stage_rows<T, P, P>(Xs, XP, xs, (size_t)H * P, ph, JP, ci.z, w);
+    stage_rows<T, N, N>(Bs, BP, bs, (size_t)G * N, ph, JP, ci.z, nullptr);
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const int tile = wave + 4 * t;
+      if (tile < NT) {
+        const int pt = tile / NNT, nt = tile % NNT;
+        for (int k0 = 0; k0 < JP; k0 += 32) {
+          Frag<T> a = frag_kmaj(Xs, XP, pt * 16, k0 + 8 * grp, k0 + 8 * grp + 4);
+          Frag<T> b = frag_kmaj(Bs, BP, nt * 16, k0 + 8 * grp, k0 + 8 * grp + 4);
+          mma(acc[t], a, b);
+        }
+      }
+    }
+  }
+  float *so = S_out + ((size_t)c * H + hd) * (size_t)(N * P);
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int tile = wave + 4 * t;
+    if (tile < NT) {
+      const int pt = tile / NNT, nt = tile % NNT;
+      const int n = nt * 16 + (lane & 15), p = pt * 16 + 4 * grp;
+      st4(so + (size_t)n * P + p, acc[t]);
+    }
+  }
+}
+
+// ----------------------------------------------------------- K3 state pass
+// Per (sequence, head), per 4 state elements: walk the sequence's chunks in
+// order, emit the state entering each chunk (as the MFMA operand type) and
+// the final state.
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_state_pass(const float *__restrict__ S,
+                                                    const float *__restrict__ s_ws,
+                                                    const int *__restrict__ seq_off,
+                                                    const float *h0, float *h_out,
+                                                    T *__restrict__ hin, int H, int NP, int Q) {
+  const int s = blockIdx.z, hd = blockIdx.y;
+  const int e = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (e >= NP) return;
+  const int c0 = seq_off[s], c1 = seq_off[s + 1];
+  const size_t hofs = ((size_t)s * H + hd) * NP + e;
+  f4 st = h0 ? ld4(h0 + hofs) : zero4();
+  if (c0 < c1) {
+    size_t base = ((size_t)c0 * H + hd) * NP + e;
+    f4 Sc = ld4(S + base);
+    float sl = s_ws[((size_t)c0 * H + hd) * Q + Q - 1];
+    for (int c = c0; c < c1; ++c) {
+      f4 Sn = Sc;
+      float sn = sl;
+      const size_t nbase = ((size_t)(c + 1) * H + hd) * NP + e;
+      if (c + 1 < c1) {  // prefetch the next chunk's state and decay
+        Sn = ld4(S + nbase);
+        sn = s_ws[((size_t)(c + 1) * H + hd) * Q + Q - 1];
+      }
+      st4T(hin + base, st);
+      const float a = expf(fminf(sl, 0.f));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) st[q] = a * st[q] + Sc[q];
+      Sc = Sn;
+      sl = sn;
+      base = nbase;
+    }
+  }
+  if (h_out) st4(h_out + hofs, st);
+}
+
+// ------------------------------------------------------------ K4 chunk scan
+// Per (chunk, head).  Wave w owns up to four 16-token output tiles
+// {w, 2W-1-w, 2W+w, 4W-1-w} (W waves), which balances the causal work.
+//   Y^T[p][i]  = exp(s_i) (H_in^T C^T)[p][i]            k = n    (A: H_in tile via transpose read)
+//             += sum_j X^T[p][j] M^T[j][i]              k = j    (A: X tile via transpose read)
+//   M^T[j][i]  = (B C^T)[j][i] exp(s_i - s_j) dt_j  (j <= i)     k = n
+// The two 16x16 results of B C^T for j-rows jb..jb+15 and jb+16..jb+31 are
+// fed straight back as the B operand (paired k map); X^T is read with the
+// same pairing.
+template <typename T, int P, int N>
+__global__ __launch_bounds__(512) void k_chunk_scan(const T *__restrict__ x, const T *__restrict__ B,
+                                                    const T *__restrict__ C,
+                                                    const float *__restrict__ D,
+                                                    const float *__restrict__ s_ws,
+                                                    const float *__restrict__ dt_ws,
+                                                    const T *__restrict__ hin,
+                                                    const int4 *__restrict__ info, int H, int G,
+                                                    int Q, float *__restrict__ y) {
+  constexpr int PAD = 16 / sizeof(T);
+  constexpr int NK = N < 32 ? 32 : N;  // contraction over n, padded to the k-step
+  constexpr int KS = NK / 32;
+  constexpr int XP = P + PAD, BP = NK + PAD, HP = P + PAD;
+  constexpr int NPT = P / 16;
+  const int c = blockIdx.x, hd = blockIdx.y;
+  const int4 ci = info[c];
+  if (ci.z <= 0) return;
+  const int len = ci.z;
+  const int g = (hd * G) / H;
+  const int JP = Q < kJP ? Q : kJP;
+  const int nw = blockDim.x >> 6, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int grp = lane >> 4, col = lane & 15;
+
+  extern __shared__ __align__(16) char smem[];
+  float *s_l = reinterpret_cast<float *>(smem);
+  float *dt_l = s_l + Q;
+  T *region = reinterpret_cast<T *>(dt_l + Q);
+  T *Hs = region;             // [NK][HP]   (first)
+  T *Bs = region;             // [JP][BP]   (then, per phase)
+  T *Xs = region + JP * BP;   // [JP][XP]
+
+  const size_t csh = (size_t)c * H + hd;
+  for (int i = threadIdx.x; i < Q; i += blockDim.x) {
+    s_l[i] = s_ws[csh * Q + i];
+    dt_l[i] = dt_ws[csh * Q + i];
+  }
+  stage_rows<T, P, P>(Hs, HP, hin + csh * (size_t)(N * P), (size_t)P, 0, NK, N, nullptr);
+  __syncthreads();
+
+  const int NTI = Q / 16;
+  int tiles[4] = {wave, 2 * nw - 1 - wave, 2 * nw + wave, 4 * nw - 1 - wave};
+  const T *Cg = C + ((size_t)ci.y * G + g) * N;
+  Frag<T> cf[4][KS];
+  float si[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = tiles[k] * 16 + col;
+    const bool valid = tiles[k] < NTI && i < len;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int n8 = ks * 32 + 8 * grp;
+      cf[k][ks] = (valid && n8 < N) ? frag_global(Cg + (size_t)i * G * N + n8) : frag_zero<T>();
+    }
+    si[k] = tiles[k] < NTI ? s_l[i] : 0.f;
+  }
+
+  f4 acc[4][NPT];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+#pragma unroll
+    for (int pt = 0; pt < NPT; ++pt) acc[k][pt] = zero4();
+    if (tiles[k] < NTI) {
+#pragma unroll
+      for (int pt = 0; pt < NPT; ++pt) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          Frag<T> a = frag_kmaj(Hs, HP, pt * 16, ks * 32 + 8 * grp, ks * 32 + 8 * grp + 4);
+          mma(acc[k][pt], a, cf[k][ks]);
+        }
+      }
+      const float ei = expf(fminf(si[k], 0.f));
+#pragma unroll
+      for (int pt = 0; pt < NPT; ++pt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[k][pt][r] *= ei;
+    }
+  }
+
+  const T *xs = x + ((size_t)ci.y * H + hd) * P;
+  const T *bs = B + ((size_t)ci.y * G + g) * N;
+  for (int ph = 0; ph < len; ph += JP) {  // phases past the chunk length add nothing
+    __syncthreads();  // previous users of the region are done
+    stage_rows<T, N, NK>(Bs, BP, bs + (size_t)ph * G * N, (size_t)G * N, 0, JP, len - ph, nullptr);
+    stage_rows<T, P, P>(Xs, XP, xs + (size_t)ph * H * P, (size_t)H * P, 0, JP, len - ph, nullptr);
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (tiles[k] >= NTI || tiles[k] * 16 >= len) continue;
+      const int ilast = tiles[k] * 16 + 15;
+      const int i = tiles[k] * 16 + col;
+      const int jend = min(ph + JP, ilast + 1);
+      for (int jb = ph; jb < jend; jb += 32) {
+        f4 g0 = zero4(), g1 = zero4();
+        const int jl = jb - ph;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          Frag<T> b0 = frag_rowk(Bs, BP, jl + col, ks * 32 + 8 * grp);
+          Frag<T> b1 = frag_rowk(Bs, BP, jl + 16 + col, ks * 32 + 8 * grp);
+          mma(g0, b0, cf[k][ks]);
+          mma(g1, b1, cf[k][ks]);
+        }
+        const f4 sj0 = ld4(s_l + jb + 4 * grp), sj1 = ld4(s_l + jb + 16 + 4 * grp);
+        const f4 dj0 = ld4(dt_l + jb + 4 * grp), dj1 = ld4(dt_l + jb + 16 + 4 * grp);
+        float m[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j0 = jb + 4 * grp + r, j1 = j0 + 16;
+          m[r] = (j0 <= i) ? g0[r] * expf(fminf(si[k] - sj0[r], 0.f)) * dj0[r] : 0.f;
+          m[4 + r] = (j1 <= i) ? g1[r] * expf(fminf(si[k] - sj1[r], 0.f)) * dj1[r] : 0.f;
+        }
+        const Frag<T> mf = frag_from_f32(m, T());
+#pragma unroll
+        for (int pt = 0; pt < NPT; ++pt) {
+          Frag<T> a = frag_kmaj(Xs, XP, pt * 16, jl + 4 * grp, jl + 16 + 4 * grp);
+          mma(acc[k][pt], a, mf);
+        }
+      }
+    }
+  }
+
+  const float dv = D[hd];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = tiles[k] * 16 + col;
+    if (tiles[k] >= NTI || i >= len) continue;
+    const size_t row = ((size_t)ci.y + i) * H + hd;
+#pragma unroll
+    for (int pt = 0; pt < NPT; ++pt) {
+      const int p = pt * 16 + 4 * grp;
+      const f4 xv = ld4f(x + row * P + p);
+      f4 o;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[r] = acc[k][pt][r] + dv * xv[r];
+      st4(y + row * P + p, o);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ launch
+static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+WorkspaceLayout prefill_layout(int64_t T, int nseq, int H, int P, int N, int Q, int elem) {
+  WorkspaceLayout L{};
+  const int64_t nc = (T + (int64_t)nseq * (Q - 1)) / Q;
+  L.nc_max = nc;
+  size_t off = 0;
+  L.info = off;
+  off = align_up(off + 16 * (size_t)(nc > 0 ? nc : 1), 256);
+  L.seq_off = off;
+  off = align_up(off + 4 * (size_t)(nseq + 1), 256);
+  L.s = off;
+  off = align_up(off + 4 * (size_t)nc * H * Q, 256);
+  L.dt = off;
+  off = align_up(off + 4 * (size_t)nc * H * Q, 256);
+  L.S = off;
+  off = align_up(off + 4 * (size_t)nc * H * N * P, 256);
+  L.hin = off;
+  off = align_up(off + (size_t)elem * nc * H * N * P, 256);
+  L.total = off;
+  return L;
+}
+
+template <typename T, int P, int N>
+static hipError_t run_prefill(const PrefillArgs &a, unsigned stages) {
+  const WorkspaceLayout L = prefill_layout(a.T, a.nseq, a.H, P, N, a.Q, sizeof(T));
+  char *ws = static_cast<char *>(a.workspace);
+  int4 *info = reinterpret_cast<int4 *>(ws + L.info);
+  int *seq_off = reinterpret_cast<int *>(ws + L.seq_off);
+  float *s_ws = reinterpret_cast<float *>(ws + L.s);
+  float *dt_ws = reinterpret_cast<float *>(ws + L.dt);
+  float *S = reinterpret_cast<float *>(ws + L.S);
+  T *hin = reinterpret_cast<T *>(ws + L.hin);
+  const int nc = (int)L.nc_max;
+  const int L_dense = a.cu ? 0 : (int)(a.T / a.nseq);
+  const int JP = a.Q < kJP ? a.Q : kJP;
+  hipStream_t st = static_cast<hipStream_t>(a.stream);
+
+  if (stages & 1u) {
+    hipLaunchKernelGGL(k_chunk_cumsum, dim3(nc > 0 ? nc : 1), dim3(256), 0, st, a.dt, a.A, a.cu,
+                       a.nseq, L_dense, a.T, a.H, a.Q, nc, info, seq_off, s_ws, dt_ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if ((stages & 2u) && nc > 0) {
+    constexpr int PAD = 16 / sizeof(T);
+    const size_t lds = (size_t)JP * ((P + PAD) + (N + PAD)) * sizeof(T) + 4 * (size_t)a.Q;
+    auto kern = k_chunk_state<T, P, N>;
+    hipError_t e = hipFuncSetAttribute((const void *)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(nc, a.H), dim3(256), lds, st, (const T *)a.x, (const T *)a.B,
+                       s_ws, dt_ws, info, a.H, a.G, a.Q, S);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (stages & 4u) {
+    const int NP = N * P;
+    hipLaunchKernelGGL(k_state_pass<T>, dim3((NP + 1023) / 1024, a.H, a.nseq), dim3(256), 0, st,
+                       S, s_ws, seq_off, a.h0, a.h_out, hin, a.H, NP, a.Q);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if ((stages & 8u) && nc > 0) {
+    constexpr int PAD = 16 / sizeof(T);
+    constexpr int NK = N < 32 ? 32 : N;
+    const size_t region =
+        std::max((size_t)NK * (P + PAD), (size_t)JP * ((NK + PAD) + (P + PAD))) * sizeof(T);
+    const size_t lds = 8 * (size_t)a.Q + region;
+    const int threads = a.Q >= 64 ? a.Q : 64;  // Q/64 waves, at least one
+    auto kern = k_chunk_scan<T, P, N>;
+    hipError_t e = hipFuncSetAttribute((const void *)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(nc, a.H), dim3(threads), lds, st, (const T *)a.x,
+                       (const T *)a.B, (const T *)a.C, a.D, s_ws, dt_ws, (const T *)hin, info,
+                       a.H, a.G, a.Q, a.y);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <typename T, int P>
+static hipError_t dispatch_N(const PrefillArgs &a, unsigned stages) {
+  switch (a.N) {
+    case 16: return run_prefill<T, P, 16>(a, stages);
+    case 32: return run_prefill<T, P, 32>(a, stages);
+    case 64: return run_prefill<T, P, 64>(a, stages);
+    case 128: return run_prefill<T, P, 128>(a, stages);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+static hipError_t dispatch_P(const PrefillArgs &a, unsigned stages) {
+  switch (a.P) {
+    case 16: return dispatch_N<T, 16>(a, stages);
+    case 32: return dispatch_N<T, 32>(a, stages);
+    case 64: return dispatch_N<T, 64>(a, stages);
+    case 128: return dispatch_N<T, 128>(a, stages);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill(const PrefillArgs &a, unsigned stages) {
+  return a.bf16 ? dispatch_P<bf16>(a, stages) : dispatch_P<float>(a, stages);
+}
+
+}  // namespace ssd

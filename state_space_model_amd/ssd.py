@@ -1,0 +1,182 @@
+"""ctypes binding over libssd.so (C ABI in include/ssd.h).
+
+Argument marshalling only: shape/dtype/device checks, output and workspace
+allocation with torch, and the current torch stream handle.  Every step of the
+computation runs in the HIP library; if the library is missing this module
+raises instead of computing anything itself.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libssd.so")
+
+SSD_F32, SSD_BF16 = 0, 1
+STAGE_CHUNK_CUMSUM, STAGE_CHUNK_STATE, STAGE_STATE_PASS, STAGE_CHUNK_SCAN = 1, 2, 4, 8
+STAGE_ALL = 15
+ERRORS = {0: "SSD_OK", -1: "SSD_ERR_INVALID_ARG", -2: "SSD_ERR_UNSUPPORTED",
+          -3: "SSD_ERR_WORKSPACE", -4: "SSD_ERR_HIP"}
+EXPORTS = ("ssd_scan_prefill_workspace", "ssd_scan_prefill", "ssd_scan_prefill_stages",
+           "ssd_step", "ssd_last_error")
+
+_lib = None
+
+
+class SSDError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"{ERRORS.get(code, code)}: {msg}")
+        self.code = code
+
+
+def load(path=LIB_PATH):
+    """Load libssd.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with state_space_model_amd/build.py")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, sz, u32 = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t,
+                             ctypes.c_uint)
+    lib.ssd_scan_prefill_workspace.argtypes = [i64, i32, i32, i32, i32, i32, i32]
+    lib.ssd_scan_prefill_workspace.restype = sz
+    pre = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, i32, i32, vp, sz,
+           vp]
+    lib.ssd_scan_prefill.argtypes = pre
+    lib.ssd_scan_prefill.restype = i32
+    lib.ssd_scan_prefill_stages.argtypes = [u32] + pre
+    lib.ssd_scan_prefill_stages.restype = i32
+    lib.ssd_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+    lib.ssd_step.restype = i32
+    lib.ssd_last_error.argtypes = []
+    lib.ssd_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(rc):
+    if rc != 0:
+        raise SSDError(rc, load().ssd_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return SSD_F32
+    if t.dtype == torch.bfloat16:
+        return SSD_BF16
+    raise TypeError(f"x/B/C must be float32 or bfloat16, got {t.dtype}")
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, name, dtype=None, dev=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if dev is not None and t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, expected {dev}")
+
+
+def workspace_bytes(total_tokens, nseq, H, P, N, chunk, dtype=torch.bfloat16):
+    code = SSD_BF16 if dtype == torch.bfloat16 else SSD_F32
+    return int(load().ssd_scan_prefill_workspace(total_tokens, nseq, H, P, N, chunk, code))
+
+
+def alloc_workspace(total_tokens, nseq, H, P, N, chunk, dtype, device):
+    n = workspace_bytes(total_tokens, nseq, H, P, N, chunk, dtype)
+    if n == 0:
+        raise SSDError(-2, "unsupported prefill shape")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def prefill(x, dt, A, B, C, D, h0=None, chunk=256, cu_seqlens=None, *, nseq=None, y=None,
+            h_out=None, workspace=None, stages=STAGE_ALL):
+    """Chunked SSD prefill.
+
+    x [T,H,P] (or [b,L,H,P]), dt [T,H], A [H], B/C [T,G,N], D [H], h0
+    [nseq,H,N,P] float32 or None, cu_seqlens int32 [nseq+1] or None (dense
+    batch: ``nseq`` sequences of T/nseq tokens; a 4-d x gives nseq = b).
+    Returns (y [T,H,P] float32, h_out [nseq,H,N,P] float32).
+    """
+    dense4 = x.dim() == 4
+    if dense4:
+        b, L, H, P = x.shape
+        nseq = b if nseq is None else nseq
+        x = x.reshape(b * L, H, P)
+        dt = dt.reshape(b * L, H)
+        B = B.reshape(b * L, *B.shape[-2:])
+        C = C.reshape(b * L, *C.shape[-2:])
+    T, H, P = x.shape
+    G, N = B.shape[-2], B.shape[-1]
+    dev = x.device
+    _need(x, "x", dev=dev)
+    code = _dtype_code(x)
+    for t, n in ((B, "B"), (C, "C")):
+        _need(t, n, x.dtype, dev)
+    for t, n in ((dt, "dt"), (A, "A"), (D, "D")):
+        _need(t, n, torch.float32, dev)
+    if tuple(dt.shape) != (T, H) or tuple(A.shape) != (H,) or tuple(D.shape) != (H,):
+        raise ValueError("dt must be [T,H], A and D [H]")
+    if tuple(B.shape) != (T, G, N) or tuple(C.shape) != (T, G, N):
+        raise ValueError("B and C must be [T,G,N]")
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+        nseq = cu_seqlens.numel() - 1
+    elif nseq is None:
+        nseq = 1
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, dev)
+        if tuple(h0.shape) != (nseq, H, N, P):
+            raise ValueError(f"h0 must be [{nseq},{H},{N},{P}]")
+    if y is None:
+        y = torch.empty((T, H, P), dtype=torch.float32, device=dev)
+    if h_out is None:
+        h_out = torch.empty((nseq, H, N, P), dtype=torch.float32, device=dev)
+    _need(y, "y", torch.float32, dev)
+    _need(h_out, "h_out", torch.float32, dev)
+    if workspace is None:
+        workspace = alloc_workspace(T, nseq, H, P, N, chunk, x.dtype, dev)
+    lib = load()
+    _check(lib.ssd_scan_prefill_stages(
+        stages, _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(y),
+        _ptr(h_out), _ptr(cu_seqlens), nseq, T, H, P, N, G, chunk, code, _ptr(workspace),
+        workspace.numel(), _stream()))
+    if dense4:
+        y = y.reshape(nseq, T // nseq, H, P)
+    return y, h_out
+
+
+def step(x, dt, A, B, C, D, h, y=None):
+    """One decode token; h [b,H,N,P] float32 is updated in place.  Returns y [b,H,P]."""
+    b, H, P = x.shape
+    G, N = B.shape[-2], B.shape[-1]
+    dev = x.device
+    _need(x, "x", dev=dev)
+    code = _dtype_code(x)
+    for t, n in ((B, "B"), (C, "C")):
+        _need(t, n, x.dtype, dev)
+    for t, n in ((dt, "dt"), (A, "A"), (D, "D"), (h, "h")):
+        _need(t, n, torch.float32, dev)
+    if tuple(h.shape) != (b, H, N, P) or tuple(B.shape) != (b, G, N) or tuple(C.shape) != (b, G, N):
+        raise ValueError("h must be [b,H,N,P], B/C [b,G,N]")
+    if tuple(dt.shape) != (b, H):
+        raise ValueError("dt must be [b,H]")
+    if y is None:
+        y = torch.empty((b, H, P), dtype=torch.float32, device=dev)
+    _need(y, "y", torch.float32, dev)
+    _check(load().ssd_step(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h),
+                           _ptr(y), b, H, P, N, G, code, _stream()))
+    return y

@@ -1,0 +1,110 @@
+"""C-ABI library checks that need no GPU: it loads, exports every symbol the
+header declares, sizes workspaces, and refuses bad arguments before any
+launch (error paths only; no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from state_space_model_amd import ssd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssd.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssd_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_binding_exports():
+    assert _declared() == sorted(ssd.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(ssd.LIB_PATH)
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_workspace_size():
+    lib = ssd.load()
+    w = lib.ssd_scan_prefill_workspace
+    n1 = w(4096, 1, 24, 64, 128, 256, 1)
+    nc = 16
+    expect_min = nc * 24 * 128 * 64 * (4 + 2) + 2 * nc * 24 * 256 * 4
+    assert expect_min <= n1 <= expect_min + 8192
+    assert w(4096, 1, 24, 64, 128, 256, 0) > n1          # float32 operand copy of H_in
+    assert w(4096, 1, 24, 64, 100, 256, 1) == 0          # unsupported N
+    assert w(4096, 1, 24, 64, 128, 96, 1) == 0           # unsupported chunk
+    assert w(-1, 1, 24, 64, 128, 256, 1) == 0
+    assert w(0, 1, 24, 64, 128, 256, 1) > 0
+
+
+def _prefill_rc(**kw):
+    lib = ssd.load()
+    a = dict(x=1, dt=1, A=1, B=1, C=1, D=1, h0=None, y=1, h_out=None, cu=None, nseq=1, T=64,
+             H=4, P=16, N=16, G=1, chunk=64, dtype=0, ws=None, wsb=0)
+    a.update(kw)
+    p = lambda v: None if v is None else ctypes.c_void_p(v)
+    rc = lib.ssd_scan_prefill(p(a["x"]), p(a["dt"]), p(a["A"]), p(a["B"]), p(a["C"]), p(a["D"]),
+                              p(a["h0"]), p(a["y"]), p(a["h_out"]), p(a["cu"]), a["nseq"], a["T"],
+                              a["H"], a["P"], a["N"], a["G"], a["chunk"], a["dtype"], p(a["ws"]),
+                              a["wsb"], None)
+    return rc, lib.ssd_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(H=6, G=4), -1, "H % G"),
+    (dict(P=24), -2, "headdim"),
+    (dict(N=100), -2, "d_state"),
+    (dict(chunk=48), -2, "chunk"),
+    (dict(chunk=1024), -2, "chunk"),
+    (dict(nseq=0), -1, "nseq"),
+    (dict(T=65, nseq=2), -1, "divisible"),
+    (dict(x=None), -1, "null"),
+    (dict(A=None), -1, "null"),
+    (dict(dtype=7), -1, "dtype"),
+    (dict(ws=None, wsb=0), -3, "workspace"),
+    (dict(ws=256, wsb=16), -3, "workspace"),
+])
+def test_prefill_rejects_before_launch(kw, code, frag):
+    rc, msg = _prefill_rc(**kw)
+    assert rc == code and frag in msg, (rc, msg)
+
+
+def test_stage_mask_rejected():
+    lib = ssd.load()
+    rc = lib.ssd_scan_prefill_stages(16, *([ctypes.c_void_p(1)] * 10), 1, 64, 4, 16, 16, 1, 64, 0,
+                                     ctypes.c_void_p(256), 1 << 30, None)
+    assert rc == -1 and "stage" in lib.ssd_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(H=6, G=4), -1, "H % G"),
+    (dict(P=8), -2, "headdim"),
+    (dict(N=0), -2, "d_state"),
+    (dict(N=2048), -2, "d_state"),
+    (dict(batch=-1), -1, "batch"),
+    (dict(x=None), -1, "null"),
+    (dict(dtype=3), -1, "dtype"),
+])
+def test_step_rejects_before_launch(kw, code, frag):
+    lib = ssd.load()
+    a = dict(x=1, batch=2, H=4, P=16, N=16, G=1, dtype=0)
+    a.update(kw)
+    p = ctypes.c_void_p
+    xptr = None if a["x"] is None else p(a["x"])
+    rc = lib.ssd_step(xptr, p(1), p(1), p(1), p(1), p(1), p(1), p(1), a["batch"], a["H"], a["P"],
+                      a["N"], a["G"], a["dtype"], None)
+    assert rc == code and frag in lib.ssd_last_error().decode()
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(64, 4, 16)
+    with pytest.raises(ValueError, match="GPU"):
+        ssd.prefill(x, torch.zeros(64, 4), torch.zeros(4), torch.zeros(64, 1, 16),
+                    torch.zeros(64, 1, 16), torch.zeros(4))

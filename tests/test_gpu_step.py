@@ -1,0 +1,89 @@
+"""GPU decode step (ssd_step through the C ABI) against the fp64 oracle."""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import TOL, log, maxabs, select_heads
+from state_space_model_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_steps(d, dtype, steps):
+    import torch
+    from state_space_model_amd import ssd
+    op = torch.bfloat16 if dtype == "bf16" else torch.float32
+    dev = "cuda"
+    h = torch.from_numpy(d["h"]).to(dev)
+    A = torch.from_numpy(d["A"]).to(dev)
+    D = torch.from_numpy(d["D"]).to(dev)
+    x = torch.from_numpy(d["x"]).to(dev).to(op)
+    dt = torch.from_numpy(d["dt"]).to(dev)
+    B = torch.from_numpy(d["B"]).to(dev).to(op)
+    C = torch.from_numpy(d["C"]).to(dev).to(op)
+    ys = []
+    for t in range(steps):
+        ys.append(ssd.step(x[t].contiguous(), dt[t].contiguous(), A, B[t].contiguous(),
+                           C[t].contiguous(), D, h))
+    torch.cuda.synchronize()
+    return np.stack([y.cpu().numpy() for y in ys]), h.cpu().numpy()
+
+
+def _oracle_steps(d, steps, bsel=None):
+    h = d["h"].astype(np.float64)
+    sl = slice(None) if bsel is None else bsel
+    h = np.ascontiguousarray(h[sl])
+    ys = []
+    for t in range(steps):
+        ys.append(oracle.step(d["x"][t][sl], d["dt"][t][sl], d["A"], d["B"][t][sl], d["C"][t][sl],
+                              d["D"], h))
+    return np.stack(ys), h
+
+
+def _small(b, H, P, N, G, steps, seed, dtype):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    d = inputs.prefill_inputs(H, P, N, G, [b * steps], seed, dtype=dtype)
+    lead = lambda a: np.ascontiguousarray(a.reshape(b, steps, *a.shape[1:]).swapaxes(0, 1))
+    return dict(x=lead(d["x"]), dt=lead(d["dt"]), B=lead(d["B"]), C=lead(d["C"]), A=d["A"],
+                D=d["D"], h=rng.normal(0, 0.1, size=(b, H, N, P)).astype(np.float32))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("b,H,P,N,G", [(1, 1, 16, 16, 1), (3, 4, 32, 48, 2), (2, 8, 64, 128, 8),
+                                       (5, 6, 128, 7, 3), (4, 2, 16, 1024, 1)])
+def test_step_small(dtype, b, H, P, N, G):
+    log(f"step small dtype={dtype} b={b} H={H} P={P} N={N} G={G}")
+    d = _small(b, H, P, N, G, 5, 100 + b + H + P + N, dtype)
+    y, h = _run_steps(d, dtype, 5)
+    ry, rh = _oracle_steps(d, 5)
+    assert maxabs(y, ry) <= TOL["f32"]
+    assert maxabs(h, rh) <= TOL["f32"]
+
+
+def test_step_codestral_workload():
+    """Full decode workload (b=64, H=128, P=64, N=128, G=8, 128 steps, float32);
+    the oracle follows a sample of batch rows (all heads, every step)."""
+    w = inputs.WORKLOADS[3]
+    log("step workload 3 (codestral decode), 128 steps")
+    d = inputs.workload_inputs(3)
+    y, h = _run_steps(d, "f32", w.steps)
+    bsel = [0, 17, 63]
+    ry, rh = _oracle_steps(d, w.steps, bsel)
+    ey, eh = maxabs(y[:, bsel], ry), maxabs(h[bsel], rh)
+    log(f"  max|dy|={ey:.3g} max|dh|={eh:.3g}")
+    assert ey <= TOL["f32"] and eh <= TOL["f32"]
+
+
+def test_step_batched_equals_solo():
+    import torch
+    from state_space_model_amd import ssd
+    d = _small(6, 4, 64, 128, 2, 1, 7, "f32")
+    dev = "cuda"
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    h = t(d["h"])
+    y = ssd.step(t(d["x"][0]), t(d["dt"][0]), t(d["A"]), t(d["B"][0]), t(d["C"][0]), t(d["D"]), h)
+    for i in range(6):
+        hi = t(d["h"][i:i + 1])
+        yi = ssd.step(t(d["x"][0][i:i + 1]), t(d["dt"][0][i:i + 1]), t(d["A"]),
+                      t(d["B"][0][i:i + 1]), t(d["C"][0][i:i + 1]), t(d["D"]), hi)
+        assert torch.equal(yi[0], y[i]) and torch.equal(hi[0], h[i])
