@@ -1,0 +1,402 @@
+#!/usr/bin/env python3
+"""Benchmark of the SSD hot path on one MI355X.
+
+One step = one pass of the whole path over one batch: the chunked prefill of
+a Mamba-2 130M-shaped layer (batch 1, 4096 tokens, 24 heads, headdim 64,
+d_state 128, 1 group, chunk 256, bf16 operands) through the four prefill
+kernels, then one decode token from the prefill's final state through the
+decode kernel.  `value` is prefill tokens/s over whole steps.
+
+The decode half of the metric (state-update GB/s against HBM peak) is
+measured in the same run on the Codestral-7B decode workload (batch 64,
+128 heads, headdim 64, d_state 128, 8 groups, 128 sequential steps, float32
+state of 268 MB) and reported under "decode".
+
+Per-kernel durations come from HIP events recorded on the stream the
+kernels run on, around back-to-back launches of each kernel alone.  The
+roofline object uses algorithmic bytes / flops per launch (not measured
+traffic); "traffic" is HBM bytes per launch from rocprofv3 counters taken
+offline for the same command (null when not available).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3     # MI355X fp32 vector
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--decode-steps", type=int, default=128)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, metavar="MIB", default=0,
+                    help="only run a plain device-to-device copy of MIB MiB ten times "
+                         "(reference kernel for scaling rocprofv3 byte counters)")
+    ap.add_argument("--summarize", metavar="DIR",
+                    help="turn rocprofv3 output under DIR into profiles/ summaries and exit")
+    return ap.parse_args()
+
+
+def log(args, msg):
+    if not args.quiet:
+        print(msg, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------ algorithmic work
+def prefill_work(w, T, nseq, h0):
+    """Algorithmic bytes and flops of the prefill, per kernel (SSD chunked form)."""
+    H, P, N, G, Q = w.H, w.P, w.N, w.G, w.chunk
+    e = 2 if w.dtype == "bf16" else 4
+    state = nseq * H * N * P * 4
+    k1 = dict(bytes=T * H * 4 + H * 4, flops=T * H)
+    # chunk state: x, B, dt read; S = sum_j w_j B_j x_j^T, 2 flop per (token, n, p)
+    k2 = dict(bytes=T * H * P * e + T * G * N * e + T * H * 4, flops=2 * T * H * N * P)
+    # state passing reads h0 and writes h_out (chunk states are implementation overhead)
+    k3 = dict(bytes=(state if h0 else 0) + state, flops=2 * (T // Q + nseq) * H * N * P)
+    # chunk scan: x, B, C, dt read, y written; C.B^T once per group and chunk (full tile),
+    # M.X per head (full tile), C.H_in per head
+    k4 = dict(bytes=T * H * P * (e + 4) + 2 * T * G * N * e + T * H * 4,
+              flops=T * (2 * Q * N * G + H * (2 * Q * P + 2 * N * P)))
+    return {"chunk_cumsum": k1, "chunk_state": k2, "state_pass": k3, "chunk_scan": k4}
+
+
+def step_work(b, H, P, N, G, e_in):
+    """Algorithmic bytes/flops of one decode step: state read+write once."""
+    return dict(bytes=2 * b * H * N * P * 4 + b * H * P * (e_in + 4) + 2 * b * G * N * e_in
+                + b * H * 4, flops=5 * b * H * N * P)
+
+
+# ------------------------------------------------------------------- timing
+def time_loop(torch, fn, iters):
+    """Average ms per call of fn(), with HIP events on the current stream."""
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(iters):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / iters
+
+
+def load_traffic():
+    """Measured HBM bytes per launch, or {} when absent or taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return {}
+    if t.get("source_hash") != source_hash():
+        return {}
+    return {wl: {k: v.get("bytes") for k, v in ks.items()} for wl, ks in t.items()
+            if isinstance(ks, dict)}
+
+
+def roofline(name, work, ms, traffic):
+    flops_rate = work["flops"] / (ms * 1e-3) / 1e12
+    bytes_rate = work["bytes"] / (ms * 1e-3) / 1e9
+    # the bound is the resource whose peak time is larger for this kernel
+    t_hbm = work["bytes"] / (HBM_PEAK_GBS * 1e9)
+    t_mfma = work["flops"] / (BF16_PEAK_TFLOPS * 1e12)
+    tr = traffic.get(name)
+    if t_mfma > t_hbm:
+        return {"kernel": name, "bound": "mfma", "achieved": round(flops_rate, 2),
+                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(flops_rate / BF16_PEAK_TFLOPS, 4), "traffic": tr,
+                "avg_us": round(ms * 1e3, 2)}
+    return {"kernel": name, "bound": "hbm", "achieved": round(bytes_rate, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(bytes_rate / HBM_PEAK_GBS, 4),
+            "traffic": tr, "avg_us": round(ms * 1e3, 2)}
+
+
+def cpu_baseline(args, d, w, budget_s=10.0):
+    """The fp64 oracle on the whole prefill workload, repeated for about budget_s."""
+    import oracle
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    x = d["x"]
+    runs = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.prefill(x, d["dt"], d["A"], d["B"], d["C"], d["D"], None, d["cu_seqlens"],
+                       threads=threads)
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    T = x.shape[0]
+    return {"value": round(runs * T / el, 1), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"whole prefill workload ({T} tokens x {w.H} heads) run {runs} times, "
+                      f"fp64 sequential recurrence, {el:.1f} s"}
+
+
+def copy_calibration(mib):
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "copies": 10}))
+
+
+def source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "state_space_model_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def _read_csv(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+KERNEL_NAMES = {  # kernel symbol fragment -> bench kernel name
+    "k_chunk_cumsum": "chunk_cumsum", "k_chunk_state": "chunk_state",
+    "k_state_pass": "state_pass", "k_chunk_scan": "chunk_scan", "k_step": "decode_step",
+}
+
+
+def _kernel_key(name, grid):
+    for frag, k in KERNEL_NAMES.items():
+        if frag in name:
+            if k == "decode_step":  # the two decode workloads differ in grid size
+                return ("codestral-7b-decode-step" if int(grid) > 24 * 256 else
+                        "mamba2-130m-layer-prefill"), k
+            return "mamba2-130m-layer-prefill", k
+    return None, None
+
+
+PROFILE_COMMANDS = {
+    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d DIR/trace -o run -- "
+             "python bench.py --no-cpu-baseline --steps 50 --warmup 5 --quiet",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/fetch -o run -- "
+             "python bench.py --no-cpu-baseline --steps 50 --warmup 5 --quiet",
+    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/write -o run -- "
+             "python bench.py --no-cpu-baseline --steps 50 --warmup 5 --quiet",
+    "cfetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/cfetch -o run -- "
+              "python bench.py --copy-calibration 1024",
+    "cwrite": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/cwrite -o run -- "
+              "python bench.py --copy-calibration 1024",
+}
+
+
+def summarize(directory):
+    """rocprofv3 CSVs -> profiles/*.txt and profiles/traffic.json.
+
+    Expects under DIR: trace/*kernel_stats.csv (kernel trace), fetch/ and write/
+    (bench --pmc FETCH_SIZE / WRITE_SIZE), cfetch/ and cwrite/ (the same
+    counters over --copy-calibration 1024).
+    """
+    import glob
+    out = {}
+
+    def pmc(sub, counter):
+        acc = {}
+        for p in glob.glob(os.path.join(directory, sub, "**", "*counter_collection.csv"),
+                           recursive=True):
+            for r in _read_csv(p):
+                if r["Counter_Name"] != counter:
+                    continue
+                acc.setdefault((r["Kernel_Name"], r["Grid_Size"]), []).append(
+                    float(r["Counter_Value"]))
+        return acc
+
+    def copy_factor(sub, counter, nbytes):
+        vals = [v for (k, g), vs in pmc(sub, counter).items() for v in vs
+                if "copy" in k.lower() or "elementwise" in k.lower()]
+        big = [v for v in vals if v * 1024 > nbytes / 4]
+        if not big:
+            return None
+        return nbytes / (float(np.median(big)) * 1024)   # true bytes per counted byte
+
+    cal = 1024 << 20
+    f_fac = copy_factor("cfetch", "FETCH_SIZE", cal)
+    w_fac = copy_factor("cwrite", "WRITE_SIZE", cal)
+    traffic = {"source_hash": source_hash(), "fetch_factor": f_fac, "write_factor": w_fac}
+    lines = []
+    for sub, counter, fac in (("fetch", "FETCH_SIZE", f_fac), ("write", "WRITE_SIZE", w_fac)):
+        for (kname, grid), vs in sorted(pmc(sub, counter).items()):
+            wl, k = _kernel_key(kname, grid)
+            if k is None or fac is None:
+                continue
+            b = float(np.mean(vs)) * 1024 * fac
+            traffic.setdefault(wl, {}).setdefault(k, {})[counter.lower()] = round(b)
+            lines.append(f"{wl:28s} {k:14s} {counter:10s} {np.mean(vs):14.1f} KiB/dispatch "
+                         f"x {fac:.4f} = {b / 1e6:10.3f} MB ({len(vs)} dispatches)")
+    for wl, ks in traffic.items():
+        if isinstance(ks, dict):
+            for k, v in ks.items():
+                if "fetch_size" in v and "write_size" in v:
+                    v["bytes"] = v["fetch_size"] + v["write_size"]
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(traffic, f, indent=1)
+    cmds = "\n".join(f"  {k:7s} {v}" for k, v in PROFILE_COMMANDS.items())
+    with open(os.path.join(ROOT, "profiles", "hbm_traffic_counters.txt"), "w") as f:
+        f.write("HBM traffic per dispatch from rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled by\n"
+                "the same counter over a plain 1 GiB device copy (true bytes / counted bytes):\n"
+                f"  fetch factor {f_fac}, write factor {w_fac}\n"
+                f"kernel sources hash {traffic['source_hash']}\n"
+                f"commands (cwd = repository root, DIR = output directory):\n{cmds}\n\n"
+                + "\n".join(lines) + "\n")
+    stats = glob.glob(os.path.join(directory, "trace", "**", "*kernel_stats.csv"), recursive=True)
+    if stats:
+        rows = _read_csv(stats[0])
+        tl = []
+        for r in rows:
+            tl.append(f"{r['Name'][:96]:96s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f}"
+                      f" {float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f}"
+                      f" {float(r['Percentage']):6.2f}")
+        with open(os.path.join(ROOT, "profiles", "kernel_trace_prefill130m_decode_codestral.txt"),
+                  "w") as f:
+            f.write("rocprofv3 kernel trace of the benchmark: prefill of the Mamba-2 130M layer\n"
+                    "workload (4096 tokens, 24 heads, P 64, N 128, chunk 256, bf16) + next-token\n"
+                    "decode, and the Codestral-7B decode workload (b 64, H 128, G 8, fp32 state).\n"
+                    f"kernel sources hash {traffic['source_hash']}\n"
+                    f"command (cwd = repository root):\n  {PROFILE_COMMANDS['trace']}\n\n"
+                    f"{'kernel':96s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}"
+                    f" {'%':>6s}\n" + "\n".join(tl) + "\n")
+    print(json.dumps(traffic, indent=1))
+
+
+def main():
+    args = parse()
+    if args.summarize:
+        summarize(args.summarize)
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+    import torch
+    from state_space_model_amd import inputs, ssd
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    wl = inputs.WORKLOADS[1]
+    d = inputs.workload_inputs(1)
+    T = d["x"].shape[0]
+    nseq = len(d["cu_seqlens"]) - 1
+    op = torch.bfloat16
+    t = lambda a, dt=None: torch.from_numpy(np.ascontiguousarray(a)).to(dev) if dt is None \
+        else torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(dt)
+    x, B, C = t(d["x"], op), t(d["B"], op), t(d["C"], op)
+    dtt, A, D = t(d["dt"]), t(d["A"]), t(d["D"])
+    y = torch.empty((T, wl.H, wl.P), dtype=torch.float32, device=dev)
+    h_out = torch.empty((nseq, wl.H, wl.N, wl.P), dtype=torch.float32, device=dev)
+    ws = ssd.alloc_workspace(T, nseq, wl.H, wl.P, wl.N, wl.chunk, op, dev)
+    # next-token decode inputs (same layer, batch 1)
+    rng = np.random.Generator(np.random.PCG64(2001))
+    xd = t(inputs.round_bf16(rng.standard_normal((nseq, wl.H, wl.P)).astype(np.float32)), op)
+    dtd = t(d["dt"][-1:].copy())
+    Bd, Cd = t(d["B"][-1:], op), t(d["C"][-1:], op)
+    yd = torch.empty((nseq, wl.H, wl.P), dtype=torch.float32, device=dev)
+
+    def prefill(stages=ssd.STAGE_ALL):
+        ssd.prefill(x, dtt, A, B, C, D, None, chunk=wl.chunk, nseq=nseq, y=y, h_out=h_out,
+                    workspace=ws, stages=stages)
+
+    def step():
+        prefill()
+        ssd.step(xd, dtd, A, Bd, Cd, D, h_out, y=yd)
+
+    log(args, f"workload: {wl.name} T={T} H={wl.H} P={wl.P} N={wl.N} Q={wl.chunk}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # ---- the timed region: exactly `steps` whole steps
+    ms_step = time_loop(torch, step, args.steps)
+    value = T / (ms_step * 1e-3)
+
+    # ---- per-kernel durations (each kernel alone, back to back)
+    iters = max(20, args.steps)
+    names = [("chunk_cumsum", ssd.STAGE_CHUNK_CUMSUM), ("chunk_state", ssd.STAGE_CHUNK_STATE),
+             ("state_pass", ssd.STAGE_STATE_PASS), ("chunk_scan", ssd.STAGE_CHUNK_SCAN)]
+    kern_ms = {}
+    for name, st in names:
+        for _ in range(3):
+            prefill(st)
+        kern_ms[name] = time_loop(torch, lambda st=st: prefill(st), iters)
+    kern_ms["decode_step"] = time_loop(torch, lambda: ssd.step(xd, dtd, A, Bd, Cd, D, h_out,
+                                                               y=yd), iters)
+    work = prefill_work(wl, T, nseq, h0=False)
+    work["decode_step"] = step_work(nseq, wl.H, wl.P, wl.N, wl.G, 2)
+    traffic = load_traffic().get(wl.name, {})
+    kernels = [roofline(n, work[n], kern_ms[n], traffic) for n in work]
+    dominant = max(kernels, key=lambda k: k["avg_us"])
+
+    # ---- decode workload (the decode half of the metric)
+    w3 = inputs.WORKLOADS[3]
+    d3 = inputs.workload_inputs(3)
+    S3 = args.decode_steps
+    x3, dt3 = t(d3["x"][:S3]), t(d3["dt"][:S3])
+    B3, C3 = t(d3["B"][:S3]), t(d3["C"][:S3])
+    A3, D3, h3 = t(d3["A"]), t(d3["D"]), t(d3["h"])
+    y3 = torch.empty((w3.batch, w3.H, w3.P), dtype=torch.float32, device=dev)
+
+    def decode_all():
+        for s in range(S3):
+            ssd.step(x3[s], dt3[s], A3, B3[s], C3[s], D3, h3, y=y3)
+
+    decode_all()
+    ms_dec = time_loop(torch, decode_all, 3) / S3
+    wd = step_work(w3.batch, w3.H, w3.P, w3.N, w3.G, 4)
+    dec_rl = roofline("decode_step", wd, ms_dec, load_traffic().get(w3.name, {}))
+    decode = {"workload": w3.name, "steps": S3, "us_per_step": round(ms_dec * 1e3, 2),
+              "state_bytes": w3.batch * w3.H * w3.N * w3.P * 4,
+              "gb_per_s": dec_rl["achieved"], "frac_hbm_peak": dec_rl["frac"],
+              "tokens_per_s": round(w3.batch / (ms_dec * 1e-3), 1), "roofline": dec_rl}
+
+    # MFMA utilisation estimate of the prefill (algorithmic flops / bf16 peak)
+    fl = sum(work[n]["flops"] for n in ("chunk_state", "chunk_scan"))
+    mfma_util = fl / (sum(kern_ms[n] for n in kern_ms if n != "decode_step") * 1e-3) / \
+        (BF16_PEAK_TFLOPS * 1e12)
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args, d, wl)
+    out = {
+        "metric": "SSD prefill tokens/s + MFMA util; decode state-update GB/s vs HBM peak",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "batch": nseq, "seq_len": T // nseq, "heads": wl.H,
+                   "headdim": wl.P, "d_state": wl.N, "groups": wl.G, "chunk": wl.chunk,
+                   "step": "prefill + next-token decode"},
+        "roofline": {k: dominant[k] for k in ("bound", "achieved", "peak", "unit", "frac",
+                                              "traffic")} | {"kernel": dominant["kernel"]},
+        "prefill_mfma_util": round(mfma_util, 4),
+        "kernels": kernels,
+        "decode": decode,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
