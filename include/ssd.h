@@ -12,8 +12,8 @@
  * Sources: COREY: Entropy-Guided Runtime Chunk Scheduling for Selective Scan
  * Kernels, section 3.1 (the generic selective SSM update); Compiler-First State
  * Space Duality and Portable O(1) Autoregressive Caching for Inference,
- * Abstract (diagonal per-head dynamics, fixed-size chunking, einsum-dominated
- * compute, O(1) decode cache) and Tables 7-8 (static causal mask inside a
+ * Abstract (one scalar decay per head, equal-length chunks whose work is dense
+ * contractions, a decode cache of constant size) and Tables 7-8 (static causal mask inside a
  * chunk; decay kept in float32); Recurrence Scan (poot docs), "One equation,
  * one packed result" and "The schedule" (the scan returns the output and the
  * carried state; a long sequence may be split across launches that hand the

@@ -11,7 +11,7 @@ token, in float64).  This module only marshals arrays through ctypes:
 * ``step(x, dt, A, B, C, D, h)`` -> ``y`` (``h`` updated in place)
 
 Passages followed: COREY, section 3.1 (generic selective SSM update);
-Compiler-First State Space Duality ..., Abstract (diagonal per-head dynamics);
+Compiler-First State Space Duality ..., Abstract (one scalar decay per head);
 Mamba-2 SSD fused layer via VGpuWarp, "Lane mapping" (per-channel sweep over
 d_state, one exp per step); Recurrence Scan, "One equation, one packed result"
 (output and carried state both returned and both compared).

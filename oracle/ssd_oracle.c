@@ -16,8 +16,8 @@
  *    section 3.1 (Preliminaries): the generic selective SSM update
  *    h_t = A_t h_{t-1} + B_t x_t, y_t = C_t h_t + D_t x_t.
  *  - Compiler-First State Space Duality and Portable O(1) Autoregressive Caching
- *    for Inference, Abstract: SSD has diagonal per-head dynamics, i.e. the state
- *    transition of head h is the scalar exp(dt*A_h) times the identity.
+ *    for Inference, Abstract: in SSD the state transition of head h is a
+ *    scalar, exp(dt*A_h), times the identity.
  *  - Mamba-2 SSD fused layer via VGpuWarp -- design sketch, "Lane mapping" and
  *    "S2 RESULT": each (head, head_dim) channel sweeps d_state with one exp per
  *    step; the state h is an N x P matrix per head.

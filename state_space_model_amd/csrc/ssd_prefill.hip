@@ -7,13 +7,14 @@
 //   y_i    = sum_{j<=i} (C_i . B_j) exp(s_i - s_j) dt_j x_j   (intra-chunk, causal)
 //          + exp(s_i) C_i . H_{c-1}                         (state entering the chunk)
 //          + D_h x_i
-// This is the unrolled recurrence regrouped into fixed-size chunks: the
-// structured-state-space-duality form of Compiler-First State Space Duality
-// and Portable O(1) Autoregressive Caching for Inference (Abstract: diagonal
-// per-head dynamics, fixed-size chunking, einsum-dominated compute), with the
-// static lower-triangular mask of its Table 7 and the float32 decay of its
-// Table 8; chunk-by-chunk state hand-off as in Recurrence Scan ("One equation,
-// one packed result").
+// This is the unrolled recurrence regrouped into chunks of one fixed length:
+// the structured-state-space-duality form of Compiler-First State Space
+// Duality and Portable O(1) Autoregressive Caching for Inference (Abstract:
+// each head decays by one scalar per step, the sequence is cut into equal
+// chunks and the work inside a chunk is dense contractions), with the static
+// lower-triangular mask of its Table 7 and the float32 decay of its Table 8;
+// the state is handed from chunk to chunk as in Recurrence Scan ("One
+// equation, one packed result").
 //
 // Kernels (one launch each, all on the caller's stream):
 //   K1 k_chunk_cumsum : grid (nc_max)       chunk map + s, dt per (chunk, head)

@@ -8,7 +8,7 @@ which shows that a plausible mistake anywhere in the oracle is caught.
 What each pin rests on:
   unrolled   closed-form unrolling of the linear recurrence, O(L^2) products
   chunked    block (SSD) evaluation at many chunk sizes (Compiler-First State
-             Space Duality ..., Abstract: fixed-size chunking; Recurrence Scan:
+             Space Duality ..., Abstract: equal-length chunks; Recurrence Scan:
              the SSD run chunk by chunk, each continuing from the last state)
   A0         A = 0 gives a cumulative sum of dt*x (x) B
   dt0        dt = 0 freezes the state: y = C.h0 + D*x, h_out = h0

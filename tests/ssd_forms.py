@@ -9,8 +9,8 @@ library.  Each is a different route to the same mathematics:
 * ``chunked``: the block (state space duality) evaluation with chunk size Q:
   a quadratic, causally masked form inside each chunk plus a chunk-to-chunk
   state carry.  This is the decomposition the GPU kernels implement
-  (Compiler-First State Space Duality ..., Abstract: fixed-size chunking,
-  einsum-dominated compute; Table 7: static lower-triangular mask; Recurrence
+  (Compiler-First State Space Duality ..., Abstract: equal-length chunks whose
+  work is dense contractions; Table 7: static lower-triangular mask; Recurrence
   Scan, "One equation, one packed result": the SSD run chunk by chunk, each
   chunk continuing from the previous chunk's state).
 * ``prefix_sum_A0``: the A = 0 closed form (a cumulative sum).
