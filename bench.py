@@ -12,8 +12,10 @@ measured in the same run on the Codestral-7B decode workload (batch 64,
 128 heads, headdim 64, d_state 128, 8 groups, 128 sequential steps, float32
 state of 268 MB) and reported under "decode".
 
-Per-kernel durations come from HIP events recorded on the stream the
-kernels run on, around back-to-back launches of each kernel alone.  The
+The timed steps are launched eagerly (pre-marshalled calls through the C ABI);
+the same step replayed from a HIP graph is reported as ms_per_step_graph.
+Per-kernel durations come from HIP events around replays of a HIP graph of
+20 launches of that kernel alone, on the replay stream.  The
 roofline object uses algorithmic bytes / flops per launch (not measured
 traffic); "traffic" is HBM bytes per launch from rocprofv3 counters taken
 offline for the same command (null when not available).
@@ -94,6 +96,22 @@ def time_loop(torch, fn, iters):
     e.record()
     torch.cuda.synchronize()
     return s.elapsed_time(e) / iters
+
+
+def graph_ms(torch, fn, reps, per_graph):
+    """Average ms per fn() call, from `reps` replays of a HIP graph holding
+    `per_graph` calls (events on the replay stream)."""
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(per_graph):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    ms = time_loop(torch, g.replay, reps) / per_graph
+    del g
+    return ms
 
 
 def load_traffic():
@@ -319,33 +337,31 @@ def main():
     Bd, Cd = t(d["B"][-1:], op), t(d["C"][-1:], op)
     yd = torch.empty((nseq, wl.H, wl.P), dtype=torch.float32, device=dev)
 
-    def prefill(stages=ssd.STAGE_ALL):
-        ssd.prefill(x, dtt, A, B, C, D, None, chunk=wl.chunk, nseq=nseq, y=y, h_out=h_out,
-                    workspace=ws, stages=stages)
+    run_prefill, _, _ = ssd.prefill(x, dtt, A, B, C, D, None, chunk=wl.chunk, nseq=nseq, y=y,
+                                    h_out=h_out, workspace=ws, prepare=True)
+    run_decode, _ = ssd.step(xd, dtd, A, Bd, Cd, D, h_out, y=yd, prepare=True)
 
     def step():
-        prefill()
-        ssd.step(xd, dtd, A, Bd, Cd, D, h_out, y=yd)
+        run_prefill()
+        run_decode()
 
     log(args, f"workload: {wl.name} T={T} H={wl.H} P={wl.P} N={wl.N} Q={wl.chunk}")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # ---- the timed region: exactly `steps` whole steps
+    # ---- the timed region: exactly `steps` whole steps, launched eagerly
     ms_step = time_loop(torch, step, args.steps)
     value = T / (ms_step * 1e-3)
+    # the same step replayed from a HIP graph (no host launch cost)
+    ms_step_graph = graph_ms(torch, step, reps=max(10, args.steps // 10), per_graph=10)
 
-    # ---- per-kernel durations (each kernel alone, back to back)
-    iters = max(20, args.steps)
+    # ---- per-kernel durations: each kernel alone, 20 launches per HIP graph
     names = [("chunk_cumsum", ssd.STAGE_CHUNK_CUMSUM), ("chunk_state", ssd.STAGE_CHUNK_STATE),
              ("state_pass", ssd.STAGE_STATE_PASS), ("chunk_scan", ssd.STAGE_CHUNK_SCAN)]
     kern_ms = {}
     for name, st in names:
-        for _ in range(3):
-            prefill(st)
-        kern_ms[name] = time_loop(torch, lambda st=st: prefill(st), iters)
-    kern_ms["decode_step"] = time_loop(torch, lambda: ssd.step(xd, dtd, A, Bd, Cd, D, h_out,
-                                                               y=yd), iters)
+        kern_ms[name] = graph_ms(torch, lambda st=st: run_prefill(st), reps=10, per_graph=20)
+    kern_ms["decode_step"] = graph_ms(torch, run_decode, reps=10, per_graph=20)
     work = prefill_work(wl, T, nseq, h0=False)
     work["decode_step"] = step_work(nseq, wl.H, wl.P, wl.N, wl.G, 2)
     traffic = load_traffic().get(wl.name, {})
@@ -361,15 +377,20 @@ def main():
     A3, D3, h3 = t(d3["A"]), t(d3["D"]), t(d3["h"])
     y3 = torch.empty((w3.batch, w3.H, w3.P), dtype=torch.float32, device=dev)
 
+    dec_calls = [ssd.step(x3[s], dt3[s], A3, B3[s], C3[s], D3, h3, y=y3, prepare=True)[0]
+                 for s in range(S3)]
+
     def decode_all():
-        for s in range(S3):
-            ssd.step(x3[s], dt3[s], A3, B3[s], C3[s], D3, h3, y=y3)
+        for call in dec_calls:
+            call()
 
     decode_all()
     ms_dec = time_loop(torch, decode_all, 3) / S3
+    ms_dec_graph = graph_ms(torch, decode_all, reps=3, per_graph=1) / S3
     wd = step_work(w3.batch, w3.H, w3.P, w3.N, w3.G, 4)
     dec_rl = roofline("decode_step", wd, ms_dec, load_traffic().get(w3.name, {}))
     decode = {"workload": w3.name, "steps": S3, "us_per_step": round(ms_dec * 1e3, 2),
+              "us_per_step_graph": round(ms_dec_graph * 1e3, 2),
               "state_bytes": w3.batch * w3.H * w3.N * w3.P * 4,
               "gb_per_s": dec_rl["achieved"], "frac_hbm_peak": dec_rl["frac"],
               "tokens_per_s": round(w3.batch / (ms_dec * 1e-3), 1), "roofline": dec_rl}
@@ -390,6 +411,7 @@ def main():
                    "step": "prefill + next-token decode"},
         "roofline": {k: dominant[k] for k in ("bound", "achieved", "peak", "unit", "frac",
                                               "traffic")} | {"kernel": dominant["kernel"]},
+        "ms_per_step_graph": round(ms_step_graph, 5),
         "prefill_mfma_util": round(mfma_util, 4),
         "kernels": kernels,
         "decode": decode,

@@ -17,14 +17,18 @@
 // equation, one packed result").
 //
 // Kernels (one launch each, all on the caller's stream):
-//   K1 k_chunk_cumsum : grid (nc_max)       chunk map + s, dt per (chunk, head)
-//   K2 k_chunk_state  : grid (nc_max, H)    S_c^T = (w o X)^T B on MFMA, k = tokens
+//   K1 k_chunk_cumsum : grid (nc_max, H/4)  chunk map + s, dt per (chunk, head)
+//   K2 k_chunk_state  : grid (nc_max, H)    S_c^T = (w o X)^T B on MFMA, k = tokens (16 waves)
 //   K3 k_state_pass   : grid (NP/1024,H,nseq) sequential H_c over the chunks of a sequence
-//   K4 k_chunk_scan   : grid (nc_max, H)    C.B^T (k = N), mask/decay, Y^T = X^T M^T
+//   K4 k_chunk_scan   : grid (nc_max, H)    one wave per 16-token tile: C.B^T (k = N), mask/decay, Y^T = X^T M^T
 //                                           (k = tokens) and exp(s) H^T C^T (k = N) on MFMA
 // Every padded row of a partial chunk has dt = 0, x = 0, B = 0: it changes
 // nothing (decay 1, no input), so the chunk-end value s_{Q-1} equals
-// s_{len-1}.
+// s_{len-1}.  The workspace holds s in base-2 units (s * log2(e)) so every
+// decay is one v_exp_f32 (2^x) of a non-positive argument.
+#include <mutex>
+#include <set>
+
 #include "ssd_device.h"
 #include "ssd_launch.h"
 
@@ -61,17 +65,12 @@ __device__ int block_incl_scan(int v, int *sh, int &total) {
   return v + prefix;
 }
 
-__global__ __launch_bounds__(256) void k_chunk_cumsum(const float *__restrict__ dt,
-                                                      const float *__restrict__ A,
-                                                      const int32_t *__restrict__ cu, int nseq,
-                                                      int L_dense, int64_t T, int H, int Q,
-                                                      int nc_max, int4 *__restrict__ info_out,
-                                                      int *__restrict__ seq_off,
-                                                      float *__restrict__ s_out,
-                                                      float *__restrict__ dt_out) {
+// Resolve chunk c of the packed batch into {seq, t0, len, index} (block-wide;
+// O(nseq / blockDim) block scans).  Block (0, 0) also writes seq_off.
+__device__ int4 locate_chunk(const int32_t *__restrict__ cu, int nseq, int L_dense, int64_t T,
+                             int Q, int c, int *__restrict__ seq_off, bool write_off) {
   __shared__ int sh_scan[16];
   __shared__ int4 sh_info;
-  const int c = blockIdx.x;
   const int tid = threadIdx.x;
   if (tid == 0) sh_info = make_int4(-1, 0, 0, 0);
   __syncthreads();
@@ -81,7 +80,7 @@ __global__ __launch_bounds__(256) void k_chunk_cumsum(const float *__restrict__ 
       const int seq = c / cps, k = c % cps;
       if (seq < nseq) sh_info = make_int4(seq, seq * L_dense + k * Q, min(Q, L_dense - k * Q), k);
     }
-    if (blockIdx.x == 0)
+    if (write_off)
       for (int s = tid; s <= nseq; s += blockDim.x) seq_off[s] = s * cps;
   } else {
     int running = 0;
@@ -101,40 +100,64 @@ __global__ __launch_bounds__(256) void k_chunk_cumsum(const float *__restrict__ 
         const int k = c - running - excl;
         sh_info = make_int4(s, start + k * Q, min(Q, len - k * Q), k);
       }
-      if (blockIdx.x == 0 && s < nseq) seq_off[s] = running + excl;
+      if (write_off && s < nseq) seq_off[s] = running + excl;
       running += total;
     }
-    if (blockIdx.x == 0 && tid == 0) seq_off[nseq] = running;
+    if (write_off && tid == 0) seq_off[nseq] = running;
   }
   __syncthreads();
-  const int4 ci = sh_info;
-  if (c >= nc_max) return;
-  if (tid == 0) info_out[c] = ci.x < 0 ? make_int4(0, 0, 0, 0) : ci;
-  if (ci.x < 0 || ci.z <= 0) return;
+  return sh_info;
+}
 
-  // chunk-local inclusive cumsum of dt*A per head; padded rows get dt = 0
-  const int wave = tid >> 6, lane = tid & 63, nw = blockDim.x >> 6;
-  for (int h = wave; h < H; h += nw) {
-    const float a = A[h];
-    float carry = 0.f;
-    float *so = s_out + ((size_t)c * H + h) * Q;
-    float *dto = dt_out + ((size_t)c * H + h) * Q;
-    for (int i0 = 0; i0 < Q; i0 += 64) {
-      const int i = i0 + lane;
-      const float d = (i < ci.z) ? dt[((size_t)ci.y + i) * H + h] : 0.f;
-      float v = d * a;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// K1: grid (chunks, ceil(H/4)), 256 threads; wave w of block y handles head
+// 4y + w.  All of a head's dt loads are issued before the scan.
+__global__ __launch_bounds__(256) void k_chunk_cumsum(const float *__restrict__ dt,
+                                                      const float *__restrict__ A,
+                                                      const int32_t *__restrict__ cu, int nseq,
+                                                      int L_dense, int64_t T, int H, int Q,
+                                                      int nc_max, int4 *__restrict__ info_out,
+                                                      int *__restrict__ seq_off,
+                                                      float *__restrict__ s_out,
+                                                      float *__restrict__ dt_out) {
+  const int c = blockIdx.x;
+  const int4 ci = locate_chunk(cu, nseq, L_dense, T, Q, c, seq_off,
+                               blockIdx.x == 0 && blockIdx.y == 0);
+  if (c >= nc_max) return;
+  if (threadIdx.x == 0 && blockIdx.y == 0) info_out[c] = ci.x < 0 ? make_int4(0, 0, 0, 0) : ci;
+  if (ci.x < 0 || ci.z <= 0) return;
+  const int lane = threadIdx.x & 63;
+  const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
+  if (h >= H) return;
+  const float a2 = A[h] * kLog2e;
+  constexpr int MAXSEG = 8;  // Q <= 512
+  const int nseg = (Q + 63) / 64;
+  float d[MAXSEG];
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        float t = __shfl_up(v, off, 64);
-        if (lane >= off) v += t;
-      }
-      v += carry;
-      if (i < Q) {
-        so[i] = v;
-        dto[i] = d;
-      }
-      carry = __shfl(v, 63, 64);
+  for (int sg = 0; sg < MAXSEG; ++sg) {
+    const int i = sg * 64 + lane;
+    d[sg] = (sg < nseg && i < ci.z) ? dt[((size_t)ci.y + i) * H + h] : 0.f;
+  }
+  float *so = s_out + ((size_t)c * H + h) * Q;
+  float *dto = dt_out + ((size_t)c * H + h) * Q;
+  float carry = 0.f;
+#pragma unroll
+  for (int sg = 0; sg < MAXSEG; ++sg) {
+    if (sg >= nseg) break;
+    const int i = sg * 64 + lane;
+    float v = d[sg] * a2;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float t = __shfl_up(v, off, 64);
+      if (lane >= off) v += t;
     }
+    v += carry;
+    if (i < Q) {
+      so[i] = v;
+      dto[i] = d[sg];
+    }
+    carry = __shfl(v, 63, 64);
   }
 }
 
@@ -165,18 +188,25 @@ __device__ __forceinline__ void stage_rows(T *tile, int pitch, const T *__restri
 constexpr int kJP = 128;  // token rows staged in LDS per phase (K2, K4)
 
 // ------------------------------------------------------------ K2 chunk state
-// S_c^T[p][n] = sum_j X'[j][p] B[j][n],  X'[j] = exp(s_end - s_j) dt_j x_j.
+// S_c^T[p][n] = sum_j X'[j][p] B[j][n],  X'[j] = 2^(s_end - s_j) dt_j x_j.
 // MFMA 16x16 tiles over (p, n); k = tokens, read from token-major LDS tiles
 // with the transpose read.  Output stored as S[c][h][n][p] (float32).
+// NW = min(16, tiles) waves; wave w owns tiles w, w+NW, ...
+template <int P, int N> struct StateTiles {
+  static constexpr int NT = (P / 16) * (N / 16);
+  static constexpr int NW = NT < 16 ? NT : 16;
+  static constexpr int TPW = NT / NW;
+};
+
 template <typename T, int P, int N>
-__global__ __launch_bounds__(256) void k_chunk_state(const T *__restrict__ x, const T *__restrict__ B,
-                                                     const float *__restrict__ s_ws,
-                                                     const float *__restrict__ dt_ws,
-                                                     const int4 *__restrict__ info, int H, int G,
-                                                     int Q, float *__restrict__ S_out) {
+__global__ __launch_bounds__(1024) void k_chunk_state(const T *__restrict__ x, const T *__restrict__ B,
+                                                      const float *__restrict__ s_ws,
+                                                      const float *__restrict__ dt_ws,
+                                                      const int4 *__restrict__ info, int H, int G,
+                                                      int Q, float *__restrict__ S_out) {
   constexpr int PAD = 16 / sizeof(T);
   constexpr int XP = P + PAD, BP = N + PAD;
-  constexpr int NPT = P / 16, NNT = N / 16, NT = NPT * NNT, TPW = (NT + 3) / 4;
+  constexpr int NNT = N / 16, NW = StateTiles<P, N>::NW, TPW = StateTiles<P, N>::TPW;
   const int c = blockIdx.x, hd = blockIdx.y;
   const int4 ci = info[c];
   if (ci.z <= 0) return;
@@ -190,7 +220,8 @@ __global__ __launch_bounds__(256) void k_chunk_state(const T *__restrict__ x, co
   const float *sc = s_ws + ((size_t)c * H + hd) * Q;
   const float *dtc = dt_ws + ((size_t)c * H + hd) * Q;
   const float s_end = sc[Q - 1];
-  for (int i = threadIdx.x; i < Q; i += blockDim.x) w[i] = expf(fminf(s_end - sc[i], 0.f)) * dtc[i];
+  for (int i = threadIdx.x; i < Q; i += blockDim.x)
+    w[i] = __builtin_amdgcn_exp2f(fminf(s_end - sc[i], 0.f)) * dtc[i];
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, grp = lane >> 4;
   f4 acc[TPW];
@@ -206,26 +237,22 @@ __global__ __launch_bounds__(256) void k_chunk_state(const T *__restrict__ x, co
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
-      const int tile = wave + 4 * t;
-      if (tile < NT) {
-        const int pt = tile / NNT, nt = tile % NNT;
-        for (int k0 = 0; k0 < JP; k0 += 32) {
-          Frag<T> a = frag_kmaj(Xs, XP, pt * 16, k0 + 8 * grp, k0 + 8 * grp + 4);
-          Frag<T> b = frag_kmaj(Bs, BP, nt * 16, k0 + 8 * grp, k0 + 8 * grp + 4);
-          mma(acc[t], a, b);
-        }
+      const int tile = wave + NW * t;
+      const int pt = tile / NNT, nt = tile % NNT;
+      for (int k0 = 0; k0 < JP; k0 += 32) {
+        Frag<T> a = frag_kmaj(Xs, XP, pt * 16, k0 + 8 * grp, k0 + 8 * grp + 4);
+        Frag<T> b = frag_kmaj(Bs, BP, nt * 16, k0 + 8 * grp, k0 + 8 * grp + 4);
+        mma(acc[t], a, b);
       }
     }
   }
   float *so = S_out + ((size_t)c * H + hd) * (size_t)(N * P);
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
-    const int tile = wave + 4 * t;
-    if (tile < NT) {
-      const int pt = tile / NNT, nt = tile % NNT;
-      const int n = nt * 16 + (lane & 15), p = pt * 16 + 4 * grp;
-      st4(so + (size_t)n * P + p, acc[t]);
-    }
+    const int tile = wave + NW * t;
+    const int pt = tile / NNT, nt = tile % NNT;
+    const int n = nt * 16 + (lane & 15), p = pt * 16 + 4 * grp;
+    st4(so + (size_t)n * P + p, acc[t]);
   }
 }
 
@@ -240,54 +267,56 @@ __global__ __launch_bounds__(256) void k_state_pass(const float *__restrict__ S,
                                                     const int *__restrict__ seq_off,
                                                     const float *h0, float *h_out,
                                                     T *__restrict__ hin, int H, int NP, int Q) {
+  constexpr int BATCH = 8;  // chunk states in flight per thread
   const int s = blockIdx.z, hd = blockIdx.y;
   const int e = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (e >= NP) return;
   const int c0 = seq_off[s], c1 = seq_off[s + 1];
   const size_t hofs = ((size_t)s * H + hd) * NP + e;
   f4 st = h0 ? ld4(h0 + hofs) : zero4();
-  if (c0 < c1) {
-    size_t base = ((size_t)c0 * H + hd) * NP + e;
-    f4 Sc = ld4(S + base);
-    float sl = s_ws[((size_t)c0 * H + hd) * Q + Q - 1];
-    for (int c = c0; c < c1; ++c) {
-      f4 Sn = Sc;
-      float sn = sl;
-      const size_t nbase = ((size_t)(c + 1) * H + hd) * NP + e;
-      if (c + 1 < c1) {  // prefetch the next chunk's state and decay
-        Sn = ld4(S + nbase);
-        sn = s_ws[((size_t)(c + 1) * H + hd) * Q + Q - 1];
-      }
-      st4T(hin + base, st);
-      const float a = expf(fminf(sl, 0.f));
+  for (int cb = c0; cb < c1; cb += BATCH) {
+    f4 Sb[BATCH];
+    float sl[BATCH];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) st[q] = a * st[q] + Sc[q];
-      Sc = Sn;
-      sl = sn;
-      base = nbase;
+    for (int u = 0; u < BATCH; ++u) {
+      if (cb + u < c1) {
+        const size_t ch = (size_t)(cb + u) * H + hd;
+        Sb[u] = ld4(S + ch * NP + e);
+        sl[u] = s_ws[ch * Q + Q - 1];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      if (cb + u < c1) {
+        st4T(hin + ((size_t)(cb + u) * H + hd) * NP + e, st);
+        const float a = __builtin_amdgcn_exp2f(fminf(sl[u], 0.f));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) st[q] = a * st[q] + Sb[u][q];
+      }
     }
   }
   if (h_out) st4(h_out + hofs, st);
 }
 
 // ------------------------------------------------------------ K4 chunk scan
-// Per (chunk, head).  Wave w owns up to four 16-token output tiles
-// {w, 2W-1-w, 2W+w, 4W-1-w} (W waves), which balances the causal work.
-//   Y^T[p][i]  = exp(s_i) (H_in^T C^T)[p][i]            k = n    (A: H_in tile via transpose read)
+// Per (chunk, head).  The chunk's Q/16 output tiles (16 tokens each) go to
+// NW = min(16, Q/16) waves; with TPW = 2 (Q = 512) wave w owns tiles
+// {w, 2NW-1-w}, which balances the causal work.
+//   Y^T[p][i]  = 2^(s_i) (H_in^T C^T)[p][i]             k = n    (A: H_in tile via transpose read)
 //             += sum_j X^T[p][j] M^T[j][i]              k = j    (A: X tile via transpose read)
-//   M^T[j][i]  = (B C^T)[j][i] exp(s_i - s_j) dt_j  (j <= i)     k = n
+//   M^T[j][i]  = (B C^T)[j][i] 2^(s_i - s_j) dt_j  (j <= i)      k = n
 // The two 16x16 results of B C^T for j-rows jb..jb+15 and jb+16..jb+31 are
 // fed straight back as the B operand (paired k map); X^T is read with the
 // same pairing.
-template <typename T, int P, int N>
-__global__ __launch_bounds__(512) void k_chunk_scan(const T *__restrict__ x, const T *__restrict__ B,
-                                                    const T *__restrict__ C,
-                                                    const float *__restrict__ D,
-                                                    const float *__restrict__ s_ws,
-                                                    const float *__restrict__ dt_ws,
-                                                    const T *__restrict__ hin,
-                                                    const int4 *__restrict__ info, int H, int G,
-                                                    int Q, float *__restrict__ y) {
+template <typename T, int P, int N, int TPW>
+__global__ __launch_bounds__(1024) void k_chunk_scan(const T *__restrict__ x, const T *__restrict__ B,
+                                                     const T *__restrict__ C,
+                                                     const float *__restrict__ D,
+                                                     const float *__restrict__ s_ws,
+                                                     const float *__restrict__ dt_ws,
+                                                     const T *__restrict__ hin,
+                                                     const int4 *__restrict__ info, int H, int G,
+                                                     int Q, float *__restrict__ y) {
   constexpr int PAD = 16 / sizeof(T);
   constexpr int NK = N < 32 ? 32 : N;  // contraction over n, padded to the k-step
   constexpr int KS = NK / 32;
@@ -318,29 +347,31 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const T *__restrict__ x, con
   stage_rows<T, P, P>(Hs, HP, hin + csh * (size_t)(N * P), (size_t)P, 0, NK, N, nullptr);
   __syncthreads();
 
-  const int NTI = Q / 16;
-  int tiles[4] = {wave, 2 * nw - 1 - wave, 2 * nw + wave, 4 * nw - 1 - wave};
+  int tiles[TPW];
+  tiles[0] = wave;
+  if (TPW == 2) tiles[TPW - 1] = 2 * nw - 1 - wave;
   const T *Cg = C + ((size_t)ci.y * G + g) * N;
-  Frag<T> cf[4][KS];
-  float si[4];
+  Frag<T> cf[TPW][KS];
+  float si[TPW];
+  bool live[TPW];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < TPW; ++k) {
     const int i = tiles[k] * 16 + col;
-    const bool valid = tiles[k] < NTI && i < len;
+    live[k] = tiles[k] * 16 < len;  // wave-uniform
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int n8 = ks * 32 + 8 * grp;
-      cf[k][ks] = (valid && n8 < N) ? frag_global(Cg + (size_t)i * G * N + n8) : frag_zero<T>();
+      cf[k][ks] = (i < len && n8 < N) ? frag_global(Cg + (size_t)i * G * N + n8) : frag_zero<T>();
     }
-    si[k] = tiles[k] < NTI ? s_l[i] : 0.f;
+    si[k] = s_l[i];
   }
 
-  f4 acc[4][NPT];
+  f4 acc[TPW][NPT];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < TPW; ++k) {
 #pragma unroll
     for (int pt = 0; pt < NPT; ++pt) acc[k][pt] = zero4();
-    if (tiles[k] < NTI) {
+    if (live[k]) {
 #pragma unroll
       for (int pt = 0; pt < NPT; ++pt) {
 #pragma unroll
@@ -349,7 +380,7 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const T *__restrict__ x, con
           mma(acc[k][pt], a, cf[k][ks]);
         }
       }
-      const float ei = expf(fminf(si[k], 0.f));
+      const float ei = __builtin_amdgcn_exp2f(fminf(si[k], 0.f));
 #pragma unroll
       for (int pt = 0; pt < NPT; ++pt)
 #pragma unroll
@@ -365,8 +396,8 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const T *__restrict__ x, con
     stage_rows<T, P, P>(Xs, XP, xs + (size_t)ph * H * P, (size_t)H * P, 0, JP, len - ph, nullptr);
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (tiles[k] >= NTI || tiles[k] * 16 >= len) continue;
+    for (int k = 0; k < TPW; ++k) {
+      if (!live[k]) continue;
       const int ilast = tiles[k] * 16 + 15;
       const int i = tiles[k] * 16 + col;
       const int jend = min(ph + JP, ilast + 1);
@@ -386,8 +417,8 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const T *__restrict__ x, con
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int j0 = jb + 4 * grp + r, j1 = j0 + 16;
-          m[r] = (j0 <= i) ? g0[r] * expf(fminf(si[k] - sj0[r], 0.f)) * dj0[r] : 0.f;
-          m[4 + r] = (j1 <= i) ? g1[r] * expf(fminf(si[k] - sj1[r], 0.f)) * dj1[r] : 0.f;
+          m[r] = (j0 <= i) ? g0[r] * __builtin_amdgcn_exp2f(fminf(si[k] - sj0[r], 0.f)) * dj0[r] : 0.f;
+          m[4 + r] = (j1 <= i) ? g1[r] * __builtin_amdgcn_exp2f(fminf(si[k] - sj1[r], 0.f)) * dj1[r] : 0.f;
         }
         const Frag<T> mf = frag_from_f32(m, T());
 #pragma unroll
@@ -401,9 +432,9 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const T *__restrict__ x, con
 
   const float dv = D[hd];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < TPW; ++k) {
     const int i = tiles[k] * 16 + col;
-    if (tiles[k] >= NTI || i >= len) continue;
+    if (!live[k] || i >= len) continue;
     const size_t row = ((size_t)ci.y + i) * H + hd;
 #pragma unroll
     for (int pt = 0; pt < NPT; ++pt) {
@@ -419,6 +450,18 @@ __global__ __launch_bounds__(512) void k_chunk_scan(const T *__restrict__ x, con
 
 // ------------------------------------------------------------------ launch
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Allow a kernel the full 160 KB of LDS (once per kernel; not a stream
+// operation, so calls under graph capture are unaffected after the first).
+static hipError_t set_lds_limit(const void *kern) {
+  static std::mutex mu;
+  static std::set<const void *> done;
+  std::lock_guard<std::mutex> lock(mu);
+  if (done.count(kern)) return hipSuccess;
+  hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (e == hipSuccess) done.insert(kern);
+  return e;
+}
 
 WorkspaceLayout prefill_layout(int64_t T, int nseq, int H, int P, int N, int Q, int elem) {
   WorkspaceLayout L{};
@@ -457,8 +500,9 @@ static hipError_t run_prefill(const PrefillArgs &a, unsigned stages) {
   hipStream_t st = static_cast<hipStream_t>(a.stream);
 
   if (stages & 1u) {
-    hipLaunchKernelGGL(k_chunk_cumsum, dim3(nc > 0 ? nc : 1), dim3(256), 0, st, a.dt, a.A, a.cu,
-                       a.nseq, L_dense, a.T, a.H, a.Q, nc, info, seq_off, s_ws, dt_ws);
+    hipLaunchKernelGGL(k_chunk_cumsum, dim3(nc > 0 ? nc : 1, (a.H + 3) / 4), dim3(256), 0, st,
+                       a.dt, a.A, a.cu, a.nseq, L_dense, a.T, a.H, a.Q, nc, info, seq_off, s_ws,
+                       dt_ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -466,11 +510,10 @@ static hipError_t run_prefill(const PrefillArgs &a, unsigned stages) {
     constexpr int PAD = 16 / sizeof(T);
     const size_t lds = (size_t)JP * ((P + PAD) + (N + PAD)) * sizeof(T) + 4 * (size_t)a.Q;
     auto kern = k_chunk_state<T, P, N>;
-    hipError_t e = hipFuncSetAttribute((const void *)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = set_lds_limit((const void *)kern);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(nc, a.H), dim3(256), lds, st, (const T *)a.x, (const T *)a.B,
-                       s_ws, dt_ws, info, a.H, a.G, a.Q, S);
+    hipLaunchKernelGGL(kern, dim3(nc, a.H), dim3(64 * StateTiles<P, N>::NW), lds, st,
+                       (const T *)a.x, (const T *)a.B, s_ws, dt_ws, info, a.H, a.G, a.Q, S);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -487,10 +530,11 @@ static hipError_t run_prefill(const PrefillArgs &a, unsigned stages) {
     const size_t region =
         std::max((size_t)NK * (P + PAD), (size_t)JP * ((NK + PAD) + (P + PAD))) * sizeof(T);
     const size_t lds = 8 * (size_t)a.Q + region;
-    const int threads = a.Q >= 64 ? a.Q : 64;  // Q/64 waves, at least one
-    auto kern = k_chunk_scan<T, P, N>;
-    hipError_t e = hipFuncSetAttribute((const void *)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const int tiles = a.Q / 16;
+    const bool two = tiles > 16;  // Q = 512: two tiles per wave
+    const int threads = 64 * (two ? tiles / 2 : tiles);
+    auto kern = two ? k_chunk_scan<T, P, N, 2> : k_chunk_scan<T, P, N, 1>;
+    hipError_t e = set_lds_limit((const void *)kern);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(nc, a.H), dim3(threads), lds, st, (const T *)a.x,
                        (const T *)a.B, (const T *)a.C, a.D, s_ws, dt_ws, (const T *)hin, info,

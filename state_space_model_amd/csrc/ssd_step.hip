@@ -12,7 +12,7 @@
 // d_state; here a 256-thread block owns one head and splits both p and n.)
 //
 // Block = 256 threads per (b, h): TPR = P/4 threads cover one state row with
-// float4 vectors, RPP = 256/TPR rows are in flight per pass; the partial
+// float4 vectors, RPP = 256/TPR rows per pass, eight passes in flight; the partial
 // y sums over rows are reduced through LDS at the end.
 #include "ssd_device.h"
 #include "ssd_launch.h"
@@ -50,13 +50,15 @@ __global__ __launch_bounds__(256) void k_step(const T *__restrict__ x, const flo
   float *hp = h + bh * (size_t)N * P + 4 * q;
   f4 yacc = zero4();
   int n = r0;
-  // four rows per thread in flight
-  for (; n + 3 * RPP < N; n += 4 * RPP) {
-    f4 v[4];
+  // eight rows per thread in flight
+  constexpr int U = 8;
+  for (; n + (U - 1) * RPP < N; n += U * RPP) {
+    f4 v[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(hp + (size_t)(n + u * RPP) * P));
+    for (int u = 0; u < U; ++u)
+      v[u] = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(hp + (size_t)(n + u * RPP) * P));
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < U; ++u) {
       const float bn = Bsh[n + u * RPP], cn = Csh[n + u * RPP];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {

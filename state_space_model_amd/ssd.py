@@ -103,13 +103,14 @@ def alloc_workspace(total_tokens, nseq, H, P, N, chunk, dtype, device):
 
 
 def prefill(x, dt, A, B, C, D, h0=None, chunk=256, cu_seqlens=None, *, nseq=None, y=None,
-            h_out=None, workspace=None, stages=STAGE_ALL):
+            h_out=None, workspace=None, stages=STAGE_ALL, prepare=False):
     """Chunked SSD prefill.
 
     x [T,H,P] (or [b,L,H,P]), dt [T,H], A [H], B/C [T,G,N], D [H], h0
     [nseq,H,N,P] float32 or None, cu_seqlens int32 [nseq+1] or None (dense
     batch: ``nseq`` sequences of T/nseq tokens; a 4-d x gives nseq = b).
-    Returns (y [T,H,P] float32, h_out [nseq,H,N,P] float32).
+    Returns (y [T,H,P] float32, h_out [nseq,H,N,P] float32); with
+    ``prepare=True`` nothing runs and (Prepared, y, h_out) is returned.
     """
     dense4 = x.dim() == 4
     if dense4:
@@ -150,16 +151,45 @@ def prefill(x, dt, A, B, C, D, h0=None, chunk=256, cu_seqlens=None, *, nseq=None
     if workspace is None:
         workspace = alloc_workspace(T, nseq, H, P, N, chunk, x.dtype, dev)
     lib = load()
-    _check(lib.ssd_scan_prefill_stages(
-        stages, _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(y),
-        _ptr(h_out), _ptr(cu_seqlens), nseq, T, H, P, N, G, chunk, code, _ptr(workspace),
-        workspace.numel(), _stream()))
+    args = (_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(y),
+            _ptr(h_out), _ptr(cu_seqlens), nseq, T, H, P, N, G, chunk, code, _ptr(workspace),
+            workspace.numel())
+    if prepare:
+        keep = (x, dt, A, B, C, D, h0, y, h_out, cu_seqlens, workspace)
+        return Prepared(lib.ssd_scan_prefill_stages, args, stages, keep), y, h_out
+    _check(lib.ssd_scan_prefill_stages(stages, *args, _stream()))
     if dense4:
         y = y.reshape(nseq, T // nseq, H, P)
     return y, h_out
 
 
-def step(x, dt, A, B, C, D, h, y=None):
+class Prepared:
+    """A validated, pre-marshalled call of one entry point.
+
+    Shapes, dtypes and pointers are checked once (by ``prefill``/``step``
+    with ``prepare=True``); calling the object only passes the current
+    stream and the stage mask.  The tensors must stay alive and unchanged in
+    shape while the object is used.  Useful in tight loops and under HIP
+    graph capture (the stream is read at call time).
+    """
+
+    def __init__(self, fn, args, stages=None, keep=()):
+        self._fn = fn
+        self._args = args
+        self._stages = stages
+        self._keep = keep   # tensors whose memory the pointers refer to
+
+    def __call__(self, stages=None):
+        s = _stream()
+        if self._stages is None:
+            rc = self._fn(*self._args, s)
+        else:
+            rc = self._fn(self._stages if stages is None else stages, *self._args, s)
+        if rc != 0:
+            _check(rc)
+
+
+def step(x, dt, A, B, C, D, h, y=None, prepare=False):
     """One decode token; h [b,H,N,P] float32 is updated in place.  Returns y [b,H,P]."""
     b, H, P = x.shape
     G, N = B.shape[-2], B.shape[-1]
@@ -177,6 +207,9 @@ def step(x, dt, A, B, C, D, h, y=None):
     if y is None:
         y = torch.empty((b, H, P), dtype=torch.float32, device=dev)
     _need(y, "y", torch.float32, dev)
-    _check(load().ssd_step(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h),
-                           _ptr(y), b, H, P, N, G, code, _stream()))
+    args = (_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h), _ptr(y), b, H, P, N,
+            G, code)
+    if prepare:
+        return Prepared(load().ssd_step, args, keep=(x, dt, A, B, C, D, h, y)), y
+    _check(load().ssd_step(*args, _stream()))
     return y
