@@ -11,7 +11,7 @@
 
 #include <new>
 
-#include "../../include/ssd.h"
+#include "ssd.h"
 #include "ssd_launch.h"
 
 namespace {

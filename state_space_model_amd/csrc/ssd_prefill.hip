@@ -18,9 +18,9 @@
 //
 // Kernels (one launch each, all on the caller's stream):
 //   K1 k_chunk_cumsum : grid (nc_max, H/4)  chunk map + s, dt per (chunk, head)
-//   K2 k_chunk_state  : grid (nc_max, H)    S_c^T = (w o X)^T B on MFMA, k = tokens (16 waves)
+//   K2 k_chunk_state  : 8*H*ceil(nc/8)    S_c^T = (w o X)^T B on MFMA, k = tokens (16 waves)
 //   K3 k_state_pass   : grid (NP/1024,H,nseq) sequential H_c over the chunks of a sequence
-//   K4 k_chunk_scan   : grid (nc_max, H)    one wave per 16-token tile: C.B^T (k = N), mask/decay, Y^T = X^T M^T
+//   K4 k_chunk_scan   : 8*H*ceil(nc/8)    one wave per 16-token tile: C.B^T (k = N), mask/decay, Y^T = X^T M^T
 //                                           (k = tokens) and exp(s) H^T C^T (k = N) on MFMA
 // Every padded row of a partial chunk has dt = 0, x = 0, B = 0: it changes
 // nothing (decay 1, no input), so the chunk-end value s_{Q-1} equals
@@ -185,7 +185,29 @@ __device__ __forceinline__ void stage_rows(T *tile, int pitch, const T *__restri
   }
 }
 
-constexpr int kJP = 128;  // token rows staged in LDS per phase (K2, K4)
+constexpr int kJP = 128;  // token rows staged in LDS per phase (K2)
+
+// LDS row padding.  Tiles read with the 16-lane transpose read (4 rows x 32
+// bytes per lane group) use a pitch of width + 16 elements, i.e. 32 bytes (bf16)
+// or 64 bytes (float) past a multiple of 128 bytes, so the rows of one
+// read land on disjoint banks.  Tiles read 16 bytes per lane along a row use
+// width + 16 bytes (8 consecutive rows of a lane octet then cover every bank).
+constexpr int kTrPad = 16;
+template <typename T> constexpr int row_pad() { return 16 / (int)sizeof(T); }
+
+// XCD-aware (chunk, head) order for a 1-D grid of 8 * H * ceil(nc / 8)
+// workgroups.  Workgroup L is dispatched to XCD L % 8; decoding
+// c = 8 (q / H) + L % 8, h = q % H with q = L / 8 puts every head of chunk c on
+// the same XCD, back to back, so the chunk's B (and C) rows are fetched from
+// HBM once and then hit that XCD's L2 for the other heads.
+struct ChunkHead {
+  int c, h;
+};
+__device__ __forceinline__ ChunkHead xcd_chunk_head(int H) {
+  const int L = blockIdx.x, q = L >> 3;
+  return ChunkHead{8 * (q / H) + (L & 7), q % H};
+}
+static inline unsigned xcd_grid(int nc, int H) { return 8u * (unsigned)H * (unsigned)((nc + 7) / 8); }
 
 // ------------------------------------------------------------ K2 chunk state
 // S_c^T[p][n] = sum_j X'[j][p] B[j][n],  X'[j] = 2^(s_end - s_j) dt_j x_j.
@@ -202,12 +224,13 @@ template <typename T, int P, int N>
 __global__ __launch_bounds__(1024) void k_chunk_state(const T *__restrict__ x, const T *__restrict__ B,
                                                       const float *__restrict__ s_ws,
                                                       const float *__restrict__ dt_ws,
-                                                      const int4 *__restrict__ info, int H, int G,
-                                                      int Q, float *__restrict__ S_out) {
-  constexpr int PAD = 16 / sizeof(T);
-  constexpr int XP = P + PAD, BP = N + PAD;
+                                                      const int4 *__restrict__ info, int nc, int H,
+                                                      int G, int Q, float *__restrict__ S_out) {
+  constexpr int XP = P + kTrPad, BP = N + kTrPad;
   constexpr int NNT = N / 16, NW = StateTiles<P, N>::NW, TPW = StateTiles<P, N>::TPW;
-  const int c = blockIdx.x, hd = blockIdx.y;
+  const ChunkHead ch = xcd_chunk_head(H);
+  const int c = ch.c, hd = ch.h;
+  if (c >= nc) return;
   const int4 ci = info[c];
   if (ci.z <= 0) return;
   const int g = (hd * G) / H;
@@ -299,152 +322,293 @@ __global__ __launch_bounds__(256) void k_state_pass(const float *__restrict__ S,
 }
 
 // ------------------------------------------------------------ K4 chunk scan
-// Per (chunk, head).  The chunk's Q/16 output tiles (16 tokens each) go to
-// NW = min(16, Q/16) waves; with TPW = 2 (Q = 512) wave w owns tiles
-// {w, 2NW-1-w}, which balances the causal work.
-//   Y^T[p][i]  = 2^(s_i) (H_in^T C^T)[p][i]             k = n    (A: H_in tile via transpose read)
-//             += sum_j X^T[p][j] M^T[j][i]              k = j    (A: X tile via transpose read)
+// Per (chunk, head).  The chunk's Q/16 output tiles (16 tokens each) are
+// spread over NW waves, TPW tiles per wave in snake order {w, 2NW-1-w},
+// which balances the causal work:
+//   Q <= 256: TPW 1, NW = Q/16      Q = 512: TPW 2, NW 16
+// Per output tile (all accumulation in float32):
+//   Y^T[p][i]  = 2^(s_i) (H_in^T C^T)[p][i]             k = n    (A: H_in tile, transpose read)
+//             += sum_j X^T[p][j] M^T[j][i]              k = j    (A: X tile, transpose read)
+//             += D x_i                                  (while the tile's own rows are staged)
 //   M^T[j][i]  = (B C^T)[j][i] 2^(s_i - s_j) dt_j  (j <= i)      k = n
-// The two 16x16 results of B C^T for j-rows jb..jb+15 and jb+16..jb+31 are
-// fed straight back as the B operand (paired k map); X^T is read with the
-// same pairing.
-template <typename T, int P, int N, int TPW>
-__global__ __launch_bounds__(1024) void k_chunk_scan(const T *__restrict__ x, const T *__restrict__ B,
-                                                     const T *__restrict__ C,
-                                                     const float *__restrict__ D,
-                                                     const float *__restrict__ s_ws,
-                                                     const float *__restrict__ dt_ws,
-                                                     const T *__restrict__ hin,
-                                                     const int4 *__restrict__ info, int H, int G,
-                                                     int Q, float *__restrict__ y) {
-  constexpr int PAD = 16 / sizeof(T);
-  constexpr int NK = N < 32 ? 32 : N;  // contraction over n, padded to the k-step
-  constexpr int KS = NK / 32;
-  constexpr int XP = P + PAD, BP = NK + PAD, HP = P + PAD;
+// A wave walks the j-blocks (32 rows) once and reuses every B-row fragment and
+// every X^T fragment for all of its tiles that the block reaches (register
+// blocking: one LDS read feeds up to TPW MFMAs).  The two 16x16 results of
+// B C^T for rows jb..jb+15 and jb+16..jb+31 are fed straight back as the B
+// operand (paired k map); X^T is read with the same pairing.  B/X rows are
+// staged JP at a time.  With one tile per wave the next phase's rows are
+// loaded into registers while the current phase computes (two LDS buffers);
+// with two tiles per wave the registers are needed for the tiles, so a phase
+// is staged between two barriers and the second workgroup on the CU covers
+// the wait.
+template <typename T, int P, int N> struct ScanCfg {
+  static constexpr int NK = N < 32 ? 32 : N;  // contraction over n, padded to the k-step
+  static constexpr int KS = NK / 32;
+  static constexpr int XP = P + kTrPad, BP = NK + row_pad<T>(), HP = P + kTrPad;
+  static constexpr int VN = 16 / sizeof(T);
+  static constexpr int VB = NK / VN, VX = P / VN;  // 16-byte vectors per staged row
+  static constexpr size_t lds_bytes(int jp, int q) {
+    return (2 * (size_t)jp * (BP + XP) + (size_t)NK * HP) * sizeof(T) + 12 * (size_t)q;
+  }
+  // rows per phase by block class: 64 for short chunks; 128 for Q >= 256 (two
+  // 128-row buffers where they fit), else 64, else 32
+  static constexpr int jp(int cls) {
+    return cls != 0 && lds_bytes(128, 512) <= 160 * 1024 ? 128
+           : lds_bytes(64, 512) <= 160 * 1024            ? 64
+                                                         : 32;
+  }
+  // 16-byte vectors per thread for one phase, by block class: class 0
+  // (Q <= 128) has 4 threads per staged row (blockDim = 4Q >= 4 JP_eff);
+  // classes 1 and 2 (Q = 256, 512) have 1024 threads
+  static constexpr int maxv(int cls) {
+    return cls == 0 ? (VB + VX + 3) / 4 : (jp(cls) * (VB + VX) + 1023) / 1024;
+  }
+};
+
+// Registers holding one phase of staged rows (B rows then X rows).
+template <typename T, int P, int N, int MAXV> struct PhaseRegs {
+  typedef ScanCfg<T, P, N> K;
+  typedef typename Vec16<T>::type V;
+  V v[MAXV];
+
+  __device__ __forceinline__ void load(const T *__restrict__ bs, size_t bstride,
+                                       const T *__restrict__ xs, size_t xstride, int jp,
+                                       int rows_left) {
+    const int nb = jp * K::VB, total = nb + jp * K::VX;
+#pragma unroll
+    for (int k = 0; k < MAXV; ++k) {
+      const int idx = threadIdx.x + k * blockDim.x;
+      v[k] = vzero<V>();
+      if (idx < nb) {
+        const int r = idx / K::VB, c = idx % K::VB;
+        if (r < rows_left && c * K::VN < N) v[k] = *reinterpret_cast<const V *>(bs + r * bstride + c * K::VN);
+      } else if (idx < total) {
+        const int r = (idx - nb) / K::VX, c = (idx - nb) % K::VX;
+        if (r < rows_left) v[k] = *reinterpret_cast<const V *>(xs + r * xstride + c * K::VN);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(T *Bs, T *Xs, int jp) const {
+    const int nb = jp * K::VB, total = nb + jp * K::VX;
+#pragma unroll
+    for (int k = 0; k < MAXV; ++k) {
+      const int idx = threadIdx.x + k * blockDim.x;
+      if (idx < nb) {
+        const int r = idx / K::VB, c = idx % K::VB;
+        *reinterpret_cast<V *>(Bs + r * K::BP + c * K::VN) = v[k];
+      } else if (idx < total) {
+        const int r = (idx - nb) / K::VX, c = (idx - nb) % K::VX;
+        *reinterpret_cast<V *>(Xs + r * K::XP + c * K::VN) = v[k];
+      }
+    }
+  }
+};
+
+// CLS: 0 = Q <= 128 (Q/16 waves), 1 = Q 256 (16 waves), 2 = Q 512 (16 waves,
+// two tiles each).
+template <typename T, int P, int N, int CLS>
+__global__ __launch_bounds__(CLS == 0 ? 512 : 1024) void k_chunk_scan(const T *__restrict__ x, const T *__restrict__ B,
+                                                    const T *__restrict__ C,
+                                                    const float *__restrict__ D,
+                                                    const float *__restrict__ s_ws,
+                                                    const float *__restrict__ dt_ws,
+                                                    const T *__restrict__ hin,
+                                                    const int4 *__restrict__ info, int nc, int H,
+                                                    int G, int Q, float *__restrict__ y) {
+  typedef ScanCfg<T, P, N> K;
+  constexpr int KS = K::KS, NK = K::NK, XP = K::XP, BP = K::BP, HP = K::HP;
   constexpr int NPT = P / 16;
-  const int c = blockIdx.x, hd = blockIdx.y;
+  constexpr int TPW = CLS == 2 ? 2 : 1;
+  const ChunkHead ch = xcd_chunk_head(H);
+  const int c = ch.c, hd = ch.h;
+  if (c >= nc) return;
   const int4 ci = info[c];
   if (ci.z <= 0) return;
   const int len = ci.z;
   const int g = (hd * G) / H;
-  const int JP = Q < kJP ? Q : kJP;
-  const int nw = blockDim.x >> 6, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int JP = Q < K::jp(CLS) ? Q : K::jp(CLS);
+  const int nw = blockDim.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = lane >> 4, col = lane & 15;
 
   extern __shared__ __align__(16) char smem[];
   float *s_l = reinterpret_cast<float *>(smem);
   float *dt_l = s_l + Q;
-  T *region = reinterpret_cast<T *>(dt_l + Q);
-  T *Hs = region;             // [NK][HP]   (first)
-  T *Bs = region;             // [JP][BP]   (then, per phase)
-  T *Xs = region + JP * BP;   // [JP][XP]
+  float *u_l = dt_l + Q;                    // 2^(s_ref(j) - s_j) dt_j, s_ref(j) = s at the end of j's 32-block
+  T *Hs = reinterpret_cast<T *>(u_l + Q);   // [NK][HP]
+  T *buf0 = Hs + NK * HP;                   // [JP][BP] then [JP][XP]
+  T *buf1 = buf0 + JP * (BP + XP);
 
   const size_t csh = (size_t)c * H + hd;
-  for (int i = threadIdx.x; i < Q; i += blockDim.x) {
-    s_l[i] = s_ws[csh * Q + i];
-    dt_l[i] = dt_ws[csh * Q + i];
-  }
-  stage_rows<T, P, P>(Hs, HP, hin + csh * (size_t)(N * P), (size_t)P, 0, NK, N, nullptr);
-  __syncthreads();
+  const T *xs = x + ((size_t)ci.y * H + hd) * P;
+  const T *bs = B + ((size_t)ci.y * G + g) * N;
+  const size_t xstride = (size_t)H * P, bstride = (size_t)G * N;
 
-  int tiles[TPW];
-  tiles[0] = wave;
-  if (TPW == 2) tiles[TPW - 1] = 2 * nw - 1 - wave;
+  // ---- prologue: every load of the first phase is issued before any wait
+  int t0[TPW];  // first row of each tile (wave-uniform)
+  t0[0] = 16 * wave;
+  if (TPW == 2) t0[1] = 16 * (2 * nw - 1 - wave);
   const T *Cg = C + ((size_t)ci.y * G + g) * N;
   Frag<T> cf[TPW][KS];
   float si[TPW];
-  bool live[TPW];
 #pragma unroll
   for (int k = 0; k < TPW; ++k) {
-    const int i = tiles[k] * 16 + col;
-    live[k] = tiles[k] * 16 < len;  // wave-uniform
+    const int i = t0[k] + col;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int n8 = ks * 32 + 8 * grp;
-      cf[k][ks] = (i < len && n8 < N) ? frag_global(Cg + (size_t)i * G * N + n8) : frag_zero<T>();
+      cf[k][ks] = (i < len && n8 < N) ? frag_global(Cg + (size_t)i * bstride + n8) : frag_zero<T>();
     }
-    si[k] = s_l[i];
+    si[k] = s_ws[csh * Q + i];
   }
+  PhaseRegs<T, P, N, K::maxv(CLS)> pr;
+  pr.load(bs, bstride, xs, xstride, JP, len);
+  for (int i = threadIdx.x; i < Q; i += blockDim.x) {
+    const float sv = s_ws[csh * Q + i], dv = dt_ws[csh * Q + i];
+    s_l[i] = sv;
+    dt_l[i] = dv;
+    u_l[i] = __builtin_amdgcn_exp2f(fminf(s_ws[csh * Q + (i | 31)] - sv, 0.f)) * dv;
+  }
+  stage_rows<T, P, P>(Hs, HP, hin + csh * (size_t)(N * P), (size_t)P, 0, NK, N, nullptr);
+  pr.store(buf0, buf0 + JP * BP, JP);
+  __syncthreads();
 
+  // ---- state entering the chunk: Y^T = 2^(s_i) H_in^T C^T (each H_in fragment
+  // feeds every tile of the wave)
   f4 acc[TPW][NPT];
 #pragma unroll
-  for (int k = 0; k < TPW; ++k) {
+  for (int k = 0; k < TPW; ++k)
 #pragma unroll
     for (int pt = 0; pt < NPT; ++pt) acc[k][pt] = zero4();
-    if (live[k]) {
 #pragma unroll
-      for (int pt = 0; pt < NPT; ++pt) {
+  for (int pt = 0; pt < NPT; ++pt) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          Frag<T> a = frag_kmaj(Hs, HP, pt * 16, ks * 32 + 8 * grp, ks * 32 + 8 * grp + 4);
-          mma(acc[k][pt], a, cf[k][ks]);
-        }
-      }
-      const float ei = __builtin_amdgcn_exp2f(fminf(si[k], 0.f));
+    for (int ks = 0; ks < KS; ++ks) {
+      const Frag<T> a = frag_kmaj(Hs, HP, pt * 16, ks * 32 + 8 * grp, ks * 32 + 8 * grp + 4);
 #pragma unroll
-      for (int pt = 0; pt < NPT; ++pt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[k][pt][r] *= ei;
+      for (int k = 0; k < TPW; ++k)
+        if (t0[k] < len) mma(acc[k][pt], a, cf[k][ks]);
     }
   }
-
-  const T *xs = x + ((size_t)ci.y * H + hd) * P;
-  const T *bs = B + ((size_t)ci.y * G + g) * N;
-  for (int ph = 0; ph < len; ph += JP) {  // phases past the chunk length add nothing
-    __syncthreads();  // previous users of the region are done
-    stage_rows<T, N, NK>(Bs, BP, bs + (size_t)ph * G * N, (size_t)G * N, 0, JP, len - ph, nullptr);
-    stage_rows<T, P, P>(Xs, XP, xs + (size_t)ph * H * P, (size_t)H * P, 0, JP, len - ph, nullptr);
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < TPW; ++k) {
-      if (!live[k]) continue;
-      const int ilast = tiles[k] * 16 + 15;
-      const int i = tiles[k] * 16 + col;
-      const int jend = min(ph + JP, ilast + 1);
-      for (int jb = ph; jb < jend; jb += 32) {
-        f4 g0 = zero4(), g1 = zero4();
-        const int jl = jb - ph;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          Frag<T> b0 = frag_rowk(Bs, BP, jl + col, ks * 32 + 8 * grp);
-          Frag<T> b1 = frag_rowk(Bs, BP, jl + 16 + col, ks * 32 + 8 * grp);
-          mma(g0, b0, cf[k][ks]);
-          mma(g1, b1, cf[k][ks]);
-        }
-        const f4 sj0 = ld4(s_l + jb + 4 * grp), sj1 = ld4(s_l + jb + 16 + 4 * grp);
-        const f4 dj0 = ld4(dt_l + jb + 4 * grp), dj1 = ld4(dt_l + jb + 16 + 4 * grp);
-        float m[8];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j0 = jb + 4 * grp + r, j1 = j0 + 16;
-          m[r] = (j0 <= i) ? g0[r] * __builtin_amdgcn_exp2f(fminf(si[k] - sj0[r], 0.f)) * dj0[r] : 0.f;
-          m[4 + r] = (j1 <= i) ? g1[r] * __builtin_amdgcn_exp2f(fminf(si[k] - sj1[r], 0.f)) * dj1[r] : 0.f;
-        }
-        const Frag<T> mf = frag_from_f32(m, T());
-#pragma unroll
-        for (int pt = 0; pt < NPT; ++pt) {
-          Frag<T> a = frag_kmaj(Xs, XP, pt * 16, jl + 4 * grp, jl + 16 + 4 * grp);
-          mma(acc[k][pt], a, mf);
-        }
-      }
-    }
-  }
-
-  const float dv = D[hd];
 #pragma unroll
   for (int k = 0; k < TPW; ++k) {
-    const int i = tiles[k] * 16 + col;
-    if (!live[k] || i >= len) continue;
-    const size_t row = ((size_t)ci.y + i) * H + hd;
+    const float ei = __builtin_amdgcn_exp2f(fminf(si[k], 0.f));
 #pragma unroll
-    for (int pt = 0; pt < NPT; ++pt) {
-      const int p = pt * 16 + 4 * grp;
-      const f4 xv = ld4f(x + row * P + p);
-      f4 o;
+    for (int pt = 0; pt < NPT; ++pt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o[r] = acc[k][pt][r] + dv * xv[r];
-      st4(y + row * P + p, o);
+      for (int r = 0; r < 4; ++r) acc[k][pt][r] *= ei;
+  }
+
+  // last row any tile of this wave needs
+  int wave_last = 0;
+#pragma unroll
+  for (int k = 0; k < TPW; ++k) wave_last = max(wave_last, t0[k] + 15);
+  wave_last = min(wave_last, len - 1);
+
+  const float dv = D[hd];
+  constexpr bool PIPE = TPW == 1;
+  int cur = 0;
+  for (int ph = 0; ph < len; ph += JP) {  // phases past the chunk length add nothing
+    T *Bs = cur ? buf1 : buf0;
+    T *Xs = Bs + JP * BP;
+    const bool more = ph + JP < len;
+    if (!PIPE && ph > 0) {  // stage this phase between two barriers
+      pr.load(bs + (size_t)ph * bstride, bstride, xs + (size_t)ph * xstride, xstride, JP,
+              len - ph);
+      pr.store(Bs, Xs, JP);
+      __syncthreads();
     }
+    if (PIPE && more)  // next phase's rows travel while this phase computes
+      pr.load(bs + (size_t)(ph + JP) * bstride, bstride, xs + (size_t)(ph + JP) * xstride,
+              xstride, JP, len - ph - JP);
+    // skip term D x_i for tiles whose rows are staged in this phase
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+      if (t0[k] >= ph && t0[k] < ph + JP && t0[k] < len) {
+#pragma unroll
+        for (int pt = 0; pt < NPT; ++pt) {
+          const f4 xv = ld4f(Xs + (t0[k] + col - ph) * XP + pt * 16 + 4 * grp);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[k][pt][r] += dv * xv[r];
+        }
+      }
+    }
+    const int jend = min(ph + JP, wave_last + 1);
+    for (int jb = ph; jb < jend; jb += 32) {
+      const int jl = jb - ph;
+      // G^T = B C^T for every tile the block reaches (tile k needs jb <= t0[k] + 15)
+      f4 g0[TPW], g1[TPW];
+#pragma unroll
+      for (int k = 0; k < TPW; ++k) g0[k] = g1[k] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const Frag<T> b0 = frag_rowk(Bs, BP, jl + col, ks * 32 + 8 * grp);
+        const Frag<T> b1 = frag_rowk(Bs, BP, jl + 16 + col, ks * 32 + 8 * grp);
+#pragma unroll
+        for (int k = 0; k < TPW; ++k) {
+          if (jb <= t0[k] + 15) {
+            mma(g0[k], b0, cf[k][ks]);
+            mma(g1[k], b1, cf[k][ks]);
+          }
+        }
+      }
+      Frag<T> mf[TPW];
+#pragma unroll
+      for (int k = 0; k < TPW; ++k) {
+        if (jb > t0[k] + 15) continue;
+        float m[8];
+        if (jb + 31 < t0[k]) {
+          // block entirely before the tile: no mask, and the decay factors through
+          // the block end, 2^(s_i - s_ref) * [2^(s_ref - s_j) dt_j], both <= 1
+          const float v = __builtin_amdgcn_exp2f(fminf(si[k] - s_l[jb + 31], 0.f));
+          const f4 u0 = ld4(u_l + jb + 4 * grp), u1 = ld4(u_l + jb + 16 + 4 * grp);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            m[r] = g0[k][r] * u0[r] * v;
+            m[4 + r] = g1[k][r] * u1[r] * v;
+          }
+        } else {  // block holding the tile's rows: causal mask, exact decay
+          const int i = t0[k] + col;
+          const f4 sj0 = ld4(s_l + jb + 4 * grp), sj1 = ld4(s_l + jb + 16 + 4 * grp);
+          const f4 dj0 = ld4(dt_l + jb + 4 * grp), dj1 = ld4(dt_l + jb + 16 + 4 * grp);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int j0 = jb + 4 * grp + r, j1 = j0 + 16;
+            // every argument is clamped to <= 0, so each product is finite and the
+            // mask can be a multiply by 0 or 1 (no branch)
+            const float e0 = __builtin_amdgcn_exp2f(fminf(si[k] - sj0[r], 0.f)) * dj0[r];
+            const float e1 = __builtin_amdgcn_exp2f(fminf(si[k] - sj1[r], 0.f)) * dj1[r];
+            m[r] = g0[k][r] * e0 * (j0 <= i ? 1.f : 0.f);
+            m[4 + r] = g1[k][r] * e1 * (j1 <= i ? 1.f : 0.f);
+          }
+        }
+        mf[k] = frag_from_f32(m, T());
+      }
+      // Y^T += X^T M^T, each X^T fragment feeding every tile the block reaches
+#pragma unroll
+      for (int pt = 0; pt < NPT; ++pt) {
+        const Frag<T> a = frag_kmaj(Xs, XP, pt * 16, jl + 4 * grp, jl + 16 + 4 * grp);
+#pragma unroll
+        for (int k = 0; k < TPW; ++k)
+          if (jb <= t0[k] + 15) mma(acc[k][pt], a, mf[k]);
+      }
+    }
+    // tiles whose rows end in this phase have seen every j <= i: store them now
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+      const int i = t0[k] + col;
+      if (t0[k] >= ph && t0[k] < ph + JP && i < len) {
+        const size_t row = ((size_t)ci.y + i) * H + hd;
+#pragma unroll
+        for (int pt = 0; pt < NPT; ++pt) st4(y + row * P + pt * 16 + 4 * grp, acc[k][pt]);
+      }
+    }
+    if (PIPE && more) {
+      T *Bn = cur ? buf0 : buf1;
+      pr.store(Bn, Bn + JP * BP, JP);
+    }
+    __syncthreads();  // PIPE: the next phase's buffer is complete; both: this one is free
+    if (PIPE) cur ^= 1;
   }
 }
 
@@ -507,13 +671,12 @@ static hipError_t run_prefill(const PrefillArgs &a, unsigned stages) {
     if (e != hipSuccess) return e;
   }
   if ((stages & 2u) && nc > 0) {
-    constexpr int PAD = 16 / sizeof(T);
-    const size_t lds = (size_t)JP * ((P + PAD) + (N + PAD)) * sizeof(T) + 4 * (size_t)a.Q;
+    const size_t lds = (size_t)JP * ((P + kTrPad) + (N + kTrPad)) * sizeof(T) + 4 * (size_t)a.Q;
     auto kern = k_chunk_state<T, P, N>;
     hipError_t e = set_lds_limit((const void *)kern);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(nc, a.H), dim3(64 * StateTiles<P, N>::NW), lds, st,
-                       (const T *)a.x, (const T *)a.B, s_ws, dt_ws, info, a.H, a.G, a.Q, S);
+    hipLaunchKernelGGL(kern, dim3(xcd_grid(nc, a.H)), dim3(64 * StateTiles<P, N>::NW), lds, st,
+                       (const T *)a.x, (const T *)a.B, s_ws, dt_ws, info, nc, a.H, a.G, a.Q, S);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -525,20 +688,19 @@ static hipError_t run_prefill(const PrefillArgs &a, unsigned stages) {
     if (e != hipSuccess) return e;
   }
   if ((stages & 8u) && nc > 0) {
-    constexpr int PAD = 16 / sizeof(T);
-    constexpr int NK = N < 32 ? 32 : N;
-    const size_t region =
-        std::max((size_t)NK * (P + PAD), (size_t)JP * ((NK + PAD) + (P + PAD))) * sizeof(T);
-    const size_t lds = 8 * (size_t)a.Q + region;
-    const int tiles = a.Q / 16;
-    const bool two = tiles > 16;  // Q = 512: two tiles per wave
-    const int threads = 64 * (two ? tiles / 2 : tiles);
-    auto kern = two ? k_chunk_scan<T, P, N, 2> : k_chunk_scan<T, P, N, 1>;
+    typedef ScanCfg<T, P, N> K;
+    // block class: Q <= 128, Q = 256 (one tile per wave), Q = 512 (two tiles per wave)
+    const int cls = a.Q <= 128 ? 0 : a.Q == 256 ? 1 : 2;
+    const int jp = a.Q < K::jp(cls) ? a.Q : K::jp(cls);
+    const size_t lds = K::lds_bytes(jp, a.Q);
+    const int threads = 64 * (a.Q / 16) / (cls == 2 ? 2 : 1);
+    auto kern = cls == 0 ? k_chunk_scan<T, P, N, 0>
+                         : cls == 1 ? k_chunk_scan<T, P, N, 1> : k_chunk_scan<T, P, N, 2>;
     hipError_t e = set_lds_limit((const void *)kern);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(nc, a.H), dim3(threads), lds, st, (const T *)a.x,
+    hipLaunchKernelGGL(kern, dim3(xcd_grid(nc, a.H)), dim3(threads), lds, st, (const T *)a.x,
                        (const T *)a.B, (const T *)a.C, a.D, s_ws, dt_ws, (const T *)hin, info,
-                       a.H, a.G, a.Q, a.y);
+                       nc, a.H, a.G, a.Q, a.y);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
