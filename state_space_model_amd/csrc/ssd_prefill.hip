@@ -322,59 +322,54 @@ __global__ __launch_bounds__(256) void k_state_pass(const float *__restrict__ S,
 }
 
 // ------------------------------------------------------------ K4 chunk scan
-// Per (chunk, head).  The chunk's Q/16 output tiles (16 tokens each) are
-// spread over NW waves, TPW tiles per wave in snake order {w, 2NW-1-w},
-// which balances the causal work:
-//   Q <= 256: TPW 1, NW = Q/16      Q = 512: TPW 2, NW 16
-// Per output tile (all accumulation in float32):
+// One workgroup per (chunk, HB heads of one B/C group, part z of SPLIT), one
+// wave per 16-token output tile.  Q <= 256: SPLIT 1, Q/16 waves, two heads per
+// workgroup when the group has an even number of heads.  Q = 512: SPLIT 2, 16
+// waves: part z owns tiles t_k = 2k + (z ^ (k & 1)), whose causal work is k + 1
+// j-blocks in both parts, and wave w takes k = w for w < NW/2, else
+// k = 3NW/2 - 1 - w, so the waves sharing a SIMD (w, w + 4, ...) carry equal
+// work.
+// Per output tile and head (all accumulation in float32):
 //   Y^T[p][i]  = 2^(s_i) (H_in^T C^T)[p][i]             k = n    (A: H_in tile, transpose read)
 //             += sum_j X^T[p][j] M^T[j][i]              k = j    (A: X tile, transpose read)
 //             += D x_i                                  (while the tile's own rows are staged)
 //   M^T[j][i]  = (B C^T)[j][i] 2^(s_i - s_j) dt_j  (j <= i)      k = n
-// A wave walks the j-blocks (32 rows) once and reuses every B-row fragment and
-// every X^T fragment for all of its tiles that the block reaches (register
-// blocking: one LDS read feeds up to TPW MFMAs).  The two 16x16 results of
-// B C^T for rows jb..jb+15 and jb+16..jb+31 are fed straight back as the B
-// operand (paired k map); X^T is read with the same pairing.  B/X rows are
-// staged JP at a time.  With one tile per wave the next phase's rows are
-// loaded into registers while the current phase computes (two LDS buffers);
-// with two tiles per wave the registers are needed for the tiles, so a phase
-// is staged between two barriers and the second workgroup on the CU covers
-// the wait.
-template <typename T, int P, int N> struct ScanCfg {
+// B C^T depends only on the chunk and group, so it is computed once per
+// j-block and applied to every head of the workgroup; the C fragments and the
+// staged B rows are likewise shared.  The two 16x16 results of B C^T for rows
+// jb..jb+15 and jb+16..jb+31 are fed straight back as the B operand (paired k
+// map); X^T is read with the same pairing.  LDS holds the H_in tiles first and
+// then, in the same space, one phase of JP staged B/X rows; the next phase's
+// rows are loaded into registers while the current one computes.
+template <typename T, int P, int N, int HB> struct ScanCfg {
   static constexpr int NK = N < 32 ? 32 : N;  // contraction over n, padded to the k-step
   static constexpr int KS = NK / 32;
   static constexpr int XP = P + kTrPad, BP = NK + row_pad<T>(), HP = P + kTrPad;
   static constexpr int VN = 16 / sizeof(T);
   static constexpr int VB = NK / VN, VX = P / VN;  // 16-byte vectors per staged row
+  static constexpr int JP = 64;                    // staged rows per phase (Q >= 64)
+  static constexpr size_t phase_elems(int jp) { return (size_t)jp * (BP + HB * XP); }
+  static constexpr size_t hs_elems() { return (size_t)HB * NK * HP; }
   static constexpr size_t lds_bytes(int jp, int q) {
-    return (2 * (size_t)jp * (BP + XP) + (size_t)NK * HP) * sizeof(T) + 12 * (size_t)q;
+    return (phase_elems(jp) > hs_elems() ? phase_elems(jp) : hs_elems()) * sizeof(T) +
+           12 * (size_t)HB * q;
   }
-  // rows per phase by block class: 64 for short chunks; 128 for Q >= 256 (two
-  // 128-row buffers where they fit), else 64, else 32
-  static constexpr int jp(int cls) {
-    return cls != 0 && lds_bytes(128, 512) <= 160 * 1024 ? 128
-           : lds_bytes(64, 512) <= 160 * 1024            ? 64
-                                                         : 32;
-  }
-  // 16-byte vectors per thread for one phase, by block class: class 0
-  // (Q <= 128) has 4 threads per staged row (blockDim = 4Q >= 4 JP_eff);
-  // classes 1 and 2 (Q = 256, 512) have 1024 threads
-  static constexpr int maxv(int cls) {
-    return cls == 0 ? (VB + VX + 3) / 4 : (jp(cls) * (VB + VX) + 1023) / 1024;
+  // 16-byte vectors each thread stages per phase
+  static constexpr int nvec(int jp, int threads) {
+    return (int)(((size_t)jp * (VB + HB * VX) + threads - 1) / threads);
   }
 };
 
-// Registers holding one phase of staged rows (B rows then X rows).
-template <typename T, int P, int N, int MAXV> struct PhaseRegs {
-  typedef ScanCfg<T, P, N> K;
+// Registers holding one phase of staged rows (B rows, then X rows of each head).
+template <typename T, int P, int N, int HB, int MAXV> struct PhaseRegs {
+  typedef ScanCfg<T, P, N, HB> K;
   typedef typename Vec16<T>::type V;
   V v[MAXV];
 
   __device__ __forceinline__ void load(const T *__restrict__ bs, size_t bstride,
                                        const T *__restrict__ xs, size_t xstride, int jp,
                                        int rows_left) {
-    const int nb = jp * K::VB, total = nb + jp * K::VX;
+    const int nb = jp * K::VB, nx = jp * K::VX, total = nb + HB * nx;
 #pragma unroll
     for (int k = 0; k < MAXV; ++k) {
       const int idx = threadIdx.x + k * blockDim.x;
@@ -383,13 +378,15 @@ template <typename T, int P, int N, int MAXV> struct PhaseRegs {
         const int r = idx / K::VB, c = idx % K::VB;
         if (r < rows_left && c * K::VN < N) v[k] = *reinterpret_cast<const V *>(bs + r * bstride + c * K::VN);
       } else if (idx < total) {
-        const int r = (idx - nb) / K::VX, c = (idx - nb) % K::VX;
-        if (r < rows_left) v[k] = *reinterpret_cast<const V *>(xs + r * xstride + c * K::VN);
+        const int e = (idx - nb) / nx, rem = (idx - nb) % nx;
+        const int r = rem / K::VX, c = rem % K::VX;
+        if (r < rows_left) v[k] = *reinterpret_cast<const V *>(xs + r * xstride + e * P + c * K::VN);
       }
     }
   }
+  // Bs: [JP][BP]; Xs: HB tiles of [JP][XP]
   __device__ __forceinline__ void store(T *Bs, T *Xs, int jp) const {
-    const int nb = jp * K::VB, total = nb + jp * K::VX;
+    const int nb = jp * K::VB, nx = jp * K::VX, total = nb + HB * nx;
 #pragma unroll
     for (int k = 0; k < MAXV; ++k) {
       const int idx = threadIdx.x + k * blockDim.x;
@@ -397,219 +394,225 @@ template <typename T, int P, int N, int MAXV> struct PhaseRegs {
         const int r = idx / K::VB, c = idx % K::VB;
         *reinterpret_cast<V *>(Bs + r * K::BP + c * K::VN) = v[k];
       } else if (idx < total) {
-        const int r = (idx - nb) / K::VX, c = (idx - nb) % K::VX;
-        *reinterpret_cast<V *>(Xs + r * K::XP + c * K::VN) = v[k];
+        const int e = (idx - nb) / nx, rem = (idx - nb) % nx;
+        const int r = rem / K::VX, c = rem % K::VX;
+        *reinterpret_cast<V *>(Xs + ((size_t)e * jp + r) * K::XP + c * K::VN) = v[k];
       }
     }
   }
 };
 
-// CLS: 0 = Q <= 128 (Q/16 waves), 1 = Q 256 (16 waves), 2 = Q 512 (16 waves,
-// two tiles each).
-template <typename T, int P, int N, int CLS>
-__global__ __launch_bounds__(CLS == 0 ? 512 : 1024) void k_chunk_scan(const T *__restrict__ x, const T *__restrict__ B,
-                                                    const T *__restrict__ C,
-                                                    const float *__restrict__ D,
-                                                    const float *__restrict__ s_ws,
-                                                    const float *__restrict__ dt_ws,
-                                                    const T *__restrict__ hin,
-                                                    const int4 *__restrict__ info, int nc, int H,
-                                                    int G, int Q, float *__restrict__ y) {
-  typedef ScanCfg<T, P, N> K;
+// NV: 16-byte vectors per thread per staged phase; LB: block size bound.
+template <typename T, int P, int N, int HB, int SPLIT, int NV, int LB>
+__global__ __launch_bounds__(LB) void k_chunk_scan(
+    const T *__restrict__ x, const T *__restrict__ B, const T *__restrict__ C,
+    const float *__restrict__ D, const float *__restrict__ s_ws, const float *__restrict__ dt_ws,
+    const T *__restrict__ hin, const int4 *__restrict__ info, int nc, int H, int G, int Q,
+    float *__restrict__ y) {
+  typedef ScanCfg<T, P, N, HB> K;
   constexpr int KS = K::KS, NK = K::NK, XP = K::XP, BP = K::BP, HP = K::HP;
   constexpr int NPT = P / 16;
-  constexpr int TPW = CLS == 2 ? 2 : 1;
-  const ChunkHead ch = xcd_chunk_head(H);
-  const int c = ch.c, hd = ch.h;
+  const ChunkHead ch = xcd_chunk_head(H / HB * SPLIT);
+  const int c = ch.c, hd0 = (ch.h / SPLIT) * HB, part = ch.h % SPLIT;
   if (c >= nc) return;
   const int4 ci = info[c];
   if (ci.z <= 0) return;
   const int len = ci.z;
-  const int g = (hd * G) / H;
-  const int JP = Q < K::jp(CLS) ? Q : K::jp(CLS);
+  const int g = (hd0 * G) / H;  // every head of the workgroup reads this group
+  const int JP = Q < K::JP ? Q : K::JP;
   const int nw = blockDim.x >> 6, lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = lane >> 4, col = lane & 15;
+  int tile = wave;
+  if (SPLIT == 2) {
+    const int k = wave < nw / 2 ? wave : 3 * nw / 2 - 1 - wave;
+    tile = 2 * k + (part ^ (k & 1));
+  }
+  const int t0 = 16 * tile;  // first row of the wave's tile (wave-uniform)
 
   extern __shared__ __align__(16) char smem[];
-  float *s_l = reinterpret_cast<float *>(smem);
-  float *dt_l = s_l + Q;
-  float *u_l = dt_l + Q;                    // 2^(s_ref(j) - s_j) dt_j, s_ref(j) = s at the end of j's 32-block
-  T *Hs = reinterpret_cast<T *>(u_l + Q);   // [NK][HP]
-  T *buf0 = Hs + NK * HP;                   // [JP][BP] then [JP][XP]
-  T *buf1 = buf0 + JP * (BP + XP);
+  float *s_l = reinterpret_cast<float *>(smem);  // [HB][Q]
+  float *dt_l = s_l + HB * Q;                     // [HB][Q]
+  float *u_l = dt_l + HB * Q;  // [HB][Q] 2^(s_ref(j) - s_j) dt_j, s_ref(j) = s at the end of j's 32-block
+  T *region = reinterpret_cast<T *>(u_l + HB * Q);
+  T *Hs = region;              // [HB][NK][HP] first
+  T *Bs = region;              // then [JP][BP] ...
+  T *Xs = region + JP * BP;    // ... and HB x [JP][XP]
 
-  const size_t csh = (size_t)c * H + hd;
-  const T *xs = x + ((size_t)ci.y * H + hd) * P;
+  const size_t csh = (size_t)c * H + hd0;  // workspace index of (chunk, first head)
+  const T *xs = x + ((size_t)ci.y * H + hd0) * P;
   const T *bs = B + ((size_t)ci.y * G + g) * N;
   const size_t xstride = (size_t)H * P, bstride = (size_t)G * N;
 
   // ---- prologue: every load of the first phase is issued before any wait
-  int t0[TPW];  // first row of each tile (wave-uniform)
-  t0[0] = 16 * wave;
-  if (TPW == 2) t0[1] = 16 * (2 * nw - 1 - wave);
   const T *Cg = C + ((size_t)ci.y * G + g) * N;
-  Frag<T> cf[TPW][KS];
-  float si[TPW];
-#pragma unroll
-  for (int k = 0; k < TPW; ++k) {
-    const int i = t0[k] + col;
+  Frag<T> cf[KS];
+  float si[HB];
+  {
+    const int i = t0 + col;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int n8 = ks * 32 + 8 * grp;
-      cf[k][ks] = (i < len && n8 < N) ? frag_global(Cg + (size_t)i * bstride + n8) : frag_zero<T>();
+      cf[ks] = (i < len && n8 < N) ? frag_global(Cg + (size_t)i * bstride + n8) : frag_zero<T>();
     }
-    si[k] = s_ws[csh * Q + i];
+#pragma unroll
+    for (int e = 0; e < HB; ++e) si[e] = s_ws[(csh + e) * Q + i];
   }
-  PhaseRegs<T, P, N, K::maxv(CLS)> pr;
+  PhaseRegs<T, P, N, HB, NV> pr;
   pr.load(bs, bstride, xs, xstride, JP, len);
-  for (int i = threadIdx.x; i < Q; i += blockDim.x) {
-    const float sv = s_ws[csh * Q + i], dv = dt_ws[csh * Q + i];
-    s_l[i] = sv;
-    dt_l[i] = dv;
-    u_l[i] = __builtin_amdgcn_exp2f(fminf(s_ws[csh * Q + (i | 31)] - sv, 0.f)) * dv;
+  for (int idx = threadIdx.x; idx < HB * Q; idx += blockDim.x) {
+    const int e = idx / Q, i = idx % Q;
+    const size_t base = (csh + e) * Q;
+    const float sv = s_ws[base + i], dv = dt_ws[base + i];
+    s_l[idx] = sv;
+    dt_l[idx] = dv;
+    u_l[idx] = __builtin_amdgcn_exp2f(fminf(s_ws[base + (i | 31)] - sv, 0.f)) * dv;
   }
-  stage_rows<T, P, P>(Hs, HP, hin + csh * (size_t)(N * P), (size_t)P, 0, NK, N, nullptr);
-  pr.store(buf0, buf0 + JP * BP, JP);
+#pragma unroll
+  for (int e = 0; e < HB; ++e)
+    stage_rows<T, P, P>(Hs + e * NK * HP, HP, hin + (csh + e) * (size_t)(N * P), (size_t)P, 0,
+                        NK, N, nullptr);
   __syncthreads();
 
-  // ---- state entering the chunk: Y^T = 2^(s_i) H_in^T C^T (each H_in fragment
-  // feeds every tile of the wave)
-  f4 acc[TPW][NPT];
+  // ---- state entering the chunk: Y^T = 2^(s_i) H_in^T C^T
+  const bool live = t0 < len;  // wave-uniform
+  f4 acc[HB][NPT];
 #pragma unroll
-  for (int k = 0; k < TPW; ++k)
+  for (int e = 0; e < HB; ++e)
 #pragma unroll
-    for (int pt = 0; pt < NPT; ++pt) acc[k][pt] = zero4();
+    for (int pt = 0; pt < NPT; ++pt) acc[e][pt] = zero4();
+  if (live) {
 #pragma unroll
-  for (int pt = 0; pt < NPT; ++pt) {
+    for (int e = 0; e < HB; ++e) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const Frag<T> a = frag_kmaj(Hs, HP, pt * 16, ks * 32 + 8 * grp, ks * 32 + 8 * grp + 4);
+      for (int pt = 0; pt < NPT; ++pt) {
 #pragma unroll
-      for (int k = 0; k < TPW; ++k)
-        if (t0[k] < len) mma(acc[k][pt], a, cf[k][ks]);
+        for (int ks = 0; ks < KS; ++ks) {
+          const Frag<T> a =
+              frag_kmaj(Hs + e * NK * HP, HP, pt * 16, ks * 32 + 8 * grp, ks * 32 + 8 * grp + 4);
+          mma(acc[e][pt], a, cf[ks]);
+        }
+      }
+      const float ei = __builtin_amdgcn_exp2f(fminf(si[e], 0.f));
+#pragma unroll
+      for (int pt = 0; pt < NPT; ++pt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[e][pt][r] *= ei;
     }
   }
-#pragma unroll
-  for (int k = 0; k < TPW; ++k) {
-    const float ei = __builtin_amdgcn_exp2f(fminf(si[k], 0.f));
-#pragma unroll
-    for (int pt = 0; pt < NPT; ++pt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[k][pt][r] *= ei;
-  }
+  __syncthreads();  // the H_in tiles are no longer read: the space takes the first phase
+  pr.store(Bs, Xs, JP);
+  __syncthreads();
 
-  // last row any tile of this wave needs
-  int wave_last = 0;
+  const int tile_last = min(t0 + 15, len - 1);
+  float dv[HB];
 #pragma unroll
-  for (int k = 0; k < TPW; ++k) wave_last = max(wave_last, t0[k] + 15);
-  wave_last = min(wave_last, len - 1);
-
-  const float dv = D[hd];
-  constexpr bool PIPE = TPW == 1;
-  int cur = 0;
+  for (int e = 0; e < HB; ++e) dv[e] = D[hd0 + e];
   for (int ph = 0; ph < len; ph += JP) {  // phases past the chunk length add nothing
-    T *Bs = cur ? buf1 : buf0;
-    T *Xs = Bs + JP * BP;
     const bool more = ph + JP < len;
-    if (!PIPE && ph > 0) {  // stage this phase between two barriers
-      pr.load(bs + (size_t)ph * bstride, bstride, xs + (size_t)ph * xstride, xstride, JP,
-              len - ph);
-      pr.store(Bs, Xs, JP);
-      __syncthreads();
-    }
-    if (PIPE && more)  // next phase's rows travel while this phase computes
+    if (more)  // next phase's rows travel while this phase computes
       pr.load(bs + (size_t)(ph + JP) * bstride, bstride, xs + (size_t)(ph + JP) * xstride,
               xstride, JP, len - ph - JP);
-    // skip term D x_i for tiles whose rows are staged in this phase
+    const bool mine = live && t0 >= ph && t0 < ph + JP;  // the tile's own rows are staged
+    if (mine) {  // skip term D x_i
 #pragma unroll
-    for (int k = 0; k < TPW; ++k) {
-      if (t0[k] >= ph && t0[k] < ph + JP && t0[k] < len) {
+      for (int e = 0; e < HB; ++e) {
 #pragma unroll
         for (int pt = 0; pt < NPT; ++pt) {
-          const f4 xv = ld4f(Xs + (t0[k] + col - ph) * XP + pt * 16 + 4 * grp);
+          const f4 xv = ld4f(Xs + ((size_t)e * JP + t0 + col - ph) * XP + pt * 16 + 4 * grp);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[k][pt][r] += dv * xv[r];
+          for (int r = 0; r < 4; ++r) acc[e][pt][r] += dv[e] * xv[r];
         }
       }
     }
-    const int jend = min(ph + JP, wave_last + 1);
+    const int jend = live ? min(ph + JP, tile_last + 1) : ph;
     for (int jb = ph; jb < jend; jb += 32) {
       const int jl = jb - ph;
-      // G^T = B C^T for every tile the block reaches (tile k needs jb <= t0[k] + 15)
-      f4 g0[TPW], g1[TPW];
-#pragma unroll
-      for (int k = 0; k < TPW; ++k) g0[k] = g1[k] = zero4();
+      // G^T = B C^T for this j-block, shared by the HB heads
+      f4 g0 = zero4(), g1 = zero4();
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const Frag<T> b0 = frag_rowk(Bs, BP, jl + col, ks * 32 + 8 * grp);
         const Frag<T> b1 = frag_rowk(Bs, BP, jl + 16 + col, ks * 32 + 8 * grp);
-#pragma unroll
-        for (int k = 0; k < TPW; ++k) {
-          if (jb <= t0[k] + 15) {
-            mma(g0[k], b0, cf[k][ks]);
-            mma(g1[k], b1, cf[k][ks]);
-          }
-        }
+        mma(g0, b0, cf[ks]);
+        mma(g1, b1, cf[ks]);
       }
-      Frag<T> mf[TPW];
+      const bool diag = jb + 31 >= t0;  // the block holds the tile's rows
 #pragma unroll
-      for (int k = 0; k < TPW; ++k) {
-        if (jb > t0[k] + 15) continue;
+      for (int e = 0; e < HB; ++e) {
+        const float *se = s_l + e * Q, *de = dt_l + e * Q, *ue = u_l + e * Q;
         float m[8];
-        if (jb + 31 < t0[k]) {
+        if (!diag) {
           // block entirely before the tile: no mask, and the decay factors through
           // the block end, 2^(s_i - s_ref) * [2^(s_ref - s_j) dt_j], both <= 1
-          const float v = __builtin_amdgcn_exp2f(fminf(si[k] - s_l[jb + 31], 0.f));
-          const f4 u0 = ld4(u_l + jb + 4 * grp), u1 = ld4(u_l + jb + 16 + 4 * grp);
+          const float v = __builtin_amdgcn_exp2f(fminf(si[e] - se[jb + 31], 0.f));
+          const f4 u0 = ld4(ue + jb + 4 * grp), u1 = ld4(ue + jb + 16 + 4 * grp);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            m[r] = g0[k][r] * u0[r] * v;
-            m[4 + r] = g1[k][r] * u1[r] * v;
+            m[r] = g0[r] * u0[r] * v;
+            m[4 + r] = g1[r] * u1[r] * v;
           }
-        } else {  // block holding the tile's rows: causal mask, exact decay
-          const int i = t0[k] + col;
-          const f4 sj0 = ld4(s_l + jb + 4 * grp), sj1 = ld4(s_l + jb + 16 + 4 * grp);
-          const f4 dj0 = ld4(dt_l + jb + 4 * grp), dj1 = ld4(dt_l + jb + 16 + 4 * grp);
+        } else {  // causal mask, exact decay
+          const int i = t0 + col;
+          const f4 sj0 = ld4(se + jb + 4 * grp), sj1 = ld4(se + jb + 16 + 4 * grp);
+          const f4 dj0 = ld4(de + jb + 4 * grp), dj1 = ld4(de + jb + 16 + 4 * grp);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int j0 = jb + 4 * grp + r, j1 = j0 + 16;
             // every argument is clamped to <= 0, so each product is finite and the
             // mask can be a multiply by 0 or 1 (no branch)
-            const float e0 = __builtin_amdgcn_exp2f(fminf(si[k] - sj0[r], 0.f)) * dj0[r];
-            const float e1 = __builtin_amdgcn_exp2f(fminf(si[k] - sj1[r], 0.f)) * dj1[r];
-            m[r] = g0[k][r] * e0 * (j0 <= i ? 1.f : 0.f);
-            m[4 + r] = g1[k][r] * e1 * (j1 <= i ? 1.f : 0.f);
+            const float e0 = __builtin_amdgcn_exp2f(fminf(si[e] - sj0[r], 0.f)) * dj0[r];
+            const float e1 = __builtin_amdgcn_exp2f(fminf(si[e] - sj1[r], 0.f)) * dj1[r];
+            m[r] = g0[r] * e0 * (j0 <= i ? 1.f : 0.f);
+            m[4 + r] = g1[r] * e1 * (j1 <= i ? 1.f : 0.f);
           }
         }
-        mf[k] = frag_from_f32(m, T());
-      }
-      // Y^T += X^T M^T, each X^T fragment feeding every tile the block reaches
+        const Frag<T> mf = frag_from_f32(m, T());
+        // Y^T += X^T M^T
+        const T *Xe = Xs + (size_t)e * JP * XP;
 #pragma unroll
-      for (int pt = 0; pt < NPT; ++pt) {
-        const Frag<T> a = frag_kmaj(Xs, XP, pt * 16, jl + 4 * grp, jl + 16 + 4 * grp);
-#pragma unroll
-        for (int k = 0; k < TPW; ++k)
-          if (jb <= t0[k] + 15) mma(acc[k][pt], a, mf[k]);
-      }
-    }
-    // tiles whose rows end in this phase have seen every j <= i: store them now
-#pragma unroll
-    for (int k = 0; k < TPW; ++k) {
-      const int i = t0[k] + col;
-      if (t0[k] >= ph && t0[k] < ph + JP && i < len) {
-        const size_t row = ((size_t)ci.y + i) * H + hd;
-#pragma unroll
-        for (int pt = 0; pt < NPT; ++pt) st4(y + row * P + pt * 16 + 4 * grp, acc[k][pt]);
+        for (int pt = 0; pt < NPT; ++pt) {
+          const Frag<T> a = frag_kmaj(Xe, XP, pt * 16, jl + 4 * grp, jl + 16 + 4 * grp);
+          mma(acc[e][pt], a, mf);
+        }
       }
     }
-    if (PIPE && more) {
-      T *Bn = cur ? buf0 : buf1;
-      pr.store(Bn, Bn + JP * BP, JP);
+    if (mine) {  // the tile has seen every j <= i: store it now
+      const int i = t0 + col;
+      if (i < len) {
+#pragma unroll
+        for (int e = 0; e < HB; ++e) {
+          const size_t row = ((size_t)ci.y + i) * H + hd0 + e;
+#pragma unroll
+          for (int pt = 0; pt < NPT; ++pt) st4(y + row * P + pt * 16 + 4 * grp, acc[e][pt]);
+        }
+      }
     }
-    __syncthreads();  // PIPE: the next phase's buffer is complete; both: this one is free
-    if (PIPE) cur ^= 1;
+    if (more) {
+      __syncthreads();  // everyone is done with this phase's rows
+      pr.store(Bs, Xs, JP);
+      __syncthreads();
+    }
   }
+}
+
+// The chunk-scan instance for a chunk-length class: THREADS = 64 * Q/16/SPLIT,
+// JPE = staged rows per phase, min(Q, 64).
+template <typename T, int P, int N, int HB, int SPLIT, int THREADS, int JPE>
+static const void *scan_kernel() {
+  constexpr int NV = ScanCfg<T, P, N, HB>::nvec(JPE, THREADS);
+  return (const void *)k_chunk_scan<T, P, N, HB, SPLIT, NV, THREADS <= 512 ? 512 : 1024>;
+}
+
+template <typename T, int P, int N, int HB>
+static const void *scan_kernel_for(int Q) {
+  switch (Q) {
+    case 32: return scan_kernel<T, P, N, HB, 1, 128, 32>();
+    case 64: return scan_kernel<T, P, N, HB, 1, 256, 64>();
+    case 128: return scan_kernel<T, P, N, HB, 1, 512, 64>();
+    case 256: return scan_kernel<T, P, N, HB, 1, 1024, 64>();
+  }
+  return nullptr;
 }
 
 // ------------------------------------------------------------------ launch
@@ -688,20 +691,32 @@ static hipError_t run_prefill(const PrefillArgs &a, unsigned stages) {
     if (e != hipSuccess) return e;
   }
   if ((stages & 8u) && nc > 0) {
-    typedef ScanCfg<T, P, N> K;
-    // block class: Q <= 128, Q = 256 (one tile per wave), Q = 512 (two tiles per wave)
-    const int cls = a.Q <= 128 ? 0 : a.Q == 256 ? 1 : 2;
-    const int jp = a.Q < K::jp(cls) ? a.Q : K::jp(cls);
-    const size_t lds = K::lds_bytes(jp, a.Q);
-    const int threads = 64 * (a.Q / 16) / (cls == 2 ? 2 : 1);
-    auto kern = cls == 0 ? k_chunk_scan<T, P, N, 0>
-                         : cls == 1 ? k_chunk_scan<T, P, N, 1> : k_chunk_scan<T, P, N, 2>;
-    hipError_t e = set_lds_limit((const void *)kern);
+    // Q <= 256: one workgroup of Q/16 waves per chunk; Q = 512: two of 16 waves.
+    // Two heads per workgroup when the group has an even number of heads and Q <= 256.
+    const int split = a.Q == 512 ? 2 : 1;
+    const int hb = (split == 1 && (a.H / a.G) % 2 == 0) ? 2 : 1;
+    const int threads = 64 * (a.Q / 16) / split;
+    const void *kern;
+    size_t lds;
+    if (hb == 2) {
+      typedef ScanCfg<T, P, N, 2> K;
+      lds = K::lds_bytes(a.Q < K::JP ? a.Q : K::JP, a.Q);
+      kern = scan_kernel_for<T, P, N, 2>(a.Q);
+    } else {
+      typedef ScanCfg<T, P, N, 1> K;
+      lds = K::lds_bytes(a.Q < K::JP ? a.Q : K::JP, a.Q);
+      kern = split == 2 ? scan_kernel<T, P, N, 1, 2, 1024, 64>() : scan_kernel_for<T, P, N, 1>(a.Q);
+    }
+    if (!kern) return hipErrorInvalidValue;
+    hipError_t e = set_lds_limit(kern);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(xcd_grid(nc, a.H)), dim3(threads), lds, st, (const T *)a.x,
-                       (const T *)a.B, (const T *)a.C, a.D, s_ws, dt_ws, (const T *)hin, info,
-                       nc, a.H, a.G, a.Q, a.y);
-    e = hipGetLastError();
+    const T *xp = (const T *)a.x, *bp = (const T *)a.B, *cp = (const T *)a.C;
+    const T *hp = (const T *)hin;
+    int nc_ = nc, H_ = a.H, G_ = a.G, Q_ = a.Q;
+    const float *Dp = a.D;
+    float *yp = a.y;
+    void *args[] = {&xp, &bp, &cp, &Dp, &s_ws, &dt_ws, &hp, &info, &nc_, &H_, &G_, &Q_, &yp};
+    e = hipLaunchKernel(kern, dim3(xcd_grid(nc, a.H / hb * split)), dim3(threads), args, lds, st);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
