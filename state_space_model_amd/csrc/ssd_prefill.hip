@@ -322,104 +322,86 @@ __global__ __launch_bounds__(256) void k_state_pass(const float *__restrict__ S,
 }
 
 // ------------------------------------------------------------ K4 chunk scan
-// One workgroup per (chunk, HB heads of one B/C group, part z of SPLIT), one
-// wave per 16-token output tile.  Q <= 256: SPLIT 1, Q/16 waves, two heads per
-// workgroup when the group has an even number of heads.  Q = 512: SPLIT 2, 16
+// One workgroup per (chunk, head, part z of SPLIT), one wave per 16-token
+// output tile.  Q <= 128: SPLIT 1, Q/16 waves.  Q >= 256: SPLIT 2, Q/32
 // waves: part z owns tiles t_k = 2k + (z ^ (k & 1)), whose causal work is k + 1
 // j-blocks in both parts, and wave w takes k = w for w < NW/2, else
-// k = 3NW/2 - 1 - w, so the waves sharing a SIMD (w, w + 4, ...) carry equal
-// work.
-// Per output tile and head (all accumulation in float32):
+// k = 3NW/2 - 1 - w, so the waves sharing a SIMD carry equal work.  At Q = 256
+// a part has 8 waves and stages 128 rows per phase (under 80 KB of LDS), so two
+// workgroups share a CU and one loads while the other computes.
+// Per output tile (all accumulation in float32):
 //   Y^T[p][i]  = 2^(s_i) (H_in^T C^T)[p][i]             k = n    (A: H_in tile, transpose read)
 //             += sum_j X^T[p][j] M^T[j][i]              k = j    (A: X tile, transpose read)
 //             += D x_i                                  (while the tile's own rows are staged)
 //   M^T[j][i]  = (B C^T)[j][i] 2^(s_i - s_j) dt_j  (j <= i)      k = n
-// B C^T depends only on the chunk and group, so it is computed once per
-// j-block and applied to every head of the workgroup; the C fragments and the
-// staged B rows are likewise shared.  The two 16x16 results of B C^T for rows
-// jb..jb+15 and jb+16..jb+31 are fed straight back as the B operand (paired k
-// map); X^T is read with the same pairing.  LDS holds the H_in tiles first and
-// then, in the same space, one phase of JP staged B/X rows; the next phase's
-// rows are loaded into registers while the current one computes.
-template <typename T, int P, int N, int HB> struct ScanCfg {
+// The two 16x16 results of B C^T for rows jb..jb+15 and jb+16..jb+31 are fed
+// straight back as the B operand (paired k map); X^T is read with the same
+// pairing.  Staging uses the direct global->LDS load (16 bytes per lane, lane
+// l writing base + 16 l): H_in and the first JP rows of B and X are requested
+// together with no staging registers, so each phase of JP rows costs one memory
+// round trip.
+__device__ __attribute__((aligned(16))) unsigned int g_zero16[4];  // zero source for padding
+
+// Fill a padded LDS tile of `rows` rows: each row has DATA 16-byte vectors
+// from `src` (row r at src + r * stride) followed by pad vectors up to SPR
+// slots; rows at or beyond `valid` are zero.  The tile spans a whole number
+// of 64-slot wave requests (the caller sizes it with tile_slots()).
+template <typename T, int SPR, int DATA>
+__device__ __forceinline__ void dma_tile(T *tile, const T *__restrict__ src, size_t stride,
+                                         int rows, int valid, int wave, int nw) {
+  constexpr int VN = 16 / sizeof(T);
+  const int total = rows * SPR;
+  const int lane = threadIdx.x & 63;
+  for (int base = wave * 64; base < total; base += nw * 64) {
+    const int s = base + lane, r = s / SPR, v = s % SPR;
+    const void *g = (s < total && r < valid && v < DATA) ? (const void *)(src + r * stride + v * VN)
+                                                       : (const void *)g_zero16;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
+                                     (__attribute__((address_space(3))) void *)(tile + base * VN),
+                                     16, 0, 0);
+  }
+}
+__host__ __device__ constexpr int tile_slots(int rows, int spr) { return (rows * spr + 63) / 64 * 64; }
+
+template <typename T, int P, int N> struct ScanCfg {
   static constexpr int NK = N < 32 ? 32 : N;  // contraction over n, padded to the k-step
   static constexpr int KS = NK / 32;
-  static constexpr int XP = P + kTrPad, BP = NK + row_pad<T>(), HP = P + kTrPad;
   static constexpr int VN = 16 / sizeof(T);
-  static constexpr int VB = NK / VN, VX = P / VN;  // 16-byte vectors per staged row
-  static constexpr int JP = 64;                    // staged rows per phase (Q >= 64)
-  static constexpr size_t phase_elems(int jp) { return (size_t)jp * (BP + HB * XP); }
-  static constexpr size_t hs_elems() { return (size_t)HB * NK * HP; }
+  static constexpr int XP = P + kTrPad, BP = NK + row_pad<T>(), HP = P + kTrPad;
+  static constexpr int XS = XP / VN, BS = BP / VN, HS = HP / VN;  // 16-byte slots per row
+  static constexpr int XD = P / VN, BD = N / VN;                   // data slots per row
   static constexpr size_t lds_bytes(int jp, int q) {
-    return (phase_elems(jp) > hs_elems() ? phase_elems(jp) : hs_elems()) * sizeof(T) +
-           12 * (size_t)HB * q;
+    return (size_t)(tile_slots(NK, HS) + tile_slots(jp, BS) + tile_slots(jp, XS)) * 16 +
+           12 * (size_t)q;
   }
-  // 16-byte vectors each thread stages per phase
-  static constexpr int nvec(int jp, int threads) {
-    return (int)(((size_t)jp * (VB + HB * VX) + threads - 1) / threads);
-  }
-};
-
-// Registers holding one phase of staged rows (B rows, then X rows of each head).
-template <typename T, int P, int N, int HB, int MAXV> struct PhaseRegs {
-  typedef ScanCfg<T, P, N, HB> K;
-  typedef typename Vec16<T>::type V;
-  V v[MAXV];
-
-  __device__ __forceinline__ void load(const T *__restrict__ bs, size_t bstride,
-                                       const T *__restrict__ xs, size_t xstride, int jp,
-                                       int rows_left) {
-    const int nb = jp * K::VB, nx = jp * K::VX, total = nb + HB * nx;
-#pragma unroll
-    for (int k = 0; k < MAXV; ++k) {
-      const int idx = threadIdx.x + k * blockDim.x;
-      v[k] = vzero<V>();
-      if (idx < nb) {
-        const int r = idx / K::VB, c = idx % K::VB;
-        if (r < rows_left && c * K::VN < N) v[k] = *reinterpret_cast<const V *>(bs + r * bstride + c * K::VN);
-      } else if (idx < total) {
-        const int e = (idx - nb) / nx, rem = (idx - nb) % nx;
-        const int r = rem / K::VX, c = rem % K::VX;
-        if (r < rows_left) v[k] = *reinterpret_cast<const V *>(xs + r * xstride + e * P + c * K::VN);
-      }
-    }
-  }
-  // Bs: [JP][BP]; Xs: HB tiles of [JP][XP]
-  __device__ __forceinline__ void store(T *Bs, T *Xs, int jp) const {
-    const int nb = jp * K::VB, nx = jp * K::VX, total = nb + HB * nx;
-#pragma unroll
-    for (int k = 0; k < MAXV; ++k) {
-      const int idx = threadIdx.x + k * blockDim.x;
-      if (idx < nb) {
-        const int r = idx / K::VB, c = idx % K::VB;
-        *reinterpret_cast<V *>(Bs + r * K::BP + c * K::VN) = v[k];
-      } else if (idx < total) {
-        const int e = (idx - nb) / nx, rem = (idx - nb) % nx;
-        const int r = rem / K::VX, c = rem % K::VX;
-        *reinterpret_cast<V *>(Xs + ((size_t)e * jp + r) * K::XP + c * K::VN) = v[k];
-      }
-    }
+  // staged rows per phase for chunk length q and `threads`: up to 128 rows in
+  // blocks of at most 512 threads (two workgroups per CU), up to 256 rows
+  // otherwise, halved until the LDS fits
+  static int jp(int q, int threads) {
+    const int lim = threads <= 512 ? 128 : 256;
+    int j = q < lim ? q : lim;
+    const size_t cap = threads <= 512 ? 80 * 1024 : 160 * 1024;
+    while (j > 32 && lds_bytes(j, q) > cap) j /= 2;
+    return j;
   }
 };
 
-// NV: 16-byte vectors per thread per staged phase; LB: block size bound.
-template <typename T, int P, int N, int HB, int SPLIT, int NV, int LB>
-__global__ __launch_bounds__(LB) void k_chunk_scan(
+template <typename T, int P, int N, int SPLIT>
+__global__ __launch_bounds__(1024) void k_chunk_scan(
     const T *__restrict__ x, const T *__restrict__ B, const T *__restrict__ C,
     const float *__restrict__ D, const float *__restrict__ s_ws, const float *__restrict__ dt_ws,
     const T *__restrict__ hin, const int4 *__restrict__ info, int nc, int H, int G, int Q,
-    float *__restrict__ y) {
-  typedef ScanCfg<T, P, N, HB> K;
+    int JP, float *__restrict__ y) {
+  typedef ScanCfg<T, P, N> K;
   constexpr int KS = K::KS, NK = K::NK, XP = K::XP, BP = K::BP, HP = K::HP;
   constexpr int NPT = P / 16;
-  const ChunkHead ch = xcd_chunk_head(H / HB * SPLIT);
-  const int c = ch.c, hd0 = (ch.h / SPLIT) * HB, part = ch.h % SPLIT;
+  const ChunkHead ch = xcd_chunk_head(H * SPLIT);
+  const int c = ch.c, hd = ch.h / SPLIT, part = ch.h % SPLIT;
   if (c >= nc) return;
   const int4 ci = info[c];
   if (ci.z <= 0) return;
   const int len = ci.z;
-  const int g = (hd0 * G) / H;  // every head of the workgroup reads this group
-  const int JP = Q < K::JP ? Q : K::JP;
+  const int g = (hd * G) / H;
   const int nw = blockDim.x >> 6, lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = lane >> 4, col = lane & 15;
@@ -431,105 +413,84 @@ __global__ __launch_bounds__(LB) void k_chunk_scan(
   const int t0 = 16 * tile;  // first row of the wave's tile (wave-uniform)
 
   extern __shared__ __align__(16) char smem[];
-  float *s_l = reinterpret_cast<float *>(smem);  // [HB][Q]
-  float *dt_l = s_l + HB * Q;                     // [HB][Q]
-  float *u_l = dt_l + HB * Q;  // [HB][Q] 2^(s_ref(j) - s_j) dt_j, s_ref(j) = s at the end of j's 32-block
-  T *region = reinterpret_cast<T *>(u_l + HB * Q);
-  T *Hs = region;              // [HB][NK][HP] first
-  T *Bs = region;              // then [JP][BP] ...
-  T *Xs = region + JP * BP;    // ... and HB x [JP][XP]
+  T *Hs = reinterpret_cast<T *>(smem);                    // [NK][HP]
+  T *Bs = Hs + tile_slots(NK, K::HS) * K::VN;             // [JP][BP]
+  T *Xs = Bs + tile_slots(JP, K::BS) * K::VN;             // [JP][XP]
+  float *s_l = reinterpret_cast<float *>(Xs + tile_slots(JP, K::XS) * K::VN);  // [Q]
+  float *dt_l = s_l + Q;                                                       // [Q]
+  float *u_l = dt_l + Q;  // [Q] 2^(s_ref(j) - s_j) dt_j, s_ref(j) = s at the end of j's 32-block
 
-  const size_t csh = (size_t)c * H + hd0;  // workspace index of (chunk, first head)
-  const T *xs = x + ((size_t)ci.y * H + hd0) * P;
+  const size_t csh = (size_t)c * H + hd;
+  const T *xs = x + ((size_t)ci.y * H + hd) * P;
   const T *bs = B + ((size_t)ci.y * G + g) * N;
   const size_t xstride = (size_t)H * P, bstride = (size_t)G * N;
 
-  // ---- prologue: every load of the first phase is issued before any wait
+  // ---- prologue: H_in, the first phase of B/X, C fragments and decays in flight together
+  dma_tile<T, K::HS, K::XD>(Hs, hin + csh * (size_t)(N * P), (size_t)P, NK, N, wave, nw);
+  dma_tile<T, K::BS, K::BD>(Bs, bs, bstride, JP, len, wave, nw);
+  dma_tile<T, K::XS, K::XD>(Xs, xs, xstride, JP, len, wave, nw);
   const T *Cg = C + ((size_t)ci.y * G + g) * N;
   Frag<T> cf[KS];
-  float si[HB];
-  {
-    const int i = t0 + col;
+  const int i = t0 + col;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int n8 = ks * 32 + 8 * grp;
-      cf[ks] = (i < len && n8 < N) ? frag_global(Cg + (size_t)i * bstride + n8) : frag_zero<T>();
-    }
-#pragma unroll
-    for (int e = 0; e < HB; ++e) si[e] = s_ws[(csh + e) * Q + i];
+  for (int ks = 0; ks < KS; ++ks) {
+    const int n8 = ks * 32 + 8 * grp;
+    cf[ks] = (i < len && n8 < N) ? frag_global(Cg + (size_t)i * bstride + n8) : frag_zero<T>();
   }
-  PhaseRegs<T, P, N, HB, NV> pr;
-  pr.load(bs, bstride, xs, xstride, JP, len);
-  for (int idx = threadIdx.x; idx < HB * Q; idx += blockDim.x) {
-    const int e = idx / Q, i = idx % Q;
-    const size_t base = (csh + e) * Q;
-    const float sv = s_ws[base + i], dv = dt_ws[base + i];
-    s_l[idx] = sv;
-    dt_l[idx] = dv;
-    u_l[idx] = __builtin_amdgcn_exp2f(fminf(s_ws[base + (i | 31)] - sv, 0.f)) * dv;
+  const float si = s_ws[csh * Q + i];
+  for (int j = threadIdx.x; j < Q; j += blockDim.x) {
+    const float sv = s_ws[csh * Q + j], dv = dt_ws[csh * Q + j];
+    s_l[j] = sv;
+    dt_l[j] = dv;
+    u_l[j] = __builtin_amdgcn_exp2f(fminf(s_ws[csh * Q + (j | 31)] - sv, 0.f)) * dv;
   }
-#pragma unroll
-  for (int e = 0; e < HB; ++e)
-    stage_rows<T, P, P>(Hs + e * NK * HP, HP, hin + (csh + e) * (size_t)(N * P), (size_t)P, 0,
-                        NK, N, nullptr);
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's direct-to-LDS loads have landed
   __syncthreads();
 
   // ---- state entering the chunk: Y^T = 2^(s_i) H_in^T C^T
   const bool live = t0 < len;  // wave-uniform
-  f4 acc[HB][NPT];
+  f4 acc[NPT];
 #pragma unroll
-  for (int e = 0; e < HB; ++e)
-#pragma unroll
-    for (int pt = 0; pt < NPT; ++pt) acc[e][pt] = zero4();
+  for (int pt = 0; pt < NPT; ++pt) acc[pt] = zero4();
   if (live) {
 #pragma unroll
-    for (int e = 0; e < HB; ++e) {
+    for (int pt = 0; pt < NPT; ++pt) {
 #pragma unroll
-      for (int pt = 0; pt < NPT; ++pt) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const Frag<T> a =
-              frag_kmaj(Hs + e * NK * HP, HP, pt * 16, ks * 32 + 8 * grp, ks * 32 + 8 * grp + 4);
-          mma(acc[e][pt], a, cf[ks]);
-        }
+      for (int ks = 0; ks < KS; ++ks) {
+        const Frag<T> a = frag_kmaj(Hs, HP, pt * 16, ks * 32 + 8 * grp, ks * 32 + 8 * grp + 4);
+        mma(acc[pt], a, cf[ks]);
       }
-      const float ei = __builtin_amdgcn_exp2f(fminf(si[e], 0.f));
-#pragma unroll
-      for (int pt = 0; pt < NPT; ++pt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[e][pt][r] *= ei;
     }
+    const float ei = __builtin_amdgcn_exp2f(fminf(si, 0.f));
+#pragma unroll
+    for (int pt = 0; pt < NPT; ++pt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[pt][r] *= ei;
   }
-  __syncthreads();  // the H_in tiles are no longer read: the space takes the first phase
-  pr.store(Bs, Xs, JP);
-  __syncthreads();
 
   const int tile_last = min(t0 + 15, len - 1);
-  float dv[HB];
-#pragma unroll
-  for (int e = 0; e < HB; ++e) dv[e] = D[hd0 + e];
+  const float dv = D[hd];
   for (int ph = 0; ph < len; ph += JP) {  // phases past the chunk length add nothing
-    const bool more = ph + JP < len;
-    if (more)  // next phase's rows travel while this phase computes
-      pr.load(bs + (size_t)(ph + JP) * bstride, bstride, xs + (size_t)(ph + JP) * xstride,
-              xstride, JP, len - ph - JP);
+    if (ph > 0) {  // stage the next JP rows (one round trip)
+      __syncthreads();
+      dma_tile<T, K::BS, K::BD>(Bs, bs + (size_t)ph * bstride, bstride, JP, len - ph, wave, nw);
+      dma_tile<T, K::XS, K::XD>(Xs, xs + (size_t)ph * xstride, xstride, JP, len - ph, wave, nw);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
     const bool mine = live && t0 >= ph && t0 < ph + JP;  // the tile's own rows are staged
     if (mine) {  // skip term D x_i
 #pragma unroll
-      for (int e = 0; e < HB; ++e) {
+      for (int pt = 0; pt < NPT; ++pt) {
+        const f4 xv = ld4f(Xs + (t0 + col - ph) * XP + pt * 16 + 4 * grp);
 #pragma unroll
-        for (int pt = 0; pt < NPT; ++pt) {
-          const f4 xv = ld4f(Xs + ((size_t)e * JP + t0 + col - ph) * XP + pt * 16 + 4 * grp);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[e][pt][r] += dv[e] * xv[r];
-        }
+        for (int r = 0; r < 4; ++r) acc[pt][r] += dv * xv[r];
       }
     }
     const int jend = live ? min(ph + JP, tile_last + 1) : ph;
     for (int jb = ph; jb < jend; jb += 32) {
       const int jl = jb - ph;
-      // G^T = B C^T for this j-block, shared by the HB heads
-      f4 g0 = zero4(), g1 = zero4();
+      f4 g0 = zero4(), g1 = zero4();  // G^T = B C^T for this j-block
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const Frag<T> b0 = frag_rowk(Bs, BP, jl + col, ks * 32 + 8 * grp);
@@ -537,82 +498,44 @@ __global__ __launch_bounds__(LB) void k_chunk_scan(
         mma(g0, b0, cf[ks]);
         mma(g1, b1, cf[ks]);
       }
-      const bool diag = jb + 31 >= t0;  // the block holds the tile's rows
+      float m[8];
+      if (jb + 31 < t0) {
+        // block entirely before the tile: no mask, and the decay factors through
+        // the block end, 2^(s_i - s_ref) * [2^(s_ref - s_j) dt_j], both <= 1
+        const float v = __builtin_amdgcn_exp2f(fminf(si - s_l[jb + 31], 0.f));
+        const f4 u0 = ld4(u_l + jb + 4 * grp), u1 = ld4(u_l + jb + 16 + 4 * grp);
 #pragma unroll
-      for (int e = 0; e < HB; ++e) {
-        const float *se = s_l + e * Q, *de = dt_l + e * Q, *ue = u_l + e * Q;
-        float m[8];
-        if (!diag) {
-          // block entirely before the tile: no mask, and the decay factors through
-          // the block end, 2^(s_i - s_ref) * [2^(s_ref - s_j) dt_j], both <= 1
-          const float v = __builtin_amdgcn_exp2f(fminf(si[e] - se[jb + 31], 0.f));
-          const f4 u0 = ld4(ue + jb + 4 * grp), u1 = ld4(ue + jb + 16 + 4 * grp);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            m[r] = g0[r] * u0[r] * v;
-            m[4 + r] = g1[r] * u1[r] * v;
-          }
-        } else {  // causal mask, exact decay
-          const int i = t0 + col;
-          const f4 sj0 = ld4(se + jb + 4 * grp), sj1 = ld4(se + jb + 16 + 4 * grp);
-          const f4 dj0 = ld4(de + jb + 4 * grp), dj1 = ld4(de + jb + 16 + 4 * grp);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int j0 = jb + 4 * grp + r, j1 = j0 + 16;
-            // every argument is clamped to <= 0, so each product is finite and the
-            // mask can be a multiply by 0 or 1 (no branch)
-            const float e0 = __builtin_amdgcn_exp2f(fminf(si[e] - sj0[r], 0.f)) * dj0[r];
-            const float e1 = __builtin_amdgcn_exp2f(fminf(si[e] - sj1[r], 0.f)) * dj1[r];
-            m[r] = g0[r] * e0 * (j0 <= i ? 1.f : 0.f);
-            m[4 + r] = g1[r] * e1 * (j1 <= i ? 1.f : 0.f);
-          }
+        for (int r = 0; r < 4; ++r) {
+          m[r] = g0[r] * u0[r] * v;
+          m[4 + r] = g1[r] * u1[r] * v;
         }
-        const Frag<T> mf = frag_from_f32(m, T());
-        // Y^T += X^T M^T
-        const T *Xe = Xs + (size_t)e * JP * XP;
+      } else {  // block holding the tile's rows: causal mask, exact decay
+        const f4 sj0 = ld4(s_l + jb + 4 * grp), sj1 = ld4(s_l + jb + 16 + 4 * grp);
+        const f4 dj0 = ld4(dt_l + jb + 4 * grp), dj1 = ld4(dt_l + jb + 16 + 4 * grp);
 #pragma unroll
-        for (int pt = 0; pt < NPT; ++pt) {
-          const Frag<T> a = frag_kmaj(Xe, XP, pt * 16, jl + 4 * grp, jl + 16 + 4 * grp);
-          mma(acc[e][pt], a, mf);
+        for (int r = 0; r < 4; ++r) {
+          const int j0 = jb + 4 * grp + r, j1 = j0 + 16;
+          // every argument is clamped to <= 0, so each product is finite and the
+          // mask can be a multiply by 0 or 1 (no branch)
+          const float e0 = __builtin_amdgcn_exp2f(fminf(si - sj0[r], 0.f)) * dj0[r];
+          const float e1 = __builtin_amdgcn_exp2f(fminf(si - sj1[r], 0.f)) * dj1[r];
+          m[r] = g0[r] * e0 * (j0 <= i ? 1.f : 0.f);
+          m[4 + r] = g1[r] * e1 * (j1 <= i ? 1.f : 0.f);
         }
       }
-    }
-    if (mine) {  // the tile has seen every j <= i: store it now
-      const int i = t0 + col;
-      if (i < len) {
+      const Frag<T> mf = frag_from_f32(m, T());
 #pragma unroll
-        for (int e = 0; e < HB; ++e) {
-          const size_t row = ((size_t)ci.y + i) * H + hd0 + e;
-#pragma unroll
-          for (int pt = 0; pt < NPT; ++pt) st4(y + row * P + pt * 16 + 4 * grp, acc[e][pt]);
-        }
+      for (int pt = 0; pt < NPT; ++pt) {  // Y^T += X^T M^T
+        const Frag<T> a = frag_kmaj(Xs, XP, pt * 16, jl + 4 * grp, jl + 16 + 4 * grp);
+        mma(acc[pt], a, mf);
       }
     }
-    if (more) {
-      __syncthreads();  // everyone is done with this phase's rows
-      pr.store(Bs, Xs, JP);
-      __syncthreads();
+    if (mine && i < len) {  // the tile has seen every j <= i: store it now
+      const size_t row = ((size_t)ci.y + i) * H + hd;
+#pragma unroll
+      for (int pt = 0; pt < NPT; ++pt) st4(y + row * P + pt * 16 + 4 * grp, acc[pt]);
     }
   }
-}
-
-// The chunk-scan instance for a chunk-length class: THREADS = 64 * Q/16/SPLIT,
-// JPE = staged rows per phase, min(Q, 64).
-template <typename T, int P, int N, int HB, int SPLIT, int THREADS, int JPE>
-static const void *scan_kernel() {
-  constexpr int NV = ScanCfg<T, P, N, HB>::nvec(JPE, THREADS);
-  return (const void *)k_chunk_scan<T, P, N, HB, SPLIT, NV, THREADS <= 512 ? 512 : 1024>;
-}
-
-template <typename T, int P, int N, int HB>
-static const void *scan_kernel_for(int Q) {
-  switch (Q) {
-    case 32: return scan_kernel<T, P, N, HB, 1, 128, 32>();
-    case 64: return scan_kernel<T, P, N, HB, 1, 256, 64>();
-    case 128: return scan_kernel<T, P, N, HB, 1, 512, 64>();
-    case 256: return scan_kernel<T, P, N, HB, 1, 1024, 64>();
-  }
-  return nullptr;
 }
 
 // ------------------------------------------------------------------ launch
@@ -691,32 +614,24 @@ static hipError_t run_prefill(const PrefillArgs &a, unsigned stages) {
     if (e != hipSuccess) return e;
   }
   if ((stages & 8u) && nc > 0) {
-    // Q <= 256: one workgroup of Q/16 waves per chunk; Q = 512: two of 16 waves.
-    // Two heads per workgroup when the group has an even number of heads and Q <= 256.
-    const int split = a.Q == 512 ? 2 : 1;
-    const int hb = (split == 1 && (a.H / a.G) % 2 == 0) ? 2 : 1;
+    // Q <= 128: one workgroup of Q/16 waves per (chunk, head); Q >= 256: two of Q/32 waves
+    typedef ScanCfg<T, P, N> K;
+    const int split = a.Q >= 256 ? 2 : 1;
     const int threads = 64 * (a.Q / 16) / split;
-    const void *kern;
-    size_t lds;
-    if (hb == 2) {
-      typedef ScanCfg<T, P, N, 2> K;
-      lds = K::lds_bytes(a.Q < K::JP ? a.Q : K::JP, a.Q);
-      kern = scan_kernel_for<T, P, N, 2>(a.Q);
-    } else {
-      typedef ScanCfg<T, P, N, 1> K;
-      lds = K::lds_bytes(a.Q < K::JP ? a.Q : K::JP, a.Q);
-      kern = split == 2 ? scan_kernel<T, P, N, 1, 2, 1024, 64>() : scan_kernel_for<T, P, N, 1>(a.Q);
-    }
-    if (!kern) return hipErrorInvalidValue;
+    const int jp = K::jp(a.Q, threads);
+    const size_t lds = K::lds_bytes(jp, a.Q);
+    if (lds > 160 * 1024) return hipErrorInvalidConfiguration;
+    const void *kern = split == 1 ? (const void *)k_chunk_scan<T, P, N, 1>
+                                  : (const void *)k_chunk_scan<T, P, N, 2>;
     hipError_t e = set_lds_limit(kern);
     if (e != hipSuccess) return e;
     const T *xp = (const T *)a.x, *bp = (const T *)a.B, *cp = (const T *)a.C;
     const T *hp = (const T *)hin;
-    int nc_ = nc, H_ = a.H, G_ = a.G, Q_ = a.Q;
+    int nc_ = nc, H_ = a.H, G_ = a.G, Q_ = a.Q, jp_ = jp;
     const float *Dp = a.D;
     float *yp = a.y;
-    void *args[] = {&xp, &bp, &cp, &Dp, &s_ws, &dt_ws, &hp, &info, &nc_, &H_, &G_, &Q_, &yp};
-    e = hipLaunchKernel(kern, dim3(xcd_grid(nc, a.H / hb * split)), dim3(threads), args, lds, st);
+    void *args[] = {&xp, &bp, &cp, &Dp, &s_ws, &dt_ws, &hp, &info, &nc_, &H_, &G_, &Q_, &jp_, &yp};
+    e = hipLaunchKernel(kern, dim3(xcd_grid(nc, a.H * split)), dim3(threads), args, lds, st);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
