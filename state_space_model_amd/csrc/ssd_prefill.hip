@@ -533,7 +533,8 @@ __global__ __launch_bounds__(1024) void k_chunk_scan(
     if (mine && i < len) {  // the tile has seen every j <= i: store it now
       const size_t row = ((size_t)ci.y + i) * H + hd;
 #pragma unroll
-      for (int pt = 0; pt < NPT; ++pt) st4(y + row * P + pt * 16 + 4 * grp, acc[pt]);
+      for (int pt = 0; pt < NPT; ++pt)
+        __builtin_nontemporal_store(acc[pt], reinterpret_cast<f4 *>(y + row * P + pt * 16 + 4 * grp));
     }
   }
 }
