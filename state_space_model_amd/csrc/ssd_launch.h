@@ -28,6 +28,8 @@ struct WorkspaceLayout {
   size_t seq_off;  // int  [nseq+1]              first chunk of each sequence
   size_t s;        // f32  [nc_max][H][Q]        chunk-local cumsum of dt*A
   size_t dt;       // f32  [nc_max][H][Q]        dt, chunk-major (0 on padded rows)
+  size_t u;        // f32  [nc_max][H][Q]        2^(s_ref(j) - s_j) dt_j, s_ref(j) = s at the
+                   //                            last row of j's 32-row block (log2 units)
   size_t S;        // f32  [nc_max][H][N][P]     chunk states
   size_t hin;      // T    [nc_max][H][N][P]     state entering each chunk (operand type)
   size_t total;
@@ -35,6 +37,15 @@ struct WorkspaceLayout {
 
 WorkspaceLayout prefill_layout(int64_t T, int nseq, int H, int P, int N, int Q, int elem);
 hipError_t launch_prefill(const PrefillArgs &a, unsigned stages);
+
+// Chunk scan with the heads of a B/C group streamed through one workgroup
+// (bfloat16, selected P/N/Q).  scan_heads_choice() returns the heads per
+// workgroup to use, or 0 where the row-split scan is the better (or only)
+// choice; launch_scan_heads() enqueues it over the workspace written by the
+// earlier stages.
+int scan_heads_choice(int P, int N, int Q, bool bf16, int nc, int H, int G);
+hipError_t launch_scan_heads(const PrefillArgs &a, const WorkspaceLayout &L, int nc, int HB,
+                             hipStream_t st);
 
 struct StepArgs {
   const void *x;

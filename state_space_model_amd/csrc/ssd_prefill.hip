@@ -26,11 +26,8 @@
 // nothing (decay 1, no input), so the chunk-end value s_{Q-1} equals
 // s_{len-1}.  The workspace holds s in base-2 units (s * log2(e)) so every
 // decay is one v_exp_f32 (2^x) of a non-positive argument.
-#include <mutex>
-#include <set>
-
-#include "ssd_device.h"
 #include "ssd_launch.h"
+#include "ssd_prefill_util.h"
 
 namespace ssd {
 
@@ -109,8 +106,6 @@ __device__ int4 locate_chunk(const int32_t *__restrict__ cu, int nseq, int L_den
   return sh_info;
 }
 
-constexpr float kLog2e = 1.4426950408889634f;
-
 // K1: grid (chunks, ceil(H/4)), 256 threads; wave w of block y handles head
 // 4y + w.  All of a head's dt loads are issued before the scan.
 __global__ __launch_bounds__(256) void k_chunk_cumsum(const float *__restrict__ dt,
@@ -120,7 +115,8 @@ __global__ __launch_bounds__(256) void k_chunk_cumsum(const float *__restrict__ 
                                                       int nc_max, int4 *__restrict__ info_out,
                                                       int *__restrict__ seq_off,
                                                       float *__restrict__ s_out,
-                                                      float *__restrict__ dt_out) {
+                                                      float *__restrict__ dt_out,
+                                                      float *__restrict__ u_out) {
   const int c = blockIdx.x;
   const int4 ci = locate_chunk(cu, nseq, L_dense, T, Q, c, seq_off,
                                blockIdx.x == 0 && blockIdx.y == 0);
@@ -141,6 +137,7 @@ __global__ __launch_bounds__(256) void k_chunk_cumsum(const float *__restrict__ 
   }
   float *so = s_out + ((size_t)c * H + h) * Q;
   float *dto = dt_out + ((size_t)c * H + h) * Q;
+  float *uo = u_out + ((size_t)c * H + h) * Q;
   float carry = 0.f;
 #pragma unroll
   for (int sg = 0; sg < MAXSEG; ++sg) {
@@ -153,9 +150,12 @@ __global__ __launch_bounds__(256) void k_chunk_cumsum(const float *__restrict__ 
       if (lane >= off) v += t;
     }
     v += carry;
+    // s at the last row of this row's 32-row block (Q is a multiple of 32)
+    const float sref = __shfl(v, lane | 31, 64);
     if (i < Q) {
       so[i] = v;
       dto[i] = d[sg];
+      uo[i] = __builtin_amdgcn_exp2f(fminf(sref - v, 0.f)) * d[sg];
     }
     carry = __shfl(v, 63, 64);
   }
@@ -187,28 +187,6 @@ __device__ __forceinline__ void stage_rows(T *tile, int pitch, const T *__restri
 
 constexpr int kJP = 128;  // token rows staged in LDS per phase (K2)
 
-// LDS row padding.  Tiles read with the 16-lane transpose read (4 rows x 32
-// bytes per lane group) use a pitch of width + 16 elements, i.e. 32 bytes (bf16)
-// or 64 bytes (float) past a multiple of 128 bytes, so the rows of one
-// read land on disjoint banks.  Tiles read 16 bytes per lane along a row use
-// width + 16 bytes (8 consecutive rows of a lane octet then cover every bank).
-constexpr int kTrPad = 16;
-template <typename T> constexpr int row_pad() { return 16 / (int)sizeof(T); }
-
-// XCD-aware (chunk, head) order for a 1-D grid of 8 * H * ceil(nc / 8)
-// workgroups.  Workgroup L is dispatched to XCD L % 8; decoding
-// c = 8 (q / H) + L % 8, h = q % H with q = L / 8 puts every head of chunk c on
-// the same XCD, back to back, so the chunk's B (and C) rows are fetched from
-// HBM once and then hit that XCD's L2 for the other heads.
-struct ChunkHead {
-  int c, h;
-};
-__device__ __forceinline__ ChunkHead xcd_chunk_head(int H) {
-  const int L = blockIdx.x, q = L >> 3;
-  return ChunkHead{8 * (q / H) + (L & 7), q % H};
-}
-static inline unsigned xcd_grid(int nc, int H) { return 8u * (unsigned)H * (unsigned)((nc + 7) / 8); }
-
 // ------------------------------------------------------------ K2 chunk state
 // S_c^T[p][n] = sum_j X'[j][p] B[j][n],  X'[j] = 2^(s_end - s_j) dt_j x_j.
 // MFMA 16x16 tiles over (p, n); k = tokens, read from token-major LDS tiles
@@ -224,14 +202,14 @@ template <typename T, int P, int N>
 __global__ __launch_bounds__(1024) void k_chunk_state(const T *__restrict__ x, const T *__restrict__ B,
                                                       const float *__restrict__ s_ws,
                                                       const float *__restrict__ dt_ws,
-                                                      const int4 *__restrict__ info, int nc, int H,
-                                                      int G, int Q, float *__restrict__ S_out) {
+                                                      ChunkMap cmap, int nc, int H, int G, int Q,
+                                                      float *__restrict__ S_out) {
   constexpr int XP = P + kTrPad, BP = N + kTrPad;
   constexpr int NNT = N / 16, NW = StateTiles<P, N>::NW, TPW = StateTiles<P, N>::TPW;
   const ChunkHead ch = xcd_chunk_head(H);
   const int c = ch.c, hd = ch.h;
   if (c >= nc) return;
-  const int4 ci = info[c];
+  const int4 ci = cmap(c);
   if (ci.z <= 0) return;
   const int g = (hd * G) / H;
   const int JP = Q < kJP ? Q : kJP;
@@ -340,29 +318,6 @@ __global__ __launch_bounds__(256) void k_state_pass(const float *__restrict__ S,
 // l writing base + 16 l): H_in and the first JP rows of B and X are requested
 // together with no staging registers, so each phase of JP rows costs one memory
 // round trip.
-__device__ __attribute__((aligned(16))) unsigned int g_zero16[4];  // zero source for padding
-
-// Fill a padded LDS tile of `rows` rows: each row has DATA 16-byte vectors
-// from `src` (row r at src + r * stride) followed by pad vectors up to SPR
-// slots; rows at or beyond `valid` are zero.  The tile spans a whole number
-// of 64-slot wave requests (the caller sizes it with tile_slots()).
-template <typename T, int SPR, int DATA>
-__device__ __forceinline__ void dma_tile(T *tile, const T *__restrict__ src, size_t stride,
-                                         int rows, int valid, int wave, int nw) {
-  constexpr int VN = 16 / sizeof(T);
-  const int total = rows * SPR;
-  const int lane = threadIdx.x & 63;
-  for (int base = wave * 64; base < total; base += nw * 64) {
-    const int s = base + lane, r = s / SPR, v = s % SPR;
-    const void *g = (s < total && r < valid && v < DATA) ? (const void *)(src + r * stride + v * VN)
-                                                       : (const void *)g_zero16;
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
-                                     (__attribute__((address_space(3))) void *)(tile + base * VN),
-                                     16, 0, 0);
-  }
-}
-__host__ __device__ constexpr int tile_slots(int rows, int spr) { return (rows * spr + 63) / 64 * 64; }
-
 template <typename T, int P, int N> struct ScanCfg {
   static constexpr int NK = N < 32 ? 32 : N;  // contraction over n, padded to the k-step
   static constexpr int KS = NK / 32;
@@ -390,7 +345,7 @@ template <typename T, int P, int N, int SPLIT>
 __global__ __launch_bounds__(1024) void k_chunk_scan(
     const T *__restrict__ x, const T *__restrict__ B, const T *__restrict__ C,
     const float *__restrict__ D, const float *__restrict__ s_ws, const float *__restrict__ dt_ws,
-    const T *__restrict__ hin, const int4 *__restrict__ info, int nc, int H, int G, int Q,
+    const T *__restrict__ hin, ChunkMap cmap, int nc, int H, int G, int Q,
     int JP, float *__restrict__ y) {
   typedef ScanCfg<T, P, N> K;
   constexpr int KS = K::KS, NK = K::NK, XP = K::XP, BP = K::BP, HP = K::HP;
@@ -398,7 +353,7 @@ __global__ __launch_bounds__(1024) void k_chunk_scan(
   const ChunkHead ch = xcd_chunk_head(H * SPLIT);
   const int c = ch.c, hd = ch.h / SPLIT, part = ch.h % SPLIT;
   if (c >= nc) return;
-  const int4 ci = info[c];
+  const int4 ci = cmap(c);
   if (ci.z <= 0) return;
   const int len = ci.z;
   const int g = (hd * G) / H;
@@ -542,18 +497,6 @@ __global__ __launch_bounds__(1024) void k_chunk_scan(
 // ------------------------------------------------------------------ launch
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Allow a kernel the full 160 KB of LDS (once per kernel; not a stream
-// operation, so calls under graph capture are unaffected after the first).
-static hipError_t set_lds_limit(const void *kern) {
-  static std::mutex mu;
-  static std::set<const void *> done;
-  std::lock_guard<std::mutex> lock(mu);
-  if (done.count(kern)) return hipSuccess;
-  hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-  if (e == hipSuccess) done.insert(kern);
-  return e;
-}
-
 WorkspaceLayout prefill_layout(int64_t T, int nseq, int H, int P, int N, int Q, int elem) {
   WorkspaceLayout L{};
   const int64_t nc = (T + (int64_t)nseq * (Q - 1)) / Q;
@@ -566,6 +509,8 @@ WorkspaceLayout prefill_layout(int64_t T, int nseq, int H, int P, int N, int Q, 
   L.s = off;
   off = align_up(off + 4 * (size_t)nc * H * Q, 256);
   L.dt = off;
+  off = align_up(off + 4 * (size_t)nc * H * Q, 256);
+  L.u = off;
   off = align_up(off + 4 * (size_t)nc * H * Q, 256);
   L.S = off;
   off = align_up(off + 4 * (size_t)nc * H * N * P, 256);
@@ -583,17 +528,19 @@ static hipError_t run_prefill(const PrefillArgs &a, unsigned stages) {
   int *seq_off = reinterpret_cast<int *>(ws + L.seq_off);
   float *s_ws = reinterpret_cast<float *>(ws + L.s);
   float *dt_ws = reinterpret_cast<float *>(ws + L.dt);
+  float *u_ws = reinterpret_cast<float *>(ws + L.u);
   float *S = reinterpret_cast<float *>(ws + L.S);
   T *hin = reinterpret_cast<T *>(ws + L.hin);
   const int nc = (int)L.nc_max;
   const int L_dense = a.cu ? 0 : (int)(a.T / a.nseq);
+  const ChunkMap cmap{info, L_dense, a.nseq, a.Q};
   const int JP = a.Q < kJP ? a.Q : kJP;
   hipStream_t st = static_cast<hipStream_t>(a.stream);
 
   if (stages & 1u) {
     hipLaunchKernelGGL(k_chunk_cumsum, dim3(nc > 0 ? nc : 1, (a.H + 3) / 4), dim3(256), 0, st,
                        a.dt, a.A, a.cu, a.nseq, L_dense, a.T, a.H, a.Q, nc, info, seq_off, s_ws,
-                       dt_ws);
+                       dt_ws, u_ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -603,7 +550,7 @@ static hipError_t run_prefill(const PrefillArgs &a, unsigned stages) {
     hipError_t e = set_lds_limit((const void *)kern);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(xcd_grid(nc, a.H)), dim3(64 * StateTiles<P, N>::NW), lds, st,
-                       (const T *)a.x, (const T *)a.B, s_ws, dt_ws, info, nc, a.H, a.G, a.Q, S);
+                       (const T *)a.x, (const T *)a.B, s_ws, dt_ws, cmap, nc, a.H, a.G, a.Q, S);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -614,7 +561,11 @@ static hipError_t run_prefill(const PrefillArgs &a, unsigned stages) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if ((stages & 8u) && nc > 0) {
+  const int HB = (stages & 8u) ? scan_heads_choice(P, N, a.Q, a.bf16, nc, a.H, a.G) : 0;
+  if ((stages & 8u) && nc > 0 && HB > 0) {
+    hipError_t e = launch_scan_heads(a, L, nc, HB, st);
+    if (e != hipSuccess) return e;
+  } else if ((stages & 8u) && nc > 0) {
     // Q <= 128: one workgroup of Q/16 waves per (chunk, head); Q >= 256: two of Q/32 waves
     typedef ScanCfg<T, P, N> K;
     const int split = a.Q >= 256 ? 2 : 1;
@@ -631,7 +582,8 @@ static hipError_t run_prefill(const PrefillArgs &a, unsigned stages) {
     int nc_ = nc, H_ = a.H, G_ = a.G, Q_ = a.Q, jp_ = jp;
     const float *Dp = a.D;
     float *yp = a.y;
-    void *args[] = {&xp, &bp, &cp, &Dp, &s_ws, &dt_ws, &hp, &info, &nc_, &H_, &G_, &Q_, &jp_, &yp};
+    ChunkMap cm = cmap;
+    void *args[] = {&xp, &bp, &cp, &Dp, &s_ws, &dt_ws, &hp, &cm, &nc_, &H_, &G_, &Q_, &jp_, &yp};
     e = hipLaunchKernel(kern, dim3(xcd_grid(nc, a.H * split)), dim3(threads), args, lds, st);
     if (e != hipSuccess) return e;
   }

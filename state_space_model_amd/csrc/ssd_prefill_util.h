@@ -1,0 +1,89 @@
+// ssd_prefill_util.h -- helpers shared by the prefill kernels: decay units,
+// LDS padding, the XCD-aware chunk order and direct global->LDS tile loads.
+#pragma once
+#include <mutex>
+#include <set>
+
+#include "ssd_device.h"
+
+namespace ssd {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// LDS row padding.  Tiles read with the 16-lane transpose read (4 rows x 32
+// bytes per lane group) use a pitch of width + 16 elements, i.e. 32 bytes (bf16)
+// or 64 bytes (float) past a multiple of 128 bytes, so the rows of one
+// read land on disjoint banks.  Tiles read 16 bytes per lane along a row use
+// width + 16 bytes (8 consecutive rows of a lane octet then cover every bank).
+constexpr int kTrPad = 16;
+template <typename T> constexpr int row_pad() { return 16 / (int)sizeof(T); }
+
+// XCD-aware (chunk, head) order for a 1-D grid of 8 * H * ceil(nc / 8)
+// workgroups.  Workgroup L is dispatched to XCD L % 8; decoding
+// c = 8 (q / H) + L % 8, h = q % H with q = L / 8 puts every head of chunk c on
+// the same XCD, back to back, so the chunk's B (and C) rows are fetched from
+// HBM once and then hit that XCD's L2 for the other heads.
+struct ChunkHead {
+  int c, h;
+};
+__device__ __forceinline__ ChunkHead xcd_chunk_head(int H) {
+  const int L = blockIdx.x, q = L >> 3;
+  return ChunkHead{8 * (q / H) + (L & 7), q % H};
+}
+static inline unsigned xcd_grid(int nc, int H) { return 8u * (unsigned)H * (unsigned)((nc + 7) / 8); }
+
+// Chunk c of the packed batch -> {sequence, first token, length, index in
+// sequence}.  A dense batch (L tokens per sequence) is pure arithmetic, so a
+// workgroup needs no memory round trip before its first load; a packed batch
+// reads the table written by the cumulative-sum stage.
+struct ChunkMap {
+  const int4 *table;  // used when L == 0
+  int L, nseq, Q;
+  __device__ __forceinline__ int4 operator()(int c) const {
+    if (L > 0) {
+      const int cps = (L + Q - 1) / Q;
+      const int seq = c / cps, k = c - seq * cps;
+      if (seq >= nseq) return make_int4(0, 0, 0, 0);
+      return make_int4(seq, seq * L + k * Q, min(Q, L - k * Q), k);
+    }
+    return table[c];
+  }
+};
+
+// zero source for padding slots (one copy per translation unit)
+static __device__ __attribute__((aligned(16))) unsigned int g_zero16[4];
+
+// Fill a padded LDS tile of `rows` rows: each row has DATA 16-byte vectors
+// from `src` (row r at src + r * stride) followed by pad vectors up to SPR
+// slots; rows at or beyond `valid` are zero.  The tile spans a whole number
+// of 64-slot wave requests (the caller sizes it with tile_slots()).
+template <typename T, int SPR, int DATA>
+__device__ __forceinline__ void dma_tile(T *tile, const T *__restrict__ src, size_t stride,
+                                         int rows, int valid, int wave, int nw) {
+  constexpr int VN = 16 / sizeof(T);
+  const int total = rows * SPR;
+  const int lane = threadIdx.x & 63;
+  for (int base = wave * 64; base < total; base += nw * 64) {
+    const int s = base + lane, r = s / SPR, v = s % SPR;
+    const void *g = (s < total && r < valid && v < DATA) ? (const void *)(src + r * stride + v * VN)
+                                                       : (const void *)g_zero16;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
+                                     (__attribute__((address_space(3))) void *)(tile + base * VN),
+                                     16, 0, 0);
+  }
+}
+__host__ __device__ constexpr int tile_slots(int rows, int spr) { return (rows * spr + 63) / 64 * 64; }
+
+// Allow a kernel the full 160 KB of LDS (once per kernel; not a stream
+// operation, so calls under graph capture are unaffected after the first).
+static inline hipError_t set_lds_limit(const void *kern) {
+  static std::mutex mu;
+  static std::set<const void *> done;
+  std::lock_guard<std::mutex> lock(mu);
+  if (done.count(kern)) return hipSuccess;
+  hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (e == hipSuccess) done.insert(kern);
+  return e;
+}
+
+}  // namespace ssd

@@ -34,7 +34,8 @@ def test_workspace_size():
     w = lib.ssd_scan_prefill_workspace
     n1 = w(4096, 1, 24, 64, 128, 256, 1)
     nc = 16
-    expect_min = nc * 24 * 128 * 64 * (4 + 2) + 2 * nc * 24 * 256 * 4
+    # S (float32) + H_in (bf16) per chunk and head, and s, dt, u per chunk, head and row
+    expect_min = nc * 24 * 128 * 64 * (4 + 2) + 3 * nc * 24 * 256 * 4
     assert expect_min <= n1 <= expect_min + 8192
     assert w(4096, 1, 24, 64, 128, 256, 0) > n1          # float32 operand copy of H_in
     assert w(4096, 1, 24, 64, 100, 256, 1) == 0          # unsupported N

@@ -10,6 +10,28 @@ from state_space_model_amd import inputs
 pytestmark = pytest.mark.gpu
 
 
+class scan_kernel:
+    """Force the chunk-scan kernel choice (SSD_PREFILL_SCAN=heads|rows) for a block."""
+
+    def __init__(self, mode):
+        self.mode = mode
+
+    def __enter__(self):
+        import os
+        self.old = os.environ.get("SSD_PREFILL_SCAN")
+        if self.mode == "auto":
+            os.environ.pop("SSD_PREFILL_SCAN", None)
+        else:
+            os.environ["SSD_PREFILL_SCAN"] = self.mode
+
+    def __exit__(self, *exc):
+        import os
+        if self.old is None:
+            os.environ.pop("SSD_PREFILL_SCAN", None)
+        else:
+            os.environ["SSD_PREFILL_SCAN"] = self.old
+
+
 def _gpu(d, dtype, chunk, with_h0=True, **kw):
     import torch
     from state_space_model_amd import ssd
@@ -37,13 +59,20 @@ SMALL = [  # (lengths, H, P, N, G, chunk, h0)
 ]
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+SCAN_MODES = [("f32", "auto"), ("bf16", "rows"), ("bf16", "heads")]
+
+
+@pytest.mark.parametrize("dtype,scan", SCAN_MODES)
 @pytest.mark.parametrize("case", range(len(SMALL)))
-def test_prefill_small(dtype, case):
+def test_prefill_small(dtype, scan, case):
+    """Every small shape in float32, and in bfloat16 through both chunk-scan
+    kernels (row-split, and heads streamed where a shape has that kernel)."""
     lengths, H, P, N, G, chunk, h0 = SMALL[case]
-    log(f"prefill small dtype={dtype} lengths={lengths} H={H} P={P} N={N} G={G} Q={chunk}")
+    log(f"prefill small dtype={dtype} scan={scan} lengths={lengths} H={H} P={P} N={N} G={G}"
+        f" Q={chunk}")
     d = inputs.prefill_inputs(H, P, N, G, lengths, 200 + case, dtype=dtype, h0=h0)
-    y, ho = _gpu(d, dtype, chunk)
+    with scan_kernel(scan):
+        y, ho = _gpu(d, dtype, chunk)
     ry, rh = _ref(d)
     ey, eh = maxabs(y, ry), maxabs(ho, rh)
     log(f"  max|dy|={ey:.3g} max|dh|={eh:.3g}")
@@ -63,29 +92,33 @@ def test_prefill_tiny_workload_f32():
 
 def test_prefill_130m_layer_workload():
     w = inputs.WORKLOADS[1]
-    log("prefill workload 1 (Mamba-2 130M layer, bf16), full oracle")
+    log("prefill workload 1 (Mamba-2 130M layer, bf16), full oracle, both scan kernels")
     d = inputs.workload_inputs(1)
-    y, ho = _gpu(d, "bf16", w.chunk)
     ry, rh = _ref(d)
-    ey, eh = maxabs(y, ry), maxabs(ho, rh)
     ssm = np.max(np.abs(ry - d["D"][None, :, None] * d["x"]))
-    log(f"  max|dy|={ey:.3g} max|dh|={eh:.3g} (max|y_ssm|={ssm:.3g})")
-    assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
+    for scan in ("auto", "heads"):
+        with scan_kernel(scan):
+            y, ho = _gpu(d, "bf16", w.chunk)
+        ey, eh = maxabs(y, ry), maxabs(ho, rh)
+        log(f"  scan={scan}: max|dy|={ey:.3g} max|dh|={eh:.3g} (max|y_ssm|={ssm:.3g})")
+        assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
 
 
 def test_prefill_2p7b_layer_workload():
     """4 x 8192 tokens, 80 heads: the GPU runs the whole workload; the oracle
     recomputes a sample of heads over every token of every sequence."""
     w = inputs.WORKLOADS[2]
-    log("prefill workload 2 (Mamba-2 2.7B layer, bf16), sampled heads")
+    log("prefill workload 2 (Mamba-2 2.7B layer, bf16), sampled heads, both scan kernels")
     d = inputs.workload_inputs(2)
-    y, ho = _gpu(d, "bf16", w.chunk)
     heads = [0, 41, 79]
     ds = select_heads(d, heads, w.G)
     ry, rh = _ref(ds)
-    ey, eh = maxabs(y[:, heads], ry), maxabs(ho[:, heads], rh)
-    log(f"  max|dy|={ey:.3g} max|dh|={eh:.3g}")
-    assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
+    for scan in ("auto", "rows"):
+        with scan_kernel(scan):
+            y, ho = _gpu(d, "bf16", w.chunk)
+        ey, eh = maxabs(y[:, heads], ry), maxabs(ho[:, heads], rh)
+        log(f"  scan={scan}: max|dy|={ey:.3g} max|dh|={eh:.3g}")
+        assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
 
 
 def test_prefill_long_context_varlen_chunk_sweep():
@@ -97,11 +130,13 @@ def test_prefill_long_context_varlen_chunk_sweep():
     heads = [3, 66]
     ds = select_heads(d, heads, w.G)
     ry, rh = _ref(ds)
-    for q in w.chunks:
-        y, ho = _gpu(d, "bf16", q)
-        ey, eh = maxabs(y[:, heads], ry), maxabs(ho[:, heads], rh)
-        log(f"  Q={q}: max|dy|={ey:.3g} max|dh|={eh:.3g}")
-        assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
+    for scan in ("auto", "rows"):
+        for q in w.chunks:
+            with scan_kernel(scan):
+                y, ho = _gpu(d, "bf16", q)
+            ey, eh = maxabs(y[:, heads], ry), maxabs(ho[:, heads], rh)
+            log(f"  scan={scan} Q={q}: max|dy|={ey:.3g} max|dh|={eh:.3g}")
+            assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
 
 
 def test_stages_separately_equal_one_call():
