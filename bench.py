@@ -66,16 +66,18 @@ def prefill_work(w, T, nseq, h0):
     H, P, N, G, Q = w.H, w.P, w.N, w.G, w.chunk
     e = 2 if w.dtype == "bf16" else 4
     state = nseq * H * N * P * 4
-    k1 = dict(bytes=T * H * 4 + H * 4, flops=T * H)
-    # chunk state: x, B, dt read; S = sum_j w_j B_j x_j^T, 2 flop per (token, n, p)
-    k2 = dict(bytes=T * H * P * e + T * G * N * e + T * H * 4, flops=2 * T * H * N * P)
+    # chunk state (with the chunk-local cumulative decay): x, B, dt read;
+    # s = cumsum(dt A) (1 flop per token and head), S = sum_j w_j B_j x_j^T
+    # (2 flop per token, n, p)
+    k2 = dict(bytes=T * H * P * e + T * G * N * e + T * H * 4 + H * 4,
+              flops=T * H + 2 * T * H * N * P)
     # state passing reads h0 and writes h_out (chunk states are implementation overhead)
     k3 = dict(bytes=(state if h0 else 0) + state, flops=2 * (T // Q + nseq) * H * N * P)
     # chunk scan: x, B, C, dt read, y written; C.B^T once per group and chunk (full tile),
     # M.X per head (full tile), C.H_in per head
     k4 = dict(bytes=T * H * P * (e + 4) + 2 * T * G * N * e + T * H * 4,
               flops=T * (2 * Q * N * G + H * (2 * Q * P + 2 * N * P)))
-    return {"chunk_cumsum": k1, "chunk_state": k2, "state_pass": k3, "chunk_scan": k4}
+    return {"chunk_state": k2, "state_pass": k3, "chunk_scan": k4}
 
 
 def step_work(b, H, P, N, G, e_in):
@@ -193,7 +195,7 @@ def _read_csv(path):
 
 
 KERNEL_NAMES = {  # kernel symbol fragment -> bench kernel name
-    "k_chunk_cumsum": "chunk_cumsum", "k_chunk_state": "chunk_state",
+    "k_chunk_state": "chunk_state",
     "k_state_pass": "state_pass", "k_chunk_scan": "chunk_scan", "k_step": "decode_step",
 }
 
@@ -356,7 +358,7 @@ def main():
     ms_step_graph = graph_ms(torch, step, reps=max(10, args.steps // 10), per_graph=10)
 
     # ---- per-kernel durations: each kernel alone, 20 launches per HIP graph
-    names = [("chunk_cumsum", ssd.STAGE_CHUNK_CUMSUM), ("chunk_state", ssd.STAGE_CHUNK_STATE),
+    names = [("chunk_state", ssd.STAGE_CHUNK_CUMSUM | ssd.STAGE_CHUNK_STATE),
              ("state_pass", ssd.STAGE_STATE_PASS), ("chunk_scan", ssd.STAGE_CHUNK_SCAN)]
     kern_ms = {}
     for name, st in names:

@@ -1,0 +1,236 @@
+// ssd_chunk_state.hip -- first stage of the chunked prefill: per (chunk, head)
+// the chunk-local cumulative decay and the chunk state, in one kernel.
+//
+// Per chunk c and head h (s in log2 units, all exponents <= 0):
+//   s_i  = log2(e) A_h sum_{k<=i} dt_k
+//   S_c  = sum_j 2^(s_{Q-1} - s_j) dt_j B_j x_j^T            (N x P, float32)
+// The chunk state is the part of the state at the chunk end contributed by
+// the chunk's own tokens: the recurrence h_t = exp(dt_t A_h) h_{t-1} +
+// dt_t x_t (x) B_t unrolled over one chunk with a zero entering state
+// (Compiler-First State Space Duality and Portable O(1) Autoregressive
+// Caching for Inference, Abstract; float32 decay as in its Table 8).
+//
+// Also written for the later stages: s, dt and u_j = 2^(s_r - s_j) dt_j (r the
+// last row of j's 32-row block), each [chunk][head][Q].
+//
+// One workgroup per (chunk, head, half of the n columns) -- two workgroups of
+// under 80 KB of LDS share a CU.  Every load of a phase (x rows, B rows, and
+// the strided dt column) goes straight to LDS in one batch, so the chunk costs
+// one memory round trip before the scan, the x scaling and the MFMAs.
+#include "ssd_launch.h"
+#include "ssd_prefill_util.h"
+
+namespace ssd {
+
+template <typename T, int P, int N> struct StateCfg {
+  static constexpr int NH = N >= 64 ? 2 : 1;  // workgroups per (chunk, head)
+  static constexpr int NN = N / NH;           // n columns per workgroup
+  static constexpr int VN = 16 / (int)sizeof(T);
+  // pitch = width + one 16-byte slot: the transpose reads of lane groups 8
+  // rows apart (one read pass) then fall on disjoint banks
+  static constexpr int XP = P + VN, BP = NN + VN;
+  static constexpr int XS = XP / VN, BS = BP / VN, XD = P / VN, BD = NN / VN;
+  static constexpr int TILES = (P / 16) * (NN / 16);
+  static constexpr int NW = TILES >= 8 ? 8 : 4;  // waves (at least 4 for the scan)
+  static constexpr int TPW = (TILES + NW - 1) / NW;
+  static constexpr int THREADS = 64 * NW;
+  static constexpr size_t lds_bytes(int jp, int q) {
+    return (size_t)(tile_slots(jp, XS) + tile_slots(jp, BS)) * 16 +
+           4 * (size_t)(3 * q + 64 + 16);  // dt (staged, padded), s, w, scan partials
+  }
+  // rows staged per phase: the whole chunk if it fits in 80 KB, else halved
+  static int jp(int q) {
+    int j = q;
+    while (j > 32 && lds_bytes(j, q) > 80 * 1024) j /= 2;
+    return j;
+  }
+};
+
+// Scale rows [0, rows) of a token-major LDS tile by w[r0 + r] (float32
+// arithmetic, rounded back to T).
+template <typename T, int PITCH, int DATA>
+__device__ __forceinline__ void scale_rows(T *tile, const float *w, int r0, int rows) {
+  typedef typename Vec16<T>::type V;
+  constexpr int VN = Vec16<T>::n;
+  for (int idx = threadIdx.x; idx < rows * DATA; idx += blockDim.x) {
+    const int r = idx / DATA, v = idx % DATA;
+    V *p = reinterpret_cast<V *>(tile + r * PITCH + v * VN);
+    *p = vscale(*p, w[r0 + r]);
+  }
+}
+
+template <typename T, int P, int N>
+__global__ __launch_bounds__((StateCfg<T, P, N>::THREADS)) void k_chunk_state(
+    const T *__restrict__ x, const float *__restrict__ dt, const float *__restrict__ A,
+    const T *__restrict__ B, ChunkMap cmap, int nc, int H, int G, int Q, int JP, int do_state,
+    float *__restrict__ s_out, float *__restrict__ dt_out, float *__restrict__ u_out,
+    float *__restrict__ S_out) {
+  typedef StateCfg<T, P, N> K;
+  constexpr int NW = K::NW, TPW = K::TPW, NNT = K::NN / 16;
+  const ChunkHead ch = xcd_chunk_head(H * K::NH);
+  const int c = ch.c, hd = ch.h / K::NH, half = ch.h % K::NH;
+  if (c >= nc) return;
+  const int4 ci = cmap(c);
+  const int len = ci.z;
+  if (len <= 0) return;
+  const int g = (hd * G) / H;
+  const int tid = threadIdx.x, lane = tid & 63, grp = lane >> 4, col = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  extern __shared__ __align__(16) char smem[];
+  T *Xs = reinterpret_cast<T *>(smem);
+  T *Bs = Xs + tile_slots(JP, K::XS) * K::VN;
+  float *dt_l = reinterpret_cast<float *>(Bs + tile_slots(JP, K::BS) * K::VN);  // [Q + 64]
+  float *s_l = dt_l + Q + 64;                                                   // [Q]
+  float *w_l = s_l + Q;                                                         // [Q]
+  float *part = w_l + Q;                                                        // [16]
+
+  const size_t xstride = (size_t)H * P, bstride = (size_t)G * N;
+  const T *xs = x + (size_t)ci.y * xstride + (size_t)hd * P;
+  const T *bs = B + (size_t)ci.y * bstride + (size_t)g * N + half * K::NN;
+
+  // ---- one batch of direct loads: the dt column, first phase of x and B
+  for (int base = wave * 64; base < Q; base += NW * 64) {
+    const int i = base + lane;
+    const void *gp = i < len ? (const void *)(dt + ((size_t)ci.y + i) * H + hd)
+                             : (const void *)g_zero16;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)gp,
+                                     (__attribute__((address_space(3))) void *)(dt_l + base), 4,
+                                     0, 0);
+  }
+  if (do_state) {
+    dma_tile<T, K::XS, K::XD>(Xs, xs, xstride, JP, len, wave, NW);
+    dma_tile<T, K::BS, K::BD>(Bs, bs, bstride, JP, len, wave, NW);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // ---- s = log2(e) A cumsum(dt): R consecutive rows per thread, block scan
+  const float a2 = A[hd] * kLog2e;
+  const int R = (Q + K::THREADS - 1) / K::THREADS;  // 1 or 2 (Q <= 512)
+  float v0 = 0.f, v1 = 0.f;
+  if (tid * R < Q) v0 = dt_l[tid * R] * a2;
+  if (R > 1 && tid * R + 1 < Q) v1 = v0 + dt_l[tid * R + 1] * a2;
+  float tot = R > 1 ? v1 : v0;
+  float incl = tot;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float t = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += t;
+  }
+  if (lane == 63) part[wave] = incl;
+  __syncthreads();
+  float pre = 0.f;
+  for (int w = 0; w < wave; ++w) pre += part[w];
+  const float excl = pre + incl - tot;
+  if (tid * R < Q) s_l[tid * R] = excl + v0;
+  if (R > 1 && tid * R + 1 < Q) s_l[tid * R + 1] = excl + v1;
+  __syncthreads();
+
+  // ---- decay weights: w_j (to the chunk end) here, u_j (to the block end) for
+  // the output stage; padded rows have dt = 0 and so weight 0
+  const float s_end = s_l[Q - 1];
+  const size_t o = ((size_t)c * H + hd) * Q;
+  for (int j = tid; j < Q; j += K::THREADS) {
+    const float sj = s_l[j], dj = dt_l[j];
+    w_l[j] = __builtin_amdgcn_exp2f(fminf(s_end - sj, 0.f)) * dj;
+    if (half == 0) {
+      s_out[o + j] = sj;
+      dt_out[o + j] = dj;
+      u_out[o + j] = __builtin_amdgcn_exp2f(fminf(s_l[j | 31] - sj, 0.f)) * dj;
+    }
+  }
+  if (!do_state) return;
+  __syncthreads();
+
+  // ---- S^T[p][n] = sum_j (w_j x_j)[p] B[j][n]   (MFMA, k = tokens)
+  f4 acc[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) acc[t] = zero4();
+  for (int ph = 0; ph < len; ph += JP) {  // phases past the chunk length add nothing
+    if (ph > 0) {
+      __syncthreads();
+      dma_tile<T, K::XS, K::XD>(Xs, xs + (size_t)ph * xstride, xstride, JP, len - ph, wave, NW);
+      dma_tile<T, K::BS, K::BD>(Bs, bs + (size_t)ph * bstride, bstride, JP, len - ph, wave, NW);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+    scale_rows<T, K::XP, K::XD>(Xs, w_l, ph, min(JP, len - ph));
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const int tile = wave + NW * t;
+      if (tile < K::TILES) {
+        const int pt = tile / NNT, nt = tile % NNT;
+        for (int k0 = 0; k0 < JP; k0 += 32) {
+          const Frag<T> a = frag_kmaj(Xs, K::XP, pt * 16, k0 + 8 * grp, k0 + 8 * grp + 4);
+          const Frag<T> b = frag_kmaj(Bs, K::BP, nt * 16, k0 + 8 * grp, k0 + 8 * grp + 4);
+          mma(acc[t], a, b);
+        }
+      }
+    }
+  }
+  float *so = S_out + ((size_t)c * H + hd) * (size_t)(N * P);
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int tile = wave + NW * t;
+    if (tile < K::TILES) {
+      const int pt = tile / NNT, nt = tile % NNT;
+      const int n = half * K::NN + nt * 16 + col, p = pt * 16 + 4 * grp;
+      st4(so + (size_t)n * P + p, acc[t]);
+    }
+  }
+}
+
+template <typename T, int P, int N>
+static hipError_t run_state(const PrefillArgs &a, const WorkspaceLayout &L, int nc, bool state,
+                            hipStream_t st) {
+  typedef StateCfg<T, P, N> K;
+  const int jp = K::jp(a.Q);
+  const size_t lds = K::lds_bytes(jp, a.Q);
+  if (lds > 160 * 1024) return hipErrorInvalidConfiguration;
+  const void *kern = (const void *)k_chunk_state<T, P, N>;
+  hipError_t e = set_lds_limit(kern);
+  if (e != hipSuccess) return e;
+  char *ws = static_cast<char *>(a.workspace);
+  const T *xp = (const T *)a.x, *bp = (const T *)a.B;
+  const float *dtp = a.dt, *Ap = a.A;
+  ChunkMap cm{reinterpret_cast<const int4 *>(ws + L.info), a.cu ? 0 : (int)(a.T / a.nseq), a.nseq,
+              a.Q};
+  int nc_ = nc, H_ = a.H, G_ = a.G, Q_ = a.Q, jp_ = jp, do_ = state ? 1 : 0;
+  float *sp = reinterpret_cast<float *>(ws + L.s), *dp = reinterpret_cast<float *>(ws + L.dt);
+  float *up = reinterpret_cast<float *>(ws + L.u), *Sp = reinterpret_cast<float *>(ws + L.S);
+  void *args[] = {&xp, &dtp, &Ap, &bp, &cm, &nc_, &H_, &G_, &Q_, &jp_, &do_, &sp, &dp, &up, &Sp};
+  return hipLaunchKernel(kern, dim3(xcd_grid(nc, a.H * K::NH)), dim3(K::THREADS), args, lds, st);
+}
+
+template <typename T, int P>
+static hipError_t state_N(const PrefillArgs &a, const WorkspaceLayout &L, int nc, bool s,
+                          hipStream_t st) {
+  switch (a.N) {
+    case 16: return run_state<T, P, 16>(a, L, nc, s, st);
+    case 32: return run_state<T, P, 32>(a, L, nc, s, st);
+    case 64: return run_state<T, P, 64>(a, L, nc, s, st);
+    case 128: return run_state<T, P, 128>(a, L, nc, s, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+static hipError_t state_P(const PrefillArgs &a, const WorkspaceLayout &L, int nc, bool s,
+                          hipStream_t st) {
+  switch (a.P) {
+    case 16: return state_N<T, 16>(a, L, nc, s, st);
+    case 32: return state_N<T, 32>(a, L, nc, s, st);
+    case 64: return state_N<T, 64>(a, L, nc, s, st);
+    case 128: return state_N<T, 128>(a, L, nc, s, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_chunk_state(const PrefillArgs &a, const WorkspaceLayout &L, int nc, bool state,
+                              hipStream_t st) {
+  return a.bf16 ? state_P<bf16>(a, L, nc, state, st) : state_P<float>(a, L, nc, state, st);
+}
+
+}  // namespace ssd

@@ -38,6 +38,11 @@ struct WorkspaceLayout {
 WorkspaceLayout prefill_layout(int64_t T, int nseq, int H, int P, int N, int Q, int elem);
 hipError_t launch_prefill(const PrefillArgs &a, unsigned stages);
 
+// Stages 1-2: chunk-local cumulative decay (s, dt, u) and, if `state`, the
+// chunk states S.
+hipError_t launch_chunk_state(const PrefillArgs &a, const WorkspaceLayout &L, int nc, bool state,
+                              hipStream_t st);
+
 // Chunk scan with the heads of a B/C group streamed through one workgroup
 // (bfloat16, selected P/N/Q).  scan_heads_choice() returns the heads per
 // workgroup to use, or 0 where the row-split scan is the better (or only)

@@ -1,4 +1,5 @@
-// ssd_prefill.hip -- chunked SSD prefill on gfx950: four kernels.
+// ssd_prefill.hip -- chunked SSD prefill on gfx950: stage launcher, chunk map,
+// state pass and the row-split chunk scan.
 //
 // Math (per sequence, head h, chunk c of Q tokens; all exponents <= 0):
 //   s_i    = sum_{k<=i} dt_k A_h                         (chunk-local, float32)
@@ -17,11 +18,12 @@
 // equation, one packed result").
 //
 // Kernels (one launch each, all on the caller's stream):
-//   K1 k_chunk_cumsum : grid (nc_max, H/4)  chunk map + s, dt per (chunk, head)
-//   K2 k_chunk_state  : 8*H*ceil(nc/8)    S_c^T = (w o X)^T B on MFMA, k = tokens (16 waves)
-//   K3 k_state_pass   : grid (NP/1024,H,nseq) sequential H_c over the chunks of a sequence
-//   K4 k_chunk_scan   : 8*H*ceil(nc/8)    one wave per 16-token tile: C.B^T (k = N), mask/decay, Y^T = X^T M^T
-//                                           (k = tokens) and exp(s) H^T C^T (k = N) on MFMA
+//   k_chunk_map        (packed batches only) chunk -> {sequence, first token, length}
+//   k_chunk_state      s, dt, u and S_c^T = (w o X)^T B on MFMA     (ssd_chunk_state.hip)
+//   k_state_pass       grid (NP/1024,H,nseq): sequential H_c over the chunks of a sequence
+//   k_chunk_scan       y, one wave per 16-token tile: C.B^T (k = N), mask/decay,
+//                      Y^T = X^T M^T (k = tokens) and 2^s H^T C^T (k = N) on MFMA
+//   k_chunk_scan_heads y for large batches, heads of a group streamed  (ssd_scan_heads.hip)
 // Every padded row of a partial chunk has dt = 0, x = 0, B = 0: it changes
 // nothing (decay 1, no input), so the chunk-end value s_{Q-1} equals
 // s_{len-1}.  The workspace holds s in base-2 units (s * log2(e)) so every
@@ -106,155 +108,16 @@ __device__ int4 locate_chunk(const int32_t *__restrict__ cu, int nseq, int L_den
   return sh_info;
 }
 
-// K1: grid (chunks, ceil(H/4)), 256 threads; wave w of block y handles head
-// 4y + w.  All of a head's dt loads are issued before the scan.
-__global__ __launch_bounds__(256) void k_chunk_cumsum(const float *__restrict__ dt,
-                                                      const float *__restrict__ A,
-                                                      const int32_t *__restrict__ cu, int nseq,
-                                                      int L_dense, int64_t T, int H, int Q,
-                                                      int nc_max, int4 *__restrict__ info_out,
-                                                      int *__restrict__ seq_off,
-                                                      float *__restrict__ s_out,
-                                                      float *__restrict__ dt_out,
-                                                      float *__restrict__ u_out) {
+// Chunk map of a packed batch: grid (chunks), 256 threads; block c writes
+// info[c], block 0 also the first chunk of every sequence.  (A dense batch
+// needs neither: its map is arithmetic.)
+__global__ __launch_bounds__(256) void k_chunk_map(const int32_t *__restrict__ cu, int nseq,
+                                                   int64_t T, int Q, int nc_max,
+                                                   int4 *__restrict__ info_out,
+                                                   int *__restrict__ seq_off) {
   const int c = blockIdx.x;
-  const int4 ci = locate_chunk(cu, nseq, L_dense, T, Q, c, seq_off,
-                               blockIdx.x == 0 && blockIdx.y == 0);
-  if (c >= nc_max) return;
-  if (threadIdx.x == 0 && blockIdx.y == 0) info_out[c] = ci.x < 0 ? make_int4(0, 0, 0, 0) : ci;
-  if (ci.x < 0 || ci.z <= 0) return;
-  const int lane = threadIdx.x & 63;
-  const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
-  if (h >= H) return;
-  const float a2 = A[h] * kLog2e;
-  constexpr int MAXSEG = 8;  // Q <= 512
-  const int nseg = (Q + 63) / 64;
-  float d[MAXSEG];
-#pragma unroll
-  for (int sg = 0; sg < MAXSEG; ++sg) {
-    const int i = sg * 64 + lane;
-    d[sg] = (sg < nseg && i < ci.z) ? dt[((size_t)ci.y + i) * H + h] : 0.f;
-  }
-  float *so = s_out + ((size_t)c * H + h) * Q;
-  float *dto = dt_out + ((size_t)c * H + h) * Q;
-  float *uo = u_out + ((size_t)c * H + h) * Q;
-  float carry = 0.f;
-#pragma unroll
-  for (int sg = 0; sg < MAXSEG; ++sg) {
-    if (sg >= nseg) break;
-    const int i = sg * 64 + lane;
-    float v = d[sg] * a2;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float t = __shfl_up(v, off, 64);
-      if (lane >= off) v += t;
-    }
-    v += carry;
-    // s at the last row of this row's 32-row block (Q is a multiple of 32)
-    const float sref = __shfl(v, lane | 31, 64);
-    if (i < Q) {
-      so[i] = v;
-      dto[i] = d[sg];
-      uo[i] = __builtin_amdgcn_exp2f(fminf(sref - v, 0.f)) * d[sg];
-    }
-    carry = __shfl(v, 63, 64);
-  }
-}
-
-// ---------------------------------------------------------- staging helpers
-// Copy rows [r0, r0+nrows) of a token-major operand into an LDS tile
-// (pitch `pitch` elements), optionally scaling row r by scale[r]; rows at or
-// beyond `len`, and columns at or beyond `width`, are zero.
-template <typename T, int WIDTH, int WPAD>
-__device__ __forceinline__ void stage_rows(T *tile, int pitch, const T *__restrict__ src,
-                                           size_t row_stride, int r0, int nrows, int len,
-                                           const float *scale) {
-  typedef typename Vec16<T>::type V;
-  constexpr int VN = Vec16<T>::n;
-  constexpr int VPR = WPAD / VN;  // 16-byte vectors per tile row
-  const int total = nrows * VPR;
-  for (int idx = threadIdx.x; idx < total; idx += blockDim.x) {
-    const int r = idx / VPR, v = idx % VPR;
-    const int row = r0 + r;
-    V val = vzero<V>();
-    if (row < len && v * VN < WIDTH) {
-      val = *reinterpret_cast<const V *>(src + (size_t)row * row_stride + v * VN);
-      if (scale) val = vscale(val, scale[row]);
-    }
-    *reinterpret_cast<V *>(tile + r * pitch + v * VN) = val;
-  }
-}
-
-constexpr int kJP = 128;  // token rows staged in LDS per phase (K2)
-
-// ------------------------------------------------------------ K2 chunk state
-// S_c^T[p][n] = sum_j X'[j][p] B[j][n],  X'[j] = 2^(s_end - s_j) dt_j x_j.
-// MFMA 16x16 tiles over (p, n); k = tokens, read from token-major LDS tiles
-// with the transpose read.  Output stored as S[c][h][n][p] (float32).
-// NW = min(16, tiles) waves; wave w owns tiles w, w+NW, ...
-template <int P, int N> struct StateTiles {
-  static constexpr int NT = (P / 16) * (N / 16);
-  static constexpr int NW = NT < 16 ? NT : 16;
-  static constexpr int TPW = NT / NW;
-};
-
-template <typename T, int P, int N>
-__global__ __launch_bounds__(1024) void k_chunk_state(const T *__restrict__ x, const T *__restrict__ B,
-                                                      const float *__restrict__ s_ws,
-                                                      const float *__restrict__ dt_ws,
-                                                      ChunkMap cmap, int nc, int H, int G, int Q,
-                                                      float *__restrict__ S_out) {
-  constexpr int XP = P + kTrPad, BP = N + kTrPad;
-  constexpr int NNT = N / 16, NW = StateTiles<P, N>::NW, TPW = StateTiles<P, N>::TPW;
-  const ChunkHead ch = xcd_chunk_head(H);
-  const int c = ch.c, hd = ch.h;
-  if (c >= nc) return;
-  const int4 ci = cmap(c);
-  if (ci.z <= 0) return;
-  const int g = (hd * G) / H;
-  const int JP = Q < kJP ? Q : kJP;
-  extern __shared__ __align__(16) char smem[];
-  T *Xs = reinterpret_cast<T *>(smem);
-  T *Bs = Xs + JP * XP;
-  float *w = reinterpret_cast<float *>(Bs + JP * BP);
-
-  const float *sc = s_ws + ((size_t)c * H + hd) * Q;
-  const float *dtc = dt_ws + ((size_t)c * H + hd) * Q;
-  const float s_end = sc[Q - 1];
-  for (int i = threadIdx.x; i < Q; i += blockDim.x)
-    w[i] = __builtin_amdgcn_exp2f(fminf(s_end - sc[i], 0.f)) * dtc[i];
-
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, grp = lane >> 4;
-  f4 acc[TPW];
-#pragma unroll
-  for (int t = 0; t < TPW; ++t) acc[t] = zero4();
-
-  const T *xs = x + ((size_t)ci.y * H + hd) * P;
-  const T *bs = B + ((size_t)ci.y * G + g) * N;
-  for (int ph = 0; ph < ci.z; ph += JP) {  // phases past the chunk length add nothing
-    __syncthreads();
-    stage_rows<T, P, P>(Xs, XP, xs, (size_t)H * P, ph, JP, ci.z, w);
-    stage_rows<T, N, N>(Bs, BP, bs, (size_t)G * N, ph, JP, ci.z, nullptr);
-    __syncthreads();
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-      const int tile = wave + NW * t;
-      const int pt = tile / NNT, nt = tile % NNT;
-      for (int k0 = 0; k0 < JP; k0 += 32) {
-        Frag<T> a = frag_kmaj(Xs, XP, pt * 16, k0 + 8 * grp, k0 + 8 * grp + 4);
-        Frag<T> b = frag_kmaj(Bs, BP, nt * 16, k0 + 8 * grp, k0 + 8 * grp + 4);
-        mma(acc[t], a, b);
-      }
-    }
-  }
-  float *so = S_out + ((size_t)c * H + hd) * (size_t)(N * P);
-#pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    const int tile = wave + NW * t;
-    const int pt = tile / NNT, nt = tile % NNT;
-    const int n = nt * 16 + (lane & 15), p = pt * 16 + 4 * grp;
-    st4(so + (size_t)n * P + p, acc[t]);
-  }
+  const int4 ci = locate_chunk(cu, nseq, 0, T, Q, c, seq_off, blockIdx.x == 0);
+  if (c < nc_max && threadIdx.x == 0) info_out[c] = ci.x < 0 ? make_int4(0, 0, 0, 0) : ci;
 }
 
 // ----------------------------------------------------------- K3 state pass
@@ -266,13 +129,21 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_state_pass(const float *__restrict__ S,
                                                     const float *__restrict__ s_ws,
                                                     const int *__restrict__ seq_off,
-                                                    const float *h0, float *h_out,
+                                                    ChunkMap cmap, const float *h0, float *h_out,
                                                     T *__restrict__ hin, int H, int NP, int Q) {
   constexpr int BATCH = 8;  // chunk states in flight per thread
   const int s = blockIdx.z, hd = blockIdx.y;
   const int e = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (e >= NP) return;
-  const int c0 = seq_off[s], c1 = seq_off[s + 1];
+  int c0, c1;  // chunks of sequence s
+  if (cmap.L > 0) {
+    const int cps = (cmap.L + Q - 1) / Q;
+    c0 = s * cps;
+    c1 = c0 + cps;
+  } else {
+    c0 = seq_off[s];
+    c1 = seq_off[s + 1];
+  }
   const size_t hofs = ((size_t)s * H + hd) * NP + e;
   f4 st = h0 ? ld4(h0 + hofs) : zero4();
   for (int cb = c0; cb < c1; cb += BATCH) {
@@ -534,30 +405,22 @@ static hipError_t run_prefill(const PrefillArgs &a, unsigned stages) {
   const int nc = (int)L.nc_max;
   const int L_dense = a.cu ? 0 : (int)(a.T / a.nseq);
   const ChunkMap cmap{info, L_dense, a.nseq, a.Q};
-  const int JP = a.Q < kJP ? a.Q : kJP;
   hipStream_t st = static_cast<hipStream_t>(a.stream);
 
-  if (stages & 1u) {
-    hipLaunchKernelGGL(k_chunk_cumsum, dim3(nc > 0 ? nc : 1, (a.H + 3) / 4), dim3(256), 0, st,
-                       a.dt, a.A, a.cu, a.nseq, L_dense, a.T, a.H, a.Q, nc, info, seq_off, s_ws,
-                       dt_ws, u_ws);
+  if ((stages & 3u) && a.cu && nc > 0) {  // packed batch: chunk map first
+    hipLaunchKernelGGL(k_chunk_map, dim3(nc), dim3(256), 0, st, a.cu, a.nseq, a.T, a.Q, nc, info,
+                       seq_off);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if ((stages & 2u) && nc > 0) {
-    const size_t lds = (size_t)JP * ((P + kTrPad) + (N + kTrPad)) * sizeof(T) + 4 * (size_t)a.Q;
-    auto kern = k_chunk_state<T, P, N>;
-    hipError_t e = set_lds_limit((const void *)kern);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(xcd_grid(nc, a.H)), dim3(64 * StateTiles<P, N>::NW), lds, st,
-                       (const T *)a.x, (const T *)a.B, s_ws, dt_ws, cmap, nc, a.H, a.G, a.Q, S);
-    e = hipGetLastError();
+  if ((stages & 3u) && nc > 0) {  // cumulative decay (stage 1) and chunk states (stage 2)
+    hipError_t e = launch_chunk_state(a, L, nc, (stages & 2u) != 0, st);
     if (e != hipSuccess) return e;
   }
   if (stages & 4u) {
     const int NP = N * P;
     hipLaunchKernelGGL(k_state_pass<T>, dim3((NP + 1023) / 1024, a.H, a.nseq), dim3(256), 0, st,
-                       S, s_ws, seq_off, a.h0, a.h_out, hin, a.H, NP, a.Q);
+                       S, s_ws, seq_off, cmap, a.h0, a.h_out, hin, a.H, NP, a.Q);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
