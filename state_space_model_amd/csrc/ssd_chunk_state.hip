@@ -13,17 +13,17 @@
 // Also written for the later stages: s, dt and u_j = 2^(s_r - s_j) dt_j (r the
 // last row of j's 32-row block), each [chunk][head][Q].
 //
-// One workgroup per (chunk, head, half of the n columns) -- two workgroups of
-// under 80 KB of LDS share a CU.  Every load of a phase (x rows, B rows, and
-// the strided dt column) goes straight to LDS in one batch, so the chunk costs
+// One workgroup per (chunk, head), or per (chunk, head, half of the n
+// columns) when there are few chunks and heads.  Every load of a phase (x
+// rows, B rows, and the strided dt column) goes straight to LDS in one batch:
 // one memory round trip before the scan, the x scaling and the MFMAs.
 #include "ssd_launch.h"
 #include "ssd_prefill_util.h"
 
 namespace ssd {
 
-template <typename T, int P, int N> struct StateCfg {
-  static constexpr int NH = N >= 64 ? 2 : 1;  // workgroups per (chunk, head)
+template <typename T, int P, int N, int NH_> struct StateCfg {
+  static constexpr int NH = NH_;              // workgroups per (chunk, head)
   static constexpr int NN = N / NH;           // n columns per workgroup
   static constexpr int VN = 16 / (int)sizeof(T);
   // pitch = width + one 16-byte slot: the transpose reads of lane groups 8
@@ -38,9 +38,9 @@ template <typename T, int P, int N> struct StateCfg {
     return (size_t)(tile_slots(jp, XS) + tile_slots(jp, BS)) * 16 +
            4 * (size_t)(3 * q + 64 + 16);  // dt (staged, padded), s, w, scan partials
   }
-  // rows staged per phase: the whole chunk if it fits in 80 KB, else halved
-  static int jp(int q) {
-    int j = q;
+  // rows staged per phase: at most `cap`, halved until the LDS fits in 80 KB
+  static int jp(int q, int cap) {
+    int j = q < cap ? q : cap;
     while (j > 32 && lds_bytes(j, q) > 80 * 1024) j /= 2;
     return j;
   }
@@ -59,13 +59,13 @@ __device__ __forceinline__ void scale_rows(T *tile, const float *w, int r0, int 
   }
 }
 
-template <typename T, int P, int N>
-__global__ __launch_bounds__((StateCfg<T, P, N>::THREADS)) void k_chunk_state(
+template <typename T, int P, int N, int NH>
+__global__ __launch_bounds__((StateCfg<T, P, N, NH>::THREADS)) void k_chunk_state(
     const T *__restrict__ x, const float *__restrict__ dt, const float *__restrict__ A,
     const T *__restrict__ B, ChunkMap cmap, int nc, int H, int G, int Q, int JP, int do_state,
     float *__restrict__ s_out, float *__restrict__ dt_out, float *__restrict__ u_out,
     float *__restrict__ S_out) {
-  typedef StateCfg<T, P, N> K;
+  typedef StateCfg<T, P, N, NH> K;
   constexpr int NW = K::NW, TPW = K::TPW, NNT = K::NN / 16;
   const ChunkHead ch = xcd_chunk_head(H * K::NH);
   const int c = ch.c, hd = ch.h / K::NH, half = ch.h % K::NH;
@@ -182,14 +182,14 @@ __global__ __launch_bounds__((StateCfg<T, P, N>::THREADS)) void k_chunk_state(
   }
 }
 
-template <typename T, int P, int N>
-static hipError_t run_state(const PrefillArgs &a, const WorkspaceLayout &L, int nc, bool state,
-                            hipStream_t st) {
-  typedef StateCfg<T, P, N> K;
-  const int jp = K::jp(a.Q);
+template <typename T, int P, int N, int NH>
+static hipError_t run_state(const PrefillArgs &a, const WorkspaceLayout &L, int nc, int jp_cap,
+                            bool state, hipStream_t st) {
+  typedef StateCfg<T, P, N, NH> K;
+  const int jp = K::jp(a.Q, jp_cap);
   const size_t lds = K::lds_bytes(jp, a.Q);
   if (lds > 160 * 1024) return hipErrorInvalidConfiguration;
-  const void *kern = (const void *)k_chunk_state<T, P, N>;
+  const void *kern = (const void *)k_chunk_state<T, P, N, NH>;
   hipError_t e = set_lds_limit(kern);
   if (e != hipSuccess) return e;
   char *ws = static_cast<char *>(a.workspace);
@@ -204,14 +204,28 @@ static hipError_t run_state(const PrefillArgs &a, const WorkspaceLayout &L, int 
   return hipLaunchKernel(kern, dim3(xcd_grid(nc, a.H * K::NH)), dim3(K::THREADS), args, lds, st);
 }
 
+// Shape of the launch.  Few (chunk, head) units: split the n columns over two
+// workgroups and stage up to 128 rows, so the whole grid is resident at once.
+// Many units: one workgroup per unit and 64-row phases -- small LDS lets four
+// workgroups share a CU, so some are always loading while others compute.
+template <typename T, int P, int N>
+static hipError_t run_state_auto(const PrefillArgs &a, const WorkspaceLayout &L, int nc,
+                                 bool state, hipStream_t st) {
+  const bool few = (long)nc * a.H < 2048;
+  if constexpr (N >= 64) {
+    if (few) return run_state<T, P, N, 2>(a, L, nc, 128, state, st);
+  }
+  return run_state<T, P, N, 1>(a, L, nc, few ? 128 : 64, state, st);
+}
+
 template <typename T, int P>
 static hipError_t state_N(const PrefillArgs &a, const WorkspaceLayout &L, int nc, bool s,
                           hipStream_t st) {
   switch (a.N) {
-    case 16: return run_state<T, P, 16>(a, L, nc, s, st);
-    case 32: return run_state<T, P, 32>(a, L, nc, s, st);
-    case 64: return run_state<T, P, 64>(a, L, nc, s, st);
-    case 128: return run_state<T, P, 128>(a, L, nc, s, st);
+    case 16: return run_state_auto<T, P, 16>(a, L, nc, s, st);
+    case 32: return run_state_auto<T, P, 32>(a, L, nc, s, st);
+    case 64: return run_state_auto<T, P, 64>(a, L, nc, s, st);
+    case 128: return run_state_auto<T, P, 128>(a, L, nc, s, st);
   }
   return hipErrorInvalidValue;
 }
