@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-large", action="store_true",
+                    help="skip the Mamba-2 2.7B layer prefill measurement")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--copy-calibration", type=int, metavar="MIB", default=0,
                     help="only run a plain device-to-device copy of MIB MiB ten times "
@@ -212,11 +214,13 @@ def _kernel_key(name, grid):
 
 PROFILE_COMMANDS = {
     "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d DIR/trace -o run -- "
-             "python bench.py --no-cpu-baseline --steps 50 --warmup 5 --quiet",
+             "python bench.py --no-cpu-baseline --no-large --steps 50 --warmup 5 --quiet",
     "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/fetch -o run -- "
-             "python bench.py --no-cpu-baseline --steps 50 --warmup 5 --quiet",
+             "python bench.py --no-cpu-baseline --no-large --steps 50 --warmup 5 --quiet",
     "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/write -o run -- "
-             "python bench.py --no-cpu-baseline --steps 50 --warmup 5 --quiet",
+             "python bench.py --no-cpu-baseline --no-large --steps 50 --warmup 5 --quiet",
+    "mfma": "rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 --output-format csv -d DIR/mfma -o run -- "
+            "python bench.py --no-cpu-baseline --no-large --steps 50 --warmup 5 --quiet",
     "cfetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/cfetch -o run -- "
               "python bench.py --copy-calibration 1024",
     "cwrite": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/cwrite -o run -- "
@@ -283,6 +287,30 @@ def summarize(directory):
                 f"kernel sources hash {traffic['source_hash']}\n"
                 f"commands (cwd = repository root, DIR = output directory):\n{cmds}\n\n"
                 + "\n".join(lines) + "\n")
+    mf_util, mf_flops = pmc("mfma", "MfmaUtil"), pmc("mfma", "MfmaFlopsBF16")
+    if mf_util:
+        from state_space_model_amd import inputs
+        w1 = inputs.WORKLOADS[1]
+        work = prefill_work(w1, w1.batch * w1.L, w1.batch, h0=False)
+        ml = []
+        for (kname, grid), vs in sorted(mf_util.items()):
+            wl, k = _kernel_key(kname, grid)
+            if wl != w1.name or k not in work:
+                continue
+            issued = float(np.mean(mf_flops.get((kname, grid), [0.0])))
+            algo = work[k]["flops"]
+            ml.append(f"{k:14s} MfmaUtil {np.mean(vs):6.2f} %   MfmaFlopsBF16 {issued / 1e9:9.3f}"
+                      f" GFLOP/dispatch   algorithmic {algo / 1e9:8.3f} GFLOP   issued/algorithmic"
+                      f" {issued / algo if algo else 0:5.2f}   ({len(vs)} dispatches)")
+        head = ["MFMA utilisation of the prefill kernels on the Mamba-2 130M layer workload",
+                "(4096 tokens, 24 heads, P 64, N 128, chunk 256, bf16), rocprofv3 derived",
+                "counters: MfmaUtil = sum(SQ_VALU_MFMA_BUSY_CYCLES) / (max(GRBM_GUI_ACTIVE)",
+                "x SIMDs) x 100 over each dispatch; MfmaFlopsBF16 = bf16 MFMA flops issued",
+                "(padding and masked blocks included), against the algorithmic flops.",
+                f"kernel sources hash {traffic['source_hash']}",
+                "command (cwd = repository root):", "  " + PROFILE_COMMANDS["mfma"], ""]
+        with open(os.path.join(ROOT, "profiles", "mfma_util_prefill130m.txt"), "w") as f:
+            f.write("\n".join(head + ml) + "\n")
     stats = glob.glob(os.path.join(directory, "trace", "**", "*kernel_stats.csv"), recursive=True)
     if stats:
         rows = _read_csv(stats[0])
@@ -301,6 +329,42 @@ def summarize(directory):
                     f"{'kernel':96s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}"
                     f" {'%':>6s}\n" + "\n".join(tl) + "\n")
     print(json.dumps(traffic, indent=1))
+
+
+def prefill_large(args, torch, inputs, ssd, dev):
+    """The Mamba-2 2.7B layer prefill (4 x 8192 tokens, 80 heads, h0 given):
+    whole-prefill time from HIP-graph replays, tokens/s and the algorithmic
+    bytes per second against the HBM peak."""
+    wl = inputs.WORKLOADS[2]
+    d = inputs.workload_inputs(2)
+    T = d["x"].shape[0]
+    nseq = len(d["cu_seqlens"]) - 1
+    op = torch.bfloat16
+    t = lambda a, dt=None: torch.from_numpy(np.ascontiguousarray(a)).to(dev) if dt is None \
+        else torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(dt)
+    run, y, h = ssd.prefill(t(d["x"], op), t(d["dt"]), t(d["A"]), t(d["B"], op), t(d["C"], op),
+                            t(d["D"]), t(d["h0"]), chunk=wl.chunk, nseq=nseq, prepare=True)
+    run()
+    torch.cuda.synchronize()
+    ms = graph_ms(torch, run, reps=10, per_graph=2)
+    kern = {n: round(graph_ms(torch, lambda st=st: run(st), reps=5, per_graph=2) * 1e3, 2)
+            for n, st in (("chunk_state", ssd.STAGE_CHUNK_CUMSUM | ssd.STAGE_CHUNK_STATE),
+                          ("state_pass", ssd.STAGE_STATE_PASS),
+                          ("chunk_scan", ssd.STAGE_CHUNK_SCAN))}
+    work = prefill_work(wl, T, nseq, h0=True)
+    # the method's bytes (each input read once, y and h_out written once) and flops
+    e = 2
+    nbytes = T * (wl.H * wl.P * (e + 4) + 2 * wl.G * wl.N * e + 4 * wl.H) + \
+        2 * nseq * wl.H * wl.N * wl.P * 4 + 8 * wl.H
+    flops = sum(w["flops"] for w in work.values())
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(args, f"2.7B layer prefill: {ms * 1e3:.1f} us")
+    return {"workload": wl.name, "tokens": T, "us": round(ms * 1e3, 2),
+            "tokens_per_s": round(T / (ms * 1e-3), 1), "algorithmic_bytes": nbytes,
+            "achieved_gb_per_s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "algorithmic_flops": flops,
+            "mfma_frac": round(flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4),
+            "kernels_us": kern}
 
 
 def main():
@@ -370,6 +434,28 @@ def main():
     kernels = [roofline(n, work[n], kern_ms[n], traffic) for n in work]
     dominant = max(kernels, key=lambda k: k["avg_us"])
 
+    # ---- the prefill from HBM: before each repeat a 512 MB buffer is written,
+    # which evicts the 256 MB last-level cache (5 untimed + 30 timed repeats)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    cold = []
+    for i in range(35):
+        flush.fill_(i & 0xFF)
+        ev0.record()
+        run_prefill()
+        ev1.record()
+        torch.cuda.synchronize()
+        if i >= 5:
+            cold.append(ev0.elapsed_time(ev1) * 1e3)
+    del flush
+    cold_us = float(np.median(cold))
+    prefill_cold = {"repeats": len(cold), "us_median": round(cold_us, 2),
+                    "us_mean": round(float(np.mean(cold)), 2),
+                    "us_std": round(float(np.std(cold)), 2),
+                    "tokens_per_s": round(T / (cold_us * 1e-6), 1)}
+
+    large = None if args.no_large else prefill_large(args, torch, inputs, ssd, dev)
+
     # ---- decode workload (the decode half of the metric)
     w3 = inputs.WORKLOADS[3]
     d3 = inputs.workload_inputs(3)
@@ -416,6 +502,8 @@ def main():
         "ms_per_step_graph": round(ms_step_graph, 5),
         "prefill_mfma_util": round(mfma_util, 4),
         "kernels": kernels,
+        "prefill_cold_cache": prefill_cold,
+        "prefill_2p7b_layer": large,
         "decode": decode,
         "cpu_baseline": cpu,
     }

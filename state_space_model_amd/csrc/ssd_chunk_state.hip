@@ -59,6 +59,65 @@ __device__ __forceinline__ void scale_rows(T *tile, const float *w, int r0, int 
   }
 }
 
+// The chunk's cumulative decay from its dt column (dt_l, staged in LDS; rows
+// past the chunk length hold 0): s_l = log2(e) A cumsum(dt) -- R consecutive
+// rows per thread, then a block scan -- and w_l[j] = 2^(s_end - s_j) dt_j.
+// With `emit`, s, dt and u_j = 2^(s_r - s_j) dt_j (r the last row of j's
+// 32-row block) are written at out_off of s_out / dt_out / u_out.  Contains
+// block barriers: every thread of the block calls it.  Returns s_end.
+template <int THREADS>
+__device__ __forceinline__ float decay_scan(const float *dt_l, float *s_l, float *w_l,
+                                            float *part, int Q, float a2, bool emit,
+                                            size_t out_off, float *__restrict__ s_out,
+                                            float *__restrict__ dt_out,
+                                            float *__restrict__ u_out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int R = (Q + THREADS - 1) / THREADS;  // 1 or 2 (Q <= 512)
+  float v0 = 0.f, v1 = 0.f;
+  if (tid * R < Q) v0 = dt_l[tid * R] * a2;
+  if (R > 1 && tid * R + 1 < Q) v1 = v0 + dt_l[tid * R + 1] * a2;
+  const float tot = R > 1 ? v1 : v0;
+  float incl = tot;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float t = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += t;
+  }
+  if (lane == 63) part[wave] = incl;
+  __syncthreads();
+  float pre = 0.f;
+  for (int w = 0; w < wave; ++w) pre += part[w];
+  const float excl = pre + incl - tot;
+  if (tid * R < Q) s_l[tid * R] = excl + v0;
+  if (R > 1 && tid * R + 1 < Q) s_l[tid * R + 1] = excl + v1;
+  __syncthreads();
+  // padded rows have dt = 0 and so weight 0
+  const float s_end = s_l[Q - 1];
+  for (int j = tid; j < Q; j += THREADS) {
+    const float sj = s_l[j], dj = dt_l[j];
+    w_l[j] = __builtin_amdgcn_exp2f(fminf(s_end - sj, 0.f)) * dj;
+    if (emit) {
+      s_out[out_off + j] = sj;
+      dt_out[out_off + j] = dj;
+      u_out[out_off + j] = __builtin_amdgcn_exp2f(fminf(s_l[j | 31] - sj, 0.f)) * dj;
+    }
+  }
+  return s_end;
+}
+
+// Direct loads of a chunk's dt column (rows past `len` read 0) into dt_l.
+__device__ __forceinline__ void dma_dt(float *dt_l, const float *__restrict__ dt, size_t row0,
+                                       int H, int hd, int Q, int len, int wave, int nw) {
+  const int lane = threadIdx.x & 63;
+  for (int base = wave * 64; base < Q; base += nw * 64) {
+    const int i = base + lane;
+    const void *gp = i < len ? (const void *)(dt + (row0 + i) * H + hd) : (const void *)g_zero16;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)gp,
+                                     (__attribute__((address_space(3))) void *)(dt_l + base), 4,
+                                     0, 0);
+  }
+}
+
 template <typename T, int P, int N, int NH>
 __global__ __launch_bounds__((StateCfg<T, P, N, NH>::THREADS)) void k_chunk_state(
     const T *__restrict__ x, const float *__restrict__ dt, const float *__restrict__ A,
@@ -90,14 +149,7 @@ __global__ __launch_bounds__((StateCfg<T, P, N, NH>::THREADS)) void k_chunk_stat
   const T *bs = B + (size_t)ci.y * bstride + (size_t)g * N + half * K::NN;
 
   // ---- one batch of direct loads: the dt column, first phase of x and B
-  for (int base = wave * 64; base < Q; base += NW * 64) {
-    const int i = base + lane;
-    const void *gp = i < len ? (const void *)(dt + ((size_t)ci.y + i) * H + hd)
-                             : (const void *)g_zero16;
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)gp,
-                                     (__attribute__((address_space(3))) void *)(dt_l + base), 4,
-                                     0, 0);
-  }
+  dma_dt(dt_l, dt, (size_t)ci.y, H, hd, Q, len, wave, NW);
   if (do_state) {
     dma_tile<T, K::XS, K::XD>(Xs, xs, xstride, JP, len, wave, NW);
     dma_tile<T, K::BS, K::BD>(Bs, bs, bstride, JP, len, wave, NW);
@@ -105,41 +157,8 @@ __global__ __launch_bounds__((StateCfg<T, P, N, NH>::THREADS)) void k_chunk_stat
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  // ---- s = log2(e) A cumsum(dt): R consecutive rows per thread, block scan
-  const float a2 = A[hd] * kLog2e;
-  const int R = (Q + K::THREADS - 1) / K::THREADS;  // 1 or 2 (Q <= 512)
-  float v0 = 0.f, v1 = 0.f;
-  if (tid * R < Q) v0 = dt_l[tid * R] * a2;
-  if (R > 1 && tid * R + 1 < Q) v1 = v0 + dt_l[tid * R + 1] * a2;
-  float tot = R > 1 ? v1 : v0;
-  float incl = tot;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float t = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += t;
-  }
-  if (lane == 63) part[wave] = incl;
-  __syncthreads();
-  float pre = 0.f;
-  for (int w = 0; w < wave; ++w) pre += part[w];
-  const float excl = pre + incl - tot;
-  if (tid * R < Q) s_l[tid * R] = excl + v0;
-  if (R > 1 && tid * R + 1 < Q) s_l[tid * R + 1] = excl + v1;
-  __syncthreads();
-
-  // ---- decay weights: w_j (to the chunk end) here, u_j (to the block end) for
-  // the output stage; padded rows have dt = 0 and so weight 0
-  const float s_end = s_l[Q - 1];
-  const size_t o = ((size_t)c * H + hd) * Q;
-  for (int j = tid; j < Q; j += K::THREADS) {
-    const float sj = s_l[j], dj = dt_l[j];
-    w_l[j] = __builtin_amdgcn_exp2f(fminf(s_end - sj, 0.f)) * dj;
-    if (half == 0) {
-      s_out[o + j] = sj;
-      dt_out[o + j] = dj;
-      u_out[o + j] = __builtin_amdgcn_exp2f(fminf(s_l[j | 31] - sj, 0.f)) * dj;
-    }
-  }
+  decay_scan<K::THREADS>(dt_l, s_l, w_l, part, Q, A[hd] * kLog2e, half == 0,
+                         ((size_t)c * H + hd) * Q, s_out, dt_out, u_out);
   if (!do_state) return;
   __syncthreads();
 

@@ -10,26 +10,29 @@ from state_space_model_amd import inputs
 pytestmark = pytest.mark.gpu
 
 
-class scan_kernel:
-    """Force the chunk-scan kernel choice (SSD_PREFILL_SCAN=heads|rows) for a block."""
+class kernels:
+    """Force the chunk-scan kernel for a block (SSD_PREFILL_SCAN=heads|rows);
+    "auto" leaves the library's choice."""
 
-    def __init__(self, mode):
-        self.mode = mode
+    def __init__(self, scan="auto"):
+        self.want = {"SSD_PREFILL_SCAN": scan}
 
     def __enter__(self):
         import os
-        self.old = os.environ.get("SSD_PREFILL_SCAN")
-        if self.mode == "auto":
-            os.environ.pop("SSD_PREFILL_SCAN", None)
-        else:
-            os.environ["SSD_PREFILL_SCAN"] = self.mode
+        self.old = {k: os.environ.get(k) for k in self.want}
+        for k, v in self.want.items():
+            if v == "auto":
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
 
     def __exit__(self, *exc):
         import os
-        if self.old is None:
-            os.environ.pop("SSD_PREFILL_SCAN", None)
-        else:
-            os.environ["SSD_PREFILL_SCAN"] = self.old
+        for k, v in self.old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
 
 
 def _gpu(d, dtype, chunk, with_h0=True, **kw):
@@ -59,10 +62,10 @@ SMALL = [  # (lengths, H, P, N, G, chunk, h0)
 ]
 
 
-SCAN_MODES = [("f32", "auto"), ("bf16", "rows"), ("bf16", "heads")]
+MODES = [("f32", "auto"), ("bf16", "rows"), ("bf16", "heads")]
 
 
-@pytest.mark.parametrize("dtype,scan", SCAN_MODES)
+@pytest.mark.parametrize("dtype,scan", MODES)
 @pytest.mark.parametrize("case", range(len(SMALL)))
 def test_prefill_small(dtype, scan, case):
     """Every small shape in float32, and in bfloat16 through both chunk-scan
@@ -71,7 +74,7 @@ def test_prefill_small(dtype, scan, case):
     log(f"prefill small dtype={dtype} scan={scan} lengths={lengths} H={H} P={P} N={N} G={G}"
         f" Q={chunk}")
     d = inputs.prefill_inputs(H, P, N, G, lengths, 200 + case, dtype=dtype, h0=h0)
-    with scan_kernel(scan):
+    with kernels(scan):
         y, ho = _gpu(d, dtype, chunk)
     ry, rh = _ref(d)
     ey, eh = maxabs(y, ry), maxabs(ho, rh)
@@ -97,7 +100,7 @@ def test_prefill_130m_layer_workload():
     ry, rh = _ref(d)
     ssm = np.max(np.abs(ry - d["D"][None, :, None] * d["x"]))
     for scan in ("auto", "heads"):
-        with scan_kernel(scan):
+        with kernels(scan):
             y, ho = _gpu(d, "bf16", w.chunk)
         ey, eh = maxabs(y, ry), maxabs(ho, rh)
         log(f"  scan={scan}: max|dy|={ey:.3g} max|dh|={eh:.3g} (max|y_ssm|={ssm:.3g})")
@@ -114,7 +117,7 @@ def test_prefill_2p7b_layer_workload():
     ds = select_heads(d, heads, w.G)
     ry, rh = _ref(ds)
     for scan in ("auto", "rows"):
-        with scan_kernel(scan):
+        with kernels(scan):
             y, ho = _gpu(d, "bf16", w.chunk)
         ey, eh = maxabs(y[:, heads], ry), maxabs(ho[:, heads], rh)
         log(f"  scan={scan}: max|dy|={ey:.3g} max|dh|={eh:.3g}")
@@ -132,7 +135,7 @@ def test_prefill_long_context_varlen_chunk_sweep():
     ry, rh = _ref(ds)
     for scan in ("auto", "rows"):
         for q in w.chunks:
-            with scan_kernel(scan):
+            with kernels(scan):
                 y, ho = _gpu(d, "bf16", q)
             ey, eh = maxabs(y[:, heads], ry), maxabs(ho[:, heads], rh)
             log(f"  scan={scan} Q={q}: max|dy|={ey:.3g} max|dh|={eh:.3g}")
@@ -156,23 +159,32 @@ def test_stages_separately_equal_one_call():
     assert torch.equal(y1, y2) and torch.equal(h1, h2)
 
 
-def test_deterministic_and_varlen_equals_solo():
+@pytest.mark.parametrize("scan", ["rows", "heads"])
+def test_deterministic_and_varlen_equals_solo(scan):
+    """Run-to-run bitwise determinism; a packed batch equals each sequence run
+    alone, bitwise; h_out may be the h0 buffer itself."""
     import torch
     from state_space_model_amd import ssd
     lengths = [333, 64, 1, 900]
     d = inputs.prefill_inputs(4, 64, 128, 2, lengths, 9, dtype="bf16", h0=True)
     t = dev_inputs(d, "bf16")
-    run = lambda: ssd.prefill(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["h0"],
-                              chunk=256, cu_seqlens=t["cu_seqlens"])
-    y1, h1 = run()
-    y2, h2 = run()
-    assert torch.equal(y1, y2) and torch.equal(h1, h2)
-    cu = d["cu_seqlens"]
-    for s in range(len(lengths)):
-        sl = slice(int(cu[s]), int(cu[s + 1]))
-        ys, hs = ssd.prefill(t["x"][sl], t["dt"][sl], t["A"], t["B"][sl], t["C"][sl], t["D"],
-                             t["h0"][s:s + 1].contiguous(), chunk=256)
-        assert torch.equal(ys, y1[sl]) and torch.equal(hs[0], h1[s])
+    with kernels(scan):
+        run = lambda: ssd.prefill(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["h0"],
+                                  chunk=256, cu_seqlens=t["cu_seqlens"])
+        y1, h1 = run()
+        y2, h2 = run()
+        assert torch.equal(y1, y2) and torch.equal(h1, h2)
+        cu = d["cu_seqlens"]
+        for s in range(len(lengths)):
+            sl = slice(int(cu[s]), int(cu[s + 1]))
+            ys, hs = ssd.prefill(t["x"][sl], t["dt"][sl], t["A"], t["B"][sl], t["C"][sl], t["D"],
+                                 t["h0"][s:s + 1].contiguous(), chunk=256)
+            assert torch.equal(ys, y1[sl]) and torch.equal(hs[0], h1[s])
+        hbuf = t["h0"].clone()
+        y3, _ = ssd.prefill(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], hbuf, chunk=256,
+                            cu_seqlens=t["cu_seqlens"], h_out=hbuf)
+        torch.cuda.synchronize()
+        assert torch.equal(y3, y1) and torch.equal(hbuf, h1)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
