@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector (packed): 256 CU x 4 SIMD x 16 lanes x 2 x 2 x 2.4 GHz
 FP32_PEAK_TFLOPS = 157.3     # MI355X fp32 vector
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -208,6 +209,8 @@ def _kernel_key(name, grid):
             if k == "decode_step":  # the two decode workloads differ in grid size
                 return ("codestral-7b-decode-step" if int(grid) > 24 * 256 else
                         "mamba2-130m-layer-prefill"), k
+            if k == "decode_multi_step":
+                return "codestral-7b-decode-step", k
             return "mamba2-130m-layer-prefill", k
     return None, None
 
@@ -483,6 +486,30 @@ def main():
               "gb_per_s": dec_rl["achieved"], "frac_hbm_peak": dec_rl["frac"],
               "tokens_per_s": round(w3.batch / (ms_dec * 1e-3), 1), "roofline": dec_rl}
 
+    # ---- the same 128 steps in one launch (inputs staged for every step): the
+    # state crosses HBM once, the update runs at fp32 vector speed
+    h3m = t(d3["h"])
+    y3m = torch.empty((S3, w3.batch, w3.H, w3.P), dtype=torch.float32, device=dev)
+    run_multi, _ = ssd.step_multi(x3, dt3, A3, B3, C3, D3, h3m, y=y3m, prepare=True)
+    run_multi()
+    torch.cuda.synchronize()
+    ms_multi = graph_ms(torch, run_multi, reps=5, per_graph=1)
+    elems = w3.batch * w3.H * w3.N * w3.P
+    mflops = 5.0 * elems * S3
+    mbytes = 2 * elems * 4 + S3 * (w3.batch * w3.H * w3.P * 8 + 2 * w3.batch * w3.G * w3.N * 4 +
+                                   w3.batch * w3.H * 4)
+    tf = mflops / (ms_multi * 1e-3) / 1e12
+    decode_multi = {"workload": w3.name, "steps": S3, "us_total": round(ms_multi * 1e3, 2),
+                    "us_per_step": round(ms_multi * 1e3 / S3, 3),
+                    "tokens_per_s": round(w3.batch * S3 / (ms_multi * 1e-3), 1),
+                    "speedup_vs_single_steps": round(ms_dec_graph * S3 / ms_multi, 2),
+                    "roofline": {"bound": "alu", "achieved": round(tf, 2),
+                                 "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                 "frac": round(tf / FP32_VECTOR_PEAK_TFLOPS, 4),
+                                 "traffic": None, "kernel": "step_multi",
+                                 "algorithmic_bytes": mbytes}}
+    del h3m, y3m
+
     # MFMA utilisation estimate of the prefill (algorithmic flops / bf16 peak)
     fl = sum(work[n]["flops"] for n in ("chunk_state", "chunk_scan"))
     mfma_util = fl / (sum(kern_ms[n] for n in kern_ms if n != "decode_step") * 1e-3) / \
@@ -505,6 +532,7 @@ def main():
         "prefill_cold_cache": prefill_cold,
         "prefill_2p7b_layer": large,
         "decode": decode,
+        "decode_multi_step": decode_multi,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -133,6 +133,28 @@ int ssd_step(const void *x, const float *dt, const float *A, const void *B, cons
              const float *D, float *h, float *y, int batch, int H, int P, int N, int G,
              ssd_dtype_t dtype, void *stream);
 
+/*
+ * `steps` decode tokens for `batch` independent states in one launch, over
+ * inputs staged for every step; the state is updated in place.  Equal to
+ * `steps` successive ssd_step() calls with the slices of step t.
+ *
+ *   x   [steps][batch][H][P]  dtype;  dt [steps][batch][H] float32
+ *   A, D [H] float32;  B, C [steps][batch][G][N]  dtype
+ *   h   [batch][H][N][P] float32, read at the start, overwritten at the end
+ *   y   [steps][batch][H][P] float32 (must not alias any input)
+ *
+ * The state stays on chip for all steps: it crosses HBM once instead of twice
+ * per step (the multi-step decode over pre-staged inputs that Compiler-First
+ * State Space Duality and Portable O(1) Autoregressive Caching for Inference,
+ * Figure 1 and Table 10, motivates by the cost of per-token launches; the
+ * steps run as a stream over time as in Recurrence Scan, "The schedule").
+ * Supported: P in {16,32,64,128}, N in {16,32,64,128}, H % G == 0.
+ * steps = 0 or batch = 0 does nothing.
+ */
+int ssd_step_multi(const void *x, const float *dt, const float *A, const void *B, const void *C,
+                   const float *D, float *h, float *y, int steps, int batch, int H, int P, int N,
+                   int G, ssd_dtype_t dtype, void *stream);
+
 /* Message for the last non-zero return on the calling thread ("" if none). */
 const char *ssd_last_error(void);
 

@@ -2,7 +2,7 @@
 
 The compute runs in the HIP library ``libssd.so`` (built from ``csrc/``);
 ``ssd.py`` is the thin ctypes binding over its C ABI (``include/ssd.h``).
-Importing this package does not load the library; ``prefill``/``step``
+Importing this package does not load the library; ``prefill``/``step``/``step_multi``
 load it on first use and raise if it is missing.
 """
 
@@ -15,3 +15,8 @@ def prefill(*args, **kwargs):
 def step(*args, **kwargs):
     from . import ssd
     return ssd.step(*args, **kwargs)
+
+
+def step_multi(*args, **kwargs):
+    from . import ssd
+    return ssd.step_multi(*args, **kwargs)

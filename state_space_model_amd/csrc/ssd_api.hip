@@ -119,6 +119,26 @@ int ssd_step(const void *x, const float *dt, const float *A, const void *B, cons
   return SSD_OK;
 }
 
+int ssd_step_multi(const void *x, const float *dt, const float *A, const void *B, const void *C,
+                   const float *D, float *h, float *y, int steps, int batch, int H, int P, int N,
+                   int G, ssd_dtype_t dtype, void *stream) {
+  g_err[0] = 0;
+  if (dtype != SSD_F32 && dtype != SSD_BF16) return fail(SSD_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (steps < 0) return fail(SSD_ERR_INVALID_ARG, "steps must be >= 0 (got %d)", steps);
+  if (batch < 0) return fail(SSD_ERR_INVALID_ARG, "batch must be >= 0 (got %d)", batch);
+  if (H < 1 || G < 1 || H % G != 0) return fail(SSD_ERR_INVALID_ARG, "need H >= 1, G >= 1, H %% G == 0 (H=%d G=%d)", H, G);
+  if (!pow2_in(P, 16, 128)) return fail(SSD_ERR_UNSUPPORTED, "headdim P=%d not in {16,32,64,128}", P);
+  if (!pow2_in(N, 16, 128)) return fail(SSD_ERR_UNSUPPORTED, "d_state N=%d not in {16,32,64,128}", N);
+  if (batch > 65535) return fail(SSD_ERR_UNSUPPORTED, "batch %d > 65535", batch);
+  if ((long long)H * (P / (P > 64 ? 64 : P)) > 0x7fffffff) return fail(SSD_ERR_UNSUPPORTED, "too many heads");
+  if (batch > 0 && (!h || (steps > 0 && (!x || !dt || !A || !B || !C || !D || !y))))
+    return fail(SSD_ERR_INVALID_ARG, "null pointer argument");
+  ssd::MultiStepArgs a{x, dt, A, B, C, D, h, y, steps, batch, H, P, N, G, dtype == SSD_BF16, stream};
+  hipError_t e = ssd::launch_step_multi(a);
+  if (e != hipSuccess) return fail(SSD_ERR_HIP, "HIP error: %s", hipGetErrorString(e));
+  return SSD_OK;
+}
+
 const char *ssd_last_error(void) { return g_err; }
 
 }  // extern "C"

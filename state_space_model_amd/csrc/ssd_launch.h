@@ -64,4 +64,16 @@ struct StepArgs {
 };
 hipError_t launch_step(const StepArgs &a);
 
+struct MultiStepArgs {
+  const void *x;
+  const float *dt, *A;
+  const void *B, *C;
+  const float *D;
+  float *h, *y;
+  int steps, batch, H, P, N, G;
+  bool bf16;
+  void *stream;
+};
+hipError_t launch_step_multi(const MultiStepArgs &a);
+
 }  // namespace ssd

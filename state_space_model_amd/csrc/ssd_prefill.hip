@@ -176,8 +176,8 @@ __global__ __launch_bounds__(256) void k_state_pass(const float *__restrict__ S,
 // waves: part z owns tiles t_k = 2k + (z ^ (k & 1)), whose causal work is k + 1
 // j-blocks in both parts, and wave w takes k = w for w < NW/2, else
 // k = 3NW/2 - 1 - w, so the waves sharing a SIMD carry equal work.  At Q = 256
-// a part has 8 waves and stages 128 rows per phase (under 80 KB of LDS), so two
-// workgroups share a CU and one loads while the other computes.
+// a part has 8 waves and stages 64 rows per phase (under 53 KB of LDS), so
+// three workgroups share a CU and some load while others compute.
 // Per output tile (all accumulation in float32):
 //   Y^T[p][i]  = 2^(s_i) (H_in^T C^T)[p][i]             k = n    (A: H_in tile, transpose read)
 //             += sum_j X^T[p][j] M^T[j][i]              k = j    (A: X tile, transpose read)
@@ -200,13 +200,14 @@ template <typename T, int P, int N> struct ScanCfg {
     return (size_t)(tile_slots(NK, HS) + tile_slots(jp, BS) + tile_slots(jp, XS)) * 16 +
            12 * (size_t)q;
   }
-  // staged rows per phase for chunk length q and `threads`: up to 128 rows in
-  // blocks of at most 512 threads (two workgroups per CU), up to 256 rows
-  // otherwise, halved until the LDS fits
+  // staged rows per phase for chunk length q and `threads`: up to 64 rows in
+  // blocks of at most 512 threads (under 53 KB, so three workgroups share a CU
+  // and the row-split grid of a small batch is resident at once), up to 256
+  // rows otherwise, halved until the LDS fits
   static int jp(int q, int threads) {
-    const int lim = threads <= 512 ? 128 : 256;
+    const int lim = threads <= 512 ? 64 : 256;
     int j = q < lim ? q : lim;
-    const size_t cap = threads <= 512 ? 80 * 1024 : 160 * 1024;
+    const size_t cap = threads <= 512 ? 53 * 1024 : 160 * 1024;
     while (j > 32 && lds_bytes(j, q) > cap) j /= 2;
     return j;
   }

@@ -113,4 +113,127 @@ hipError_t launch_step(const StepArgs &a) {
   return a.bf16 ? run_step<bf16>(a) : run_step<float>(a);
 }
 
+// ------------------------------------------------------------------------
+// Many decode steps in one launch, over inputs staged for every step:
+//   x [S][b][H][P], dt [S][b][H], B, C [S][b][G][N], y [S][b][H][P]
+// equal to S successive single steps.  One wave per (b, h, 64-column part of
+// p) keeps its slice of the state in registers for all S steps, so the state
+// crosses HBM once (read at the start, written at the end) instead of twice per
+// step; the work per step is then the 5 flops per state element of the update
+// and the output (the fp32 vector units bound it).  This is the recurrence run
+// as a stream over time, as Recurrence Scan does ("The schedule"); a step's
+// inputs are fetched while the previous step is computed.
+//
+// Lane l: column group c = l % (PL/4) (4 consecutive p), row group
+// r = l / (PL/4) owning rows [r RPL, (r+1) RPL); y[p] is summed over the row
+// groups with xor shuffles.
+template <typename T, int PL, int N>
+__global__ __launch_bounds__(64) void k_step_multi(const T *__restrict__ x,
+                                                   const float *__restrict__ dt,
+                                                   const float *__restrict__ A,
+                                                   const T *__restrict__ B, const T *__restrict__ C,
+                                                   const float *__restrict__ D,
+                                                   float *__restrict__ h, float *__restrict__ y,
+                                                   int steps, int batch, int H, int P, int G) {
+  constexpr int TPR = PL / 4;       // lanes per state row
+  constexpr int RG = 64 / TPR;      // row groups
+  constexpr int RPL = N / RG;       // rows per lane
+  static_assert(RPL >= 1 && N % RG == 0, "rows per lane");
+  __shared__ __align__(16) float bc[2 * N];  // B then C of the current step
+  const int lane = threadIdx.x, c = lane % TPR, r = lane / TPR;
+  const int parts = P / PL;
+  const int hd = blockIdx.x / parts, part = blockIdx.x % parts, b = blockIdx.y;
+  const int g = (hd * G) / H;
+  const int p0 = part * PL + 4 * c;
+  const size_t bh = (size_t)b * H + hd;
+  const size_t xs = (size_t)batch * H * P, ds = (size_t)batch * H, bs = (size_t)batch * G * N;
+  const float A2 = A[hd], dv = D[hd];
+
+  float *hp = h + bh * (size_t)N * P + p0;
+  f4 st[RPL];
+#pragma unroll
+  for (int k = 0; k < RPL; ++k) st[k] = ld4(hp + (size_t)(r * RPL + k) * P);
+
+  // step inputs, prefetched one step ahead: lanes < N/4 carry B, the next N/4 C
+  const bool bl = lane < N / 4, cl = !bl && lane < N / 2;
+  const T *bsrc = B + ((size_t)b * G + g) * N + 4 * lane;
+  const T *csrc = C + ((size_t)b * G + g) * N + 4 * (lane - N / 4);
+  auto fetch = [&](int t, f4 &xv, float &dtv, f4 &bcv) {
+    xv = ld4f(x + t * xs + bh * P + p0);
+    dtv = dt[t * ds + bh];
+    bcv = bl ? ld4f(bsrc + t * bs) : cl ? ld4f(csrc + t * bs) : zero4();
+  };
+  f4 xv, bcv;
+  float dtv;
+  if (steps > 0) fetch(0, xv, dtv, bcv);
+  for (int t = 0; t < steps; ++t) {
+    if (bl || cl) st4(bc + 4 * lane, bcv);
+    __syncthreads();
+    const f4 xc = xv;
+    const float dtc = dtv;
+    if (t + 1 < steps) fetch(t + 1, xv, dtv, bcv);
+    const float a = expf(fminf(dtc * A2, 0.f));
+    f4 dx, yp = zero4();
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dx[e] = dtc * xc[e];
+#pragma unroll
+    for (int k = 0; k < RPL; ++k) {
+      const float bn = bc[r * RPL + k], cn = bc[N + r * RPL + k];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        st[k][e] = a * st[k][e] + dx[e] * bn;
+        yp[e] += cn * st[k][e];
+      }
+    }
+#pragma unroll
+    for (int off = TPR; off < 64; off <<= 1)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) yp[e] += __shfl_xor(yp[e], off, 64);
+    if (r == 0) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) yp[e] += dv * xc[e];
+      st4(y + t * xs + bh * P + p0, yp);
+    }
+    __syncthreads();  // bc is rewritten by the next step
+  }
+#pragma unroll
+  for (int k = 0; k < RPL; ++k) st4(hp + (size_t)(r * RPL + k) * P, st[k]);
+}
+
+template <typename T, int PL>
+static hipError_t multi_N(const MultiStepArgs &a, hipStream_t st) {
+  dim3 grid(a.H * (a.P / PL), a.batch);
+#define SSD_LAUNCH(n)                                                                            \
+  hipLaunchKernelGGL((k_step_multi<T, PL, n>), grid, dim3(64), 0, st, (const T *)a.x, a.dt, a.A, \
+                     (const T *)a.B, (const T *)a.C, a.D, a.h, a.y, a.steps, a.batch, a.H, a.P,  \
+                     a.G);                                                                       \
+  break;
+  switch (a.N) {
+    case 16: SSD_LAUNCH(16)
+    case 32: SSD_LAUNCH(32)
+    case 64: SSD_LAUNCH(64)
+    case 128: SSD_LAUNCH(128)
+    default: return hipErrorInvalidValue;
+  }
+#undef SSD_LAUNCH
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t run_multi(const MultiStepArgs &a) {
+  hipStream_t st = static_cast<hipStream_t>(a.stream);
+  switch (a.P) {
+    case 16: return multi_N<T, 16>(a, st);
+    case 32: return multi_N<T, 32>(a, st);
+    case 64: return multi_N<T, 64>(a, st);
+    case 128: return multi_N<T, 64>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_step_multi(const MultiStepArgs &a) {
+  if (a.batch == 0 || a.steps == 0) return hipSuccess;
+  return a.bf16 ? run_multi<bf16>(a) : run_multi<float>(a);
+}
+
 }  // namespace ssd

@@ -19,7 +19,7 @@ STAGE_ALL = 15
 ERRORS = {0: "SSD_OK", -1: "SSD_ERR_INVALID_ARG", -2: "SSD_ERR_UNSUPPORTED",
           -3: "SSD_ERR_WORKSPACE", -4: "SSD_ERR_HIP"}
 EXPORTS = ("ssd_scan_prefill_workspace", "ssd_scan_prefill", "ssd_scan_prefill_stages",
-           "ssd_step", "ssd_last_error")
+           "ssd_step", "ssd_step_multi", "ssd_last_error")
 
 _lib = None
 
@@ -50,6 +50,9 @@ def load(path=LIB_PATH):
     lib.ssd_scan_prefill_stages.restype = i32
     lib.ssd_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
     lib.ssd_step.restype = i32
+    lib.ssd_step_multi.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                   vp]
+    lib.ssd_step_multi.restype = i32
     lib.ssd_last_error.argtypes = []
     lib.ssd_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -212,4 +215,32 @@ def step(x, dt, A, B, C, D, h, y=None, prepare=False):
     if prepare:
         return Prepared(load().ssd_step, args, keep=(x, dt, A, B, C, D, h, y)), y
     _check(load().ssd_step(*args, _stream()))
+    return y
+
+
+def step_multi(x, dt, A, B, C, D, h, y=None, prepare=False):
+    """`steps` decode tokens in one launch; h [b,H,N,P] float32 is updated in
+    place.  x [S,b,H,P], dt [S,b,H], B/C [S,b,G,N].  Returns y [S,b,H,P]."""
+    S, b, H, P = x.shape
+    G, N = B.shape[-2], B.shape[-1]
+    dev = x.device
+    _need(x, "x", dev=dev)
+    code = _dtype_code(x)
+    for t, n in ((B, "B"), (C, "C")):
+        _need(t, n, x.dtype, dev)
+    for t, n in ((dt, "dt"), (A, "A"), (D, "D"), (h, "h")):
+        _need(t, n, torch.float32, dev)
+    if tuple(h.shape) != (b, H, N, P) or tuple(B.shape) != (S, b, G, N) or \
+            tuple(C.shape) != (S, b, G, N):
+        raise ValueError("h must be [b,H,N,P], B/C [S,b,G,N]")
+    if tuple(dt.shape) != (S, b, H):
+        raise ValueError("dt must be [S,b,H]")
+    if y is None:
+        y = torch.empty((S, b, H, P), dtype=torch.float32, device=dev)
+    _need(y, "y", torch.float32, dev)
+    args = (_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h), _ptr(y), S, b, H, P,
+            N, G, code)
+    if prepare:
+        return Prepared(load().ssd_step_multi, args, keep=(x, dt, A, B, C, D, h, y)), y
+    _check(load().ssd_step_multi(*args, _stream()))
     return y

@@ -103,6 +103,27 @@ def test_step_rejects_before_launch(kw, code, frag):
     assert rc == code and frag in lib.ssd_last_error().decode()
 
 
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(H=6, G=4), -1, "H % G"),
+    (dict(P=8), -2, "headdim"),
+    (dict(N=48), -2, "d_state"),
+    (dict(N=256), -2, "d_state"),
+    (dict(steps=-1), -1, "steps"),
+    (dict(batch=-1), -1, "batch"),
+    (dict(x=None), -1, "null"),
+    (dict(dtype=3), -1, "dtype"),
+])
+def test_step_multi_rejects_before_launch(kw, code, frag):
+    lib = ssd.load()
+    a = dict(x=1, steps=3, batch=2, H=4, P=16, N=16, G=1, dtype=0)
+    a.update(kw)
+    p = ctypes.c_void_p
+    xptr = None if a["x"] is None else p(a["x"])
+    rc = lib.ssd_step_multi(xptr, p(1), p(1), p(1), p(1), p(1), p(1), p(1), a["steps"], a["batch"],
+                            a["H"], a["P"], a["N"], a["G"], a["dtype"], None)
+    assert rc == code and frag in lib.ssd_last_error().decode()
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros(64, 4, 16)

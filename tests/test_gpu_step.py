@@ -87,3 +87,69 @@ def test_step_batched_equals_solo():
         yi = ssd.step(t(d["x"][0][i:i + 1]), t(d["dt"][0][i:i + 1]), t(d["A"]),
                       t(d["B"][0][i:i + 1]), t(d["C"][0][i:i + 1]), t(d["D"]), hi)
         assert torch.equal(yi[0], y[i]) and torch.equal(hi[0], h[i])
+
+
+def _run_multi(d, dtype, steps):
+    import torch
+    from state_space_model_amd import ssd
+    op = torch.bfloat16 if dtype == "bf16" else torch.float32
+    dev = "cuda"
+    t = lambda a, o=None: torch.from_numpy(np.ascontiguousarray(a)).to(dev) if o is None \
+        else torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(o)
+    h = t(d["h"])
+    y = ssd.step_multi(t(d["x"][:steps], op), t(d["dt"][:steps]), t(d["A"]),
+                       t(d["B"][:steps], op), t(d["C"][:steps], op), t(d["D"]), h)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), h.cpu().numpy()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("b,H,P,N,G,steps", [(1, 1, 16, 16, 1, 1), (3, 4, 32, 64, 2, 7),
+                                             (2, 8, 64, 128, 8, 37), (5, 6, 128, 32, 3, 9),
+                                             (2, 3, 16, 128, 1, 20), (1, 2, 128, 128, 2, 5)])
+def test_step_multi_small(dtype, b, H, P, N, G, steps):
+    """Many steps in one launch equal the fp64 oracle stepped token by token,
+    and the same number of single-step launches on the GPU."""
+    log(f"step_multi small dtype={dtype} b={b} H={H} P={P} N={N} G={G} steps={steps}")
+    d = _small(b, H, P, N, G, steps, 300 + b + H + P + N + steps, dtype)
+    y, h = _run_multi(d, dtype, steps)
+    ry, rh = _oracle_steps(d, steps)
+    ey, eh = maxabs(y, ry), maxabs(h, rh)
+    ys, hs = _run_steps(d, dtype, steps)
+    log(f"  vs oracle max|dy|={ey:.3g} max|dh|={eh:.3g}; vs single steps "
+        f"{maxabs(y, ys):.3g} {maxabs(h, hs):.3g}")
+    assert ey <= TOL["f32"] and eh <= TOL["f32"]
+    assert maxabs(y, ys) <= 1e-5 and maxabs(h, hs) <= 1e-5
+
+
+def test_step_multi_codestral_workload():
+    """The Codestral decode workload's 128 steps in one launch against the
+    oracle (a sample of batch rows, all heads, every step)."""
+    w = inputs.WORKLOADS[3]
+    log("step_multi workload 3 (codestral decode), 128 steps in one launch")
+    d = inputs.workload_inputs(3)
+    y, h = _run_multi(d, "f32", w.steps)
+    bsel = [0, 17, 63]
+    ry, rh = _oracle_steps(d, w.steps, bsel)
+    ey, eh = maxabs(y[:, bsel], ry), maxabs(h[bsel], rh)
+    log(f"  max|dy|={ey:.3g} max|dh|={eh:.3g}")
+    assert ey <= TOL["f32"] and eh <= TOL["f32"]
+
+
+def test_step_multi_edge_cases():
+    """Zero steps leave the state alone; a zero batch does nothing; bad shapes
+    are refused before any launch."""
+    import torch
+    from state_space_model_amd import ssd
+    d = _small(2, 2, 32, 16, 1, 3, 77, "f32")
+    dev = "cuda"
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    h = t(d["h"])
+    y = ssd.step_multi(t(d["x"][:0]), t(d["dt"][:0]), t(d["A"]), t(d["B"][:0]), t(d["C"][:0]),
+                       t(d["D"]), h)
+    torch.cuda.synchronize()
+    assert y.numel() == 0 and np.array_equal(h.cpu().numpy(), d["h"])
+    lib = ssd.load()
+    rc = lib.ssd_step_multi(None, None, None, None, None, None, None, None, 1, 1, 2, 32, 100, 1,
+                            0, None)
+    assert rc == -2 and b"d_state" in lib.ssd_last_error()
