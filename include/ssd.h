@@ -144,10 +144,11 @@ int ssd_step(const void *x, const float *dt, const float *A, const void *B, cons
  *   y   [steps][batch][H][P] float32 (must not alias any input)
  *
  * The state stays on chip for all steps: it crosses HBM once instead of twice
- * per step (the multi-step decode over pre-staged inputs that Compiler-First
- * State Space Duality and Portable O(1) Autoregressive Caching for Inference,
- * Figure 1 and Table 10, motivates by the cost of per-token launches; the
- * steps run as a stream over time as in Recurrence Scan, "The schedule").
+ * per step.  This is the decode loop kept on the device with one launch from
+ * the host (Compiler-First State Space Duality and Portable O(1)
+ * Autoregressive Caching for Inference, Figure 1; the loop's throughput is its
+ * Table 10), with the steps run as a stream over time as in Recurrence Scan,
+ * "The schedule".
  * Supported: P in {16,32,64,128}, N in {16,32,64,128}, H % G == 0.
  * steps = 0 or batch = 0 does nothing.
  */
