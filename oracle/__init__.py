@@ -44,6 +44,10 @@ def _bind(lib):
     lib.ssd_ref_prefill.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, P, P, I]
     lib.ssd_ref_prefill.restype = I
     lib.ssd_ref_step.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I]
+    lib.ssd_ref_conv1d_step.argtypes = [P, P, P, P, I, I, I, I, P]
+    lib.ssd_ref_conv1d_step.restype = I
+    lib.ssd_ref_gated_rmsnorm.argtypes = [P, P, P, ctypes.c_double, I, I, P]
+    lib.ssd_ref_gated_rmsnorm.restype = I
     lib.ssd_ref_step.restype = I
     return lib
 
@@ -108,3 +112,38 @@ def step(x, dt, A, B, C, D, h, threads=None, lib=None):
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
     return y
+
+
+def conv1d_step(u, win, w, bias=None, silu=True, lib=None):
+    """One token of the causal depthwise conv.  u [b,C]; win [b,C,W] float64,
+    updated in place (oldest tap first); w [C,W]; bias [C] or None.
+    Returns the output [b,C] f64 (after silu when ``silu``)."""
+    lib = lib or load()
+    u, w = _f32(u), _f32(w)
+    bias = None if bias is None else _f32(bias)
+    b, C = u.shape
+    W = w.shape[1]
+    assert isinstance(win, np.ndarray) and win.dtype == np.float64 and win.flags.c_contiguous
+    assert win.shape == (b, C, W) and w.shape == (C, W)
+    assert bias is None or bias.shape == (C,)
+    out = np.empty((b, C), dtype=np.float64)
+    rc = lib.ssd_ref_conv1d_step(_ptr(u), _ptr(win), _ptr(w), _ptr(bias), int(bool(silu)), b, C,
+                                 W, _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    return out
+
+
+def gated_rmsnorm(y, z, w, eps=1e-5, lib=None):
+    """y [b,D] (float64), z [b,D], w [D]: y*silu(z) normalised by its root mean
+    square over D (plus eps), times w.  Returns [b,D] f64."""
+    lib = lib or load()
+    y = np.ascontiguousarray(np.asarray(y, dtype=np.float64))
+    z, w = _f32(z), _f32(w)
+    b, D = y.shape
+    assert z.shape == (b, D) and w.shape == (D,)
+    out = np.empty((b, D), dtype=np.float64)
+    rc = lib.ssd_ref_gated_rmsnorm(_ptr(y), _ptr(z), _ptr(w), float(eps), b, D, _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    return out

@@ -29,6 +29,9 @@
  * negative decay rate itself, the input term is dt*x (x) B with no zero-order-hold
  * factor, D is a per-head scalar skip, head h reads group floor(h*G/H).
  *
+ * The decode-layer operations around the scan (the causal conv1d step and
+ * the gated RMS norm) are at the end of this file, with their own passages.
+ *
  * Inputs are float32 (bf16 inputs are upcast exactly before the call); all
  * arithmetic and the outputs are float64.  Layouts are row-major:
  *   x [T][H][P], dt [T][H], A [H], B [T][G][N], C [T][G][N], D [H],
@@ -121,6 +124,68 @@ int ssd_ref_step(const float *x, const float *dt, const float *A,
                   (double)A[hd], B + ((size_t)b * G + g) * N,
                   C + ((size_t)b * G + g) * N, (double)D[hd],
                   y + ((size_t)b * H + hd) * P, P, N);
+    }
+    return 0;
+}
+
+/*
+ * Decode-layer operations on either side of the scan.  Mamba-2 SSD fused
+ * layer via VGpuWarp -- design sketch lists them among the layer steps to move
+ * onto the device: the causal conv1d step (a per-channel FIR over d_conv taps
+ * with a rolling buffer) and the gated RMS norm (y times silu(z), then the root
+ * mean square over d_inner, times norm_w).
+ *
+ * Causal conv1d, one token, per channel c: the window win[c][0..W-1] (oldest
+ * first) drops win[c][0], moves the rest down one place and takes u[c] as its
+ * newest entry win[c][W-1]; the output is
+ *     v = bias[c] + sum_k w[c][k] * win[c][k]          (bias NULL: 0)
+ * and, when silu != 0, v * sigmoid(v).
+ * Layouts: u [b][C], win [b][C][W] fp64 (updated in place), w [C][W],
+ * bias [C], out [b][C] fp64.
+ */
+int ssd_ref_conv1d_step(const float *u, double *win, const float *w, const float *bias,
+                        int silu, int batch, int channels, int width, double *out)
+{
+    if (batch < 0 || channels < 1 || width < 1)
+        return -1;
+    for (int b = 0; b < batch; ++b) {
+        for (int c = 0; c < channels; ++c) {
+            double *wd = win + ((size_t)b * channels + c) * width;
+            for (int k = 0; k + 1 < width; ++k)
+                wd[k] = wd[k + 1];
+            wd[width - 1] = (double)u[(size_t)b * channels + c];
+            double v = bias ? (double)bias[c] : 0.0;
+            for (int k = 0; k < width; ++k)
+                v += (double)w[(size_t)c * width + k] * wd[k];
+            if (silu)
+                v = v / (1.0 + exp(-v));
+            out[(size_t)b * channels + c] = v;
+        }
+    }
+    return 0;
+}
+
+/*
+ * Gated RMS norm over the D channels of one token:
+ *     g = y * silu(z),   out = g / sqrt(mean(g^2) + eps) * w
+ * Layouts: y [b][D] fp64, z [b][D], w [D], out [b][D] fp64.
+ */
+int ssd_ref_gated_rmsnorm(const double *y, const float *z, const float *w, double eps,
+                          int batch, int dim, double *out)
+{
+    if (batch < 0 || dim < 1 || eps < 0.0)
+        return -1;
+    for (int b = 0; b < batch; ++b) {
+        double ss = 0.0;
+        for (int d = 0; d < dim; ++d) {
+            const double zz = (double)z[(size_t)b * dim + d];
+            const double g = y[(size_t)b * dim + d] * (zz / (1.0 + exp(-zz)));
+            out[(size_t)b * dim + d] = g;
+            ss += g * g;
+        }
+        const double r = 1.0 / sqrt(ss / dim + eps);
+        for (int d = 0; d < dim; ++d)
+            out[(size_t)b * dim + d] *= r * (double)w[d];
     }
     return 0;
 }

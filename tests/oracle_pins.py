@@ -22,6 +22,8 @@ What each pin rests on:
   varlen     a packed batch equals separate runs of its sequences
   padding    appended (dt = 0, x = 0) tokens leave h_out unchanged
   golden     hand-derived worked examples (tests/golden/hand_worked.json)
+The pins of the decode-layer operations (conv1d step, gated RMS norm) are in
+LAYER_PINS at the end of this file.
 """
 import json
 import os
@@ -230,4 +232,115 @@ PINS = {
     "unrolled": pin_unrolled, "chunked": pin_chunked, "A0": pin_A0, "dt0": pin_dt0,
     "split": pin_split, "steps": pin_steps, "lfilter": pin_lfilter, "groups": pin_groups,
     "linear": pin_linear, "varlen": pin_varlen, "padding": pin_padding, "golden": pin_golden,
+}
+
+
+# ---------------------------------------------------------------------------
+# Pins of the decode-layer operations around the scan (the causal conv1d step
+# and the gated RMS norm, Mamba-2 SSD fused layer via VGpuWarp -- design
+# sketch, the list of layer steps to move onto the device).  Each takes an
+# oracle handle with ``conv1d_step``/``gated_rmsnorm`` callables.
+#   conv_shift   a one-hot tap selects the input k tokens back (pure shift)
+#   conv_fir     a token-by-token run equals numpy.convolve of each channel's
+#                input history with its taps (zero history), plus the bias
+#   conv_silu    the activation is x * scipy.special.expit(x)
+#   norm_torch   the norm equals torch's rms_norm of y * silu(z), in float64
+#   norm_const   a constant gated row g gives g / sqrt(g^2 + eps) * w
+#   norm_scale   without eps the result does not depend on the scale of y
+
+def _conv_run(orc, u, w, bias, silu):
+    T, b, C = u.shape
+    win = np.zeros((b, C, w.shape[1]), np.float64)
+    return np.stack([orc.conv1d_step(u[t], win, w, bias, silu) for t in range(T)]), win
+
+
+def pin_conv_shift(orc):
+    T, b, C, W = 9, 2, 5, 4
+    rng = np.random.Generator(np.random.PCG64(61))
+    u = rng.standard_normal((T, b, C)).astype(np.float32)
+    worst = 0.0
+    for back in range(W):
+        w = np.zeros((C, W), np.float32)
+        w[:, W - 1 - back] = 1.0
+        out, win = _conv_run(orc, u, w, None, False)
+        ref = np.concatenate([np.zeros((back, b, C)), u[:T - back].astype(np.float64)])
+        worst = max(worst, _rel(out, ref))
+    worst = max(worst, _rel(win, np.moveaxis(u[T - W:], 0, -1)))  # window = last W inputs
+    return worst == 0.0, f"max rel err {worst:.3g}"
+
+
+def pin_conv_fir(orc):
+    T, b, C, W = 13, 3, 6, 4
+    rng = np.random.Generator(np.random.PCG64(67))
+    u = rng.standard_normal((T, b, C)).astype(np.float32)
+    w = rng.standard_normal((C, W)).astype(np.float32)
+    bias = rng.standard_normal(C).astype(np.float32)
+    out, _ = _conv_run(orc, u, w, bias, False)
+    ref = np.empty((T, b, C))
+    for i in range(b):
+        for c in range(C):
+            # taps are oldest first, so the kernel applied by convolution is reversed
+            ref[:, i, c] = np.convolve(u[:, i, c].astype(np.float64),
+                                       w[c, ::-1].astype(np.float64))[:T] + bias[c]
+    e = _rel(out, ref)
+    return e <= RTOL, f"rel err {e:.3g}"
+
+
+def pin_conv_silu(orc):
+    from scipy.special import expit
+    b, C, W = 4, 7, 3
+    rng = np.random.Generator(np.random.PCG64(71))
+    u = (3.0 * rng.standard_normal((1, b, C))).astype(np.float32)
+    w = np.zeros((C, W), np.float32)
+    w[:, -1] = 1.0
+    out, _ = _conv_run(orc, u, w, None, True)
+    x = u[0].astype(np.float64)
+    e = _rel(out[0], x * expit(x))
+    return e <= RTOL, f"rel err {e:.3g}"
+
+
+def _norm_case(seed, b=3, D=40):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    y = rng.standard_normal((b, D))
+    z = (2.0 * rng.standard_normal((b, D))).astype(np.float32)
+    w = rng.uniform(0.5, 1.5, D).astype(np.float32)
+    return y, z, w
+
+
+def pin_norm_torch(orc):
+    import torch
+    from scipy.special import expit
+    y, z, w = _norm_case(73)
+    eps = 1e-5
+    out = orc.gated_rmsnorm(y, z, w, eps)
+    g = torch.from_numpy(y * (z.astype(np.float64) * expit(z.astype(np.float64))))
+    ref = torch.nn.functional.rms_norm(g, (g.shape[1],), weight=torch.from_numpy(
+        w.astype(np.float64)), eps=eps).numpy()
+    e = _rel(out, ref)
+    return e <= 1e-10, f"rel err {e:.3g}"
+
+
+def pin_norm_const(orc):
+    b, D = 2, 16
+    z = np.full((b, D), 40.0, np.float32)             # silu(40) = 40 to fp64 rounding
+    y = np.array([[0.3] * D, [-2.0] * D], np.float64)
+    w = np.linspace(0.5, 2.0, D).astype(np.float32)
+    eps = 1e-3
+    g = y * 40.0
+    ref = g / np.sqrt(g * g + eps) * w.astype(np.float64)
+    e = _rel(orc.gated_rmsnorm(y, z, w, eps), ref)
+    return e <= 1e-12, f"rel err {e:.3g}"
+
+
+def pin_norm_scale(orc):
+    y, z, w = _norm_case(79)
+    a = orc.gated_rmsnorm(y, z, w, 0.0)
+    e = max(_rel(orc.gated_rmsnorm(7.5 * y, z, w, 0.0), a),
+            _rel(orc.gated_rmsnorm(1e-3 * y, z, w, 0.0), a))
+    return e <= 1e-12, f"rel err {e:.3g}"
+
+
+LAYER_PINS = {
+    "conv_shift": pin_conv_shift, "conv_fir": pin_conv_fir, "conv_silu": pin_conv_silu,
+    "norm_torch": pin_norm_torch, "norm_const": pin_norm_const, "norm_scale": pin_norm_scale,
 }

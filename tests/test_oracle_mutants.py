@@ -69,3 +69,58 @@ def test_mutant_is_caught(name, tmp_path_factory):
         if not ok:
             caught.append(pname)
     assert caught, f"mutant {name} passed every pin"
+
+
+# Planted mistakes in the decode-layer operations (conv1d step, gated norm);
+# each must fail at least one of the layer pins.
+LAYER_MUTANTS = [
+    ("conv-newest-first", "wd[width - 1] = (double)u[(size_t)b * channels + c];",
+     "wd[0] = (double)u[(size_t)b * channels + c];"),
+    ("conv-no-shift", "wd[k] = wd[k + 1];", "wd[k] = wd[k];"),
+    ("conv-bias-dropped", "double v = bias ? (double)bias[c] : 0.0;", "double v = 0.0;"),
+    ("conv-tap-transposed", "v += (double)w[(size_t)c * width + k] * wd[k];",
+     "v += (double)w[(size_t)c * width + (width - 1 - k)] * wd[k];"),
+    ("conv-silu-sign", "v = v / (1.0 + exp(-v));", "v = v / (1.0 + exp(v));"),
+    ("norm-sum-not-mean", "sqrt(ss / dim + eps)", "sqrt(ss + eps)"),
+    ("norm-gate-dropped", "* (zz / (1.0 + exp(-zz)));", "* 1.0;"),
+    ("norm-gate-sigmoid", "* (zz / (1.0 + exp(-zz)));", "* (1.0 / (1.0 + exp(-zz)));"),
+    ("norm-weight-dropped", "*= r * (double)w[d];", "*= r;"),
+    ("norm-eps-outside", "sqrt(ss / dim + eps)", "(sqrt(ss / dim) + eps)"),
+]
+
+
+@functools.lru_cache(maxsize=None)
+def _layer_mutant_lib(name, tmpdir):
+    orig, repl = next((o, r) for n, o, r in LAYER_MUTANTS if n == name)
+    assert orig in SRC, f"mutation site for {name} not found in the oracle source"
+    src = SRC.replace(orig, repl)
+    path = os.path.join(tmpdir, f"lmut_{name}.c")
+    with open(path, "w") as f:
+        f.write(src)
+    lib = obuild.build(path, os.path.join(tmpdir, f"liblmut_{name}.so"),
+                       extra_flags=("-Wno-unused-variable", "-Wno-unused-but-set-variable"))
+    return oracle.load(lib)
+
+
+@pytest.mark.parametrize("name", [m[0] for m in LAYER_MUTANTS])
+def test_layer_mutant_is_caught(name, tmp_path_factory):
+    lib = _layer_mutant_lib(name, str(tmp_path_factory.getbasetemp()))
+
+    class Orc:
+        @staticmethod
+        def conv1d_step(*a, **k):
+            return oracle.conv1d_step(*a, lib=lib, **k)
+
+        @staticmethod
+        def gated_rmsnorm(*a, **k):
+            return oracle.gated_rmsnorm(*a, lib=lib, **k)
+
+    caught = []
+    for pname, pin in oracle_pins.LAYER_PINS.items():
+        try:
+            ok, _ = pin(Orc)
+        except (ValueError, AssertionError, FloatingPointError):
+            ok = False
+        if not ok:
+            caught.append(pname)
+    assert caught, f"mutant {name} passed every layer pin"

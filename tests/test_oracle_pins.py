@@ -14,3 +14,14 @@ class _Orc:
 def test_pin(name):
     ok, detail = oracle_pins.PINS[name](_Orc)
     assert ok, f"pin {name} failed: {detail}"
+
+
+class _LayerOrc:
+    conv1d_step = staticmethod(oracle.conv1d_step)
+    gated_rmsnorm = staticmethod(oracle.gated_rmsnorm)
+
+
+@pytest.mark.parametrize("name", sorted(oracle_pins.LAYER_PINS))
+def test_layer_pin(name):
+    ok, detail = oracle_pins.LAYER_PINS[name](_LayerOrc)
+    assert ok, f"pin {name} failed: {detail}"
