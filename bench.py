@@ -209,7 +209,7 @@ def _kernel_key(name, grid):
             if k == "decode_step":  # the two decode workloads differ in grid size
                 return ("codestral-7b-decode-step" if int(grid) > 24 * 256 else
                         "mamba2-130m-layer-prefill"), k
-            if k == "decode_multi_step":
+            if k in ("decode_multi_step", "conv1d_step", "gated_rmsnorm"):
                 return "codestral-7b-decode-step", k
             return "mamba2-130m-layer-prefill", k
     return None, None
@@ -370,6 +370,34 @@ def prefill_large(args, torch, inputs, ssd, dev):
             "kernels_us": kern}
 
 
+def decode_layer_bench(torch, ssd, w3, dev, ms_scan):
+    """One token of the decode layer body (conv1d step + SiLU, the scan, the
+    gated RMS norm) at the Codestral shape with synthetic weights."""
+    b, H, P, N, G, W = w3.batch, w3.H, w3.P, w3.N, w3.G, 4
+    inner, Cn = H * P, H * P + 2 * G * N
+    g = torch.Generator(device="cpu").manual_seed(3003)
+    r = lambda *s: torch.randn(*s, generator=g)
+    xbc = r(b, Cn).to(dev, torch.bfloat16)
+    z = r(b, inner).to(dev, torch.bfloat16)
+    dt = (torch.rand(b, H, generator=g) * 0.1 + 1e-3).to(dev)
+    A = -(torch.rand(H, generator=g) * 15 + 1).to(dev)
+    D = torch.rand(H, generator=g).to(dev)
+    st = r(b, Cn, W).to(dev)
+    cw = (r(Cn, W) / W).to(dev)
+    cb = (0.1 * r(Cn)).to(dev)
+    h = (0.1 * r(b, H, N, P)).to(dev)
+    nw = (torch.rand(inner, generator=g) + 0.5).to(dev)
+    run, _ = ssd.decode_layer_step(xbc, z, dt, A, D, st, cw, cb, h, nw, 1e-5, H=H, P=P, N=N, G=G,
+                                   prepare=True)
+    run()
+    torch.cuda.synchronize()
+    ms = graph_ms(torch, run, reps=5, per_graph=20)
+    return {"shape": {"batch": b, "heads": H, "headdim": P, "d_state": N, "groups": G,
+                      "d_conv": W, "conv_channels": Cn, "d_inner": inner, "dtype": "bf16"},
+            "us": round(ms * 1e3, 2), "scan_alone_us": round(ms_scan * 1e3, 2),
+            "conv_and_norm_us": round((ms - ms_scan) * 1e3, 2)}
+
+
 def main():
     args = parse()
     if args.summarize:
@@ -510,6 +538,10 @@ def main():
                                  "algorithmic_bytes": mbytes}}
     del h3m, y3m
 
+    # ---- the decode layer body around the scan at the same shape (d_conv 4,
+    # conv channels H*P + 2*G*N, bf16 activations): conv -> scan -> gated norm
+    layer = decode_layer_bench(torch, ssd, w3, dev, ms_dec_graph)
+
     # MFMA utilisation estimate of the prefill (algorithmic flops / bf16 peak)
     fl = sum(work[n]["flops"] for n in ("chunk_state", "chunk_scan"))
     mfma_util = fl / (sum(kern_ms[n] for n in kern_ms if n != "decode_step") * 1e-3) / \
@@ -533,6 +565,7 @@ def main():
         "prefill_2p7b_layer": large,
         "decode": decode,
         "decode_multi_step": decode_multi,
+        "decode_layer_step": layer,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -156,6 +156,60 @@ int ssd_step_multi(const void *x, const float *dt, const float *A, const void *B
                    const float *D, float *h, float *y, int steps, int batch, int H, int P, int N,
                    int G, ssd_dtype_t dtype, void *stream);
 
+/*
+ * Decode-layer operations on either side of the scan (Mamba-2 SSD fused layer
+ * via VGpuWarp -- design sketch, its list of layer steps to move onto the
+ * device: the causal conv1d step, a per-channel FIR over d_conv taps with a
+ * rolling buffer kept in device memory, and the gated RMS norm, y times
+ * silu(z), then the root mean square over d_inner, times norm_w).
+ *
+ * ssd_conv1d_step: one token of a causal depthwise convolution.
+ *   u          [batch][channels]         dtype    this token's inputs
+ *   conv_state [batch][channels][width]  float32  window, oldest tap first;
+ *              rolled in place (drops the oldest, appends u)
+ *   w          [channels][width] float32;  bias [channels] float32 or NULL
+ *   out        [batch][channels]         dtype    bias + sum_k w[c][k] win[c][k],
+ *              then v * sigmoid(v) when silu != 0 (must not alias any input)
+ *   Supported: width in 1..8.
+ */
+int ssd_conv1d_step(const void *u, float *conv_state, const float *w, const float *bias,
+                    int silu, void *out, int batch, int channels, int width, ssd_dtype_t dtype,
+                    void *stream);
+
+/*
+ * ssd_gated_rmsnorm: out = g / sqrt(mean_d(g^2) + eps) * w with g = y * silu(z),
+ * per token row.
+ *   y [batch][dim] float32;  z [batch][dim] dtype;  w [dim] float32;  eps >= 0
+ *   out [batch][dim] float32 (must not alias y or z)
+ */
+int ssd_gated_rmsnorm(const float *y, const void *z, const float *w, float eps, float *out,
+                      int batch, int dim, ssd_dtype_t dtype, void *stream);
+
+/*
+ * ssd_decode_layer_step: the layer body around the scan for one token, all on
+ * the device: conv1d step (with SiLU) over the x|B|C channels, ssd_step on
+ * the convolved x, B, C, then the gated RMS norm of y.  Equal to
+ * ssd_conv1d_step(silu=1) + ssd_step + ssd_gated_rmsnorm.
+ *   xbc      [batch][H*P + 2*G*N]  dtype    in_proj's x | B | C channels
+ *   z        [batch][H*P]          dtype    gate
+ *   dt       [batch][H] float32;  A, D [H] float32
+ *   conv_state [batch][H*P + 2*G*N][width] float32, rolled in place
+ *   conv_w   [H*P + 2*G*N][width] float32;  conv_b [H*P + 2*G*N] float32 or NULL
+ *   h        [batch][H][N][P] float32, updated in place
+ *   norm_w   [H*P] float32;  eps >= 0
+ *   out      [batch][H*P] float32   the normalised, gated scan output
+ *   xbc_act  [batch][H*P + 2*G*N] float32, y [batch][H*P] float32: caller-owned
+ *            scratch (the convolved channels, kept in the scan's float32, and
+ *            the scan output)
+ *   Supported: P in {16,32,64,128}, 4 <= N <= 1024 with N % 4 == 0,
+ *   width in 1..8, H % G == 0.
+ */
+int ssd_decode_layer_step(const void *xbc, const void *z, const float *dt, const float *A,
+                          const float *D, float *conv_state, const float *conv_w,
+                          const float *conv_b, float *h, const float *norm_w, float eps,
+                          float *out, float *xbc_act, float *y, int batch, int H, int P, int N,
+                          int G, int width, ssd_dtype_t dtype, void *stream);
+
 /* Message for the last non-zero return on the calling thread ("" if none). */
 const char *ssd_last_error(void);
 

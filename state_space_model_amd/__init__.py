@@ -20,3 +20,8 @@ def step(*args, **kwargs):
 def step_multi(*args, **kwargs):
     from . import ssd
     return ssd.step_multi(*args, **kwargs)
+
+
+def decode_layer_step(*args, **kwargs):
+    from . import ssd
+    return ssd.decode_layer_step(*args, **kwargs)

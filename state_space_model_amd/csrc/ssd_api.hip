@@ -139,6 +139,71 @@ int ssd_step_multi(const void *x, const float *dt, const float *A, const void *B
   return SSD_OK;
 }
 
+int ssd_conv1d_step(const void *u, float *conv_state, const float *w, const float *bias,
+                    int silu, void *out, int batch, int channels, int width, ssd_dtype_t dtype,
+                    void *stream) {
+  g_err[0] = 0;
+  if (dtype != SSD_F32 && dtype != SSD_BF16) return fail(SSD_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (batch < 0 || channels < 1) return fail(SSD_ERR_INVALID_ARG, "need batch >= 0, channels >= 1 (batch=%d channels=%d)", batch, channels);
+  if (width < 1 || width > 8) return fail(SSD_ERR_UNSUPPORTED, "conv width %d not in 1..8", width);
+  if (batch > 65535) return fail(SSD_ERR_UNSUPPORTED, "batch %d > 65535", batch);
+  if (batch > 0 && (!u || !conv_state || !w || !out)) return fail(SSD_ERR_INVALID_ARG, "null pointer argument");
+  hipError_t e = ssd::launch_conv1d_step(u, conv_state, w, bias, silu != 0, out, batch, channels,
+                                         width, dtype == SSD_BF16, false,
+                                         static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SSD_ERR_HIP, "HIP error: %s", hipGetErrorString(e));
+  return SSD_OK;
+}
+
+int ssd_gated_rmsnorm(const float *y, const void *z, const float *w, float eps, float *out,
+                      int batch, int dim, ssd_dtype_t dtype, void *stream) {
+  g_err[0] = 0;
+  if (dtype != SSD_F32 && dtype != SSD_BF16) return fail(SSD_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (batch < 0 || dim < 1) return fail(SSD_ERR_INVALID_ARG, "need batch >= 0, dim >= 1 (batch=%d dim=%d)", batch, dim);
+  if (!(eps >= 0.f)) return fail(SSD_ERR_INVALID_ARG, "eps must be >= 0");
+  if (batch > 0 && (!y || !z || !w || !out)) return fail(SSD_ERR_INVALID_ARG, "null pointer argument");
+  hipError_t e = ssd::launch_gated_rmsnorm(y, z, w, eps, out, batch, dim, dtype == SSD_BF16,
+                                           static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SSD_ERR_HIP, "HIP error: %s", hipGetErrorString(e));
+  return SSD_OK;
+}
+
+int ssd_decode_layer_step(const void *xbc, const void *z, const float *dt, const float *A,
+                          const float *D, float *conv_state, const float *conv_w,
+                          const float *conv_b, float *h, const float *norm_w, float eps,
+                          float *out, float *xbc_act, float *y, int batch, int H, int P, int N,
+                          int G, int width, ssd_dtype_t dtype, void *stream) {
+  g_err[0] = 0;
+  if (dtype != SSD_F32 && dtype != SSD_BF16) return fail(SSD_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (batch < 0) return fail(SSD_ERR_INVALID_ARG, "batch must be >= 0 (got %d)", batch);
+  if (H < 1 || G < 1 || H % G != 0) return fail(SSD_ERR_INVALID_ARG, "need H >= 1, G >= 1, H %% G == 0 (H=%d G=%d)", H, G);
+  if (!pow2_in(P, 16, 128)) return fail(SSD_ERR_UNSUPPORTED, "headdim P=%d not in {16,32,64,128}", P);
+  if (N < 1 || N > 1024 || N % 4 != 0) return fail(SSD_ERR_UNSUPPORTED, "d_state N=%d: need 4 <= N <= 1024, N %% 4 == 0", N);
+  if (width < 1 || width > 8) return fail(SSD_ERR_UNSUPPORTED, "conv width %d not in 1..8", width);
+  if (!(eps >= 0.f)) return fail(SSD_ERR_INVALID_ARG, "eps must be >= 0");
+  if (batch > 65535) return fail(SSD_ERR_UNSUPPORTED, "batch %d > 65535", batch);
+  if (batch > 0 && (!xbc || !z || !dt || !A || !D || !conv_state || !conv_w || !h || !norm_w ||
+                    !out || !xbc_act || !y))
+    return fail(SSD_ERR_INVALID_ARG, "null pointer argument");
+  if (batch == 0) return SSD_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool bf = dtype == SSD_BF16;
+  const int inner = H * P, channels = inner + 2 * G * N;
+  // the convolved channels stay float32 (the scan's arithmetic type), so the
+  // layer adds no rounding of its own between the conv and the scan
+  hipError_t e = ssd::launch_conv1d_step(xbc, conv_state, conv_w, conv_b, true, xbc_act, batch,
+                                         channels, width, bf, true, st);
+  if (e == hipSuccess) {
+    const float *act = xbc_act;
+    ssd::StepArgs a{act, dt, A, act + inner, act + inner + (size_t)G * N, D, h, y, batch, H, P, N,
+                    G, false, stream, (size_t)channels, (size_t)channels};
+    e = ssd::launch_step(a);
+  }
+  if (e == hipSuccess) e = ssd::launch_gated_rmsnorm(y, z, norm_w, eps, out, batch, inner, bf, st);
+  if (e != hipSuccess) return fail(SSD_ERR_HIP, "HIP error: %s", hipGetErrorString(e));
+  return SSD_OK;
+}
+
 const char *ssd_last_error(void) { return g_err; }
 
 }  // extern "C"

@@ -61,6 +61,7 @@ struct StepArgs {
   int batch, H, P, N, G;
   bool bf16;
   void *stream;
+  size_t x_bstride = 0, bc_bstride = 0;  // elements between batch rows (0: packed)
 };
 hipError_t launch_step(const StepArgs &a);
 
@@ -75,5 +76,12 @@ struct MultiStepArgs {
   void *stream;
 };
 hipError_t launch_step_multi(const MultiStepArgs &a);
+
+// Decode-layer operations around the scan (ssd_layer.hip).
+hipError_t launch_conv1d_step(const void *u, float *state, const float *w, const float *bias,
+                              bool silu, void *out, int batch, int channels, int width,
+                              bool is_bf16, bool out_f32, hipStream_t st);
+hipError_t launch_gated_rmsnorm(const float *y, const void *z, const float *w, float eps,
+                                float *out, int batch, int dim, bool is_bf16, hipStream_t st);
 
 }  // namespace ssd

@@ -24,7 +24,8 @@ __global__ __launch_bounds__(256) void k_step(const T *__restrict__ x, const flo
                                               const float *__restrict__ A,
                                               const T *__restrict__ B, const T *__restrict__ C,
                                               const float *__restrict__ D, float *__restrict__ h,
-                                              float *__restrict__ y, int H, int N, int G) {
+                                              float *__restrict__ y, int H, int N, int G,
+                                              size_t xbs, size_t bcs) {
   constexpr int TPR = P / 4;
   constexpr int RPP = 256 / TPR;
   __shared__ float Bsh[1024], Csh[1024];
@@ -32,8 +33,8 @@ __global__ __launch_bounds__(256) void k_step(const T *__restrict__ x, const flo
   const int hd = blockIdx.x, b = blockIdx.y;
   const int g = (hd * G) / H;
   const int tid = threadIdx.x, q = tid % TPR, r0 = tid / TPR;
-  const T *Bp = B + ((size_t)b * G + g) * N;
-  const T *Cp = C + ((size_t)b * G + g) * N;
+  const T *Bp = B + (size_t)b * bcs + (size_t)g * N;  // x, B, C rows are xbs / bcs apart
+  const T *Cp = C + (size_t)b * bcs + (size_t)g * N;
   for (int n = tid; n < N; n += 256) {
     Bsh[n] = to_f32(Bp[n]);
     Csh[n] = to_f32(Cp[n]);
@@ -41,7 +42,7 @@ __global__ __launch_bounds__(256) void k_step(const T *__restrict__ x, const flo
   const size_t bh = (size_t)b * H + hd;
   const float dtv = dt[bh];
   const float a = expf(fminf(dtv * A[hd], 0.f));
-  const f4 xv = ld4f(x + bh * P + 4 * q);
+  const f4 xv = ld4f(x + (size_t)b * xbs + (size_t)hd * P + 4 * q);
   f4 dx;
 #pragma unroll
   for (int e = 0; e < 4; ++e) dx[e] = dtv * xv[e];
@@ -98,13 +99,20 @@ template <typename T>
 static hipError_t run_step(const StepArgs &a) {
   hipStream_t st = static_cast<hipStream_t>(a.stream);
   dim3 grid(a.H, a.batch);
+  const size_t xbs = a.x_bstride ? a.x_bstride : (size_t)a.H * a.P;
+  const size_t bcs = a.bc_bstride ? a.bc_bstride : (size_t)a.G * a.N;
+#define SSD_LAUNCH(p)                                                                          \
+  hipLaunchKernelGGL((k_step<T, p>), grid, dim3(256), 0, st, (const T *)a.x, a.dt, a.A,        \
+                     (const T *)a.B, (const T *)a.C, a.D, a.h, a.y, a.H, a.N, a.G, xbs, bcs); \
+  break;
   switch (a.P) {
-    case 16: hipLaunchKernelGGL((k_step<T, 16>), grid, dim3(256), 0, st, (const T *)a.x, a.dt, a.A, (const T *)a.B, (const T *)a.C, a.D, a.h, a.y, a.H, a.N, a.G); break;
-    case 32: hipLaunchKernelGGL((k_step<T, 32>), grid, dim3(256), 0, st, (const T *)a.x, a.dt, a.A, (const T *)a.B, (const T *)a.C, a.D, a.h, a.y, a.H, a.N, a.G); break;
-    case 64: hipLaunchKernelGGL((k_step<T, 64>), grid, dim3(256), 0, st, (const T *)a.x, a.dt, a.A, (const T *)a.B, (const T *)a.C, a.D, a.h, a.y, a.H, a.N, a.G); break;
-    case 128: hipLaunchKernelGGL((k_step<T, 128>), grid, dim3(256), 0, st, (const T *)a.x, a.dt, a.A, (const T *)a.B, (const T *)a.C, a.D, a.h, a.y, a.H, a.N, a.G); break;
+    case 16: SSD_LAUNCH(16)
+    case 32: SSD_LAUNCH(32)
+    case 64: SSD_LAUNCH(64)
+    case 128: SSD_LAUNCH(128)
     default: return hipErrorInvalidValue;
   }
+#undef SSD_LAUNCH
   return hipGetLastError();
 }
 

@@ -19,7 +19,8 @@ STAGE_ALL = 15
 ERRORS = {0: "SSD_OK", -1: "SSD_ERR_INVALID_ARG", -2: "SSD_ERR_UNSUPPORTED",
           -3: "SSD_ERR_WORKSPACE", -4: "SSD_ERR_HIP"}
 EXPORTS = ("ssd_scan_prefill_workspace", "ssd_scan_prefill", "ssd_scan_prefill_stages",
-           "ssd_step", "ssd_step_multi", "ssd_last_error")
+           "ssd_step", "ssd_step_multi", "ssd_conv1d_step", "ssd_gated_rmsnorm",
+           "ssd_decode_layer_step", "ssd_last_error")
 
 _lib = None
 
@@ -53,6 +54,14 @@ def load(path=LIB_PATH):
     lib.ssd_step_multi.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                    vp]
     lib.ssd_step_multi.restype = i32
+    f32 = ctypes.c_float
+    lib.ssd_conv1d_step.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, vp]
+    lib.ssd_conv1d_step.restype = i32
+    lib.ssd_gated_rmsnorm.argtypes = [vp, vp, vp, f32, vp, i32, i32, i32, vp]
+    lib.ssd_gated_rmsnorm.restype = i32
+    lib.ssd_decode_layer_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp,
+                                          i32, i32, i32, i32, i32, i32, i32, vp]
+    lib.ssd_decode_layer_step.restype = i32
     lib.ssd_last_error.argtypes = []
     lib.ssd_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -244,3 +253,87 @@ def step_multi(x, dt, A, B, C, D, h, y=None, prepare=False):
         return Prepared(load().ssd_step_multi, args, keep=(x, dt, A, B, C, D, h, y)), y
     _check(load().ssd_step_multi(*args, _stream()))
     return y
+
+
+def conv1d_step(u, conv_state, w, bias=None, silu=True, out=None):
+    """One token of the causal depthwise conv.  u [b,C] (float32 or bfloat16);
+    conv_state [b,C,W] float32, rolled in place; w [C,W]; bias [C] or None.
+    Returns out [b,C] in u's dtype."""
+    b, C = u.shape
+    W = w.shape[1]
+    dev = u.device
+    _need(u, "u", dev=dev)
+    code = _dtype_code(u)
+    for t, n in ((conv_state, "conv_state"), (w, "w")):
+        _need(t, n, torch.float32, dev)
+    if bias is not None:
+        _need(bias, "bias", torch.float32, dev)
+    if tuple(conv_state.shape) != (b, C, W) or tuple(w.shape) != (C, W) or \
+            (bias is not None and tuple(bias.shape) != (C,)):
+        raise ValueError("conv_state must be [b,C,W], w [C,W], bias [C]")
+    if out is None:
+        out = torch.empty_like(u)
+    _need(out, "out", u.dtype, dev)
+    _check(load().ssd_conv1d_step(_ptr(u), _ptr(conv_state), _ptr(w), _ptr(bias), int(bool(silu)),
+                                  _ptr(out), b, C, W, code, _stream()))
+    return out
+
+
+def gated_rmsnorm(y, z, w, eps=1e-5, out=None):
+    """y [b,D] float32, z [b,D] (float32 or bfloat16), w [D]:
+    y*silu(z) / sqrt(mean(.^2) + eps) * w.  Returns [b,D] float32."""
+    b, D = y.shape
+    dev = y.device
+    _need(y, "y", torch.float32, dev)
+    _need(z, "z", dev=dev)
+    code = _dtype_code(z)
+    _need(w, "w", torch.float32, dev)
+    if tuple(z.shape) != (b, D) or tuple(w.shape) != (D,):
+        raise ValueError("z must be [b,D], w [D]")
+    if out is None:
+        out = torch.empty_like(y)
+    _need(out, "out", torch.float32, dev)
+    _check(load().ssd_gated_rmsnorm(_ptr(y), _ptr(z), _ptr(w), float(eps), _ptr(out), b, D, code,
+                                    _stream()))
+    return out
+
+
+def decode_layer_step(xbc, z, dt, A, D, conv_state, conv_w, conv_b, h, norm_w, eps=1e-5, *,
+                      H, P, N, G, out=None, xbc_act=None, y=None, prepare=False):
+    """The layer body around the scan for one token: conv1d step (+SiLU) over
+    the x|B|C channels, the decode step, the gated RMS norm.  xbc [b, H*P+2*G*N],
+    z [b, H*P], dt [b,H]; conv_state [b, H*P+2*G*N, W] and h [b,H,N,P] are
+    updated in place.  Returns out [b, H*P] float32."""
+    b, Cn = xbc.shape
+    inner = H * P
+    W = conv_w.shape[1]
+    dev = xbc.device
+    _need(xbc, "xbc", dev=dev)
+    code = _dtype_code(xbc)
+    _need(z, "z", xbc.dtype, dev)
+    for t, n in ((dt, "dt"), (A, "A"), (D, "D"), (conv_state, "conv_state"),
+                 (conv_w, "conv_w"), (h, "h"), (norm_w, "norm_w")):
+        _need(t, n, torch.float32, dev)
+    if conv_b is not None:
+        _need(conv_b, "conv_b", torch.float32, dev)
+    if Cn != inner + 2 * G * N or tuple(z.shape) != (b, inner) or tuple(dt.shape) != (b, H) or \
+            tuple(conv_state.shape) != (b, Cn, W) or tuple(conv_w.shape) != (Cn, W) or \
+            tuple(h.shape) != (b, H, N, P) or tuple(norm_w.shape) != (inner,):
+        raise ValueError("inconsistent decode-layer shapes")
+    if out is None:
+        out = torch.empty((b, inner), dtype=torch.float32, device=dev)
+    if xbc_act is None:
+        xbc_act = torch.empty(xbc.shape, dtype=torch.float32, device=dev)
+    if y is None:
+        y = torch.empty((b, inner), dtype=torch.float32, device=dev)
+    for t, n, dt_ in ((out, "out", torch.float32), (xbc_act, "xbc_act", torch.float32),
+                      (y, "y", torch.float32)):
+        _need(t, n, dt_, dev)
+    args = (_ptr(xbc), _ptr(z), _ptr(dt), _ptr(A), _ptr(D), _ptr(conv_state), _ptr(conv_w),
+            _ptr(conv_b), _ptr(h), _ptr(norm_w), float(eps), _ptr(out), _ptr(xbc_act), _ptr(y),
+            b, H, P, N, G, W, code)
+    if prepare:
+        keep = (xbc, z, dt, A, D, conv_state, conv_w, conv_b, h, norm_w, out, xbc_act, y)
+        return Prepared(load().ssd_decode_layer_step, args, keep=keep), out
+    _check(load().ssd_decode_layer_step(*args, _stream()))
+    return out
