@@ -48,6 +48,8 @@ def _bind(lib):
     lib.ssd_ref_conv1d_step.restype = I
     lib.ssd_ref_gated_rmsnorm.argtypes = [P, P, P, ctypes.c_double, I, I, P]
     lib.ssd_ref_gated_rmsnorm.restype = I
+    lib.ssd_ref_selective_scan.argtypes = [P, P, P, P, P, P, P, I, I, I, I, P, P, I]
+    lib.ssd_ref_selective_scan.restype = I
     lib.ssd_ref_step.restype = I
     return lib
 
@@ -147,3 +149,26 @@ def gated_rmsnorm(y, z, w, eps=1e-5, lib=None):
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
     return out
+
+
+def selective_scan(x, dt, A, B, C, D, h0=None, threads=None, lib=None):
+    """Mamba-1 selective scan in fp64.  x, dt [b,L,d]; A [d,N]; B, C [b,L,N];
+    D [d]; h0 [b,d,N] or None.  Returns (y [b,L,d] f64, h_out [b,d,N] f64)."""
+    lib = lib or load()
+    x, dt, A, B, C, D = (_f32(v) for v in (x, dt, A, B, C, D))
+    b, L, d = x.shape
+    N = A.shape[1]
+    assert dt.shape == (b, L, d) and A.shape == (d, N) and D.shape == (d,)
+    assert B.shape == (b, L, N) and C.shape == (b, L, N)
+    h0c = None
+    if h0 is not None:
+        h0c = np.ascontiguousarray(np.asarray(h0, dtype=np.float64))
+        assert h0c.shape == (b, d, N)
+    y = np.empty((b, L, d), dtype=np.float64)
+    h_out = np.empty((b, d, N), dtype=np.float64)
+    rc = lib.ssd_ref_selective_scan(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                    _ptr(h0c), b, L, d, N, _ptr(y), _ptr(h_out),
+                                    threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    return y, h_out

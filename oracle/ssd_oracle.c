@@ -30,7 +30,8 @@
  * factor, D is a per-head scalar skip, head h reads group floor(h*G/H).
  *
  * The decode-layer operations around the scan (the causal conv1d step and
- * the gated RMS norm) are at the end of this file, with their own passages.
+ * the gated RMS norm) and the Mamba-1 selective scan are at the end of this
+ * file, with their own passages.
  *
  * Inputs are float32 (bf16 inputs are upcast exactly before the call); all
  * arithmetic and the outputs are float64.  Layouts are row-major:
@@ -186,6 +187,53 @@ int ssd_ref_gated_rmsnorm(const double *y, const float *z, const float *w, doubl
         const double r = 1.0 / sqrt(ss / dim + eps);
         for (int d = 0; d < dim; ++d)
             out[(size_t)b * dim + d] *= r * (double)w[d];
+    }
+    return 0;
+}
+
+/*
+ * Mamba-1 selective scan: the generic selective update of COREY: Entropy-Guided
+ * Runtime Chunk Scheduling for Selective Scan Kernels, section 3.1
+ * (h_t = A_t h_{t-1} + B_t x_t, y_t = C_t h_t + D_t x_t) with a diagonal
+ * transition per channel and state, discretised as the SSD path above:
+ *
+ *   h_t[d][n] = exp(dt_t[d] * A[d][n]) * h_{t-1}[d][n] + dt_t[d] * B_t[n] * x_t[d]
+ *   y_t[d]    = sum_n C_t[n] * h_t[d][n] + D[d] * x_t[d]
+ *
+ * (the kernel that section 5.1 of that page times at batch 1, d 1024, L 4096,
+ * d_state 16).  Layouts: x, dt [b][L][d]; A [d][N]; B, C [b][L][N]; D [d];
+ * h0, h_out [b][d][N] (h0 NULL: zeros); y [b][L][d].
+ */
+int ssd_ref_selective_scan(const float *x, const float *dt, const float *A, const float *B,
+                           const float *C, const float *D, const double *h0, int batch, int L,
+                           int dim, int N, double *y, double *h_out, int nthreads)
+{
+    if (batch < 0 || L < 0 || dim < 1 || N < 1)
+        return -1;
+    if (nthreads < 1)
+        nthreads = 1;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+    for (long u = 0; u < (long)batch * dim; ++u) {
+        const int b = (int)(u / dim), d = (int)(u % dim);
+        double *h = (double *)malloc(sizeof(double) * (size_t)N);
+        for (int n = 0; n < N; ++n)
+            h[n] = h0 ? h0[((size_t)b * dim + d) * N + n] : 0.0;
+        for (int t = 0; t < L; ++t) {
+            const size_t td = ((size_t)b * L + t) * dim + d;
+            const double dtv = (double)dt[td], xv = (double)x[td];
+            const float *Bt = B + ((size_t)b * L + t) * N;
+            const float *Ct = C + ((size_t)b * L + t) * N;
+            double acc = 0.0;
+            for (int n = 0; n < N; ++n) {
+                h[n] = exp(dtv * (double)A[(size_t)d * N + n]) * h[n] + dtv * (double)Bt[n] * xv;
+                acc += (double)Ct[n] * h[n];
+            }
+            y[td] = acc + (double)D[d] * xv;
+        }
+        if (h_out)
+            for (int n = 0; n < N; ++n)
+                h_out[((size_t)b * dim + d) * N + n] = h[n];
+        free(h);
     }
     return 0;
 }

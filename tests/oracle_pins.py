@@ -23,7 +23,8 @@ What each pin rests on:
   padding    appended (dt = 0, x = 0) tokens leave h_out unchanged
   golden     hand-derived worked examples (tests/golden/hand_worked.json)
 The pins of the decode-layer operations (conv1d step, gated RMS norm) are in
-LAYER_PINS at the end of this file.
+LAYER_PINS, those of the Mamba-1 selective scan in S6_PINS, at the end of this
+file.
 """
 import json
 import os
@@ -343,4 +344,127 @@ def pin_norm_scale(orc):
 LAYER_PINS = {
     "conv_shift": pin_conv_shift, "conv_fir": pin_conv_fir, "conv_silu": pin_conv_silu,
     "norm_torch": pin_norm_torch, "norm_const": pin_norm_const, "norm_scale": pin_norm_scale,
+}
+
+
+# ---------------------------------------------------------------------------
+# Pins of the Mamba-1 selective scan (per channel d and state n: decay
+# exp(dt_t[d] A[d][n]), input dt_t[d] B_t[n] x_t[d], output sum_n C_t[n] h + D x).
+# Each takes an oracle handle with ``selective_scan`` and, for s6_ssd,
+# ``prefill`` (the pinned SSD oracle).
+#   s6_ssd        A constant over n is the SSD recurrence with P = 1, G = 1
+#   s6_lfilter    one channel, one state, constant coefficients: scipy lfilter
+#   s6_unrolled   closed-form unrolling of each (d, n) recurrence, O(L^2)
+#   s6_states     the output is the sum over n of one-state scans (plus D x)
+#   s6_split      two calls handing the state on equal one call
+#   s6_perm       permuting the channels permutes the outputs and states
+
+def _s6_case(b, L, d, N, seed, h0=True):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = rng.standard_normal((b, L, d)).astype(np.float32)
+    dt = np.exp(rng.uniform(np.log(1e-3), np.log(0.5), (b, L, d))).astype(np.float32)
+    A = (-np.exp(rng.uniform(0.0, np.log(16.0), (d, N)))).astype(np.float32)
+    B = (rng.standard_normal((b, L, N)) / np.sqrt(N)).astype(np.float32)
+    C = (rng.standard_normal((b, L, N)) / np.sqrt(N)).astype(np.float32)
+    D = rng.uniform(0.0, 1.0, d).astype(np.float32)
+    h = rng.normal(0.0, 0.3, (b, d, N)) if h0 else None
+    return x, dt, A, B, C, D, h
+
+
+def pin_s6_ssd(orc):
+    b, L, d, N = 2, 11, 5, 3
+    x, dt, A, B, C, D, h0 = _s6_case(b, L, d, N, 83)
+    A = np.repeat(A[:, :1], N, axis=1)           # one decay rate per channel
+    y, ho = orc.selective_scan(x, dt, A, B, C, D, h0)
+    cu = np.arange(b + 1) * L
+    ry, rh = orc.prefill(x.reshape(b * L, d, 1), dt.reshape(b * L, d), A[:, 0],
+                         B.reshape(b * L, 1, N), C.reshape(b * L, 1, N), D,
+                         h0.reshape(b, d, N, 1), cu)
+    e = max(_rel(y, ry.reshape(b, L, d)), _rel(ho, rh.reshape(b, d, N)))
+    return e <= RTOL, f"rel err {e:.3g}"
+
+
+def pin_s6_lfilter(orc):
+    from scipy.signal import lfilter
+    L = 30
+    rng = np.random.Generator(np.random.PCG64(89))
+    x = rng.standard_normal(L).astype(np.float32)
+    dt, A, Bv, Cv, Dv, h0 = np.float32(0.21), np.float32(-2.5), np.float32(1.3), \
+        np.float32(0.7), np.float32(0.4), -0.6
+    a = np.exp(np.float64(dt) * np.float64(A))
+    hs = lfilter([np.float64(dt) * np.float64(Bv)], [1.0, -a], x.astype(np.float64),
+                 zi=[a * h0])[0]
+    ry = np.float64(Cv) * hs + np.float64(Dv) * x
+    y, ho = orc.selective_scan(x.reshape(1, L, 1), np.full((1, L, 1), dt, np.float32),
+                               np.array([[A]]), np.full((1, L, 1), Bv, np.float32),
+                               np.full((1, L, 1), Cv, np.float32), np.array([Dv]),
+                               np.full((1, 1, 1), h0))
+    e = max(_rel(y.ravel(), ry), _rel(ho.ravel(), hs[-1:]))
+    return e <= RTOL, f"rel err {e:.3g}"
+
+
+def pin_s6_unrolled(orc):
+    b, L, d, N = 1, 9, 3, 4
+    x, dt, A, B, C, D, h0 = _s6_case(b, L, d, N, 97)
+    y, ho = orc.selective_scan(x, dt, A, B, C, D, h0)
+    x64, dt64, B64, C64 = (v.astype(np.float64)[0] for v in (x, dt, B, C))
+    ry = np.empty((L, d))
+    rh = np.empty((d, N))
+    for c in range(d):
+        for t in range(L):
+            acc = 0.0
+            for n in range(N):
+                dec = lambda lo, hi: np.exp(np.sum(dt64[lo:hi, c]) * np.float64(A[c, n]))
+                h = dec(0, t + 1) * h0[0, c, n]
+                for s in range(t + 1):
+                    h += dec(s + 1, t + 1) * dt64[s, c] * B64[s, n] * x64[s, c]
+                acc += C64[t, n] * h
+                if t == L - 1:
+                    rh[c, n] = h
+            ry[t, c] = acc + np.float64(D[c]) * x64[t, c]
+    e = max(_rel(y[0], ry), _rel(ho[0], rh))
+    return e <= 1e-11, f"rel err {e:.3g}"
+
+
+def pin_s6_states(orc):
+    b, L, d, N = 2, 10, 4, 5
+    x, dt, A, B, C, D, h0 = _s6_case(b, L, d, N, 101)
+    y, ho = orc.selective_scan(x, dt, A, B, C, D, h0)
+    acc = D.astype(np.float64)[None, None, :] * x.astype(np.float64)
+    hs = []
+    for n in range(N):
+        yn, hn = orc.selective_scan(x, dt, A[:, n:n + 1], B[:, :, n:n + 1], C[:, :, n:n + 1],
+                                    np.zeros_like(D), h0[:, :, n:n + 1])
+        acc = acc + yn
+        hs.append(hn)
+    e = max(_rel(y, acc), _rel(ho, np.concatenate(hs, axis=2)))
+    return e <= RTOL, f"rel err {e:.3g}"
+
+
+def pin_s6_split(orc):
+    b, L, d, N = 2, 13, 3, 4
+    x, dt, A, B, C, D, h0 = _s6_case(b, L, d, N, 103)
+    y, ho = orc.selective_scan(x, dt, A, B, C, D, h0)
+    worst = 0.0
+    for k in (0, 1, 6, 12, 13):
+        y1, h1 = orc.selective_scan(x[:, :k], dt[:, :k], A, B[:, :k], C[:, :k], D, h0)
+        y2, h2 = orc.selective_scan(x[:, k:], dt[:, k:], A, B[:, k:], C[:, k:], D, h1)
+        worst = max(worst, _rel(np.concatenate([y1, y2], axis=1), y), _rel(h2, ho))
+    return worst <= RTOL, f"max rel err {worst:.3g}"
+
+
+def pin_s6_perm(orc):
+    b, L, d, N = 2, 7, 6, 3
+    x, dt, A, B, C, D, h0 = _s6_case(b, L, d, N, 107)
+    perm = np.array([3, 0, 5, 1, 4, 2])
+    y, ho = orc.selective_scan(x, dt, A, B, C, D, h0)
+    yp, hp = orc.selective_scan(x[:, :, perm], dt[:, :, perm], A[perm], B, C, D[perm],
+                                h0[:, perm])
+    e = max(_rel(yp, y[:, :, perm]), _rel(hp, ho[:, perm]))
+    return e == 0.0, f"rel err {e:.3g}"
+
+
+S6_PINS = {
+    "s6_ssd": pin_s6_ssd, "s6_lfilter": pin_s6_lfilter, "s6_unrolled": pin_s6_unrolled,
+    "s6_states": pin_s6_states, "s6_split": pin_s6_split, "s6_perm": pin_s6_perm,
 }

@@ -124,3 +124,55 @@ def test_layer_mutant_is_caught(name, tmp_path_factory):
         if not ok:
             caught.append(pname)
     assert caught, f"mutant {name} passed every layer pin"
+
+
+
+# Planted mistakes in the Mamba-1 selective scan; each must fail a selective-scan pin.
+S6_MUTANTS = [
+    ("s6-A-transposed", "exp(dtv * (double)A[(size_t)d * N + n])",
+     "exp(dtv * (double)A[((size_t)n * dim + d) % ((size_t)dim * N)])"),
+    ("s6-dt-of-channel-0", "const double dtv = (double)dt[td], xv",
+     "const double dtv = (double)dt[td - d], xv"),
+    ("s6-C-replaced-by-B", "acc += (double)Ct[n] * h[n];", "acc += (double)Bt[n] * h[n];"),
+    ("s6-skip-dropped", "y[td] = acc + (double)D[d] * xv;", "y[td] = acc;"),
+    ("s6-dt-dropped-from-input", "+ dtv * (double)Bt[n] * xv;", "+ (double)Bt[n] * xv;"),
+    ("s6-h0-ignored", "h[n] = h0 ? h0[((size_t)b * dim + d) * N + n] : 0.0;", "h[n] = 0.0;"),
+    ("s6-B-of-next-token", "const float *Bt = B + ((size_t)b * L + t) * N;",
+     "const float *Bt = B + ((size_t)b * L + (t + 1) % L) * N;"),
+]
+
+
+@functools.lru_cache(maxsize=None)
+def _s6_mutant_lib(name, tmpdir):
+    orig, repl = next((o, r) for n, o, r in S6_MUTANTS if n == name)
+    assert orig in SRC, f"mutation site for {name} not found in the oracle source"
+    path = os.path.join(tmpdir, f"s6mut_{name}.c")
+    with open(path, "w") as f:
+        f.write(SRC.replace(orig, repl))
+    lib = obuild.build(path, os.path.join(tmpdir, f"libs6mut_{name}.so"),
+                       extra_flags=("-Wno-unused-variable", "-Wno-unused-but-set-variable"))
+    return oracle.load(lib)
+
+
+@pytest.mark.parametrize("name", [m[0] for m in S6_MUTANTS])
+def test_selective_scan_mutant_is_caught(name, tmp_path_factory):
+    lib = _s6_mutant_lib(name, str(tmp_path_factory.getbasetemp()))
+
+    class Orc:
+        @staticmethod
+        def selective_scan(*a, **k):
+            return oracle.selective_scan(*a, lib=lib, **k)
+
+        @staticmethod
+        def prefill(*a, **k):
+            return oracle.prefill(*a, **k)   # the real SSD oracle: the reference side
+
+    caught = []
+    for pname, pin in oracle_pins.S6_PINS.items():
+        try:
+            ok, _ = pin(Orc)
+        except (ValueError, AssertionError, FloatingPointError):
+            ok = False
+        if not ok:
+            caught.append(pname)
+    assert caught, f"mutant {name} passed every selective-scan pin"

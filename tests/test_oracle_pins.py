@@ -25,3 +25,14 @@ class _LayerOrc:
 def test_layer_pin(name):
     ok, detail = oracle_pins.LAYER_PINS[name](_LayerOrc)
     assert ok, f"pin {name} failed: {detail}"
+
+
+class _S6Orc:
+    selective_scan = staticmethod(oracle.selective_scan)
+    prefill = staticmethod(oracle.prefill)
+
+
+@pytest.mark.parametrize("name", sorted(oracle_pins.S6_PINS))
+def test_selective_scan_pin(name):
+    ok, detail = oracle_pins.S6_PINS[name](_S6Orc)
+    assert ok, f"pin {name} failed: {detail}"
