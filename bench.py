@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+TRANSCENDENTAL_PEAK_TPS = 9.83  # v_exp_f32 at a quarter of the fp32 lane rate: 256 x 4 x 16 x 2.4 GHz / 4
 FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector (packed): 256 CU x 4 SIMD x 16 lanes x 2 x 2 x 2.4 GHz
 FP32_PEAK_TFLOPS = 157.3     # MI355X fp32 vector
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -211,6 +212,8 @@ def _kernel_key(name, grid):
                         "mamba2-130m-layer-prefill"), k
             if k in ("decode_multi_step", "conv1d_step", "gated_rmsnorm"):
                 return "codestral-7b-decode-step", k
+            if k.startswith("s6_"):
+                return "mamba1-w1-selective-scan", k
             return "mamba2-130m-layer-prefill", k
     return None, None
 
@@ -368,6 +371,32 @@ def prefill_large(args, torch, inputs, ssd, dev):
             "algorithmic_flops": flops,
             "mfma_frac": round(flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4),
             "kernels_us": kern}
+
+
+def selective_scan_bench(torch, inputs, ssd, dev):
+    """The Mamba-1 selective scan at COREY's W1 shape (batch 1, d_inner 1024,
+    L 4096, d_state 16, float16), whole scan from HIP-graph replays."""
+    w = inputs.S6_W1
+    d = inputs.selective_scan_inputs(w["batch"], w["L"], w["dim"], w["N"], 1100, w["dtype"])
+    t = lambda a, o=None: torch.from_numpy(np.ascontiguousarray(a)).to(dev) if o is None \
+        else torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(o)
+    h16 = torch.float16
+    run, y, h = ssd.selective_scan(t(d["x"], h16), t(d["dt"], h16), t(d["A"]), t(d["B"], h16),
+                                   t(d["C"], h16), t(d["D"]), None, prepare=True)
+    run()
+    torch.cuda.synchronize()
+    ms = graph_ms(torch, run, reps=10, per_graph=10)
+    b, L, dim, N = w["batch"], w["L"], w["dim"], w["N"]
+    exps = b * L * dim * N                       # one decay per (token, channel, state)
+    nbytes = b * L * dim * (2 + 2 + 4) + 2 * b * L * N * 2 + dim * N * 4 + dim * 4 + b * dim * N * 4
+    rate = exps / (ms * 1e-3) / 1e12
+    return {"workload": w["name"], "shape": {k: w[k] for k in ("batch", "L", "dim", "N", "dtype")},
+            "us": round(ms * 1e3, 2), "tokens_per_s": round(b * L / (ms * 1e-3), 1),
+            "achieved_gb_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "roofline": {"bound": "alu", "achieved": round(rate, 3),
+                         "peak": TRANSCENDENTAL_PEAK_TPS, "unit": "Texp/s",
+                         "frac": round(rate / TRANSCENDENTAL_PEAK_TPS, 4), "traffic": None,
+                         "kernel": "selective_scan"}}
 
 
 def decode_layer_bench(torch, ssd, w3, dev, ms_scan):
@@ -542,6 +571,9 @@ def main():
     # conv channels H*P + 2*G*N, bf16 activations): conv -> scan -> gated norm
     layer = decode_layer_bench(torch, ssd, w3, dev, ms_dec_graph)
 
+    # ---- Mamba-1 selective scan at the COREY W1 shape (a second scan family)
+    s6 = selective_scan_bench(torch, inputs, ssd, dev)
+
     # MFMA utilisation estimate of the prefill (algorithmic flops / bf16 peak)
     fl = sum(work[n]["flops"] for n in ("chunk_state", "chunk_scan"))
     mfma_util = fl / (sum(kern_ms[n] for n in kern_ms if n != "decode_step") * 1e-3) / \
@@ -566,6 +598,7 @@ def main():
         "decode": decode,
         "decode_multi_step": decode_multi,
         "decode_layer_step": layer,
+        "selective_scan_w1": s6,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

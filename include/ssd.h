@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype_t;
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1, SSD_F16 = 2 } ssd_dtype_t;  /* F16: selective scan only */
 
 enum {
     SSD_OK = 0,
@@ -209,6 +209,33 @@ int ssd_decode_layer_step(const void *xbc, const void *z, const float *dt, const
                           const float *conv_b, float *h, const float *norm_w, float eps,
                           float *out, float *xbc_act, float *y, int batch, int H, int P, int N,
                           int G, int width, ssd_dtype_t dtype, void *stream);
+
+/*
+ * Mamba-1 selective scan: a diagonal transition per channel d and state n (the
+ * per-channel form of the selective update of COREY: Entropy-Guided Runtime
+ * Chunk Scheduling for Selective Scan Kernels, section 3.1, discretised as the
+ * SSD path; the kernel its section 5.1 times at batch 1, d 1024, L 4096,
+ * d_state 16):
+ *     h_t[d][n] = exp(dt_t[d] A[d][n]) h_{t-1}[d][n] + dt_t[d] B_t[n] x_t[d]
+ *     y_t[d]    = sum_n C_t[n] h_t[d][n] + D[d] x_t[d]
+ *
+ *   x, dt   [batch][L][dim]   dtype (float32, bfloat16 or float16)
+ *   A       [dim][N] float32 (<= 0);  D [dim] float32
+ *   B, C    [batch][L][N]     dtype
+ *   h0      [batch][dim][N] float32, or NULL for zeros
+ *   y       [batch][L][dim] float32 (must not alias any input)
+ *   h_out   [batch][dim][N] float32, or NULL; may be h0
+ *   workspace / workspace_bytes: device scratch of at least
+ *           ssd_selective_scan_workspace(batch, L, dim, N) bytes
+ * Arithmetic is float32.  Supported: N in {1,2,4,8,16}.  L = 0 copies h0 (or
+ * zeros) to h_out.  Splitting the sequence and passing h_out on as h0 gives
+ * the same result as one call.
+ */
+size_t ssd_selective_scan_workspace(int batch, int L, int dim, int N);
+int ssd_selective_scan(const void *x, const void *dt, const float *A, const void *B,
+                       const void *C, const float *D, const float *h0, float *y, float *h_out,
+                       int batch, int L, int dim, int N, ssd_dtype_t dtype, void *workspace,
+                       size_t workspace_bytes, void *stream);
 
 /* Message for the last non-zero return on the calling thread ("" if none). */
 const char *ssd_last_error(void);

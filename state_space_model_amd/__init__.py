@@ -25,3 +25,8 @@ def step_multi(*args, **kwargs):
 def decode_layer_step(*args, **kwargs):
     from . import ssd
     return ssd.decode_layer_step(*args, **kwargs)
+
+
+def selective_scan(*args, **kwargs):
+    from . import ssd
+    return ssd.selective_scan(*args, **kwargs)

@@ -204,6 +204,34 @@ int ssd_decode_layer_step(const void *xbc, const void *z, const float *dt, const
   return SSD_OK;
 }
 
+size_t ssd_selective_scan_workspace(int batch, int L, int dim, int N) {
+  if (batch < 0 || L < 0 || dim < 1 || !(N == 1 || N == 2 || N == 4 || N == 8 || N == 16)) return 0;
+  return ssd::s6_workspace(batch, L, dim, N);
+}
+
+int ssd_selective_scan(const void *x, const void *dt, const float *A, const void *B,
+                       const void *C, const float *D, const float *h0, float *y, float *h_out,
+                       int batch, int L, int dim, int N, ssd_dtype_t dtype, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+  g_err[0] = 0;
+  if (dtype != SSD_F32 && dtype != SSD_BF16 && dtype != SSD_F16)
+    return fail(SSD_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (batch < 0 || L < 0 || dim < 1) return fail(SSD_ERR_INVALID_ARG, "need batch >= 0, L >= 0, dim >= 1 (batch=%d L=%d dim=%d)", batch, L, dim);
+  if (!(N == 1 || N == 2 || N == 4 || N == 8 || N == 16)) return fail(SSD_ERR_UNSUPPORTED, "d_state N=%d not in {1,2,4,8,16}", N);
+  if (batch > 65535) return fail(SSD_ERR_UNSUPPORTED, "batch %d > 65535", batch);
+  if ((long long)L > 65535LL * (8192 / N)) return fail(SSD_ERR_UNSUPPORTED, "sequence length %d too long", L);
+  if (batch > 0 && L > 0 && (!x || !dt || !A || !B || !C || !D || !y))
+    return fail(SSD_ERR_INVALID_ARG, "null pointer argument");
+  if (batch > 0 && !A) return fail(SSD_ERR_INVALID_ARG, "null pointer argument");
+  const size_t need = ssd::s6_workspace(batch, L, dim, N);
+  if (batch > 0 && (!workspace || workspace_bytes < need))
+    return fail(SSD_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  ssd::S6Args a{x, dt, A, B, C, D, h0, y, h_out, batch, L, dim, N, (int)dtype, workspace, stream};
+  hipError_t e = ssd::launch_selective_scan(a);
+  if (e != hipSuccess) return fail(SSD_ERR_HIP, "HIP error: %s", hipGetErrorString(e));
+  return SSD_OK;
+}
+
 const char *ssd_last_error(void) { return g_err; }
 
 }  // extern "C"

@@ -77,6 +77,24 @@ struct MultiStepArgs {
 };
 hipError_t launch_step_multi(const MultiStepArgs &a);
 
+// Mamba-1 selective scan (ssd_s6.hip).  dtype: 0 float32, 1 bfloat16, 2 float16.
+struct S6Args {
+  const void *x, *dt;
+  const float *A;
+  const void *B, *C;
+  const float *D, *h0;
+  float *y, *h_out;
+  int batch, L, dim, N, dtype;
+  void *workspace;
+  void *stream;
+};
+struct S6Plan {
+  int seg, nseg;  // tokens per segment, segments
+};
+S6Plan s6_plan(int batch, int L, int dim, int N);
+size_t s6_workspace(int batch, int L, int dim, int N);
+hipError_t launch_selective_scan(const S6Args &a);
+
 // Decode-layer operations around the scan (ssd_layer.hip).
 hipError_t launch_conv1d_step(const void *u, float *state, const float *w, const float *bias,
                               bool silu, void *out, int batch, int channels, int width,

@@ -131,3 +131,33 @@ def workload_inputs(k, seed=None):
     else:
         lengths = np.full(w.batch, w.L, dtype=np.int64)
     return _prefill_from(rng, w.H, w.P, w.N, w.G, lengths, w.dtype, w.h0)
+
+
+def round_f16(a):
+    """Round float32 values to the nearest float16 (ties to even); returns float32."""
+    return np.ascontiguousarray(a, dtype=np.float32).astype(np.float16).astype(np.float32)
+
+
+# The Mamba-1 selective-scan workload timed by COREY (section 5.1, Tables 2
+# and 17): batch 1, d_inner 1024, L 4096, d_state 16, float16 activations.
+S6_W1 = dict(name="mamba1-w1-selective-scan", batch=1, L=4096, dim=1024, N=16, dtype="f16")
+
+
+def selective_scan_inputs(batch, L, dim, N, seed, dtype="f16", h0=False):
+    """Seeded Mamba-1 selective-scan inputs, drawn in this order: per channel
+    dt bias (as the SSD workloads), A[d][n] = -exp(U[log 1, log 16]),
+    D ~ U[0,1]; per token x ~ N(0,1), dt = softplus(N(0,0.5^2) + bias),
+    B, C ~ N(0,1)/sqrt(N); then h0 ~ N(0,0.1^2) if asked.  x, dt, B, C are
+    rounded once to the operand dtype ("f32", "bf16" or "f16")."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    dt0 = np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), size=dim))
+    bias = np.log(np.expm1(dt0))
+    A = (-np.exp(rng.uniform(0.0, np.log(16.0), size=(dim, N)))).astype(np.float32)
+    D = rng.uniform(0.0, 1.0, size=dim).astype(np.float32)
+    x = rng.standard_normal(size=(batch, L, dim)).astype(np.float32)
+    dt = _softplus(rng.normal(0.0, 0.5, size=(batch, L, dim)) + bias).astype(np.float32)
+    B = (rng.standard_normal(size=(batch, L, N)) / np.sqrt(N)).astype(np.float32)
+    C = (rng.standard_normal(size=(batch, L, N)) / np.sqrt(N)).astype(np.float32)
+    h = rng.normal(0.0, 0.1, size=(batch, dim, N)).astype(np.float32) if h0 else None
+    rnd = {"f32": lambda v: v, "bf16": round_bf16, "f16": round_f16}[dtype]
+    return dict(x=rnd(x), dt=rnd(dt), A=A, B=rnd(B), C=rnd(C), D=D, h0=h)

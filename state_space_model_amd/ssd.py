@@ -13,14 +13,15 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libssd.so")
 
-SSD_F32, SSD_BF16 = 0, 1
+SSD_F32, SSD_BF16, SSD_F16 = 0, 1, 2
 STAGE_CHUNK_CUMSUM, STAGE_CHUNK_STATE, STAGE_STATE_PASS, STAGE_CHUNK_SCAN = 1, 2, 4, 8
 STAGE_ALL = 15
 ERRORS = {0: "SSD_OK", -1: "SSD_ERR_INVALID_ARG", -2: "SSD_ERR_UNSUPPORTED",
           -3: "SSD_ERR_WORKSPACE", -4: "SSD_ERR_HIP"}
 EXPORTS = ("ssd_scan_prefill_workspace", "ssd_scan_prefill", "ssd_scan_prefill_stages",
            "ssd_step", "ssd_step_multi", "ssd_conv1d_step", "ssd_gated_rmsnorm",
-           "ssd_decode_layer_step", "ssd_last_error")
+           "ssd_decode_layer_step", "ssd_selective_scan_workspace", "ssd_selective_scan",
+           "ssd_last_error")
 
 _lib = None
 
@@ -62,6 +63,11 @@ def load(path=LIB_PATH):
     lib.ssd_decode_layer_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp,
                                           i32, i32, i32, i32, i32, i32, i32, vp]
     lib.ssd_decode_layer_step.restype = i32
+    lib.ssd_selective_scan_workspace.argtypes = [i32, i32, i32, i32]
+    lib.ssd_selective_scan_workspace.restype = sz
+    lib.ssd_selective_scan.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                       vp, sz, vp]
+    lib.ssd_selective_scan.restype = i32
     lib.ssd_last_error.argtypes = []
     lib.ssd_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -337,3 +343,48 @@ def decode_layer_step(xbc, z, dt, A, D, conv_state, conv_w, conv_b, h, norm_w, e
         return Prepared(load().ssd_decode_layer_step, args, keep=keep), out
     _check(load().ssd_decode_layer_step(*args, _stream()))
     return out
+
+
+def selective_scan(x, dt, A, B, C, D, h0=None, *, y=None, h_out=None, workspace=None,
+                   prepare=False):
+    """Mamba-1 selective scan.  x, dt [b,L,d] and B, C [b,L,N] in float32,
+    bfloat16 or float16; A [d,N], D [d] float32; h0 [b,d,N] float32 or None.
+    Returns (y [b,L,d] float32, h_out [b,d,N] float32)."""
+    b, L, d = x.shape
+    N = A.shape[1]
+    dev = x.device
+    _need(x, "x", dev=dev)
+    codes = {torch.float32: SSD_F32, torch.bfloat16: SSD_BF16, torch.float16: SSD_F16}
+    if x.dtype not in codes:
+        raise TypeError(f"x must be float32, bfloat16 or float16, got {x.dtype}")
+    code = codes[x.dtype]
+    for t, n in ((dt, "dt"), (B, "B"), (C, "C")):
+        _need(t, n, x.dtype, dev)
+    for t, n in ((A, "A"), (D, "D")):
+        _need(t, n, torch.float32, dev)
+    if tuple(dt.shape) != (b, L, d) or tuple(A.shape) != (d, N) or tuple(D.shape) != (d,) or \
+            tuple(B.shape) != (b, L, N) or tuple(C.shape) != (b, L, N):
+        raise ValueError("dt must be [b,L,d], A [d,N], D [d], B/C [b,L,N]")
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, dev)
+        if tuple(h0.shape) != (b, d, N):
+            raise ValueError("h0 must be [b,d,N]")
+    if y is None:
+        y = torch.empty((b, L, d), dtype=torch.float32, device=dev)
+    if h_out is None:
+        h_out = torch.empty((b, d, N), dtype=torch.float32, device=dev)
+    _need(y, "y", torch.float32, dev)
+    _need(h_out, "h_out", torch.float32, dev)
+    lib = load()
+    if workspace is None:
+        n = int(lib.ssd_selective_scan_workspace(b, L, d, N))
+        if n == 0:
+            raise SSDError(-2, "unsupported selective-scan shape")
+        workspace = torch.empty(n, dtype=torch.uint8, device=dev)
+    args = (_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(y), _ptr(h_out),
+            b, L, d, N, code, _ptr(workspace), workspace.numel())
+    if prepare:
+        keep = (x, dt, A, B, C, D, h0, y, h_out, workspace)
+        return Prepared(lib.ssd_selective_scan, args, keep=keep), y, h_out
+    _check(lib.ssd_selective_scan(*args, _stream()))
+    return y, h_out

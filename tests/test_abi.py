@@ -124,6 +124,26 @@ def test_step_multi_rejects_before_launch(kw, code, frag):
     assert rc == code and frag in lib.ssd_last_error().decode()
 
 
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(N=3), -2, "d_state"),
+    (dict(N=32), -2, "d_state"),
+    (dict(dim=0), -1, "dim"),
+    (dict(L=-1), -1, "L >= 0"),
+    (dict(x=None), -1, "null"),
+    (dict(dtype=5), -1, "dtype"),
+    (dict(ws=0), -3, "workspace"),
+])
+def test_selective_scan_rejects_before_launch(kw, code, frag):
+    lib = ssd.load()
+    a = dict(x=1, batch=1, L=64, dim=8, N=4, dtype=2, ws=1 << 20)
+    a.update(kw)
+    p = ctypes.c_void_p
+    xptr = None if a["x"] is None else p(a["x"])
+    rc = lib.ssd_selective_scan(xptr, p(1), p(1), p(1), p(1), p(1), None, p(1), None, a["batch"],
+                                a["L"], a["dim"], a["N"], a["dtype"], p(1), a["ws"], None)
+    assert rc == code and frag in lib.ssd_last_error().decode()
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros(64, 4, 16)
