@@ -9,6 +9,7 @@ token, in float64).  This module only marshals arrays through ctypes:
 
 * ``prefill(x, dt, A, B, C, D, h0=None, cu_seqlens=None)`` -> ``(y, h_out)``
 * ``step(x, dt, A, B, C, D, h)`` -> ``y`` (``h`` updated in place)
+* ``prefill_backward(..., dy, dh_out)`` -> gradients of the prefill inputs
 
 Passages followed: COREY, section 3.1 (generic selective SSM update);
 Compiler-First State Space Duality ..., Abstract (one scalar decay per head);
@@ -51,6 +52,9 @@ def _bind(lib):
     lib.ssd_ref_selective_scan.argtypes = [P, P, P, P, P, P, P, I, I, I, I, P, P, I]
     lib.ssd_ref_selective_scan.restype = I
     lib.ssd_ref_step.restype = I
+    lib.ssd_ref_prefill_backward.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, P, P,
+                                             P, P, P, P, P, P, P, I]
+    lib.ssd_ref_prefill_backward.restype = I
     return lib
 
 
@@ -172,3 +176,38 @@ def selective_scan(x, dt, A, B, C, D, h0=None, threads=None, lib=None):
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
     return y, h_out
+
+
+def prefill_backward(x, dt, A, B, C, D, dy, h0=None, dh_out=None, cu_seqlens=None, threads=None,
+                     lib=None):
+    """Reverse-mode gradients of ``prefill`` in fp64 for a loss with
+    dL/dy = dy [T,H,P] and dL/dh_out = dh_out [nseq,H,N,P] (None = 0).
+    Returns a dict with dx [T,H,P], ddt [T,H], dA [H], dB/dC [T,G,N], dD [H]
+    and dh0 [nseq,H,N,P] (all float64)."""
+    lib = lib or load()
+    x, dt, A, B, C, D = (_f32(v) for v in (x, dt, A, B, C, D))
+    T, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    if cu_seqlens is None:
+        cu_seqlens = np.array([0, T], dtype=np.int64)
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    nseq = cu.shape[0] - 1
+    assert cu[0] == 0 and cu[-1] == T
+    assert dt.shape == (T, H) and A.shape == (H,) and D.shape == (H,)
+    assert B.shape == (T, G, N) and C.shape == (T, G, N)
+    f64 = lambda a: None if a is None else np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+    h0c, dyc, dhc = f64(h0), f64(dy), f64(dh_out)
+    assert dyc.shape == (T, H, P)
+    assert h0c is None or h0c.shape == (nseq, H, N, P)
+    assert dhc is None or dhc.shape == (nseq, H, N, P)
+    out = dict(dx=np.empty((T, H, P)), ddt=np.empty((T, H)), dA=np.empty(H),
+               dB=np.empty((T, G, N)), dC=np.empty((T, G, N)), dD=np.empty(H),
+               dh0=np.empty((nseq, H, N, P)))
+    rc = lib.ssd_ref_prefill_backward(
+        _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0c), _ptr(cu), nseq, H, P,
+        N, G, _ptr(dyc), _ptr(dhc), _ptr(out["dx"]), _ptr(out["ddt"]), _ptr(out["dA"]),
+        _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dh0"]),
+        threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    return out

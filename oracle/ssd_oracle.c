@@ -30,8 +30,9 @@
  * factor, D is a per-head scalar skip, head h reads group floor(h*G/H).
  *
  * The decode-layer operations around the scan (the causal conv1d step and
- * the gated RMS norm) and the Mamba-1 selective scan are at the end of this
- * file, with their own passages.
+ * the gated RMS norm), the Mamba-1 selective scan and the reverse-mode
+ * gradients of the recurrence (the backward half of a training step) are at
+ * the end of this file, with their own passages.
  *
  * Inputs are float32 (bf16 inputs are upcast exactly before the call); all
  * arithmetic and the outputs are float64.  Layouts are row-major:
@@ -236,4 +237,144 @@ int ssd_ref_selective_scan(const float *x, const float *dt, const float *A, cons
         free(h);
     }
     return 0;
+}
+
+/*
+ * Gradients of the SSD recurrence above (reverse mode, fp64) for a scalar loss
+ * L with dL/dy = dy [T][H][P] and dL/dh_out = dh_out [nseq][H][N][P] (NULL: 0).
+ * Per (sequence, head) the states h_t are recomputed forward and kept; then,
+ * walking the tokens backward with g_t = dL/dh_t (everything downstream of
+ * h_t):
+ *   g_t        = C_t (x) dy_t + a_{t+1} g_{t+1}     (g of the last token adds dh_out)
+ *   dC_t[n]   += sum_p h_t[n][p] dy_t[p]
+ *   dx_t[p]    = D dy_t[p] + dt_t sum_n B_t[n] g_t[n][p]
+ *   dB_t[n]   += dt_t sum_p x_t[p] g_t[n][p]
+ *   da_t       = sum_{n,p} g_t[n][p] h_{t-1}[n][p]          (a_t = exp(dt_t A))
+ *   ddt_t      = A a_t da_t + sum_{n,p} g_t[n][p] x_t[p] B_t[n]
+ *   dA        += dt_t a_t da_t;   dD += sum_p dy_t[p] x_t[p];   dh0 = a_first g_first
+ * dB and dC [T][G][N] sum over the heads of a group; dA, dD [H] over every
+ * sequence.  This is the chain rule through the unrolled recurrence, the
+ * training-side counterpart of the forward scan (Compiler-First State Space
+ * Duality and Portable O(1) Autoregressive Caching for Inference, Table 13
+ * times forward plus backward steps).  Arrays as in ssd_ref_prefill; every
+ * output is written (zeros where nothing flows).
+ */
+int ssd_ref_prefill_backward(const float *x, const float *dt, const float *A,
+                             const float *B, const float *C, const float *D,
+                             const double *h0, const int64_t *cu, int nseq,
+                             int H, int P, int N, int G,
+                             const double *dy, const double *dh_out,
+                             double *dx, double *ddt, double *dA, double *dB,
+                             double *dC, double *dD, double *dh0, int nthreads)
+{
+    if (!x || !dt || !A || !B || !C || !D || !cu || !dy) return -1;
+    if (!dx || !ddt || !dA || !dB || !dC || !dD) return -1;
+    if (nseq < 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0 || H % G != 0) return -1;
+    for (int s = 0; s < nseq; ++s)
+        if (cu[s + 1] < cu[s]) return -1;
+    const int64_t T = nseq > 0 ? cu[nseq] : 0;
+    const size_t NP = (size_t)N * P;
+    /* per-head contributions, reduced over heads / sequences afterwards */
+    double *dBh = (double *)calloc((size_t)(T > 0 ? T : 1) * H * N, sizeof(double));
+    double *dCh = (double *)calloc((size_t)(T > 0 ? T : 1) * H * N, sizeof(double));
+    double *dAs = (double *)calloc((size_t)(nseq > 0 ? nseq : 1) * H, sizeof(double));
+    double *dDs = (double *)calloc((size_t)(nseq > 0 ? nseq : 1) * H, sizeof(double));
+    if (!dBh || !dCh || !dAs || !dDs) { free(dBh); free(dCh); free(dAs); free(dDs); return -1; }
+    const long units = (long)nseq * H;
+    if (nthreads <= 0) nthreads = 1;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+    for (long u = 0; u < units; ++u) {
+        const int s = (int)(u / H), hd = (int)(u % H);
+        const int g = (int)(((long)hd * G) / H);
+        const int64_t t0 = cu[s], L = cu[s + 1] - cu[s];
+        const double Ah = (double)A[hd], Dh = (double)D[hd];
+        const size_t hoff = ((size_t)s * H + hd) * NP;
+        /* hs[k] = state after k tokens (hs[0] = h0) */
+        double *hs = (double *)malloc(sizeof(double) * NP * (size_t)(L + 1));
+        double *gg = (double *)malloc(sizeof(double) * NP);
+        if (!hs || !gg) { bad = 1; free(hs); free(gg); continue; }
+        if (h0) memcpy(hs, h0 + hoff, sizeof(double) * NP);
+        else memset(hs, 0, sizeof(double) * NP);
+        for (int64_t k = 0; k < L; ++k) {
+            const int64_t t = t0 + k;
+            const double dtv = (double)dt[(size_t)t * H + hd], a = exp(dtv * Ah);
+            const float *xt = x + ((size_t)t * H + hd) * P, *Bt = B + ((size_t)t * G + g) * N;
+            const double *hp = hs + NP * (size_t)k;
+            double *hn = hs + NP * (size_t)(k + 1);
+            for (int n = 0; n < N; ++n)
+                for (int p = 0; p < P; ++p)
+                    hn[(size_t)n * P + p] = a * hp[(size_t)n * P + p] + dtv * (double)xt[p] * (double)Bt[n];
+        }
+        if (dh_out) memcpy(gg, dh_out + hoff, sizeof(double) * NP);
+        else memset(gg, 0, sizeof(double) * NP);
+        double dAacc = 0.0, dDacc = 0.0, a_next = 1.0;
+        for (int64_t k = L - 1; k >= 0; --k) {
+            const int64_t t = t0 + k;
+            const double dtv = (double)dt[(size_t)t * H + hd], a = exp(dtv * Ah);
+            const float *xt = x + ((size_t)t * H + hd) * P;
+            const float *Bt = B + ((size_t)t * G + g) * N, *Ct = C + ((size_t)t * G + g) * N;
+            const double *dyt = dy + ((size_t)t * H + hd) * P;
+            const double *ht = hs + NP * (size_t)(k + 1), *hprev = hs + NP * (size_t)k;
+            /* g_t = a_{t+1} g_{t+1} + C_t (x) dy_t  (a_next = 1 for the last token) */
+            for (int n = 0; n < N; ++n)
+                for (int p = 0; p < P; ++p)
+                    gg[(size_t)n * P + p] = a_next * gg[(size_t)n * P + p] + (double)Ct[n] * dyt[p];
+            double *dxt = dx + ((size_t)t * H + hd) * P;
+            for (int p = 0; p < P; ++p) {
+                double acc = 0.0;
+                for (int n = 0; n < N; ++n)
+                    acc += (double)Bt[n] * gg[(size_t)n * P + p];
+                dxt[p] = Dh * dyt[p] + dtv * acc;
+                dDacc += dyt[p] * (double)xt[p];
+            }
+            double da = 0.0, gxb = 0.0;
+            for (int n = 0; n < N; ++n) {
+                double cb = 0.0, bb = 0.0;
+                for (int p = 0; p < P; ++p) {
+                    const double gv = gg[(size_t)n * P + p];
+                    cb += ht[(size_t)n * P + p] * dyt[p];
+                    bb += (double)xt[p] * gv;
+                    da += gv * hprev[(size_t)n * P + p];
+                }
+                dCh[((size_t)t * H + hd) * N + n] = cb;
+                dBh[((size_t)t * H + hd) * N + n] = dtv * bb;
+                gxb += bb * (double)Bt[n];
+            }
+            ddt[(size_t)t * H + hd] = Ah * a * da + gxb;
+            dAacc += dtv * a * da;
+            a_next = a;
+        }
+        if (dh0)
+            for (size_t e = 0; e < NP; ++e)
+                dh0[hoff + e] = a_next * gg[e];
+        dAs[(size_t)s * H + hd] = dAacc;
+        dDs[(size_t)s * H + hd] = dDacc;
+        free(hs);
+        free(gg);
+    }
+    /* sums over the heads of a group and over the sequences */
+    for (int64_t t = 0; t < T; ++t)
+        for (int g = 0; g < G; ++g)
+            for (int n = 0; n < N; ++n) {
+                double sb = 0.0, sc = 0.0;
+                for (int hd = 0; hd < H; ++hd)
+                    if ((int)(((long)hd * G) / H) == g) {
+                        sb += dBh[((size_t)t * H + hd) * N + n];
+                        sc += dCh[((size_t)t * H + hd) * N + n];
+                    }
+                dB[((size_t)t * G + g) * N + n] = sb;
+                dC[((size_t)t * G + g) * N + n] = sc;
+            }
+    for (int hd = 0; hd < H; ++hd) {
+        double sa = 0.0, sd = 0.0;
+        for (int s = 0; s < nseq; ++s) {
+            sa += dAs[(size_t)s * H + hd];
+            sd += dDs[(size_t)s * H + hd];
+        }
+        dA[hd] = sa;
+        dD[hd] = sd;
+    }
+    free(dBh); free(dCh); free(dAs); free(dDs);
+    return bad ? -1 : 0;
 }

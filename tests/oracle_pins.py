@@ -468,3 +468,144 @@ S6_PINS = {
     "s6_ssd": pin_s6_ssd, "s6_lfilter": pin_s6_lfilter, "s6_unrolled": pin_s6_unrolled,
     "s6_states": pin_s6_states, "s6_split": pin_s6_split, "s6_perm": pin_s6_perm,
 }
+
+
+# ---------------------------------------------------------------------------
+# Pins of the reverse-mode gradients (``prefill_backward``).  The loss is
+# L = <dy, y> + <dh_out, h_out> for fixed random dy, dh_out; each pin takes an
+# oracle handle with ``prefill`` (the pinned forward) and ``prefill_backward``.
+#   bwd_affine   x, h0, B, C and D each enter L affinely with the rest fixed, so
+#                every partial derivative is exactly L(v = e_i) - L(v = 0):
+#                brute force over every element, on a packed batch of two
+#                sequences with two heads per group
+#   bwd_fd       dt and A enter through exp(dt A): Richardson-extrapolated
+#                central differences on an exactly representable grid
+#   bwd_euler    homogeneity: <dC, C> = <dy, y - D x>; with h0 = 0,
+#                <dB, B> = <dy, y - D x> + <dh_out, h_out> and
+#                <ddt, dt> - <dA, A> = <dB, B>; <dD, D> = <dy, D x>;
+#                <dx, x> + <dh0, h0> = L
+#   bwd_split    a sequence cut in two, the second part's dh0 handed back as
+#                the first part's dh_out, gives the gradients of one call
+
+def _bwd_case(lens, H, P, N, G, seed, h0=True, grid=False):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    T = int(sum(lens))
+    nseq = len(lens)
+    x = rng.standard_normal((T, H, P)).astype(np.float32)
+    if grid:   # dt on 2^-10 steps, A on 2^-6 steps: +-2^-12, +-2^-10 stay exact
+        dt = (rng.integers(1, 200, (T, H)) * 2.0 ** -10).astype(np.float32)
+        A = (-rng.integers(8, 400, H) * 2.0 ** -6).astype(np.float32)
+    else:
+        dt = np.exp(rng.uniform(np.log(1e-3), np.log(0.2), (T, H))).astype(np.float32)
+        A = (-np.exp(rng.uniform(0.0, np.log(8.0), H))).astype(np.float32)
+    B = (rng.standard_normal((T, G, N)) / np.sqrt(N)).astype(np.float32)
+    C = (rng.standard_normal((T, G, N)) / np.sqrt(N)).astype(np.float32)
+    D = rng.uniform(0.0, 1.0, H).astype(np.float32)
+    hz = rng.normal(0.0, 0.3, (nseq, H, N, P)) if h0 else None
+    dy = rng.standard_normal((T, H, P))
+    dh = rng.standard_normal((nseq, H, N, P))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    return dict(x=x, dt=dt, A=A, B=B, C=C, D=D, h0=hz, dy=dy, dh=dh, cu=cu)
+
+
+def _loss(orc, c, **over):
+    v = dict(c, **over)
+    y, ho = orc.prefill(v["x"], v["dt"], v["A"], v["B"], v["C"], v["D"], v["h0"], v["cu"],
+                        threads=1)
+    return float(np.sum(v["dy"] * y) + np.sum(v["dh"] * ho))
+
+
+def _grads(orc, c, **over):
+    v = dict(c, **over)
+    return orc.prefill_backward(v["x"], v["dt"], v["A"], v["B"], v["C"], v["D"], v["dy"],
+                                v["h0"], v["dh"], v["cu"], threads=1)
+
+
+def pin_bwd_affine(orc):
+    c = _bwd_case([5, 4], 4, 2, 3, 2, 131)
+    g = _grads(orc, c)
+    worst = 0.0
+    for key, arr in (("x", c["x"]), ("B", c["B"]), ("C", c["C"]), ("D", c["D"]),
+                     ("h0", c["h0"])):
+        num = np.empty(arr.shape)
+        zero = np.zeros_like(arr)
+        base = _loss(orc, c, **{key: zero})
+        for i in np.ndindex(arr.shape):
+            e = zero.copy()
+            e[i] = 1
+            num[i] = _loss(orc, c, **{key: e}) - base
+        worst = max(worst, _rel(g["d" + key], num))
+    return worst <= 1e-11, f"max rel err {worst:.3g}"
+
+
+def pin_bwd_fd(orc):
+    c = _bwd_case([6, 3], 3, 2, 2, 1, 137, grid=True)
+    g = _grads(orc, c)
+
+    def richardson(key, idx, h):
+        def diff(s):
+            lo, hi = c[key].copy(), c[key].copy()
+            lo[idx] -= np.float32(s)
+            hi[idx] += np.float32(s)
+            return (_loss(orc, c, **{key: hi}) - _loss(orc, c, **{key: lo})) / (2 * s)
+        return (4 * diff(h / 2) - diff(h)) / 3
+
+    worst = 0.0
+    for key, h in (("dt", 2.0 ** -12), ("A", 2.0 ** -10)):
+        num = np.array([richardson(key, i, h) for i in np.ndindex(c[key].shape)])
+        worst = max(worst, _rel(g["d" + key].ravel(), num))
+    return worst <= 1e-8, f"max rel err {worst:.3g}"
+
+
+def pin_bwd_euler(orc):
+    worst = 0.0
+    for seed, lens, (H, P, N, G) in ((139, [40, 1, 23], (4, 8, 16, 2)),
+                                     (149, [64], (6, 4, 8, 3))):
+        c = _bwd_case(lens, H, P, N, G, seed, h0=True)
+        g = _grads(orc, c)
+        y, ho = orc.prefill(c["x"], c["dt"], c["A"], c["B"], c["C"], c["D"], c["h0"], c["cu"])
+        x64 = c["x"].astype(np.float64)
+        dxD = x64 * c["D"].astype(np.float64)[None, :, None]
+        L = np.sum(c["dy"] * y) + np.sum(c["dh"] * ho)
+        scale = max(1.0, abs(L), float(np.sum(np.abs(c["dy"] * y))))
+        rel = lambda a, b: abs(a - b) / scale
+        worst = max(worst,
+                    rel(np.sum(g["dC"] * c["C"]), np.sum(c["dy"] * (y - dxD))),
+                    rel(np.sum(g["dD"] * c["D"]), np.sum(c["dy"] * dxD)),
+                    rel(np.sum(g["dx"] * x64) + np.sum(g["dh0"] * c["h0"]), L))
+        c0 = dict(c, h0=None)
+        g0 = _grads(orc, c0)
+        y0, h0o = orc.prefill(c["x"], c["dt"], c["A"], c["B"], c["C"], c["D"], None, c["cu"])
+        dBB = np.sum(g0["dB"] * c["B"])
+        worst = max(worst,
+                    rel(dBB, np.sum(c["dy"] * (y0 - dxD)) + np.sum(c["dh"] * h0o)),
+                    rel(np.sum(g0["ddt"] * c["dt"]) - np.sum(g0["dA"] * c["A"]), dBB))
+    return worst <= 1e-12, f"max rel err {worst:.3g}"
+
+
+def pin_bwd_split(orc):
+    c = _bwd_case([17], 3, 4, 5, 1, 151)
+    full = _grads(orc, c)
+    worst = 0.0
+    for k in (1, 8, 16):
+        a = lambda v: v[:k]
+        b = lambda v: v[k:]
+        part1 = dict(c, x=a(c["x"]), dt=a(c["dt"]), B=a(c["B"]), C=a(c["C"]), dy=a(c["dy"]),
+                     cu=np.array([0, k], np.int64))
+        _, hmid = orc.prefill(part1["x"], part1["dt"], c["A"], part1["B"], part1["C"], c["D"],
+                              c["h0"], part1["cu"])
+        part2 = dict(c, x=b(c["x"]), dt=b(c["dt"]), B=b(c["B"]), C=b(c["C"]), dy=b(c["dy"]),
+                     h0=hmid, cu=np.array([0, 17 - k], np.int64))
+        g2 = _grads(orc, part2)
+        g1 = _grads(orc, dict(part1, dh=g2["dh0"]))
+        for key in ("dx", "ddt", "dB", "dC"):
+            worst = max(worst, _rel(np.concatenate([g1[key], g2[key]]), full[key]))
+        worst = max(worst, _rel(g1["dA"] + g2["dA"], full["dA"]),
+                    _rel(g1["dD"] + g2["dD"], full["dD"]), _rel(g1["dh0"], full["dh0"]))
+    return worst <= RTOL, f"max rel err {worst:.3g}"
+
+
+BWD_PINS = {
+    "bwd_affine": pin_bwd_affine, "bwd_fd": pin_bwd_fd, "bwd_euler": pin_bwd_euler,
+    "bwd_split": pin_bwd_split,
+}

@@ -176,3 +176,63 @@ def test_selective_scan_mutant_is_caught(name, tmp_path_factory):
         if not ok:
             caught.append(pname)
     assert caught, f"mutant {name} passed every selective-scan pin"
+
+
+# Planted mistakes in the reverse-mode gradients; each must fail a backward pin
+# (the forward side of those pins is the real oracle).
+BWD_MUTANTS = [
+    ("bwd-skip-dropped-from-dx", "dxt[p] = Dh * dyt[p] + dtv * acc;", "dxt[p] = dtv * acc;"),
+    ("bwd-ddt-decay-sign", "ddt[(size_t)t * H + hd] = Ah * a * da + gxb;",
+     "ddt[(size_t)t * H + hd] = -Ah * a * da + gxb;"),
+    ("bwd-adjoint-not-decayed", "= a_next * gg[(size_t)n * P + p] + (double)Ct[n]",
+     "= gg[(size_t)n * P + p] + (double)Ct[n]"),
+    ("bwd-dB-without-dt", "= dtv * bb;", "= bb;"),
+    ("bwd-dA-without-dt", "dAacc += dtv * a * da;", "dAacc += a * da;"),
+    ("bwd-dh0-not-decayed", "dh0[hoff + e] = a_next * gg[e];", "dh0[hoff + e] = gg[e];"),
+    ("bwd-da-uses-new-state", "da += gv * hprev[(size_t)n * P + p];",
+     "da += gv * ht[(size_t)n * P + p];"),
+    ("bwd-dC-uses-old-state", "cb += ht[(size_t)n * P + p] * dyt[p];",
+     "cb += hprev[(size_t)n * P + p] * dyt[p];"),
+    ("bwd-dA-last-sequence-only", "sa += dAs[(size_t)s * H + hd];",
+     "sa = dAs[(size_t)s * H + hd];"),
+    ("bwd-dh_out-ignored", "if (dh_out) memcpy(gg, dh_out + hoff", "if (0) memcpy(gg, dh_out + hoff"),
+    ("bwd-dD-without-x", "dDacc += dyt[p] * (double)xt[p];", "dDacc += dyt[p];"),
+    ("bwd-group-sum-first-head", "if ((int)(((long)hd * G) / H) == g) {",
+     "if (hd == g * (H / G)) {"),
+]
+
+
+@functools.lru_cache(maxsize=None)
+def _bwd_mutant_lib(name, tmpdir):
+    orig, repl = next((o, r) for n, o, r in BWD_MUTANTS if n == name)
+    assert SRC.count(orig) == 1, f"mutation site for {name} not unique in the oracle source"
+    path = os.path.join(tmpdir, f"bwdmut_{name}.c")
+    with open(path, "w") as f:
+        f.write(SRC.replace(orig, repl))
+    lib = obuild.build(path, os.path.join(tmpdir, f"libbwdmut_{name}.so"),
+                       extra_flags=("-Wno-unused-variable", "-Wno-unused-but-set-variable"))
+    return oracle.load(lib)
+
+
+@pytest.mark.parametrize("name", [m[0] for m in BWD_MUTANTS])
+def test_backward_mutant_is_caught(name, tmp_path_factory):
+    lib = _bwd_mutant_lib(name, str(tmp_path_factory.getbasetemp()))
+
+    class Orc:
+        @staticmethod
+        def prefill(*a, **k):
+            return oracle.prefill(*a, **k)   # the real forward oracle
+
+        @staticmethod
+        def prefill_backward(*a, **k):
+            return oracle.prefill_backward(*a, lib=lib, **k)
+
+    caught = []
+    for pname, pin in oracle_pins.BWD_PINS.items():
+        try:
+            ok, _ = pin(Orc)
+        except (ValueError, AssertionError, FloatingPointError):
+            ok = False
+        if not ok:
+            caught.append(pname)
+    assert caught, f"mutant {name} passed every backward pin"

@@ -36,3 +36,14 @@ class _S6Orc:
 def test_selective_scan_pin(name):
     ok, detail = oracle_pins.S6_PINS[name](_S6Orc)
     assert ok, f"pin {name} failed: {detail}"
+
+
+class _BwdOrc:
+    prefill = staticmethod(oracle.prefill)
+    prefill_backward = staticmethod(oracle.prefill_backward)
+
+
+@pytest.mark.parametrize("name", sorted(oracle_pins.BWD_PINS))
+def test_backward_pin(name):
+    ok, detail = oracle_pins.BWD_PINS[name](_BwdOrc)
+    assert ok, f"pin {name} failed: {detail}"
