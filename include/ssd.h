@@ -237,6 +237,40 @@ int ssd_selective_scan(const void *x, const void *dt, const float *A, const void
                        int batch, int L, int dim, int N, ssd_dtype_t dtype, void *workspace,
                        size_t workspace_bytes, void *stream);
 
+/*
+ * Gradients of ssd_scan_prefill() -- the backward half of a training step
+ * (Compiler-First State Space Duality and Portable O(1) Autoregressive Caching
+ * for Inference, Table 13: forward plus backward of the chunked scan) -- for a
+ * loss L with dL/dy = dy and dL/dh_out = dh_out.
+ *
+ *   x, dt, A, B, C, D, h0, cu_seqlens, nseq, total_tokens, H, P, N, G, chunk,
+ *   dtype      exactly as passed to ssd_scan_prefill()
+ *   dy       [T][H][P]       dtype    dL/dy
+ *   dh_out   [nseq][H][N][P] float32  dL/dh_out, or NULL for zeros
+ * Outputs (float32; each written in full, none may alias an input or another):
+ *   dx [T][H][P], ddt [T][H], dA [H], dB [T][G][N], dC [T][G][N], dD [H],
+ *   dh0 [nseq][H][N][P] (or NULL to skip)
+ *   workspace / workspace_bytes  device scratch of at least
+ *            ssd_scan_prefill_backward_workspace(...) bytes (256-byte aligned)
+ *
+ * Per chunk, with G_t = dL/dh_t: dx_t = D dy_t + dt_t B_t^T G_t,
+ * dB_t = dt_t G_t x_t (summed over the heads of a group), dC_t = h_t dy_t,
+ * and dL/d(dt_t A) = <G_t, h_t> - dt_t x_t^T G_t^T B_t, from which ddt and dA
+ * follow.  The states are recomputed from the inputs: nothing is kept from the
+ * forward call.  Sums over heads, chunks and sequences run in a fixed order:
+ * the result is deterministic.  Supported shapes as ssd_scan_prefill().
+ * T = 0 gives dA = dD = 0 and dh0 = dh_out (or zeros).
+ */
+size_t ssd_scan_prefill_backward_workspace(int64_t total_tokens, int nseq, int H, int P, int N,
+                                           int G, int chunk, ssd_dtype_t dtype);
+int ssd_scan_prefill_backward(const void *x, const float *dt, const float *A, const void *B,
+                              const void *C, const float *D, const float *h0, const void *dy,
+                              const float *dh_out, float *dx, float *ddt,
+                              float *dA, float *dB, float *dC, float *dD, float *dh0,
+                              const int32_t *cu_seqlens, int nseq, int64_t total_tokens, int H,
+                              int P, int N, int G, int chunk, ssd_dtype_t dtype, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
 /* Message for the last non-zero return on the calling thread ("" if none). */
 const char *ssd_last_error(void);
 

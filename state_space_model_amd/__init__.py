@@ -30,3 +30,8 @@ def decode_layer_step(*args, **kwargs):
 def selective_scan(*args, **kwargs):
     from . import ssd
     return ssd.selective_scan(*args, **kwargs)
+
+
+def prefill_backward(*args, **kwargs):
+    from . import ssd
+    return ssd.prefill_backward(*args, **kwargs)

@@ -232,6 +232,52 @@ int ssd_selective_scan(const void *x, const void *dt, const float *A, const void
   return SSD_OK;
 }
 
+size_t ssd_scan_prefill_backward_workspace(int64_t total_tokens, int nseq, int H, int P, int N,
+                                           int G, int chunk, ssd_dtype_t dtype) {
+  if (dtype != SSD_F32 && dtype != SSD_BF16) return 0;
+  if (nseq < 1 || total_tokens < 0 || total_tokens > INT32_MAX || H < 1 || G < 1 || H % G != 0)
+    return 0;
+  if (!pow2_in(P, 16, 128) || !pow2_in(N, 16, 128) || !pow2_in(chunk, 32, 512)) return 0;
+  return ssd::bwd_layout(total_tokens, nseq, H, P, N, G, chunk, dtype == SSD_BF16 ? 2 : 4).total;
+}
+
+int ssd_scan_prefill_backward(const void *x, const float *dt, const float *A, const void *B,
+                              const void *C, const float *D, const float *h0, const void *dy,
+                              const float *dh_out, float *dx, float *ddt,
+                              float *dA, float *dB, float *dC, float *dD, float *dh0,
+                              const int32_t *cu_seqlens, int nseq, int64_t total_tokens, int H,
+                              int P, int N, int G, int chunk, ssd_dtype_t dtype, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+  g_err[0] = 0;
+  int rc = check_prefill(x, dt, A, B, C, D, dx, nseq, total_tokens, H, P, N, G, chunk, dtype,
+                         cu_seqlens);
+  if (rc) return rc;
+  if (total_tokens > 0 && (!dy || !ddt || !dB || !dC))
+    return fail(SSD_ERR_INVALID_ARG, "null dy/ddt/dB/dC pointer");
+  if (!dA || !dD) return fail(SSD_ERR_INVALID_ARG, "null dA/dD pointer");
+  const ssd::BwdLayout L = ssd::bwd_layout(total_tokens, nseq, H, P, N, G, chunk,
+                                           dtype == SSD_BF16 ? 2 : 4);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(SSD_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, L.total);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(SSD_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  ssd::BwdArgs a{};
+  a.f = ssd::PrefillArgs{x, dt, A, B, C, D, h0, nullptr, nullptr, cu_seqlens, nseq,
+                         total_tokens, H, P, N, G, chunk, dtype == SSD_BF16, workspace, stream};
+  a.dy = dy;
+  a.dh_out = dh_out;
+  a.dx = dx;
+  a.ddt = ddt;
+  a.dA = dA;
+  a.dB = dB;
+  a.dC = dC;
+  a.dD = dD;
+  a.dh0 = dh0;
+  hipError_t e = ssd::launch_prefill_backward(a);
+  if (e != hipSuccess) return fail(SSD_ERR_HIP, "HIP error: %s", hipGetErrorString(e));
+  return SSD_OK;
+}
+
 const char *ssd_last_error(void) { return g_err; }
 
 }  // extern "C"

@@ -13,6 +13,10 @@
 // Also written for the later stages: s, dt and u_j = 2^(s_r - s_j) dt_j (r the
 // last row of j's 32-row block), each [chunk][head][Q].
 //
+// The gradient pass runs the same kernel with BWD set, on C and dy in place of
+// B and x: Sb_c = sum_t 2^(s_t) C_t dy_t^T, the gradient that the chunk's own
+// outputs send to the state entering it (y_t holds 2^(s_t) C_t . H_in).
+//
 // One workgroup per (chunk, head), or per (chunk, head, half of the n
 // columns) when there are few chunks and heads.  Every load of a phase (x
 // rows, B rows, and the strided dt column) goes straight to LDS in one batch:
@@ -61,13 +65,14 @@ __device__ __forceinline__ void scale_rows(T *tile, const float *w, int r0, int 
 
 // The chunk's cumulative decay from its dt column (dt_l, staged in LDS; rows
 // past the chunk length hold 0): s_l = log2(e) A cumsum(dt) -- R consecutive
-// rows per thread, then a block scan -- and w_l[j] = 2^(s_end - s_j) dt_j.
+// rows per thread, then a block scan -- and w_l[j] = 2^(s_end - s_j) dt_j
+// (with `bwd`: w_l[j] = 2^(s_j).
 // With `emit`, s, dt and u_j = 2^(s_r - s_j) dt_j (r the last row of j's
 // 32-row block) are written at out_off of s_out / dt_out / u_out.  Contains
 // block barriers: every thread of the block calls it.  Returns s_end.
 template <int THREADS>
 __device__ __forceinline__ float decay_scan(const float *dt_l, float *s_l, float *w_l,
-                                            float *part, int Q, float a2, bool emit,
+                                            float *part, int Q, float a2, bool emit, bool bwd,
                                             size_t out_off, float *__restrict__ s_out,
                                             float *__restrict__ dt_out,
                                             float *__restrict__ u_out) {
@@ -95,7 +100,8 @@ __device__ __forceinline__ float decay_scan(const float *dt_l, float *s_l, float
   const float s_end = s_l[Q - 1];
   for (int j = tid; j < Q; j += THREADS) {
     const float sj = s_l[j], dj = dt_l[j];
-    w_l[j] = __builtin_amdgcn_exp2f(fminf(s_end - sj, 0.f)) * dj;
+    w_l[j] = bwd ? __builtin_amdgcn_exp2f(fminf(sj, 0.f))
+                 : __builtin_amdgcn_exp2f(fminf(s_end - sj, 0.f)) * dj;
     if (emit) {
       s_out[out_off + j] = sj;
       dt_out[out_off + j] = dj;
@@ -118,7 +124,7 @@ __device__ __forceinline__ void dma_dt(float *dt_l, const float *__restrict__ dt
   }
 }
 
-template <typename T, int P, int N, int NH>
+template <typename T, int P, int N, int NH, bool BWD>
 __global__ __launch_bounds__((StateCfg<T, P, N, NH>::THREADS)) void k_chunk_state(
     const T *__restrict__ x, const float *__restrict__ dt, const float *__restrict__ A,
     const T *__restrict__ B, ChunkMap cmap, int nc, int H, int G, int Q, int JP, int do_state,
@@ -157,7 +163,7 @@ __global__ __launch_bounds__((StateCfg<T, P, N, NH>::THREADS)) void k_chunk_stat
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  decay_scan<K::THREADS>(dt_l, s_l, w_l, part, Q, A[hd] * kLog2e, half == 0,
+  decay_scan<K::THREADS>(dt_l, s_l, w_l, part, Q, A[hd] * kLog2e, half == 0 && !BWD, BWD,
                          ((size_t)c * H + hd) * Q, s_out, dt_out, u_out);
   if (!do_state) return;
   __syncthreads();
@@ -203,12 +209,13 @@ __global__ __launch_bounds__((StateCfg<T, P, N, NH>::THREADS)) void k_chunk_stat
 
 template <typename T, int P, int N, int NH>
 static hipError_t run_state(const PrefillArgs &a, const WorkspaceLayout &L, int nc, int jp_cap,
-                            bool state, hipStream_t st) {
+                            bool state, bool bwd, hipStream_t st) {
   typedef StateCfg<T, P, N, NH> K;
   const int jp = K::jp(a.Q, jp_cap);
   const size_t lds = K::lds_bytes(jp, a.Q);
   if (lds > 160 * 1024) return hipErrorInvalidConfiguration;
-  const void *kern = (const void *)k_chunk_state<T, P, N, NH>;
+  const void *kern = bwd ? (const void *)k_chunk_state<T, P, N, NH, true>
+                        : (const void *)k_chunk_state<T, P, N, NH, false>;
   hipError_t e = set_lds_limit(kern);
   if (e != hipSuccess) return e;
   char *ws = static_cast<char *>(a.workspace);
@@ -229,41 +236,42 @@ static hipError_t run_state(const PrefillArgs &a, const WorkspaceLayout &L, int 
 // workgroups share a CU, so some are always loading while others compute.
 template <typename T, int P, int N>
 static hipError_t run_state_auto(const PrefillArgs &a, const WorkspaceLayout &L, int nc,
-                                 bool state, hipStream_t st) {
+                                 bool state, bool bwd, hipStream_t st) {
   const bool few = (long)nc * a.H < 2048;
   if constexpr (N >= 64) {
-    if (few) return run_state<T, P, N, 2>(a, L, nc, 128, state, st);
+    if (few) return run_state<T, P, N, 2>(a, L, nc, 128, state, bwd, st);
   }
-  return run_state<T, P, N, 1>(a, L, nc, few ? 128 : 64, state, st);
+  return run_state<T, P, N, 1>(a, L, nc, few ? 128 : 64, state, bwd, st);
 }
 
 template <typename T, int P>
-static hipError_t state_N(const PrefillArgs &a, const WorkspaceLayout &L, int nc, bool s,
+static hipError_t state_N(const PrefillArgs &a, const WorkspaceLayout &L, int nc, bool s, bool b,
                           hipStream_t st) {
   switch (a.N) {
-    case 16: return run_state_auto<T, P, 16>(a, L, nc, s, st);
-    case 32: return run_state_auto<T, P, 32>(a, L, nc, s, st);
-    case 64: return run_state_auto<T, P, 64>(a, L, nc, s, st);
-    case 128: return run_state_auto<T, P, 128>(a, L, nc, s, st);
+    case 16: return run_state_auto<T, P, 16>(a, L, nc, s, b, st);
+    case 32: return run_state_auto<T, P, 32>(a, L, nc, s, b, st);
+    case 64: return run_state_auto<T, P, 64>(a, L, nc, s, b, st);
+    case 128: return run_state_auto<T, P, 128>(a, L, nc, s, b, st);
   }
   return hipErrorInvalidValue;
 }
 
 template <typename T>
-static hipError_t state_P(const PrefillArgs &a, const WorkspaceLayout &L, int nc, bool s,
+static hipError_t state_P(const PrefillArgs &a, const WorkspaceLayout &L, int nc, bool s, bool b,
                           hipStream_t st) {
   switch (a.P) {
-    case 16: return state_N<T, 16>(a, L, nc, s, st);
-    case 32: return state_N<T, 32>(a, L, nc, s, st);
-    case 64: return state_N<T, 64>(a, L, nc, s, st);
-    case 128: return state_N<T, 128>(a, L, nc, s, st);
+    case 16: return state_N<T, 16>(a, L, nc, s, b, st);
+    case 32: return state_N<T, 32>(a, L, nc, s, b, st);
+    case 64: return state_N<T, 64>(a, L, nc, s, b, st);
+    case 128: return state_N<T, 128>(a, L, nc, s, b, st);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_chunk_state(const PrefillArgs &a, const WorkspaceLayout &L, int nc, bool state,
-                              hipStream_t st) {
-  return a.bf16 ? state_P<bf16>(a, L, nc, state, st) : state_P<float>(a, L, nc, state, st);
+                              hipStream_t st, bool bwd) {
+  return a.bf16 ? state_P<bf16>(a, L, nc, state, bwd, st)
+                : state_P<float>(a, L, nc, state, bwd, st);
 }
 
 }  // namespace ssd

@@ -19,6 +19,7 @@ struct PrefillArgs {
   bool bf16;
   void *workspace;
   void *stream;
+  float *hin32 = nullptr;  // optional float32 copy of the state entering each chunk
 };
 
 // Byte offsets of the prefill workspace regions (each 256-byte aligned).
@@ -39,9 +40,10 @@ WorkspaceLayout prefill_layout(int64_t T, int nseq, int H, int P, int N, int Q, 
 hipError_t launch_prefill(const PrefillArgs &a, unsigned stages);
 
 // Stages 1-2: chunk-local cumulative decay (s, dt, u) and, if `state`, the
-// chunk states S.
+// chunk states S.  With `bwd` (a.x = dy, a.B = C): only the gradient chunk
+// states Sb_c = sum_t 2^(s_t) C_t dy_t^T, written over S.
 hipError_t launch_chunk_state(const PrefillArgs &a, const WorkspaceLayout &L, int nc, bool state,
-                              hipStream_t st);
+                              hipStream_t st, bool bwd = false);
 
 // Chunk scan with the heads of a B/C group streamed through one workgroup
 // (bfloat16, selected P/N/Q).  scan_heads_choice() returns the heads per
@@ -51,6 +53,28 @@ hipError_t launch_chunk_state(const PrefillArgs &a, const WorkspaceLayout &L, in
 int scan_heads_choice(int P, int N, int Q, bool bf16, int nc, int H, int G);
 hipError_t launch_scan_heads(const PrefillArgs &a, const WorkspaceLayout &L, int nc, int HB,
                              hipStream_t st);
+
+// Gradients of the prefill (ssd_backward.hip).
+struct BwdArgs {
+  PrefillArgs f;        // the forward's inputs (f.y and f.h_out unused)
+  const void *dy;       // dL/dy, operand type
+  const float *dh_out;  // dL/dh_out or null
+  float *dx, *ddt, *dA, *dB, *dC, *dD, *dh0;  // dh0 may be null
+};
+// The forward's workspace followed by the gradient pass's regions.
+struct BwdLayout {
+  WorkspaceLayout fwd;
+  size_t hfin;    // f32 [nseq][H][N][P]  final states (the forward recompute)
+  size_t hin32;   // f32 [nc][H][N][P]    state entering each chunk, float32
+  size_t dHc;     // T   [nc][H][N][P]    dL/d(state leaving chunk c)
+  size_t epart;   // f32 [nc][H][NP/256]  wave partials of <dH_c, H_c>
+  size_t rows;             // f32 6 x [nc][H][Q]  per-row terms of dz (q, cv, r, dyx, rs x 2)
+  size_t dApart, dDpart;   // f32 [nc][H]
+  size_t dBh, dCh;         // f32 [T][H][N]  per-head dB, dC (only when H > G)
+  size_t total;
+};
+BwdLayout bwd_layout(int64_t T, int nseq, int H, int P, int N, int G, int Q, int elem);
+hipError_t launch_prefill_backward(const BwdArgs &a);
 
 struct StepArgs {
   const void *x;

@@ -122,15 +122,16 @@ __global__ __launch_bounds__(256) void k_chunk_map(const int32_t *__restrict__ c
 
 // ----------------------------------------------------------- K3 state pass
 // Per (sequence, head), per 4 state elements: walk the sequence's chunks in
-// order, emit the state entering each chunk (as the MFMA operand type) and
-// the final state.
+// order, emit the state entering each chunk (as the MFMA operand type, and
+// optionally as float32) and the final state.
 
 template <typename T>
 __global__ __launch_bounds__(256) void k_state_pass(const float *__restrict__ S,
                                                     const float *__restrict__ s_ws,
                                                     const int *__restrict__ seq_off,
                                                     ChunkMap cmap, const float *h0, float *h_out,
-                                                    T *__restrict__ hin, int H, int NP, int Q) {
+                                                    T *__restrict__ hin, int H, int NP, int Q,
+                                                    float *__restrict__ hin32) {
   constexpr int BATCH = 8;  // chunk states in flight per thread
   const int s = blockIdx.z, hd = blockIdx.y;
   const int e = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
@@ -161,6 +162,7 @@ __global__ __launch_bounds__(256) void k_state_pass(const float *__restrict__ S,
     for (int u = 0; u < BATCH; ++u) {
       if (cb + u < c1) {
         st4T(hin + ((size_t)(cb + u) * H + hd) * NP + e, st);
+        if (hin32) st4(hin32 + ((size_t)(cb + u) * H + hd) * NP + e, st);
         const float a = __builtin_amdgcn_exp2f(fminf(sl[u], 0.f));
 #pragma unroll
         for (int q = 0; q < 4; ++q) st[q] = a * st[q] + Sb[u][q];
@@ -408,9 +410,12 @@ static hipError_t run_prefill(const PrefillArgs &a, unsigned stages) {
   const ChunkMap cmap{info, L_dense, a.nseq, a.Q};
   hipStream_t st = static_cast<hipStream_t>(a.stream);
 
-  if ((stages & 3u) && a.cu && nc > 0) {  // packed batch: chunk map first
-    hipLaunchKernelGGL(k_chunk_map, dim3(nc), dim3(256), 0, st, a.cu, a.nseq, a.T, a.Q, nc, info,
-                       seq_off);
+  if ((stages & 3u) && (a.cu || L_dense == 0)) {
+    // packed (or empty) batch: chunk map first.  Block 0 also writes the first
+    // chunk of every sequence, which the state pass reads even when there are
+    // no chunks at all (then every entry is 0).
+    hipLaunchKernelGGL(k_chunk_map, dim3(nc > 0 ? nc : 1), dim3(256), 0, st, a.cu, a.nseq, a.T,
+                       a.Q, nc, info, seq_off);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -421,7 +426,7 @@ static hipError_t run_prefill(const PrefillArgs &a, unsigned stages) {
   if (stages & 4u) {
     const int NP = N * P;
     hipLaunchKernelGGL(k_state_pass<T>, dim3((NP + 1023) / 1024, a.H, a.nseq), dim3(256), 0, st,
-                       S, s_ws, seq_off, cmap, a.h0, a.h_out, hin, a.H, NP, a.Q);
+                       S, s_ws, seq_off, cmap, a.h0, a.h_out, hin, a.H, NP, a.Q, a.hin32);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

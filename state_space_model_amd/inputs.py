@@ -161,3 +161,15 @@ def selective_scan_inputs(batch, L, dim, N, seed, dtype="f16", h0=False):
     h = rng.normal(0.0, 0.1, size=(batch, dim, N)).astype(np.float32) if h0 else None
     rnd = {"f32": lambda v: v, "bf16": round_bf16, "f16": round_f16}[dtype]
     return dict(x=rnd(x), dt=rnd(dt), A=A, B=rnd(B), C=rnd(C), D=D, h0=h)
+
+
+def cotangents(T, nseq, H, P, N, seed, dtype="bf16", dh_out=True):
+    """Seeded upstream gradients for the prefill's backward: dy [T,H,P] ~ N(0,1)
+    (rounded to bfloat16 values for dtype "bf16", the type it is passed in) and
+    dh_out [nseq,H,N,P] ~ N(0, 0.1^2) float32, or None."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    dy = rng.standard_normal((T, H, P)).astype(np.float32)
+    if dtype == "bf16":
+        dy = round_bf16(dy)
+    dh = rng.normal(0.0, 0.1, (nseq, H, N, P)).astype(np.float32) if dh_out else None
+    return dy, dh

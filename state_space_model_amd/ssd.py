@@ -21,7 +21,7 @@ ERRORS = {0: "SSD_OK", -1: "SSD_ERR_INVALID_ARG", -2: "SSD_ERR_UNSUPPORTED",
 EXPORTS = ("ssd_scan_prefill_workspace", "ssd_scan_prefill", "ssd_scan_prefill_stages",
            "ssd_step", "ssd_step_multi", "ssd_conv1d_step", "ssd_gated_rmsnorm",
            "ssd_decode_layer_step", "ssd_selective_scan_workspace", "ssd_selective_scan",
-           "ssd_last_error")
+           "ssd_scan_prefill_backward_workspace", "ssd_scan_prefill_backward", "ssd_last_error")
 
 _lib = None
 
@@ -68,6 +68,11 @@ def load(path=LIB_PATH):
     lib.ssd_selective_scan.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                        vp, sz, vp]
     lib.ssd_selective_scan.restype = i32
+    lib.ssd_scan_prefill_backward_workspace.argtypes = [i64, i32, i32, i32, i32, i32, i32, i32]
+    lib.ssd_scan_prefill_backward_workspace.restype = sz
+    lib.ssd_scan_prefill_backward.argtypes = [vp] * 17 + [i32, i64, i32, i32, i32, i32, i32, i32,
+                                                          vp, sz, vp]
+    lib.ssd_scan_prefill_backward.restype = i32
     lib.ssd_last_error.argtypes = []
     lib.ssd_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -205,6 +210,64 @@ class Prepared:
             rc = self._fn(self._stages if stages is None else stages, *self._args, s)
         if rc != 0:
             _check(rc)
+
+
+def prefill_backward(x, dt, A, B, C, D, dy, h0=None, dh_out=None, chunk=256, cu_seqlens=None,
+                     *, nseq=None, workspace=None, prepare=False):
+    """Gradients of ``prefill`` for dL/dy = dy and dL/dh_out = dh_out.
+
+    x, dt, A, B, C, D, h0, cu_seqlens, nseq, chunk as given to ``prefill``
+    (packed [T,...] layout); dy [T,H,P] in x's dtype; dh_out [nseq,H,N,P]
+    float32 or None.  Returns a dict of float32
+    tensors dx [T,H,P], ddt [T,H], dA [H], dB/dC [T,G,N], dD [H],
+    dh0 [nseq,H,N,P]; with ``prepare=True`` nothing runs and
+    (Prepared, grads) is returned.
+    """
+    T, H, P = x.shape
+    G, N = B.shape[-2], B.shape[-1]
+    dev = x.device
+    _need(x, "x", dev=dev)
+    code = _dtype_code(x)
+    for t, n in ((B, "B"), (C, "C"), (dy, "dy")):
+        _need(t, n, x.dtype, dev)
+    for t, n in ((dt, "dt"), (A, "A"), (D, "D")):
+        _need(t, n, torch.float32, dev)
+    if tuple(dt.shape) != (T, H) or tuple(A.shape) != (H,) or tuple(D.shape) != (H,):
+        raise ValueError("dt must be [T,H], A and D [H]")
+    if tuple(B.shape) != (T, G, N) or tuple(C.shape) != (T, G, N):
+        raise ValueError("B and C must be [T,G,N]")
+    if tuple(dy.shape) != (T, H, P):
+        raise ValueError("dy must be [T,H,P]")
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+        nseq = cu_seqlens.numel() - 1
+    elif nseq is None:
+        nseq = 1
+    for t, n in ((h0, "h0"), (dh_out, "dh_out")):
+        if t is not None:
+            _need(t, n, torch.float32, dev)
+            if tuple(t.shape) != (nseq, H, N, P):
+                raise ValueError(f"{n} must be [{nseq},{H},{N},{P}]")
+    lib = load()
+    if workspace is None:
+        n = int(lib.ssd_scan_prefill_backward_workspace(T, nseq, H, P, N, G, chunk, code))
+        if n == 0:
+            raise SSDError(-2, "unsupported prefill shape")
+        workspace = torch.empty(n, dtype=torch.uint8, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = dict(dx=torch.empty((T, H, P), **f32), ddt=torch.empty((T, H), **f32),
+             dA=torch.empty(H, **f32), dB=torch.empty((T, G, N), **f32),
+             dC=torch.empty((T, G, N), **f32), dD=torch.empty(H, **f32),
+             dh0=torch.empty((nseq, H, N, P), **f32))
+    args = (_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(dy),
+            _ptr(dh_out), _ptr(g["dx"]), _ptr(g["ddt"]), _ptr(g["dA"]), _ptr(g["dB"]),
+            _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dh0"]), _ptr(cu_seqlens), nseq, T, H, P, N, G,
+            chunk, code, _ptr(workspace), workspace.numel())
+    if prepare:
+        keep = (x, dt, A, B, C, D, h0, dy, dh_out, cu_seqlens, workspace, g)
+        return Prepared(lib.ssd_scan_prefill_backward, args, None, keep), g
+    _check(lib.ssd_scan_prefill_backward(*args, _stream()))
+    return g
 
 
 def step(x, dt, A, B, C, D, h, y=None, prepare=False):

@@ -144,6 +144,56 @@ def test_selective_scan_rejects_before_launch(kw, code, frag):
     assert rc == code and frag in lib.ssd_last_error().decode()
 
 
+def test_backward_workspace_size():
+    lib = ssd.load()
+    w = lib.ssd_scan_prefill_backward_workspace
+    fwd = lib.ssd_scan_prefill_workspace(4096, 1, 24, 64, 128, 256, 1)
+    n1 = w(4096, 1, 24, 64, 128, 1, 256, 1)
+    nc = 16
+    # the forward's workspace, then: final states (f32), states entering each chunk
+    # (f32), dH per chunk (bf16), the <dH, H> partials, six per-row arrays,
+    # dA/dD partials, per-head dB and dC
+    extra = (24 * 128 * 64 * 4 + nc * 24 * 128 * 64 * (4 + 2) + nc * 24 * 32 * 4
+             + 6 * nc * 24 * 256 * 4 + 2 * nc * 24 * 4 + 2 * 4096 * 24 * 128 * 4)
+    assert fwd + extra <= n1 <= fwd + extra + 16 * 256
+    assert w(4096, 1, 24, 64, 128, 24, 256, 1) < n1       # H == G: no per-head dB/dC
+    assert w(4096, 1, 24, 64, 128, 5, 256, 1) == 0        # H % G != 0
+    assert w(4096, 1, 24, 64, 100, 1, 256, 1) == 0        # unsupported N
+    assert w(0, 1, 24, 64, 128, 1, 256, 1) > 0
+
+
+def _backward_rc(**kw):
+    lib = ssd.load()
+    a = dict(x=1, dy=1, ddt=1, dA=1, dB=1, dC=1, dD=1, nseq=1, T=64, H=4, P=16, N=16, G=1,
+             chunk=64, dtype=0, ws=None, wsb=0)
+    a.update(kw)
+    p = lambda v: None if v is None else ctypes.c_void_p(v)
+    one = p(1)
+    rc = lib.ssd_scan_prefill_backward(p(a["x"]), one, one, one, one, one, None,
+                                       p(a["dy"]), None, one, p(a["ddt"]), p(a["dA"]), p(a["dB"]),
+                                       p(a["dC"]), p(a["dD"]), None, None, a["nseq"], a["T"],
+                                       a["H"], a["P"], a["N"], a["G"], a["chunk"], a["dtype"],
+                                       p(a["ws"]), a["wsb"], None)
+    return rc, lib.ssd_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(H=6, G=4), -1, "H % G"),
+    (dict(P=24), -2, "headdim"),
+    (dict(N=100), -2, "d_state"),
+    (dict(chunk=48), -2, "chunk"),
+    (dict(x=None), -1, "null"),
+    (dict(dy=None), -1, "null"),
+    (dict(dA=None), -1, "null"),
+    (dict(dtype=2), -1, "dtype"),
+    (dict(ws=None, wsb=0), -3, "workspace"),
+    (dict(ws=256, wsb=16), -3, "workspace"),
+])
+def test_backward_rejects_before_launch(kw, code, frag):
+    rc, msg = _backward_rc(**kw)
+    assert rc == code and frag in msg, (rc, msg)
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros(64, 4, 16)
