@@ -50,6 +50,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-large", action="store_true",
                     help="skip the Mamba-2 2.7B layer prefill measurement")
+    ap.add_argument("--no-train", action="store_true",
+                    help="skip the training-step (forward + backward) measurement")
+    ap.add_argument("--train-only", action="store_true",
+                    help="only run --steps forward + backward passes of the 130M layer (for "
+                         "profiling) and print their timing")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--copy-calibration", type=int, metavar="MIB", default=0,
                     help="only run a plain device-to-device copy of MIB MiB ten times "
@@ -198,15 +203,27 @@ def _read_csv(path):
         return list(csv.DictReader(f))
 
 
-KERNEL_NAMES = {  # kernel symbol fragment -> bench kernel name
-    "k_chunk_state": "chunk_state",
-    "k_state_pass": "state_pass", "k_chunk_scan": "chunk_scan", "k_step": "decode_step",
+KERNEL_NAMES = {  # kernel symbol fragment -> bench kernel name (first match wins)
+    "k_step_multi": "decode_multi_step", "k_conv1d_step": "conv1d_step",
+    "k_gated_rmsnorm": "gated_rmsnorm", "k_s6_summary": "s6_summary", "k_s6_pass": "s6_pass",
+    "k_s6_replay": "s6_replay", "k_bwd_scan": "bwd_scan", "k_state_pass_bwd": "state_pass_bwd",
+    "k_bwd_ddt": "bwd_ddt", "k_bwd_group_sum": "bwd_group_sum", "k_bwd_head_sum": "bwd_head_sum",
+    "k_chunk_state": "chunk_state", "k_state_pass": "state_pass", "k_chunk_scan": "chunk_scan",
+    "k_chunk_map": "chunk_map", "k_step": "decode_step",
 }
+BWD_SCAN_MODES = {"0": "bwd_scan_dx", "1": "bwd_scan_db", "2": "bwd_scan_dc"}
 
 
-def _kernel_key(name, grid):
+def _kernel_key(name, grid, train=False):
     for frag, k in KERNEL_NAMES.items():
         if frag in name:
+            if k == "bwd_scan":  # template mode: k_bwd_scan<T, MODE, ...>
+                mode = name.split(frag, 1)[1].split(",")[1].strip() if "<" in name else ""
+                k = BWD_SCAN_MODES.get(mode, k)
+            if k == "chunk_state" and "true>" in name:
+                k = "chunk_state_bwd"
+            if train or k.startswith("bwd") or k.endswith("_bwd"):
+                return "mamba2-130m-layer-train", k
             if k == "decode_step":  # the two decode workloads differ in grid size
                 return ("codestral-7b-decode-step" if int(grid) > 24 * 256 else
                         "mamba2-130m-layer-prefill"), k
@@ -220,13 +237,15 @@ def _kernel_key(name, grid):
 
 PROFILE_COMMANDS = {
     "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d DIR/trace -o run -- "
-             "python bench.py --no-cpu-baseline --no-large --steps 50 --warmup 5 --quiet",
+             "python bench.py --no-cpu-baseline --no-large --no-train --steps 50 --warmup 5 --quiet",
     "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/fetch -o run -- "
-             "python bench.py --no-cpu-baseline --no-large --steps 50 --warmup 5 --quiet",
+             "python bench.py --no-cpu-baseline --no-large --no-train --steps 50 --warmup 5 --quiet",
     "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/write -o run -- "
-             "python bench.py --no-cpu-baseline --no-large --steps 50 --warmup 5 --quiet",
+             "python bench.py --no-cpu-baseline --no-large --no-train --steps 50 --warmup 5 --quiet",
     "mfma": "rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 --output-format csv -d DIR/mfma -o run -- "
-            "python bench.py --no-cpu-baseline --no-large --steps 50 --warmup 5 --quiet",
+            "python bench.py --no-cpu-baseline --no-large --no-train --steps 50 --warmup 5 --quiet",
+    "ttrace": "rocprofv3 --kernel-trace --stats --output-format csv -d DIR/ttrace -o run -- "
+              "python bench.py --train-only --steps 50 --warmup 5 --quiet",
     "cfetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/cfetch -o run -- "
               "python bench.py --copy-calibration 1024",
     "cwrite": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/cwrite -o run -- "
@@ -317,6 +336,21 @@ def summarize(directory):
                 "command (cwd = repository root):", "  " + PROFILE_COMMANDS["mfma"], ""]
         with open(os.path.join(ROOT, "profiles", "mfma_util_prefill130m.txt"), "w") as f:
             f.write("\n".join(head + ml) + "\n")
+    tstats = glob.glob(os.path.join(directory, "ttrace", "**", "*kernel_stats.csv"),
+                       recursive=True)
+    if tstats:
+        tl = []
+        for r in _read_csv(tstats[0]):
+            tl.append(f"{r['Name'][:96]:96s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f}"
+                      f" {float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f}"
+                      f" {float(r['Percentage']):6.2f}")
+        with open(os.path.join(ROOT, "profiles", "kernel_trace_train130m.txt"), "w") as f:
+            f.write("rocprofv3 kernel trace of forward + backward of the Mamba-2 130M layer scan\n"
+                    "(4096 tokens, 24 heads, P 64, N 128, chunk 256, bf16, h0 = 0, dL/dh_out = 0)\n"
+                    f"kernel sources hash {traffic['source_hash']}\n"
+                    f"command (cwd = repository root):\n  {PROFILE_COMMANDS['ttrace']}\n\n"
+                    f"{'kernel':96s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}"
+                    f" {'%':>6s}\n" + "\n".join(tl) + "\n")
     stats = glob.glob(os.path.join(directory, "trace", "**", "*kernel_stats.csv"), recursive=True)
     if stats:
         rows = _read_csv(stats[0])
@@ -371,6 +405,82 @@ def prefill_large(args, torch, inputs, ssd, dev):
             "algorithmic_flops": flops,
             "mfma_frac": round(flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4),
             "kernels_us": kern}
+
+
+def train_work(w, T, nseq):
+    """Algorithmic bytes and flops of the backward over the chunked form, for a
+    training step (h0 = 0, no dL/dh_out).  Bytes: x, dy, B, C, dt read once;
+    dx, ddt, dB, dC written once (float32), dh0 written.  Flops (full tiles, as
+    the forward): per group C.B^T (2QN); per head dy.x^T (2QP), the three
+    masked products of dX, dB, dC (2QP + 2QN + 2QN), and five state products
+    (recomputed chunk state, gradient chunk state and the state terms of dX,
+    dB, dC; 2NP each)."""
+    H, P, N, G, Q = w.H, w.P, w.N, w.G, w.chunk
+    e = 2 if w.dtype == "bf16" else 4
+    nbytes = T * (H * P * (2 * e + 4) + G * N * (2 * e + 8) + H * 8) + nseq * H * N * P * 4
+    flops = T * (G * 2 * Q * N + H * (4 * Q * P + 4 * Q * N + 10 * N * P))
+    return dict(bytes=nbytes, flops=flops)
+
+
+def training_setup(torch, inputs, ssd, dev):
+    """Prepared forward and backward calls over the Mamba-2 130M layer workload
+    (bf16, h0 = 0), with a seeded dL/dy and no dL/dh_out."""
+    wl = inputs.WORKLOADS[1]
+    d = inputs.workload_inputs(1)
+    T = d["x"].shape[0]
+    nseq = len(d["cu_seqlens"]) - 1
+    op = torch.bfloat16
+    t = lambda a, dt=None: torch.from_numpy(np.ascontiguousarray(a)).to(dev) if dt is None \
+        else torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(dt)
+    dy, _ = inputs.cotangents(T, nseq, wl.H, wl.P, wl.N, 4001, "bf16", dh_out=False)
+    args = (t(d["x"], op), t(d["dt"]), t(d["A"]), t(d["B"], op), t(d["C"], op), t(d["D"]))
+    fwd, _, _ = ssd.prefill(*args, None, chunk=wl.chunk, nseq=nseq, prepare=True)
+    bwd, grads = ssd.prefill_backward(*args, t(dy, op), None, None, chunk=wl.chunk, nseq=nseq,
+                                      prepare=True)
+    return wl, T, nseq, fwd, bwd
+
+
+def training_step_bench(args, torch, inputs, ssd, dev):
+    """Forward + backward of the Mamba-2 130M layer's scan (the pair a training
+    step runs), each from HIP-graph replays; the backward against its
+    algorithmic bytes and flops."""
+    wl, T, nseq, fwd, bwd = training_setup(torch, inputs, ssd, dev)
+
+    def both():
+        fwd()
+        bwd()
+
+    both()
+    torch.cuda.synchronize()
+    ms_f = graph_ms(torch, fwd, reps=10, per_graph=10)
+    ms_b = graph_ms(torch, bwd, reps=10, per_graph=10)
+    ms_fb = graph_ms(torch, both, reps=10, per_graph=10)
+    wb = train_work(wl, T, nseq)
+    tf = wb["flops"] / (ms_b * 1e-3) / 1e12
+    gbs = wb["bytes"] / (ms_b * 1e-3) / 1e9
+    log(args, f"130M layer forward + backward: {ms_fb * 1e3:.1f} us (backward {ms_b * 1e3:.1f})")
+    return {"workload": wl.name, "tokens": T, "forward_us": round(ms_f * 1e3, 2),
+            "backward_us": round(ms_b * 1e3, 2), "forward_backward_us": round(ms_fb * 1e3, 2),
+            "tokens_per_s": round(T / (ms_fb * 1e-3), 1),
+            "backward_algorithmic_flops": wb["flops"], "backward_algorithmic_bytes": wb["bytes"],
+            "backward_mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4),
+            "backward_hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def train_only(args):
+    """--train-only: `steps` forward + backward passes (for rocprofv3)."""
+    import torch
+    from state_space_model_amd import inputs, ssd
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    wl, T, nseq, fwd, bwd = training_setup(torch, inputs, ssd, dev)
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    ms = time_loop(torch, lambda: (fwd(), bwd()), args.steps)
+    print(json.dumps({"workload": wl.name, "steps": args.steps,
+                      "forward_backward_us": round(ms * 1e3, 2)}), flush=True)
 
 
 def selective_scan_bench(torch, inputs, ssd, dev):
@@ -438,6 +548,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.train_only:
+        train_only(args)
         return
     import torch
     from state_space_model_amd import inputs, ssd
@@ -574,6 +687,9 @@ def main():
     # ---- Mamba-1 selective scan at the COREY W1 shape (a second scan family)
     s6 = selective_scan_bench(torch, inputs, ssd, dev)
 
+    # ---- forward + backward of the 130M layer scan (a training step's share)
+    train = None if args.no_train else training_step_bench(args, torch, inputs, ssd, dev)
+
     # MFMA utilisation estimate of the prefill (algorithmic flops / bf16 peak)
     fl = sum(work[n]["flops"] for n in ("chunk_state", "chunk_scan"))
     mfma_util = fl / (sum(kern_ms[n] for n in kern_ms if n != "decode_step") * 1e-3) / \
@@ -599,6 +715,7 @@ def main():
         "decode_multi_step": decode_multi,
         "decode_layer_step": layer,
         "selective_scan_w1": s6,
+        "training_step_130m": train,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
