@@ -422,11 +422,11 @@ def train_work(w, T, nseq):
     return dict(bytes=nbytes, flops=flops)
 
 
-def training_setup(torch, inputs, ssd, dev):
-    """Prepared forward and backward calls over the Mamba-2 130M layer workload
-    (bf16, h0 = 0), with a seeded dL/dy and no dL/dh_out."""
-    wl = inputs.WORKLOADS[1]
-    d = inputs.workload_inputs(1)
+def training_setup(torch, inputs, ssd, dev, k=1):
+    """Prepared forward and backward calls over prefill workload k (bf16; the
+    130M layer by default, h0 = 0), with a seeded dL/dy and no dL/dh_out."""
+    wl = inputs.WORKLOADS[k]
+    d = inputs.workload_inputs(k)
     T = d["x"].shape[0]
     nseq = len(d["cu_seqlens"]) - 1
     op = torch.bfloat16
@@ -434,17 +434,18 @@ def training_setup(torch, inputs, ssd, dev):
         else torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(dt)
     dy, _ = inputs.cotangents(T, nseq, wl.H, wl.P, wl.N, 4001, "bf16", dh_out=False)
     args = (t(d["x"], op), t(d["dt"]), t(d["A"]), t(d["B"], op), t(d["C"], op), t(d["D"]))
-    fwd, _, _ = ssd.prefill(*args, None, chunk=wl.chunk, nseq=nseq, prepare=True)
-    bwd, grads = ssd.prefill_backward(*args, t(dy, op), None, None, chunk=wl.chunk, nseq=nseq,
+    h0 = None if d["h0"] is None else t(d["h0"])
+    fwd, _, _ = ssd.prefill(*args, h0, chunk=wl.chunk, nseq=nseq, prepare=True)
+    bwd, grads = ssd.prefill_backward(*args, t(dy, op), h0, None, chunk=wl.chunk, nseq=nseq,
                                       prepare=True)
     return wl, T, nseq, fwd, bwd
 
 
-def training_step_bench(args, torch, inputs, ssd, dev):
-    """Forward + backward of the Mamba-2 130M layer's scan (the pair a training
-    step runs), each from HIP-graph replays; the backward against its
+def training_step_bench(args, torch, inputs, ssd, dev, k=1):
+    """Forward + backward of a layer's scan (the pair a training step runs) on
+    prefill workload k, each from HIP-graph replays; the backward against its
     algorithmic bytes and flops."""
-    wl, T, nseq, fwd, bwd = training_setup(torch, inputs, ssd, dev)
+    wl, T, nseq, fwd, bwd = training_setup(torch, inputs, ssd, dev, k)
 
     def both():
         fwd()
@@ -458,7 +459,7 @@ def training_step_bench(args, torch, inputs, ssd, dev):
     wb = train_work(wl, T, nseq)
     tf = wb["flops"] / (ms_b * 1e-3) / 1e12
     gbs = wb["bytes"] / (ms_b * 1e-3) / 1e9
-    log(args, f"130M layer forward + backward: {ms_fb * 1e3:.1f} us (backward {ms_b * 1e3:.1f})")
+    log(args, f"{wl.name} forward + backward: {ms_fb * 1e3:.1f} us (backward {ms_b * 1e3:.1f})")
     return {"workload": wl.name, "tokens": T, "forward_us": round(ms_f * 1e3, 2),
             "backward_us": round(ms_b * 1e3, 2), "forward_backward_us": round(ms_fb * 1e3, 2),
             "tokens_per_s": round(T / (ms_fb * 1e-3), 1),
@@ -689,6 +690,8 @@ def main():
 
     # ---- forward + backward of the 130M layer scan (a training step's share)
     train = None if args.no_train else training_step_bench(args, torch, inputs, ssd, dev)
+    train_large = None if (args.no_train or args.no_large) else \
+        training_step_bench(args, torch, inputs, ssd, dev, k=2)
 
     # MFMA utilisation estimate of the prefill (algorithmic flops / bf16 peak)
     fl = sum(work[n]["flops"] for n in ("chunk_state", "chunk_scan"))
@@ -716,6 +719,7 @@ def main():
         "decode_layer_step": layer,
         "selective_scan_w1": s6,
         "training_step_130m": train,
+        "training_step_2p7b": train_large,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -36,8 +36,8 @@
 //   k_bwd_scan<DB>      dB per head                        (reverse-time masked scan)
 //   k_bwd_scan<DC>      dC per head, r                     (forward-time masked scan)
 //   k_bwd_ddt           dz by a suffix scan, ddt, per-chunk dA and dD
-//   k_bwd_group_sum     dB, dC summed over the heads of a group (H > G only)
-//   k_bwd_head_sum      dA, dD summed over the chunks
+//   k_bwd_sums          dA, dD summed over the chunks; dB, dC over the partial
+//                       rows of a group (only when heads are not all summed on chip)
 // The three masked scans are one kernel: a wave owns 16 output rows i and
 // sweeps 32-row source blocks j (j >= i reverse, j <= i forward):
 //   M^T[j][i] = (K_j . Q_i) 2^(|s_i - s_j|) w_j, masked      k = KD  (MFMA)
@@ -46,6 +46,8 @@
 // with (Q, K, V, state) = (B, C, dy, dH_c) for DX, (x, dy, C, dH_c) for DB and
 // (dy, x, B, H_in) for DC.  Sums over heads and chunks are fixed-order: every
 // result is deterministic.
+#include <stdlib.h>
+
 #include "ssd_launch.h"
 #include "ssd_prefill_util.h"
 
@@ -91,16 +93,20 @@ template <typename T, int MODE, int KD, int VD> struct BwdScanCfg {
   }
 };
 
-// One workgroup per (chunk, head, part of SPLIT); one wave per 16-row output
-// tile, tiles dealt to the parts and waves as in the forward chunk scan so that
-// the waves of a SIMD carry equal work.  MAXT bounds the workgroup (512 up to
-// Q = 256, which leaves 256 VGPRs a lane; 1024 for Q = 512).
-template <typename T, int MODE, int P, int N, int SPLIT, int MAXT>
+// One workgroup per (chunk, block of hb heads of one group, part of SPLIT);
+// one wave per 16-row output tile, tiles dealt to the parts and waves as in
+// the forward chunk scan so that the waves of a SIMD carry equal work.  DB and
+// DC sum the hb heads in their accumulators (DB takes dt_i into its own-row
+// operand, so no per-head factor is left), which leaves H / hb partial rows
+// per token for the group sum instead of H; DX has hb = 1.  MAXT bounds the
+// workgroup (512 up to Q = 256, which leaves 256 VGPRs a lane; 1024 for
+// Q = 512).
+template <typename T, int MODE, int P, int N, int SPLIT, int MAXT, bool MULTI>
 __global__ __launch_bounds__(MAXT) void k_bwd_scan(
     const T *__restrict__ x, const T *__restrict__ dy, const T *__restrict__ B,
     const T *__restrict__ C, const float *__restrict__ D, const float *__restrict__ s_ws,
     const float *__restrict__ dt_ws, const float *__restrict__ u_ws,
-    const T *__restrict__ state, ChunkMap cmap, int nc, int H, int G, int Q, int JP,
+    const T *__restrict__ state, ChunkMap cmap, int nc, int H, int G, int Q, int JP, int hb,
     float *__restrict__ out, int ostride, BwdRows rows) {
   constexpr int KD = MODE == kBwdDX ? N : P;
   constexpr int VD = MODE == kBwdDX ? P : N;
@@ -108,13 +114,14 @@ __global__ __launch_bounds__(MAXT) void k_bwd_scan(
   constexpr bool REV = K::REV;
   constexpr int KS = K::KS, NVT = VD / 16;
   constexpr int KSP = (P < 32 ? 32 : P) / 32;  // k-steps of the dy . x products (DX)
-  const ChunkHead chd = xcd_chunk_head(H * SPLIT);
-  const int c = chd.c, hd = chd.h / SPLIT, part = chd.h % SPLIT;
+  if (!MULTI) hb = 1;
+  const ChunkHead chd = xcd_chunk_head((H / hb) * SPLIT);
+  const int c = chd.c, blk = chd.h / SPLIT, part = chd.h % SPLIT;
   if (c >= nc) return;
   const int4 ci = cmap(c);
   if (ci.z <= 0) return;
   const int len = ci.z;
-  const int g = (hd * G) / H;
+  const int hd0 = blk * hb, g = (hd0 * G) / H;  // the block's heads share group g
   const int nw = blockDim.x >> 6, lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = lane >> 4, col = lane & 15;
@@ -124,6 +131,9 @@ __global__ __launch_bounds__(MAXT) void k_bwd_scan(
     tile = 2 * k + (part ^ (k & 1));
   }
   const int t0 = 16 * tile;
+  const int i = t0 + col;
+  const bool live = t0 < len;  // wave-uniform
+  const int tile_last = min(t0 + 15, len - 1);
 
   extern __shared__ __align__(16) char smem[];
   T *Ss = reinterpret_cast<T *>(smem);                    // state  [SR][SP]
@@ -134,218 +144,230 @@ __global__ __launch_bounds__(MAXT) void k_bwd_scan(
   float *u_l = dt_l + Q;                                                        // [Q]
   float *rs_l = u_l + Q;  // DX: [nw][Q] W row sums, one row per wave
 
-  const size_t csh = (size_t)c * H + hd;
   const size_t hstride = (size_t)H * P, gstride = (size_t)G * N;
-  const T *xh = x + (size_t)ci.y * hstride + (size_t)hd * P;
-  const T *dyh = dy + (size_t)ci.y * hstride + (size_t)hd * P;
   const T *Bg = B + (size_t)ci.y * gstride + (size_t)g * N;
   const T *Cg = C + (size_t)ci.y * gstride + (size_t)g * N;
-  const T *qg = MODE == kBwdDX ? Bg : (MODE == kBwdDB ? xh : dyh);
-  const T *kg = MODE == kBwdDX ? Cg : (MODE == kBwdDB ? dyh : xh);
-  const T *vg = MODE == kBwdDX ? dyh : (MODE == kBwdDB ? Cg : Bg);
-  const size_t qs = MODE == kBwdDX ? gstride : hstride;
-  const size_t ks_ = MODE == kBwdDX ? gstride : hstride;
-  const size_t vs = MODE == kBwdDX ? hstride : gstride;
-
-  // ---- prologue: the state tile and the first phase of K/V rows in flight together
-  dma_tile<T, K::SS, K::SD>(Ss, state + csh * (size_t)(N * P), (size_t)P, K::SR,
-                            K::ST_ROWS ? VD : KD, wave, nw);
-  dma_tile<T, K::KSL, K::KDS>(Ks, kg, ks_, JP, len, wave, nw);
-  dma_tile<T, K::VSL, K::VDS>(Vs, vg, vs, JP, len, wave, nw);
-  Frag<T> qf[KS];
-  const int i = t0 + col;
-#pragma unroll
-  for (int kk = 0; kk < KS; ++kk) {
-    const int k8 = kk * 32 + 8 * grp;
-    qf[kk] = (i < len && k8 < KD) ? frag_global(qg + (size_t)i * qs + k8) : frag_zero<T>();
-  }
-  Frag<T> xf[KSP];  // DX: the tile's own x rows, for dy_t . x_i
-  if constexpr (MODE == kBwdDX) {
-#pragma unroll
-    for (int kk = 0; kk < KSP; ++kk) {
-      const int k8 = kk * 32 + 8 * grp;
-      xf[kk] = (i < len && k8 < P) ? frag_global(xh + (size_t)i * hstride + k8) : frag_zero<T>();
-    }
-    for (int j = threadIdx.x; j < nw * Q; j += blockDim.x) rs_l[j] = 0.f;
-  }
-  const float si = s_ws[csh * Q + i];
-  for (int j = threadIdx.x; j < Q; j += blockDim.x) {
-    const float sv = s_ws[csh * Q + j];
-    s_l[j] = sv;
-    dt_l[j] = dt_ws[csh * Q + j];
-    if (REV) {  // u_j = 2^(s_j - s_(jb-1)), jb the first row of j's 32-row block
-      const int jb = j & ~31;
-      const float sp = jb > 0 ? s_ws[csh * Q + jb - 1] : 0.f;
-      u_l[j] = __builtin_amdgcn_exp2f(fminf(sv - sp, 0.f));
-    } else {  // u_j = 2^(s_r - s_j) dt_j, r the last row of j's block
-      u_l[j] = u_ws[csh * Q + j];
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  // ---- the state term: out^T = scale_i (state . Q_i)
-  const bool live = t0 < len;  // wave-uniform
   f4 acc[NVT];
 #pragma unroll
   for (int vt = 0; vt < NVT; ++vt) acc[vt] = zero4();
-  if (live) {
-#pragma unroll
-    for (int vt = 0; vt < NVT; ++vt) {
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        Frag<T> a;
-        if constexpr (K::ST_ROWS)
-          a = frag_rowk(Ss, K::SP, vt * 16 + col, kk * 32 + 8 * grp);
-        else
-          a = frag_kmaj(Ss, K::SP, vt * 16, kk * 32 + 8 * grp, kk * 32 + 8 * grp + 4);
-        mma(acc[vt], a, qf[kk]);
-      }
-    }
-    const float sc = MODE == kBwdDC ? __builtin_amdgcn_exp2f(fminf(si, 0.f))
-                                    : __builtin_amdgcn_exp2f(fminf(s_l[Q - 1] - si, 0.f));
-#pragma unroll
-    for (int vt = 0; vt < NVT; ++vt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[vt][r] *= sc;
-  }
-  // lane partials of the state-path terms: DX v_i / dt_i = x_i . acc_i,
-  // DC r_i = C_i . acc_i (summed over the lane groups in the epilogue)
-  float sp = 0.f;
-  if (live && i < len && MODE != kBwdDB) {
-    const T *row = MODE == kBwdDX ? xh + (size_t)i * hstride : Cg + (size_t)i * gstride;
-#pragma unroll
-    for (int vt = 0; vt < NVT; ++vt) {
-      const f4 w4 = ld4f(row + vt * 16 + 4 * grp);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sp += w4[r] * acc[vt][r];
-    }
-  }
-  float csum = 0.f;  // DX: this lane's share of the W column sum of i
-  const float dti = dt_l[i];
+  float sp = 0.f, csum = 0.f, dti = 0.f;  // DX: v_i / dt_i and W column-sum partials
 
-  // ---- the masked intra-chunk terms
-  const int tile_last = min(t0 + 15, len - 1);
-  for (int ph = 0; ph < len; ph += JP) {
-    if (ph > 0) {
-      __syncthreads();
-      dma_tile<T, K::KSL, K::KDS>(Ks, kg + (size_t)ph * ks_, ks_, JP, len - ph, wave, nw);
-      dma_tile<T, K::VSL, K::VDS>(Vs, vg + (size_t)ph * vs, vs, JP, len - ph, wave, nw);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+  const int nheads = MULTI ? hb : 1;  // one head: no loop
+  for (int hh = 0; hh < nheads; ++hh) {
+    const int hd = hd0 + hh;
+    const size_t csh = (size_t)c * H + hd;
+    const T *xh = x + (size_t)ci.y * hstride + (size_t)hd * P;
+    const T *dyh = dy + (size_t)ci.y * hstride + (size_t)hd * P;
+    const T *qg = MODE == kBwdDX ? Bg : (MODE == kBwdDB ? xh : dyh);
+    const T *kg = MODE == kBwdDX ? Cg : (MODE == kBwdDB ? dyh : xh);
+    const T *vg = MODE == kBwdDX ? dyh : (MODE == kBwdDB ? Cg : Bg);
+    const size_t qs = MODE == kBwdDX ? gstride : hstride;
+    const size_t ks_ = MODE == kBwdDX ? gstride : hstride;
+    const size_t vs = MODE == kBwdDX ? hstride : gstride;
+    if (hh > 0) __syncthreads();  // the previous head's tiles are no longer read
+
+    // ---- prologue: the state tile and the first phase of K/V rows in flight together
+    dma_tile<T, K::SS, K::SD>(Ss, state + csh * (size_t)(N * P), (size_t)P, K::SR,
+                              K::ST_ROWS ? VD : KD, wave, nw);
+    dma_tile<T, K::KSL, K::KDS>(Ks, kg, ks_, JP, len, wave, nw);
+    dma_tile<T, K::VSL, K::VDS>(Vs, vg, vs, JP, len, wave, nw);
+    dti = dt_ws[csh * Q + i];
+    Frag<T> qf[KS];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const int k8 = kk * 32 + 8 * grp;
+      qf[kk] = (i < len && k8 < KD) ? frag_global(qg + (size_t)i * qs + k8) : frag_zero<T>();
+      if constexpr (MULTI && MODE == kBwdDB) qf[kk] = frag_scale(qf[kk], dti);  // dt_i x_i
     }
-    int jb0, jend;
-    if (REV) {
-      jb0 = max(ph, t0 & ~31);
-      jend = live ? min(ph + JP, len) : jb0;
-    } else {
-      jb0 = ph;
-      jend = live ? min(ph + JP, tile_last + 1) : ph;
+    Frag<T> xf[KSP];  // DX: the tile's own x rows, for dy_t . x_i
+    if constexpr (MODE == kBwdDX) {
+#pragma unroll
+      for (int kk = 0; kk < KSP; ++kk) {
+        const int k8 = kk * 32 + 8 * grp;
+        xf[kk] = (i < len && k8 < P) ? frag_global(xh + (size_t)i * hstride + k8)
+                                     : frag_zero<T>();
+      }
+      for (int j = threadIdx.x; j < nw * Q; j += blockDim.x) rs_l[j] = 0.f;
     }
-    for (int jb = jb0; jb < jend; jb += 32) {
-      const int jl = jb - ph;
-      f4 g0 = zero4(), g1 = zero4();  // (K Q^T) for rows jb..jb+15 and jb+16..jb+31
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        const Frag<T> k0 = frag_rowk(Ks, K::KP, jl + col, kk * 32 + 8 * grp);
-        const Frag<T> k1 = frag_rowk(Ks, K::KP, jl + 16 + col, kk * 32 + 8 * grp);
-        mma(g0, k0, qf[kk]);
-        mma(g1, k1, qf[kk]);
+    const float si = s_ws[csh * Q + i];
+    for (int j = threadIdx.x; j < Q; j += blockDim.x) {
+      const float sv = s_ws[csh * Q + j];
+      s_l[j] = sv;
+      dt_l[j] = dt_ws[csh * Q + j];
+      if (REV) {  // u_j = 2^(s_j - s_(jb-1)), jb the first row of j's 32-row block
+        const int jb = j & ~31;
+        const float sprev = jb > 0 ? s_ws[csh * Q + jb - 1] : 0.f;
+        u_l[j] = __builtin_amdgcn_exp2f(fminf(sv - sprev, 0.f));
+      } else {  // u_j = 2^(s_r - s_j) dt_j, r the last row of j's block
+        u_l[j] = u_ws[csh * Q + j];
       }
-      float m[8];
-      const bool off = REV ? (jb > t0 + 15) : (jb + 31 < t0);
-      if (off) {
-        // block entirely past (reverse) or before (forward) the tile: the decay
-        // factors through the block edge, both factors <= 1
-        const float v = REV ? __builtin_amdgcn_exp2f(fminf(s_l[jb - 1] - si, 0.f))
-                            : __builtin_amdgcn_exp2f(fminf(si - s_l[jb + 31], 0.f));
-        const f4 u0 = ld4(u_l + jb + 4 * grp), u1 = ld4(u_l + jb + 16 + 4 * grp);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          m[r] = g0[r] * u0[r] * v;
-          m[4 + r] = g1[r] * u1[r] * v;
-        }
-      } else {  // the block holding the tile's rows: causal mask, exact decay
-        const f4 sj0 = ld4(s_l + jb + 4 * grp), sj1 = ld4(s_l + jb + 16 + 4 * grp);
-        const f4 dj0 = ld4(dt_l + jb + 4 * grp), dj1 = ld4(dt_l + jb + 16 + 4 * grp);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j0 = jb + 4 * grp + r, j1 = j0 + 16;
-          float e0, e1, k0, k1;
-          if (REV) {
-            e0 = __builtin_amdgcn_exp2f(fminf(sj0[r] - si, 0.f));
-            e1 = __builtin_amdgcn_exp2f(fminf(sj1[r] - si, 0.f));
-            k0 = j0 >= i ? 1.f : 0.f;
-            k1 = j1 >= i ? 1.f : 0.f;
-          } else {
-            e0 = __builtin_amdgcn_exp2f(fminf(si - sj0[r], 0.f)) * dj0[r];
-            e1 = __builtin_amdgcn_exp2f(fminf(si - sj1[r], 0.f)) * dj1[r];
-            k0 = j0 <= i ? 1.f : 0.f;
-            k1 = j1 <= i ? 1.f : 0.f;
-          }
-          m[r] = g0[r] * e0 * k0;
-          m[4 + r] = g1[r] * e1 * k1;
-        }
-      }
-      const Frag<T> mf = frag_from_f32(m, T());
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // ---- the state term: out^T += scale_i (state . Q_i)
+    if (live) {
+      const float sc = MODE == kBwdDC ? __builtin_amdgcn_exp2f(fminf(si, 0.f))
+                                      : __builtin_amdgcn_exp2f(fminf(s_l[Q - 1] - si, 0.f));
+      // one 16x16 tile at a time (a single temporary), with the lane partials of
+      // the state-path terms: DX v_i / dt_i = x_i . st_i, DC r_i = C_i . st_i
+      // (summed over the lane groups below)
+      float part_sp = 0.f;
+      const T *row = MODE == kBwdDX ? xh + (size_t)i * hstride : Cg + (size_t)i * gstride;
 #pragma unroll
       for (int vt = 0; vt < NVT; ++vt) {
-        const Frag<T> a = frag_kmaj(Vs, K::VP, vt * 16, jl + 4 * grp, jl + 16 + 4 * grp);
-        mma(acc[vt], a, mf);
-      }
-      if constexpr (MODE == kBwdDX) {
-        // W[t][i] = m dt_i (dy_t . x_i) in float32; rows t = jb + 4 grp + r (+16)
-        f4 d0 = zero4(), d1 = zero4();
+        // one head: straight into the (zero) accumulator; several: a temporary
+        f4 st = MULTI ? zero4() : acc[vt];
 #pragma unroll
-        for (int kk = 0; kk < KSP; ++kk) {
-          const Frag<T> a0 = frag_rowk(Vs, K::VP, jl + col, kk * 32 + 8 * grp);
-          const Frag<T> a1 = frag_rowk(Vs, K::VP, jl + 16 + col, kk * 32 + 8 * grp);
-          mma(d0, a0, xf[kk]);
-          mma(d1, a1, xf[kk]);
+        for (int kk = 0; kk < KS; ++kk) {
+          Frag<T> a;
+          if constexpr (K::ST_ROWS)
+            a = frag_rowk(Ss, K::SP, vt * 16 + col, kk * 32 + 8 * grp);
+          else
+            a = frag_kmaj(Ss, K::SP, vt * 16, kk * 32 + 8 * grp, kk * 32 + 8 * grp + 4);
+          mma(st, a, qf[kk]);
         }
-        float w[8];
+        f4 w4 = zero4();
+        if (MODE != kBwdDB && i < len) w4 = ld4f(row + vt * 16 + 4 * grp);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          w[r] = m[r] * d0[r] * dti;
-          w[4 + r] = m[4 + r] * d1[r] * dti;
-          csum += w[r] + w[4 + r];
+          const float v = st[r] * sc;
+          acc[vt][r] = MULTI ? acc[vt][r] + v : v;
+          part_sp += w4[r] * v;
         }
-        // row sums over the 16 columns of the lane group: a reduce-scatter in
-        // which lane col ends with the total of value (col>>1) of the 8
-        const bool b8 = col & 8, b4 = col & 4, b2 = col & 2;
-        float w4[4], w2[2];
+      }
+      if constexpr (MODE == kBwdDX) sp = part_sp;
+      if constexpr (MODE == kBwdDC) {  // r_t of this head
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float snd = b8 ? w[k] : w[k + 4];
-          w4[k] = (b8 ? w[k + 4] : w[k]) + __shfl_xor(snd, 8, 64);
-        }
+        for (int off = 16; off < 64; off <<= 1) part_sp += __shfl_xor(part_sp, off, 64);
+        if (grp == 0 && i < len) rows.r[csh * Q + i] = part_sp;
+      }
+    }
+
+    // ---- the masked intra-chunk terms
+    for (int ph = 0; ph < len; ph += JP) {
+      if (ph > 0) {
+        __syncthreads();
+        dma_tile<T, K::KSL, K::KDS>(Ks, kg + (size_t)ph * ks_, ks_, JP, len - ph, wave, nw);
+        dma_tile<T, K::VSL, K::VDS>(Vs, vg + (size_t)ph * vs, vs, JP, len - ph, wave, nw);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
+      int jb0, jend;
+      if (REV) {
+        jb0 = max(ph, t0 & ~31);
+        jend = live ? min(ph + JP, len) : jb0;
+      } else {
+        jb0 = ph;
+        jend = live ? min(ph + JP, tile_last + 1) : ph;
+      }
+      for (int jb = jb0; jb < jend; jb += 32) {
+        const int jl = jb - ph;
+        f4 g0 = zero4(), g1 = zero4();  // (K Q^T) for rows jb..jb+15 and jb+16..jb+31
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const float snd = b4 ? w4[k] : w4[k + 2];
-          w2[k] = (b4 ? w4[k + 2] : w4[k]) + __shfl_xor(snd, 4, 64);
+        for (int kk = 0; kk < KS; ++kk) {
+          const Frag<T> k0 = frag_rowk(Ks, K::KP, jl + col, kk * 32 + 8 * grp);
+          const Frag<T> k1 = frag_rowk(Ks, K::KP, jl + 16 + col, kk * 32 + 8 * grp);
+          mma(g0, k0, qf[kk]);
+          mma(g1, k1, qf[kk]);
         }
-        float w1 = (b2 ? w2[1] : w2[0]) + __shfl_xor(b2 ? w2[0] : w2[1], 2, 64);
-        w1 += __shfl_xor(w1, 1, 64);
-        if ((col & 1) == 0) {
-          const int idx = col >> 1;  // value index: rows 4 grp + idx, or 16 + 4 grp + idx - 4
-          const int t = jb + (idx < 4 ? 4 * grp + idx : 16 + 4 * grp + idx - 4);
-          rs_l[wave * Q + t] = w1;
+        float m[8];
+        const bool off = REV ? (jb > t0 + 15) : (jb + 31 < t0);
+        if (off) {
+          // block entirely past (reverse) or before (forward) the tile: the decay
+          // factors through the block edge, both factors <= 1
+          const float v = REV ? __builtin_amdgcn_exp2f(fminf(s_l[jb - 1] - si, 0.f))
+                              : __builtin_amdgcn_exp2f(fminf(si - s_l[jb + 31], 0.f));
+          const f4 u0 = ld4(u_l + jb + 4 * grp), u1 = ld4(u_l + jb + 16 + 4 * grp);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            m[r] = g0[r] * u0[r] * v;
+            m[4 + r] = g1[r] * u1[r] * v;
+          }
+        } else {  // the block holding the tile's rows: causal mask, exact decay
+          const f4 sj0 = ld4(s_l + jb + 4 * grp), sj1 = ld4(s_l + jb + 16 + 4 * grp);
+          const f4 dj0 = ld4(dt_l + jb + 4 * grp), dj1 = ld4(dt_l + jb + 16 + 4 * grp);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int j0 = jb + 4 * grp + r, j1 = j0 + 16;
+            float e0, e1, k0, k1;
+            if (REV) {
+              e0 = __builtin_amdgcn_exp2f(fminf(sj0[r] - si, 0.f));
+              e1 = __builtin_amdgcn_exp2f(fminf(sj1[r] - si, 0.f));
+              k0 = j0 >= i ? 1.f : 0.f;
+              k1 = j1 >= i ? 1.f : 0.f;
+            } else {
+              e0 = __builtin_amdgcn_exp2f(fminf(si - sj0[r], 0.f)) * dj0[r];
+              e1 = __builtin_amdgcn_exp2f(fminf(si - sj1[r], 0.f)) * dj1[r];
+              k0 = j0 <= i ? 1.f : 0.f;
+              k1 = j1 <= i ? 1.f : 0.f;
+            }
+            m[r] = g0[r] * e0 * k0;
+            m[4 + r] = g1[r] * e1 * k1;
+          }
+        }
+        const Frag<T> mf = frag_from_f32(m, T());
+#pragma unroll
+        for (int vt = 0; vt < NVT; ++vt) {
+          const Frag<T> a = frag_kmaj(Vs, K::VP, vt * 16, jl + 4 * grp, jl + 16 + 4 * grp);
+          mma(acc[vt], a, mf);
+        }
+        if constexpr (MODE == kBwdDX) {
+          // W[t][i] = m dt_i (dy_t . x_i) in float32; rows t = jb + 4 grp + r (+16)
+          f4 d0 = zero4(), d1 = zero4();
+#pragma unroll
+          for (int kk = 0; kk < KSP; ++kk) {
+            const Frag<T> a0 = frag_rowk(Vs, K::VP, jl + col, kk * 32 + 8 * grp);
+            const Frag<T> a1 = frag_rowk(Vs, K::VP, jl + 16 + col, kk * 32 + 8 * grp);
+            mma(d0, a0, xf[kk]);
+            mma(d1, a1, xf[kk]);
+          }
+          float w[8];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            w[r] = m[r] * d0[r] * dti;
+            w[4 + r] = m[4 + r] * d1[r] * dti;
+            csum += w[r] + w[4 + r];
+          }
+          // row sums over the 16 columns of the lane group: a reduce-scatter in
+          // which lane col ends with the total of value (col>>1) of the 8
+          const bool b8 = col & 8, b4 = col & 4, b2 = col & 2;
+          float w4[4], w2[2];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float snd = b8 ? w[k] : w[k + 4];
+            w4[k] = (b8 ? w[k + 4] : w[k]) + __shfl_xor(snd, 8, 64);
+          }
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const float snd = b4 ? w4[k] : w4[k + 2];
+            w2[k] = (b4 ? w4[k + 2] : w4[k]) + __shfl_xor(snd, 4, 64);
+          }
+          float w1 = (b2 ? w2[1] : w2[0]) + __shfl_xor(b2 ? w2[0] : w2[1], 2, 64);
+          w1 += __shfl_xor(w1, 1, 64);
+          if ((col & 1) == 0) {
+            const int idx = col >> 1;  // value index: rows 4 grp + idx, or 16 + 4 grp + idx - 4
+            const int t = jb + (idx < 4 ? 4 * grp + idx : 16 + 4 * grp + idx - 4);
+            rs_l[wave * Q + t] = w1;
+          }
         }
       }
     }
-  }
-  if constexpr (MODE == kBwdDX) {  // W row sums of this part: fixed-order sum over the waves
-    __syncthreads();
-    for (int t = threadIdx.x; t < len; t += blockDim.x) {
-      float sum = 0.f;
-      for (int w = 0; w < nw; ++w) sum += rs_l[w * Q + t];
-      rows.rs[(csh * SPLIT + part) * Q + t] = sum;
+    if constexpr (MODE == kBwdDX) {  // W row sums of this part: fixed-order sum over the waves
+      __syncthreads();
+      for (int t = threadIdx.x; t < len; t += blockDim.x) {
+        float sum = 0.f;
+        for (int w = 0; w < nw; ++w) sum += rs_l[w * Q + t];
+        rows.rs[(csh * SPLIT + part) * Q + t] = sum;
+      }
     }
   }
 
   // ---- epilogue: lane holds column i, rows v = 16 vt + 4 grp + r
   if (!live) return;
   if constexpr (MODE == kBwdDX) {
+    const int hd = hd0;
+    const size_t csh = (size_t)c * H + hd;
     float qp = 0.f, dp = 0.f;
     const float Dh = D[hd];
     if (i < len) {
@@ -377,22 +399,15 @@ __global__ __launch_bounds__(MAXT) void k_bwd_scan(
       rows.dyx[csh * Q + i] = dp;
       rows.cv[csh * Q + i] = csum + dti * sp;  // W column sum + v_i
     }
-  } else {
-    if constexpr (MODE == kBwdDC) {
+  } else if (i < len) {
+    const size_t orow = ((size_t)ci.y + i) * ostride + (ostride == G ? g : blk);
+    const float sc = (MODE == kBwdDB && !MULTI) ? dti : 1.f;  // DB of one head: dt_i here
 #pragma unroll
-      for (int off = 16; off < 64; off <<= 1) sp += __shfl_xor(sp, off, 64);
-      if (grp == 0 && i < len) rows.r[csh * Q + i] = sp;
-    }
-    if (i < len) {
-      const float sc = MODE == kBwdDB ? dt_l[i] : 1.f;
-      const size_t orow = ((size_t)ci.y + i) * ostride + (ostride == H ? hd : g);
+    for (int vt = 0; vt < NVT; ++vt) {
+      f4 o = acc[vt];
 #pragma unroll
-      for (int vt = 0; vt < NVT; ++vt) {
-        f4 o = acc[vt];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] *= sc;
-        st4(out + orow * N + vt * 16 + 4 * grp, o);
-      }
+      for (int r = 0; r < 4; ++r) o[r] *= sc;
+      st4(out + orow * N + vt * 16 + 4 * grp, o);
     }
   }
 }
@@ -528,59 +543,76 @@ __global__ __launch_bounds__(512) void k_bwd_ddt(BwdRows rows, int nsplit,
   }
 }
 
-// dB[t][g] = sum over the heads of group g of dBh[t][h] (the same for dC).
-__global__ __launch_bounds__(256) void k_bwd_group_sum(const float *__restrict__ dBh,
-                                                       const float *__restrict__ dCh,
-                                                       float *__restrict__ dB,
-                                                       float *__restrict__ dC, int64_t T, int H,
-                                                       int G, int N) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+// Fixed-order sums, one launch: workgroups [0, H) add the per-chunk partials
+// of dA[h] and dD[h]; the rest (when parts > 1) add the `parts` partial rows of
+// each group of dB and dC (partial row k of group g is row g * parts + k).
+__global__ __launch_bounds__(256) void k_bwd_sums(const float *__restrict__ dApart,
+                                                  const float *__restrict__ dDpart, int nc,
+                                                  int H, float *__restrict__ dA,
+                                                  float *__restrict__ dD,
+                                                  const float *__restrict__ dBp,
+                                                  const float *__restrict__ dCp,
+                                                  float *__restrict__ dB, float *__restrict__ dC,
+                                                  int64_t T, int G, int N, int parts) {
+  const int tid = threadIdx.x;
+  if ((int)blockIdx.x < H) {
+    __shared__ float part[2][4];
+    const int hd = blockIdx.x, lane = tid & 63, wave = tid >> 6;
+    float sa = 0.f, sd = 0.f;
+    for (int c = tid; c < nc; c += 256) {
+      sa += dApart[(size_t)c * H + hd];
+      sd += dDpart[(size_t)c * H + hd];
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      sa += __shfl_xor(sa, off, 64);
+      sd += __shfl_xor(sd, off, 64);
+    }
+    if (lane == 0) {
+      part[0][wave] = sa;
+      part[1][wave] = sd;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      dA[hd] = part[0][0] + part[0][1] + part[0][2] + part[0][3];
+      dD[hd] = part[1][0] + part[1][1] + part[1][2] + part[1][3];
+    }
+    return;
+  }
+  const int64_t idx = (int64_t)(blockIdx.x - H) * 256 + tid;
   const int nq = N / 4;
   if (idx >= T * G * nq) return;
   const int n = (int)(idx % nq) * 4, g = (int)((idx / nq) % G);
   const int64_t t = idx / ((int64_t)nq * G);
-  const int hg = H / G;
   f4 sb = zero4(), sc = zero4();
-  for (int k = 0; k < hg; ++k) {
-    const size_t o = ((size_t)t * H + (size_t)g * hg + k) * N + n;
-    sb += ld4(dBh + o);
-    sc += ld4(dCh + o);
+  for (int k = 0; k < parts; ++k) {
+    const size_t o = ((size_t)t * G * parts + (size_t)g * parts + k) * N + n;
+    sb += ld4(dBp + o);
+    sc += ld4(dCp + o);
   }
   const size_t o = ((size_t)t * G + g) * N + n;
   st4(dB + o, sb);
   st4(dC + o, sc);
 }
 
-// dA[h], dD[h]: sums of the per-chunk partials, one workgroup per head.
-__global__ __launch_bounds__(256) void k_bwd_head_sum(const float *__restrict__ dApart,
-                                                      const float *__restrict__ dDpart, int nc,
-                                                      int H, float *__restrict__ dA,
-                                                      float *__restrict__ dD) {
-  __shared__ float part[2][4];
-  const int hd = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  float sa = 0.f, sd = 0.f;
-  for (int c = tid; c < nc; c += 256) {
-    sa += dApart[(size_t)c * H + hd];
-    sd += dDpart[(size_t)c * H + hd];
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    sa += __shfl_xor(sa, off, 64);
-    sd += __shfl_xor(sd, off, 64);
-  }
-  if (lane == 0) {
-    part[0][wave] = sa;
-    part[1][wave] = sd;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    dA[hd] = part[0][0] + part[0][1] + part[0][2] + part[0][3];
-    dD[hd] = part[1][0] + part[1][1] + part[1][2] + part[1][3];
-  }
-}
-
 // ------------------------------------------------------------------ launch
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Heads per DB/DC workgroup: the largest divisor of H/G that still leaves at
+// least 768 workgroups (three per CU), so few chunks keep every head apart and
+// many chunks sum most heads of a group on chip.  SSD_BWD_HEADS=<n> asks for n
+// instead (used if it divides H/G).
+static int bwd_heads_per_block(int64_t nc, int H, int G, int Q) {
+  const int hpg = H / G, split = Q >= 256 ? 2 : 1;
+  if (const char *e = getenv("SSD_BWD_HEADS")) {
+    const int want = atoi(e);
+    if (want >= 1 && hpg % want == 0) return want;
+  }
+  const int64_t units = nc * H * split;
+  for (int d = hpg; d > 1; --d)
+    if (hpg % d == 0 && units / d >= 768) return d;
+  return 1;
+}
 
 BwdLayout bwd_layout(int64_t T, int nseq, int H, int P, int N, int G, int Q, int elem) {
   BwdLayout L{};
@@ -602,7 +634,8 @@ BwdLayout bwd_layout(int64_t T, int nseq, int H, int P, int N, int G, int Q, int
   off = align_up(off + 4 * nc * H, 256);
   L.dDpart = off;
   off = align_up(off + 4 * nc * H, 256);
-  const size_t per_head = H > G ? 4 * (size_t)(T > 0 ? T : 0) * H * N : 0;
+  const int hb = bwd_heads_per_block(L.fwd.nc_max, H, G, Q);
+  const size_t per_head = hb < H / G ? 4 * (size_t)(T > 0 ? T : 0) * (H / hb) * N : 0;
   L.dBh = off;
   off = align_up(off + per_head, 256);
   L.dCh = off;
@@ -619,7 +652,7 @@ static BwdRows bwd_rows(char *ws, const BwdLayout &L, int nc, int H, int Q) {
 
 template <typename T, int MODE, int P, int N>
 static hipError_t launch_bwd_scan(const BwdArgs &a, const BwdLayout &L, int nc, const T *state,
-                                  float *out, int ostride, hipStream_t st) {
+                                  float *out, int ostride, int hb, hipStream_t st) {
   constexpr int KD = MODE == kBwdDX ? N : P, VD = MODE == kBwdDX ? P : N;
   typedef BwdScanCfg<T, MODE, KD, VD> K;
   const int Q = a.f.Q;
@@ -628,9 +661,20 @@ static hipError_t launch_bwd_scan(const BwdArgs &a, const BwdLayout &L, int nc, 
   const int jp = K::jp(Q, threads);
   const size_t lds = K::lds_bytes(jp, Q, threads / 64);
   if (lds > 160 * 1024) return hipErrorInvalidConfiguration;
-  const void *kern = split == 1     ? (const void *)k_bwd_scan<T, MODE, P, N, 1, 512>
-                     : threads <= 512 ? (const void *)k_bwd_scan<T, MODE, P, N, 2, 512>
-                                      : (const void *)k_bwd_scan<T, MODE, P, N, 2, 1024>;
+  const void *kern;
+  if (hb > 1) {  // several heads per workgroup (DB and DC only)
+    if constexpr (MODE != kBwdDX) {
+      kern = split == 1     ? (const void *)k_bwd_scan<T, MODE, P, N, 1, 512, true>
+             : threads <= 512 ? (const void *)k_bwd_scan<T, MODE, P, N, 2, 512, true>
+                              : (const void *)k_bwd_scan<T, MODE, P, N, 2, 1024, true>;
+    } else {
+      return hipErrorInvalidValue;
+    }
+  } else {
+    kern = split == 1     ? (const void *)k_bwd_scan<T, MODE, P, N, 1, 512, false>
+           : threads <= 512 ? (const void *)k_bwd_scan<T, MODE, P, N, 2, 512, false>
+                            : (const void *)k_bwd_scan<T, MODE, P, N, 2, 1024, false>;
+  }
   hipError_t e = set_lds_limit(kern);
   if (e != hipSuccess) return e;
   char *ws = static_cast<char *>(a.f.workspace);
@@ -642,11 +686,12 @@ static hipError_t launch_bwd_scan(const BwdArgs &a, const BwdLayout &L, int nc, 
   const float *up = reinterpret_cast<const float *>(ws + L.fwd.u);
   ChunkMap cm{reinterpret_cast<const int4 *>(ws + L.fwd.info),
               a.f.cu ? 0 : (int)(a.f.T / a.f.nseq), a.f.nseq, Q};
-  int nc_ = nc, H_ = a.f.H, G_ = a.f.G, Q_ = Q, jp_ = jp, os_ = ostride;
+  int nc_ = nc, H_ = a.f.H, G_ = a.f.G, Q_ = Q, jp_ = jp, hb_ = hb, os_ = ostride;
   BwdRows rows = bwd_rows(ws, L, nc, a.f.H, Q);
   void *args[] = {&xp, &dyp, &bp, &cp, &Dp, &sp, &dtp, &up, &state, &cm, &nc_,
-                  &H_, &G_, &Q_, &jp_, &out, &os_, &rows};
-  return hipLaunchKernel(kern, dim3(xcd_grid(nc, a.f.H * split)), dim3(threads), args, lds, st);
+                  &H_, &G_, &Q_, &jp_, &hb_, &out, &os_, &rows};
+  return hipLaunchKernel(kern, dim3(xcd_grid(nc, (a.f.H / hb) * split)), dim3(threads), args, lds,
+                         st);
 }
 
 template <typename T, int P, int N>
@@ -689,16 +734,17 @@ static hipError_t run_backward(const BwdArgs &a) {
                      hin32, dHc, epart, a.dh0, f.H, NP, f.Q);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  const int hb = bwd_heads_per_block(nc, f.H, f.G, f.Q);
+  const int parts = f.H / f.G / hb;  // partial rows per group and token (1: written directly)
+  float *dBo = parts == 1 ? a.dB : reinterpret_cast<float *>(ws + L.dBh);
+  float *dCo = parts == 1 ? a.dC : reinterpret_cast<float *>(ws + L.dCh);
   if (nc > 0) {
-    const bool direct = f.H == f.G;  // one head per group: no head sum
-    float *dBo = direct ? a.dB : reinterpret_cast<float *>(ws + L.dBh);
-    float *dCo = direct ? a.dC : reinterpret_cast<float *>(ws + L.dCh);
-    const int os = direct ? f.G : f.H;
-    e = launch_bwd_scan<T, kBwdDX, P, N>(a, L, nc, dHc, a.dx, f.H, st);
+    const int os = f.H / hb;
+    e = launch_bwd_scan<T, kBwdDX, P, N>(a, L, nc, dHc, a.dx, f.H, 1, st);
     if (e != hipSuccess) return e;
-    e = launch_bwd_scan<T, kBwdDB, P, N>(a, L, nc, dHc, dBo, os, st);
+    e = launch_bwd_scan<T, kBwdDB, P, N>(a, L, nc, dHc, dBo, os, hb, st);
     if (e != hipSuccess) return e;
-    e = launch_bwd_scan<T, kBwdDC, P, N>(a, L, nc, hin, dCo, os, st);
+    e = launch_bwd_scan<T, kBwdDC, P, N>(a, L, nc, hin, dCo, os, hb, st);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_bwd_ddt, dim3((unsigned)nc * f.H), dim3(f.Q < 64 ? 64 : f.Q), 0, st,
                        bwd_rows(ws, L, nc, f.H, f.Q), f.Q >= 256 ? 2 : 1,
@@ -706,16 +752,10 @@ static hipError_t run_backward(const BwdArgs &a) {
                        f.H, f.Q, a.ddt, dApart, dDpart);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (!direct && f.T > 0) {
-      const int64_t n = f.T * f.G * (N / 4);
-      hipLaunchKernelGGL(k_bwd_group_sum, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                         dBo, dCo, a.dB, a.dC, f.T, f.H, f.G, N);
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
   }
-  hipLaunchKernelGGL(k_bwd_head_sum, dim3(f.H), dim3(256), 0, st, dApart, dDpart, nc, f.H, a.dA,
-                     a.dD);
+  const int64_t ngs = (parts > 1 && nc > 0) ? (f.T * f.G * (N / 4) + 255) / 256 : 0;
+  hipLaunchKernelGGL(k_bwd_sums, dim3((unsigned)(f.H + ngs)), dim3(256), 0, st, dApart, dDpart,
+                     nc, f.H, a.dA, a.dD, dBo, dCo, a.dB, a.dC, f.T, f.G, N, parts);
   return hipGetLastError();
 }
 

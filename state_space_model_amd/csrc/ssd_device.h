@@ -52,6 +52,18 @@ __device__ __forceinline__ Frag<float> frag_from_f32(const float (&m)[8], float)
   for (int e = 0; e < 8; ++e) f.v[e] = m[e];
   return f;
 }
+// Fragment times a scalar (float32 arithmetic, rounded back for bf16).
+__device__ __forceinline__ Frag<bf16> frag_scale(const Frag<bf16> &f, float s) {
+  Frag<bf16> o;
+  o.v = cvt_bf8(cvt_f8(f.v) * s);
+  return o;
+}
+__device__ __forceinline__ Frag<float> frag_scale(const Frag<float> &f, float s) {
+  Frag<float> o;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o.v[e] = f.v[e] * s;
+  return o;
+}
 template <typename T> __device__ __forceinline__ Frag<T> frag_zero() {
   const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   return frag_from_f32(z, T());

@@ -70,7 +70,8 @@ struct BwdLayout {
   size_t epart;   // f32 [nc][H][NP/256]  wave partials of <dH_c, H_c>
   size_t rows;             // f32 6 x [nc][H][Q]  per-row terms of dz (q, cv, r, dyx, rs x 2)
   size_t dApart, dDpart;   // f32 [nc][H]
-  size_t dBh, dCh;         // f32 [T][H][N]  per-head dB, dC (only when H > G)
+  size_t dBh, dCh;         // f32 [T][H/hb][N]  partial dB, dC per block of hb heads
+                           //                  (absent when one block holds a whole group)
   size_t total;
 };
 BwdLayout bwd_layout(int64_t T, int nseq, int H, int P, int N, int G, int Q, int elem);
