@@ -10,6 +10,7 @@ token, in float64).  This module only marshals arrays through ctypes:
 * ``prefill(x, dt, A, B, C, D, h0=None, cu_seqlens=None)`` -> ``(y, h_out)``
 * ``step(x, dt, A, B, C, D, h)`` -> ``y`` (``h`` updated in place)
 * ``prefill_backward(..., dy, dh_out)`` -> gradients of the prefill inputs
+* ``gated_delta_rule(q, k, v, g, beta, h0=None, cu_seqlens=None)`` -> ``(o, h_out)``
 
 Passages followed: COREY, section 3.1 (generic selective SSM update);
 Compiler-First State Space Duality ..., Abstract (one scalar decay per head);
@@ -55,6 +56,8 @@ def _bind(lib):
     lib.ssd_ref_prefill_backward.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, P, P,
                                              P, P, P, P, P, P, P, I]
     lib.ssd_ref_prefill_backward.restype = I
+    lib.ssd_ref_gated_delta_rule.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P, P, I]
+    lib.ssd_ref_gated_delta_rule.restype = I
     return lib
 
 
@@ -211,3 +214,32 @@ def prefill_backward(x, dt, A, B, C, D, dy, h0=None, dh_out=None, cu_seqlens=Non
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
     return out
+
+
+def gated_delta_rule(q, k, v, g, beta, h0=None, cu_seqlens=None, threads=None, lib=None):
+    """Gated delta rule in fp64, token by token.  q, k [T,G,K]; v [T,H,V];
+    g (log-gate, <= 0), beta [T,H]; h0 [nseq,H,V,K] or None; cu_seqlens
+    [nseq+1] or None (one sequence).  Returns (o [T,H,V], h_out [nseq,H,V,K])."""
+    lib = lib or load()
+    q, k, v, g, beta = (_f32(a) for a in (q, k, v, g, beta))
+    T, G, K = q.shape
+    H, V = v.shape[1], v.shape[2]
+    if cu_seqlens is None:
+        cu_seqlens = np.array([0, T], dtype=np.int64)
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    nseq = cu.shape[0] - 1
+    assert cu[0] == 0 and cu[-1] == T
+    assert k.shape == (T, G, K) and v.shape == (T, H, V)
+    assert g.shape == (T, H) and beta.shape == (T, H)
+    h0c = None
+    if h0 is not None:
+        h0c = np.ascontiguousarray(np.asarray(h0, dtype=np.float64))
+        assert h0c.shape == (nseq, H, V, K)
+    o = np.empty((T, H, V), dtype=np.float64)
+    h_out = np.empty((nseq, H, V, K), dtype=np.float64)
+    rc = lib.ssd_ref_gated_delta_rule(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0c),
+                                      _ptr(cu), nseq, H, G, K, V, _ptr(o), _ptr(h_out),
+                                      threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    return o, h_out

@@ -30,9 +30,9 @@
  * factor, D is a per-head scalar skip, head h reads group floor(h*G/H).
  *
  * The decode-layer operations around the scan (the causal conv1d step and
- * the gated RMS norm), the Mamba-1 selective scan and the reverse-mode
- * gradients of the recurrence (the backward half of a training step) are at
- * the end of this file, with their own passages.
+ * the gated RMS norm), the Mamba-1 selective scan, the reverse-mode gradients
+ * of the recurrence (the backward half of a training step) and the gated
+ * delta rule are at the end of this file, with their own passages.
  *
  * Inputs are float32 (bf16 inputs are upcast exactly before the call); all
  * arithmetic and the outputs are float64.  Layouts are row-major:
@@ -376,5 +376,74 @@ int ssd_ref_prefill_backward(const float *x, const float *dt, const float *A,
         dD[hd] = sd;
     }
     free(dBh); free(dCh); free(dAs); free(dDs);
+    return bad ? -1 : 0;
+}
+
+/*
+ * Gated delta rule: the other scan family of Recurrence Scan ("Gated delta
+ * rule (GDN) layers ... each token updates a per-head state matrix, and the
+ * state is carried from one step to the next"; the scan returns the output and
+ * the carried state, "One equation, one packed result").  The page gives no
+ * equation; this is the published gated delta rule, per sequence and head h
+ * (q, k read group g = floor(h*G/H)), state S [V][K] (row i = value index):
+ *   a_t   = exp(g_t)                                   (g_t <= 0: the gate)
+ *   u     = S_{t-1} k_t                                (V vector)
+ *   S_t   = a_t S_{t-1} + beta_t (v_t - a_t u) k_t^T  (delta-rule correction)
+ *   o_t   = S_t q_t
+ * i.e. S_t = S_{t-1} a_t (I - beta_t k_t k_t^T) + beta_t v_t k_t^T.  q, k, v, g,
+ * beta arrive final: any normalisation of k, scale of q, activation of beta
+ * and log-gate are the caller's.  Layouts: q, k [T][G][K]; v [T][H][V];
+ * g, beta [T][H]; h0, h_out [nseq][H][V][K] (h0 NULL: zeros); o [T][H][V].
+ * Sequences are packed along T by cu (cu[s] .. cu[s+1]-1).
+ */
+int ssd_ref_gated_delta_rule(const float *q, const float *k, const float *v, const float *g,
+                             const float *beta, const double *h0, const int64_t *cu, int nseq,
+                             int H, int G, int K, int V, double *o, double *h_out,
+                             int nthreads)
+{
+    if (!cu || nseq < 0 || H <= 0 || G <= 0 || K <= 0 || V <= 0 || H % G != 0) return -1;
+    for (int s = 0; s < nseq; ++s)
+        if (cu[s + 1] < cu[s]) return -1;
+    if (nseq > 0 && cu[nseq] > 0 && (!q || !k || !v || !g || !beta || !o)) return -1;
+    const long units = (long)nseq * H;
+    const size_t VK = (size_t)V * K;
+    if (nthreads <= 0) nthreads = 1;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+    for (long un = 0; un < units; ++un) {
+        const int s = (int)(un / H), hd = (int)(un % H);
+        const int gr = (int)(((long)hd * G) / H);
+        double *S = (double *)malloc(sizeof(double) * VK);
+        double *u = (double *)malloc(sizeof(double) * V);
+        if (!S || !u) { bad = 1; free(S); free(u); continue; }
+        const size_t soff = ((size_t)s * H + hd) * VK;
+        if (h0) memcpy(S, h0 + soff, sizeof(double) * VK);
+        else memset(S, 0, sizeof(double) * VK);
+        for (int64_t t = cu[s]; t < cu[s + 1]; ++t) {
+            const float *qt = q + ((size_t)t * G + gr) * K, *kt = k + ((size_t)t * G + gr) * K;
+            const float *vt = v + ((size_t)t * H + hd) * V;
+            const double a = exp((double)g[(size_t)t * H + hd]);
+            const double b = (double)beta[(size_t)t * H + hd];
+            for (int i = 0; i < V; ++i) {
+                double acc = 0.0;
+                for (int j = 0; j < K; ++j) acc += S[(size_t)i * K + j] * (double)kt[j];
+                u[i] = acc;
+            }
+            for (int i = 0; i < V; ++i) {
+                const double c = b * ((double)vt[i] - a * u[i]);
+                for (int j = 0; j < K; ++j)
+                    S[(size_t)i * K + j] = a * S[(size_t)i * K + j] + c * (double)kt[j];
+            }
+            double *ot = o + ((size_t)t * H + hd) * V;
+            for (int i = 0; i < V; ++i) {
+                double acc = 0.0;
+                for (int j = 0; j < K; ++j) acc += S[(size_t)i * K + j] * (double)qt[j];
+                ot[i] = acc;
+            }
+        }
+        if (h_out) memcpy(h_out + soff, S, sizeof(double) * VK);
+        free(S);
+        free(u);
+    }
     return bad ? -1 : 0;
 }

@@ -609,3 +609,138 @@ BWD_PINS = {
     "bwd_affine": pin_bwd_affine, "bwd_fd": pin_bwd_fd, "bwd_euler": pin_bwd_euler,
     "bwd_split": pin_bwd_split,
 }
+
+
+# ---------------------------------------------------------------------------
+# Pins of the gated delta rule (``gated_delta_rule``): per head, state S [V][K],
+# S_t = S_{t-1} a_t (I - beta_t k_t k_t^T) + beta_t v_t k_t^T, o_t = S_t q_t.
+#   gdn_products    the state as explicit products of the K x K transition
+#                   matrices (no rank-one update anywhere), O(L^2 K^3)
+#   gdn_beta0       beta = 0: the state only decays, o_t = (prod a) S_0 q_t
+#   gdn_retrieval   a = 1, beta = 1, unit keys, q = k: each token reads back
+#                   exactly the value it wrote, o = v
+#   gdn_orthogonal  beta = 1, orthonormal keys, h0 = 0: no correction is ever
+#                   needed, the rule is decayed linear attention
+#                   o_t = sum_{r<=t} (prod_{r<s<=t} a_s) (k_r . q_t) v_r
+#   gdn_split       two calls handing the state on equal one call
+#   gdn_groups      G groups equal G = H with q, k repeated over each head block
+
+def _gdn_case(lens, H, G, K, V, seed, h0=True, unit_k=True):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    T = int(sum(lens))
+    q = (rng.standard_normal((T, G, K)) / np.sqrt(K)).astype(np.float32)
+    k = rng.standard_normal((T, G, K))
+    if unit_k:
+        k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    k = k.astype(np.float32)
+    v = rng.standard_normal((T, H, V)).astype(np.float32)
+    g = np.log(rng.uniform(0.8, 1.0, (T, H))).astype(np.float32)
+    beta = rng.uniform(0.1, 0.9, (T, H)).astype(np.float32)
+    hz = rng.normal(0.0, 0.3, (len(lens), H, V, K)) if h0 else None
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    return q, k, v, g, beta, hz, cu
+
+
+def pin_gdn_products(orc):
+    worst = 0.0
+    for seed, (L, H, G, K, V) in ((161, (6, 2, 1, 3, 4)), (163, (5, 3, 3, 4, 2))):
+        q, k, v, g, beta, h0, cu = _gdn_case([L], H, G, K, V, seed)
+        o, ho = orc.gated_delta_rule(q, k, v, g, beta, h0, cu)
+        ro = np.empty((L, H, V))
+        for h in range(H):
+            gr = h * G // H
+            Am = [np.exp(np.float64(g[t, h])) *
+                  (np.eye(K) - np.float64(beta[t, h]) *
+                   np.outer(k[t, gr].astype(np.float64), k[t, gr].astype(np.float64)))
+                  for t in range(L)]
+            for t in range(L):
+                prod = np.eye(K)
+                for s_ in range(t + 1):
+                    prod = prod @ Am[s_]
+                S = h0[0, h] @ prod
+                for r in range(t + 1):
+                    tail = np.eye(K)
+                    for s_ in range(r + 1, t + 1):
+                        tail = tail @ Am[s_]
+                    S = S + np.float64(beta[r, h]) * np.outer(v[r, h].astype(np.float64),
+                                                              k[r, gr].astype(np.float64)) @ tail
+                ro[t, h] = S @ q[t, gr].astype(np.float64)
+                if t == L - 1:
+                    worst = max(worst, _rel(ho[0, h], S))
+        worst = max(worst, _rel(o, ro))
+    return worst <= 1e-12, f"max rel err {worst:.3g}"
+
+
+def pin_gdn_beta0(orc):
+    L, H, G, K, V = 7, 2, 1, 4, 3
+    q, k, v, g, beta, h0, cu = _gdn_case([L], H, G, K, V, 167)
+    beta = np.zeros_like(beta)
+    o, ho = orc.gated_delta_rule(q, k, v, g, beta, h0, cu)
+    dec = np.exp(np.cumsum(g.astype(np.float64), axis=0))       # [L, H]
+    ro = np.einsum("th,hvk,tk->thv", dec, h0[0], q[:, 0].astype(np.float64))
+    e = max(_rel(o, ro), _rel(ho[0], dec[-1][:, None, None] * h0[0]))
+    return e <= 1e-12, f"rel err {e:.3g}"
+
+
+def pin_gdn_retrieval(orc):
+    L, H, G, K, V = 9, 2, 2, 5, 3
+    q, k, v, g, beta, h0, cu = _gdn_case([L], H, G, K, V, 173)
+    # exactly unit keys in fp32: four entries +-1/2 and one zero, random signs
+    # and position (neither orthogonal nor parallel to each other in general)
+    rng = np.random.Generator(np.random.PCG64(175))
+    k = 0.5 * rng.choice([-1.0, 1.0], size=(L, G, K))
+    k[np.arange(L)[:, None], np.arange(G)[None, :], rng.integers(0, K, (L, G))] = 0.0
+    k = k.astype(np.float32)
+    o, _ = orc.gated_delta_rule(k, k, v, np.zeros_like(g), np.ones_like(beta), h0, cu)
+    e = _rel(o, v)
+    return e <= 1e-12, f"rel err {e:.3g}"
+
+
+def pin_gdn_orthogonal(orc):
+    from scipy.linalg import hadamard
+    L, H, G, K, V = 6, 2, 1, 16, 3
+    q, k, v, g, beta, _, cu = _gdn_case([L], H, G, K, V, 179)
+    rng = np.random.Generator(np.random.PCG64(181))
+    # rows of the 16 x 16 Hadamard matrix / 4: exactly orthonormal in fp32
+    k = (hadamard(K)[rng.permutation(K)[:L]] / 4.0).astype(np.float32)[:, None, :]
+    o, ho = orc.gated_delta_rule(q, k, v, g, np.ones_like(beta), None, cu)
+    k64, q64, v64 = (a.astype(np.float64) for a in (k[:, 0], q[:, 0], v))
+    g64 = g.astype(np.float64)
+    ro = np.zeros((L, H, V))
+    for t in range(L):
+        for r in range(t + 1):
+            w = np.exp(np.sum(g64[r + 1:t + 1], axis=0))         # [H]
+            ro[t] += w[:, None] * (k64[r] @ q64[t]) * v64[r]
+    e = _rel(o, ro)
+    return e <= 1e-12, f"rel err {e:.3g}"
+
+
+def pin_gdn_split(orc):
+    lens = [13]
+    q, k, v, g, beta, h0, cu = _gdn_case(lens, 3, 1, 4, 5, 191)
+    o, ho = orc.gated_delta_rule(q, k, v, g, beta, h0, cu)
+    worst = 0.0
+    for c in (0, 1, 6, 12, 13):
+        a, b = slice(0, c), slice(c, 13)
+        o1, h1 = orc.gated_delta_rule(q[a], k[a], v[a], g[a], beta[a], h0, np.array([0, c]))
+        o2, h2 = orc.gated_delta_rule(q[b], k[b], v[b], g[b], beta[b], h1, np.array([0, 13 - c]))
+        worst = max(worst, _rel(np.concatenate([o1, o2]), o), _rel(h2, ho))
+    return worst <= RTOL, f"max rel err {worst:.3g}"
+
+
+def pin_gdn_groups(orc):
+    lens = [5, 4]
+    H, G, K, V = 6, 2, 3, 4
+    q, k, v, g, beta, h0, cu = _gdn_case(lens, H, G, K, V, 193)
+    o, ho = orc.gated_delta_rule(q, k, v, g, beta, h0, cu)
+    rep = np.repeat(np.arange(G), H // G)
+    o2, h2 = orc.gated_delta_rule(q[:, rep], k[:, rep], v, g, beta, h0, cu)
+    e = max(_rel(o, o2), _rel(ho, h2))
+    return e == 0.0, f"rel err {e:.3g}"
+
+
+GDN_PINS = {
+    "gdn_products": pin_gdn_products, "gdn_beta0": pin_gdn_beta0,
+    "gdn_retrieval": pin_gdn_retrieval, "gdn_orthogonal": pin_gdn_orthogonal,
+    "gdn_split": pin_gdn_split, "gdn_groups": pin_gdn_groups,
+}

@@ -236,3 +236,54 @@ def test_backward_mutant_is_caught(name, tmp_path_factory):
         if not ok:
             caught.append(pname)
     assert caught, f"mutant {name} passed every backward pin"
+
+
+# Planted mistakes in the gated delta rule; each must fail a delta-rule pin.
+GDN_MUTANTS = [
+    ("gdn-gate-missing-in-correction", "const double c = b * ((double)vt[i] - a * u[i]);",
+     "const double c = b * ((double)vt[i] - u[i]);"),
+    ("gdn-beta-dropped", "const double c = b * ((double)vt[i] - a * u[i]);",
+     "const double c = ((double)vt[i] - a * u[i]);"),
+    ("gdn-gate-sign", "const double a = exp((double)g[(size_t)t * H + hd]);",
+     "const double a = exp(-(double)g[(size_t)t * H + hd]);"),
+    ("gdn-output-reads-key", "acc += S[(size_t)i * K + j] * (double)qt[j];",
+     "acc += S[(size_t)i * K + j] * (double)kt[j];"),
+    ("gdn-correction-reads-query", "for (int j = 0; j < K; ++j) acc += S[(size_t)i * K + j] * (double)kt[j];\n                u[i] = acc;",
+     "for (int j = 0; j < K; ++j) acc += S[(size_t)i * K + j] * (double)qt[j];\n                u[i] = acc;"),
+    ("gdn-write-on-query", "S[(size_t)i * K + j] = a * S[(size_t)i * K + j] + c * (double)kt[j];",
+     "S[(size_t)i * K + j] = a * S[(size_t)i * K + j] + c * (double)qt[j];"),
+    ("gdn-h0-ignored", "if (h0) memcpy(S, h0 + soff", "if (0) memcpy(S, h0 + soff"),
+    ("gdn-group-modulo", "const int gr = (int)(((long)hd * G) / H);", "const int gr = (int)(hd % G);"),
+]
+
+
+@functools.lru_cache(maxsize=None)
+def _gdn_mutant_lib(name, tmpdir):
+    orig, repl = next((o, r) for n, o, r in GDN_MUTANTS if n == name)
+    assert SRC.count(orig) == 1, f"mutation site for {name} not unique in the oracle source"
+    path = os.path.join(tmpdir, f"gdnmut_{name}.c")
+    with open(path, "w") as f:
+        f.write(SRC.replace(orig, repl))
+    lib = obuild.build(path, os.path.join(tmpdir, f"libgdnmut_{name}.so"),
+                       extra_flags=("-Wno-unused-variable", "-Wno-unused-but-set-variable"))
+    return oracle.load(lib)
+
+
+@pytest.mark.parametrize("name", [m[0] for m in GDN_MUTANTS])
+def test_gated_delta_rule_mutant_is_caught(name, tmp_path_factory):
+    lib = _gdn_mutant_lib(name, str(tmp_path_factory.getbasetemp()))
+
+    class Orc:
+        @staticmethod
+        def gated_delta_rule(*a, **k):
+            return oracle.gated_delta_rule(*a, lib=lib, **k)
+
+    caught = []
+    for pname, pin in oracle_pins.GDN_PINS.items():
+        try:
+            ok, _ = pin(Orc)
+        except (ValueError, AssertionError, FloatingPointError):
+            ok = False
+        if not ok:
+            caught.append(pname)
+    assert caught, f"mutant {name} passed every delta-rule pin"

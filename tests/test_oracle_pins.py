@@ -47,3 +47,13 @@ class _BwdOrc:
 def test_backward_pin(name):
     ok, detail = oracle_pins.BWD_PINS[name](_BwdOrc)
     assert ok, f"pin {name} failed: {detail}"
+
+
+class _GdnOrc:
+    gated_delta_rule = staticmethod(oracle.gated_delta_rule)
+
+
+@pytest.mark.parametrize("name", sorted(oracle_pins.GDN_PINS))
+def test_gated_delta_rule_pin(name):
+    ok, detail = oracle_pins.GDN_PINS[name](_GdnOrc)
+    assert ok, f"pin {name} failed: {detail}"
