@@ -271,6 +271,38 @@ int ssd_scan_prefill_backward(const void *x, const float *dt, const float *A, co
                               int P, int N, int G, int chunk, ssd_dtype_t dtype, void *workspace,
                               size_t workspace_bytes, void *stream);
 
+/*
+ * Gated delta rule scan: the delta-rule family of Recurrence Scan (poot docs:
+ * gated delta rule layers replace attention by a per-head state matrix that
+ * each token updates and that is carried from step to step; the scan returns
+ * the output and the carried state, "One equation, one packed result"; "The
+ * schedule": a streaming kernel with a workgroup per head and block of state
+ * columns, the state on chip, a runtime loop over tokens, and a state column's
+ * rows shared by several lanes that add their partial dot products each token).
+ * The page writes no equation; this is the published gated delta rule, per
+ * sequence and head h (q, k read group g = floor(h*G/H)), state S [V][K]:
+ *
+ *     a_t = exp(g_t);   S_t = a_t S_{t-1} + beta_t (v_t - a_t S_{t-1} k_t) k_t^T
+ *     o_t = S_t q_t
+ *
+ *   q, k     [T][G][K]       dtype    query and key (already normalised/scaled:
+ *                                     the library applies no L2 norm or scale)
+ *   v        [T][H][V]       dtype
+ *   g        [T][H]          float32  log-gate, <= 0 (not checked)
+ *   beta     [T][H]          float32  write strength (after its activation)
+ *   h0       [nseq][H][V][K] float32  initial states, or NULL for zeros
+ *   o        [T][H][V]       float32  output (must not alias any input)
+ *   h_out    [nseq][H][V][K] float32  final states, or NULL; may be h0
+ *   cu_seqlens  device int32 [nseq+1] or NULL (dense: nseq sequences of T/nseq)
+ * Supported: K in {64,128,256}, V a multiple of 16 up to 1024, H % G == 0.
+ * Arithmetic and the state are float32.  No workspace.  Splitting a sequence
+ * and passing h_out on as h0 gives the same result as one call.
+ */
+int ssd_gated_delta_rule(const void *q, const void *k, const void *v, const float *g,
+                         const float *beta, const float *h0, float *o, float *h_out,
+                         const int32_t *cu_seqlens, int nseq, int64_t total_tokens, int H, int G,
+                         int K, int V, ssd_dtype_t dtype, void *stream);
+
 /* Message for the last non-zero return on the calling thread ("" if none). */
 const char *ssd_last_error(void);
 

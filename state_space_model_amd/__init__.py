@@ -35,3 +35,8 @@ def selective_scan(*args, **kwargs):
 def prefill_backward(*args, **kwargs):
     from . import ssd
     return ssd.prefill_backward(*args, **kwargs)
+
+
+def gated_delta_rule(*args, **kwargs):
+    from . import ssd
+    return ssd.gated_delta_rule(*args, **kwargs)

@@ -278,6 +278,29 @@ int ssd_scan_prefill_backward(const void *x, const float *dt, const float *A, co
   return SSD_OK;
 }
 
+int ssd_gated_delta_rule(const void *q, const void *k, const void *v, const float *g,
+                         const float *beta, const float *h0, float *o, float *h_out,
+                         const int32_t *cu_seqlens, int nseq, int64_t total_tokens, int H, int G,
+                         int K, int V, ssd_dtype_t dtype, void *stream) {
+  g_err[0] = 0;
+  if (dtype != SSD_F32 && dtype != SSD_BF16) return fail(SSD_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (nseq < 1) return fail(SSD_ERR_INVALID_ARG, "nseq must be >= 1 (got %d)", nseq);
+  if (total_tokens < 0 || total_tokens > INT32_MAX) return fail(SSD_ERR_INVALID_ARG, "total_tokens %lld out of range", (long long)total_tokens);
+  if (H < 1 || G < 1 || H % G != 0) return fail(SSD_ERR_INVALID_ARG, "need H >= 1, G >= 1, H %% G == 0 (H=%d G=%d)", H, G);
+  if (!(K == 64 || K == 128 || K == 256)) return fail(SSD_ERR_UNSUPPORTED, "key dim K=%d not in {64,128,256}", K);
+  if (V < 16 || V > 1024 || V % 16 != 0) return fail(SSD_ERR_UNSUPPORTED, "value dim V=%d: need 16 <= V <= 1024, V %% 16 == 0", V);
+  if (H > 65535 || nseq > 65535) return fail(SSD_ERR_UNSUPPORTED, "H or nseq above 65535");
+  if (!cu_seqlens && total_tokens % nseq != 0)
+    return fail(SSD_ERR_INVALID_ARG, "dense batch: total_tokens %lld not divisible by nseq %d", (long long)total_tokens, nseq);
+  if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !o))
+    return fail(SSD_ERR_INVALID_ARG, "null q/k/v/g/beta/o pointer");
+  ssd::GdnArgs a{q, k, v, g, beta, h0, o, h_out, cu_seqlens, nseq, total_tokens, H, G, K, V,
+                 dtype == SSD_BF16, stream};
+  hipError_t e = ssd::launch_gated_delta_rule(a);
+  if (e != hipSuccess) return fail(SSD_ERR_HIP, "HIP error: %s", hipGetErrorString(e));
+  return SSD_OK;
+}
+
 const char *ssd_last_error(void) { return g_err; }
 
 }  // extern "C"

@@ -120,6 +120,20 @@ S6Plan s6_plan(int batch, int L, int dim, int N);
 size_t s6_workspace(int batch, int L, int dim, int N);
 hipError_t launch_selective_scan(const S6Args &a);
 
+// Gated delta rule (ssd_gdn.hip).
+struct GdnArgs {
+  const void *q, *k, *v;
+  const float *g, *beta, *h0;
+  float *o, *h_out;
+  const int32_t *cu;
+  int nseq;
+  int64_t T;
+  int H, G, K, V;
+  bool bf16;
+  void *stream;
+};
+hipError_t launch_gated_delta_rule(const GdnArgs &a);
+
 // Decode-layer operations around the scan (ssd_layer.hip).
 hipError_t launch_conv1d_step(const void *u, float *state, const float *w, const float *bias,
                               bool silu, void *out, int batch, int channels, int width,

@@ -173,3 +173,30 @@ def cotangents(T, nseq, H, P, N, seed, dtype="bf16", dh_out=True):
         dy = round_bf16(dy)
     dh = rng.normal(0.0, 0.1, (nseq, H, N, P)).astype(np.float32) if dh_out else None
     return dy, dh
+
+
+# Gated delta rule: a layer shape of the family Recurrence Scan names (its GDN
+# layers), 32 value heads over 16 query/key groups, K = V = 128 (the pages give
+# no shape; synthetic values stand in for a trained layer's activations).
+GDN_W = dict(name="gdn-layer-prefill", batch=1, L=4096, H=32, G=16, K=128, V=128, dtype="bf16")
+
+
+def gdn_inputs(lengths, H, G, K, V, seed, dtype="bf16", h0=False):
+    """Seeded gated-delta-rule inputs for packed sequences: q ~ N(0,1)/sqrt(K),
+    k = unit-norm N(0,1) rows, v ~ N(0,1) (q, k, v rounded to bf16 values for
+    dtype "bf16" after normalising), gate g = log U[0.9, 1], beta = sigmoid of
+    N(0,1), h0 ~ N(0, 0.1^2) when asked.  Returns a dict with cu_seqlens."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lengths = np.asarray(lengths, dtype=np.int64)
+    T = int(lengths.sum())
+    q = (rng.standard_normal((T, G, K)) / np.sqrt(K)).astype(np.float32)
+    k = rng.standard_normal((T, G, K))
+    k = (k / np.maximum(np.linalg.norm(k, axis=-1, keepdims=True), 1e-6)).astype(np.float32)
+    v = rng.standard_normal((T, H, V)).astype(np.float32)
+    g = np.log(rng.uniform(0.9, 1.0, (T, H))).astype(np.float32)
+    beta = (1.0 / (1.0 + np.exp(-rng.standard_normal((T, H))))).astype(np.float32)
+    hz = rng.normal(0.0, 0.1, (len(lengths), H, V, K)).astype(np.float32) if h0 else None
+    if dtype == "bf16":
+        q, k, v = round_bf16(q), round_bf16(k), round_bf16(v)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    return dict(q=q, k=k, v=v, g=g, beta=beta, h0=hz, cu_seqlens=cu)

@@ -21,7 +21,8 @@ ERRORS = {0: "SSD_OK", -1: "SSD_ERR_INVALID_ARG", -2: "SSD_ERR_UNSUPPORTED",
 EXPORTS = ("ssd_scan_prefill_workspace", "ssd_scan_prefill", "ssd_scan_prefill_stages",
            "ssd_step", "ssd_step_multi", "ssd_conv1d_step", "ssd_gated_rmsnorm",
            "ssd_decode_layer_step", "ssd_selective_scan_workspace", "ssd_selective_scan",
-           "ssd_scan_prefill_backward_workspace", "ssd_scan_prefill_backward", "ssd_last_error")
+           "ssd_scan_prefill_backward_workspace", "ssd_scan_prefill_backward",
+           "ssd_gated_delta_rule", "ssd_last_error")
 
 _lib = None
 
@@ -73,6 +74,8 @@ def load(path=LIB_PATH):
     lib.ssd_scan_prefill_backward.argtypes = [vp] * 17 + [i32, i64, i32, i32, i32, i32, i32, i32,
                                                           vp, sz, vp]
     lib.ssd_scan_prefill_backward.restype = i32
+    lib.ssd_gated_delta_rule.argtypes = [vp] * 9 + [i32, i64, i32, i32, i32, i32, i32, vp]
+    lib.ssd_gated_delta_rule.restype = i32
     lib.ssd_last_error.argtypes = []
     lib.ssd_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -268,6 +271,51 @@ def prefill_backward(x, dt, A, B, C, D, dy, h0=None, dh_out=None, chunk=256, cu_
         return Prepared(lib.ssd_scan_prefill_backward, args, None, keep), g
     _check(lib.ssd_scan_prefill_backward(*args, _stream()))
     return g
+
+
+def gated_delta_rule(q, k, v, g, beta, h0=None, cu_seqlens=None, *, nseq=None, o=None,
+                     h_out=None, prepare=False):
+    """Gated delta rule scan.  q, k [T,G,K]; v [T,H,V] (float32 or bfloat16,
+    all the same); g, beta [T,H] float32; h0 [nseq,H,V,K] float32 or None;
+    cu_seqlens int32 [nseq+1] or None (dense: ``nseq`` sequences of T/nseq).
+    Returns (o [T,H,V] float32, h_out [nseq,H,V,K] float32); with
+    ``prepare=True`` nothing runs and (Prepared, o, h_out) is returned."""
+    T, G, K = q.shape
+    H, V = v.shape[1], v.shape[2]
+    dev = q.device
+    _need(q, "q", dev=dev)
+    code = _dtype_code(q)
+    for t, n in ((k, "k"), (v, "v")):
+        _need(t, n, q.dtype, dev)
+    for t, n in ((g, "g"), (beta, "beta")):
+        _need(t, n, torch.float32, dev)
+    if tuple(k.shape) != (T, G, K) or v.shape[0] != T:
+        raise ValueError("k must be [T,G,K] and v [T,H,V]")
+    if tuple(g.shape) != (T, H) or tuple(beta.shape) != (T, H):
+        raise ValueError("g and beta must be [T,H]")
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+        nseq = cu_seqlens.numel() - 1
+    elif nseq is None:
+        nseq = 1
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, dev)
+        if tuple(h0.shape) != (nseq, H, V, K):
+            raise ValueError(f"h0 must be [{nseq},{H},{V},{K}]")
+    if o is None:
+        o = torch.empty((T, H, V), dtype=torch.float32, device=dev)
+    if h_out is None:
+        h_out = torch.empty((nseq, H, V, K), dtype=torch.float32, device=dev)
+    _need(o, "o", torch.float32, dev)
+    _need(h_out, "h_out", torch.float32, dev)
+    lib = load()
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o), _ptr(h_out),
+            _ptr(cu_seqlens), nseq, T, H, G, K, V, code)
+    if prepare:
+        keep = (q, k, v, g, beta, h0, o, h_out, cu_seqlens)
+        return Prepared(lib.ssd_gated_delta_rule, args, None, keep), o, h_out
+    _check(lib.ssd_gated_delta_rule(*args, _stream()))
+    return o, h_out
 
 
 def step(x, dt, A, B, C, D, h, y=None, prepare=False):

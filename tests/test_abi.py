@@ -194,6 +194,27 @@ def test_backward_rejects_before_launch(kw, code, frag):
     assert rc == code and frag in msg, (rc, msg)
 
 
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(K=96), -2, "key dim"),
+    (dict(V=20), -2, "value dim"),
+    (dict(V=2048), -2, "value dim"),
+    (dict(H=6, G=4), -1, "H % G"),
+    (dict(nseq=0), -1, "nseq"),
+    (dict(T=65, nseq=2), -1, "divisible"),
+    (dict(q=None), -1, "null"),
+    (dict(dtype=2), -1, "dtype"),
+])
+def test_gated_delta_rule_rejects_before_launch(kw, code, frag):
+    lib = ssd.load()
+    a = dict(q=1, nseq=1, T=64, H=4, G=2, K=128, V=64, dtype=0)
+    a.update(kw)
+    p = ctypes.c_void_p
+    qp = None if a["q"] is None else p(a["q"])
+    rc = lib.ssd_gated_delta_rule(qp, p(1), p(1), p(1), p(1), None, p(1), None, None, a["nseq"],
+                                  a["T"], a["H"], a["G"], a["K"], a["V"], a["dtype"], None)
+    assert rc == code and frag in lib.ssd_last_error().decode()
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros(64, 4, 16)
