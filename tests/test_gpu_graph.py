@@ -46,3 +46,52 @@ def test_graph_replays_equal_eager():
         once()      # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(y, ref[0]) and torch.equal(h, ref[1])
+
+
+def test_graph_backward_and_delta_rule_replays_equal_eager():
+    """Forward + backward of the prefill and a delta-rule scan in one HIP graph
+    (the backward's reductions are fixed-order, so replays are bitwise equal)."""
+    import torch
+    from state_space_model_amd import ssd
+    log("graph: prefill forward + backward (varlen, bf16, 4 heads in 2 groups) + delta rule, "
+        "4 replays")
+    d = inputs.prefill_inputs(4, 64, 64, 2, [300, 77], 33, dtype="bf16", h0=True)
+    t = dev_inputs(d, "bf16")
+    T = int(d["cu_seqlens"][-1])
+    dy, dh = inputs.cotangents(T, 2, 4, 64, 64, 34, "bf16")
+    dyt = torch.from_numpy(dy).cuda().to(torch.bfloat16)
+    dht = torch.from_numpy(dh).cuda()
+    args = (t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"])
+    run_f, y, h = ssd.prefill(*args, t["h0"], chunk=64, cu_seqlens=t["cu_seqlens"], prepare=True)
+    run_b, g = ssd.prefill_backward(*args, dyt, t["h0"], dht, chunk=64,
+                                    cu_seqlens=t["cu_seqlens"], prepare=True)
+    dg = inputs.gdn_inputs([90, 40], 4, 2, 128, 32, 35, dtype="bf16", h0=True)
+    gt = lambda a, o=None: torch.from_numpy(np.ascontiguousarray(a)).cuda() if o is None \
+        else torch.from_numpy(np.ascontiguousarray(a)).cuda().to(o)
+    bf = torch.bfloat16
+    run_g, o, ho = ssd.gated_delta_rule(gt(dg["q"], bf), gt(dg["k"], bf), gt(dg["v"], bf),
+                                        gt(dg["g"]), gt(dg["beta"]), gt(dg["h0"]),
+                                        gt(dg["cu_seqlens"].astype(np.int32)), prepare=True)
+    outs = [y, h, o, ho] + [g[k] for k in sorted(g)]
+
+    def once():
+        run_f()
+        run_b()
+        run_g()
+
+    once()
+    torch.cuda.synchronize()
+    ref = [a.clone() for a in outs]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        once()
+    for r in range(4):
+        for a in outs:
+            a.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert all(torch.equal(a, b) for a, b in zip(outs, ref)), r
+        once()      # eager work between replays
+        torch.cuda.synchronize()
+        assert all(torch.equal(a, b) for a, b in zip(outs, ref)), r
