@@ -486,6 +486,42 @@ def train_only(args):
                       "forward_backward_us": round(ms * 1e3, 2)}), flush=True)
 
 
+def long_context_bench(args, torch, inputs, ssd, dev):
+    """The long-context packed batch (8 sequences of 1K-32K tokens, 80 heads,
+    each with its own h0, bf16): the whole prefill at every chunk size, from
+    HIP-graph replays, against the method's algorithmic bytes."""
+    wl = inputs.WORKLOADS[4]
+    d = inputs.workload_inputs(4)
+    T = d["x"].shape[0]
+    nseq = len(d["cu_seqlens"]) - 1
+    op = torch.bfloat16
+    t = lambda a, dt=None: torch.from_numpy(np.ascontiguousarray(a)).to(dev) if dt is None \
+        else torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(dt)
+    args_ = (t(d["x"], op), t(d["dt"]), t(d["A"]), t(d["B"], op), t(d["C"], op), t(d["D"]),
+             t(d["h0"]))
+    cu = t(d["cu_seqlens"].astype(np.int32))
+    e = 2
+    nbytes = T * (wl.H * wl.P * (e + 4) + 2 * wl.G * wl.N * e + 4 * wl.H) + \
+        2 * nseq * wl.H * wl.N * wl.P * 4 + 8 * wl.H
+    out = {"workload": wl.name, "tokens": T,
+           "lengths": [int(v) for v in np.diff(d["cu_seqlens"])], "chunks": {}}
+    y = torch.empty((T, wl.H, wl.P), dtype=torch.float32, device=dev)
+    h = torch.empty((nseq, wl.H, wl.N, wl.P), dtype=torch.float32, device=dev)
+    for q in wl.chunks:
+        run, _, _ = ssd.prefill(*args_, chunk=q, cu_seqlens=cu, y=y, h_out=h, prepare=True)
+        run()
+        torch.cuda.synchronize()
+        ms = graph_ms(torch, run, reps=3, per_graph=2)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out["chunks"][str(q)] = {"us": round(ms * 1e3, 1),
+                                 "tokens_per_s": round(T / (ms * 1e-3), 1),
+                                 "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+        del run
+        torch.cuda.empty_cache()
+    log(args, f"long-context prefill: {out['chunks']}")
+    return out
+
+
 def selective_scan_bench(torch, inputs, ssd, dev):
     """The Mamba-1 selective scan at COREY's W1 shape (batch 1, d_inner 1024,
     L 4096, d_state 16, float16), whole scan from HIP-graph replays."""
@@ -662,6 +698,7 @@ def main():
                     "tokens_per_s": round(T / (cold_us * 1e-6), 1)}
 
     large = None if args.no_large else prefill_large(args, torch, inputs, ssd, dev)
+    longctx = None if args.no_large else long_context_bench(args, torch, inputs, ssd, dev)
 
     # ---- decode workload (the decode half of the metric)
     w3 = inputs.WORKLOADS[3]
@@ -750,6 +787,7 @@ def main():
         "kernels": kernels,
         "prefill_cold_cache": prefill_cold,
         "prefill_2p7b_layer": large,
+        "prefill_long_context_varlen": longctx,
         "decode": decode,
         "decode_multi_step": decode_multi,
         "decode_layer_step": layer,
