@@ -613,7 +613,7 @@ def main():
         summarize(args.summarize)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this library has no "
               "multi-GPU path", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
