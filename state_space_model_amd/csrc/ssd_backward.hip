@@ -329,22 +329,26 @@ __global__ __launch_bounds__(MAXT) void k_bwd_scan(
             w[4 + r] = m[4 + r] * d1[r] * dti;
             csum += w[r] + w[4 + r];
           }
-          // row sums over the 16 columns of the lane group: a reduce-scatter in
-          // which lane col ends with the total of value (col>>1) of the 8
+          // row sums over the 16 columns of the lane group: a reduce-scatter
+          // with DPP moves inside the 16-lane row, pairing lane col with
+          // 15 - col (row_mirror), then 7 - col within each half
+          // (row_half_mirror), then col ^ 2 and col ^ 1 (quad_perm); at each
+          // step the lane keeps one half of its values and adds the partner's
+          // copy of that half.  Lane col ends with the total of value col >> 1.
           const bool b8 = col & 8, b4 = col & 4, b2 = col & 2;
           float w4[4], w2[2];
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
             const float snd = b8 ? w[k] : w[k + 4];
-            w4[k] = (b8 ? w[k + 4] : w[k]) + __shfl_xor(snd, 8, 64);
+            w4[k] = (b8 ? w[k + 4] : w[k]) + dpp_mov<0x140>(snd);
           }
 #pragma unroll
           for (int k = 0; k < 2; ++k) {
             const float snd = b4 ? w4[k] : w4[k + 2];
-            w2[k] = (b4 ? w4[k + 2] : w4[k]) + __shfl_xor(snd, 4, 64);
+            w2[k] = (b4 ? w4[k + 2] : w4[k]) + dpp_mov<0x141>(snd);
           }
-          float w1 = (b2 ? w2[1] : w2[0]) + __shfl_xor(b2 ? w2[0] : w2[1], 2, 64);
-          w1 += __shfl_xor(w1, 1, 64);
+          float w1 = (b2 ? w2[1] : w2[0]) + dpp_mov<0x4E>(b2 ? w2[0] : w2[1]);
+          w1 += dpp_mov<0xB1>(w1);
           if ((col & 1) == 0) {
             const int idx = col >> 1;  // value index: rows 4 grp + idx, or 16 + 4 grp + idx - 4
             const int t = jb + (idx < 4 ? 4 * grp + idx : 16 + 4 * grp + idx - 4);

@@ -166,6 +166,14 @@ __device__ __forceinline__ bf16x8 vscale(bf16x8 v, float s) { return cvt_bf8(cvt
 __device__ __forceinline__ f4 vscale(f4 v, float s) { return v * s; }
 template <typename V> __device__ __forceinline__ V vzero() { return __builtin_bit_cast(V, i4v{0, 0, 0, 0}); }
 
+// A float from another lane of the same 16-lane DPP row (CTRL: a DPP control
+// code, e.g. 0xB1 quad_perm [1,0,3,2], 0x4E quad_perm [2,3,0,1], 0x140
+// row_mirror, 0x141 row_half_mirror, 0x128 row_ror:8).  One VALU move.
+template <int CTRL> __device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
 }  // namespace ssd
 
 namespace ssd {

@@ -25,11 +25,6 @@ namespace ssd {
 constexpr int kGdnSplit = 16;                      // lanes per state row
 constexpr int kGdnRows = 256 / kGdnSplit;          // rows per workgroup
 
-template <int CTRL> __device__ __forceinline__ float dpp_mov(float v) {
-  return __builtin_bit_cast(float,
-                            __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
-}
-
 // Sum over the 16 lanes of a DPP row, left in every lane: xor 1 and xor 2
 // inside each quad (quad_perm [1,0,3,2], [2,3,0,1]), then lane i with 7 - i
 // (row_half_mirror: quad 0 with 1, quad 2 with 3) and lane i with 15 - i
