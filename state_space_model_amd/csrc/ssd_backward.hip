@@ -418,10 +418,10 @@ __global__ __launch_bounds__(MAXT) void k_bwd_scan(
 
 // ----------------------------------------------------- backward state pass
 // Per (sequence, head), per 4 state elements: walk the chunks last to first
-// with g = dH_c; write dH_c (operand type), the wave's share of <dH_c, H_c>
-// (H_c = the state entering chunk c+1, or the final state, both float32: the
-// dot enters dz of every row of the chunk), then g <- 2^(s_end) g + Sb_c.  The
-// last g is dh0.
+// with g = dH_c; write dH_c (operand type), each 16-lane row's share of
+// <dH_c, H_c> (H_c = the state entering chunk c+1, or the final state, both
+// float32: the dot enters dz of every row of the chunk; summed in the row by
+// DPP moves), then g <- 2^(s_end) g + Sb_c.  The last g is dh0.
 template <typename T>
 __global__ __launch_bounds__(256) void k_state_pass_bwd(
     const float *__restrict__ Sb, const float *__restrict__ s_ws, const int *__restrict__ seq_off,
@@ -433,7 +433,7 @@ __global__ __launch_bounds__(256) void k_state_pass_bwd(
   const int tid = blockIdx.x * blockDim.x + threadIdx.x;
   const int e = tid * 4;
   if (e >= NP) return;  // NP is a multiple of 256: whole waves leave
-  const int npw = NP / 256, wid = tid >> 6, lane = threadIdx.x & 63;
+  const int npr = NP / 64, rid = tid >> 4, lane16 = threadIdx.x & 15;
   int c0, c1;
   if (cmap.L > 0) {
     const int cps = (cmap.L + Q - 1) / Q;
@@ -463,9 +463,11 @@ __global__ __launch_bounds__(256) void k_state_pass_bwd(
       if (cb - u >= c0) {  // wave-uniform
         const size_t ch = (size_t)(cb - u) * H + hd;
         float d = gv[0] * hend[0] + gv[1] * hend[1] + gv[2] * hend[2] + gv[3] * hend[3];
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) d += __shfl_xor(d, off, 64);
-        if (lane == 0) epart[ch * npw + wid] = d;
+        d += dpp_mov<0xB1>(d);   // xor 1
+        d += dpp_mov<0x4E>(d);   // xor 2
+        d += dpp_mov<0x141>(d);  // lane i with 7 - i
+        d += dpp_mov<0x140>(d);  // lane i with 15 - i
+        if (lane16 == 0) epart[ch * npr + rid] = d;
         st4T(dHc + ch * NP + e, gv);
         const float a = __builtin_amdgcn_exp2f(fminf(sl[u], 0.f));
 #pragma unroll
@@ -631,7 +633,7 @@ BwdLayout bwd_layout(int64_t T, int nseq, int H, int P, int N, int G, int Q, int
   L.dHc = off;
   off = align_up(off + (size_t)elem * nc * H * NP, 256);
   L.epart = off;
-  off = align_up(off + 4 * nc * H * (NP / 256), 256);
+  off = align_up(off + 4 * nc * H * (NP / 64), 256);
   L.rows = off;  // q, cv, r, dyx, then rs for two parts
   off = align_up(off + 4 * 6 * nc * H * Q, 256);
   L.dApart = off;
@@ -752,7 +754,7 @@ static hipError_t run_backward(const BwdArgs &a) {
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_bwd_ddt, dim3((unsigned)nc * f.H), dim3(f.Q < 64 ? 64 : f.Q), 0, st,
                        bwd_rows(ws, L, nc, f.H, f.Q), f.Q >= 256 ? 2 : 1,
-                       reinterpret_cast<const float *>(ws + L.fwd.dt), epart, NP / 256, f.A, cmap,
+                       reinterpret_cast<const float *>(ws + L.fwd.dt), epart, NP / 64, f.A, cmap,
                        f.H, f.Q, a.ddt, dApart, dDpart);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -67,7 +67,7 @@ struct BwdLayout {
   size_t hfin;    // f32 [nseq][H][N][P]  final states (the forward recompute)
   size_t hin32;   // f32 [nc][H][N][P]    state entering each chunk, float32
   size_t dHc;     // T   [nc][H][N][P]    dL/d(state leaving chunk c)
-  size_t epart;   // f32 [nc][H][NP/256]  wave partials of <dH_c, H_c>
+  size_t epart;   // f32 [nc][H][NP/64]   16-lane-row partials of <dH_c, H_c>
   size_t rows;             // f32 6 x [nc][H][Q]  per-row terms of dz (q, cv, r, dyx, rs x 2)
   size_t dApart, dDpart;   // f32 [nc][H]
   size_t dBh, dCh;         // f32 [T][H/hb][N]  partial dB, dC per block of hb heads

@@ -153,7 +153,7 @@ def test_backward_workspace_size():
     # the forward's workspace, then: final states (f32), states entering each chunk
     # (f32), dH per chunk (bf16), the <dH, H> partials, six per-row arrays,
     # dA/dD partials, per-head dB and dC
-    extra = (24 * 128 * 64 * 4 + nc * 24 * 128 * 64 * (4 + 2) + nc * 24 * 32 * 4
+    extra = (24 * 128 * 64 * 4 + nc * 24 * 128 * 64 * (4 + 2) + nc * 24 * 128 * 4
              + 6 * nc * 24 * 256 * 4 + 2 * nc * 24 * 4 + 2 * 4096 * 24 * 128 * 4)
     assert fwd + extra <= n1 <= fwd + extra + 16 * 256
     assert w(4096, 1, 24, 64, 128, 24, 256, 1) < n1       # H == G: no per-head dB/dC
