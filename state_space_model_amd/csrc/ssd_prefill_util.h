@@ -63,13 +63,25 @@ __device__ __forceinline__ void dma_tile(T *tile, const T *__restrict__ src, siz
   constexpr int VN = 16 / sizeof(T);
   const int total = rows * SPR;
   const int lane = threadIdx.x & 63;
-  for (int base = wave * 64; base < total; base += nw * 64) {
-    const int s = base + lane, r = s / SPR, v = s % SPR;
-    const void *g = (s < total && r < valid && v < DATA) ? (const void *)(src + r * stride + v * VN)
-                                                       : (const void *)g_zero16;
+  // slot s = base + lane sits at row r = s / SPR, vector v = s % SPR; both are
+  // advanced by the wave-uniform step instead of divided again per request
+  const int step = nw * 64;
+  const int dr = step / SPR, dv = step - dr * SPR;
+  const int s0 = wave * 64 + lane;
+  int r = s0 / SPR, v = s0 - r * SPR;
+  const int lim = min(valid, rows);  // slots past the tile end have r >= rows
+  const T *zero = reinterpret_cast<const T *>(g_zero16);
+  for (int base = wave * 64; base < total; base += step) {
+    const T *g = (r < lim && v < DATA) ? src + (size_t)r * stride + v * VN : zero;
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
                                      (__attribute__((address_space(3))) void *)(tile + base * VN),
                                      16, 0, 0);
+    v += dv;
+    r += dr;
+    if (v >= SPR) {
+      v -= SPR;
+      ++r;
+    }
   }
 }
 __host__ __device__ constexpr int tile_slots(int rows, int spr) { return (rows * spr + 63) / 64 * 64; }
