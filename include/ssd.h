@@ -303,6 +303,32 @@ int ssd_gated_delta_rule(const void *q, const void *k, const void *v, const floa
                          const int32_t *cu_seqlens, int nseq, int64_t total_tokens, int H, int G,
                          int K, int V, ssd_dtype_t dtype, void *stream);
 
+/*
+ * The same gated delta rule in chunks of 64 tokens, with the work on MFMA:
+ * within a chunk the recurrence is regrouped exactly into a unit
+ * lower-triangular system (I + A) D = diag(beta) V - diag(beta gamma) K S_0^T
+ * for the chunk's write vectors D, whose state-free part (U, W) is solved for
+ * every chunk at once, and three products per chunk carry the state: D = U -
+ * W S_0^T, O = diag(gamma) Q S_0^T + P D and S_C = gamma_C S_0 + D~^T K, with
+ * gamma the chunk-local cumulative gate, A_tj = beta_t (gamma_t/gamma_j)
+ * k_t.k_j and P_tj = (gamma_t/gamma_j) q_t.k_j (j < t, resp. j <= t).
+ * Arguments as ssd_gated_delta_rule(), plus
+ *   workspace / workspace_bytes   device scratch of at least
+ *            ssd_gated_delta_rule_chunked_workspace(...) bytes (256-aligned)
+ * Supported: K in {64,128}, V a multiple of 16 with V + K <= 256, H % G == 0
+ * (the workspace query returns 0 for other shapes: use the streaming call).
+ * Arithmetic float32; with bfloat16 operands the state and D enter the
+ * products as bfloat16 pairs (hi + lo) and U, W, P are held in bfloat16.
+ * h_out may be h0.  Errors as ssd_gated_delta_rule(), and SSD_ERR_WORKSPACE.
+ */
+size_t ssd_gated_delta_rule_chunked_workspace(int64_t total_tokens, int nseq, int H, int K, int V,
+                                              ssd_dtype_t dtype);
+int ssd_gated_delta_rule_chunked(const void *q, const void *k, const void *v, const float *g,
+                                 const float *beta, const float *h0, float *o, float *h_out,
+                                 const int32_t *cu_seqlens, int nseq, int64_t total_tokens, int H,
+                                 int G, int K, int V, ssd_dtype_t dtype, void *workspace,
+                                 size_t workspace_bytes, void *stream);
+
 /* Message for the last non-zero return on the calling thread ("" if none). */
 const char *ssd_last_error(void);
 

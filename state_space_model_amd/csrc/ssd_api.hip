@@ -278,11 +278,9 @@ int ssd_scan_prefill_backward(const void *x, const float *dt, const float *A, co
   return SSD_OK;
 }
 
-int ssd_gated_delta_rule(const void *q, const void *k, const void *v, const float *g,
-                         const float *beta, const float *h0, float *o, float *h_out,
-                         const int32_t *cu_seqlens, int nseq, int64_t total_tokens, int H, int G,
-                         int K, int V, ssd_dtype_t dtype, void *stream) {
-  g_err[0] = 0;
+static int gdn_check(const void *q, const void *k, const void *v, const float *g,
+                     const float *beta, float *o, const int32_t *cu_seqlens, int nseq,
+                     int64_t total_tokens, int H, int G, int K, int V, ssd_dtype_t dtype) {
   if (dtype != SSD_F32 && dtype != SSD_BF16) return fail(SSD_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
   if (nseq < 1) return fail(SSD_ERR_INVALID_ARG, "nseq must be >= 1 (got %d)", nseq);
   if (total_tokens < 0 || total_tokens > INT32_MAX) return fail(SSD_ERR_INVALID_ARG, "total_tokens %lld out of range", (long long)total_tokens);
@@ -294,9 +292,47 @@ int ssd_gated_delta_rule(const void *q, const void *k, const void *v, const floa
     return fail(SSD_ERR_INVALID_ARG, "dense batch: total_tokens %lld not divisible by nseq %d", (long long)total_tokens, nseq);
   if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !o))
     return fail(SSD_ERR_INVALID_ARG, "null q/k/v/g/beta/o pointer");
+  return SSD_OK;
+}
+
+int ssd_gated_delta_rule(const void *q, const void *k, const void *v, const float *g,
+                         const float *beta, const float *h0, float *o, float *h_out,
+                         const int32_t *cu_seqlens, int nseq, int64_t total_tokens, int H, int G,
+                         int K, int V, ssd_dtype_t dtype, void *stream) {
+  g_err[0] = 0;
+  const int rc = gdn_check(q, k, v, g, beta, o, cu_seqlens, nseq, total_tokens, H, G, K, V, dtype);
+  if (rc != SSD_OK) return rc;
   ssd::GdnArgs a{q, k, v, g, beta, h0, o, h_out, cu_seqlens, nseq, total_tokens, H, G, K, V,
                  dtype == SSD_BF16, stream};
   hipError_t e = ssd::launch_gated_delta_rule(a);
+  if (e != hipSuccess) return fail(SSD_ERR_HIP, "HIP error: %s", hipGetErrorString(e));
+  return SSD_OK;
+}
+
+size_t ssd_gated_delta_rule_chunked_workspace(int64_t total_tokens, int nseq, int H, int K, int V,
+                                              ssd_dtype_t dtype) {
+  if (total_tokens < 0 || total_tokens > INT32_MAX || nseq < 1 || H < 1) return 0;
+  if (dtype != SSD_F32 && dtype != SSD_BF16) return 0;
+  if (!ssd::gdn_chunk_supported(K, V)) return 0;
+  return ssd::gdn_chunk_layout(total_tokens, nseq, H, K, V, dtype == SSD_BF16 ? 2 : 4).total;
+}
+
+int ssd_gated_delta_rule_chunked(const void *q, const void *k, const void *v, const float *g,
+                                 const float *beta, const float *h0, float *o, float *h_out,
+                                 const int32_t *cu_seqlens, int nseq, int64_t total_tokens, int H,
+                                 int G, int K, int V, ssd_dtype_t dtype, void *workspace,
+                                 size_t workspace_bytes, void *stream) {
+  g_err[0] = 0;
+  const int rc = gdn_check(q, k, v, g, beta, o, cu_seqlens, nseq, total_tokens, H, G, K, V, dtype);
+  if (rc != SSD_OK) return rc;
+  if (!ssd::gdn_chunk_supported(K, V))
+    return fail(SSD_ERR_UNSUPPORTED, "chunked form: need K in {64,128}, V %% 16 == 0, V + K <= 256 (K=%d V=%d)", K, V);
+  const size_t need = ssd::gdn_chunk_layout(total_tokens, nseq, H, K, V, dtype == SSD_BF16 ? 2 : 4).total;
+  if (!workspace || workspace_bytes < need)
+    return fail(SSD_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
+  ssd::GdnArgs a{q, k, v, g, beta, h0, o, h_out, cu_seqlens, nseq, total_tokens, H, G, K, V,
+                 dtype == SSD_BF16, stream, workspace};
+  hipError_t e = ssd::launch_gdn_chunked(a);
   if (e != hipSuccess) return fail(SSD_ERR_HIP, "HIP error: %s", hipGetErrorString(e));
   return SSD_OK;
 }

@@ -131,8 +131,25 @@ struct GdnArgs {
   int H, G, K, V;
   bool bf16;
   void *stream;
+  void *workspace = nullptr;  // chunked form only
 };
 hipError_t launch_gated_delta_rule(const GdnArgs &a);
+
+// Chunked gated delta rule (ssd_gdn_chunk.hip): supported shapes, workspace
+// layout (byte offsets, 256-aligned) and the launch.
+struct GdnLayout {
+  int64_t nc_max;        // upper bound on the chunks of 64 tokens
+  size_t info, seq_off;  // chunk map of a packed batch
+  size_t U, W, P;        // T [T][H][V], [T][H][K], [T][H][64]
+  size_t total;
+};
+bool gdn_chunk_supported(int K, int V);
+GdnLayout gdn_chunk_layout(int64_t T, int nseq, int H, int K, int V, int elem);
+hipError_t launch_gdn_chunked(const GdnArgs &a);
+
+// Chunk map of a packed batch for chunk length Q (ssd_prefill.hip).
+hipError_t launch_chunk_map(const int32_t *cu, int nseq, int64_t T, int Q, int nc, int4 *info,
+                            int *seq_off, hipStream_t st);
 
 // Decode-layer operations around the scan (ssd_layer.hip).
 hipError_t launch_conv1d_step(const void *u, float *state, const float *w, const float *bias,

@@ -120,6 +120,13 @@ __global__ __launch_bounds__(256) void k_chunk_map(const int32_t *__restrict__ c
   if (c < nc_max && threadIdx.x == 0) info_out[c] = ci.x < 0 ? make_int4(0, 0, 0, 0) : ci;
 }
 
+hipError_t launch_chunk_map(const int32_t *cu, int nseq, int64_t T, int Q, int nc, int4 *info,
+                            int *seq_off, hipStream_t st) {
+  hipLaunchKernelGGL(k_chunk_map, dim3(nc > 0 ? nc : 1), dim3(256), 0, st, cu, nseq, T, Q, nc, info,
+                     seq_off);
+  return hipGetLastError();
+}
+
 // ----------------------------------------------------------- K3 state pass
 // Per (sequence, head), per 4 state elements: walk the sequence's chunks in
 // order, emit the state entering each chunk (as the MFMA operand type, and

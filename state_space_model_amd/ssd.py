@@ -22,7 +22,8 @@ EXPORTS = ("ssd_scan_prefill_workspace", "ssd_scan_prefill", "ssd_scan_prefill_s
            "ssd_step", "ssd_step_multi", "ssd_conv1d_step", "ssd_gated_rmsnorm",
            "ssd_decode_layer_step", "ssd_selective_scan_workspace", "ssd_selective_scan",
            "ssd_scan_prefill_backward_workspace", "ssd_scan_prefill_backward",
-           "ssd_gated_delta_rule", "ssd_last_error")
+           "ssd_gated_delta_rule", "ssd_gated_delta_rule_chunked_workspace",
+           "ssd_gated_delta_rule_chunked", "ssd_last_error")
 
 _lib = None
 
@@ -76,6 +77,11 @@ def load(path=LIB_PATH):
     lib.ssd_scan_prefill_backward.restype = i32
     lib.ssd_gated_delta_rule.argtypes = [vp] * 9 + [i32, i64, i32, i32, i32, i32, i32, vp]
     lib.ssd_gated_delta_rule.restype = i32
+    lib.ssd_gated_delta_rule_chunked_workspace.argtypes = [i64, i32, i32, i32, i32, i32]
+    lib.ssd_gated_delta_rule_chunked_workspace.restype = sz
+    lib.ssd_gated_delta_rule_chunked.argtypes = [vp] * 9 + [i32, i64, i32, i32, i32, i32, i32, vp,
+                                                            sz, vp]
+    lib.ssd_gated_delta_rule_chunked.restype = i32
     lib.ssd_last_error.argtypes = []
     lib.ssd_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -274,10 +280,13 @@ def prefill_backward(x, dt, A, B, C, D, dy, h0=None, dh_out=None, chunk=256, cu_
 
 
 def gated_delta_rule(q, k, v, g, beta, h0=None, cu_seqlens=None, *, nseq=None, o=None,
-                     h_out=None, prepare=False):
+                     h_out=None, form="auto", workspace=None, prepare=False):
     """Gated delta rule scan.  q, k [T,G,K]; v [T,H,V] (float32 or bfloat16,
     all the same); g, beta [T,H] float32; h0 [nseq,H,V,K] float32 or None;
     cu_seqlens int32 [nseq+1] or None (dense: ``nseq`` sequences of T/nseq).
+    ``form``: "chunked" (chunks of 64 tokens on MFMA; K in {64,128}, V % 16
+    == 0, V + K <= 256), "stream" (token by token, any supported shape), or
+    "auto" (chunked where the shape allows).
     Returns (o [T,H,V] float32, h_out [nseq,H,V,K] float32); with
     ``prepare=True`` nothing runs and (Prepared, o, h_out) is returned."""
     T, G, K = q.shape
@@ -311,10 +320,22 @@ def gated_delta_rule(q, k, v, g, beta, h0=None, cu_seqlens=None, *, nseq=None, o
     lib = load()
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o), _ptr(h_out),
             _ptr(cu_seqlens), nseq, T, H, G, K, V, code)
+    if form not in ("auto", "chunked", "stream"):
+        raise ValueError(f"form must be auto, chunked or stream (got {form!r})")
+    nws = int(lib.ssd_gated_delta_rule_chunked_workspace(T, nseq, H, K, V, code))
+    if form == "chunked" and nws == 0:
+        raise SSDError(-2, f"chunked gated delta rule does not support K={K} V={V}")
+    fn = lib.ssd_gated_delta_rule
+    if nws > 0 and form != "stream":
+        if workspace is None:
+            workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
+        _need(workspace, "workspace", torch.uint8, dev)
+        args = args + (_ptr(workspace), workspace.numel())
+        fn = lib.ssd_gated_delta_rule_chunked
     if prepare:
-        keep = (q, k, v, g, beta, h0, o, h_out, cu_seqlens)
-        return Prepared(lib.ssd_gated_delta_rule, args, None, keep), o, h_out
-    _check(lib.ssd_gated_delta_rule(*args, _stream()))
+        keep = (q, k, v, g, beta, h0, o, h_out, cu_seqlens, workspace)
+        return Prepared(fn, args, None, keep), o, h_out
+    _check(fn(*args, _stream()))
     return o, h_out
 
 
