@@ -315,7 +315,7 @@ int ssd_gated_delta_rule(const void *q, const void *k, const void *v, const floa
  * Arguments as ssd_gated_delta_rule(), plus
  *   workspace / workspace_bytes   device scratch of at least
  *            ssd_gated_delta_rule_chunked_workspace(...) bytes (256-aligned)
- * Supported: K in {64,128}, V a multiple of 16 with V + K <= 256, H % G == 0
+ * Supported: K in {64,128}, V a multiple of 32 with V + K <= 256, H % G == 0
  * (the workspace query returns 0 for other shapes: use the streaming call).
  * Arithmetic float32; with bfloat16 operands the state and D enter the
  * products as bfloat16 pairs (hi + lo) and U, W, P are held in bfloat16.

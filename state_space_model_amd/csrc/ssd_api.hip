@@ -326,7 +326,7 @@ int ssd_gated_delta_rule_chunked(const void *q, const void *k, const void *v, co
   const int rc = gdn_check(q, k, v, g, beta, o, cu_seqlens, nseq, total_tokens, H, G, K, V, dtype);
   if (rc != SSD_OK) return rc;
   if (!ssd::gdn_chunk_supported(K, V))
-    return fail(SSD_ERR_UNSUPPORTED, "chunked form: need K in {64,128}, V %% 16 == 0, V + K <= 256 (K=%d V=%d)", K, V);
+    return fail(SSD_ERR_UNSUPPORTED, "chunked form: need K in {64,128}, V %% 32 == 0, V + K <= 256 (K=%d V=%d)", K, V);
   const size_t need = ssd::gdn_chunk_layout(total_tokens, nseq, H, K, V, dtype == SSD_BF16 ? 2 : 4).total;
   if (!workspace || workspace_bytes < need)
     return fail(SSD_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);

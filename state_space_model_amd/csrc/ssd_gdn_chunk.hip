@@ -24,12 +24,12 @@
 //                (I + A) X = [diag(beta) Vc | diag(beta gamma) Kc] in float32
 //                (a thread per column, the column in registers), U, W, P to
 //                the workspace, indexed by token.
-//   k_gdn_walk   one workgroup per (sequence, head, 16 state rows v): walks
+//   k_gdn_walk   one workgroup per (sequence, head, block of state rows v): walks
 //                the chunks with the state block in MFMA accumulators; per
 //                chunk D = U - W S_0^T, O, and the state update are three
-//                MFMA products.  The next chunk's U, W, P, q, k, g are
-//                staged into a second LDS buffer while the current chunk is
-//                computed.  For bfloat16 operands the state and D enter the
+//                MFMA products.  With bfloat16 operands the next chunk's U, W,
+//                P, q, k, gamma are loaded into registers while the current
+//                chunk is computed, and written to LDS at the chunk boundary.  For bfloat16 operands the state and D enter the
 //                products as a bfloat16 pair hi + lo (x = hi + lo to 16 bits
 //                of mantissa), so only U, W, P carry one bfloat16 rounding.
 #include "ssd_device.h"
@@ -39,7 +39,6 @@
 namespace ssd {
 
 constexpr int kGc = 64;   // tokens per chunk
-constexpr int kGvb = 16;  // state rows v per walking workgroup
 
 __device__ __forceinline__ void split_pair(float x, bf16 &hi, bf16 &lo) {
   hi = (bf16)x;
@@ -82,7 +81,8 @@ __global__ __launch_bounds__(256) void k_gdn_prep(const T *__restrict__ q, const
                                                   const float *__restrict__ g,
                                                   const float *__restrict__ beta, ChunkMap cmap,
                                                   int nc, int H, int G, int V, T *__restrict__ U,
-                                                  T *__restrict__ W, T *__restrict__ Pm) {
+                                                  T *__restrict__ W, T *__restrict__ Pm,
+                                                  float *__restrict__ E) {
   typedef GdnPrepCfg<T, K> F;
   constexpr int KP = F::KP, AP = F::AP, VN = F::VN;
   extern __shared__ __align__(16) char smem[];
@@ -113,6 +113,13 @@ __global__ __launch_bounds__(256) void k_gdn_prep(const T *__restrict__ q, const
   if (wave == 0) {
     const float s = wave_scan64(gl[lane]);
     gl[lane] = s;
+    // per token: gamma_t = 2^(G_t) and the write scale 2^(G_C - G_t) of the walk
+    const float GC = __shfl(s, 63, 64);  // rows past the chunk add 0
+    if (lane < len) {
+      float *e = E + ((size_t)(t0 + lane) * H + hd) * 2;
+      e[0] = __builtin_amdgcn_exp2f(fminf(s, 0.f));
+      e[1] = __builtin_amdgcn_exp2f(fminf(GC - s, 0.f));
+    }
   }
   __syncthreads();
 
@@ -195,48 +202,55 @@ __global__ __launch_bounds__(256) void k_gdn_prep(const T *__restrict__ q, const
 }
 
 // ------------------------------------------------------------------ walk
-template <typename T, int K> struct GdnWalkCfg {
+// VB state rows per workgroup, VB/4 waves: wave w owns output tile (rows
+// t = 16 (w % 4) .., columns v = 16 (w / 4) ..) of D and O, and K/64 tiles of
+// the state block (rows v of the same 16, columns k = 16 ((w % 4) K/64 + u)).
+template <typename T, int K, int VB> struct GdnWalkCfg {
   static constexpr int VN = 16 / (int)sizeof(T);
-  static constexpr bool SPL = sizeof(T) == 2;    // bfloat16: hi + lo pairs
-  static constexpr int NBUF = SPL ? 2 : 1;       // staged chunks in LDS
+  static constexpr bool SPL = sizeof(T) == 2;    // bfloat16: hi + lo pairs, register prefetch
+  static constexpr int NW = VB / 4;              // waves
+  static constexpr int NT = 64 * NW;             // threads
   static constexpr int KP = K + VN;              // W, q, k row pitch
-  static constexpr int UP = kGvb + VN;           // U rows (16 columns)
+  static constexpr int UP = VB + VN;             // U rows
   static constexpr int PP = kGc + VN;            // P rows
-  static constexpr int DP = kGvb + VN;           // D [j][v] pitch
+  static constexpr int DP = VB + VN;             // D [j][v] pitch
   static constexpr int SP = K + VN;              // S_0 [v][k] pitch
-  // one staged chunk: W, q, k [64][KP], U [64][UP], P [64][PP] (T), g [64] (float)
+  // one staged chunk: W, q, k [64][KP], U [64][UP], P [64][PP] (T), gamma, scale [64] (float)
   static constexpr int W_OFF = 0;
   static constexpr int Q_OFF = W_OFF + kGc * KP * (int)sizeof(T);
   static constexpr int K_OFF = Q_OFF + kGc * KP * (int)sizeof(T);
   static constexpr int U_OFF = K_OFF + kGc * KP * (int)sizeof(T);
   static constexpr int P_OFF = U_OFF + kGc * UP * (int)sizeof(T);
   static constexpr int G_OFF = P_OFF + kGc * PP * (int)sizeof(T);
-  static constexpr int BUF = G_OFF + kGc * 4;
-  // then S_0 (hi, lo), D (hi, lo), D~ (hi, lo), gamma and the D~ row scale
+  static constexpr int BUF = G_OFF + 2 * kGc * 4;
+  // then S_0 (hi, lo), D (hi, lo), D~ (hi, lo)
   static constexpr int NS = SPL ? 2 : 1;
-  static constexpr int S_OFF = NBUF * BUF;
-  static constexpr int D_OFF = S_OFF + NS * kGvb * SP * (int)sizeof(T);
-  static constexpr int E_OFF = D_OFF + 2 * NS * kGc * DP * (int)sizeof(T);
-  static constexpr int LDS = E_OFF + 2 * kGc * 4;
-  static_assert(BUF % 16 == 0 && S_OFF % 16 == 0 && D_OFF % 16 == 0 && E_OFF % 16 == 0, "align");
+  static constexpr int S_OFF = BUF;
+  static constexpr int D_OFF = S_OFF + NS * VB * SP * (int)sizeof(T);
+  static constexpr int LDS = D_OFF + 2 * NS * kGc * DP * (int)sizeof(T);
+  // 16-byte pieces of one chunk's W, q, k, U, P and of the whole, per thread
+  static constexpr int PW = kGc * K / VN, PU = kGc * VB / VN, PPn = kGc * kGc / VN;
+  static constexpr int PIECES = 3 * PW + PU + PPn;
+  static constexpr int PPT = (PIECES + NT - 1) / NT;
+  static_assert(BUF % 16 == 0 && S_OFF % 16 == 0 && D_OFF % 16 == 0, "align");
+  static_assert(LDS <= 160 * 1024, "LDS");
 };
 
-template <typename T, int K>
-__global__ __launch_bounds__(256) void k_gdn_walk(
-    const T *__restrict__ q, const T *__restrict__ k, const float *__restrict__ g,
+template <typename T, int K, int VB>
+__global__ __launch_bounds__(VB * 16) void k_gdn_walk(
+    const T *__restrict__ q, const T *__restrict__ k, const float *__restrict__ E,
     const T *__restrict__ U, const T *__restrict__ W, const T *__restrict__ Pm, const float *h0,
     float *__restrict__ o, float *h_out, const int32_t *__restrict__ cu, int L_dense, int nseq,
     int H, int G, int V) {
-  typedef GdnWalkCfg<T, K> F;
+  typedef GdnWalkCfg<T, K, VB> F;
   constexpr int VN = F::VN, KP = F::KP, UP = F::UP, PP = F::PP, DP = F::DP, SP = F::SP;
   constexpr bool SPL = F::SPL;
-  constexpr int KT = K / 16;        // 16-column k tiles of the state
-  constexpr int KTW = KT / 4;       // per wave
-  static_assert(KT % 4 == 0, "K must be a multiple of 64");
+  constexpr int KTW = K / 64;       // state tiles per wave
+  typedef typename Vec16<T>::type Vv;
 
   // XCD-aware order: the v-blocks of one head share an XCD (its L2 holds the
-  // chunk's U, W, P, q, k for all of them)
-  const int nvb = V / kGvb;
+  // chunk's W, P, q, k for all of them)
+  const int nvb = V / VB;
   const int L = blockIdx.x, per = 8 * nvb;
   const int hb = L / per, rem = L - hb * per;
   const int vb = rem >> 3, hs = hb * 8 + (rem & 7);  // hs = s * H + h
@@ -245,6 +259,7 @@ __global__ __launch_bounds__(256) void k_gdn_walk(
   const int gr = (int)(((long)hd * G) / H);
   const int tid = threadIdx.x, lane = tid & 63, grp = lane >> 4, col = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tt = wave & 3, vt = wave >> 2;  // this wave's t tile and v tile
   int t0, t1;
   if (cu) {
     t0 = cu[s];
@@ -255,74 +270,109 @@ __global__ __launch_bounds__(256) void k_gdn_walk(
   }
 
   extern __shared__ __align__(16) char smem[];
-  T *Ss = reinterpret_cast<T *>(smem + F::S_OFF);                // [NS][16][SP]
-  T *Ds = reinterpret_cast<T *>(smem + F::D_OFF);                // [NS][64][DP]
-  T *Dt = Ds + F::NS * kGc * DP;                                 // [NS][64][DP]  scaled rows
-  float *gam = reinterpret_cast<float *>(smem + F::E_OFF);       // [64]
-  float *dsc = gam + kGc;                                        // [64]
+  T *Ws = reinterpret_cast<T *>(smem + F::W_OFF);
+  T *Qs = reinterpret_cast<T *>(smem + F::Q_OFF);
+  T *Ks = reinterpret_cast<T *>(smem + F::K_OFF);
+  T *Us = reinterpret_cast<T *>(smem + F::U_OFF);
+  T *Ps = reinterpret_cast<T *>(smem + F::P_OFF);
+  float *gam = reinterpret_cast<float *>(smem + F::G_OFF);  // gamma_t (0 past the chunk)
+  float *dsc = gam + kGc;                                    // 2^(G_C - G_t)
+  T *Ss = reinterpret_cast<T *>(smem + F::S_OFF);            // [NS][VB][SP]
+  T *Ds = reinterpret_cast<T *>(smem + F::D_OFF);            // [NS][64][DP]
+  T *Dt = Ds + F::NS * kGc * DP;                             // [NS][64][DP]  scaled rows
 
-  auto stage = [&](int b, int tb) {
-    char *buf = smem + b * F::BUF;
+  // piece p of a chunk -> (source row pointer, row, 16-byte vector, LDS tile)
+  auto piece = [&](int p, int tb, const T *&src, T *&dst) {
+    int r, v;
+    if (p < 3 * F::PW) {
+      const int m = p / F::PW, e = p - m * F::PW;
+      r = e / (K / VN);
+      v = e - r * (K / VN);
+      const T *base = m == 0 ? W + ((size_t)tb * H + hd) * K
+                      : (m == 1 ? q : k) + ((size_t)tb * G + gr) * K;
+      const size_t stride = m == 0 ? (size_t)H * K : (size_t)G * K;
+      src = base + r * stride + v * VN;
+      dst = (m == 0 ? Ws : m == 1 ? Qs : Ks) + r * KP + v * VN;
+    } else if (p < 3 * F::PW + F::PU) {
+      const int e = p - 3 * F::PW;
+      r = e / (VB / VN);
+      v = e - r * (VB / VN);
+      src = U + ((size_t)(tb + r) * H + hd) * V + vb * VB + v * VN;
+      dst = Us + r * UP + v * VN;
+    } else {
+      const int e = p - 3 * F::PW - F::PU;
+      r = e / (kGc / VN);
+      v = e - r * (kGc / VN);
+      src = Pm + ((size_t)(tb + r) * H + hd) * kGc + v * VN;
+      dst = Ps + r * PP + v * VN;
+    }
+    return r;
+  };
+  Vv pre[F::PPT];
+  float2 epre = make_float2(0.f, 0.f);
+  auto fetch = [&](int tb) {  // the chunk at tb -> registers
     const int len = min(kGc, t1 - tb);
-    dma_tile<T, KP / VN, K / VN>(reinterpret_cast<T *>(buf + F::W_OFF),
-                                 W + ((size_t)tb * H + hd) * K, (size_t)H * K, kGc, len, wave, 4);
-    dma_tile<T, KP / VN, K / VN>(reinterpret_cast<T *>(buf + F::Q_OFF),
-                                 q + ((size_t)tb * G + gr) * K, (size_t)G * K, kGc, len, wave, 4);
-    dma_tile<T, KP / VN, K / VN>(reinterpret_cast<T *>(buf + F::K_OFF),
-                                 k + ((size_t)tb * G + gr) * K, (size_t)G * K, kGc, len, wave, 4);
-    dma_tile<T, UP / VN, kGvb / VN>(reinterpret_cast<T *>(buf + F::U_OFF),
-                                    U + ((size_t)tb * H + hd) * V + vb * kGvb, (size_t)H * V, kGc,
-                                    len, wave, 4);
-    dma_tile<T, PP / VN, kGc / VN>(reinterpret_cast<T *>(buf + F::P_OFF),
-                                   Pm + ((size_t)tb * H + hd) * kGc, (size_t)H * kGc, kGc, len, wave,
-                                   4);
-    dma_col64(reinterpret_cast<float *>(buf + F::G_OFF), g + (size_t)tb * H + hd, (size_t)H, len,
-              wave);
+#pragma unroll
+    for (int c = 0; c < F::PPT; ++c) {
+      const int p = tid + c * F::NT;
+      pre[c] = vzero<Vv>();
+      if (p < F::PIECES) {
+        const T *src;
+        T *dst;
+        const int r = piece(p, tb, src, dst);
+        if (r < len) pre[c] = *reinterpret_cast<const Vv *>(src);
+      }
+    }
+    if (tid < kGc)
+      epre = tid < len ? *reinterpret_cast<const float2 *>(E + ((size_t)(tb + tid) * H + hd) * 2)
+                       : make_float2(0.f, 0.f);
+  };
+  auto commit = [&](int tb) {  // registers -> LDS
+#pragma unroll
+    for (int c = 0; c < F::PPT; ++c) {
+      const int p = tid + c * F::NT;
+      if (p < F::PIECES) {
+        const T *src;
+        T *dst;
+        piece(p, tb, src, dst);
+        *reinterpret_cast<Vv *>(dst) = pre[c];
+      }
+    }
+    if (tid < kGc) {
+      gam[tid] = epre.x;
+      dsc[tid] = epre.y;
+    }
   };
 
-  // the state block: rows v = vb*16 + 4*grp + r, columns k = kt*16 + col
+  // the state block: rows v = vb*VB + 16 vt + 4 grp + r, columns k = (4 (tt) KTW + u) 16 + col
   f4 st[KTW];
-  const size_t sofs = ((size_t)hs * V + vb * kGvb) * K;
+  const size_t sofs = ((size_t)hs * V + vb * VB + vt * 16) * K;
 #pragma unroll
   for (int u = 0; u < KTW; ++u) {
-    const int kc = (wave * KTW + u) * 16 + col;
+    const int kc = (tt * KTW + u) * 16 + col;
 #pragma unroll
     for (int r = 0; r < 4; ++r) st[u][r] = h0 ? h0[sofs + (size_t)(4 * grp + r) * K + kc] : 0.f;
   }
 
-  if (t0 < t1) stage(0, t0);
-  int cur = 0;
+  if (t0 < t1) fetch(t0);
   for (int tb = t0; tb < t1; tb += kGc) {
     const int len = min(kGc, t1 - tb);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();  // chunk tb staged; the previous chunk's buffer is free
-    if (F::NBUF == 2 && tb + kGc < t1) stage(cur ^ 1, tb + kGc);
-    const char *buf = smem + cur * F::BUF;
-    const T *Ws = reinterpret_cast<const T *>(buf + F::W_OFF);
-    const T *Qs = reinterpret_cast<const T *>(buf + F::Q_OFF);
-    const T *Ks = reinterpret_cast<const T *>(buf + F::K_OFF);
-    const T *Us = reinterpret_cast<const T *>(buf + F::U_OFF);
-    const T *Ps = reinterpret_cast<const T *>(buf + F::P_OFF);
-    const float *gs = reinterpret_cast<const float *>(buf + F::G_OFF);
+    __syncthreads();  // every read of the previous chunk's tiles is done
+    commit(tb);
+    if (tb + kGc < t1) fetch(tb + kGc);  // lands while this chunk is computed
 
-    // gamma_t = 2^(G_t), row scale 2^(G_C - G_j); the state block to LDS
-    if (wave == 0) {
-      const float Gt = wave_scan64(fminf(gs[lane], 0.f) * kLog2e);
-      const float GC = __shfl(Gt, 63, 64);  // rows past the chunk add 0
-      gam[lane] = __builtin_amdgcn_exp2f(fminf(Gt, 0.f));
-      dsc[lane] = __builtin_amdgcn_exp2f(fminf(GC - Gt, 0.f));
-    }
+    // the state block to LDS
 #pragma unroll
     for (int u = 0; u < KTW; ++u) {
-      const int kc = (wave * KTW + u) * 16 + col;
+      const int kc = (tt * KTW + u) * 16 + col;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int vr = 4 * grp + r;
+        const int vr = vt * 16 + 4 * grp + r;
         if constexpr (SPL) {
           bf16 hi, lo;
           split_pair(st[u][r], hi, lo);
           Ss[vr * SP + kc] = hi;
-          Ss[kGvb * SP + vr * SP + kc] = lo;
+          Ss[VB * SP + vr * SP + kc] = lo;
         } else {
           Ss[vr * SP + kc] = from_f32<T>(st[u][r]);
         }
@@ -330,38 +380,38 @@ __global__ __launch_bounds__(256) void k_gdn_walk(
     }
     __syncthreads();
 
-    // D = U - W S_0^T and Qc S_0^T for rows t of this wave's tile, 16 columns v
+    // D = U - W S_0^T and Qc S_0^T for this wave's tile
     f4 ws = zero4(), qs = zero4();
 #pragma unroll
     for (int k0 = 0; k0 < K; k0 += 32) {
-      const Frag<T> a = frag_rowk(Ws, KP, wave * 16 + col, k0 + 8 * grp);
-      const Frag<T> aq = frag_rowk(Qs, KP, wave * 16 + col, k0 + 8 * grp);
-      const Frag<T> b = frag_rowk(Ss, SP, col, k0 + 8 * grp);
+      const Frag<T> a = frag_rowk(Ws, KP, tt * 16 + col, k0 + 8 * grp);
+      const Frag<T> aq = frag_rowk(Qs, KP, tt * 16 + col, k0 + 8 * grp);
+      const Frag<T> b = frag_rowk(Ss, SP, vt * 16 + col, k0 + 8 * grp);
       mma(ws, a, b);
       mma(qs, aq, b);
       if constexpr (SPL) {
-        const Frag<T> bl = frag_rowk(Ss + kGvb * SP, SP, col, k0 + 8 * grp);
+        const Frag<T> bl = frag_rowk(Ss + VB * SP, SP, vt * 16 + col, k0 + 8 * grp);
         mma(ws, a, bl);
         mma(qs, aq, bl);
       }
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int t = wave * 16 + 4 * grp + r;
-      const float d = to_f32(Us[t * UP + col]) - ws[r];
+      const int t = tt * 16 + 4 * grp + r, vc = vt * 16 + col;
+      const float d = to_f32(Us[t * UP + vc]) - ws[r];
       const float dt = d * dsc[t];
       qs[r] *= gam[t];
       if constexpr (SPL) {
         bf16 hi, lo;
         split_pair(d, hi, lo);
-        Ds[t * DP + col] = hi;
-        Ds[kGc * DP + t * DP + col] = lo;
+        Ds[t * DP + vc] = hi;
+        Ds[kGc * DP + t * DP + vc] = lo;
         split_pair(dt, hi, lo);
-        Dt[t * DP + col] = hi;
-        Dt[kGc * DP + t * DP + col] = lo;
+        Dt[t * DP + vc] = hi;
+        Dt[kGc * DP + t * DP + vc] = lo;
       } else {
-        Ds[t * DP + col] = from_f32<T>(d);
-        Dt[t * DP + col] = from_f32<T>(dt);
+        Ds[t * DP + vc] = from_f32<T>(d);
+        Dt[t * DP + vc] = from_f32<T>(dt);
       }
     }
     __syncthreads();
@@ -369,47 +419,42 @@ __global__ __launch_bounds__(256) void k_gdn_walk(
     // O = diag(gamma) Qc S_0^T + P D   (k = j)
 #pragma unroll
     for (int j0 = 0; j0 < kGc; j0 += 32) {
-      const Frag<T> a = frag_rowk(Ps, PP, wave * 16 + col, j0 + 8 * grp);
-      const Frag<T> b = frag_kmaj(Ds, DP, 0, j0 + 8 * grp, j0 + 8 * grp + 4);
+      const Frag<T> a = frag_rowk(Ps, PP, tt * 16 + col, j0 + 8 * grp);
+      const Frag<T> b = frag_kmaj(Ds, DP, vt * 16, j0 + 8 * grp, j0 + 8 * grp + 4);
       mma(qs, a, b);
       if constexpr (SPL) {
-        const Frag<T> bl = frag_kmaj(Ds + kGc * DP, DP, 0, j0 + 8 * grp, j0 + 8 * grp + 4);
+        const Frag<T> bl = frag_kmaj(Ds + kGc * DP, DP, vt * 16, j0 + 8 * grp, j0 + 8 * grp + 4);
         mma(qs, a, bl);
       }
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int t = wave * 16 + 4 * grp + r;
-      if (t < len) o[((size_t)(tb + t) * H + hd) * V + vb * kGvb + col] = qs[r];
+      const int t = tt * 16 + 4 * grp + r;
+      if (t < len) o[((size_t)(tb + t) * H + hd) * V + vb * VB + vt * 16 + col] = qs[r];
     }
     // S <- gamma_C S_0 + D~^T Kc   (k = j)
-    const float gC = gam[kGc - 1];  // rows past the chunk add 0 to G
+    const float gC = gam[len - 1];
 #pragma unroll
     for (int u = 0; u < KTW; ++u) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) st[u][r] *= gC;
-      const int kt = wave * KTW + u;
+      const int kt = tt * KTW + u;
 #pragma unroll
       for (int j0 = 0; j0 < kGc; j0 += 32) {
-        const Frag<T> a = frag_kmaj(Dt, DP, 0, j0 + 8 * grp, j0 + 8 * grp + 4);
+        const Frag<T> a = frag_kmaj(Dt, DP, vt * 16, j0 + 8 * grp, j0 + 8 * grp + 4);
         const Frag<T> b = frag_kmaj(Ks, KP, kt * 16, j0 + 8 * grp, j0 + 8 * grp + 4);
         mma(st[u], a, b);
         if constexpr (SPL) {
-          const Frag<T> al = frag_kmaj(Dt + kGc * DP, DP, 0, j0 + 8 * grp, j0 + 8 * grp + 4);
+          const Frag<T> al = frag_kmaj(Dt + kGc * DP, DP, vt * 16, j0 + 8 * grp, j0 + 8 * grp + 4);
           mma(st[u], al, b);
         }
       }
     }
-    if (F::NBUF == 1 && tb + kGc < t1) {
-      __syncthreads();  // every read of the one buffer is done
-      stage(0, tb + kGc);
-    }
-    cur ^= F::NBUF - 1;
   }
   if (h_out) {
 #pragma unroll
     for (int u = 0; u < KTW; ++u) {
-      const int kc = (wave * KTW + u) * 16 + col;
+      const int kc = (tt * KTW + u) * 16 + col;
 #pragma unroll
       for (int r = 0; r < 4; ++r) h_out[sofs + (size_t)(4 * grp + r) * K + kc] = st[u][r];
     }
@@ -418,7 +463,7 @@ __global__ __launch_bounds__(256) void k_gdn_walk(
 
 // ------------------------------------------------------------------ launch
 bool gdn_chunk_supported(int K, int V) {
-  return (K == 64 || K == 128) && V % kGvb == 0 && V + K <= 256;
+  return (K == 64 || K == 128) && V % 32 == 0 && V + K <= 256;
 }
 
 GdnLayout gdn_chunk_layout(int64_t T, int nseq, int H, int K, int V, int elem) {
@@ -437,6 +482,8 @@ GdnLayout gdn_chunk_layout(int64_t T, int nseq, int H, int K, int V, int elem) {
   off = up(off + (size_t)elem * T * H * K);
   Lw.P = off;
   off = up(off + (size_t)elem * T * H * kGc);
+  Lw.E = off;
+  off = up(off + (size_t)8 * T * H);
   Lw.total = off;
   return Lw;
 }
@@ -450,6 +497,7 @@ static hipError_t gdn_chunk_run(const GdnArgs &a) {
   int *seq_off = reinterpret_cast<int *>(ws + Lw.seq_off);
   T *Up = reinterpret_cast<T *>(ws + Lw.U), *Wp = reinterpret_cast<T *>(ws + Lw.W);
   T *Pp = reinterpret_cast<T *>(ws + Lw.P);
+  float *Ep = reinterpret_cast<float *>(ws + Lw.E);
   const int nc = (int)Lw.nc_max;
   const int L_dense = a.cu ? 0 : (int)(a.T / a.nseq);
   if (nc > 0) {
@@ -465,24 +513,26 @@ static hipError_t gdn_chunk_run(const GdnArgs &a) {
     const float *gp = a.g, *bp = a.beta;
     ChunkMap cm{info, L_dense, a.nseq, kGc};
     int nc_ = nc, H_ = a.H, G_ = a.G, V_ = a.V;
-    void *args[] = {&qp, &kkp, &vp, &gp, &bp, &cm, &nc_, &H_, &G_, &V_, &Up, &Wp, &Pp};
+    void *args[] = {&qp, &kkp, &vp, &gp, &bp, &cm, &nc_, &H_, &G_, &V_, &Up, &Wp, &Pp, &Ep};
     e = hipLaunchKernel(kp, dim3(nc, a.H), dim3(256), args, FP::LDS, st);
     if (e != hipSuccess) return e;
   }
-  typedef GdnWalkCfg<T, K> FW;
-  const void *kw = (const void *)k_gdn_walk<T, K>;
+  constexpr int VB = sizeof(T) == 2 ? 32 : 16;  // float32 tiles: 16 rows keep the LDS in bounds
+  if (a.V % VB != 0) return hipErrorInvalidValue;
+  typedef GdnWalkCfg<T, K, VB> FW;
+  const void *kw = (const void *)k_gdn_walk<T, K, VB>;
   hipError_t e = set_lds_limit(kw);
   if (e != hipSuccess) return e;
   const T *qp = (const T *)a.q, *kkp = (const T *)a.k;
-  const float *gp = a.g, *h0p = a.h0;
+  const float *Ec = Ep, *h0p = a.h0;
   const T *Uc = Up, *Wc = Wp, *Pc = Pp;
   float *op = a.o, *hop = a.h_out;
   const int32_t *cup = a.cu;
   int Ld = L_dense, ns = a.nseq, H_ = a.H, G_ = a.G, V_ = a.V;
-  void *args[] = {&qp, &kkp, &gp, &Uc, &Wc, &Pc, &h0p, &op, &hop, &cup, &Ld, &ns, &H_, &G_, &V_};
+  void *args[] = {&qp, &kkp, &Ec, &Uc, &Wc, &Pc, &h0p, &op, &hop, &cup, &Ld, &ns, &H_, &G_, &V_};
   const int heads = a.nseq * a.H;
-  const unsigned grid = (unsigned)((heads + 7) / 8) * 8u * (unsigned)(a.V / kGvb);
-  return hipLaunchKernel(kw, dim3(grid), dim3(256), args, FW::LDS, st);
+  const unsigned grid = (unsigned)((heads + 7) / 8) * 8u * (unsigned)(a.V / VB);
+  return hipLaunchKernel(kw, dim3(grid), dim3(FW::NT), args, FW::LDS, st);
 }
 
 hipError_t launch_gdn_chunked(const GdnArgs &a) {

@@ -141,6 +141,7 @@ struct GdnLayout {
   int64_t nc_max;        // upper bound on the chunks of 64 tokens
   size_t info, seq_off;  // chunk map of a packed batch
   size_t U, W, P;        // T [T][H][V], [T][H][K], [T][H][64]
+  size_t E;              // f32 [T][H][2]  gamma_t and the write scale 2^(G_C - G_t)
   size_t total;
 };
 bool gdn_chunk_supported(int K, int V);

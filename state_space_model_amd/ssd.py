@@ -284,7 +284,7 @@ def gated_delta_rule(q, k, v, g, beta, h0=None, cu_seqlens=None, *, nseq=None, o
     """Gated delta rule scan.  q, k [T,G,K]; v [T,H,V] (float32 or bfloat16,
     all the same); g, beta [T,H] float32; h0 [nseq,H,V,K] float32 or None;
     cu_seqlens int32 [nseq+1] or None (dense: ``nseq`` sequences of T/nseq).
-    ``form``: "chunked" (chunks of 64 tokens on MFMA; K in {64,128}, V % 16
+    ``form``: "chunked" (chunks of 64 tokens on MFMA; K in {64,128}, V % 32
     == 0, V + K <= 256), "stream" (token by token, any supported shape), or
     "auto" (chunked where the shape allows).
     Returns (o [T,H,V] float32, h_out [nseq,H,V,K] float32); with

@@ -19,7 +19,7 @@ FORMS = ["stream", "chunked"]
 
 
 def _chunked_ok(K, V):
-    return K in (64, 128) and V % 16 == 0 and V + K <= 256
+    return K in (64, 128) and V % 32 == 0 and V + K <= 256
 
 
 def _gpu(d, dtype, dense_nseq=None, h0=True, form="stream"):
@@ -121,7 +121,7 @@ def test_gdn_packed_dense_solo_split(form):
 def test_gdn_empty_and_alias(form):
     import torch
     from state_space_model_amd import ssd
-    d = inputs.gdn_inputs([0, 0], 2, 1, 64, 16, 970, dtype="f32", h0=True)
+    d = inputs.gdn_inputs([0, 0], 2, 1, 64, 32, 970, dtype="f32", h0=True)
     o, ho = _gpu(d, "f32", form=form)
     assert o.size == 0 and np.array_equal(ho, d["h0"])
     d = inputs.gdn_inputs([90, 40], 2, 1, 64, 32, 971, dtype="f32", h0=True)
