@@ -163,15 +163,19 @@ __global__ __launch_bounds__(256) void k_gdn_prep(const T *__restrict__ q, const
   // (I + A) X = R by forward substitution, one column of R per thread:
   // columns [0, V) are beta_t v_t, columns [V, V + K) are beta_t gamma_t k_t
   if (tid < V + K) {
+    // no branch per row: every load is issued before the first is used
+    // (rows past the chunk read the last row and are zeroed by beta = 0)
     float x[kGc];
+    if (tid < V) {
 #pragma unroll
-    for (int t = 0; t < kGc; ++t) {
-      float r = 0.f;
-      if (t < len) {
-        r = tid < V ? bl[t] * to_f32(v[((size_t)(t0 + t) * H + hd) * V + tid])
-                    : bl[t] * __builtin_amdgcn_exp2f(fminf(gl[t], 0.f)) * to_f32(Ks[t * KP + tid - V]);
+      for (int t = 0; t < kGc; ++t) {
+        const int tr = min(t, len - 1);
+        x[t] = bl[t] * to_f32(v[((size_t)(t0 + tr) * H + hd) * V + tid]);
       }
-      x[t] = r;
+    } else {
+#pragma unroll
+      for (int t = 0; t < kGc; ++t)
+        x[t] = bl[t] * __builtin_amdgcn_exp2f(fminf(gl[t], 0.f)) * to_f32(Ks[t * KP + tid - V]);
     }
     // column by column: once x_j is final, remove its share from every later
     // row (column j of A is row j of the transposed tile)
@@ -488,6 +492,24 @@ GdnLayout gdn_chunk_layout(int64_t T, int nseq, int H, int K, int V, int elem) {
   return Lw;
 }
 
+template <typename T, int K, int VB>
+static hipError_t gdn_walk_launch(const GdnArgs &a, int L_dense, const float *Ec, const T *Uc,
+                                  const T *Wc, const T *Pc, hipStream_t st) {
+  typedef GdnWalkCfg<T, K, VB> FW;
+  const void *kw = (const void *)k_gdn_walk<T, K, VB>;
+  hipError_t e = set_lds_limit(kw);
+  if (e != hipSuccess) return e;
+  const T *qp = (const T *)a.q, *kkp = (const T *)a.k;
+  const float *h0p = a.h0;
+  float *op = a.o, *hop = a.h_out;
+  const int32_t *cup = a.cu;
+  int Ld = L_dense, ns = a.nseq, H_ = a.H, G_ = a.G, V_ = a.V;
+  void *args[] = {&qp, &kkp, &Ec, &Uc, &Wc, &Pc, &h0p, &op, &hop, &cup, &Ld, &ns, &H_, &G_, &V_};
+  const int heads = a.nseq * a.H;
+  const unsigned grid = (unsigned)((heads + 7) / 8) * 8u * (unsigned)(a.V / VB);
+  return hipLaunchKernel(kw, dim3(grid), dim3(FW::NT), args, FW::LDS, st);
+}
+
 template <typename T, int K>
 static hipError_t gdn_chunk_run(const GdnArgs &a) {
   const GdnLayout Lw = gdn_chunk_layout(a.T, a.nseq, a.H, K, a.V, sizeof(T));
@@ -517,22 +539,14 @@ static hipError_t gdn_chunk_run(const GdnArgs &a) {
     e = hipLaunchKernel(kp, dim3(nc, a.H), dim3(256), args, FP::LDS, st);
     if (e != hipSuccess) return e;
   }
-  constexpr int VB = sizeof(T) == 2 ? 32 : 16;  // float32 tiles: 16 rows keep the LDS in bounds
-  if (a.V % VB != 0) return hipErrorInvalidValue;
-  typedef GdnWalkCfg<T, K, VB> FW;
-  const void *kw = (const void *)k_gdn_walk<T, K, VB>;
-  hipError_t e = set_lds_limit(kw);
-  if (e != hipSuccess) return e;
-  const T *qp = (const T *)a.q, *kkp = (const T *)a.k;
-  const float *Ec = Ep, *h0p = a.h0;
-  const T *Uc = Up, *Wc = Wp, *Pc = Pp;
-  float *op = a.o, *hop = a.h_out;
-  const int32_t *cup = a.cu;
-  int Ld = L_dense, ns = a.nseq, H_ = a.H, G_ = a.G, V_ = a.V;
-  void *args[] = {&qp, &kkp, &Ec, &Uc, &Wc, &Pc, &h0p, &op, &hop, &cup, &Ld, &ns, &H_, &G_, &V_};
-  const int heads = a.nseq * a.H;
-  const unsigned grid = (unsigned)((heads + 7) / 8) * 8u * (unsigned)(a.V / VB);
-  return hipLaunchKernel(kw, dim3(grid), dim3(FW::NT), args, FW::LDS, st);
+  // bfloat16: 32 state rows per workgroup (64 halve the re-reads of each
+  // chunk's W, P, q, k but leave three quarters of the CUs idle at 32 heads:
+  // 329 against 260 us); float32: 16 (its tiles fill the LDS)
+  if constexpr (sizeof(T) == 2) {
+    return gdn_walk_launch<T, K, 32>(a, L_dense, Ep, Up, Wp, Pp, st);
+  } else {
+    return gdn_walk_launch<T, K, 16>(a, L_dense, Ep, Up, Wp, Pp, st);
+  }
 }
 
 hipError_t launch_gdn_chunked(const GdnArgs &a) {
