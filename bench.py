@@ -207,7 +207,8 @@ KERNEL_NAMES = {  # kernel symbol fragment -> bench kernel name (first match win
     "k_step_multi": "decode_multi_step", "k_conv1d_step": "conv1d_step",
     "k_gated_rmsnorm": "gated_rmsnorm", "k_s6_summary": "s6_summary", "k_s6_pass": "s6_pass",
     "k_s6_replay": "s6_replay", "k_bwd_scan": "bwd_scan", "k_state_pass_bwd": "state_pass_bwd",
-    "k_bwd_ddt": "bwd_ddt", "k_bwd_sums": "bwd_sums", "k_gdn": "gated_delta_rule",
+    "k_bwd_ddt": "bwd_ddt", "k_bwd_sums": "bwd_sums", "k_gdn_prep": "gdn_chunk_prep",
+    "k_gdn_walk": "gdn_chunk_walk", "k_gdn": "gated_delta_rule",
     "k_chunk_state": "chunk_state", "k_state_pass": "state_pass", "k_chunk_scan": "chunk_scan",
     "k_chunk_map": "chunk_map", "k_step": "decode_step",
 }
@@ -231,7 +232,7 @@ def _kernel_key(name, grid, train=False):
                 return "codestral-7b-decode-step", k
             if k.startswith("s6_"):
                 return "mamba1-w1-selective-scan", k
-            if k == "gated_delta_rule":
+            if k in ("gated_delta_rule", "gdn_chunk_prep", "gdn_chunk_walk"):
                 return "gdn-layer-prefill", k
             return "mamba2-130m-layer-prefill", k
     return None, None
@@ -549,34 +550,44 @@ def selective_scan_bench(torch, inputs, ssd, dev):
 
 
 def gdn_bench(torch, inputs, ssd, dev):
-    """The gated delta rule scan at its layer shape (batch 1, 4096 tokens, 32
-    heads over 16 query/key groups, K = V = 128, bf16), whole scan from HIP-graph
-    replays.  Per token and head the rule does 6 V K flops (S k, the update,
-    S q); the streaming kernel walks the tokens in order, so the time per token
-    (the chain's step) is reported beside the flop rate."""
+    """The gated delta rule at its layer shape (batch 1, 4096 tokens, 32 heads
+    over 16 query/key groups, K = V = 128, bf16), whole scan from HIP-graph
+    replays, in both forms: chunked (chunks of 64 tokens on MFMA; the one the
+    binding picks) and token by token.  Per token and head the rule does 6 V K
+    flops (S k, the update, S q): that is the algorithmic rate reported; the
+    chunked form runs on bf16 MFMA, so its roofline is priced against that
+    peak, the streaming form's against the fp32 vector peak."""
     w = inputs.GDN_W
     d = inputs.gdn_inputs([w["L"]] * w["batch"], w["H"], w["G"], w["K"], w["V"], 950,
                           dtype=w["dtype"])
     op = torch.bfloat16
     t = lambda a, o=None: torch.from_numpy(np.ascontiguousarray(a)).to(dev) if o is None \
         else torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(o)
-    run, o, h = ssd.gated_delta_rule(t(d["q"], op), t(d["k"], op), t(d["v"], op), t(d["g"]),
-                                     t(d["beta"]), None, None, nseq=w["batch"], prepare=True)
-    run()
-    torch.cuda.synchronize()
-    ms = graph_ms(torch, run, reps=5, per_graph=5)
+    args = (t(d["q"], op), t(d["k"], op), t(d["v"], op), t(d["g"]), t(d["beta"]), None, None)
     T, H, G, K, V = w["batch"] * w["L"], w["H"], w["G"], w["K"], w["V"]
     flops = 6.0 * T * H * V * K
-    nbytes = T * (2 * G * K * 2 + H * V * 2 + 8 * H + 4 * H * V) + w["batch"] * H * V * K * 4
-    tf = flops / (ms * 1e-3) / 1e12
+    us = {}
+    for form in ("chunked", "stream"):
+        run, o, h = ssd.gated_delta_rule(*args, nseq=w["batch"], form=form, prepare=True)
+        run()
+        torch.cuda.synchronize()
+        us[form] = graph_ms(torch, run, reps=5, per_graph=5) * 1e3
+    tf = flops / (us["chunked"] * 1e-6) / 1e12
+    tfs = flops / (us["stream"] * 1e-6) / 1e12
     return {"workload": w["name"], "shape": {k: w[k] for k in ("batch", "L", "H", "G", "K", "V",
                                                                  "dtype")},
-            "us": round(ms * 1e3, 2), "tokens_per_s": round(T / (ms * 1e-3), 1),
-            "ns_per_token_step": round(ms * 1e6 / w["L"], 2),
-            "achieved_gb_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
-            "roofline": {"bound": "alu", "achieved": round(tf, 3), "peak": FP32_VECTOR_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tf / FP32_VECTOR_PEAK_TFLOPS, 4),
-                         "traffic": None, "kernel": "gated_delta_rule"}}
+            "form": "chunked", "us": round(us["chunked"], 2),
+            "tokens_per_s": round(T / (us["chunked"] * 1e-6), 1),
+            "stream_us": round(us["stream"], 2),
+            "stream_ns_per_token_step": round(us["stream"] * 1e3 / w["L"], 2),
+            "speedup_vs_stream": round(us["stream"] / us["chunked"], 2),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                         "traffic": None, "kernel": "gdn_chunk_prep+gdn_chunk_walk"},
+            "stream_roofline": {"bound": "alu", "achieved": round(tfs, 3),
+                                "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                "frac": round(tfs / FP32_VECTOR_PEAK_TFLOPS, 4),
+                                "kernel": "gated_delta_rule"}}
 
 
 def decode_layer_bench(torch, ssd, w3, dev, ms_scan):
