@@ -179,20 +179,30 @@ __global__ __launch_bounds__(256) void k_gdn_prep(const T *__restrict__ q, const
     }
     // column by column: once x_j is final, remove its share from every later
     // row (column j of A is row j of the transposed tile)
+    // column j + 1 of A is read while step j runs (the LDS latency would
+    // otherwise stand between every two steps of the chain)
+    f4 acur[kGc / 4], anext[kGc / 4];
+#pragma unroll
+    for (int q4 = 0; q4 < kGc / 4; ++q4) acur[q4] = ld4(As + q4 * 4);
 #pragma unroll
     for (int j = 0; j < kGc - 1; ++j) {
+      if (j + 1 < kGc - 1) {
+#pragma unroll
+        for (int q4 = (j + 2) / 4; q4 < kGc / 4; ++q4) anext[q4] = ld4(As + (j + 1) * AP + q4 * 4);
+      }
       const float xj = x[j];
 #pragma unroll
-      for (int t = (j + 1) & ~3; t < kGc; t += 4) {
-        const f4 a = ld4(As + j * AP + t);
+      for (int q4 = (j + 1) / 4; q4 < kGc / 4; ++q4) {
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-          if (t + u > j) x[t + u] -= a[u] * xj;
+          if (q4 * 4 + u > j) x[q4 * 4 + u] -= acur[q4][u] * xj;
       }
       // every later row is updated now: without this the compiler defers the
       // updates to each row's last use and keeps all of A in registers
 #pragma unroll
       for (int t = j + 1; t < kGc; ++t) asm volatile("" : "+v"(x[t]));
+#pragma unroll
+      for (int q4 = (j + 2) / 4; q4 < kGc / 4; ++q4) acur[q4] = anext[q4];
     }
 #pragma unroll
     for (int t = 0; t < kGc; ++t) {
