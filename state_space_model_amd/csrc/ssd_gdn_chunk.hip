@@ -45,17 +45,6 @@ __device__ __forceinline__ void split_pair(float x, bf16 &hi, bf16 &lo) {
   lo = (bf16)(x - (float)hi);
 }
 
-// Direct loads of a strided float column (one value per row, rows >= len
-// read 0) into 64 consecutive LDS floats.
-__device__ __forceinline__ void dma_col64(float *dst, const float *__restrict__ src, size_t stride,
-                                          int len, int wave) {
-  if (wave != 0) return;
-  const int lane = threadIdx.x & 63;
-  const void *gp = lane < len ? (const void *)(src + (size_t)lane * stride) : (const void *)g_zero16;
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)gp,
-                                   (__attribute__((address_space(3))) void *)dst, 4, 0, 0);
-}
-
 // Inclusive prefix sum of 64 floats held one per lane of a wave.
 __device__ __forceinline__ float wave_scan64(float v) {
   const int lane = threadIdx.x & 63;
