@@ -166,3 +166,20 @@ def test_gdn_chunked_equals_stream_and_rejects():
     rc = lib.ssd_gated_delta_rule_chunked(p(z), p(z), p(z), p(f), p(f), None, p(o), None, None,
                                           1, 100, 2, 1, 256, 64, 1, p(ws), ws.numel(), None)
     assert rc == -2
+
+
+@pytest.mark.parametrize("form", FORMS)
+def test_gdn_long_sequence(form):
+    """One 16384-token sequence (256 chunks) with h0, 4 heads over 2 groups,
+    K = V = 128, bf16: the chunked form's bfloat16-pair products must not let
+    the error grow along the state's chain of chunks (every element of o and
+    h_out against the full oracle)."""
+    log(f"gdn long sequence (16384 tokens, H 4, G 2, K = V = 128, bf16), {form}")
+    d = inputs.gdn_inputs([16384], 4, 2, 128, 128, 990, dtype="bf16", h0=True)
+    o, ho = _gpu(d, "bf16", form=form)
+    ro, rh = _ref(d)
+    eo, eh = maxabs(o, ro), maxabs(ho, rh)
+    tail = maxabs(o[-2048:], ro[-2048:])
+    log(f"  max|do|={eo:.3g} (last 2048 tokens {tail:.3g}) max|dh|={eh:.3g} "
+        f"(max|o|={np.max(np.abs(ro)):.3g})")
+    assert eo <= TOL["bf16"] and eh <= TOL["bf16"]
