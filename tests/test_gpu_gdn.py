@@ -48,6 +48,8 @@ SMALL = [  # (lengths, H, G, K, V, h0)
     ([33, 0, 70], 6, 2, 64, 128, True),
     ([1000], 2, 2, 128, 128, True),
     ([1, 1, 40], 4, 1, 128, 16, True),
+    ([150, 40], 2, 1, 64, 192, True),
+    ([97], 4, 4, 128, 96, False),
 ]
 
 
