@@ -427,7 +427,9 @@ def train_work(w, T, nseq):
 
 def training_setup(torch, inputs, ssd, dev, k=1):
     """Prepared forward and backward calls over prefill workload k (bf16; the
-    130M layer by default, h0 = 0), with a seeded dL/dy and no dL/dh_out."""
+    130M layer by default, h0 = 0), with a seeded dL/dy and no dL/dh_out: the
+    training forward (which leaves its states for the backward) and the
+    backward that takes them; also the backward that recomputes them."""
     wl = inputs.WORKLOADS[k]
     d = inputs.workload_inputs(k)
     T = d["x"].shape[0]
@@ -438,17 +440,20 @@ def training_setup(torch, inputs, ssd, dev, k=1):
     dy, _ = inputs.cotangents(T, nseq, wl.H, wl.P, wl.N, 4001, "bf16", dh_out=False)
     args = (t(d["x"], op), t(d["dt"]), t(d["A"]), t(d["B"], op), t(d["C"], op), t(d["D"]))
     h0 = None if d["h0"] is None else t(d["h0"])
-    fwd, _, _ = ssd.prefill(*args, h0, chunk=wl.chunk, nseq=nseq, prepare=True)
+    fwd, _, _, saved = ssd.prefill_train(*args, h0, chunk=wl.chunk, nseq=nseq, prepare=True)
     bwd, grads = ssd.prefill_backward(*args, t(dy, op), h0, None, chunk=wl.chunk, nseq=nseq,
-                                      prepare=True)
-    return wl, T, nseq, fwd, bwd
+                                      saved=saved, prepare=True)
+    bwd_re, _ = ssd.prefill_backward(*args, t(dy, op), h0, None, chunk=wl.chunk, nseq=nseq,
+                                     prepare=True)
+    return wl, T, nseq, fwd, bwd, bwd_re
 
 
 def training_step_bench(args, torch, inputs, ssd, dev, k=1):
     """Forward + backward of a layer's scan (the pair a training step runs) on
     prefill workload k, each from HIP-graph replays; the backward against its
-    algorithmic bytes and flops."""
-    wl, T, nseq, fwd, bwd = training_setup(torch, inputs, ssd, dev, k)
+    algorithmic bytes and flops.  The forward leaves its states for the
+    backward; the backward that recomputes them is timed beside it."""
+    wl, T, nseq, fwd, bwd, bwd_re = training_setup(torch, inputs, ssd, dev, k)
 
     def both():
         fwd()
@@ -459,12 +464,16 @@ def training_step_bench(args, torch, inputs, ssd, dev, k=1):
     ms_f = graph_ms(torch, fwd, reps=10, per_graph=10)
     ms_b = graph_ms(torch, bwd, reps=10, per_graph=10)
     ms_fb = graph_ms(torch, both, reps=10, per_graph=10)
+    bwd_re()
+    torch.cuda.synchronize()
+    ms_re = graph_ms(torch, bwd_re, reps=10, per_graph=10)
     wb = train_work(wl, T, nseq)
     tf = wb["flops"] / (ms_b * 1e-3) / 1e12
     gbs = wb["bytes"] / (ms_b * 1e-3) / 1e9
     log(args, f"{wl.name} forward + backward: {ms_fb * 1e3:.1f} us (backward {ms_b * 1e3:.1f})")
     return {"workload": wl.name, "tokens": T, "forward_us": round(ms_f * 1e3, 2),
             "backward_us": round(ms_b * 1e3, 2), "forward_backward_us": round(ms_fb * 1e3, 2),
+            "backward_recompute_us": round(ms_re * 1e3, 2),
             "tokens_per_s": round(T / (ms_fb * 1e-3), 1),
             "backward_algorithmic_flops": wb["flops"], "backward_algorithmic_bytes": wb["bytes"],
             "backward_mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4),
@@ -477,7 +486,7 @@ def train_only(args):
     from state_space_model_amd import inputs, ssd
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    wl, T, nseq, fwd, bwd = training_setup(torch, inputs, ssd, dev)
+    wl, T, nseq, fwd, bwd, _ = training_setup(torch, inputs, ssd, dev)
     for _ in range(args.warmup):
         fwd()
         bwd()

@@ -272,6 +272,37 @@ int ssd_scan_prefill_backward(const void *x, const float *dt, const float *A, co
                               size_t workspace_bytes, void *stream);
 
 /*
+ * A training step without the backward's forward recompute.
+ *
+ * ssd_scan_prefill_train_forward() computes y and h_out exactly as
+ * ssd_scan_prefill() (bitwise) and leaves in `workspace` -- sized by
+ * ssd_scan_prefill_backward_workspace() for the same shapes and chunk -- the
+ * chunk map, the chunk-local decays, the states entering every chunk (operand
+ * type and float32) and the final states, which the backward would otherwise
+ * recompute.  ssd_scan_prefill_backward_saved() then takes the same arguments
+ * as ssd_scan_prefill_backward() and skips that recompute: its results are
+ * bitwise those of ssd_scan_prefill_backward().  Preconditions (not checked):
+ * the inputs (x, dt, A, B, C, D, h0, cu_seqlens) and shapes are the training
+ * forward's, and nothing wrote the workspace in between except other
+ * ssd_scan_prefill_backward_saved() calls on it (the backward leaves the
+ * saved part intact, so the same forward serves several backward calls).
+ * Errors as ssd_scan_prefill() / ssd_scan_prefill_backward().
+ */
+int ssd_scan_prefill_train_forward(const void *x, const float *dt, const float *A, const void *B,
+                                   const void *C, const float *D, const float *h0, float *y,
+                                   float *h_out, const int32_t *cu_seqlens, int nseq,
+                                   int64_t total_tokens, int H, int P, int N, int G, int chunk,
+                                   ssd_dtype_t dtype, void *workspace, size_t workspace_bytes,
+                                   void *stream);
+int ssd_scan_prefill_backward_saved(const void *x, const float *dt, const float *A, const void *B,
+                                    const void *C, const float *D, const float *h0,
+                                    const void *dy, const float *dh_out, float *dx, float *ddt,
+                                    float *dA, float *dB, float *dC, float *dD, float *dh0,
+                                    const int32_t *cu_seqlens, int nseq, int64_t total_tokens,
+                                    int H, int P, int N, int G, int chunk, ssd_dtype_t dtype,
+                                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Gated delta rule scan: the delta-rule family of Recurrence Scan (poot docs:
  * gated delta rule layers replace attention by a per-head state matrix that
  * each token updates and that is carried from step to step; the scan returns

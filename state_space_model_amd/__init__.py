@@ -40,3 +40,8 @@ def prefill_backward(*args, **kwargs):
 def gated_delta_rule(*args, **kwargs):
     from . import ssd
     return ssd.gated_delta_rule(*args, **kwargs)
+
+
+def prefill_train(*args, **kwargs):
+    from . import ssd
+    return ssd.prefill_train(*args, **kwargs)

@@ -241,13 +241,13 @@ size_t ssd_scan_prefill_backward_workspace(int64_t total_tokens, int nseq, int H
   return ssd::bwd_layout(total_tokens, nseq, H, P, N, G, chunk, dtype == SSD_BF16 ? 2 : 4).total;
 }
 
-int ssd_scan_prefill_backward(const void *x, const float *dt, const float *A, const void *B,
-                              const void *C, const float *D, const float *h0, const void *dy,
-                              const float *dh_out, float *dx, float *ddt,
-                              float *dA, float *dB, float *dC, float *dD, float *dh0,
-                              const int32_t *cu_seqlens, int nseq, int64_t total_tokens, int H,
-                              int P, int N, int G, int chunk, ssd_dtype_t dtype, void *workspace,
-                              size_t workspace_bytes, void *stream) {
+static int backward_impl(bool saved, const void *x, const float *dt, const float *A,
+                         const void *B, const void *C, const float *D, const float *h0,
+                         const void *dy, const float *dh_out, float *dx, float *ddt, float *dA,
+                         float *dB, float *dC, float *dD, float *dh0, const int32_t *cu_seqlens,
+                         int nseq, int64_t total_tokens, int H, int P, int N, int G, int chunk,
+                         ssd_dtype_t dtype, void *workspace, size_t workspace_bytes,
+                         void *stream) {
   g_err[0] = 0;
   int rc = check_prefill(x, dt, A, B, C, D, dx, nseq, total_tokens, H, P, N, G, chunk, dtype,
                          cu_seqlens);
@@ -273,7 +273,55 @@ int ssd_scan_prefill_backward(const void *x, const float *dt, const float *A, co
   a.dC = dC;
   a.dD = dD;
   a.dh0 = dh0;
+  a.saved = saved;
   hipError_t e = ssd::launch_prefill_backward(a);
+  if (e != hipSuccess) return fail(SSD_ERR_HIP, "HIP error: %s", hipGetErrorString(e));
+  return SSD_OK;
+}
+
+int ssd_scan_prefill_backward(const void *x, const float *dt, const float *A, const void *B,
+                              const void *C, const float *D, const float *h0, const void *dy,
+                              const float *dh_out, float *dx, float *ddt,
+                              float *dA, float *dB, float *dC, float *dD, float *dh0,
+                              const int32_t *cu_seqlens, int nseq, int64_t total_tokens, int H,
+                              int P, int N, int G, int chunk, ssd_dtype_t dtype, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+  return backward_impl(false, x, dt, A, B, C, D, h0, dy, dh_out, dx, ddt, dA, dB, dC, dD, dh0,
+                       cu_seqlens, nseq, total_tokens, H, P, N, G, chunk, dtype, workspace,
+                       workspace_bytes, stream);
+}
+
+int ssd_scan_prefill_backward_saved(const void *x, const float *dt, const float *A, const void *B,
+                                    const void *C, const float *D, const float *h0,
+                                    const void *dy, const float *dh_out, float *dx, float *ddt,
+                                    float *dA, float *dB, float *dC, float *dD, float *dh0,
+                                    const int32_t *cu_seqlens, int nseq, int64_t total_tokens,
+                                    int H, int P, int N, int G, int chunk, ssd_dtype_t dtype,
+                                    void *workspace, size_t workspace_bytes, void *stream) {
+  return backward_impl(true, x, dt, A, B, C, D, h0, dy, dh_out, dx, ddt, dA, dB, dC, dD, dh0,
+                       cu_seqlens, nseq, total_tokens, H, P, N, G, chunk, dtype, workspace,
+                       workspace_bytes, stream);
+}
+
+int ssd_scan_prefill_train_forward(const void *x, const float *dt, const float *A, const void *B,
+                                   const void *C, const float *D, const float *h0, float *y,
+                                   float *h_out, const int32_t *cu_seqlens, int nseq,
+                                   int64_t total_tokens, int H, int P, int N, int G, int chunk,
+                                   ssd_dtype_t dtype, void *workspace, size_t workspace_bytes,
+                                   void *stream) {
+  g_err[0] = 0;
+  int rc = check_prefill(x, dt, A, B, C, D, y, nseq, total_tokens, H, P, N, G, chunk, dtype,
+                         cu_seqlens);
+  if (rc) return rc;
+  const ssd::BwdLayout L = ssd::bwd_layout(total_tokens, nseq, H, P, N, G, chunk,
+                                           dtype == SSD_BF16 ? 2 : 4);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(SSD_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, L.total);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(SSD_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  ssd::PrefillArgs a{x, dt, A, B, C, D, h0, y, h_out, cu_seqlens, nseq, total_tokens, H, P, N, G,
+                     chunk, dtype == SSD_BF16, workspace, stream};
+  hipError_t e = ssd::launch_prefill_train_forward(a);
   if (e != hipSuccess) return fail(SSD_ERR_HIP, "HIP error: %s", hipGetErrorString(e));
   return SSD_OK;
 }

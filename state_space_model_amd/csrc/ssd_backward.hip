@@ -720,13 +720,16 @@ static hipError_t run_backward(const BwdArgs &a) {
                       f.cu ? 0 : (int)(f.T / f.nseq), f.nseq, f.Q};
   hipError_t e;
 
-  // forward recompute: s, dt, u, chunk states, H_in per chunk and the final states
-  PrefillArgs fa = f;
-  fa.y = nullptr;
-  fa.h_out = hfin;
-  fa.hin32 = hin32;
-  e = launch_prefill(fa, 7u);
-  if (e != hipSuccess) return e;
+  // forward recompute: s, dt, u, chunk states, H_in per chunk and the final
+  // states (skipped when a training forward left them in the workspace)
+  if (!a.saved) {
+    PrefillArgs fa = f;
+    fa.y = nullptr;
+    fa.h_out = hfin;
+    fa.hin32 = hin32;
+    e = launch_prefill(fa, 7u);
+    if (e != hipSuccess) return e;
+  }
   if (nc > 0) {  // Sb_c over the spent chunk states
     PrefillArgs ba = f;
     ba.x = a.dy;
@@ -789,6 +792,19 @@ static hipError_t bwd_P(const BwdArgs &a) {
 
 hipError_t launch_prefill_backward(const BwdArgs &a) {
   return a.f.bf16 ? bwd_P<bf16>(a) : bwd_P<float>(a);
+}
+
+hipError_t launch_prefill_train_forward(const PrefillArgs &f) {
+  const BwdLayout L = bwd_layout(f.T, f.nseq, f.H, f.P, f.N, f.G, f.Q, f.bf16 ? 2 : 4);
+  char *ws = static_cast<char *>(f.workspace);
+  float *hfin = reinterpret_cast<float *>(ws + L.hfin);
+  PrefillArgs fa = f;
+  fa.h_out = hfin;
+  fa.hin32 = reinterpret_cast<float *>(ws + L.hin32);
+  hipError_t e = launch_prefill(fa, 15u);
+  if (e != hipSuccess || !f.h_out) return e;
+  return hipMemcpyAsync(f.h_out, hfin, sizeof(float) * (size_t)f.nseq * f.H * f.N * f.P,
+                        hipMemcpyDeviceToDevice, static_cast<hipStream_t>(f.stream));
 }
 
 }  // namespace ssd

@@ -60,6 +60,7 @@ struct BwdArgs {
   const void *dy;       // dL/dy, operand type
   const float *dh_out;  // dL/dh_out or null
   float *dx, *ddt, *dA, *dB, *dC, *dD, *dh0;  // dh0 may be null
+  bool saved = false;   // the workspace holds a training forward's states: no recompute
 };
 // The forward's workspace followed by the gradient pass's regions.
 struct BwdLayout {
@@ -76,6 +77,11 @@ struct BwdLayout {
 };
 BwdLayout bwd_layout(int64_t T, int nseq, int H, int P, int N, int G, int Q, int elem);
 hipError_t launch_prefill_backward(const BwdArgs &a);
+// The forward of a training step: y and h_out as launch_prefill, leaving in
+// the backward workspace (f.workspace) everything the backward would
+// recompute (chunk map, s, dt, u, the entering states as operand type and
+// float32, the final states).
+hipError_t launch_prefill_train_forward(const PrefillArgs &f);
 
 struct StepArgs {
   const void *x;

@@ -22,6 +22,7 @@ EXPORTS = ("ssd_scan_prefill_workspace", "ssd_scan_prefill", "ssd_scan_prefill_s
            "ssd_step", "ssd_step_multi", "ssd_conv1d_step", "ssd_gated_rmsnorm",
            "ssd_decode_layer_step", "ssd_selective_scan_workspace", "ssd_selective_scan",
            "ssd_scan_prefill_backward_workspace", "ssd_scan_prefill_backward",
+           "ssd_scan_prefill_train_forward", "ssd_scan_prefill_backward_saved",
            "ssd_gated_delta_rule", "ssd_gated_delta_rule_chunked_workspace",
            "ssd_gated_delta_rule_chunked", "ssd_last_error")
 
@@ -75,6 +76,11 @@ def load(path=LIB_PATH):
     lib.ssd_scan_prefill_backward.argtypes = [vp] * 17 + [i32, i64, i32, i32, i32, i32, i32, i32,
                                                           vp, sz, vp]
     lib.ssd_scan_prefill_backward.restype = i32
+    lib.ssd_scan_prefill_backward_saved.argtypes = lib.ssd_scan_prefill_backward.argtypes
+    lib.ssd_scan_prefill_backward_saved.restype = i32
+    lib.ssd_scan_prefill_train_forward.argtypes = [vp] * 10 + [i32, i64, i32, i32, i32, i32, i32,
+                                                               i32, vp, sz, vp]
+    lib.ssd_scan_prefill_train_forward.restype = i32
     lib.ssd_gated_delta_rule.argtypes = [vp] * 9 + [i32, i64, i32, i32, i32, i32, i32, vp]
     lib.ssd_gated_delta_rule.restype = i32
     lib.ssd_gated_delta_rule_chunked_workspace.argtypes = [i64, i32, i32, i32, i32, i32]
@@ -221,13 +227,69 @@ class Prepared:
             _check(rc)
 
 
+class TrainSaved:
+    """What ``prefill_train`` leaves for ``prefill_backward(..., saved=...)``:
+    the backward workspace holding the forward's chunk map, decays and
+    states, and the shape it was made for."""
+
+    def __init__(self, workspace, key):
+        self.workspace = workspace
+        self.key = key
+
+
+def prefill_train(x, dt, A, B, C, D, h0=None, chunk=256, cu_seqlens=None, *, nseq=None,
+                  y=None, h_out=None, prepare=False):
+    """The forward of a training step: (y, h_out) bitwise as ``prefill``, plus
+    a ``TrainSaved`` that lets ``prefill_backward`` skip its forward
+    recompute.  Packed [T,...] layout as ``prefill_backward``.  With
+    ``prepare=True`` nothing runs and (Prepared, y, h_out, saved) is returned."""
+    T, H, P = x.shape
+    G, N = B.shape[-2], B.shape[-1]
+    dev = x.device
+    _need(x, "x", dev=dev)
+    code = _dtype_code(x)
+    for t, n in ((B, "B"), (C, "C")):
+        _need(t, n, x.dtype, dev)
+    for t, n in ((dt, "dt"), (A, "A"), (D, "D")):
+        _need(t, n, torch.float32, dev)
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+        nseq = cu_seqlens.numel() - 1
+    elif nseq is None:
+        nseq = 1
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, dev)
+        if tuple(h0.shape) != (nseq, H, N, P):
+            raise ValueError(f"h0 must be [{nseq},{H},{N},{P}]")
+    if y is None:
+        y = torch.empty((T, H, P), dtype=torch.float32, device=dev)
+    if h_out is None:
+        h_out = torch.empty((nseq, H, N, P), dtype=torch.float32, device=dev)
+    lib = load()
+    n = int(lib.ssd_scan_prefill_backward_workspace(T, nseq, H, P, N, G, chunk, code))
+    if n == 0:
+        raise SSDError(-2, "unsupported prefill shape")
+    workspace = torch.empty(n, dtype=torch.uint8, device=dev)
+    saved = TrainSaved(workspace, (T, nseq, H, P, N, G, chunk, code))
+    args = (_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(y),
+            _ptr(h_out), _ptr(cu_seqlens), nseq, T, H, P, N, G, chunk, code, _ptr(workspace),
+            workspace.numel())
+    if prepare:
+        keep = (x, dt, A, B, C, D, h0, y, h_out, cu_seqlens, workspace)
+        return Prepared(lib.ssd_scan_prefill_train_forward, args, None, keep), y, h_out, saved
+    _check(lib.ssd_scan_prefill_train_forward(*args, _stream()))
+    return y, h_out, saved
+
+
 def prefill_backward(x, dt, A, B, C, D, dy, h0=None, dh_out=None, chunk=256, cu_seqlens=None,
-                     *, nseq=None, workspace=None, prepare=False):
+                     *, nseq=None, workspace=None, saved=None, prepare=False):
     """Gradients of ``prefill`` for dL/dy = dy and dL/dh_out = dh_out.
 
     x, dt, A, B, C, D, h0, cu_seqlens, nseq, chunk as given to ``prefill``
     (packed [T,...] layout); dy [T,H,P] in x's dtype; dh_out [nseq,H,N,P]
-    float32 or None.  Returns a dict of float32
+    float32 or None.  ``saved``: the ``TrainSaved`` of a ``prefill_train`` on
+    the same inputs -- the forward's states are then taken from it instead of
+    recomputed (same result, bitwise).  Returns a dict of float32
     tensors dx [T,H,P], ddt [T,H], dA [H], dB/dC [T,G,N], dD [H],
     dh0 [nseq,H,N,P]; with ``prepare=True`` nothing runs and
     (Prepared, grads) is returned.
@@ -258,6 +320,12 @@ def prefill_backward(x, dt, A, B, C, D, dy, h0=None, dh_out=None, chunk=256, cu_
             if tuple(t.shape) != (nseq, H, N, P):
                 raise ValueError(f"{n} must be [{nseq},{H},{N},{P}]")
     lib = load()
+    fn = lib.ssd_scan_prefill_backward
+    if saved is not None:
+        if saved.key != (T, nseq, H, P, N, G, chunk, code):
+            raise ValueError("saved forward was made for another shape, chunk or dtype")
+        workspace = saved.workspace
+        fn = lib.ssd_scan_prefill_backward_saved
     if workspace is None:
         n = int(lib.ssd_scan_prefill_backward_workspace(T, nseq, H, P, N, G, chunk, code))
         if n == 0:
@@ -274,8 +342,8 @@ def prefill_backward(x, dt, A, B, C, D, dy, h0=None, dh_out=None, chunk=256, cu_
             chunk, code, _ptr(workspace), workspace.numel())
     if prepare:
         keep = (x, dt, A, B, C, D, h0, dy, dh_out, cu_seqlens, workspace, g)
-        return Prepared(lib.ssd_scan_prefill_backward, args, None, keep), g
-    _check(lib.ssd_scan_prefill_backward(*args, _stream()))
+        return Prepared(fn, args, None, keep), g
+    _check(fn(*args, _stream()))
     return g
 
 

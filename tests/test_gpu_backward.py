@@ -268,3 +268,48 @@ def test_backward_empty_and_single_tokens():
     dy, dh = inputs.cotangents(3, 3, H, P, N, 74, "f32")
     _compare(_gpu_bwd(d, dy, dh, "f32", 32), _ref_bwd(d, dy, dh), TOL["f32"])
     torch.cuda.synchronize()
+
+
+TRAIN_CASES = [  # (lengths, H, P, N, G, chunk, h0, dh_out, dtype)
+    ([4096], 24, 64, 128, 1, 256, False, False, "bf16"),
+    ([700, 1, 0, 300], 4, 64, 128, 2, 128, True, True, "bf16"),
+    ([513, 64], 6, 32, 64, 3, 64, True, False, "f32"),
+    ([1100, 513], 2, 64, 128, 1, 512, True, True, "f32"),
+    ([2048] * 4, 80, 64, 128, 1, 256, True, True, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", range(len(TRAIN_CASES)))
+def test_train_forward_and_saved_backward_bitwise(case):
+    """The training forward gives y and h_out bitwise as the plain prefill, and
+    the backward that takes its saved states gives every gradient bitwise as
+    the backward that recomputes them -- twice in a row on the same saved
+    states (the backward leaves them intact)."""
+    import torch
+    from state_space_model_amd import ssd
+    lengths, H, P, N, G, chunk, h0, dh, dtype = TRAIN_CASES[case]
+    log(f"train forward + saved backward: lengths={lengths} H={H} P={P} N={N} G={G} "
+        f"Q={chunk} h0={h0} dh_out={dh} {dtype}")
+    d = inputs.prefill_inputs(H, P, N, G, lengths, 1300 + case, dtype=dtype, h0=h0)
+    t = dev_inputs(d, dtype)
+    T, nseq = int(d["cu_seqlens"][-1]), len(lengths)
+    dy, dhv = inputs.cotangents(T, nseq, H, P, N, 1400 + case, dtype, dh)
+    dyt = torch.from_numpy(dy).cuda().to(t["x"].dtype)
+    dht = None if dhv is None else torch.from_numpy(dhv).cuda()
+    fwd = (t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"])
+    y1, h1 = ssd.prefill(*fwd, t["h0"], chunk=chunk, cu_seqlens=t["cu_seqlens"])
+    y2, h2, saved = ssd.prefill_train(*fwd, t["h0"], chunk=chunk, cu_seqlens=t["cu_seqlens"])
+    g1 = ssd.prefill_backward(*fwd, dyt, t["h0"], dht, chunk=chunk, cu_seqlens=t["cu_seqlens"])
+    g2 = ssd.prefill_backward(*fwd, dyt, t["h0"], dht, chunk=chunk, cu_seqlens=t["cu_seqlens"],
+                              saved=saved)
+    g3 = ssd.prefill_backward(*fwd, dyt, t["h0"], dht, chunk=chunk, cu_seqlens=t["cu_seqlens"],
+                              saved=saved)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(h1, h2)
+    for k in GRADS:
+        assert torch.equal(g1[k], g2[k]), k
+        assert torch.equal(g1[k], g3[k]), k
+    with pytest.raises(ValueError):
+        ssd.prefill_backward(*fwd, dyt, t["h0"], dht, chunk=chunk * 2 if chunk < 512 else 64,
+                             cu_seqlens=t["cu_seqlens"], saved=saved)
+    log("  bitwise equal")
