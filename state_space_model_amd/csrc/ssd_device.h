@@ -125,6 +125,22 @@ __device__ __forceinline__ Frag<bf16> frag_kmaj(const bf16 *tile, int pitch, int
                                 1, 2, 3, 4, 5, 6, 7);
   return f;
 }
+// frag_kmaj (bf16) with the two row-quad addresses given as byte offsets
+// into an LDS tile (each lane's own address, as frag_kmaj computes them).
+__device__ __forceinline__ Frag<bf16> frag_kmaj_at(const char *lds, int lo, int hi) {
+  const short4v a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)(lds + lo));
+  const short4v b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)(lds + hi));
+  Frag<bf16> f;
+  f.v = __builtin_shufflevector(__builtin_bit_cast(bf16x4, a), __builtin_bit_cast(bf16x4, b), 0,
+                                1, 2, 3, 4, 5, 6, 7);
+  return f;
+}
+// frag_rowk (bf16) at a byte offset: the lane's 8 k-values, 16 bytes.
+__device__ __forceinline__ Frag<bf16> frag_rowk_at(const char *lds, int off) {
+  Frag<bf16> f;
+  f.v = *reinterpret_cast<const bf16x8 *>(lds + off);
+  return f;
+}
 __device__ __forceinline__ Frag<float> frag_kmaj(const float *tile, int pitch, int m0, int rlo,
                                                  int rhi) {
   const int c = m0 + (threadIdx.x & 15);

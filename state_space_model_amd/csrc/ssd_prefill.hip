@@ -205,7 +205,12 @@ template <typename T, int P, int N> struct ScanCfg {
   static constexpr int XP = P + kTrPad, BP = NK + row_pad<T>(), HP = P + kTrPad;
   static constexpr int XS = XP / VN, BS = BP / VN, HS = HP / VN;  // 16-byte slots per row
   static constexpr int XD = P / VN, BD = N / VN;                   // data slots per row
+  // bf16 with 128-byte x and H_in rows and 256-byte B rows: block-swizzled
+  // tiles (whole-block loads, no padding slots) instead of padded rows
+  static constexpr bool SWZ = sizeof(T) == 2 && P == 64 && N == 128;
   static constexpr size_t lds_bytes(int jp, int q) {
+    if (SWZ)
+      return (size_t)(NK / 8 + jp / 8) * kBlk128 + (size_t)(jp / 4) * kBlk256 + 12 * (size_t)q;
     return (size_t)(tile_slots(NK, HS) + tile_slots(jp, BS) + tile_slots(jp, XS)) * 16 +
            12 * (size_t)q;
   }
@@ -231,6 +236,7 @@ __global__ __launch_bounds__(1024) void k_chunk_scan(
   typedef ScanCfg<T, P, N> K;
   constexpr int KS = K::KS, NK = K::NK, XP = K::XP, BP = K::BP, HP = K::HP;
   constexpr int NPT = P / 16;
+  constexpr bool SWZ = K::SWZ;
   const ChunkHead ch = xcd_chunk_head(H * SPLIT);
   const int c = ch.c, hd = ch.h / SPLIT, part = ch.h % SPLIT;
   if (c >= nc) return;
@@ -249,22 +255,41 @@ __global__ __launch_bounds__(1024) void k_chunk_scan(
   const int t0 = 16 * tile;  // first row of the wave's tile (wave-uniform)
 
   extern __shared__ __align__(16) char smem[];
-  T *Hs = reinterpret_cast<T *>(smem);                    // [NK][HP]
-  T *Bs = Hs + tile_slots(NK, K::HS) * K::VN;             // [JP][BP]
-  T *Xs = Bs + tile_slots(JP, K::BS) * K::VN;             // [JP][XP]
-  float *s_l = reinterpret_cast<float *>(Xs + tile_slots(JP, K::XS) * K::VN);  // [Q]
-  float *dt_l = s_l + Q;                                                       // [Q]
+  // padded layout: H_in [NK][HP], B [JP][BP], X [JP][XP] (elements)
+  T *Hs = reinterpret_cast<T *>(smem);
+  T *Bs = Hs + tile_slots(NK, K::HS) * K::VN;
+  T *Xs = Bs + tile_slots(JP, K::BS) * K::VN;
+  // swizzled layout: H_in NK/8 blocks, B JP/4 blocks, X JP/8 blocks
+  char *Hc = smem;
+  char *Bc = Hc + (NK / 8) * kBlk128;
+  char *Xc = Bc + (JP / 4) * kBlk256;
+  float *s_l = SWZ ? reinterpret_cast<float *>(Xc + (JP / 8) * kBlk128)
+                   : reinterpret_cast<float *>(Xs + tile_slots(JP, K::XS) * K::VN);  // [Q]
+  float *dt_l = s_l + Q;                                                          // [Q]
   float *u_l = dt_l + Q;  // [Q] 2^(s_ref(j) - s_j) dt_j, s_ref(j) = s at the end of j's 32-block
 
   const size_t csh = (size_t)c * H + hd;
   const T *xs = x + ((size_t)ci.y * H + hd) * P;
   const T *bs = B + ((size_t)ci.y * G + g) * N;
   const size_t xstride = (size_t)H * P, bstride = (size_t)G * N;
+  // swizzled loads: byte strides, and each lane's offset into a block's rows
+  const uint32_t xsb = (uint32_t)(xstride * sizeof(T)), bsb = (uint32_t)(bstride * sizeof(T));
+  const int lb8 = lane >> 3, lb4 = lane >> 4;
+  const uint32_t xl = lb8 * xsb + 16 * ((lane & 7) ^ (2 * swz8(lb8)));
+  const uint32_t bl = lb4 * bsb + 16 * ((lane & 15) ^ lb4);
+  const uint32_t hl = lb8 * (P * sizeof(T)) + 16 * ((lane & 7) ^ (2 * swz8(lb8)));
 
   // ---- prologue: H_in, the first phase of B/X, C fragments and decays in flight together
-  dma_tile<T, K::HS, K::XD>(Hs, hin + csh * (size_t)(N * P), (size_t)P, NK, N, wave, nw);
-  dma_tile<T, K::BS, K::BD>(Bs, bs, bstride, JP, len, wave, nw);
-  dma_tile<T, K::XS, K::XD>(Xs, xs, xstride, JP, len, wave, nw);
+  if constexpr (SWZ) {
+    const int v0 = max(0, min(len, JP));
+    dma_swz<kBlk128>(Hc, hin + csh * (size_t)(N * P), N * P * sizeof(T), hl, 1024, NK / 8, wave, nw);
+    dma_swz<kBlk256>(Bc, bs, v0 * bsb, bl, 4 * bsb, JP / 4, wave, nw);
+    dma_swz<kBlk128>(Xc, xs, v0 * xsb, xl, 8 * xsb, JP / 8, wave, nw);
+  } else {
+    dma_tile<T, K::HS, K::XD>(Hs, hin + csh * (size_t)(N * P), (size_t)P, NK, N, wave, nw);
+    dma_tile<T, K::BS, K::BD>(Bs, bs, bstride, JP, len, wave, nw);
+    dma_tile<T, K::XS, K::XD>(Xs, xs, xstride, JP, len, wave, nw);
+  }
   const T *Cg = C + ((size_t)ci.y * G + g) * N;
   Frag<T> cf[KS];
   const int i = t0 + col;
@@ -283,6 +308,20 @@ __global__ __launch_bounds__(1024) void k_chunk_scan(
   __builtin_amdgcn_s_waitcnt(0);  // this thread's direct-to-LDS loads have landed
   __syncthreads();
 
+  // lane byte offsets into the swizzled tiles (bits 5-6 hold the segment
+  // swizzle, so segment pt is reached by XOR with 32 pt):
+  //  H_in rows ks*32 + 8 grp + col/4 (+4): block 4 ks + grp, row col/4 (+4)
+  //  X rows jl + 4 grp + col/4 (+16): block jl/8 + grp/2 (+2), row 4 (grp&1) + col/4
+  //  B rows jl + col (+16): block jl/4 + col/4 (+4), row col&3, vector 4 ks + grp
+  //  D x, row r0 + col: block r0/8 + col/8, row col&7, 8 bytes at 32 pt + 8 grp
+  const int c4 = col >> 2, cq = 8 * (col & 3);
+  const int hlo = grp * kBlk128 + c4 * 128 + cq + 32 * swz8(c4);
+  const int hhi = grp * kBlk128 + (4 + c4) * 128 + cq + 32 * swz8(4 + c4);
+  const int xb = 4 * (grp & 1) + c4;
+  const int xo = (grp >> 1) * kBlk128 + xb * 128 + cq + 32 * swz8(xb);
+  const int bo = c4 * kBlk256 + (col & 3) * 256 + 16 * (grp ^ (col & 3));
+  const int dxo = (col >> 3) * kBlk128 + (col & 7) * 128 + 8 * grp + 32 * swz8(col & 7);
+
   // ---- state entering the chunk: Y^T = 2^(s_i) H_in^T C^T
   const bool live = t0 < len;  // wave-uniform
   f4 acc[NPT];
@@ -293,7 +332,11 @@ __global__ __launch_bounds__(1024) void k_chunk_scan(
     for (int pt = 0; pt < NPT; ++pt) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const Frag<T> a = frag_kmaj(Hs, HP, pt * 16, ks * 32 + 8 * grp, ks * 32 + 8 * grp + 4);
+        Frag<T> a;
+        if constexpr (SWZ)
+          a = frag_kmaj_at(Hc + ks * 4 * kBlk128, hlo ^ (32 * pt), hhi ^ (32 * pt));
+        else
+          a = frag_kmaj(Hs, HP, pt * 16, ks * 32 + 8 * grp, ks * 32 + 8 * grp + 4);
         mma(acc[pt], a, cf[ks]);
       }
     }
@@ -309,8 +352,14 @@ __global__ __launch_bounds__(1024) void k_chunk_scan(
   for (int ph = 0; ph < len; ph += JP) {  // phases past the chunk length add nothing
     if (ph > 0) {  // stage the next JP rows (one round trip)
       __syncthreads();
-      dma_tile<T, K::BS, K::BD>(Bs, bs + (size_t)ph * bstride, bstride, JP, len - ph, wave, nw);
-      dma_tile<T, K::XS, K::XD>(Xs, xs + (size_t)ph * xstride, xstride, JP, len - ph, wave, nw);
+      if constexpr (SWZ) {
+        const int vr = min(len - ph, JP);
+        dma_swz<kBlk256>(Bc, bs + (size_t)ph * bstride, vr * bsb, bl, 4 * bsb, JP / 4, wave, nw);
+        dma_swz<kBlk128>(Xc, xs + (size_t)ph * xstride, vr * xsb, xl, 8 * xsb, JP / 8, wave, nw);
+      } else {
+        dma_tile<T, K::BS, K::BD>(Bs, bs + (size_t)ph * bstride, bstride, JP, len - ph, wave, nw);
+        dma_tile<T, K::XS, K::XD>(Xs, xs + (size_t)ph * xstride, xstride, JP, len - ph, wave, nw);
+      }
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
@@ -318,7 +367,11 @@ __global__ __launch_bounds__(1024) void k_chunk_scan(
     if (mine) {  // skip term D x_i
 #pragma unroll
       for (int pt = 0; pt < NPT; ++pt) {
-        const f4 xv = ld4f(Xs + (t0 + col - ph) * XP + pt * 16 + 4 * grp);
+        f4 xv;
+        if constexpr (SWZ)
+          xv = ld4f(reinterpret_cast<const T *>(Xc + (t0 - ph) / 8 * kBlk128 + (dxo ^ (32 * pt))));
+        else
+          xv = ld4f(Xs + (t0 + col - ph) * XP + pt * 16 + 4 * grp);
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[pt][r] += dv * xv[r];
       }
@@ -329,8 +382,15 @@ __global__ __launch_bounds__(1024) void k_chunk_scan(
       f4 g0 = zero4(), g1 = zero4();  // G^T = B C^T for this j-block
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const Frag<T> b0 = frag_rowk(Bs, BP, jl + col, ks * 32 + 8 * grp);
-        const Frag<T> b1 = frag_rowk(Bs, BP, jl + 16 + col, ks * 32 + 8 * grp);
+        Frag<T> b0, b1;
+        if constexpr (SWZ) {
+          const char *bb = Bc + (jl / 4) * kBlk256 + 64 * ks;
+          b0 = frag_rowk_at(bb, bo);
+          b1 = frag_rowk_at(bb + 4 * kBlk256, bo);
+        } else {
+          b0 = frag_rowk(Bs, BP, jl + col, ks * 32 + 8 * grp);
+          b1 = frag_rowk(Bs, BP, jl + 16 + col, ks * 32 + 8 * grp);
+        }
         mma(g0, b0, cf[ks]);
         mma(g1, b1, cf[ks]);
       }
@@ -362,7 +422,13 @@ __global__ __launch_bounds__(1024) void k_chunk_scan(
       const Frag<T> mf = frag_from_f32(m, T());
 #pragma unroll
       for (int pt = 0; pt < NPT; ++pt) {  // Y^T += X^T M^T
-        const Frag<T> a = frag_kmaj(Xs, XP, pt * 16, jl + 4 * grp, jl + 16 + 4 * grp);
+        Frag<T> a;
+        if constexpr (SWZ) {
+          const char *xb_ = Xc + (jl / 8) * kBlk128;
+          a = frag_kmaj_at(xb_, xo ^ (32 * pt), (xo ^ (32 * pt)) + 2 * kBlk128);
+        } else {
+          a = frag_kmaj(Xs, XP, pt * 16, jl + 4 * grp, jl + 16 + 4 * grp);
+        }
         mma(acc[pt], a, mf);
       }
     }

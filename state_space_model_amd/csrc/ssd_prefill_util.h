@@ -86,6 +86,46 @@ __device__ __forceinline__ void dma_tile(T *tile, const T *__restrict__ src, siz
 }
 __host__ __device__ constexpr int tile_slots(int rows, int spr) { return (rows * spr + 63) / 64 * 64; }
 
+// Block-swizzled bf16 tiles.  A tile of 128- or 256-byte rows is held as
+// 1 KB blocks (8 or 4 rows: one direct-load request each) at a pitch of
+// kBlk128 = 1152 or kBlk256 = 1088 bytes.  Inside a block the 16-byte vectors
+// of row b are permuted by an XOR with a function of b instead of padding
+// every row, so a request is one whole block and each lane loads the same
+// (row in block, vector) in every request: its source offset is a constant
+// plus the request's row offset, and no slot is padding.
+//  - 128-byte rows, read by the transposed 8-byte read (a 16-lane group
+//    reads 4 rows x one 32-byte segment s): segment s of row b sits at
+//    s ^ swz8(b).  Rows 0..7 of a block at one segment then fall on 8
+//    distinct 32-byte bank groups of a 256-byte bank window (and any 4
+//    aligned rows on distinct groups of a 128-byte one); the 1152-byte pitch
+//    (128 mod 256) separates rows 0..3 (or 4..7) of neighbouring blocks.
+//  - 256-byte rows, read 16 bytes per lane down 16 rows: vector v of row b
+//    sits at v ^ b, and the 1088-byte pitch (64 mod 256) shifts each block,
+//    so 16 consecutive rows at one vector hit 16 distinct 16-byte bank groups.
+constexpr int kBlk128 = 1152, kBlk256 = 1088;
+__host__ __device__ constexpr int swz8(int b) { return ((b >> 1) & 3) ^ ((b & 1) << 1); }
+
+// Load blocks q = wave, wave + nw, ... < nreq of a swizzled tile (block q at
+// lds + q * BLK) from `src`: the lane's byte offset into block 0's rows is
+// lane_off and block q starts q * req_bytes further.  Only the first
+// valid_bytes of `src` are read: bytes at or past it arrive as zero (the
+// buffer range check), which is how rows past the end of the data are
+// zero-filled.  valid_bytes and every offset must stay below 2^31.
+template <int BLK>
+__device__ __forceinline__ void dma_swz(char *lds, const void *src, uint32_t valid_bytes,
+                                        uint32_t lane_off, uint32_t req_bytes, int nreq,
+                                        int wave, int nw) {
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void *>(src), (short)0, (int)valid_bytes, 0x00020000);
+  uint32_t off = lane_off + (uint32_t)wave * req_bytes;
+  const uint32_t step = (uint32_t)nw * req_bytes;
+  for (int q = wave; q < nreq; q += nw) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void *)(lds + q * BLK), 16, off, 0, 0, 0);
+    off += step;
+  }
+}
+
 // Allow a kernel the full 160 KB of LDS (once per kernel; not a stream
 // operation, so calls under graph capture are unaffected after the first).
 static inline hipError_t set_lds_limit(const void *kern) {
