@@ -38,9 +38,12 @@ template <typename T, int P, int N, int NH_> struct StateCfg {
   static constexpr int NW = TILES >= 8 ? 8 : 4;  // waves (at least 4 for the scan)
   static constexpr int TPW = (TILES + NW - 1) / NW;
   static constexpr int THREADS = 64 * NW;
+  // bf16 with 128-byte x rows and 128-byte B half-rows: block-swizzled tiles
+  static constexpr bool SWZ = sizeof(T) == 2 && P == 64 && NN == 64;
   static constexpr size_t lds_bytes(int jp, int q) {
-    return (size_t)(tile_slots(jp, XS) + tile_slots(jp, BS)) * 16 +
-           4 * (size_t)(3 * q + 64 + 16);  // dt (staged, padded), s, w, scan partials
+    const size_t tiles = SWZ ? (size_t)(jp / 8) * 2 * kBlk128
+                             : (size_t)(tile_slots(jp, XS) + tile_slots(jp, BS)) * 16;
+    return tiles + 4 * (size_t)(3 * q + 64 + 16);  // dt (staged, padded), s, w, scan partials
   }
   // rows staged per phase: at most `cap`, halved until the LDS fits in 80 KB
   static int jp(int q, int cap) {
@@ -59,6 +62,18 @@ __device__ __forceinline__ void scale_rows(T *tile, const float *w, int r0, int 
   for (int idx = threadIdx.x; idx < rows * DATA; idx += blockDim.x) {
     const int r = idx / DATA, v = idx % DATA;
     V *p = reinterpret_cast<V *>(tile + r * PITCH + v * VN);
+    *p = vscale(*p, w[r0 + r]);
+  }
+}
+
+// scale_rows for a block-swizzled tile of 128-byte rows (a row's vectors are
+// permuted within the row, which a per-row scale does not see)
+template <typename T>
+__device__ __forceinline__ void scale_rows_swz(char *tile, const float *w, int r0, int rows) {
+  typedef typename Vec16<T>::type V;
+  for (int idx = threadIdx.x; idx < rows * 8; idx += blockDim.x) {
+    const int r = idx >> 3;
+    V *p = reinterpret_cast<V *>(tile + (r >> 3) * kBlk128 + (r & 7) * 128 + 16 * (idx & 7));
     *p = vscale(*p, w[r0 + r]);
   }
 }
@@ -142,10 +157,13 @@ __global__ __launch_bounds__((StateCfg<T, P, N, NH>::THREADS)) void k_chunk_stat
   const int tid = threadIdx.x, lane = tid & 63, grp = lane >> 4, col = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
+  constexpr bool SWZ = K::SWZ;
   extern __shared__ __align__(16) char smem[];
-  T *Xs = reinterpret_cast<T *>(smem);
+  T *Xs = reinterpret_cast<T *>(smem);  // padded: [JP][XP], [JP][BP]
   T *Bs = Xs + tile_slots(JP, K::XS) * K::VN;
-  float *dt_l = reinterpret_cast<float *>(Bs + tile_slots(JP, K::BS) * K::VN);  // [Q + 64]
+  char *Xc = smem, *Bc = smem + (JP / 8) * kBlk128;  // swizzled: JP/8 blocks each
+  float *dt_l = SWZ ? reinterpret_cast<float *>(Bc + (JP / 8) * kBlk128)
+                    : reinterpret_cast<float *>(Bs + tile_slots(JP, K::BS) * K::VN);  // [Q + 64]
   float *s_l = dt_l + Q + 64;                                                   // [Q]
   float *w_l = s_l + Q;                                                         // [Q]
   float *part = w_l + Q;                                                        // [16]
@@ -154,11 +172,22 @@ __global__ __launch_bounds__((StateCfg<T, P, N, NH>::THREADS)) void k_chunk_stat
   const T *xs = x + (size_t)ci.y * xstride + (size_t)hd * P;
   const T *bs = B + (size_t)ci.y * bstride + (size_t)g * N + half * K::NN;
 
+  // swizzled loads: byte strides and the lane's offset into a block's rows
+  const uint32_t xsb = (uint32_t)(xstride * sizeof(T)), bsb = (uint32_t)(bstride * sizeof(T));
+  const int lb8 = lane >> 3;
+  const uint32_t lo8 = 16 * ((lane & 7) ^ (2 * swz8(lb8)));
+
   // ---- one batch of direct loads: the dt column, first phase of x and B
   dma_dt(dt_l, dt, (size_t)ci.y, H, hd, Q, len, wave, NW);
   if (do_state) {
-    dma_tile<T, K::XS, K::XD>(Xs, xs, xstride, JP, len, wave, NW);
-    dma_tile<T, K::BS, K::BD>(Bs, bs, bstride, JP, len, wave, NW);
+    if constexpr (SWZ) {
+      const uint32_t v0 = (uint32_t)min(len, JP);
+      dma_swz<kBlk128>(Xc, xs, v0 * xsb, lb8 * xsb + lo8, 8 * xsb, JP / 8, wave, NW);
+      dma_swz<kBlk128>(Bc, bs, (v0 - 1) * bsb + 128, lb8 * bsb + lo8, 8 * bsb, JP / 8, wave, NW);
+    } else {
+      dma_tile<T, K::XS, K::XD>(Xs, xs, xstride, JP, len, wave, NW);
+      dma_tile<T, K::BS, K::BD>(Bs, bs, bstride, JP, len, wave, NW);
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -175,21 +204,44 @@ __global__ __launch_bounds__((StateCfg<T, P, N, NH>::THREADS)) void k_chunk_stat
   for (int ph = 0; ph < len; ph += JP) {  // phases past the chunk length add nothing
     if (ph > 0) {
       __syncthreads();
-      dma_tile<T, K::XS, K::XD>(Xs, xs + (size_t)ph * xstride, xstride, JP, len - ph, wave, NW);
-      dma_tile<T, K::BS, K::BD>(Bs, bs + (size_t)ph * bstride, bstride, JP, len - ph, wave, NW);
+      if constexpr (SWZ) {
+        const uint32_t vr = (uint32_t)min(len - ph, JP);
+        dma_swz<kBlk128>(Xc, xs + (size_t)ph * xstride, vr * xsb, lb8 * xsb + lo8, 8 * xsb,
+                         JP / 8, wave, NW);
+        dma_swz<kBlk128>(Bc, bs + (size_t)ph * bstride, (vr - 1) * bsb + 128, lb8 * bsb + lo8,
+                         8 * bsb, JP / 8, wave, NW);
+      } else {
+        dma_tile<T, K::XS, K::XD>(Xs, xs + (size_t)ph * xstride, xstride, JP, len - ph, wave, NW);
+        dma_tile<T, K::BS, K::BD>(Bs, bs + (size_t)ph * bstride, bstride, JP, len - ph, wave, NW);
+      }
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
-    scale_rows<T, K::XP, K::XD>(Xs, w_l, ph, min(JP, len - ph));
+    if constexpr (SWZ)
+      scale_rows_swz<T>(Xc, w_l, ph, min(JP, len - ph));
+    else
+      scale_rows<T, K::XP, K::XD>(Xs, w_l, ph, min(JP, len - ph));
     __syncthreads();
+    // swizzled transposed reads of rows k0 + 8 grp + col/4 (+4): block
+    // k0/8 + grp, row col/4 (+4); segment pt (or nt) by XOR with 32 pt
+    const int c4 = col >> 2, cq = 8 * (col & 3);
+    const int rlo = grp * kBlk128 + c4 * 128 + cq + 32 * swz8(c4);
+    const int rhi = grp * kBlk128 + (4 + c4) * 128 + cq + 32 * swz8(4 + c4);
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
       const int tile = wave + NW * t;
       if (tile < K::TILES) {
         const int pt = tile / NNT, nt = tile % NNT;
         for (int k0 = 0; k0 < JP; k0 += 32) {
-          const Frag<T> a = frag_kmaj(Xs, K::XP, pt * 16, k0 + 8 * grp, k0 + 8 * grp + 4);
-          const Frag<T> b = frag_kmaj(Bs, K::BP, nt * 16, k0 + 8 * grp, k0 + 8 * grp + 4);
+          Frag<T> a, b;
+          if constexpr (SWZ) {
+            const int kb = (k0 / 8) * kBlk128;
+            a = frag_kmaj_at(Xc + kb, rlo ^ (32 * pt), rhi ^ (32 * pt));
+            b = frag_kmaj_at(Bc + kb, rlo ^ (32 * nt), rhi ^ (32 * nt));
+          } else {
+            a = frag_kmaj(Xs, K::XP, pt * 16, k0 + 8 * grp, k0 + 8 * grp + 4);
+            b = frag_kmaj(Bs, K::BP, nt * 16, k0 + 8 * grp, k0 + 8 * grp + 4);
+          }
           mma(acc[t], a, b);
         }
       }
