@@ -38,10 +38,12 @@ template <typename T, int P, int N, int NH_> struct StateCfg {
   static constexpr int NW = TILES >= 8 ? 8 : 4;  // waves (at least 4 for the scan)
   static constexpr int TPW = (TILES + NW - 1) / NW;
   static constexpr int THREADS = 64 * NW;
-  // bf16 with 128-byte x rows and 128-byte B half-rows: block-swizzled tiles
-  static constexpr bool SWZ = sizeof(T) == 2 && P == 64 && NN == 64;
+  // bf16 with 128-byte x rows and 128- or 256-byte B rows: block-swizzled tiles
+  static constexpr bool SWZ = sizeof(T) == 2 && P == 64 && (NN == 64 || NN == 128);
+  static constexpr int B_BLK = NN == 64 ? kBlk128 : kBlk256T;  // B block pitch
+  static constexpr int B_RPB = NN == 64 ? 8 : 4;               // B rows per block
   static constexpr size_t lds_bytes(int jp, int q) {
-    const size_t tiles = SWZ ? (size_t)(jp / 8) * 2 * kBlk128
+    const size_t tiles = SWZ ? (size_t)(jp / 8) * kBlk128 + (size_t)(jp / B_RPB) * B_BLK
                              : (size_t)(tile_slots(jp, XS) + tile_slots(jp, BS)) * 16;
     return tiles + 4 * (size_t)(3 * q + 64 + 16);  // dt (staged, padded), s, w, scan partials
   }
@@ -161,8 +163,8 @@ __global__ __launch_bounds__((StateCfg<T, P, N, NH>::THREADS)) void k_chunk_stat
   extern __shared__ __align__(16) char smem[];
   T *Xs = reinterpret_cast<T *>(smem);  // padded: [JP][XP], [JP][BP]
   T *Bs = Xs + tile_slots(JP, K::XS) * K::VN;
-  char *Xc = smem, *Bc = smem + (JP / 8) * kBlk128;  // swizzled: JP/8 blocks each
-  float *dt_l = SWZ ? reinterpret_cast<float *>(Bc + (JP / 8) * kBlk128)
+  char *Xc = smem, *Bc = smem + (JP / 8) * kBlk128;  // swizzled: JP/8 and JP/B_RPB blocks
+  float *dt_l = SWZ ? reinterpret_cast<float *>(Bc + (JP / K::B_RPB) * K::B_BLK)
                     : reinterpret_cast<float *>(Bs + tile_slots(JP, K::BS) * K::VN);  // [Q + 64]
   float *s_l = dt_l + Q + 64;                                                   // [Q]
   float *w_l = s_l + Q;                                                         // [Q]
@@ -174,8 +176,13 @@ __global__ __launch_bounds__((StateCfg<T, P, N, NH>::THREADS)) void k_chunk_stat
 
   // swizzled loads: byte strides and the lane's offset into a block's rows
   const uint32_t xsb = (uint32_t)(xstride * sizeof(T)), bsb = (uint32_t)(bstride * sizeof(T));
-  const int lb8 = lane >> 3;
+  const int lb8 = lane >> 3, lb4 = lane >> 4;
   const uint32_t lo8 = 16 * ((lane & 7) ^ (2 * swz8(lb8)));
+  // B: 128-byte half-rows as x; 256-byte rows 4 to a block, this wave's
+  // blocks all of the parity of `wave` (NW is even)
+  const uint32_t bl = K::B_RPB == 8 ? lb8 * bsb + lo8
+                                    : lb4 * bsb + 16 * ((lane & 15) ^ (2 * (lb4 ^ (4 * (wave & 1)))));
+  const uint32_t brow = 2 * K::NN;  // bytes of a B row in the tile
 
   // ---- one batch of direct loads: the dt column, first phase of x and B
   dma_dt(dt_l, dt, (size_t)ci.y, H, hd, Q, len, wave, NW);
@@ -183,7 +190,8 @@ __global__ __launch_bounds__((StateCfg<T, P, N, NH>::THREADS)) void k_chunk_stat
     if constexpr (SWZ) {
       const uint32_t v0 = (uint32_t)min(len, JP);
       dma_swz<kBlk128>(Xc, xs, v0 * xsb, lb8 * xsb + lo8, 8 * xsb, JP / 8, wave, NW);
-      dma_swz<kBlk128>(Bc, bs, (v0 - 1) * bsb + 128, lb8 * bsb + lo8, 8 * bsb, JP / 8, wave, NW);
+      dma_swz<K::B_BLK>(Bc, bs, (v0 - 1) * bsb + brow, bl, K::B_RPB * bsb, JP / K::B_RPB, wave,
+                        NW);
     } else {
       dma_tile<T, K::XS, K::XD>(Xs, xs, xstride, JP, len, wave, NW);
       dma_tile<T, K::BS, K::BD>(Bs, bs, bstride, JP, len, wave, NW);
@@ -208,8 +216,8 @@ __global__ __launch_bounds__((StateCfg<T, P, N, NH>::THREADS)) void k_chunk_stat
         const uint32_t vr = (uint32_t)min(len - ph, JP);
         dma_swz<kBlk128>(Xc, xs + (size_t)ph * xstride, vr * xsb, lb8 * xsb + lo8, 8 * xsb,
                          JP / 8, wave, NW);
-        dma_swz<kBlk128>(Bc, bs + (size_t)ph * bstride, (vr - 1) * bsb + 128, lb8 * bsb + lo8,
-                         8 * bsb, JP / 8, wave, NW);
+        dma_swz<K::B_BLK>(Bc, bs + (size_t)ph * bstride, (vr - 1) * bsb + brow, bl,
+                          K::B_RPB * bsb, JP / K::B_RPB, wave, NW);
       } else {
         dma_tile<T, K::XS, K::XD>(Xs, xs + (size_t)ph * xstride, xstride, JP, len - ph, wave, NW);
         dma_tile<T, K::BS, K::BD>(Bs, bs + (size_t)ph * bstride, bstride, JP, len - ph, wave, NW);
@@ -222,11 +230,16 @@ __global__ __launch_bounds__((StateCfg<T, P, N, NH>::THREADS)) void k_chunk_stat
     else
       scale_rows<T, K::XP, K::XD>(Xs, w_l, ph, min(JP, len - ph));
     __syncthreads();
-    // swizzled transposed reads of rows k0 + 8 grp + col/4 (+4): block
-    // k0/8 + grp, row col/4 (+4); segment pt (or nt) by XOR with 32 pt
+    // swizzled transposed reads use the paired k map: rows k0 + 4 grp + col/4
+    // and k0 + 16 + 4 grp + col/4 (any map works when both operands share it);
+    // segment pt (or nt) by XOR with 32 pt (bits 5-6, or 5-7, of the offsets)
+    //  x, and B half-rows: block k0/8 + grp/2 (+2), row 4 (grp&1) + col/4
+    //  B rows of 256 bytes: block k0/4 + grp (+4), row col/4, parity grp&1
     const int c4 = col >> 2, cq = 8 * (col & 3);
-    const int rlo = grp * kBlk128 + c4 * 128 + cq + 32 * swz8(c4);
-    const int rhi = grp * kBlk128 + (4 + c4) * 128 + cq + 32 * swz8(4 + c4);
+    const int xb = 4 * (grp & 1) + c4;
+    const int xo = (grp >> 1) * kBlk128 + xb * 128 + cq + 32 * swz8(xb);
+    const int bo = K::B_RPB == 8 ? xo : grp * kBlk256T + c4 * 256 + cq + 32 * (c4 ^ (4 * (grp & 1)));
+    constexpr int BHI = K::B_RPB == 8 ? 2 * kBlk128 : 4 * kBlk256T;  // +16 rows
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
       const int tile = wave + NW * t;
@@ -235,9 +248,10 @@ __global__ __launch_bounds__((StateCfg<T, P, N, NH>::THREADS)) void k_chunk_stat
         for (int k0 = 0; k0 < JP; k0 += 32) {
           Frag<T> a, b;
           if constexpr (SWZ) {
-            const int kb = (k0 / 8) * kBlk128;
-            a = frag_kmaj_at(Xc + kb, rlo ^ (32 * pt), rhi ^ (32 * pt));
-            b = frag_kmaj_at(Bc + kb, rlo ^ (32 * nt), rhi ^ (32 * nt));
+            const char *xk = Xc + (k0 / 8) * kBlk128;
+            const char *bk = Bc + (k0 / K::B_RPB) * K::B_BLK;
+            a = frag_kmaj_at(xk, xo ^ (32 * pt), (xo ^ (32 * pt)) + 2 * kBlk128);
+            b = frag_kmaj_at(bk, bo ^ (32 * nt), (bo ^ (32 * nt)) + BHI);
           } else {
             a = frag_kmaj(Xs, K::XP, pt * 16, k0 + 8 * grp, k0 + 8 * grp + 4);
             b = frag_kmaj(Bs, K::BP, nt * 16, k0 + 8 * grp, k0 + 8 * grp + 4);

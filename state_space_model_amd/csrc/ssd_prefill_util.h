@@ -102,7 +102,14 @@ __host__ __device__ constexpr int tile_slots(int rows, int spr) { return (rows *
 //  - 256-byte rows, read 16 bytes per lane down 16 rows: vector v of row b
 //    sits at v ^ b, and the 1088-byte pitch (64 mod 256) shifts each block,
 //    so 16 consecutive rows at one vector hit 16 distinct 16-byte bank groups.
-constexpr int kBlk128 = 1152, kBlk256 = 1088;
+//  - 256-byte rows read by the transposed read at rows r0 + 4 g + (0..3) of
+//    lane group g (r0 a multiple of 8, so group g reads block r0/4 + g):
+//    blocks of 4 rows at a pitch of 1024 bytes, and segment s of row b of
+//    block q sits at s ^ b ^ (4 (q & 1)).  A half-wave (groups 0 and 1) then
+//    reads 4 distinct segments of one half of the 256-byte window per block,
+//    the two blocks in opposite halves.  A wave's requests keep one block
+//    parity when the workgroup has an even number of waves.
+constexpr int kBlk128 = 1152, kBlk256 = 1088, kBlk256T = 1024;
 __host__ __device__ constexpr int swz8(int b) { return ((b >> 1) & 3) ^ ((b & 1) << 1); }
 
 // Load blocks q = wave, wave + nw, ... < nreq of a swizzled tile (block q at

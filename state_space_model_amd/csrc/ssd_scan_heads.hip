@@ -37,37 +37,60 @@ template <int P, int N, int Q> struct HeadsCfg {
   static constexpr int KS = N / 32;       // k-steps over n
   static constexpr int NPT = P / 16;      // 16-column tiles of p
   static constexpr int VN = 8;            // bf16 per 16 bytes
+  // 128-byte x / H_in rows and 256-byte B rows: block-swizzled tiles
+  static constexpr bool SWZ = P == 64 && N == 128;
   static constexpr int XP = P + kTrPad, HP = P + kTrPad, BP = N + 8;  // LDS pitches (elements)
   static constexpr int XS = XP / VN, HS = HP / VN, BS = BP / VN;       // 16-byte slots per row
   static constexpr int PD = P / VN, ND = N / VN;                       // data slots per row
   static constexpr int QS = Q / 4;                                     // slots of one float row
-  // one head's buffer: X [Q][XP], H_in [N][HP], s, dt, u [Q] (bytes, 16-aligned)
+  // one head's buffer: X, H_in, s, dt, u (bytes, 16-aligned)
+  static constexpr int X_BYTES = SWZ ? Q / 8 * kBlk128 : tile_slots(Q, XS) * 16;
+  static constexpr int H_BYTES = SWZ ? N / 8 * kBlk128 : tile_slots(N, HS) * 16;
   static constexpr int X_OFF = 0;
-  static constexpr int H_OFF = X_OFF + tile_slots(Q, XS) * 16;
-  static constexpr int S_OFF = H_OFF + tile_slots(N, HS) * 16;
+  static constexpr int H_OFF = X_OFF + X_BYTES;
+  static constexpr int S_OFF = H_OFF + H_BYTES;
   static constexpr int DT_OFF = S_OFF + tile_slots(1, QS) * 16;
   static constexpr int U_OFF = DT_OFF + tile_slots(1, QS) * 16;
   static constexpr int BUF = U_OFF + tile_slots(1, QS) * 16;
-  static constexpr int B_BYTES = tile_slots(Q, BS) * 16;  // B [Q][BP], only before the heads
+  // B, only before the heads
+  static constexpr int B_BYTES = SWZ ? Q / 4 * kBlk256 : tile_slots(Q, BS) * 16;
   static constexpr int LDS = BUF + (BUF > B_BYTES ? BUF : B_BYTES);
   static_assert(P % 16 == 0 && N % 32 == 0 && Q % 32 == 0, "tile shape");
 };
 
-// Issue the direct loads of one head into buffer `buf` (no wait).
+// Issue the direct loads of one head into buffer `buf` (no wait).  Swizzled
+// tiles: xl / hl are the lane's offsets into a block's x / H_in rows.
 template <int P, int N, int Q>
 __device__ __forceinline__ void load_head(char *buf, const bf16 *__restrict__ xs, size_t xstride,
                                           const bf16 *__restrict__ hs, const float *__restrict__ s,
                                           const float *__restrict__ dt,
-                                          const float *__restrict__ u, int len, int wave) {
+                                          const float *__restrict__ u, int len, int wave,
+                                          uint32_t xl, uint32_t hl) {
   typedef HeadsCfg<P, N, Q> K;
-  dma_tile<bf16, K::XS, K::PD>(reinterpret_cast<bf16 *>(buf + K::X_OFF), xs, xstride, Q, len,
-                               wave, K::NW);
-  dma_tile<bf16, K::HS, K::PD>(reinterpret_cast<bf16 *>(buf + K::H_OFF), hs, (size_t)P, N, N,
-                               wave, K::NW);
-  dma_tile<float, K::QS, K::QS>(reinterpret_cast<float *>(buf + K::S_OFF), s, 0, 1, 1, wave, K::NW);
-  dma_tile<float, K::QS, K::QS>(reinterpret_cast<float *>(buf + K::DT_OFF), dt, 0, 1, 1, wave,
-                                K::NW);
-  dma_tile<float, K::QS, K::QS>(reinterpret_cast<float *>(buf + K::U_OFF), u, 0, 1, 1, wave, K::NW);
+  if constexpr (K::SWZ) {
+    const uint32_t xsb = (uint32_t)(xstride * sizeof(bf16));
+    dma_swz<kBlk128>(buf + K::X_OFF, xs, len * xsb, xl, 8 * xsb, Q / 8, wave, K::NW);
+    dma_swz<kBlk128>(buf + K::H_OFF, hs, N * P * 2, hl, 1024, N * P * 2 / 1024, wave, K::NW);
+    // the three float rows, 1 KB requests from different waves
+    const uint32_t fl = 16 * (threadIdx.x & 63);
+    constexpr int NR = (Q * 4 + 1023) / 1024;
+    const int w1 = wave >= 1 % K::NW ? wave - 1 % K::NW : wave - 1 % K::NW + K::NW;
+    const int w2 = wave >= 2 % K::NW ? wave - 2 % K::NW : wave - 2 % K::NW + K::NW;
+    dma_swz<1024>(buf + K::S_OFF, s, Q * 4, fl, 1024, NR, wave, K::NW);
+    dma_swz<1024>(buf + K::DT_OFF, dt, Q * 4, fl, 1024, NR, w1, K::NW);
+    dma_swz<1024>(buf + K::U_OFF, u, Q * 4, fl, 1024, NR, w2, K::NW);
+  } else {
+    dma_tile<bf16, K::XS, K::PD>(reinterpret_cast<bf16 *>(buf + K::X_OFF), xs, xstride, Q, len,
+                                 wave, K::NW);
+    dma_tile<bf16, K::HS, K::PD>(reinterpret_cast<bf16 *>(buf + K::H_OFF), hs, (size_t)P, N, N,
+                                 wave, K::NW);
+    dma_tile<float, K::QS, K::QS>(reinterpret_cast<float *>(buf + K::S_OFF), s, 0, 1, 1, wave,
+                                  K::NW);
+    dma_tile<float, K::QS, K::QS>(reinterpret_cast<float *>(buf + K::DT_OFF), dt, 0, 1, 1, wave,
+                                  K::NW);
+    dma_tile<float, K::QS, K::QS>(reinterpret_cast<float *>(buf + K::U_OFF), u, 0, 1, 1, wave,
+                                  K::NW);
+  }
 }
 
 // The decayed, masked block of M^T for one slot: m = (B C^T)[j][i] * 2^(s_i - s_j) dt_j
@@ -118,6 +141,7 @@ __global__ __launch_bounds__(64 * (Q / 32)) void k_chunk_scan_heads(
     int G, int HB, float *__restrict__ y) {
   typedef HeadsCfg<P, N, Q> K;
   constexpr int NS = K::NS, KS = K::KS, NPT = K::NPT;
+  constexpr bool SWZ = K::SWZ;
   const ChunkHead ch = xcd_chunk_head(H / HB);
   const int c = ch.c, h0 = ch.h * HB;
   if (c >= nc) return;
@@ -144,15 +168,25 @@ __global__ __launch_bounds__(64 * (Q / 32)) void k_chunk_scan_heads(
     o = (size_t)c * H + hd;
     hs = hin + o * (size_t)(N * P);
   };
+  // swizzled loads: the lane's offsets into a block's x, H_in and B rows
+  const int lb8 = lane >> 3, lb4 = lane >> 4;
+  const uint32_t xsb = (uint32_t)(xstride * 2), bsb = (uint32_t)(bstride * 2);
+  const uint32_t xl = lb8 * xsb + 16 * ((lane & 7) ^ (2 * swz8(lb8)));
+  const uint32_t hl = lb8 * (P * 2) + 16 * ((lane & 7) ^ (2 * swz8(lb8)));
 
   // ---- prologue: head h0 -> buffer 0, B -> buffer 1, C^T fragments -> registers
   {
     const bf16 *xs, *hs;
     size_t o;
     head_ptrs(h0, xs, hs, o);
-    load_head<P, N, Q>(buf0, xs, xstride, hs, s_ws + o * Q, dt_ws + o * Q, u_ws + o * Q, len, wave);
+    load_head<P, N, Q>(buf0, xs, xstride, hs, s_ws + o * Q, dt_ws + o * Q, u_ws + o * Q, len, wave,
+                       xl, hl);
   }
-  dma_tile<bf16, K::BS, K::ND>(const_cast<bf16 *>(Bs), bc, bstride, Q, len, wave, K::NW);
+  if constexpr (SWZ)
+    dma_swz<kBlk256>(buf1, bc, len * bsb, lb4 * bsb + 16 * ((lane & 15) ^ lb4), 4 * bsb, Q / 4,
+                     wave, K::NW);
+  else
+    dma_tile<bf16, K::BS, K::ND>(const_cast<bf16 *>(Bs), bc, bstride, Q, len, wave, K::NW);
   Frag<bf16> cfA[KS], cfB[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
@@ -162,6 +196,20 @@ __global__ __launch_bounds__(64 * (Q / 32)) void k_chunk_scan_heads(
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+
+  // lane byte offsets into the swizzled tiles (bits 5-6 hold the segment
+  // swizzle, so segment pt is reached by XOR with 32 pt):
+  //  H_in rows ks*32 + 8 grp + col/4 (+4): block 4 ks + grp, row col/4 (+4)
+  //  X rows jb + 4 grp + col/4 (+16): block jb/8 + grp/2 (+2), row 4 (grp&1) + col/4
+  //  B rows 32 k + col (+16): block 8 k + col/4 (+4), row col&3, vector 4 ks + grp
+  //  D x, row 16 t + col: block 2 t + col/8, row col&7, 8 bytes at 32 pt + 8 grp
+  const int c4 = col >> 2, cq = 8 * (col & 3);
+  const int hlo = grp * kBlk128 + c4 * 128 + cq + 32 * swz8(c4);
+  const int hhi = grp * kBlk128 + (4 + c4) * 128 + cq + 32 * swz8(4 + c4);
+  const int xb = 4 * (grp & 1) + c4;
+  const int xo = (grp >> 1) * kBlk128 + xb * 128 + cq + 32 * swz8(xb);
+  const int bo = c4 * kBlk256 + (col & 3) * 256 + 16 * (grp ^ (col & 3));
+  const int dxo = (col >> 3) * kBlk128 + (col & 7) * 128 + 8 * grp + 32 * swz8(col & 7);
 
   // ---- C.B^T for every slot of both tiles (k = n), kept in registers as
   // bfloat16 (the operand precision of the product it feeds)
@@ -173,8 +221,15 @@ __global__ __launch_bounds__(64 * (Q / 32)) void k_chunk_scan_heads(
       const bool a = k < nA;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const Frag<bf16> b0 = frag_rowk(Bs, K::BP, 32 * k + col, ks * 32 + 8 * grp);
-        const Frag<bf16> b1 = frag_rowk(Bs, K::BP, 32 * k + 16 + col, ks * 32 + 8 * grp);
+        Frag<bf16> b0, b1;
+        if constexpr (SWZ) {
+          const char *bb = buf1 + 8 * k * kBlk256 + 64 * ks;
+          b0 = frag_rowk_at(bb, bo);
+          b1 = frag_rowk_at(bb + 4 * kBlk256, bo);
+        } else {
+          b0 = frag_rowk(Bs, K::BP, 32 * k + col, ks * 32 + 8 * grp);
+          b1 = frag_rowk(Bs, K::BP, 32 * k + 16 + col, ks * 32 + 8 * grp);
+        }
         mma(gB0, b0, cfB[ks]);
         mma(gB1, b1, cfB[ks]);
         if (a) {
@@ -200,7 +255,7 @@ __global__ __launch_bounds__(64 * (Q / 32)) void k_chunk_scan_heads(
       size_t o;
       head_ptrs(hd + 1, xs, hs, o);
       load_head<P, N, Q>((hk & 1) ? buf0 : buf1, xs, xstride, hs, s_ws + o * Q, dt_ws + o * Q,
-                         u_ws + o * Q, len, wave);
+                         u_ws + o * Q, len, wave, xl, hl);
     }
     const bf16 *Xs = reinterpret_cast<const bf16 *>(cur + K::X_OFF);
     const bf16 *Hs = reinterpret_cast<const bf16 *>(cur + K::H_OFF);
@@ -219,7 +274,11 @@ __global__ __launch_bounds__(64 * (Q / 32)) void k_chunk_scan_heads(
       accB[pt] = zero4();
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const Frag<bf16> a = frag_kmaj(Hs, K::HP, pt * 16, ks * 32 + 8 * grp, ks * 32 + 8 * grp + 4);
+        Frag<bf16> a;
+        if constexpr (SWZ)
+          a = frag_kmaj_at(cur + K::H_OFF + ks * 4 * kBlk128, hlo ^ (32 * pt), hhi ^ (32 * pt));
+        else
+          a = frag_kmaj(Hs, K::HP, pt * 16, ks * 32 + 8 * grp, ks * 32 + 8 * grp + 4);
         mma(accA[pt], a, cfA[ks]);
         mma(accB[pt], a, cfB[ks]);
       }
@@ -230,8 +289,15 @@ __global__ __launch_bounds__(64 * (Q / 32)) void k_chunk_scan_heads(
       const float dv = D[hd];
 #pragma unroll
       for (int pt = 0; pt < NPT; ++pt) {  // + D x_i
-        const f4 xA = ld4f(Xs + iA * K::XP + pt * 16 + 4 * grp);
-        const f4 xB = ld4f(Xs + iB * K::XP + pt * 16 + 4 * grp);
+        f4 xA, xB;
+        if constexpr (SWZ) {
+          const char *xc_ = cur + K::X_OFF + (dxo ^ (32 * pt));
+          xA = ld4f(reinterpret_cast<const bf16 *>(xc_ + 2 * tA * kBlk128));
+          xB = ld4f(reinterpret_cast<const bf16 *>(xc_ + 2 * tB * kBlk128));
+        } else {
+          xA = ld4f(Xs + iA * K::XP + pt * 16 + 4 * grp);
+          xB = ld4f(Xs + iB * K::XP + pt * 16 + 4 * grp);
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           accA[pt][r] = accA[pt][r] * eA + dv * xA[r];
@@ -252,7 +318,13 @@ __global__ __launch_bounds__(64 * (Q / 32)) void k_chunk_scan_heads(
       if (k < nA) mA = decay_block(cb[NS - 1 - k], jb, 16 * tA, iAh, siA, s_l, dt_l, u_l, grp);
 #pragma unroll
       for (int pt = 0; pt < NPT; ++pt) {
-        const Frag<bf16> xa = frag_kmaj(Xs, K::XP, pt * 16, jb + 4 * grp, jb + 16 + 4 * grp);
+        Frag<bf16> xa;
+        if constexpr (SWZ) {
+          const char *xb_ = cur + K::X_OFF + (jb / 8) * kBlk128;
+          xa = frag_kmaj_at(xb_, xo ^ (32 * pt), (xo ^ (32 * pt)) + 2 * kBlk128);
+        } else {
+          xa = frag_kmaj(Xs, K::XP, pt * 16, jb + 4 * grp, jb + 16 + 4 * grp);
+        }
         mma(accB[pt], xa, mB);
         mma(accA[pt], xa, mA);
       }
