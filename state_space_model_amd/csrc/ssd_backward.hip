@@ -77,10 +77,23 @@ template <typename T, int MODE, int KD, int VD> struct BwdScanCfg {
   static constexpr int SP = ST_ROWS ? KP : VP;  // state tile pitch
   static constexpr int SD = (ST_ROWS ? KD : VD) / VN;
   static constexpr int SS = SP / VN, KSL = KP / VN, VSL = VP / VN, KDS = KD / VN, VDS = VD / VN;
+  // bf16 with P = 64, N = 128: block-swizzled tiles -- the state [N][P] in
+  // 128-byte rows; K and V rows of 64 (128 bytes) or 128 (256 bytes) values
+  static constexpr bool SWZ = sizeof(T) == 2 && (MODE == kBwdDX ? (KD == 128 && VD == 64)
+                                                                : (KD == 64 && VD == 128));
+  static constexpr size_t s_bytes() { return SWZ ? 16 * kBlk128 : tile_slots(SR, SS) * 16; }
+  static constexpr size_t k_bytes(int jp) {
+    return SWZ ? (KD == 128 ? (size_t)(jp / 4) * kBlk256 : (size_t)(jp / 8) * kBlk128)
+               : (size_t)tile_slots(jp, KSL) * 16;
+  }
+  static constexpr size_t v_bytes(int jp) {
+    return SWZ ? (VD == 64 ? (size_t)(jp / 8) * kBlk128 : (size_t)(jp / 4) * kBlk256T)
+               : (size_t)tile_slots(jp, VSL) * 16;
+  }
   // + s, dt, u rows; DX also keeps one row of W row sums per wave
   static constexpr size_t lds_bytes(int jp, int q, int nw) {
-    return (size_t)(tile_slots(SR, SS) + tile_slots(jp, KSL) + tile_slots(jp, VSL)) * 16 +
-           12 * (size_t)q + (MODE == kBwdDX ? 4 * (size_t)nw * q : 0);
+    return s_bytes() + k_bytes(jp) + v_bytes(jp) + 12 * (size_t)q +
+           (MODE == kBwdDX ? 4 * (size_t)nw * q : 0);
   }
   // rows per phase: up to 64 in blocks of at most 512 threads (under 61 KB),
   // up to 256 otherwise, halved until the LDS fits
@@ -135,16 +148,53 @@ __global__ __launch_bounds__(MAXT) void k_bwd_scan(
   const bool live = t0 < len;  // wave-uniform
   const int tile_last = min(t0 + 15, len - 1);
 
+  constexpr bool SWZ = K::SWZ;
   extern __shared__ __align__(16) char smem[];
-  T *Ss = reinterpret_cast<T *>(smem);                    // state  [SR][SP]
-  T *Ks = Ss + tile_slots(K::SR, K::SS) * K::VN;          // K rows [JP][KP]
-  T *Vs = Ks + tile_slots(JP, K::KSL) * K::VN;            // V rows [JP][VP]
-  float *s_l = reinterpret_cast<float *>(Vs + tile_slots(JP, K::VSL) * K::VN);  // [Q]
+  char *Sc = smem, *Kc = Sc + K::s_bytes(), *Vc = Kc + K::k_bytes(JP);
+  T *Ss = reinterpret_cast<T *>(Sc);  // padded: state [SR][SP]
+  T *Ks = reinterpret_cast<T *>(Kc);  //         K rows [JP][KP]
+  T *Vs = reinterpret_cast<T *>(Vc);  //         V rows [JP][VP]
+  float *s_l = reinterpret_cast<float *>(Vc + K::v_bytes(JP));  // [Q]
   float *dt_l = s_l + Q;                                                        // [Q]
   float *u_l = dt_l + Q;                                                        // [Q]
   float *rs_l = u_l + Q;  // DX: [nw][Q] W row sums, one row per wave
 
   const size_t hstride = (size_t)H * P, gstride = (size_t)G * N;
+  // swizzled tiles: the lane's offsets into a block's rows (x / dy rows of
+  // 128 bytes, B / C rows of 256 bytes; the 256-byte V rows keep the block
+  // parity of `wave`, nw being even) and into the rows it reads
+  const uint32_t hsb = (uint32_t)(hstride * 2), gsb = (uint32_t)(gstride * 2);
+  const int lb8 = lane >> 3, lb4 = lane >> 4;
+  const uint32_t lo8 = 16 * ((lane & 7) ^ (2 * swz8(lb8)));
+  const uint32_t sl = lb8 * (P * 2) + lo8;
+  const uint32_t kl = KD == 128 ? lb4 * gsb + 16 * ((lane & 15) ^ lb4) : lb8 * hsb + lo8;
+  const uint32_t vl = VD == 64 ? lb8 * hsb + lo8
+                               : lb4 * gsb + 16 * ((lane & 15) ^ (2 * (lb4 ^ (4 * (wave & 1)))));
+  const uint32_t ksb = KD == 128 ? gsb : hsb, vsb = VD == 64 ? hsb : gsb;
+  const int c4 = col >> 2, cq = 8 * (col & 3);
+  //  transposed, natural k map (state, DX): rows 32 kk + 8 grp + col/4 (+4)
+  const int so_lo = grp * kBlk128 + c4 * 128 + cq + 32 * swz8(c4);
+  const int so_hi = grp * kBlk128 + (4 + c4) * 128 + cq + 32 * swz8(4 + c4);
+  //  row reads of 128-byte rows r0 + col: block r0/8 + col/8, vector 4 kk + grp
+  const int r128 = (col >> 3) * kBlk128 + (col & 7) * 128 + 16 * (grp ^ (2 * swz8(col & 7)));
+  //  row reads of 256-byte rows jl + col: block jl/4 + col/4, vector 4 kk + grp
+  const int r256 = c4 * kBlk256 + (col & 3) * 256 + 16 * (grp ^ (col & 3));
+  //  transposed, paired k map (V): rows jl + 4 grp + col/4 (+16)
+  const int xb = 4 * (grp & 1) + c4;
+  const int v128 = (grp >> 1) * kBlk128 + xb * 128 + cq + 32 * swz8(xb);
+  const int v256 = grp * kBlk256T + c4 * 256 + cq + 32 * (c4 ^ (4 * (grp & 1)));
+  auto load_k = [&](const T *src, int rows) {
+    if constexpr (KD == 128)
+      dma_swz<kBlk256>(Kc, src, rows * ksb, kl, 4 * ksb, JP / 4, wave, nw);
+    else
+      dma_swz<kBlk128>(Kc, src, rows * ksb, kl, 8 * ksb, JP / 8, wave, nw);
+  };
+  auto load_v = [&](const T *src, int rows) {
+    if constexpr (VD == 64)
+      dma_swz<kBlk128>(Vc, src, rows * vsb, vl, 8 * vsb, JP / 8, wave, nw);
+    else
+      dma_swz<kBlk256T>(Vc, src, rows * vsb, vl, 4 * vsb, JP / 4, wave, nw);
+  };
   const T *Bg = B + (size_t)ci.y * gstride + (size_t)g * N;
   const T *Cg = C + (size_t)ci.y * gstride + (size_t)g * N;
   f4 acc[NVT];
@@ -167,10 +217,18 @@ __global__ __launch_bounds__(MAXT) void k_bwd_scan(
     if (hh > 0) __syncthreads();  // the previous head's tiles are no longer read
 
     // ---- prologue: the state tile and the first phase of K/V rows in flight together
-    dma_tile<T, K::SS, K::SD>(Ss, state + csh * (size_t)(N * P), (size_t)P, K::SR,
-                              K::ST_ROWS ? VD : KD, wave, nw);
-    dma_tile<T, K::KSL, K::KDS>(Ks, kg, ks_, JP, len, wave, nw);
-    dma_tile<T, K::VSL, K::VDS>(Vs, vg, vs, JP, len, wave, nw);
+    if constexpr (SWZ) {
+      const int v0 = min(len, JP);
+      dma_swz<kBlk128>(Sc, state + csh * (size_t)(N * P), N * P * 2, sl, 1024, N * P * 2 / 1024,
+                       wave, nw);
+      load_k(kg, v0);
+      load_v(vg, v0);
+    } else {
+      dma_tile<T, K::SS, K::SD>(Ss, state + csh * (size_t)(N * P), (size_t)P, K::SR,
+                                K::ST_ROWS ? VD : KD, wave, nw);
+      dma_tile<T, K::KSL, K::KDS>(Ks, kg, ks_, JP, len, wave, nw);
+      dma_tile<T, K::VSL, K::VDS>(Vs, vg, vs, JP, len, wave, nw);
+    }
     dti = dt_ws[csh * Q + i];
     Frag<T> qf[KS];
 #pragma unroll
@@ -221,7 +279,11 @@ __global__ __launch_bounds__(MAXT) void k_bwd_scan(
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
           Frag<T> a;
-          if constexpr (K::ST_ROWS)
+          if constexpr (SWZ && K::ST_ROWS)
+            a = frag_rowk_at(Sc + 2 * vt * kBlk128, r128 ^ (64 * kk));
+          else if constexpr (SWZ)
+            a = frag_kmaj_at(Sc + kk * 4 * kBlk128, so_lo ^ (32 * vt), so_hi ^ (32 * vt));
+          else if constexpr (K::ST_ROWS)
             a = frag_rowk(Ss, K::SP, vt * 16 + col, kk * 32 + 8 * grp);
           else
             a = frag_kmaj(Ss, K::SP, vt * 16, kk * 32 + 8 * grp, kk * 32 + 8 * grp + 4);
@@ -248,8 +310,14 @@ __global__ __launch_bounds__(MAXT) void k_bwd_scan(
     for (int ph = 0; ph < len; ph += JP) {
       if (ph > 0) {
         __syncthreads();
-        dma_tile<T, K::KSL, K::KDS>(Ks, kg + (size_t)ph * ks_, ks_, JP, len - ph, wave, nw);
-        dma_tile<T, K::VSL, K::VDS>(Vs, vg + (size_t)ph * vs, vs, JP, len - ph, wave, nw);
+        if constexpr (SWZ) {
+          const int vr = min(len - ph, JP);
+          load_k(kg + (size_t)ph * ks_, vr);
+          load_v(vg + (size_t)ph * vs, vr);
+        } else {
+          dma_tile<T, K::KSL, K::KDS>(Ks, kg + (size_t)ph * ks_, ks_, JP, len - ph, wave, nw);
+          dma_tile<T, K::VSL, K::VDS>(Vs, vg + (size_t)ph * vs, vs, JP, len - ph, wave, nw);
+        }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
       }
@@ -266,8 +334,19 @@ __global__ __launch_bounds__(MAXT) void k_bwd_scan(
         f4 g0 = zero4(), g1 = zero4();  // (K Q^T) for rows jb..jb+15 and jb+16..jb+31
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
-          const Frag<T> k0 = frag_rowk(Ks, K::KP, jl + col, kk * 32 + 8 * grp);
-          const Frag<T> k1 = frag_rowk(Ks, K::KP, jl + 16 + col, kk * 32 + 8 * grp);
+          Frag<T> k0, k1;
+          if constexpr (SWZ && KD == 128) {
+            const char *kb = Kc + (jl / 4) * kBlk256 + 64 * kk;
+            k0 = frag_rowk_at(kb, r256);
+            k1 = frag_rowk_at(kb + 4 * kBlk256, r256);
+          } else if constexpr (SWZ) {
+            const char *kb = Kc + (jl / 8) * kBlk128;
+            k0 = frag_rowk_at(kb, r128 ^ (64 * kk));
+            k1 = frag_rowk_at(kb + 2 * kBlk128, r128 ^ (64 * kk));
+          } else {
+            k0 = frag_rowk(Ks, K::KP, jl + col, kk * 32 + 8 * grp);
+            k1 = frag_rowk(Ks, K::KP, jl + 16 + col, kk * 32 + 8 * grp);
+          }
           mma(g0, k0, qf[kk]);
           mma(g1, k1, qf[kk]);
         }
@@ -309,7 +388,16 @@ __global__ __launch_bounds__(MAXT) void k_bwd_scan(
         const Frag<T> mf = frag_from_f32(m, T());
 #pragma unroll
         for (int vt = 0; vt < NVT; ++vt) {
-          const Frag<T> a = frag_kmaj(Vs, K::VP, vt * 16, jl + 4 * grp, jl + 16 + 4 * grp);
+          Frag<T> a;
+          if constexpr (SWZ && VD == 64) {
+            const int o = v128 ^ (32 * vt);
+            a = frag_kmaj_at(Vc + (jl / 8) * kBlk128, o, o + 2 * kBlk128);
+          } else if constexpr (SWZ) {
+            const int o = v256 ^ (32 * vt);
+            a = frag_kmaj_at(Vc + jl * 256, o, o + 4 * kBlk256T);
+          } else {
+            a = frag_kmaj(Vs, K::VP, vt * 16, jl + 4 * grp, jl + 16 + 4 * grp);
+          }
           mma(acc[vt], a, mf);
         }
         if constexpr (MODE == kBwdDX) {
@@ -317,8 +405,15 @@ __global__ __launch_bounds__(MAXT) void k_bwd_scan(
           f4 d0 = zero4(), d1 = zero4();
 #pragma unroll
           for (int kk = 0; kk < KSP; ++kk) {
-            const Frag<T> a0 = frag_rowk(Vs, K::VP, jl + col, kk * 32 + 8 * grp);
-            const Frag<T> a1 = frag_rowk(Vs, K::VP, jl + 16 + col, kk * 32 + 8 * grp);
+            Frag<T> a0, a1;
+            if constexpr (SWZ) {
+              const char *vb = Vc + (jl / 8) * kBlk128;
+              a0 = frag_rowk_at(vb, r128 ^ (64 * kk));
+              a1 = frag_rowk_at(vb + 2 * kBlk128, r128 ^ (64 * kk));
+            } else {
+              a0 = frag_rowk(Vs, K::VP, jl + col, kk * 32 + 8 * grp);
+              a1 = frag_rowk(Vs, K::VP, jl + 16 + col, kk * 32 + 8 * grp);
+            }
             mma(d0, a0, xf[kk]);
             mma(d1, a1, xf[kk]);
           }
