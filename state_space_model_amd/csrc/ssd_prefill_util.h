@@ -112,23 +112,36 @@ __host__ __device__ constexpr int tile_slots(int rows, int spr) { return (rows *
 constexpr int kBlk128 = 1152, kBlk256 = 1088, kBlk256T = 1024;
 __host__ __device__ constexpr int swz8(int b) { return ((b >> 1) & 3) ^ ((b & 1) << 1); }
 
+// One 16-byte-per-lane buffer load into LDS at lds_addr + 16 * lane, issued
+// from inline assembly.  The compiler then does not see a pending LDS write:
+// through the builtin it would wait for every such load before the next LDS
+// read anywhere in the workgroup's code, which serialises a load into one
+// buffer with reads of the other.  Callers wait themselves (s_waitcnt
+// vmcnt(0) and a barrier) before anything reads the loaded bytes.
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t rs, uint32_t lds_addr,
+                                           uint32_t voff) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "{m0}"(lds_addr)
+               : "memory");
+}
+
 // Load blocks q = wave, wave + nw, ... < nreq of a swizzled tile (block q at
 // lds + q * BLK) from `src`: the lane's byte offset into block 0's rows is
 // lane_off and block q starts q * req_bytes further.  Only the first
 // valid_bytes of `src` are read: bytes at or past it arrive as zero (the
 // buffer range check), which is how rows past the end of the data are
-// zero-filled.  valid_bytes and every offset must stay below 2^31.
+// zero-filled.  valid_bytes and every offset must stay below 2^31.  No wait:
+// the caller waits for vmcnt(0) and synchronises before reading the tile.
 template <int BLK>
 __device__ __forceinline__ void dma_swz(char *lds, const void *src, uint32_t valid_bytes,
                                         uint32_t lane_off, uint32_t req_bytes, int nreq,
                                         int wave, int nw) {
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<void *>(src), (short)0, (int)valid_bytes, 0x00020000);
+  const uint32_t base = (uint32_t)(size_t)(__attribute__((address_space(3))) char *)lds;
   uint32_t off = lane_off + (uint32_t)wave * req_bytes;
   const uint32_t step = (uint32_t)nw * req_bytes;
   for (int q = wave; q < nreq; q += nw) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rs, (__attribute__((address_space(3))) void *)(lds + q * BLK), 16, off, 0, 0, 0);
+    lds_load16(rs, base + q * BLK, off);
     off += step;
   }
 }
