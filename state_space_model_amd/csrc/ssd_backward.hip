@@ -894,12 +894,10 @@ hipError_t launch_prefill_train_forward(const PrefillArgs &f) {
   char *ws = static_cast<char *>(f.workspace);
   float *hfin = reinterpret_cast<float *>(ws + L.hfin);
   PrefillArgs fa = f;
-  fa.h_out = hfin;
+  fa.h_out = hfin;  // the state pass writes the final state here and to the caller's h_out
+  fa.h_out2 = f.h_out;
   fa.hin32 = reinterpret_cast<float *>(ws + L.hin32);
-  hipError_t e = launch_prefill(fa, 15u);
-  if (e != hipSuccess || !f.h_out) return e;
-  return hipMemcpyAsync(f.h_out, hfin, sizeof(float) * (size_t)f.nseq * f.H * f.N * f.P,
-                        hipMemcpyDeviceToDevice, static_cast<hipStream_t>(f.stream));
+  return launch_prefill(fa, 15u);
 }
 
 }  // namespace ssd

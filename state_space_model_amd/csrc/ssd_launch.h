@@ -20,6 +20,7 @@ struct PrefillArgs {
   void *workspace;
   void *stream;
   float *hin32 = nullptr;  // optional float32 copy of the state entering each chunk
+  float *h_out2 = nullptr;  // optional second destination of the final state
 };
 
 // Byte offsets of the prefill workspace regions (each 256-byte aligned).

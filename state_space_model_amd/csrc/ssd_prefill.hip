@@ -130,7 +130,8 @@ hipError_t launch_chunk_map(const int32_t *cu, int nseq, int64_t T, int Q, int n
 // ----------------------------------------------------------- K3 state pass
 // Per (sequence, head), per 4 state elements: walk the sequence's chunks in
 // order, emit the state entering each chunk (as the MFMA operand type, and
-// optionally as float32) and the final state.
+// optionally as float32) and the final state (to h_out, and to h_out2 when
+// given).
 
 template <typename T>
 __global__ __launch_bounds__(256) void k_state_pass(const float *__restrict__ S,
@@ -138,7 +139,7 @@ __global__ __launch_bounds__(256) void k_state_pass(const float *__restrict__ S,
                                                     const int *__restrict__ seq_off,
                                                     ChunkMap cmap, const float *h0, float *h_out,
                                                     T *__restrict__ hin, int H, int NP, int Q,
-                                                    float *__restrict__ hin32) {
+                                                    float *__restrict__ hin32, float *h_out2) {
   constexpr int BATCH = 8;  // chunk states in flight per thread
   const int s = blockIdx.z, hd = blockIdx.y;
   const int e = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
@@ -177,6 +178,7 @@ __global__ __launch_bounds__(256) void k_state_pass(const float *__restrict__ S,
     }
   }
   if (h_out) st4(h_out + hofs, st);
+  if (h_out2) st4(h_out2 + hofs, st);
 }
 
 // ------------------------------------------------------------ K4 chunk scan
@@ -499,7 +501,7 @@ static hipError_t run_prefill(const PrefillArgs &a, unsigned stages) {
   if (stages & 4u) {
     const int NP = N * P;
     hipLaunchKernelGGL(k_state_pass<T>, dim3((NP + 1023) / 1024, a.H, a.nseq), dim3(256), 0, st,
-                       S, s_ws, seq_off, cmap, a.h0, a.h_out, hin, a.H, NP, a.Q, a.hin32);
+                       S, s_ws, seq_off, cmap, a.h0, a.h_out, hin, a.H, NP, a.Q, a.hin32, a.h_out2);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
