@@ -505,7 +505,10 @@ static hipError_t run_prefill(const PrefillArgs &a, unsigned stages) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int HB = (stages & 8u) ? scan_heads_choice(P, N, a.Q, a.bf16, nc, a.H, a.G) : 0;
+  // the head-count choice counts the chunks exactly for a dense batch (nc is
+  // an upper bound)
+  const int nc_real = L_dense > 0 ? a.nseq * ((L_dense + a.Q - 1) / a.Q) : nc;
+  const int HB = (stages & 8u) ? scan_heads_choice(P, N, a.Q, a.bf16, nc_real, a.H, a.G) : 0;
   if ((stages & 8u) && nc > 0 && HB > 0) {
     hipError_t e = launch_scan_heads(a, L, nc, HB, st);
     if (e != hipSuccess) return e;

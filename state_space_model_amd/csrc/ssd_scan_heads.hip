@@ -22,6 +22,7 @@
 // constant.  Each lane holds, per slot, the pair layout of two stacked 16x16
 // results (rows 4g..4g+3 and 16+4g..16+4g+3 of the block, column i): after the
 // decay it is the B operand of Y^T += X^T M^T as it stands.
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 
@@ -387,11 +388,13 @@ static hipError_t run_heads(const PrefillArgs &a, const WorkspaceLayout &L, int 
 
 // Whether to stream heads, and how many per workgroup (0: use the row-split
 // scan).  Streaming pays once there are several workgroups of heads per CU:
-// one workgroup fills a CU (LDS), and a short stream spends most of its time
-// loading B and forming C.B^T.  HB is the largest divisor of H/G up to 8 that
-// still leaves two workgroups per CU.  SSD_PREFILL_SCAN=heads|rows overrides
-// the choice (used by the tests to run both kernels on the same shapes).
-static int pick_heads(int nc, int H, int G) {
+// a short stream spends most of its time loading B and forming C.B^T.  The
+// head count d (a divisor of H/G) minimises rounds(d) * (d + 2): rounds of
+// resident workgroups (`slots` of them at once) times the time of one
+// workgroup, d heads plus a fixed cost (B, C.B^T, the first head's loads)
+// taken as two heads' worth.  Ties go to the larger d.  SSD_PREFILL_SCAN=heads|rows overrides the choice
+// of kernel (used by the tests to run both kernels on the same shapes).
+static int pick_heads(int nc, int H, int G, long slots) {
   const char *force = getenv("SSD_PREFILL_SCAN");
   const bool want_rows = force && strcmp(force, "rows") == 0;
   const bool want_heads = force && strcmp(force, "heads") == 0;
@@ -399,24 +402,41 @@ static int pick_heads(int nc, int H, int G) {
   if (want_rows || (!want_heads && units < 2048)) return 0;
   const int hg = H / G;
   int best = 1;
-  for (int d = 1; d <= hg && d <= 8; ++d)
-    if (hg % d == 0 && (units / d >= 512 || d == 1)) best = d;
+  long best_cost = -1;
+  for (int d = 1; d <= hg; ++d) {
+    if (hg % d) continue;
+    const long wgs = units / d, rounds = (wgs + slots - 1) / slots;
+    const long cost = rounds * (d + 2);
+    if (best_cost < 0 || cost <= best_cost) {
+      best = d;
+      best_cost = cost;
+    }
+  }
   return best;
 }
 
 #define SSD_HEADS_CASES(X) X(64, 128, 256) X(64, 128, 128) X(64, 128, 64) X(64, 64, 256) \
   X(64, 64, 128) X(32, 128, 256) X(32, 64, 256)
 
-static bool has_instance(int P, int N, int Q, bool bf16) {
-  if (!bf16) return false;
-#define SSD_CASE(p, n, q) if (P == p && N == n && Q == q) return true;
+// Workgroups of one instance resident on the chip at once (256 CUs): bounded
+// by LDS and by the waves a CU holds at the kernel's register use (two per
+// SIMD); 0 when there is no instance for the shape.
+static long heads_slots(int P, int N, int Q, bool bf16) {
+  if (!bf16) return 0;
+#define SSD_CASE(p, n, q)                                                    \
+  if (P == p && N == n && Q == q) {                                          \
+    const long by_lds = (160L * 1024) / HeadsCfg<p, n, q>::LDS;              \
+    const long by_waves = 8 / HeadsCfg<p, n, q>::NW;                         \
+    return 256 * std::max(1L, std::min(by_lds, by_waves));                   \
+  }
   SSD_HEADS_CASES(SSD_CASE)
 #undef SSD_CASE
-  return false;
+  return 0;
 }
 
 int scan_heads_choice(int P, int N, int Q, bool bf16, int nc, int H, int G) {
-  return has_instance(P, N, Q, bf16) ? pick_heads(nc, H, G) : 0;
+  const long slots = heads_slots(P, N, Q, bf16);
+  return slots > 0 ? pick_heads(nc, H, G, slots) : 0;
 }
 
 hipError_t launch_scan_heads(const PrefillArgs &a, const WorkspaceLayout &L, int nc, int HB,
