@@ -82,6 +82,26 @@ def test_prefill_small(dtype, scan, case):
     assert ey <= TOL[dtype] and eh <= TOL[dtype]
 
 
+def test_prefill_heads_streamed_several_heads_per_workgroup():
+    """80 heads in 2 groups at chunk 256 over a packed pair of ragged
+    sequences (17 chunks x 80 heads): forced onto the heads-streamed scan, the
+    head-count rule gives each workgroup 8 heads of a group, so the next-head
+    loads, the buffer swap and the shared C.B^T all run; checked against the
+    full oracle in bfloat16 and against the row-split scan."""
+    lengths, H, P, N, G, chunk = [2500, 1596], 80, 64, 128, 2, 256
+    log(f"prefill heads streamed, several heads per workgroup: lengths={lengths} H={H} G={G}")
+    d = inputs.prefill_inputs(H, P, N, G, lengths, 4242, dtype="bf16", h0=True)
+    with kernels("heads"):
+        y, ho = _gpu(d, "bf16", chunk)
+    with kernels("rows"):
+        y2, ho2 = _gpu(d, "bf16", chunk)
+    ry, rh = _ref(d)
+    ey, eh = maxabs(y, ry), maxabs(ho, rh)
+    log(f"  max|dy|={ey:.3g} max|dh|={eh:.3g} vs rows {maxabs(y, y2):.3g}")
+    assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
+    assert maxabs(ho, ho2) == 0.0  # the state path is the same kernels in both
+
+
 def test_prefill_tiny_workload_f32():
     w = inputs.WORKLOADS[0]
     log("prefill workload 0 (tiny, float32)")
