@@ -210,9 +210,11 @@ template <typename T, int P, int N> struct ScanCfg {
   // bf16 with 128-byte x and H_in rows and 256-byte B rows: block-swizzled
   // tiles (whole-block loads, no padding slots) instead of padded rows
   static constexpr bool SWZ = sizeof(T) == 2 && P == 64 && N == 128;
+  // one float row of q values, staged whole 1 KB requests at a time
+  static constexpr size_t frow_bytes(int q) { return ((size_t)q * 4 + 1023) / 1024 * 1024; }
   static constexpr size_t lds_bytes(int jp, int q) {
     if (SWZ)
-      return (size_t)(NK / 8 + jp / 8) * kBlk128 + (size_t)(jp / 4) * kBlk256 + 12 * (size_t)q;
+      return (size_t)(NK / 8 + jp / 8) * kBlk128 + (size_t)(jp / 4) * kBlk256 + 3 * frow_bytes(q);
     return (size_t)(tile_slots(NK, HS) + tile_slots(jp, BS) + tile_slots(jp, XS)) * 16 +
            12 * (size_t)q;
   }
@@ -233,8 +235,8 @@ template <typename T, int P, int N, int SPLIT>
 __global__ __launch_bounds__(1024) void k_chunk_scan(
     const T *__restrict__ x, const T *__restrict__ B, const T *__restrict__ C,
     const float *__restrict__ D, const float *__restrict__ s_ws, const float *__restrict__ dt_ws,
-    const T *__restrict__ hin, ChunkMap cmap, int nc, int H, int G, int Q,
-    int JP, float *__restrict__ y) {
+    const float *__restrict__ u_ws, const T *__restrict__ hin, ChunkMap cmap, int nc, int H,
+    int G, int Q, int JP, float *__restrict__ y) {
   typedef ScanCfg<T, P, N> K;
   constexpr int KS = K::KS, NK = K::NK, XP = K::XP, BP = K::BP, HP = K::HP;
   constexpr int NPT = P / 16;
@@ -267,8 +269,10 @@ __global__ __launch_bounds__(1024) void k_chunk_scan(
   char *Xc = Bc + (JP / 4) * kBlk256;
   float *s_l = SWZ ? reinterpret_cast<float *>(Xc + (JP / 8) * kBlk128)
                    : reinterpret_cast<float *>(Xs + tile_slots(JP, K::XS) * K::VN);  // [Q]
-  float *dt_l = s_l + Q;                                                          // [Q]
-  float *u_l = dt_l + Q;  // [Q] 2^(s_ref(j) - s_j) dt_j, s_ref(j) = s at the end of j's 32-block
+  // [Q] each (swizzled layout: rows rounded up to 1 KB, filled by whole requests)
+  const int FR = SWZ ? (int)K::frow_bytes(Q) / 4 : Q;
+  float *dt_l = s_l + FR;
+  float *u_l = dt_l + FR;  // 2^(s_ref(j) - s_j) dt_j, s_ref(j) = s at the end of j's 32-block
 
   const size_t csh = (size_t)c * H + hd;
   const T *xs = x + ((size_t)ci.y * H + hd) * P;
@@ -287,6 +291,13 @@ __global__ __launch_bounds__(1024) void k_chunk_scan(
     dma_swz<kBlk128>(Hc, hin + csh * (size_t)(N * P), N * P * sizeof(T), hl, 1024, NK / 8, wave, nw);
     dma_swz<kBlk256>(Bc, bs, v0 * bsb, bl, 4 * bsb, JP / 4, wave, nw);
     dma_swz<kBlk128>(Xc, xs, v0 * xsb, xl, 8 * xsb, JP / 8, wave, nw);
+    // the chunk's s, dt and u rows (written by the chunk-state stage), one
+    // wave each
+    const uint32_t fl = 16 * lane;
+    const int nr = FR / 256, w1 = (wave + nw - 1 % nw) % nw, w2 = (wave + nw - 2 % nw) % nw;
+    dma_swz<1024>(reinterpret_cast<char *>(s_l), s_ws + csh * Q, Q * 4, fl, 1024, nr, wave, nw);
+    dma_swz<1024>(reinterpret_cast<char *>(dt_l), dt_ws + csh * Q, Q * 4, fl, 1024, nr, w1, nw);
+    dma_swz<1024>(reinterpret_cast<char *>(u_l), u_ws + csh * Q, Q * 4, fl, 1024, nr, w2, nw);
   } else {
     dma_tile<T, K::HS, K::XD>(Hs, hin + csh * (size_t)(N * P), (size_t)P, NK, N, wave, nw);
     dma_tile<T, K::BS, K::BD>(Bs, bs, bstride, JP, len, wave, nw);
@@ -301,11 +312,12 @@ __global__ __launch_bounds__(1024) void k_chunk_scan(
     cf[ks] = (i < len && n8 < N) ? frag_global(Cg + (size_t)i * bstride + n8) : frag_zero<T>();
   }
   const float si = s_ws[csh * Q + i];
-  for (int j = threadIdx.x; j < Q; j += blockDim.x) {
-    const float sv = s_ws[csh * Q + j], dv = dt_ws[csh * Q + j];
-    s_l[j] = sv;
-    dt_l[j] = dv;
-    u_l[j] = __builtin_amdgcn_exp2f(fminf(s_ws[csh * Q + (j | 31)] - sv, 0.f)) * dv;
+  if (!SWZ) {
+    for (int j = threadIdx.x; j < Q; j += blockDim.x) {
+      s_l[j] = s_ws[csh * Q + j];
+      dt_l[j] = dt_ws[csh * Q + j];
+      u_l[j] = u_ws[csh * Q + j];
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);  // this thread's direct-to-LDS loads have landed
   __syncthreads();
@@ -530,7 +542,8 @@ static hipError_t run_prefill(const PrefillArgs &a, unsigned stages) {
     const float *Dp = a.D;
     float *yp = a.y;
     ChunkMap cm = cmap;
-    void *args[] = {&xp, &bp, &cp, &Dp, &s_ws, &dt_ws, &hp, &cm, &nc_, &H_, &G_, &Q_, &jp_, &yp};
+    void *args[] = {&xp, &bp, &cp, &Dp, &s_ws, &dt_ws, &u_ws, &hp, &cm, &nc_, &H_, &G_, &Q_, &jp_,
+                    &yp};
     e = hipLaunchKernel(kern, dim3(xcd_grid(nc, a.H * split)), dim3(threads), args, lds, st);
     if (e != hipSuccess) return e;
   }
