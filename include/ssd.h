@@ -93,7 +93,9 @@ size_t ssd_scan_prefill_workspace(int64_t total_tokens, int nseq, int H, int P, 
  *            ssd_scan_prefill_workspace(...) bytes (256-byte aligned)
  *
  * Supported: P in {16,32,64,128}, N in {16,32,64,128}, chunk in
- * {32,64,128,256,512}, H % G == 0.  T = 0 copies h0 (or zeros) to h_out.
+ * {32,64,128,256,512}, H % G == 0, and H*P*chunk*4 and G*N*chunk*4 below
+ * 2^31 (a chunk's rows are addressed with 32-bit offsets; otherwise
+ * SSD_ERR_UNSUPPORTED).  T = 0 copies h0 (or zeros) to h_out.
  * Splitting a sequence at any token and passing h_out of the first part as h0
  * of the second gives the same result as one call.
  */

@@ -46,6 +46,9 @@ int check_prefill(const void *x, const float *dt, const float *A, const void *B,
     return fail(SSD_ERR_INVALID_ARG, "null x/dt/B/C/y pointer");
   if (!A || !D) return fail(SSD_ERR_INVALID_ARG, "null A/D pointer");
   if ((int64_t)T * H > INT32_MAX * 16LL) return fail(SSD_ERR_UNSUPPORTED, "problem too large");
+  // tile loads address a chunk's rows with 32-bit byte offsets
+  if ((int64_t)chunk * H * P * 4 > INT32_MAX || (int64_t)chunk * G * N * 4 > INT32_MAX)
+    return fail(SSD_ERR_UNSUPPORTED, "chunk x row stride too large (H*P*chunk*4 and G*N*chunk*4 must stay below 2^31)");
   return SSD_OK;
 }
 

@@ -63,6 +63,7 @@ def _prefill_rc(**kw):
     (dict(N=100), -2, "d_state"),
     (dict(chunk=48), -2, "chunk"),
     (dict(chunk=1024), -2, "chunk"),
+    (dict(H=8192, P=128, chunk=512), -2, "row stride"),  # 32-bit tile offsets
     (dict(nseq=0), -1, "nseq"),
     (dict(T=65, nseq=2), -1, "divisible"),
     (dict(x=None), -1, "null"),
