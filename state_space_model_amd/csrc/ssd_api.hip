@@ -82,6 +82,7 @@ size_t ssd_scan_prefill_workspace(int64_t total_tokens, int nseq, int H, int P, 
   if (dtype != SSD_F32 && dtype != SSD_BF16) return 0;
   if (nseq < 1 || total_tokens < 0 || total_tokens > INT32_MAX || H < 1) return 0;
   if (!pow2_in(P, 16, 128) || !pow2_in(N, 16, 128) || !pow2_in(chunk, 32, 512)) return 0;
+  if ((int64_t)chunk * H * P * 4 > INT32_MAX) return 0;  // as check_prefill
   return ssd::prefill_layout(total_tokens, nseq, H, P, N, chunk, dtype == SSD_BF16 ? 2 : 4).total;
 }
 
@@ -241,6 +242,7 @@ size_t ssd_scan_prefill_backward_workspace(int64_t total_tokens, int nseq, int H
   if (nseq < 1 || total_tokens < 0 || total_tokens > INT32_MAX || H < 1 || G < 1 || H % G != 0)
     return 0;
   if (!pow2_in(P, 16, 128) || !pow2_in(N, 16, 128) || !pow2_in(chunk, 32, 512)) return 0;
+  if ((int64_t)chunk * H * P * 4 > INT32_MAX || (int64_t)chunk * G * N * 4 > INT32_MAX) return 0;
   return ssd::bwd_layout(total_tokens, nseq, H, P, N, G, chunk, dtype == SSD_BF16 ? 2 : 4).total;
 }
 

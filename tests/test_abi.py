@@ -40,6 +40,7 @@ def test_workspace_size():
     assert w(4096, 1, 24, 64, 128, 256, 0) > n1          # float32 operand copy of H_in
     assert w(4096, 1, 24, 64, 100, 256, 1) == 0          # unsupported N
     assert w(4096, 1, 24, 64, 128, 96, 1) == 0           # unsupported chunk
+    assert w(4096, 1, 8192, 128, 128, 512, 1) == 0       # rows past 32-bit tile offsets
     assert w(-1, 1, 24, 64, 128, 256, 1) == 0
     assert w(0, 1, 24, 64, 128, 256, 1) > 0
 
