@@ -63,6 +63,7 @@ SMALL = [  # (lengths, H, P, N, G, chunk, h0, dh_out)
     ([1100, 513], 2, 64, 128, 1, 512, True, True),
     ([96], 8, 16, 128, 8, 32, False, True),
     ([700, 1], 6, 64, 128, 2, 256, True, True),
+    ([130, 45], 4, 64, 128, 2, 32, True, True),  # chunk 32: two-wave workgroups
 ]
 
 

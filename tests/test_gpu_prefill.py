@@ -59,6 +59,7 @@ SMALL = [  # (lengths, H, P, N, G, chunk, h0)
     ([520, 0, 77], 4, 128, 16, 4, 256, True),
     ([1100, 513], 2, 64, 128, 1, 512, True),
     ([96], 8, 16, 128, 8, 32, False),
+    ([130, 45], 4, 64, 128, 2, 32, True),  # block-swizzled tiles at chunk 32 (two waves)
 ]
 
 
