@@ -34,6 +34,11 @@ struct WorkspaceLayout {
                    //                            last row of j's 32-row block (log2 units)
   size_t S;        // f32  [nc_max][H][N][P]     chunk states
   size_t hin;      // T    [nc_max][H][N][P]     state entering each chunk (operand type)
+  // bf16 C.B^T fragments of each (chunk, group) for the row-split chunk scan,
+  // [nc_max][<=H][Q/16][Q/32][64 lanes][8], present (has_cbg) for bf16 with
+  // P 64, N 128, chunk <= 256 and fewer than 2048 (chunk, head) units
+  size_t cbg;
+  bool has_cbg;
   size_t total;
 };
 

@@ -133,14 +133,75 @@ hipError_t launch_chunk_map(const int32_t *cu, int nseq, int64_t T, int Q, int n
 // optionally as float32) and the final state (to h_out, and to h_out2 when
 // given).
 
+// C.B^T for the row-split chunk scan, once per (chunk, B/C group) instead of
+// once per head (bf16, N = 128): one wave per (chunk, group, 16-row output
+// tile t, 32-row block k <= t/2 of source rows j) forms the pair of 16x16
+// results (B_j . C_i) of the scan's block step -- the same MFMA
+// sequence, rows past the chunk read as zero -- and stores them rounded to
+// bf16 in that step's fragment order (lane l: column i = 16 t + l % 16, rows
+// j = 32 k + 4 (l / 16) + r and 32 k + 16 + 4 (l / 16) + r): 1 KB per (t, k).
+// Blocks starting past the chunk end are never read and not written.
+struct CbgArgs {
+  const bf16 *B, *C;
+  bf16 *out;  // [nc][G][Q/16][Q/32][64][8]
+  int G, nc, nz;  // nz: z-slices of the state pass proper (its sequences)
+};
+__device__ __forceinline__ void cbg_unit(const CbgArgs &a, ChunkMap cmap, int Q, int u) {
+  constexpr int N = 128, KS = N / 32;
+  const int NT = Q / 16, NKB = Q / 32;
+  // unit u = ((chunk * G + group) * NT + t) * NKB + k: one 1 KB block each,
+  // so every unit is a single round trip of loads
+  const int k = u % NKB, t = (u / NKB) % NT, cg = u / (NKB * NT), c = cg / a.G,
+            gr = cg - c * a.G;
+  if (c >= a.nc || k > t / 2) return;
+  const int4 ci = cmap(c);
+  const int len = ci.z;
+  if (len <= 0 || 32 * k >= len) return;
+  const int lane = threadIdx.x & 63, grp = lane >> 4, col = lane & 15;
+  const size_t bstride = (size_t)a.G * N;
+  const bf16 *Cg = a.C + (size_t)ci.y * bstride + (size_t)gr * N;
+  const bf16 *Bg = a.B + (size_t)ci.y * bstride + (size_t)gr * N;
+  const int i = 16 * t + col;
+  Frag<bf16> cf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    cf[ks] = i < len ? frag_global(Cg + (size_t)i * bstride + ks * 32 + 8 * grp) : frag_zero<bf16>();
+  bf16 *out = a.out + (((size_t)cg * NT + t) * NKB + k) * 512;
+  const int j0 = 32 * k + col, j1 = j0 + 16;
+  Frag<bf16> b0[KS], b1[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int n8 = ks * 32 + 8 * grp;
+    b0[ks] = j0 < len ? frag_global(Bg + (size_t)j0 * bstride + n8) : frag_zero<bf16>();
+    b1[ks] = j1 < len ? frag_global(Bg + (size_t)j1 * bstride + n8) : frag_zero<bf16>();
+  }
+  f4 g0 = zero4(), g1 = zero4();
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    mma(g0, b0[ks], cf[ks]);
+    mma(g1, b1[ks], cf[ks]);
+  }
+  *reinterpret_cast<bf16x8 *>(out + lane * 8) =
+      cvt_bf8(f8v{g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]});
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_state_pass(const float *__restrict__ S,
                                                     const float *__restrict__ s_ws,
                                                     const int *__restrict__ seq_off,
                                                     ChunkMap cmap, const float *h0, float *h_out,
                                                     T *__restrict__ hin, int H, int NP, int Q,
-                                                    float *__restrict__ hin32, float *h_out2) {
+                                                    float *__restrict__ hin32, float *h_out2,
+                                                    CbgArgs cbg) {
   constexpr int BATCH = 8;  // chunk states in flight per thread
+  // extra z-slices (dispatched after every block of the walk): C.B^T units,
+  // four a block
+  if (sizeof(T) == 2 && (int)blockIdx.z >= cbg.nz) {
+    const int lb = (((int)blockIdx.z - cbg.nz) * (int)gridDim.y + (int)blockIdx.y) *
+                       (int)gridDim.x + (int)blockIdx.x;
+    cbg_unit(cbg, cmap, Q, lb * 4 + (int)(threadIdx.x >> 6));
+    return;
+  }
   const int s = blockIdx.z, hd = blockIdx.y;
   const int e = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (e >= NP) return;
@@ -212,35 +273,38 @@ template <typename T, int P, int N> struct ScanCfg {
   static constexpr bool SWZ = sizeof(T) == 2 && P == 64 && N == 128;
   // one float row of q values, staged whole 1 KB requests at a time
   static constexpr size_t frow_bytes(int q) { return ((size_t)q * 4 + 1023) / 1024 * 1024; }
-  static constexpr size_t lds_bytes(int jp, int q) {
+  // cbg: C.B^T comes precomputed (no B tile)
+  static constexpr size_t lds_bytes(int jp, int q, bool cbg = false) {
     if (SWZ)
-      return (size_t)(NK / 8 + jp / 8) * kBlk128 + (size_t)(jp / 4) * kBlk256 + 3 * frow_bytes(q);
+      return (size_t)(NK / 8 + jp / 8) * kBlk128 + (cbg ? 0 : (size_t)(jp / 4) * kBlk256) +
+             3 * frow_bytes(q);
     return (size_t)(tile_slots(NK, HS) + tile_slots(jp, BS) + tile_slots(jp, XS)) * 16 +
            12 * (size_t)q;
   }
-  // staged rows per phase for chunk length q and `threads`: up to 64 rows in
-  // blocks of at most 512 threads (under 53 KB, so three workgroups share a CU
-  // and the row-split grid of a small batch is resident at once), up to 256
-  // rows otherwise, halved until the LDS fits
-  static int jp(int q, int threads) {
-    const int lim = threads <= 512 ? 64 : 256;
+  // staged rows per phase for chunk length q and `threads`: up to 64 rows
+  // (128 without a B tile) in blocks of at most 512 threads (under 53 KB, so
+  // three workgroups share a CU and the row-split grid of a small batch is
+  // resident at once), up to 256 rows otherwise, halved until the LDS fits
+  static int jp(int q, int threads, bool cbg = false) {
+    const int lim = threads <= 512 ? (cbg ? 128 : 64) : 256;
     int j = q < lim ? q : lim;
     const size_t cap = threads <= 512 ? 53 * 1024 : 160 * 1024;
-    while (j > 32 && lds_bytes(j, q) > cap) j /= 2;
+    while (j > 32 && lds_bytes(j, q, cbg) > cap) j /= 2;
     return j;
   }
 };
 
-template <typename T, int P, int N, int SPLIT>
+template <typename T, int P, int N, int SPLIT, bool CBG>
 __global__ __launch_bounds__(1024) void k_chunk_scan(
     const T *__restrict__ x, const T *__restrict__ B, const T *__restrict__ C,
     const float *__restrict__ D, const float *__restrict__ s_ws, const float *__restrict__ dt_ws,
     const float *__restrict__ u_ws, const T *__restrict__ hin, ChunkMap cmap, int nc, int H,
-    int G, int Q, int JP, float *__restrict__ y) {
+    int G, int Q, int JP, float *__restrict__ y, const T *__restrict__ cbg) {
   typedef ScanCfg<T, P, N> K;
   constexpr int KS = K::KS, NK = K::NK, XP = K::XP, BP = K::BP, HP = K::HP;
   constexpr int NPT = P / 16;
   constexpr bool SWZ = K::SWZ;
+  static_assert(!CBG || SWZ, "precomputed C.B^T only with the block-swizzled tiles");
   const ChunkHead ch = xcd_chunk_head(H * SPLIT);
   const int c = ch.c, hd = ch.h / SPLIT, part = ch.h % SPLIT;
   if (c >= nc) return;
@@ -266,7 +330,7 @@ __global__ __launch_bounds__(1024) void k_chunk_scan(
   // swizzled layout: H_in NK/8 blocks, B JP/4 blocks, X JP/8 blocks
   char *Hc = smem;
   char *Bc = Hc + (NK / 8) * kBlk128;
-  char *Xc = Bc + (JP / 4) * kBlk256;
+  char *Xc = Bc + (CBG ? 0 : (JP / 4) * kBlk256);
   float *s_l = SWZ ? reinterpret_cast<float *>(Xc + (JP / 8) * kBlk128)
                    : reinterpret_cast<float *>(Xs + tile_slots(JP, K::XS) * K::VN);  // [Q]
   // [Q] each (swizzled layout: rows rounded up to 1 KB, filled by whole requests)
@@ -289,7 +353,7 @@ __global__ __launch_bounds__(1024) void k_chunk_scan(
   if constexpr (SWZ) {
     const int v0 = max(0, min(len, JP));
     dma_swz<kBlk128>(Hc, hin + csh * (size_t)(N * P), N * P * sizeof(T), hl, 1024, NK / 8, wave, nw);
-    dma_swz<kBlk256>(Bc, bs, v0 * bsb, bl, 4 * bsb, JP / 4, wave, nw);
+    if (!CBG) dma_swz<kBlk256>(Bc, bs, v0 * bsb, bl, 4 * bsb, JP / 4, wave, nw);
     dma_swz<kBlk128>(Xc, xs, v0 * xsb, xl, 8 * xsb, JP / 8, wave, nw);
     // the chunk's s, dt and u rows (written by the chunk-state stage), one
     // wave each
@@ -368,7 +432,8 @@ __global__ __launch_bounds__(1024) void k_chunk_scan(
       __syncthreads();
       if constexpr (SWZ) {
         const int vr = min(len - ph, JP);
-        dma_swz<kBlk256>(Bc, bs + (size_t)ph * bstride, vr * bsb, bl, 4 * bsb, JP / 4, wave, nw);
+        if (!CBG)
+          dma_swz<kBlk256>(Bc, bs + (size_t)ph * bstride, vr * bsb, bl, 4 * bsb, JP / 4, wave, nw);
         dma_swz<kBlk128>(Xc, xs + (size_t)ph * xstride, vr * xsb, xl, 8 * xsb, JP / 8, wave, nw);
       } else {
         dma_tile<T, K::BS, K::BD>(Bs, bs + (size_t)ph * bstride, bstride, JP, len - ph, wave, nw);
@@ -391,11 +456,27 @@ __global__ __launch_bounds__(1024) void k_chunk_scan(
       }
     }
     const int jend = live ? min(ph + JP, tile_last + 1) : ph;
+    // precomputed C.B^T: this tile's 1 KB fragments, one block ahead
+    const T *gt =
+        CBG ? cbg + ((((size_t)c * G + g) * (Q / 16) + tile) * (Q / 32)) * 512 + lane * 8 : cbg;
+    typedef typename Vec16<T>::type Vg;
+    Vg gnext = vzero<Vg>();
+    if (CBG && ph < jend) gnext = *reinterpret_cast<const Vg *>(gt + (ph / 32) * 512);
     for (int jb = ph; jb < jend; jb += 32) {
       const int jl = jb - ph;
       f4 g0 = zero4(), g1 = zero4();  // G^T = B C^T for this j-block
+      if constexpr (CBG) {
+        const Vg gcur = gnext;
+        if (jb + 32 < jend) gnext = *reinterpret_cast<const Vg *>(gt + (jb / 32 + 1) * 512);
+        const f8v gf = cvt_f8(gcur);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
+        for (int r = 0; r < 4; ++r) {
+          g0[r] = gf[r];
+          g1[r] = gf[4 + r];
+        }
+      }
+#pragma unroll
+      for (int ks = 0; ks < (CBG ? 0 : KS); ++ks) {
         Frag<T> b0, b1;
         if constexpr (SWZ) {
           const char *bb = Bc + (jl / 4) * kBlk256 + 64 * ks;
@@ -477,6 +558,9 @@ WorkspaceLayout prefill_layout(int64_t T, int nseq, int H, int P, int N, int Q, 
   off = align_up(off + 4 * (size_t)nc * H * N * P, 256);
   L.hin = off;
   off = align_up(off + (size_t)elem * nc * H * N * P, 256);
+  L.cbg = off;
+  L.has_cbg = elem == 2 && P == 64 && N == 128 && Q <= 256 && nc * H < 2048;
+  if (L.has_cbg) off = align_up(off + (size_t)nc * H * (Q / 16) * (Q / 32) * 1024, 256);
   L.total = off;
   return L;
 }
@@ -510,17 +594,32 @@ static hipError_t run_prefill(const PrefillArgs &a, unsigned stages) {
     hipError_t e = launch_chunk_state(a, L, nc, (stages & 2u) != 0, st);
     if (e != hipSuccess) return e;
   }
-  if (stages & 4u) {
-    const int NP = N * P;
-    hipLaunchKernelGGL(k_state_pass<T>, dim3((NP + 1023) / 1024, a.H, a.nseq), dim3(256), 0, st,
-                       S, s_ws, seq_off, cmap, a.h0, a.h_out, hin, a.H, NP, a.Q, a.hin32, a.h_out2);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   // the head-count choice counts the chunks exactly for a dense batch (nc is
   // an upper bound)
   const int nc_real = L_dense > 0 ? a.nseq * ((L_dense + a.Q - 1) / a.Q) : nc;
-  const int HB = (stages & 8u) ? scan_heads_choice(P, N, a.Q, a.bf16, nc_real, a.H, a.G) : 0;
+  const int HB = scan_heads_choice(P, N, a.Q, a.bf16, nc_real, a.H, a.G);
+  // the row-split scan reads C.B^T precomputed per (chunk, group) where the
+  // workspace holds it; the state-pass launch forms it (stage 4), in extra
+  // workgroups that run beside the latency-bound walk over the chunks
+  const bool use_cbg = L.has_cbg && HB == 0 && ScanCfg<T, P, N>::SWZ;
+  T *cbg = reinterpret_cast<T *>(ws + L.cbg);
+  if (stages & 4u) {
+    const int NP = N * P, npb = (NP + 1023) / 1024;
+    CbgArgs ca{nullptr, nullptr, nullptr, a.G, nc, a.nseq};
+    int gz = 0;
+    if (use_cbg && nc > 0) {
+      ca.B = reinterpret_cast<const bf16 *>(a.B);
+      ca.C = reinterpret_cast<const bf16 *>(a.C);
+      ca.out = reinterpret_cast<bf16 *>(cbg);
+      const long units = (long)nc * a.G * (a.Q / 16) * (a.Q / 32);
+      const long blocks = (units + 3) / 4, per_z = (long)npb * a.H;
+      gz = (int)((blocks + per_z - 1) / per_z);
+    }
+    hipLaunchKernelGGL(k_state_pass<T>, dim3(npb, a.H, a.nseq + gz), dim3(256), 0, st, S, s_ws,
+                       seq_off, cmap, a.h0, a.h_out, hin, a.H, NP, a.Q, a.hin32, a.h_out2, ca);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if ((stages & 8u) && nc > 0 && HB > 0) {
     hipError_t e = launch_scan_heads(a, L, nc, HB, st);
     if (e != hipSuccess) return e;
@@ -529,11 +628,21 @@ static hipError_t run_prefill(const PrefillArgs &a, unsigned stages) {
     typedef ScanCfg<T, P, N> K;
     const int split = a.Q >= 256 ? 2 : 1;
     const int threads = 64 * (a.Q / 16) / split;
-    const int jp = K::jp(a.Q, threads);
-    const size_t lds = K::lds_bytes(jp, a.Q);
+    const int jp = K::jp(a.Q, threads, use_cbg);
+    const size_t lds = K::lds_bytes(jp, a.Q, use_cbg);
     if (lds > 160 * 1024) return hipErrorInvalidConfiguration;
-    const void *kern = split == 1 ? (const void *)k_chunk_scan<T, P, N, 1>
-                                  : (const void *)k_chunk_scan<T, P, N, 2>;
+    const void *kern;
+    if constexpr (K::SWZ) {
+      if (use_cbg)
+        kern = split == 1 ? (const void *)k_chunk_scan<T, P, N, 1, true>
+                          : (const void *)k_chunk_scan<T, P, N, 2, true>;
+      else
+        kern = split == 1 ? (const void *)k_chunk_scan<T, P, N, 1, false>
+                          : (const void *)k_chunk_scan<T, P, N, 2, false>;
+    } else {
+      kern = split == 1 ? (const void *)k_chunk_scan<T, P, N, 1, false>
+                        : (const void *)k_chunk_scan<T, P, N, 2, false>;
+    }
     hipError_t e = set_lds_limit(kern);
     if (e != hipSuccess) return e;
     const T *xp = (const T *)a.x, *bp = (const T *)a.B, *cp = (const T *)a.C;
@@ -542,8 +651,9 @@ static hipError_t run_prefill(const PrefillArgs &a, unsigned stages) {
     const float *Dp = a.D;
     float *yp = a.y;
     ChunkMap cm = cmap;
+    const T *gp = cbg;
     void *args[] = {&xp, &bp, &cp, &Dp, &s_ws, &dt_ws, &u_ws, &hp, &cm, &nc_, &H_, &G_, &Q_, &jp_,
-                    &yp};
+                    &yp, &gp};
     e = hipLaunchKernel(kern, dim3(xcd_grid(nc, a.H * split)), dim3(threads), args, lds, st);
     if (e != hipSuccess) return e;
   }

@@ -36,8 +36,16 @@ def test_workspace_size():
     nc = 16
     # S (float32) + H_in (bf16) per chunk and head, and s, dt, u per chunk, head and row
     expect_min = nc * 24 * 128 * 64 * (4 + 2) + 3 * nc * 24 * 256 * 4
-    assert expect_min <= n1 <= expect_min + 8192
-    assert w(4096, 1, 24, 64, 128, 256, 0) > n1          # float32 operand copy of H_in
+    # bf16, P 64, N 128, chunk 256 and fewer than 2048 chunk-head units: the
+    # row-split scan's C.B^T fragments, 1 KB per (16-row tile, 32-row block)
+    cbg = nc * 24 * (256 // 16) * (256 // 32) * 1024
+    assert expect_min + cbg <= n1 <= expect_min + cbg + 8192
+    n32 = w(4096, 1, 24, 64, 128, 256, 0)                # float32: H_in in float32, no C.B^T
+    expect32 = nc * 24 * 128 * 64 * (4 + 4) + 3 * nc * 24 * 256 * 4
+    assert expect32 <= n32 <= expect32 + 8192
+    # past 2048 units (the heads-streamed scan): no C.B^T region
+    n80 = w(4096, 1, 160, 64, 128, 256, 1)
+    assert n80 <= nc * 160 * 128 * 64 * 6 + 3 * nc * 160 * 256 * 4 + 8192
     assert w(4096, 1, 24, 64, 100, 256, 1) == 0          # unsupported N
     assert w(4096, 1, 24, 64, 128, 96, 1) == 0           # unsupported chunk
     assert w(4096, 1, 8192, 128, 128, 512, 1) == 0       # rows past 32-bit tile offsets
