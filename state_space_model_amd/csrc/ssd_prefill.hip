@@ -149,11 +149,17 @@ struct CbgArgs {
 __device__ __forceinline__ void cbg_unit(const CbgArgs &a, ChunkMap cmap, int Q, int u) {
   constexpr int N = 128, KS = N / 32;
   const int NT = Q / 16, NKB = Q / 32;
-  // unit u = ((chunk * G + group) * NT + t) * NKB + k: one 1 KB block each,
-  // so every unit is a single round trip of loads
-  const int k = u % NKB, t = (u / NKB) % NT, cg = u / (NKB * NT), c = cg / a.G,
-            gr = cg - c * a.G;
-  if (c >= a.nc || k > t / 2) return;
+  // unit u = (chunk * G + group) * npairs + p over the blocks the scan reads,
+  // k <= t/2: tiles 2m and 2m+1 read m+1 blocks each, so the pairs of tiles
+  // below m hold m (m+1) units; one 1 KB block per unit, a single round trip
+  const int npairs = (NT / 2) * (NT / 2 + 1);
+  const int cg = u / npairs, p = u - cg * npairs, c = cg / a.G, gr = cg - c * a.G;
+  if (c >= a.nc) return;
+  int m = (int)((__builtin_sqrtf(4.f * p + 1.f) - 1.f) * 0.5f);
+  while (m * (m + 1) > p) --m;
+  while ((m + 1) * (m + 2) <= p) ++m;
+  const int r = p - m * (m + 1), hi = r > m ? 1 : 0;
+  const int t = 2 * m + hi, k = r - hi * (m + 1);
   const int4 ci = cmap(c);
   const int len = ci.z;
   if (len <= 0 || 32 * k >= len) return;
@@ -611,7 +617,7 @@ static hipError_t run_prefill(const PrefillArgs &a, unsigned stages) {
       ca.B = reinterpret_cast<const bf16 *>(a.B);
       ca.C = reinterpret_cast<const bf16 *>(a.C);
       ca.out = reinterpret_cast<bf16 *>(cbg);
-      const long units = (long)nc * a.G * (a.Q / 16) * (a.Q / 32);
+      const long units = (long)nc * a.G * (a.Q / 32) * (a.Q / 32 + 1);
       const long blocks = (units + 3) / 4, per_z = (long)npb * a.H;
       gz = (int)((blocks + per_z - 1) / per_z);
     }
