@@ -70,6 +70,15 @@ def log(args, msg):
 
 
 # ------------------------------------------------------------ algorithmic work
+def cbg_launch(w, T, nseq):
+    """Whether the row-split chunk scan reads C.B^T formed in the state-pass
+    launch (the library's rule: bf16, P 64, N 128, chunk <= 256, fewer than
+    2048 chunk-head units)."""
+    nc = (T + nseq * (w.chunk - 1)) // w.chunk
+    return (w.dtype == "bf16" and w.P == 64 and w.N == 128 and w.chunk <= 256
+            and nc * w.H < 2048)
+
+
 def prefill_work(w, T, nseq, h0):
     """Algorithmic bytes and flops of the prefill, per kernel (SSD chunked form)."""
     H, P, N, G, Q = w.H, w.P, w.N, w.G, w.chunk
@@ -84,8 +93,12 @@ def prefill_work(w, T, nseq, h0):
     k3 = dict(bytes=(state if h0 else 0) + state, flops=2 * (T // Q + nseq) * H * N * P)
     # chunk scan: x, B, C, dt read, y written; C.B^T once per group and chunk (full tile),
     # M.X per head (full tile), C.H_in per head
-    k4 = dict(bytes=T * H * P * (e + 4) + 2 * T * G * N * e + T * H * 4,
-              flops=T * (2 * Q * N * G + H * (2 * Q * P + 2 * N * P)))
+    cb_bytes, cb_flops = T * G * N * e, T * 2 * Q * N * G
+    k4 = dict(bytes=T * H * P * (e + 4) + T * G * N * e + cb_bytes + T * H * 4,
+              flops=T * H * (2 * Q * P + 2 * N * P) + cb_flops)
+    if cbg_launch(w, T, nseq):  # C.B^T (and the B rows) move to the state-pass launch
+        k3 = dict(bytes=k3["bytes"] + cb_bytes, flops=k3["flops"] + cb_flops)
+        k4 = dict(bytes=k4["bytes"] - cb_bytes, flops=k4["flops"] - cb_flops)
     return {"chunk_state": k2, "state_pass": k3, "chunk_scan": k4}
 
 
