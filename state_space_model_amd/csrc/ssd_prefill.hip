@@ -266,7 +266,10 @@ __global__ __launch_bounds__(256) void k_state_pass(const float *__restrict__ S,
 // pairing.  Staging uses the direct global->LDS load (16 bytes per lane, lane
 // l writing base + 16 l): H_in and the first JP rows of B and X are requested
 // together with no staging registers, so each phase of JP rows costs one memory
-// round trip.
+// round trip.  With CBG (bf16, P 64, N 128, chunk <= 256, small batches) the
+// B C^T pairs come precomputed per (chunk, group) from the state-pass launch
+// (cbg_unit) as 1 KB fragment blocks read one block ahead: no B tile, and
+// 128-row phases of X.
 template <typename T, int P, int N> struct ScanCfg {
   static constexpr int NK = N < 32 ? 32 : N;  // contraction over n, padded to the k-step
   static constexpr int KS = NK / 32;
