@@ -131,7 +131,8 @@ hipError_t launch_chunk_map(const int32_t *cu, int nseq, int64_t T, int Q, int n
 // Per (sequence, head), per 4 state elements: walk the sequence's chunks in
 // order, emit the state entering each chunk (as the MFMA operand type, and
 // optionally as float32) and the final state (to h_out, and to h_out2 when
-// given).
+// given).  For the row-split scan with precomputed C.B^T, the same launch
+// carries the C.B^T units (cbg_unit) in extra z-slices past the sequences.
 
 // C.B^T for the row-split chunk scan, once per (chunk, B/C group) instead of
 // once per head (bf16, N = 128): one wave per (chunk, group, 16-row output
