@@ -53,6 +53,37 @@ def test_workspace_size():
     assert w(0, 1, 24, 64, 128, 256, 1) > 0
 
 
+def test_cbg_region_follows_the_row_split_rule():
+    """The workspace holds the row split's C.B^T fragments exactly where the
+    bench's per-launch work model says C.B^T moves to the state-pass launch
+    (bf16, P 64, N 128, chunk <= 256, fewer than 2048 chunk-head units)."""
+    import importlib.util
+    import os
+    from types import SimpleNamespace
+    spec = importlib.util.spec_from_file_location(
+        "bench_model", os.path.join(os.path.dirname(__file__), "..", "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    w = ssd.load().ssd_scan_prefill_workspace
+    for T, nseq, H, P, N, Q, dt in [(4096, 1, 24, 64, 128, 256, "bf16"),
+                                    (4096, 1, 24, 64, 128, 256, "f32"),
+                                    (4096, 1, 24, 64, 64, 256, "bf16"),
+                                    (4096, 1, 24, 64, 128, 512, "bf16"),
+                                    (32768, 4, 80, 64, 128, 256, "bf16"),
+                                    (1000, 3, 127, 64, 128, 64, "bf16"),
+                                    (1000, 3, 128, 64, 128, 64, "bf16")]:
+        e = 2 if dt == "bf16" else 4
+        nc = (T + nseq * (Q - 1)) // Q
+        region = nc * H * (Q // 16) * (Q // 32) * 1024
+        base = sum(-(-b // 256) * 256 for b in (16 * max(nc, 1), 4 * (nseq + 1),
+                                                  4 * nc * H * Q, 4 * nc * H * Q, 4 * nc * H * Q,
+                                                  4 * nc * H * N * P, e * nc * H * N * P))
+        got = w(T, nseq, H, P, N, Q, 1 if dt == "bf16" else 0)
+        wl = SimpleNamespace(dtype=dt, P=P, N=N, chunk=Q, H=H)
+        has = bench.cbg_launch(wl, T, nseq)
+        assert got == base + (-(-region // 256) * 256 if has else 0), (T, nseq, H, P, N, Q, dt)
+
+
 def _prefill_rc(**kw):
     lib = ssd.load()
     a = dict(x=1, dt=1, A=1, B=1, C=1, D=1, h0=None, y=1, h_out=None, cu=None, nseq=1, T=64,
