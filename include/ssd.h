@@ -68,7 +68,12 @@ enum {
 /*
  * Workspace bytes needed by ssd_scan_prefill() for `total_tokens` tokens in
  * `nseq` sequences (chunking restarts at every sequence start).  Returns 0 for
- * arguments ssd_scan_prefill() would reject.
+ * arguments ssd_scan_prefill() would reject.  Besides the per-chunk decays and
+ * states it holds, for bf16 with P 64, N 128, chunk <= 256 and fewer than
+ * 2048 (chunk, head) units, the intra-chunk C.B^T of every chunk as bf16
+ * fragments (chunk^2 / 512 KB per chunk and head, sized by H since the group
+ * count is not an argument): SSD_STAGE_STATE_PASS writes them and
+ * SSD_STAGE_CHUNK_SCAN reads them.
  */
 size_t ssd_scan_prefill_workspace(int64_t total_tokens, int nseq, int H, int P, int N,
                                   int chunk, ssd_dtype_t dtype);
