@@ -65,17 +65,30 @@ enum {
     SSD_STAGE_ALL = 15u
 };
 
+/* Kernel-variant bits, OR-ed into the `stages` mask of
+ * ssd_scan_prefill_stages().  Without them the library picks each kernel by
+ * problem size; a bit forces one implementation (for tests and tuning).  All
+ * variants compute the same result up to floating-point reassociation.  The
+ * stage calls of one split sequence must all pass the same bits. */
+enum {
+    SSD_VARIANT_SCAN_ROWS = 0x100u,  /* chunk scan: a workgroup per (chunk, head, half) */
+    SSD_VARIANT_SCAN_HEADS = 0x200u, /* chunk scan: the heads of a B/C group streamed
+                                        through one workgroup (bf16, P 64, N 128 and a
+                                        few other shapes; otherwise the row split) */
+    SSD_VARIANT_MASK = 0x300u
+};
+
 /*
  * Workspace bytes needed by ssd_scan_prefill() for `total_tokens` tokens in
- * `nseq` sequences (chunking restarts at every sequence start).  Returns 0 for
- * arguments ssd_scan_prefill() would reject.  Besides the per-chunk decays and
- * states it holds, for bf16 with P 64, N 128, chunk <= 256 and fewer than
- * 2048 (chunk, head) units, the intra-chunk C.B^T of every chunk as bf16
- * fragments (chunk^2 / 512 KB per chunk and head, sized by H since the group
- * count is not an argument): SSD_STAGE_STATE_PASS writes them and
- * SSD_STAGE_CHUNK_SCAN reads them.
+ * `nseq` sequences of H heads in G B/C groups (chunking restarts at every
+ * sequence start).  Returns 0 for arguments ssd_scan_prefill() would reject
+ * (including H % G != 0 and the 2^31 row-offset limit below).  Besides the
+ * per-chunk decays and states it holds, for bf16 with P 64, N 128 and
+ * chunk <= 256, the intra-chunk C.B^T of every (chunk, group) as bf16
+ * fragments (chunk^2 / 512 KB each): SSD_STAGE_STATE_PASS writes them when
+ * the row-split chunk scan will run, and SSD_STAGE_CHUNK_SCAN reads them.
  */
-size_t ssd_scan_prefill_workspace(int64_t total_tokens, int nseq, int H, int P, int N,
+size_t ssd_scan_prefill_workspace(int64_t total_tokens, int nseq, int H, int P, int N, int G,
                                   int chunk, ssd_dtype_t dtype);
 
 /*
@@ -100,7 +113,9 @@ size_t ssd_scan_prefill_workspace(int64_t total_tokens, int nseq, int H, int P, 
  * Supported: P in {16,32,64,128}, N in {16,32,64,128}, chunk in
  * {32,64,128,256,512}, H % G == 0, and H*P*chunk*4 and G*N*chunk*4 below
  * 2^31 (a chunk's rows are addressed with 32-bit offsets; otherwise
- * SSD_ERR_UNSUPPORTED).  T = 0 copies h0 (or zeros) to h_out.
+ * SSD_ERR_UNSUPPORTED).  A chunk of 16 is refused (SSD_ERR_UNSUPPORTED): the
+ * matrix-core step over tokens is 32 wide, and any chunk gives the same
+ * result up to reassociation.  T = 0 copies h0 (or zeros) to h_out.
  * Splitting a sequence at any token and passing h_out of the first part as h0
  * of the second gives the same result as one call.
  */
@@ -112,10 +127,12 @@ int ssd_scan_prefill(const void *x, const float *dt, const float *A, const void 
 
 /*
  * The same computation as ssd_scan_prefill(), running only the stages in the
- * bitmask `stages` (SSD_STAGE_*).  Stages communicate through the workspace,
- * so running CHUNK_CUMSUM, CHUNK_STATE, STATE_PASS and CHUNK_SCAN in that order,
- * in one call or in four calls with identical arguments, equals one
- * ssd_scan_prefill() call.  Used to time and test each stage on its own.
+ * bitmask `stages` (SSD_STAGE_*, optionally with SSD_VARIANT_* bits).  Stages
+ * communicate through the workspace, so running CHUNK_CUMSUM, CHUNK_STATE,
+ * STATE_PASS and CHUNK_SCAN in that order, in one call or in four calls with
+ * identical arguments, equals one ssd_scan_prefill() call.  Used to time and
+ * test each stage, and each kernel variant, on its own.  Other bits:
+ * SSD_ERR_INVALID_ARG.
  */
 int ssd_scan_prefill_stages(unsigned stages, const void *x, const float *dt, const float *A,
                             const void *B, const void *C, const float *D, const float *h0,

@@ -70,7 +70,10 @@ def _ptr(a):
 
 
 def default_threads():
-    return max(1, len(os.sched_getaffinity(0)))
+    """Threads for the oracle: the CPUs this process may use, at most
+    OMP_NUM_THREADS (16 when unset)."""
+    cap = int(os.environ.get("OMP_NUM_THREADS") or 16)
+    return max(1, min(cap, len(os.sched_getaffinity(0))))
 
 
 def prefill(x, dt, A, B, C, D, h0=None, cu_seqlens=None, threads=None, lib=None):

@@ -380,10 +380,10 @@ int ssd_ref_prefill_backward(const float *x, const float *dt, const float *A,
 }
 
 /*
- * Gated delta rule: the other scan family of Recurrence Scan ("Gated delta
- * rule (GDN) layers ... each token updates a per-head state matrix, and the
- * state is carried from one step to the next"; the scan returns the output and
- * the carried state, "One equation, one packed result").  The page gives no
+ * Gated delta rule: the other scan family that Recurrence Scan covers ("One
+ * equation, one packed result": a per-head matrix state that every token
+ * rewrites and that the scan carries forward and returns beside the
+ * output).  The page gives no
  * equation; this is the published gated delta rule, per sequence and head h
  * (q, k read group g = floor(h*G/H)), state S [V][K] (row i = value index):
  *   a_t   = exp(g_t)                                   (g_t <= 0: the gate)

@@ -39,7 +39,9 @@ int check_prefill(const void *x, const float *dt, const float *A, const void *B,
   if (H % G != 0) return fail(SSD_ERR_INVALID_ARG, "H %% G != 0 (H=%d G=%d)", H, G);
   if (!pow2_in(P, 16, 128)) return fail(SSD_ERR_UNSUPPORTED, "headdim P=%d not in {16,32,64,128}", P);
   if (!pow2_in(N, 16, 128)) return fail(SSD_ERR_UNSUPPORTED, "d_state N=%d not in {16,32,64,128}", N);
-  if (!pow2_in(chunk, 32, 512)) return fail(SSD_ERR_UNSUPPORTED, "chunk=%d not in {32,64,128,256,512}", chunk);
+  if (!pow2_in(chunk, 32, 512))
+    return fail(SSD_ERR_UNSUPPORTED, "chunk=%d not in {32,64,128,256,512}%s", chunk,
+                chunk == 16 ? " (the token step of the matrix cores is 32: use chunk 32)" : "");
   if (!cu && T % nseq != 0)
     return fail(SSD_ERR_INVALID_ARG, "dense batch: total_tokens %lld not divisible by nseq %d", (long long)T, nseq);
   if (T > 0 && (!x || !dt || !B || !C || !y))
@@ -59,16 +61,20 @@ int prefill_impl(unsigned stages, const void *x, const float *dt, const float *A
   g_err[0] = 0;
   int rc = check_prefill(x, dt, A, B, C, D, y, nseq, T, H, P, N, G, chunk, dtype, cu);
   if (rc) return rc;
-  if (stages & ~(unsigned)SSD_STAGE_ALL) return fail(SSD_ERR_INVALID_ARG, "unknown stage bits 0x%x", stages);
+  if (stages & ~(unsigned)(SSD_STAGE_ALL | SSD_VARIANT_MASK))
+    return fail(SSD_ERR_INVALID_ARG, "unknown stage bits 0x%x", stages);
+  if ((stages & SSD_VARIANT_SCAN_ROWS) && (stages & SSD_VARIANT_SCAN_HEADS))
+    return fail(SSD_ERR_INVALID_ARG, "SSD_VARIANT_SCAN_ROWS and _HEADS are exclusive");
   const ssd::WorkspaceLayout L =
-      ssd::prefill_layout(T, nseq, H, P, N, chunk, dtype == SSD_BF16 ? 2 : 4);
+      ssd::prefill_layout(T, nseq, H, P, N, G, chunk, dtype == SSD_BF16 ? 2 : 4);
   if (!workspace || workspace_bytes < L.total)
     return fail(SSD_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, L.total);
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
     return fail(SSD_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   ssd::PrefillArgs a{x, dt, A, B, C, D, h0, y, h_out, cu, nseq, T, H, P, N, G, chunk,
                      dtype == SSD_BF16, workspace, stream};
-  hipError_t e = ssd::launch_prefill(a, stages);
+  a.variant = stages & SSD_VARIANT_MASK;
+  hipError_t e = ssd::launch_prefill(a, stages & SSD_STAGE_ALL);
   if (e != hipSuccess) return fail(SSD_ERR_HIP, "HIP error: %s", hipGetErrorString(e));
   return SSD_OK;
 }
@@ -77,13 +83,17 @@ int prefill_impl(unsigned stages, const void *x, const float *dt, const float *A
 
 extern "C" {
 
-size_t ssd_scan_prefill_workspace(int64_t total_tokens, int nseq, int H, int P, int N, int chunk,
-                                  ssd_dtype_t dtype) {
+size_t ssd_scan_prefill_workspace(int64_t total_tokens, int nseq, int H, int P, int N, int G,
+                                  int chunk, ssd_dtype_t dtype) {
   if (dtype != SSD_F32 && dtype != SSD_BF16) return 0;
-  if (nseq < 1 || total_tokens < 0 || total_tokens > INT32_MAX || H < 1) return 0;
+  if (nseq < 1 || total_tokens < 0 || total_tokens > INT32_MAX || H < 1 || G < 1 || H % G != 0)
+    return 0;
   if (!pow2_in(P, 16, 128) || !pow2_in(N, 16, 128) || !pow2_in(chunk, 32, 512)) return 0;
-  if ((int64_t)chunk * H * P * 4 > INT32_MAX) return 0;  // as check_prefill
-  return ssd::prefill_layout(total_tokens, nseq, H, P, N, chunk, dtype == SSD_BF16 ? 2 : 4).total;
+  // as check_prefill
+  if ((int64_t)total_tokens * H > INT32_MAX * 16LL) return 0;
+  if ((int64_t)chunk * H * P * 4 > INT32_MAX || (int64_t)chunk * G * N * 4 > INT32_MAX) return 0;
+  return ssd::prefill_layout(total_tokens, nseq, H, P, N, G, chunk, dtype == SSD_BF16 ? 2 : 4)
+      .total;
 }
 
 int ssd_scan_prefill(const void *x, const float *dt, const float *A, const void *B, const void *C,

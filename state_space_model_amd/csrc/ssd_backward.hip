@@ -701,14 +701,9 @@ static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Heads per DB/DC workgroup: the largest divisor of H/G that still leaves at
 // least 768 workgroups (three per CU), so few chunks keep every head apart and
-// many chunks sum most heads of a group on chip.  SSD_BWD_HEADS=<n> asks for n
-// instead (used if it divides H/G).
+// many chunks sum most heads of a group on chip.
 static int bwd_heads_per_block(int64_t nc, int H, int G, int Q) {
   const int hpg = H / G, split = Q >= 256 ? 2 : 1;
-  if (const char *e = getenv("SSD_BWD_HEADS")) {
-    const int want = atoi(e);
-    if (want >= 1 && hpg % want == 0) return want;
-  }
   const int64_t units = nc * H * split;
   for (int d = hpg; d > 1; --d)
     if (hpg % d == 0 && units / d >= 768) return d;
@@ -717,7 +712,7 @@ static int bwd_heads_per_block(int64_t nc, int H, int G, int Q) {
 
 BwdLayout bwd_layout(int64_t T, int nseq, int H, int P, int N, int G, int Q, int elem) {
   BwdLayout L{};
-  L.fwd = prefill_layout(T, nseq, H, P, N, Q, elem);
+  L.fwd = prefill_layout(T, nseq, H, P, N, G, Q, elem);
   const size_t nc = (size_t)(L.fwd.nc_max > 0 ? L.fwd.nc_max : 1);
   const size_t NP = (size_t)N * P;
   size_t off = L.fwd.total;
@@ -822,6 +817,7 @@ static hipError_t run_backward(const BwdArgs &a) {
     fa.y = nullptr;
     fa.h_out = hfin;
     fa.hin32 = hin32;
+    fa.scan_follows = false;  // only the states are recomputed
     e = launch_prefill(fa, 7u);
     if (e != hipSuccess) return e;
   }

@@ -1,6 +1,6 @@
 // ssd_gdn.hip -- gated delta rule scan on gfx950: the delta-rule family of
-// Recurrence Scan (poot docs; "Gated delta rule (GDN) layers ... each token
-// updates a per-head state matrix"), as the streaming kernel of its "The
+// Recurrence Scan (poot docs, "One equation, one packed result": a per-head
+// matrix state rewritten by every token), as the streaming kernel of its "The
 // schedule": a workgroup per (sequence, head, block of state rows), the state
 // held on chip for the whole sequence, a runtime loop over tokens, and each
 // row's dot products split over several lanes that add their partial sums

@@ -21,6 +21,8 @@ struct PrefillArgs {
   void *stream;
   float *hin32 = nullptr;  // optional float32 copy of the state entering each chunk
   float *h_out2 = nullptr;  // optional second destination of the final state
+  unsigned variant = 0;     // SSD_VARIANT_* bits (0: the library's choice by size)
+  bool scan_follows = true; // false: no chunk scan reads this workspace (skip C.B^T)
 };
 
 // Byte offsets of the prefill workspace regions (each 256-byte aligned).
@@ -35,14 +37,14 @@ struct WorkspaceLayout {
   size_t S;        // f32  [nc_max][H][N][P]     chunk states
   size_t hin;      // T    [nc_max][H][N][P]     state entering each chunk (operand type)
   // bf16 C.B^T fragments of each (chunk, group) for the row-split chunk scan,
-  // [nc_max][<=H][Q/16][Q/32][64 lanes][8], present (has_cbg) for bf16 with
-  // P 64, N 128, chunk <= 256 and fewer than 2048 (chunk, head) units
+  // [nc_max][G][Q/16][Q/32][64 lanes][8], present (has_cbg) for bf16 with
+  // P 64, N 128 and chunk <= 256
   size_t cbg;
   bool has_cbg;
   size_t total;
 };
 
-WorkspaceLayout prefill_layout(int64_t T, int nseq, int H, int P, int N, int Q, int elem);
+WorkspaceLayout prefill_layout(int64_t T, int nseq, int H, int P, int N, int G, int Q, int elem);
 hipError_t launch_prefill(const PrefillArgs &a, unsigned stages);
 
 // Stages 1-2: chunk-local cumulative decay (s, dt, u) and, if `state`, the
@@ -56,7 +58,7 @@ hipError_t launch_chunk_state(const PrefillArgs &a, const WorkspaceLayout &L, in
 // workgroup to use, or 0 where the row-split scan is the better (or only)
 // choice; launch_scan_heads() enqueues it over the workspace written by the
 // earlier stages.
-int scan_heads_choice(int P, int N, int Q, bool bf16, int nc, int H, int G);
+int scan_heads_choice(int P, int N, int Q, bool bf16, int nc, int H, int G, unsigned variant);
 hipError_t launch_scan_heads(const PrefillArgs &a, const WorkspaceLayout &L, int nc, int HB,
                              hipStream_t st);
 

@@ -549,7 +549,8 @@ __global__ __launch_bounds__(1024) void k_chunk_scan(
 // ------------------------------------------------------------------ launch
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-WorkspaceLayout prefill_layout(int64_t T, int nseq, int H, int P, int N, int Q, int elem) {
+WorkspaceLayout prefill_layout(int64_t T, int nseq, int H, int P, int N, int G, int Q,
+                               int elem) {
   WorkspaceLayout L{};
   const int64_t nc = (T + (int64_t)nseq * (Q - 1)) / Q;
   L.nc_max = nc;
@@ -569,15 +570,15 @@ WorkspaceLayout prefill_layout(int64_t T, int nseq, int H, int P, int N, int Q, 
   L.hin = off;
   off = align_up(off + (size_t)elem * nc * H * N * P, 256);
   L.cbg = off;
-  L.has_cbg = elem == 2 && P == 64 && N == 128 && Q <= 256 && nc * H < 2048;
-  if (L.has_cbg) off = align_up(off + (size_t)nc * H * (Q / 16) * (Q / 32) * 1024, 256);
+  L.has_cbg = elem == 2 && P == 64 && N == 128 && Q <= 256;
+  if (L.has_cbg) off = align_up(off + (size_t)nc * G * (Q / 16) * (Q / 32) * 1024, 256);
   L.total = off;
   return L;
 }
 
 template <typename T, int P, int N>
 static hipError_t run_prefill(const PrefillArgs &a, unsigned stages) {
-  const WorkspaceLayout L = prefill_layout(a.T, a.nseq, a.H, P, N, a.Q, sizeof(T));
+  const WorkspaceLayout L = prefill_layout(a.T, a.nseq, a.H, P, N, a.G, a.Q, sizeof(T));
   char *ws = static_cast<char *>(a.workspace);
   int4 *info = reinterpret_cast<int4 *>(ws + L.info);
   int *seq_off = reinterpret_cast<int *>(ws + L.seq_off);
@@ -607,17 +608,19 @@ static hipError_t run_prefill(const PrefillArgs &a, unsigned stages) {
   // the head-count choice counts the chunks exactly for a dense batch (nc is
   // an upper bound)
   const int nc_real = L_dense > 0 ? a.nseq * ((L_dense + a.Q - 1) / a.Q) : nc;
-  const int HB = scan_heads_choice(P, N, a.Q, a.bf16, nc_real, a.H, a.G);
+  const int HB = scan_heads_choice(P, N, a.Q, a.bf16, nc_real, a.H, a.G, a.variant);
   // the row-split scan reads C.B^T precomputed per (chunk, group) where the
   // workspace holds it; the state-pass launch forms it (stage 4), in extra
-  // workgroups that run beside the latency-bound walk over the chunks
+  // workgroups that run beside the latency-bound walk over the chunks, unless
+  // no scan will read this workspace
   const bool use_cbg = L.has_cbg && HB == 0 && ScanCfg<T, P, N>::SWZ;
+  const bool form_cbg = use_cbg && a.scan_follows;
   T *cbg = reinterpret_cast<T *>(ws + L.cbg);
   if (stages & 4u) {
     const int NP = N * P, npb = (NP + 1023) / 1024;
     CbgArgs ca{nullptr, nullptr, nullptr, a.G, nc, a.nseq};
     int gz = 0;
-    if (use_cbg && nc > 0) {
+    if (form_cbg && nc > 0) {
       ca.B = reinterpret_cast<const bf16 *>(a.B);
       ca.C = reinterpret_cast<const bf16 *>(a.C);
       ca.out = reinterpret_cast<bf16 *>(cbg);

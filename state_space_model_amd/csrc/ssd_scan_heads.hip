@@ -23,9 +23,8 @@
 // results (rows 4g..4g+3 and 16+4g..16+4g+3 of the block, column i): after the
 // decay it is the B operand of Y^T += X^T M^T as it stands.
 #include <algorithm>
-#include <cstdlib>
-#include <cstring>
 
+#include "ssd.h"
 #include "ssd_launch.h"
 #include "ssd_prefill_util.h"
 
@@ -392,12 +391,11 @@ static hipError_t run_heads(const PrefillArgs &a, const WorkspaceLayout &L, int 
 // head count d (a divisor of H/G) minimises rounds(d) * (d + 2): rounds of
 // resident workgroups (`slots` of them at once) times the time of one
 // workgroup, d heads plus a fixed cost (B, C.B^T, the first head's loads)
-// taken as two heads' worth.  Ties go to the larger d.  SSD_PREFILL_SCAN=heads|rows overrides the choice
-// of kernel (used by the tests to run both kernels on the same shapes).
-static int pick_heads(int nc, int H, int G, long slots) {
-  const char *force = getenv("SSD_PREFILL_SCAN");
-  const bool want_rows = force && strcmp(force, "rows") == 0;
-  const bool want_heads = force && strcmp(force, "heads") == 0;
+// taken as two heads' worth.  Ties go to the larger d.  The variant bits
+// SSD_VARIANT_SCAN_ROWS / _HEADS of the call force either kernel.
+static int pick_heads(int nc, int H, int G, long slots, unsigned variant) {
+  const bool want_rows = (variant & SSD_VARIANT_SCAN_ROWS) != 0;
+  const bool want_heads = (variant & SSD_VARIANT_SCAN_HEADS) != 0;
   const long units = (long)nc * H;
   if (want_rows || (!want_heads && units < 2048)) return 0;
   const int hg = H / G;
@@ -434,9 +432,9 @@ static long heads_slots(int P, int N, int Q, bool bf16) {
   return 0;
 }
 
-int scan_heads_choice(int P, int N, int Q, bool bf16, int nc, int H, int G) {
+int scan_heads_choice(int P, int N, int Q, bool bf16, int nc, int H, int G, unsigned variant) {
   const long slots = heads_slots(P, N, Q, bf16);
-  return slots > 0 ? pick_heads(nc, H, G, slots) : 0;
+  return slots > 0 ? pick_heads(nc, H, G, slots, variant) : 0;
 }
 
 hipError_t launch_scan_heads(const PrefillArgs &a, const WorkspaceLayout &L, int nc, int HB,

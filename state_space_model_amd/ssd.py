@@ -16,6 +16,8 @@ LIB_PATH = os.path.join(_HERE, "libssd.so")
 SSD_F32, SSD_BF16, SSD_F16 = 0, 1, 2
 STAGE_CHUNK_CUMSUM, STAGE_CHUNK_STATE, STAGE_STATE_PASS, STAGE_CHUNK_SCAN = 1, 2, 4, 8
 STAGE_ALL = 15
+VARIANT_SCAN_ROWS, VARIANT_SCAN_HEADS = 0x100, 0x200
+SCAN_VARIANTS = {"auto": 0, "rows": VARIANT_SCAN_ROWS, "heads": VARIANT_SCAN_HEADS}
 ERRORS = {0: "SSD_OK", -1: "SSD_ERR_INVALID_ARG", -2: "SSD_ERR_UNSUPPORTED",
           -3: "SSD_ERR_WORKSPACE", -4: "SSD_ERR_HIP"}
 EXPORTS = ("ssd_scan_prefill_workspace", "ssd_scan_prefill", "ssd_scan_prefill_stages",
@@ -45,7 +47,7 @@ def load(path=LIB_PATH):
     lib = ctypes.CDLL(path)
     vp, i32, i64, sz, u32 = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t,
                              ctypes.c_uint)
-    lib.ssd_scan_prefill_workspace.argtypes = [i64, i32, i32, i32, i32, i32, i32]
+    lib.ssd_scan_prefill_workspace.argtypes = [i64, i32, i32, i32, i32, i32, i32, i32]
     lib.ssd_scan_prefill_workspace.restype = sz
     pre = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, i32, i32, vp, sz,
            vp]
@@ -128,25 +130,35 @@ def _need(t, name, dtype=None, dev=None):
         raise ValueError(f"{name} is on {t.device}, expected {dev}")
 
 
-def workspace_bytes(total_tokens, nseq, H, P, N, chunk, dtype=torch.bfloat16):
+def _shape(t, name, shape):
+    """Reject a tensor whose shape is not exactly `shape` (the C ABI cannot
+    check the size of a device buffer, so an undersized one would be written
+    out of bounds)."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {list(shape)}, got {list(t.shape)}")
+
+
+def workspace_bytes(total_tokens, nseq, H, P, N, G, chunk, dtype=torch.bfloat16):
     code = SSD_BF16 if dtype == torch.bfloat16 else SSD_F32
-    return int(load().ssd_scan_prefill_workspace(total_tokens, nseq, H, P, N, chunk, code))
+    return int(load().ssd_scan_prefill_workspace(total_tokens, nseq, H, P, N, G, chunk, code))
 
 
-def alloc_workspace(total_tokens, nseq, H, P, N, chunk, dtype, device):
-    n = workspace_bytes(total_tokens, nseq, H, P, N, chunk, dtype)
+def alloc_workspace(total_tokens, nseq, H, P, N, G, chunk, dtype, device):
+    n = workspace_bytes(total_tokens, nseq, H, P, N, G, chunk, dtype)
     if n == 0:
         raise SSDError(-2, "unsupported prefill shape")
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
 def prefill(x, dt, A, B, C, D, h0=None, chunk=256, cu_seqlens=None, *, nseq=None, y=None,
-            h_out=None, workspace=None, stages=STAGE_ALL, prepare=False):
+            h_out=None, workspace=None, stages=STAGE_ALL, scan="auto", prepare=False):
     """Chunked SSD prefill.
 
     x [T,H,P] (or [b,L,H,P]), dt [T,H], A [H], B/C [T,G,N], D [H], h0
     [nseq,H,N,P] float32 or None, cu_seqlens int32 [nseq+1] or None (dense
     batch: ``nseq`` sequences of T/nseq tokens; a 4-d x gives nseq = b).
+    ``scan``: "auto" (the library's choice), "rows" or "heads" forces the
+    chunk-scan kernel (SSD_VARIANT_SCAN_*).
     Returns (y [T,H,P] float32, h_out [nseq,H,N,P] float32); with
     ``prepare=True`` nothing runs and (Prepared, y, h_out) is returned.
     """
@@ -186,8 +198,14 @@ def prefill(x, dt, A, B, C, D, h0=None, chunk=256, cu_seqlens=None, *, nseq=None
         h_out = torch.empty((nseq, H, N, P), dtype=torch.float32, device=dev)
     _need(y, "y", torch.float32, dev)
     _need(h_out, "h_out", torch.float32, dev)
+    _shape(y, "y", (T, H, P))
+    _shape(h_out, "h_out", (nseq, H, N, P))
     if workspace is None:
-        workspace = alloc_workspace(T, nseq, H, P, N, chunk, x.dtype, dev)
+        workspace = alloc_workspace(T, nseq, H, P, N, G, chunk, x.dtype, dev)
+    _need(workspace, "workspace", torch.uint8, dev)
+    if scan not in SCAN_VARIANTS:
+        raise ValueError(f"scan must be one of {sorted(SCAN_VARIANTS)} (got {scan!r})")
+    stages = stages | SCAN_VARIANTS[scan]
     lib = load()
     args = (_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(y),
             _ptr(h_out), _ptr(cu_seqlens), nseq, T, H, P, N, G, chunk, code, _ptr(workspace),
@@ -218,11 +236,15 @@ class Prepared:
         self._keep = keep   # tensors whose memory the pointers refer to
 
     def __call__(self, stages=None):
+        """Run the call; ``stages`` (prefill only) replaces the stage bits,
+        keeping the call's kernel-variant bits."""
         s = _stream()
         if self._stages is None:
             rc = self._fn(*self._args, s)
         else:
-            rc = self._fn(self._stages if stages is None else stages, *self._args, s)
+            st = self._stages if stages is None else \
+                (stages & STAGE_ALL) | (self._stages & ~STAGE_ALL)
+            rc = self._fn(st, *self._args, s)
         if rc != 0:
             _check(rc)
 
@@ -252,6 +274,11 @@ def prefill_train(x, dt, A, B, C, D, h0=None, chunk=256, cu_seqlens=None, *, nse
         _need(t, n, x.dtype, dev)
     for t, n in ((dt, "dt"), (A, "A"), (D, "D")):
         _need(t, n, torch.float32, dev)
+    _shape(dt, "dt", (T, H))
+    _shape(A, "A", (H,))
+    _shape(D, "D", (H,))
+    _shape(B, "B", (T, G, N))
+    _shape(C, "C", (T, G, N))
     if cu_seqlens is not None:
         _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
         nseq = cu_seqlens.numel() - 1
@@ -265,6 +292,10 @@ def prefill_train(x, dt, A, B, C, D, h0=None, chunk=256, cu_seqlens=None, *, nse
         y = torch.empty((T, H, P), dtype=torch.float32, device=dev)
     if h_out is None:
         h_out = torch.empty((nseq, H, N, P), dtype=torch.float32, device=dev)
+    _need(y, "y", torch.float32, dev)
+    _need(h_out, "h_out", torch.float32, dev)
+    _shape(y, "y", (T, H, P))
+    _shape(h_out, "h_out", (nseq, H, N, P))
     lib = load()
     n = int(lib.ssd_scan_prefill_backward_workspace(T, nseq, H, P, N, G, chunk, code))
     if n == 0:
@@ -331,6 +362,7 @@ def prefill_backward(x, dt, A, B, C, D, dy, h0=None, dh_out=None, chunk=256, cu_
         if n == 0:
             raise SSDError(-2, "unsupported prefill shape")
         workspace = torch.empty(n, dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, dev)
     f32 = dict(dtype=torch.float32, device=dev)
     g = dict(dx=torch.empty((T, H, P), **f32), ddt=torch.empty((T, H), **f32),
              dA=torch.empty(H, **f32), dB=torch.empty((T, G, N), **f32),
@@ -385,6 +417,8 @@ def gated_delta_rule(q, k, v, g, beta, h0=None, cu_seqlens=None, *, nseq=None, o
         h_out = torch.empty((nseq, H, V, K), dtype=torch.float32, device=dev)
     _need(o, "o", torch.float32, dev)
     _need(h_out, "h_out", torch.float32, dev)
+    _shape(o, "o", (T, H, V))
+    _shape(h_out, "h_out", (nseq, H, V, K))
     lib = load()
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o), _ptr(h_out),
             _ptr(cu_seqlens), nseq, T, H, G, K, V, code)
@@ -422,9 +456,12 @@ def step(x, dt, A, B, C, D, h, y=None, prepare=False):
         raise ValueError("h must be [b,H,N,P], B/C [b,G,N]")
     if tuple(dt.shape) != (b, H):
         raise ValueError("dt must be [b,H]")
+    _shape(A, "A", (H,))
+    _shape(D, "D", (H,))
     if y is None:
         y = torch.empty((b, H, P), dtype=torch.float32, device=dev)
     _need(y, "y", torch.float32, dev)
+    _shape(y, "y", (b, H, P))
     args = (_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h), _ptr(y), b, H, P, N,
             G, code)
     if prepare:
@@ -450,9 +487,12 @@ def step_multi(x, dt, A, B, C, D, h, y=None, prepare=False):
         raise ValueError("h must be [b,H,N,P], B/C [S,b,G,N]")
     if tuple(dt.shape) != (S, b, H):
         raise ValueError("dt must be [S,b,H]")
+    _shape(A, "A", (H,))
+    _shape(D, "D", (H,))
     if y is None:
         y = torch.empty((S, b, H, P), dtype=torch.float32, device=dev)
     _need(y, "y", torch.float32, dev)
+    _shape(y, "y", (S, b, H, P))
     args = (_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h), _ptr(y), S, b, H, P,
             N, G, code)
     if prepare:
@@ -480,6 +520,7 @@ def conv1d_step(u, conv_state, w, bias=None, silu=True, out=None):
     if out is None:
         out = torch.empty_like(u)
     _need(out, "out", u.dtype, dev)
+    _shape(out, "out", (b, C))
     _check(load().ssd_conv1d_step(_ptr(u), _ptr(conv_state), _ptr(w), _ptr(bias), int(bool(silu)),
                                   _ptr(out), b, C, W, code, _stream()))
     return out
@@ -499,6 +540,7 @@ def gated_rmsnorm(y, z, w, eps=1e-5, out=None):
     if out is None:
         out = torch.empty_like(y)
     _need(out, "out", torch.float32, dev)
+    _shape(out, "out", (b, D))
     _check(load().ssd_gated_rmsnorm(_ptr(y), _ptr(z), _ptr(w), float(eps), _ptr(out), b, D, code,
                                     _stream()))
     return out
@@ -535,6 +577,13 @@ def decode_layer_step(xbc, z, dt, A, D, conv_state, conv_w, conv_b, h, norm_w, e
     for t, n, dt_ in ((out, "out", torch.float32), (xbc_act, "xbc_act", torch.float32),
                       (y, "y", torch.float32)):
         _need(t, n, dt_, dev)
+    _shape(out, "out", (b, inner))
+    _shape(xbc_act, "xbc_act", (b, Cn))
+    _shape(y, "y", (b, inner))
+    _shape(A, "A", (H,))
+    _shape(D, "D", (H,))
+    if conv_b is not None:
+        _shape(conv_b, "conv_b", (Cn,))
     args = (_ptr(xbc), _ptr(z), _ptr(dt), _ptr(A), _ptr(D), _ptr(conv_state), _ptr(conv_w),
             _ptr(conv_b), _ptr(h), _ptr(norm_w), float(eps), _ptr(out), _ptr(xbc_act), _ptr(y),
             b, H, P, N, G, W, code)
@@ -575,12 +624,15 @@ def selective_scan(x, dt, A, B, C, D, h0=None, *, y=None, h_out=None, workspace=
         h_out = torch.empty((b, d, N), dtype=torch.float32, device=dev)
     _need(y, "y", torch.float32, dev)
     _need(h_out, "h_out", torch.float32, dev)
+    _shape(y, "y", (b, L, d))
+    _shape(h_out, "h_out", (b, d, N))
     lib = load()
     if workspace is None:
         n = int(lib.ssd_selective_scan_workspace(b, L, d, N))
         if n == 0:
             raise SSDError(-2, "unsupported selective-scan shape")
         workspace = torch.empty(n, dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, dev)
     args = (_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(y), _ptr(h_out),
             b, L, d, N, code, _ptr(workspace), workspace.numel())
     if prepare:

@@ -47,8 +47,29 @@ def select_heads(d, heads, G):
     return out
 
 
-def maxabs(a, b):
-    a = np.asarray(a, np.float64)
-    b = np.asarray(b, np.float64)
+def maxabs(a, b, block=1 << 22):
+    """max |a - b| over every element, in float64 (blockwise, so that large
+    arrays need no full-size temporaries)."""
+    a = np.asarray(a)
+    b = np.asarray(b)
     assert a.shape == b.shape, (a.shape, b.shape)
-    return float(np.max(np.abs(a - b), initial=0.0))
+    fa, fb = a.reshape(-1), b.reshape(-1)
+    m = 0.0
+    for i in range(0, fa.size, block):
+        d = np.abs(fa[i:i + block].astype(np.float64) - fb[i:i + block].astype(np.float64))
+        m = max(m, float(np.max(d, initial=0.0)))
+    return m
+
+
+def ssm_scale(y_ref, x, D):
+    """max |y_ref - D x|: the size of the state-space part of the output (the
+    skip term D x dominates |y| at these distributions)."""
+    T = y_ref.shape[0]
+    m = 0.0
+    for i in range(0, T, 4096):
+        part = y_ref[i:i + 4096] - D[None, :, None].astype(np.float64) * x[i:i + 4096]
+        m = max(m, float(np.max(np.abs(part), initial=0.0)))
+    return m
+
+
+SSM_REL_TOL = 1e-2   # bound on max|dy| / max|y_ref - D x| in bfloat16 mode

@@ -11,8 +11,8 @@ library.  Each is a different route to the same mathematics:
   state carry.  This is the decomposition the GPU kernels implement
   (Compiler-First State Space Duality ..., Abstract: equal-length chunks whose
   work is dense contractions; Table 7: static lower-triangular mask; Recurrence
-  Scan, "One equation, one packed result": the SSD run chunk by chunk, each
-  chunk continuing from the previous chunk's state).
+  Scan, "One equation, one packed result": chunks processed in order, the
+  state left by one being the starting state of the next).
 * ``prefix_sum_A0``: the A = 0 closed form (a cumulative sum).
 Arrays: x [L,H,P], dt [L,H], A [H], B/C [L,G,N], D [H], h0 [H,N,P].
 """

@@ -32,56 +32,51 @@ def test_library_exports_every_declared_symbol():
 def test_workspace_size():
     lib = ssd.load()
     w = lib.ssd_scan_prefill_workspace
-    n1 = w(4096, 1, 24, 64, 128, 256, 1)
+    n1 = w(4096, 1, 24, 64, 128, 1, 256, 1)
     nc = 16
     # S (float32) + H_in (bf16) per chunk and head, and s, dt, u per chunk, head and row
     expect_min = nc * 24 * 128 * 64 * (4 + 2) + 3 * nc * 24 * 256 * 4
-    # bf16, P 64, N 128, chunk 256 and fewer than 2048 chunk-head units: the
-    # row-split scan's C.B^T fragments, 1 KB per (16-row tile, 32-row block)
-    cbg = nc * 24 * (256 // 16) * (256 // 32) * 1024
+    # bf16, P 64, N 128, chunk 256: the row-split scan's C.B^T fragments per
+    # (chunk, group), 1 KB per (16-row tile, 32-row block)
+    cbg = nc * 1 * (256 // 16) * (256 // 32) * 1024
     assert expect_min + cbg <= n1 <= expect_min + cbg + 8192
-    n32 = w(4096, 1, 24, 64, 128, 256, 0)                # float32: H_in in float32, no C.B^T
+    # the C.B^T region grows with the group count, not the head count
+    n8 = w(4096, 1, 24, 64, 128, 8, 256, 1)
+    assert n8 - n1 == 7 * cbg
+    n32 = w(4096, 1, 24, 64, 128, 1, 256, 0)             # float32: H_in in float32, no C.B^T
     expect32 = nc * 24 * 128 * 64 * (4 + 4) + 3 * nc * 24 * 256 * 4
     assert expect32 <= n32 <= expect32 + 8192
-    # past 2048 units (the heads-streamed scan): no C.B^T region
-    n80 = w(4096, 1, 160, 64, 128, 256, 1)
-    assert n80 <= nc * 160 * 128 * 64 * 6 + 3 * nc * 160 * 256 * 4 + 8192
-    assert w(4096, 1, 24, 64, 100, 256, 1) == 0          # unsupported N
-    assert w(4096, 1, 24, 64, 128, 96, 1) == 0           # unsupported chunk
-    assert w(4096, 1, 8192, 128, 128, 512, 1) == 0       # rows past 32-bit tile offsets
-    assert w(-1, 1, 24, 64, 128, 256, 1) == 0
-    assert w(0, 1, 24, 64, 128, 256, 1) > 0
+    assert w(4096, 1, 24, 64, 100, 1, 256, 1) == 0       # unsupported N
+    assert w(4096, 1, 24, 64, 128, 1, 96, 1) == 0        # unsupported chunk
+    assert w(4096, 1, 24, 64, 128, 1, 16, 1) == 0        # chunk 16 is refused
+    assert w(4096, 1, 24, 64, 128, 5, 256, 1) == 0       # H % G != 0
+    assert w(4096, 1, 8192, 128, 128, 1, 512, 1) == 0    # x rows past 32-bit tile offsets
+    assert w(4096, 1, 8192, 16, 128, 8192, 512, 1) == 0  # B rows past 32-bit tile offsets
+    assert w(-1, 1, 24, 64, 128, 1, 256, 1) == 0
+    assert w(0, 1, 24, 64, 128, 1, 256, 1) > 0
 
 
-def test_cbg_region_follows_the_row_split_rule():
-    """The workspace holds the row split's C.B^T fragments exactly where the
-    bench's per-launch work model says C.B^T moves to the state-pass launch
-    (bf16, P 64, N 128, chunk <= 256, fewer than 2048 chunk-head units)."""
-    import importlib.util
-    import os
-    from types import SimpleNamespace
-    spec = importlib.util.spec_from_file_location(
-        "bench_model", os.path.join(os.path.dirname(__file__), "..", "bench.py"))
-    bench = importlib.util.module_from_spec(spec)
-    spec.loader.exec_module(bench)
+def test_cbg_region_sized_by_groups():
+    """The workspace holds the row split's C.B^T fragments for every (chunk,
+    group) for bf16 with P 64, N 128 and chunk <= 256, and nothing else
+    depends on G."""
     w = ssd.load().ssd_scan_prefill_workspace
-    for T, nseq, H, P, N, Q, dt in [(4096, 1, 24, 64, 128, 256, "bf16"),
-                                    (4096, 1, 24, 64, 128, 256, "f32"),
-                                    (4096, 1, 24, 64, 64, 256, "bf16"),
-                                    (4096, 1, 24, 64, 128, 512, "bf16"),
-                                    (32768, 4, 80, 64, 128, 256, "bf16"),
-                                    (1000, 3, 127, 64, 128, 64, "bf16"),
-                                    (1000, 3, 128, 64, 128, 64, "bf16")]:
+    for T, nseq, H, P, N, G, Q, dt in [(4096, 1, 24, 64, 128, 1, 256, "bf16"),
+                                       (4096, 1, 24, 64, 128, 1, 256, "f32"),
+                                       (4096, 1, 24, 64, 64, 1, 256, "bf16"),
+                                       (4096, 1, 24, 64, 128, 1, 512, "bf16"),
+                                       (32768, 4, 80, 64, 128, 1, 256, "bf16"),
+                                       (1000, 3, 128, 64, 128, 8, 64, "bf16"),
+                                       (1000, 3, 128, 64, 128, 2, 32, "bf16")]:
         e = 2 if dt == "bf16" else 4
         nc = (T + nseq * (Q - 1)) // Q
-        region = nc * H * (Q // 16) * (Q // 32) * 1024
+        region = nc * G * (Q // 16) * (Q // 32) * 1024
         base = sum(-(-b // 256) * 256 for b in (16 * max(nc, 1), 4 * (nseq + 1),
                                                   4 * nc * H * Q, 4 * nc * H * Q, 4 * nc * H * Q,
                                                   4 * nc * H * N * P, e * nc * H * N * P))
-        got = w(T, nseq, H, P, N, Q, 1 if dt == "bf16" else 0)
-        wl = SimpleNamespace(dtype=dt, P=P, N=N, chunk=Q, H=H)
-        has = bench.cbg_launch(wl, T, nseq)
-        assert got == base + (-(-region // 256) * 256 if has else 0), (T, nseq, H, P, N, Q, dt)
+        got = w(T, nseq, H, P, N, G, Q, 1 if dt == "bf16" else 0)
+        has = dt == "bf16" and P == 64 and N == 128 and Q <= 256
+        assert got == base + (-(-region // 256) * 256 if has else 0), (T, nseq, H, P, N, G, Q, dt)
 
 
 def _prefill_rc(**kw):
@@ -102,6 +97,7 @@ def _prefill_rc(**kw):
     (dict(P=24), -2, "headdim"),
     (dict(N=100), -2, "d_state"),
     (dict(chunk=48), -2, "chunk"),
+    (dict(chunk=16), -2, "use chunk 32"),
     (dict(chunk=1024), -2, "chunk"),
     (dict(H=8192, P=128, chunk=512), -2, "row stride"),  # 32-bit tile offsets
     (dict(nseq=0), -1, "nseq"),
@@ -117,11 +113,20 @@ def test_prefill_rejects_before_launch(kw, code, frag):
     assert rc == code and frag in msg, (rc, msg)
 
 
-def test_stage_mask_rejected():
+@pytest.mark.parametrize("stages,frag", [(16, "stage"), (0x400, "stage"),
+                                          (0x30f, "exclusive")])
+def test_stage_mask_rejected(stages, frag):
     lib = ssd.load()
-    rc = lib.ssd_scan_prefill_stages(16, *([ctypes.c_void_p(1)] * 10), 1, 64, 4, 16, 16, 1, 64, 0,
-                                     ctypes.c_void_p(256), 1 << 30, None)
-    assert rc == -1 and "stage" in lib.ssd_last_error().decode()
+    rc = lib.ssd_scan_prefill_stages(stages, *([ctypes.c_void_p(1)] * 10), 1, 64, 4, 16, 16, 1,
+                                     64, 0, ctypes.c_void_p(256), 1 << 30, None)
+    assert rc == -1 and frag in lib.ssd_last_error().decode()
+
+
+def test_variant_bits_match_the_header():
+    src = open(HEADER).read()
+    vals = {k: int(v, 16) for k, v in re.findall(r"(SSD_VARIANT_\w+)\s*=\s*(0x[0-9a-fA-F]+)u", src)}
+    assert vals["SSD_VARIANT_SCAN_ROWS"] == ssd.VARIANT_SCAN_ROWS
+    assert vals["SSD_VARIANT_SCAN_HEADS"] == ssd.VARIANT_SCAN_HEADS
 
 
 @pytest.mark.parametrize("kw,code,frag", [
@@ -188,7 +193,7 @@ def test_selective_scan_rejects_before_launch(kw, code, frag):
 def test_backward_workspace_size():
     lib = ssd.load()
     w = lib.ssd_scan_prefill_backward_workspace
-    fwd = lib.ssd_scan_prefill_workspace(4096, 1, 24, 64, 128, 256, 1)
+    fwd = lib.ssd_scan_prefill_workspace(4096, 1, 24, 64, 128, 1, 256, 1)
     n1 = w(4096, 1, 24, 64, 128, 1, 256, 1)
     nc = 16
     # the forward's workspace, then: final states (f32), states entering each chunk
@@ -262,3 +267,96 @@ def test_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError, match="GPU"):
         ssd.prefill(x, torch.zeros(64, 4), torch.zeros(4), torch.zeros(64, 1, 16),
                     torch.zeros(64, 1, 16), torch.zeros(4))
+
+
+class _NoLib:
+    """Stands in for libssd.so: any call into it fails the test (the binding
+    must refuse bad shapes before calling the library)."""
+
+    def __getattr__(self, name):
+        raise AssertionError(f"library called ({name}) despite a bad argument")
+
+
+@pytest.fixture
+def no_device(monkeypatch):
+    """Let CPU tensors pass the binding's device check, and make any library
+    call an error, so the shape checks can be tested without a GPU."""
+    import torch
+
+    def need(t, name, dtype=None, dev=None):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch tensor")
+        if dtype is not None and t.dtype != dtype:
+            raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+    monkeypatch.setattr(ssd, "_need", need)
+    monkeypatch.setattr(ssd, "load", lambda *a: _NoLib())
+
+
+def _prefill_args(T=64, H=4, P=16, N=16, G=1):
+    import torch
+    f = torch.float32
+    return (torch.zeros(T, H, P), torch.zeros(T, H, dtype=f), torch.zeros(H), torch.zeros(T, G, N),
+            torch.zeros(T, G, N), torch.zeros(H))
+
+
+@pytest.mark.parametrize("bad", ["y", "h_out", "A", "D", "dt", "B"])
+def test_binding_rejects_wrong_prefill_shapes(no_device, bad):
+    import torch
+    x, dt, A, B, C, D = _prefill_args()
+    kw = dict(y=torch.zeros(64, 4, 16), h_out=torch.zeros(1, 4, 16, 16),
+              workspace=torch.zeros(1 << 16, dtype=torch.uint8))
+    if bad == "y":
+        kw["y"] = torch.zeros(63, 4, 16)
+    elif bad == "h_out":
+        kw["h_out"] = torch.zeros(1, 4, 16, 8)
+    elif bad == "A":
+        A = torch.zeros(3)
+    elif bad == "D":
+        D = torch.zeros(4, 1)
+    elif bad == "dt":
+        dt = torch.zeros(64, 3)
+    elif bad == "B":
+        B = torch.zeros(64, 1, 8)
+    with pytest.raises(ValueError):
+        ssd.prefill(x, dt, A, B, C, D, **kw)
+
+
+@pytest.mark.parametrize("bad", ["y", "h_out"])
+def test_binding_rejects_wrong_train_forward_shapes(no_device, bad):
+    import torch
+    x, dt, A, B, C, D = _prefill_args()
+    kw = dict(y=torch.zeros(64, 4, 16), h_out=torch.zeros(1, 4, 16, 16))
+    kw[bad] = torch.zeros(2, 4, 16, 16) if bad == "h_out" else torch.zeros(64, 4, 8)
+    with pytest.raises(ValueError):
+        ssd.prefill_train(x, dt, A, B, C, D, **kw)
+
+
+@pytest.mark.parametrize("bad", ["y", "A", "D"])
+@pytest.mark.parametrize("multi", [False, True])
+def test_binding_rejects_wrong_step_shapes(no_device, bad, multi):
+    import torch
+    b, H, P, N, G, S = 2, 4, 16, 16, 1, 3
+    lead = (S, b) if multi else (b,)
+    x, dt = torch.zeros(*lead, H, P), torch.zeros(*lead, H)
+    Bm, Cm = torch.zeros(*lead, G, N), torch.zeros(*lead, G, N)
+    A, D, h = torch.zeros(H), torch.zeros(H), torch.zeros(b, H, N, P)
+    y = torch.zeros(*lead, H, P)
+    if bad == "y":
+        y = torch.zeros(*lead, H, P - 1)
+    elif bad == "A":
+        A = torch.zeros(H + 1)
+    else:
+        D = torch.zeros(1)
+    fn = ssd.step_multi if multi else ssd.step
+    with pytest.raises(ValueError):
+        fn(x, dt, A, Bm, Cm, D, h, y=y)
+
+
+def test_binding_rejects_wrong_scan_variant(no_device):
+    import torch
+    x, dt, A, B, C, D = _prefill_args()
+    with pytest.raises(ValueError, match="scan"):
+        ssd.prefill(x, dt, A, B, C, D, y=torch.zeros(64, 4, 16),
+                    h_out=torch.zeros(1, 4, 16, 16),
+                    workspace=torch.zeros(1 << 16, dtype=torch.uint8), scan="diagonal")
