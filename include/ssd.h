@@ -75,7 +75,15 @@ enum {
     SSD_VARIANT_SCAN_HEADS = 0x200u, /* chunk scan: the heads of a B/C group streamed
                                         through one workgroup (bf16, P 64, N 128 and a
                                         few other shapes; otherwise the row split) */
-    SSD_VARIANT_MASK = 0x300u
+    SSD_VARIANT_STATE_CHUNKS = 0x400u, /* states: every chunk state written, then passed
+                                          along the chunks by a second kernel */
+    SSD_VARIANT_STATE_WALK = 0x800u,   /* states: one kernel walks each sequence's chunks
+                                          with the state in registers (bf16, P 64,
+                                          N 128, chunk <= 256; otherwise the chunk
+                                          states).  Stages 1,
+                                          2 and 4 are then one kernel: each of those bits
+                                          runs all three (h_out is written with bit 4) */
+    SSD_VARIANT_MASK = 0xF00u
 };
 
 /*
@@ -90,6 +98,15 @@ enum {
  */
 size_t ssd_scan_prefill_workspace(int64_t total_tokens, int nseq, int H, int P, int N, int G,
                                   int chunk, ssd_dtype_t dtype);
+
+/*
+ * The kernels ssd_scan_prefill() would run for these shapes (packed != 0: a
+ * cu_seqlens array will be passed): one SSD_VARIANT_STATE_* bit for the
+ * states and one SSD_VARIANT_SCAN_* bit for the chunk scan; 0 for arguments
+ * the prefill would reject.  A planning query: nothing is enqueued.
+ */
+unsigned ssd_scan_prefill_plan(int64_t total_tokens, int nseq, int H, int P, int N, int G,
+                               int chunk, ssd_dtype_t dtype, int packed);
 
 /*
  * Chunked SSD prefill over a packed batch of sequences.

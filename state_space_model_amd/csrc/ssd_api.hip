@@ -65,6 +65,8 @@ int prefill_impl(unsigned stages, const void *x, const float *dt, const float *A
     return fail(SSD_ERR_INVALID_ARG, "unknown stage bits 0x%x", stages);
   if ((stages & SSD_VARIANT_SCAN_ROWS) && (stages & SSD_VARIANT_SCAN_HEADS))
     return fail(SSD_ERR_INVALID_ARG, "SSD_VARIANT_SCAN_ROWS and _HEADS are exclusive");
+  if ((stages & SSD_VARIANT_STATE_CHUNKS) && (stages & SSD_VARIANT_STATE_WALK))
+    return fail(SSD_ERR_INVALID_ARG, "SSD_VARIANT_STATE_CHUNKS and _WALK are exclusive");
   const ssd::WorkspaceLayout L =
       ssd::prefill_layout(T, nseq, H, P, N, G, chunk, dtype == SSD_BF16 ? 2 : 4);
   if (!workspace || workspace_bytes < L.total)
@@ -94,6 +96,13 @@ size_t ssd_scan_prefill_workspace(int64_t total_tokens, int nseq, int H, int P, 
   if ((int64_t)chunk * H * P * 4 > INT32_MAX || (int64_t)chunk * G * N * 4 > INT32_MAX) return 0;
   return ssd::prefill_layout(total_tokens, nseq, H, P, N, G, chunk, dtype == SSD_BF16 ? 2 : 4)
       .total;
+}
+
+unsigned ssd_scan_prefill_plan(int64_t total_tokens, int nseq, int H, int P, int N, int G,
+                               int chunk, ssd_dtype_t dtype, int packed) {
+  if (ssd_scan_prefill_workspace(total_tokens, nseq, H, P, N, G, chunk, dtype) == 0) return 0;
+  return ssd::prefill_plan(total_tokens, nseq, H, P, N, G, chunk, dtype == SSD_BF16, packed != 0,
+                           0u);
 }
 
 int ssd_scan_prefill(const void *x, const float *dt, const float *A, const void *B, const void *C,

@@ -41,10 +41,16 @@ struct WorkspaceLayout {
   // P 64, N 128 and chunk <= 256
   size_t cbg;
   bool has_cbg;
+  // B of every (chunk, group) in MFMA fragment order for the state walk,
+  // [nc_max][G][Q/32][N/16][64 lanes][8] bf16 (bf16 with P 64, N 128)
+  size_t bfrag;
+  bool has_bfrag;
   size_t total;
 };
 
 WorkspaceLayout prefill_layout(int64_t T, int nseq, int H, int P, int N, int G, int Q, int elem);
+unsigned prefill_plan(int64_t T, int nseq, int H, int P, int N, int G, int Q, bool bf16,
+                      bool packed, unsigned variant);
 hipError_t launch_prefill(const PrefillArgs &a, unsigned stages);
 
 // Stages 1-2: chunk-local cumulative decay (s, dt, u) and, if `state`, the
@@ -52,6 +58,19 @@ hipError_t launch_prefill(const PrefillArgs &a, unsigned stages);
 // states Sb_c = sum_t 2^(s_t) C_t dy_t^T, written over S.
 hipError_t launch_chunk_state(const PrefillArgs &a, const WorkspaceLayout &L, int nc, bool state,
                               hipStream_t st, bool bwd = false);
+
+// Stages 1, 2 and 4 in one kernel for large batches (ssd_state_walk.hip): a
+// workgroup per (sequence, head) walks the sequence's
+// chunks in order with the state in registers, writing s, dt, u and the
+// entering states (operand type) -- the chunk states never reach memory.
+// walk_choice() says whether the library uses it for a call (the variant bits
+// force either way); launch_state_walk() enqueues it (after the chunk map of a
+// packed batch), writing h_out only when write_hout.
+constexpr long kWalkMinChains = 128;
+bool walk_supported(int P, int N, int Q, bool bf16);
+bool walk_choice(int P, int N, int Q, bool bf16, int nseq, int H, bool packed, unsigned variant);
+hipError_t launch_state_walk(const PrefillArgs &a, const WorkspaceLayout &L, int nc,
+                             bool write_hout, hipStream_t st);
 
 // Chunk scan with the heads of a B/C group streamed through one workgroup
 // (bfloat16, selected P/N/Q).  scan_heads_choice() returns the heads per

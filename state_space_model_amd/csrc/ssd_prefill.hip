@@ -28,6 +28,7 @@
 // nothing (decay 1, no input), so the chunk-end value s_{Q-1} equals
 // s_{len-1}.  The workspace holds s in base-2 units (s * log2(e)) so every
 // decay is one v_exp_f32 (2^x) of a non-positive argument.
+#include "ssd.h"
 #include "ssd_launch.h"
 #include "ssd_prefill_util.h"
 
@@ -572,8 +573,24 @@ WorkspaceLayout prefill_layout(int64_t T, int nseq, int H, int P, int N, int G, 
   L.cbg = off;
   L.has_cbg = elem == 2 && P == 64 && N == 128 && Q <= 256;
   if (L.has_cbg) off = align_up(off + (size_t)nc * G * (Q / 16) * (Q / 32) * 1024, 256);
+  L.bfrag = off;
+  L.has_bfrag = walk_supported(P, N, Q, elem == 2);
+  if (L.has_bfrag) off = align_up(off + (size_t)nc * G * Q * N * 2, 256);
   L.total = off;
   return L;
+}
+
+// Which implementation runs each part of a call: SSD_VARIANT_STATE_* for the
+// states (stages 1, 2, 4) and SSD_VARIANT_SCAN_* for the chunk scan.
+unsigned prefill_plan(int64_t T, int nseq, int H, int P, int N, int G, int Q, bool bf16,
+                      bool packed, unsigned variant) {
+  const int64_t nc = (T + (int64_t)nseq * (Q - 1)) / Q;
+  const int L_dense = packed ? 0 : (int)(T / nseq);
+  const int nc_real = L_dense > 0 ? nseq * ((L_dense + Q - 1) / Q) : (int)nc;
+  const bool walk = nc > 0 && walk_choice(P, N, Q, bf16, nseq, H, packed, variant);
+  const int HB = scan_heads_choice(P, N, Q, bf16, nc_real, H, G, variant);
+  return (walk ? SSD_VARIANT_STATE_WALK : SSD_VARIANT_STATE_CHUNKS) |
+         (HB > 0 ? SSD_VARIANT_SCAN_HEADS : SSD_VARIANT_SCAN_ROWS);
 }
 
 template <typename T, int P, int N>
@@ -592,7 +609,10 @@ static hipError_t run_prefill(const PrefillArgs &a, unsigned stages) {
   const ChunkMap cmap{info, L_dense, a.nseq, a.Q};
   hipStream_t st = static_cast<hipStream_t>(a.stream);
 
-  if ((stages & 3u) && (a.cu || L_dense == 0)) {
+  // the state walk does stages 1, 2 and 4 in one kernel
+  const bool walk =
+      nc > 0 && walk_choice(P, N, a.Q, a.bf16, a.nseq, a.H, a.cu != nullptr, a.variant);
+  if ((stages & (walk ? 7u : 3u)) && (a.cu || L_dense == 0)) {
     // packed (or empty) batch: chunk map first.  Block 0 also writes the first
     // chunk of every sequence, which the state pass reads even when there are
     // no chunks at all (then every entry is 0).
@@ -601,7 +621,10 @@ static hipError_t run_prefill(const PrefillArgs &a, unsigned stages) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if ((stages & 3u) && nc > 0) {  // cumulative decay (stage 1) and chunk states (stage 2)
+  if (walk && (stages & 7u)) {
+    hipError_t e = launch_state_walk(a, L, nc, (stages & 4u) != 0, st);
+    if (e != hipSuccess) return e;
+  } else if ((stages & 3u) && nc > 0) {  // cumulative decay (stage 1) and chunk states (stage 2)
     hipError_t e = launch_chunk_state(a, L, nc, (stages & 2u) != 0, st);
     if (e != hipSuccess) return e;
   }
@@ -628,10 +651,15 @@ static hipError_t run_prefill(const PrefillArgs &a, unsigned stages) {
       const long blocks = (units + 3) / 4, per_z = (long)npb * a.H;
       gz = (int)((blocks + per_z - 1) / per_z);
     }
-    hipLaunchKernelGGL(k_state_pass<T>, dim3(npb, a.H, a.nseq + gz), dim3(256), 0, st, S, s_ws,
-                       seq_off, cmap, a.h0, a.h_out, hin, a.H, NP, a.Q, a.hin32, a.h_out2, ca);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    // with the walk, the launch carries only the C.B^T units (if any)
+    if (walk) ca.nz = 0;
+    const int gzs = walk ? gz : a.nseq + gz;
+    if (gzs > 0) {
+      hipLaunchKernelGGL(k_state_pass<T>, dim3(npb, a.H, gzs), dim3(256), 0, st, S, s_ws,
+                         seq_off, cmap, a.h0, a.h_out, hin, a.H, NP, a.Q, a.hin32, a.h_out2, ca);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   if ((stages & 8u) && nc > 0 && HB > 0) {
     hipError_t e = launch_scan_heads(a, L, nc, HB, st);

@@ -1,0 +1,430 @@
+// ssd_state_walk.hip -- the state half of the chunked prefill for large
+// batches in one kernel: per chunk the cumulative decay, the chunk state and
+// the carried state, walking each sequence's chunks in order with the state
+// held in registers, so no chunk state is written to memory and read back.
+//
+// Per (sequence, head) and its chunks c in order (s in log2 units, every
+// exponent <= 0):
+//   s_i    = log2(e) A_h sum_{k<=i} dt_k                       chunk-local
+//   S_c^T  = sum_j x_j (2^(s_end - s_j) dt_j B_j)^T             P x N, MFMA over tokens
+//   H_in_c = H                                                  stored for the chunk scan
+//   H      = 2^(s_end) H + S_c                                  float32, in registers
+// with H = h0 (or 0) before the first chunk and h_out = H after the last: the
+// recurrence regrouped into fixed-length chunks (Compiler-First State Space
+// Duality and Portable O(1) Autoregressive Caching for Inference, Abstract:
+// one scalar decay per head, equal chunks whose work is dense contractions;
+// float32 decay as in its Table 8), and the state handed from chunk to chunk
+// as Recurrence Scan's schedule carries it from one launch to the next ("The
+// schedule").  Also written for the chunk scan: s, dt and u_j = 2^(s_r - s_j)
+// dt_j (r the last row of j's 32-row block), [chunk][head][Q].
+//
+// The chunk states do not depend on one another, only their sum does, so the
+// walk's serial part is one multiply-add per state element per chunk; what a
+// chain waits for is its loads.  A workgroup (4 waves) owns one chain -- a
+// (sequence, head) -- and streams its chunks with the next chunk's loads in
+// flight: the x rows go straight to LDS (block-swizzled, read transposed as the
+// MFMA A operand), the decay-scaled B rows come from a copy of B already in
+// MFMA fragment order (k_bfrag) straight into registers, so B, which every head
+// of a group shares, is never staged per head.  Every wave computes the
+// chunk's decay itself (a scan of 64 lanes), so no barrier waits for it.  A
+// wave owns two n-tiles and all four p-tiles of the chain's P x N state.
+#include "ssd.h"
+#include "ssd_launch.h"
+#include "ssd_prefill_util.h"
+
+namespace ssd {
+
+// B in MFMA fragment order for the chunk-state product:
+// out[chunk][group][Q/32][N/16][64 lanes][8] bf16.  Lane l of fragment (ks, nt)
+// holds column n = 16 nt + l % 16 at tokens 32 ks + 4 (l / 16) + r (slots
+// 0..3) and 32 ks + 16 + 4 (l / 16) + r (slots 4..7), r = 0..3 -- the paired
+// token map of the x fragments read transposed from LDS -- and zero past the
+// chunk's end.  One workgroup per (chunk, group), a wave per fragment.
+__global__ __launch_bounds__(256) void k_bfrag(const bf16 *__restrict__ B, ChunkMap cmap, int nc,
+                                               int G, int Q, bf16 *__restrict__ out) {
+  constexpr int N = 128, NTL = N / 16;
+  const int c = blockIdx.x / G, g = blockIdx.x - (blockIdx.x / G) * G;
+  if (c >= nc) return;
+  const int4 ci = cmap(c);
+  const int len = ci.z;
+  if (len <= 0) return;
+  const int lane = threadIdx.x & 63, grp = lane >> 4, col = lane & 15;
+  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const size_t bstride = (size_t)G * N;
+  // raw 16-bit patterns (the fragment is assembled with integer ops, not by
+  // element inserts into a bf16 vector)
+  const unsigned short *bg =
+      reinterpret_cast<const unsigned short *>(B) + (size_t)ci.y * bstride + (size_t)g * N;
+  const int nfr = (Q / 32) * NTL;
+  bf16 *oc = out + ((size_t)c * G + g) * (size_t)nfr * 512;
+  for (int f = wave; f < nfr; f += nw) {
+    const int ks = f / NTL, nt = f - (f / NTL) * NTL;
+    const int n = 16 * nt + col, j0 = 32 * ks + 4 * grp;
+    uint32_t v[8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      v[r] = j0 + r < len ? bg[(size_t)(j0 + r) * bstride + n] : 0u;
+      v[4 + r] = j0 + 16 + r < len ? bg[(size_t)(j0 + 16 + r) * bstride + n] : 0u;
+    }
+    const i4v packed = i4v{(int)(v[0] | (v[1] << 16)), (int)(v[2] | (v[3] << 16)),
+                           (int)(v[4] | (v[5] << 16)), (int)(v[6] | (v[7] << 16))};
+    *reinterpret_cast<i4v *>(oc + (size_t)f * 512 + lane * 8) = packed;
+  }
+}
+
+template <int Q, int NH, int JP_> struct WalkCfg {
+  static constexpr int P = 64, N = 128;
+  static constexpr int NW = 4;                  // waves
+  static constexpr int NT = N / 16 / NH;        // n-tiles of the chain's state block
+  static constexpr int NTW = NT / NW;           // n-tiles per wave
+  static constexpr int JP = JP_ < Q ? JP_ : Q;  // rows per phase
+  static constexpr int NPH = Q / JP;            // phases per chunk
+  static constexpr int KSP = JP / 32;           // token k-steps per phase
+  static constexpr int XB = (JP / 8) * kBlk128;  // one phase's x tile
+  static constexpr int DTN = Q < 64 ? 64 : Q;   // floats of a dt column buffer (whole-wave loads)
+  static constexpr int OFF_DT = 2 * XB;
+  static constexpr int OFF_W = OFF_DT + 2 * DTN * 4;  // a w row per wave
+  static constexpr int LDS = OFF_W + NW * DTN * 4;
+  static_assert(NTW >= 1 && NT % NW == 0 && Q <= 256, "walk shape");
+};
+
+// One 4-byte-per-lane buffer load into LDS at lds_addr + 4 * lane, issued from
+// inline assembly for the reason given at lds_load16 (the caller waits).
+__device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t rs, uint32_t lds_addr,
+                                          uint32_t voff) {
+  asm volatile("buffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "{m0}"(lds_addr)
+               : "memory");
+}
+
+// The chunk's cumulative decay, computed by every wave from the chunk's dt
+// column in LDS (rows past its length hold 0), R consecutive rows per lane:
+// s = log2(e) A cumsum(dt), w_j = 2^(s_end - s_j) dt_j into the wave's own LDS
+// row w_l (read back by the same wave only: no barrier); with `emit`, s, dt
+// and u_j = 2^(s_r - s_j) dt_j at `off` of the output rows.  Returns s_end.
+template <int Q>
+__device__ __forceinline__ float walk_decay(const float *dt_l, float *w_l, float a2, bool emit,
+                                            size_t off, float *__restrict__ s_out,
+                                            float *__restrict__ dt_out,
+                                            float *__restrict__ u_out) {
+  constexpr int R = Q >= 64 ? Q / 64 : 1;
+  const int lane = threadIdx.x & 63;
+  float d[R], sv[R];
+  float run = 0.f;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int i = lane * R + r;
+    d[r] = i < Q ? dt_l[i] : 0.f;
+    run += d[r] * a2;
+    sv[r] = run;
+  }
+  float incl = run;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  const float excl = incl - run;
+#pragma unroll
+  for (int r = 0; r < R; ++r) sv[r] += excl;
+  // row Q - 1 sits in slot R - 1 of lane (Q - 1) / R; the last row of a lane's
+  // 32-row block in slot R - 1 of the block's last lane
+  const float s_end = __shfl(sv[R - 1], (Q - 1) / R, 64);
+  const float s_ref = __shfl(sv[R - 1], lane | (32 / R - 1), 64);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int i = lane * R + r;
+    if (i < Q) {
+      w_l[i] = __builtin_amdgcn_exp2f(fminf(s_end - sv[r], 0.f)) * d[r];
+      if (emit) {
+        s_out[off + i] = sv[r];
+        dt_out[off + i] = d[r];
+        u_out[off + i] = __builtin_amdgcn_exp2f(fminf(s_ref - sv[r], 0.f)) * d[r];
+      }
+    }
+  }
+  return s_end;
+}
+
+// The x rows of phase ph of chunk ci -> a block-swizzled LDS tile (rows past
+// the chunk read 0).  The source address and length are made wave-uniform
+// explicitly so the buffer descriptor stays in scalar registers.
+template <typename K>
+__device__ __forceinline__ void walk_issue_x(const bf16 *__restrict__ x, int4 ci, int ph,
+                                             size_t xstride, int hd, uint32_t xl, char *tile,
+                                             int wave) {
+  const int t0 = __builtin_amdgcn_readfirstlane(ci.y), len = __builtin_amdgcn_readfirstlane(ci.z);
+  const int r0 = ph * K::JP;
+  const int vr = max(0, min(K::JP, len - r0));
+  const uint32_t xsb = (uint32_t)(xstride * 2);
+  const uint64_t xa =
+      reinterpret_cast<uint64_t>(x + ((size_t)t0 + r0) * xstride + (size_t)hd * K::P);
+  const uint64_t xu = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)xa) |
+                      ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(xa >> 32)) << 32);
+  dma_swz<kBlk128>(tile, reinterpret_cast<const void *>(xu),
+                   (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)vr * xsb)), xl,
+                   8 * xsb, K::JP / 8, wave, K::NW);
+}
+
+// The dt column of chunk ci (rows past the chunk read 0) -> LDS at lds_addr.
+template <typename K>
+__device__ __forceinline__ void walk_issue_dt(const float *__restrict__ dt, int4 ci, int H, int hd,
+                                              uint32_t lds_addr, int wave) {
+  const int t0 = __builtin_amdgcn_readfirstlane(ci.y), len = __builtin_amdgcn_readfirstlane(ci.z);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float *>(dt + (size_t)t0 * H + hd), (short)0, len > 0 ? (len - 1) * H * 4 + 4 : 0,
+      0x00020000);
+  const int lane = threadIdx.x & 63;
+  for (int r = wave * 64; r < K::DTN; r += K::NW * 64)
+    lds_load4(rs, lds_addr + r * 4, (uint32_t)(r + lane) * (uint32_t)H * 4);
+}
+
+// The B fragments of phase ph of a chunk (bc: the chunk's fragments at this
+// wave's first n-tile and lane) for the wave's NTW n-tiles.
+template <typename K>
+__device__ __forceinline__ void walk_load_b(const bf16 *bc, int ph,
+                                            bf16x8 (&bf)[K::NTW][K::KSP]) {
+  constexpr int NTL = K::N / 16;
+#pragma unroll
+  for (int k = 0; k < K::KSP; ++k)
+#pragma unroll
+    for (int t = 0; t < K::NTW; ++t)
+      bf[t][k] = *reinterpret_cast<const bf16x8 *>(
+          bc + (size_t)((ph * K::KSP + k) * NTL + t) * 512);
+}
+
+template <int Q, int NH, int JP_>
+__global__ __launch_bounds__(256) void k_state_walk(
+    const bf16 *__restrict__ x, const float *__restrict__ dt, const float *__restrict__ A,
+    const bf16 *__restrict__ bfr, const int *__restrict__ seq_off, ChunkMap cmap, int H, int G,
+    int nchain, const float *h0, float *h_out, float *__restrict__ s_out,
+    float *__restrict__ dt_out, float *__restrict__ u_out, bf16 *__restrict__ hin,
+    float *__restrict__ hin32, float *h_out2) {
+  typedef WalkCfg<Q, NH, JP_> K;
+  constexpr int P = K::P, N = K::N, NTW = K::NTW, NPT = P / 16, KSP = K::KSP, NPH = K::NPH;
+  constexpr int NTL = N / 16, JP = K::JP;
+  // chains in contiguous blocks per XCD (workgroup L runs on XCD L % 8), so the
+  // chains of one sequence, which read the same B fragments, share an L2
+  const int per = (nchain + 7) >> 3;
+  const int chn = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+  if (chn >= nchain) return;
+  const int part = chn % NH, sh = chn / NH;
+  const int hd = __builtin_amdgcn_readfirstlane(sh % H), s = __builtin_amdgcn_readfirstlane(sh / H);
+  int c0, c1;  // chunks of sequence s
+  if (cmap.L > 0) {
+    const int cps = (cmap.L + Q - 1) / Q;
+    c0 = s * cps;
+    c1 = c0 + cps;
+  } else {
+    c0 = __builtin_amdgcn_readfirstlane(seq_off[s]);
+    c1 = __builtin_amdgcn_readfirstlane(seq_off[s + 1]);
+  }
+  const int g = (hd * G) / H;
+  const int lane = threadIdx.x & 63, grp = lane >> 4, col = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  extern __shared__ __align__(16) char smem[];
+  float *w_l = reinterpret_cast<float *>(smem + K::OFF_W) + wave * K::DTN;  // this wave's row
+  const uint32_t lds0 = (uint32_t)(size_t)(__attribute__((address_space(3))) char *)smem;
+
+  // the chain's state block in the accumulator layout of S^T tiles: tile
+  // (t, pt) of a lane holds H[n][p .. p+3], n = 16 (nt0 + t) + col, p = 16 pt + 4 grp
+  const int nt0 = part * K::NT + wave * NTW;
+  const size_t hofs = ((size_t)s * H + hd) * (size_t)(N * P);
+  f4 Hs[NTW][NPT];
+#pragma unroll
+  for (int t = 0; t < NTW; ++t)
+#pragma unroll
+    for (int pt = 0; pt < NPT; ++pt)
+      Hs[t][pt] = h0 ? ld4(h0 + hofs + (size_t)(16 * (nt0 + t) + col) * P + 16 * pt + 4 * grp)
+                     : zero4();
+
+  const size_t xstride = (size_t)H * P;
+  const int lb8 = lane >> 3;
+  const uint32_t xl = lb8 * (uint32_t)(xstride * 2) + 16 * ((lane & 7) ^ (2 * swz8(lb8)));
+  // B fragments of this wave's n-tiles: chunk c's at bfw + c * bfc
+  const bf16 *bfw = bfr + (size_t)g * ((Q / 32) * NTL) * 512 + (size_t)nt0 * 512 + lane * 8;
+  const size_t bfc = (size_t)G * ((Q / 32) * NTL) * 512;
+  // x fragment offsets (paired token map: rows k0 + 4 grp + col/4 and
+  // k0 + 16 + 4 grp + col/4; p-tile pt by XOR with 32 pt)
+  const int c4 = col >> 2, cq = 8 * (col & 3);
+  const int xbk = 4 * (grp & 1) + c4;
+  const int xo = (grp >> 1) * kBlk128 + xbk * 128 + cq + 32 * swz8(xbk);
+  const float a2 = A[hd] * kLog2e;
+
+  typedef bf16x8 BF[NTW][KSP];
+  BF bcur;
+  int4 cn = make_int4(0, 0, 0, 0);  // the next chunk's map entry, read a chunk ahead
+  if (c0 < c1) {
+    const int4 ci = cmap(c0);
+    walk_issue_dt<K>(dt, ci, H, hd, lds0 + K::OFF_DT, wave);
+    walk_issue_x<K>(x, ci, 0, xstride, hd, xl, smem, wave);
+    walk_load_b<K>(bfw + (size_t)c0 * bfc, 0, bcur);
+    if (c0 + 1 < c1) cn = cmap(c0 + 1);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  int xbuf = 0;
+  for (int c = c0; c < c1; ++c) {
+    const int4 ci = cmap(c);
+    const int db = (c - c0) & 1;
+    const int4 cnow = cn;  // chunk c + 1
+    float s_end = 0.f;
+    f4 S[NTW][NPT];
+#pragma unroll
+    for (int t = 0; t < NTW; ++t)
+#pragma unroll
+      for (int pt = 0; pt < NPT; ++pt) S[t][pt] = zero4();
+#pragma unroll
+    for (int ph = 0; ph < NPH; ++ph) {
+      // the next phase's loads first (this chunk's next rows, or the next
+      // chunk's first rows and its dt column), so nothing issued later in the
+      // phase stands before them
+      BF bnext;
+      if (ph + 1 < NPH) {
+        walk_issue_x<K>(x, ci, ph + 1, xstride, hd, xl, smem + (xbuf ^ 1) * K::XB, wave);
+        walk_load_b<K>(bfw + (size_t)(c) * bfc, ph + 1, bnext);
+      } else if (c + 1 < c1) {
+        walk_issue_x<K>(x, cnow, 0, xstride, hd, xl, smem + (xbuf ^ 1) * K::XB, wave);
+        walk_issue_dt<K>(dt, cnow, H, hd, lds0 + K::OFF_DT + (db ^ 1) * K::DTN * 4, wave);
+        walk_load_b<K>(bfw + (size_t)(c + 1) * bfc, 0, bnext);
+        if (c + 2 < c1) cn = cmap(c + 2);
+      }
+      if (ph == 0) {
+        // the state entering chunk c, in the operand type, for the chunk scan
+        const size_t hco = ((size_t)c * H + hd) * (size_t)(N * P);
+#pragma unroll
+        for (int t = 0; t < NTW; ++t)
+#pragma unroll
+          for (int pt = 0; pt < NPT; ++pt) {
+            const size_t e = hco + (size_t)(16 * (nt0 + t) + col) * P + 16 * pt + 4 * grp;
+            st4T(hin + e, Hs[t][pt]);
+            if (hin32) st4(hin32 + e, Hs[t][pt]);  // a training forward keeps them in float32
+          }
+        // the chunk's decay, in every wave (wave 0 of part 0 writes s, dt, u)
+        s_end = walk_decay<Q>(reinterpret_cast<const float *>(smem + K::OFF_DT + db * K::DTN * 4),
+                              w_l, a2, part == 0 && wave == 0, ((size_t)c * H + hd) * Q, s_out,
+                              dt_out, u_out);
+      }
+      // S^T += sum over this phase's tokens of x_j (w_j B_j)^T
+      const char *xt = smem + xbuf * K::XB;
+#pragma unroll
+      for (int k = 0; k < KSP; ++k) {
+        const int j0 = ph * JP + 32 * k;
+        Frag<bf16> xa[NPT];
+        const char *xk = xt + 4 * k * kBlk128;
+#pragma unroll
+        for (int pt = 0; pt < NPT; ++pt)
+          xa[pt] = frag_kmaj_at(xk, xo ^ (32 * pt), (xo ^ (32 * pt)) + 2 * kBlk128);
+        const f4 w0 = ld4(w_l + j0 + 4 * grp), w1 = ld4(w_l + j0 + 16 + 4 * grp);
+        Frag<bf16> bw[NTW];
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) {
+          const f8v bv = cvt_f8(bcur[t][k]);
+          bw[t].v = cvt_bf8(f8v{bv[0] * w0[0], bv[1] * w0[1], bv[2] * w0[2], bv[3] * w0[3],
+                                bv[4] * w1[0], bv[5] * w1[1], bv[6] * w1[2], bv[7] * w1[3]});
+        }
+#pragma unroll
+        for (int pt = 0; pt < NPT; ++pt)
+#pragma unroll
+          for (int t = 0; t < NTW; ++t) mma(S[t][pt], xa[pt], bw[t]);
+      }
+      // the next phase's loads have landed and this phase's buffers are free
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+#pragma unroll
+      for (int t = 0; t < NTW; ++t)
+#pragma unroll
+        for (int k = 0; k < KSP; ++k) bcur[t][k] = bnext[t][k];
+      xbuf ^= 1;
+    }
+    // carry: H = 2^(s_end) H + S
+    const float a = __builtin_amdgcn_exp2f(fminf(s_end, 0.f));
+#pragma unroll
+    for (int t = 0; t < NTW; ++t)
+#pragma unroll
+      for (int pt = 0; pt < NPT; ++pt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) Hs[t][pt][q] = a * Hs[t][pt][q] + S[t][pt][q];
+  }
+#pragma unroll
+  for (int t = 0; t < NTW; ++t)
+#pragma unroll
+    for (int pt = 0; pt < NPT; ++pt) {
+      const size_t e = hofs + (size_t)(16 * (nt0 + t) + col) * P + 16 * pt + 4 * grp;
+      if (h_out) st4(h_out + e, Hs[t][pt]);
+      if (h_out2) st4(h_out2 + e, Hs[t][pt]);
+    }
+}
+
+// ------------------------------------------------------------------ launch
+bool walk_supported(int P, int N, int Q, bool bf16) {
+  return bf16 && P == 64 && N == 128 && Q >= 32 && Q <= 256;
+}
+
+// The walk pays when there are enough chains to fill the chip and each chain
+// is short: a chain is one workgroup streaming its sequence's chunks, so a
+// packed batch whose longest sequence is unknown on the host keeps the chunk
+// states (the variant bits force either way).
+bool walk_choice(int P, int N, int Q, bool bf16, int nseq, int H, bool packed, unsigned variant) {
+  if (!walk_supported(P, N, Q, bf16) || (variant & SSD_VARIANT_STATE_CHUNKS)) return false;
+  if (variant & SSD_VARIANT_STATE_WALK) return true;
+  return !packed && (long)nseq * H >= kWalkMinChains;
+}
+
+// Launch shape: NH workgroups per (sequence, head) chain (each owns N/NH of
+// the state's n columns) and JP rows per pipeline phase.
+#ifndef SSD_WALK_NH
+#define SSD_WALK_NH 2
+#endif
+#ifndef SSD_WALK_JP
+#define SSD_WALK_JP 128
+#endif
+
+template <int Q, int NH, int JP>
+static hipError_t run_walk(const PrefillArgs &a, const WorkspaceLayout &L, bool write_hout,
+                           hipStream_t st) {
+  typedef WalkCfg<Q, NH, JP> K;
+  const void *kern = (const void *)k_state_walk<Q, NH, JP>;
+  hipError_t e = set_lds_limit(kern);
+  if (e != hipSuccess) return e;
+  char *ws = static_cast<char *>(a.workspace);
+  const bf16 *xp = (const bf16 *)a.x;
+  const float *dtp = a.dt, *Ap = a.A;
+  const bf16 *bp = reinterpret_cast<const bf16 *>(ws + L.bfrag);
+  const int *so = reinterpret_cast<const int *>(ws + L.seq_off);
+  ChunkMap cm{reinterpret_cast<const int4 *>(ws + L.info), a.cu ? 0 : (int)(a.T / a.nseq), a.nseq,
+              a.Q};
+  int H_ = a.H, G_ = a.G, nch = a.nseq * a.H * NH;
+  const float *h0p = a.h0;
+  float *hop = write_hout ? a.h_out : nullptr, *hop2 = write_hout ? a.h_out2 : nullptr;
+  float *sp = reinterpret_cast<float *>(ws + L.s), *dp = reinterpret_cast<float *>(ws + L.dt);
+  float *up = reinterpret_cast<float *>(ws + L.u);
+  bf16 *hp = reinterpret_cast<bf16 *>(ws + L.hin);
+  float *h32 = a.hin32;
+  void *args[] = {&xp, &dtp, &Ap, &bp, &so, &cm, &H_, &G_, &nch, &h0p, &hop, &sp, &dp, &up, &hp,
+                  &h32, &hop2};
+  const unsigned grid = 8u * (unsigned)((nch + 7) / 8);
+  return hipLaunchKernel(kern, dim3(grid), dim3(64 * K::NW), args, K::LDS, st);
+}
+
+hipError_t launch_state_walk(const PrefillArgs &a, const WorkspaceLayout &L, int nc,
+                             bool write_hout, hipStream_t st) {
+  if (nc > 0) {
+    ChunkMap cm{reinterpret_cast<const int4 *>(static_cast<char *>(a.workspace) + L.info),
+                a.cu ? 0 : (int)(a.T / a.nseq), a.nseq, a.Q};
+    hipLaunchKernelGGL(k_bfrag, dim3((unsigned)nc * a.G), dim3(256), 0, st,
+                       (const bf16 *)a.B, cm, nc, a.G, a.Q,
+                       reinterpret_cast<bf16 *>(static_cast<char *>(a.workspace) + L.bfrag));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  switch (a.Q) {
+    case 32: return run_walk<32, SSD_WALK_NH, SSD_WALK_JP>(a, L, write_hout, st);
+    case 64: return run_walk<64, SSD_WALK_NH, SSD_WALK_JP>(a, L, write_hout, st);
+    case 128: return run_walk<128, SSD_WALK_NH, SSD_WALK_JP>(a, L, write_hout, st);
+    case 256: return run_walk<256, SSD_WALK_NH, SSD_WALK_JP>(a, L, write_hout, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ssd

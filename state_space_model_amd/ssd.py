@@ -17,10 +17,13 @@ SSD_F32, SSD_BF16, SSD_F16 = 0, 1, 2
 STAGE_CHUNK_CUMSUM, STAGE_CHUNK_STATE, STAGE_STATE_PASS, STAGE_CHUNK_SCAN = 1, 2, 4, 8
 STAGE_ALL = 15
 VARIANT_SCAN_ROWS, VARIANT_SCAN_HEADS = 0x100, 0x200
+VARIANT_STATE_CHUNKS, VARIANT_STATE_WALK = 0x400, 0x800
 SCAN_VARIANTS = {"auto": 0, "rows": VARIANT_SCAN_ROWS, "heads": VARIANT_SCAN_HEADS}
+STATE_VARIANTS = {"auto": 0, "chunks": VARIANT_STATE_CHUNKS, "walk": VARIANT_STATE_WALK}
 ERRORS = {0: "SSD_OK", -1: "SSD_ERR_INVALID_ARG", -2: "SSD_ERR_UNSUPPORTED",
           -3: "SSD_ERR_WORKSPACE", -4: "SSD_ERR_HIP"}
-EXPORTS = ("ssd_scan_prefill_workspace", "ssd_scan_prefill", "ssd_scan_prefill_stages",
+EXPORTS = ("ssd_scan_prefill_workspace", "ssd_scan_prefill_plan", "ssd_scan_prefill",
+           "ssd_scan_prefill_stages",
            "ssd_step", "ssd_step_multi", "ssd_conv1d_step", "ssd_gated_rmsnorm",
            "ssd_decode_layer_step", "ssd_selective_scan_workspace", "ssd_selective_scan",
            "ssd_scan_prefill_backward_workspace", "ssd_scan_prefill_backward",
@@ -49,6 +52,8 @@ def load(path=LIB_PATH):
                              ctypes.c_uint)
     lib.ssd_scan_prefill_workspace.argtypes = [i64, i32, i32, i32, i32, i32, i32, i32]
     lib.ssd_scan_prefill_workspace.restype = sz
+    lib.ssd_scan_prefill_plan.argtypes = [i64, i32, i32, i32, i32, i32, i32, i32, i32]
+    lib.ssd_scan_prefill_plan.restype = u32
     pre = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, i32, i32, vp, sz,
            vp]
     lib.ssd_scan_prefill.argtypes = pre
@@ -143,6 +148,18 @@ def workspace_bytes(total_tokens, nseq, H, P, N, G, chunk, dtype=torch.bfloat16)
     return int(load().ssd_scan_prefill_workspace(total_tokens, nseq, H, P, N, G, chunk, code))
 
 
+def plan(total_tokens, nseq, H, P, N, G, chunk, dtype=torch.bfloat16, packed=False):
+    """The kernels a prefill of these shapes runs: {"state": "chunks"|"walk",
+    "scan": "rows"|"heads"}, or None for shapes the library refuses."""
+    code = SSD_BF16 if dtype == torch.bfloat16 else SSD_F32
+    v = int(load().ssd_scan_prefill_plan(total_tokens, nseq, H, P, N, G, chunk, code,
+                                         int(bool(packed))))
+    if v == 0:
+        return None
+    return {"state": "walk" if v & VARIANT_STATE_WALK else "chunks",
+            "scan": "heads" if v & VARIANT_SCAN_HEADS else "rows"}
+
+
 def alloc_workspace(total_tokens, nseq, H, P, N, G, chunk, dtype, device):
     n = workspace_bytes(total_tokens, nseq, H, P, N, G, chunk, dtype)
     if n == 0:
@@ -151,14 +168,16 @@ def alloc_workspace(total_tokens, nseq, H, P, N, G, chunk, dtype, device):
 
 
 def prefill(x, dt, A, B, C, D, h0=None, chunk=256, cu_seqlens=None, *, nseq=None, y=None,
-            h_out=None, workspace=None, stages=STAGE_ALL, scan="auto", prepare=False):
+            h_out=None, workspace=None, stages=STAGE_ALL, scan="auto", state="auto",
+            prepare=False):
     """Chunked SSD prefill.
 
     x [T,H,P] (or [b,L,H,P]), dt [T,H], A [H], B/C [T,G,N], D [H], h0
     [nseq,H,N,P] float32 or None, cu_seqlens int32 [nseq+1] or None (dense
     batch: ``nseq`` sequences of T/nseq tokens; a 4-d x gives nseq = b).
     ``scan``: "auto" (the library's choice), "rows" or "heads" forces the
-    chunk-scan kernel (SSD_VARIANT_SCAN_*).
+    chunk-scan kernel (SSD_VARIANT_SCAN_*); ``state``: "auto", "chunks" or
+    "walk" forces how the states are formed (SSD_VARIANT_STATE_*).
     Returns (y [T,H,P] float32, h_out [nseq,H,N,P] float32); with
     ``prepare=True`` nothing runs and (Prepared, y, h_out) is returned.
     """
@@ -205,7 +224,9 @@ def prefill(x, dt, A, B, C, D, h0=None, chunk=256, cu_seqlens=None, *, nseq=None
     _need(workspace, "workspace", torch.uint8, dev)
     if scan not in SCAN_VARIANTS:
         raise ValueError(f"scan must be one of {sorted(SCAN_VARIANTS)} (got {scan!r})")
-    stages = stages | SCAN_VARIANTS[scan]
+    if state not in STATE_VARIANTS:
+        raise ValueError(f"state must be one of {sorted(STATE_VARIANTS)} (got {state!r})")
+    stages = stages | SCAN_VARIANTS[scan] | STATE_VARIANTS[state]
     lib = load()
     args = (_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(y),
             _ptr(h_out), _ptr(cu_seqlens), nseq, T, H, P, N, G, chunk, code, _ptr(workspace),

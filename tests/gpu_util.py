@@ -8,9 +8,13 @@ import numpy as np
 TOL = {"f32": 1e-4, "bf16": 2e-2}   # max-abs on every compared element of y and h_out
 
 
+RECORD = []   # error figures of this session, printed in pytest's terminal summary
+
+
 def log(msg):
     print(msg, flush=True)
     sys.stdout.flush()
+    RECORD.append(msg)
 
 
 def dev_inputs(d, dtype):

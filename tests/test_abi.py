@@ -39,10 +39,12 @@ def test_workspace_size():
     # bf16, P 64, N 128, chunk 256: the row-split scan's C.B^T fragments per
     # (chunk, group), 1 KB per (16-row tile, 32-row block)
     cbg = nc * 1 * (256 // 16) * (256 // 32) * 1024
-    assert expect_min + cbg <= n1 <= expect_min + cbg + 8192
-    # the C.B^T region grows with the group count, not the head count
+    # and B of every (chunk, group) in MFMA fragment order for the state walk
+    bfrag = nc * 1 * 256 * 128 * 2
+    assert expect_min + cbg + bfrag <= n1 <= expect_min + cbg + bfrag + 8192
+    # the C.B^T and B-fragment regions grow with the group count, not the head count
     n8 = w(4096, 1, 24, 64, 128, 8, 256, 1)
-    assert n8 - n1 == 7 * cbg
+    assert n8 - n1 == 7 * (cbg + bfrag)
     n32 = w(4096, 1, 24, 64, 128, 1, 256, 0)             # float32: H_in in float32, no C.B^T
     expect32 = nc * 24 * 128 * 64 * (4 + 4) + 3 * nc * 24 * 256 * 4
     assert expect32 <= n32 <= expect32 + 8192
@@ -76,7 +78,30 @@ def test_cbg_region_sized_by_groups():
                                                   4 * nc * H * N * P, e * nc * H * N * P))
         got = w(T, nseq, H, P, N, G, Q, 1 if dt == "bf16" else 0)
         has = dt == "bf16" and P == 64 and N == 128 and Q <= 256
-        assert got == base + (-(-region // 256) * 256 if has else 0), (T, nseq, H, P, N, G, Q, dt)
+        walk = dt == "bf16" and P == 64 and N == 128 and Q <= 256
+        bfrag = nc * G * Q * N * 2
+        assert got == base + (-(-region // 256) * 256 if has else 0) + \
+            (-(-bfrag // 256) * 256 if walk else 0), (T, nseq, H, P, N, G, Q, dt)
+
+
+def test_plan_query():
+    """The planning query names the kernels a call runs: the state walk for a
+    dense batch of at least 128 (sequence, head) chains (bf16, P 64, N 128,
+    chunk <= 256), the heads-streamed scan from 2048 (chunk, head) units."""
+    plan = ssd.plan
+    assert plan(32768, 4, 80, 64, 128, 1, 256) == {"state": "walk", "scan": "heads"}
+    assert plan(4096, 1, 24, 64, 128, 1, 256) == {"state": "chunks", "scan": "rows"}
+    assert plan(32768, 4, 80, 64, 128, 1, 256, torch_f32()) == {"state": "chunks",
+                                                                 "scan": "rows"}
+    assert plan(32768, 4, 80, 64, 128, 1, 512) == {"state": "chunks", "scan": "rows"}
+    assert plan(85952, 8, 80, 64, 128, 1, 64, packed=True) == {"state": "chunks",
+                                                                "scan": "heads"}
+    assert plan(4096, 1, 24, 64, 100, 1, 256) is None
+
+
+def torch_f32():
+    import torch
+    return torch.float32
 
 
 def _prefill_rc(**kw):
@@ -113,8 +138,8 @@ def test_prefill_rejects_before_launch(kw, code, frag):
     assert rc == code and frag in msg, (rc, msg)
 
 
-@pytest.mark.parametrize("stages,frag", [(16, "stage"), (0x400, "stage"),
-                                          (0x30f, "exclusive")])
+@pytest.mark.parametrize("stages,frag", [(16, "stage"), (0x1000, "stage"),
+                                          (0x30f, "exclusive"), (0xc0f, "exclusive")])
 def test_stage_mask_rejected(stages, frag):
     lib = ssd.load()
     rc = lib.ssd_scan_prefill_stages(stages, *([ctypes.c_void_p(1)] * 10), 1, 64, 4, 16, 16, 1,
@@ -127,6 +152,8 @@ def test_variant_bits_match_the_header():
     vals = {k: int(v, 16) for k, v in re.findall(r"(SSD_VARIANT_\w+)\s*=\s*(0x[0-9a-fA-F]+)u", src)}
     assert vals["SSD_VARIANT_SCAN_ROWS"] == ssd.VARIANT_SCAN_ROWS
     assert vals["SSD_VARIANT_SCAN_HEADS"] == ssd.VARIANT_SCAN_HEADS
+    assert vals["SSD_VARIANT_STATE_CHUNKS"] == ssd.VARIANT_STATE_CHUNKS
+    assert vals["SSD_VARIANT_STATE_WALK"] == ssd.VARIANT_STATE_WALK
 
 
 @pytest.mark.parametrize("kw,code,frag", [

@@ -16,15 +16,16 @@ from state_space_model_amd import inputs
 pytestmark = pytest.mark.gpu
 
 SCANS = ("auto", "rows", "heads")
+STATES = ("chunks", "walk")   # how the chunk states are formed and carried
 
 
-def _gpu(d, dtype, chunk, with_h0=True, scan="auto", **kw):
+def _gpu(d, dtype, chunk, with_h0=True, scan="auto", state="auto", **kw):
     import torch
     from state_space_model_amd import ssd
     t = dev_inputs(d, dtype)
     y, ho = ssd.prefill(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"],
                         t["h0"] if with_h0 else None, chunk=chunk,
-                        cu_seqlens=t["cu_seqlens"], scan=scan, **kw)
+                        cu_seqlens=t["cu_seqlens"], scan=scan, state=state, **kw)
     torch.cuda.synchronize()
     out = y.cpu().numpy(), ho.cpu().numpy()
     del y, ho, t
@@ -62,21 +63,24 @@ SMALL = [  # (lengths, H, P, N, G, chunk, h0)
 ]
 
 
-MODES = [("f32", "auto"), ("bf16", "rows"), ("bf16", "heads")]
+MODES = [("f32", "auto", "auto"), ("bf16", "rows", "chunks"), ("bf16", "heads", "chunks"),
+         ("bf16", "rows", "walk"), ("bf16", "heads", "walk")]
 
 
-@pytest.mark.parametrize("dtype,scan", MODES)
+@pytest.mark.parametrize("dtype,scan,state", MODES)
 @pytest.mark.parametrize("case", range(len(SMALL)))
-def test_prefill_small(dtype, scan, case):
+def test_prefill_small(dtype, scan, state, case):
     """Every small shape in float32, and in bfloat16 through both chunk-scan
-    kernels (row-split, and heads streamed where a shape has that kernel)."""
+    kernels (row-split, and heads streamed where a shape has that kernel) and
+    both ways of forming the states (chunk states, and the walk where a shape
+    has it)."""
     lengths, H, P, N, G, chunk, h0 = SMALL[case]
-    log(f"prefill small dtype={dtype} scan={scan} lengths={lengths} H={H} P={P} N={N} G={G}"
-        f" Q={chunk}")
+    log(f"prefill small dtype={dtype} scan={scan} state={state} lengths={lengths} H={H} P={P}"
+        f" N={N} G={G} Q={chunk}")
     d = inputs.prefill_inputs(H, P, N, G, lengths, 200 + case, dtype=dtype, h0=h0)
-    y, ho = _gpu(d, dtype, chunk, scan=scan)
+    y, ho = _gpu(d, dtype, chunk, scan=scan, state=state)
     ry, rh = _ref(d)
-    _check(f"{dtype} {scan}", y, ho, ry, rh, TOL[dtype])
+    _check(f"{dtype} {scan} {state}", y, ho, ry, rh, TOL[dtype])
 
 
 def test_prefill_heads_streamed_several_heads_per_workgroup():
@@ -91,11 +95,12 @@ def test_prefill_heads_streamed_several_heads_per_workgroup():
     d = inputs.prefill_inputs(H, P, N, G, lengths, 4242, dtype="bf16", h0=True)
     ry, rh = _ref(d)
     ssm = ssm_scale(ry, d["x"], d["D"])
-    y, ho = _gpu(d, "bf16", chunk, scan="heads")
-    _check("heads", y, ho, ry, rh, TOL["bf16"], ssm)
-    y2, ho2 = _gpu(d, "bf16", chunk, scan="rows")
-    _check("rows", y2, ho2, ry, rh, TOL["bf16"], ssm)
-    assert maxabs(ho, ho2) == 0.0  # the state path is the same kernels in both
+    for state in STATES:
+        y, ho = _gpu(d, "bf16", chunk, scan="heads", state=state)
+        _check(f"heads {state}", y, ho, ry, rh, TOL["bf16"], ssm)
+        y2, ho2 = _gpu(d, "bf16", chunk, scan="rows", state=state)
+        _check(f"rows {state}", y2, ho2, ry, rh, TOL["bf16"], ssm)
+        assert maxabs(ho, ho2) == 0.0  # the state path is the same kernels in both
 
 
 def test_prefill_tiny_workload_f32():
@@ -107,10 +112,10 @@ def test_prefill_tiny_workload_f32():
     _check("f32", y, ho, ry, rh, TOL["f32"])
 
 
-def _workload_all_elements(k, scans, d_zero=False):
+def _workload_all_elements(k, scans, d_zero=False, states=STATES):
     """Workload k: one full oracle run, every element of y and h_out compared
-    for each chunk-scan kernel; with d_zero the skip term is removed (D = 0),
-    so y is the state-space part alone."""
+    for each chunk-scan kernel and each way of forming the states; with d_zero
+    the skip term is removed (D = 0), so y is the state-space part alone."""
     w = inputs.WORKLOADS[k]
     d = inputs.workload_inputs(k)
     ry, rh = _ref(d)
@@ -121,10 +126,12 @@ def _workload_all_elements(k, scans, d_zero=False):
         d = dict(d, D=np.zeros_like(d["D"]))
     ssm = ssm_scale(ry, d["x"], d["D"])
     log(f"  oracle done: max|y_ssm|={ssm:.3g}")
-    for scan in scans:
-        y, ho = _gpu(d, "bf16", w.chunk, scan=scan)
-        _check(f"scan={scan}{' D=0' if d_zero else ''}", y, ho, ry, rh, TOL["bf16"], ssm)
-        del y, ho
+    for state in states:
+        for scan in scans:
+            y, ho = _gpu(d, "bf16", w.chunk, scan=scan, state=state)
+            _check(f"scan={scan} state={state}{' D=0' if d_zero else ''}", y, ho, ry, rh,
+                   TOL["bf16"], ssm)
+            del y, ho
 
 
 def test_prefill_130m_layer_workload():
@@ -146,7 +153,7 @@ def test_prefill_2p7b_layer_workload():
 
 def test_prefill_2p7b_layer_workload_no_skip():
     log("prefill workload 2 with D = 0 (y is the state-space part alone)")
-    _workload_all_elements(2, ("auto",), d_zero=True)
+    _workload_all_elements(2, ("auto",), d_zero=True, states=("auto",))
 
 
 def test_prefill_long_context_varlen_chunk_sweep():
@@ -159,11 +166,12 @@ def test_prefill_long_context_varlen_chunk_sweep():
     ry, rh = _ref(d)
     ssm = ssm_scale(ry, d["x"], d["D"])
     log(f"  oracle done: max|y_ssm|={ssm:.3g}")
-    for scan in ("auto", "rows"):
-        for q in w.chunks:
-            y, ho = _gpu(d, "bf16", q, scan=scan)
-            _check(f"scan={scan} Q={q}", y, ho, ry, rh, TOL["bf16"], ssm)
-            del y, ho
+    for state in STATES:
+        for scan in ("auto", "rows"):
+            for q in w.chunks:
+                y, ho = _gpu(d, "bf16", q, scan=scan, state=state)
+                _check(f"scan={scan} state={state} Q={q}", y, ho, ry, rh, TOL["bf16"], ssm)
+                del y, ho
 
 
 # ---- the method's closed forms and degenerate cases, through the kernels, at
@@ -173,46 +181,46 @@ def _layer_inputs(seed, dtype, h0=True):
     return inputs.prefill_inputs(24, 64, 128, 1, [4096], seed, dtype=dtype, h0=h0)
 
 
-@pytest.mark.parametrize("dtype,scan", MODES)
-def test_prefill_no_decay_is_a_prefix_sum(dtype, scan):
+@pytest.mark.parametrize("dtype,scan,state", MODES)
+def test_prefill_no_decay_is_a_prefix_sum(dtype, scan, state):
     """A = 0: no decay, the state is h0 plus the running sum of dt x (x) B.
     float32 within 1e-4 of the output's scale, bfloat16 within 2e-2."""
     d = _layer_inputs(61, dtype)
     d["A"] = np.zeros_like(d["A"])
-    log(f"prefill A=0 dtype={dtype} scan={scan}")
+    log(f"prefill A=0 dtype={dtype} scan={scan} state={state}")
     ry, rh = _ref(d)
     scale = max(1.0, float(np.max(np.abs(ry))), float(np.max(np.abs(rh))))
-    y, ho = _gpu(d, dtype, 256, scan=scan)
-    _check(f"A=0 {dtype} {scan} (scale {scale:.3g})", y, ho, ry, rh, TOL[dtype] * scale)
+    y, ho = _gpu(d, dtype, 256, scan=scan, state=state)
+    _check(f"A=0 {dtype} {scan} {state} (scale {scale:.3g})", y, ho, ry, rh, TOL[dtype] * scale)
 
 
-@pytest.mark.parametrize("dtype,scan", MODES)
-def test_prefill_zero_step_keeps_the_state(dtype, scan):
+@pytest.mark.parametrize("dtype,scan,state", MODES)
+def test_prefill_zero_step_keeps_the_state(dtype, scan, state):
     """dt = 0: nothing enters and nothing decays, so h_out equals h0 bit for
     bit and y = C h0 + D x."""
     d = _layer_inputs(62, dtype)
     d["dt"] = np.zeros_like(d["dt"])
-    log(f"prefill dt=0 dtype={dtype} scan={scan}")
+    log(f"prefill dt=0 dtype={dtype} scan={scan} state={state}")
     ry, rh = _ref(d)
-    y, ho = _gpu(d, dtype, 256, scan=scan)
+    y, ho = _gpu(d, dtype, 256, scan=scan, state=state)
     assert np.array_equal(ho, d["h0"]), "h_out differs from h0 with dt = 0"
     ssm = ssm_scale(ry, d["x"], d["D"]) if dtype == "bf16" else None
-    _check(f"dt=0 {dtype} {scan}", y, ho, ry, rh, TOL[dtype], ssm)
+    _check(f"dt=0 {dtype} {scan} {state}", y, ho, ry, rh, TOL[dtype], ssm)
 
 
-@pytest.mark.parametrize("dtype,scan", MODES)
-def test_prefill_strong_decay(dtype, scan):
+@pytest.mark.parametrize("dtype,scan,state", MODES)
+def test_prefill_strong_decay(dtype, scan, state):
     """A = -16 with dt in [0.5, 1]: every step decays the state by 1e-7 to
     3e-4 and a chunk's decay underflows to zero (the fully decayed regime)."""
     d = _layer_inputs(63, dtype)
     rng = np.random.Generator(np.random.PCG64(64))
     d["A"] = np.full_like(d["A"], -16.0)
     d["dt"] = rng.uniform(0.5, 1.0, size=d["dt"].shape).astype(np.float32)
-    log(f"prefill strong decay dtype={dtype} scan={scan}")
+    log(f"prefill strong decay dtype={dtype} scan={scan} state={state}")
     ry, rh = _ref(d)
-    y, ho = _gpu(d, dtype, 256, scan=scan)
+    y, ho = _gpu(d, dtype, 256, scan=scan, state=state)
     ssm = ssm_scale(ry, d["x"], d["D"]) if dtype == "bf16" else None
-    _check(f"strong decay {dtype} {scan}", y, ho, ry, rh, TOL[dtype], ssm)
+    _check(f"strong decay {dtype} {scan} {state}", y, ho, ry, rh, TOL[dtype], ssm)
 
 
 def test_stages_separately_equal_one_call():
@@ -222,19 +230,27 @@ def test_stages_separately_equal_one_call():
     t = dev_inputs(d, "bf16")
     args = (t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["h0"])
     for scan in SCANS:
-        y1, h1 = ssd.prefill(*args, chunk=128, cu_seqlens=t["cu_seqlens"], scan=scan)
-        ws = ssd.alloc_workspace(1000, 2, 4, 64, 128, 1, 128, torch.bfloat16, "cuda")
-        y2 = torch.empty_like(y1)
-        h2 = torch.empty_like(h1)
-        for st in (1, 2, 4, 8):
-            ssd.prefill(*args, chunk=128, cu_seqlens=t["cu_seqlens"], y=y2, h_out=h2,
-                        workspace=ws, stages=st, scan=scan)
-        torch.cuda.synchronize()
-        assert torch.equal(y1, y2) and torch.equal(h1, h2), scan
+        for state in STATES:
+            kw = dict(chunk=128, cu_seqlens=t["cu_seqlens"], scan=scan, state=state)
+            y1, h1 = ssd.prefill(*args, **kw)
+            ws = ssd.alloc_workspace(1000, 2, 4, 64, 128, 1, 128, torch.bfloat16, "cuda")
+            y2 = torch.empty_like(y1)
+            h2 = torch.empty_like(h1)
+            for st in (1, 2, 4, 8):
+                ssd.prefill(*args, y=y2, h_out=h2, workspace=ws, stages=st, **kw)
+            torch.cuda.synchronize()
+            assert torch.equal(y1, y2) and torch.equal(h1, h2), (scan, state)
+            # h_out may be the h0 buffer itself, also with the stages run one by one
+            hbuf = t["h0"].clone()
+            for st in (1, 2, 4, 8):
+                ssd.prefill(*args[:6], hbuf, y=y2, h_out=hbuf, workspace=ws, stages=st, **kw)
+            torch.cuda.synchronize()
+            assert torch.equal(y1, y2) and torch.equal(h1, hbuf), (scan, state)
 
 
+@pytest.mark.parametrize("state", STATES)
 @pytest.mark.parametrize("scan", ["rows", "heads"])
-def test_deterministic_and_varlen_equals_solo(scan):
+def test_deterministic_and_varlen_equals_solo(scan, state):
     """Run-to-run bitwise determinism; a packed batch equals each sequence run
     alone, bitwise; h_out may be the h0 buffer itself."""
     import torch
@@ -243,7 +259,7 @@ def test_deterministic_and_varlen_equals_solo(scan):
     d = inputs.prefill_inputs(4, 64, 128, 2, lengths, 9, dtype="bf16", h0=True)
     t = dev_inputs(d, "bf16")
     run = lambda: ssd.prefill(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["h0"],
-                              chunk=256, cu_seqlens=t["cu_seqlens"], scan=scan)
+                              chunk=256, cu_seqlens=t["cu_seqlens"], scan=scan, state=state)
     y1, h1 = run()
     y2, h2 = run()
     assert torch.equal(y1, y2) and torch.equal(h1, h2)
@@ -251,11 +267,11 @@ def test_deterministic_and_varlen_equals_solo(scan):
     for s in range(len(lengths)):
         sl = slice(int(cu[s]), int(cu[s + 1]))
         ys, hs = ssd.prefill(t["x"][sl], t["dt"][sl], t["A"], t["B"][sl], t["C"][sl], t["D"],
-                             t["h0"][s:s + 1].contiguous(), chunk=256, scan=scan)
+                             t["h0"][s:s + 1].contiguous(), chunk=256, scan=scan, state=state)
         assert torch.equal(ys, y1[sl]) and torch.equal(hs[0], h1[s])
     hbuf = t["h0"].clone()
     y3, _ = ssd.prefill(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], hbuf, chunk=256,
-                        cu_seqlens=t["cu_seqlens"], h_out=hbuf, scan=scan)
+                        cu_seqlens=t["cu_seqlens"], h_out=hbuf, scan=scan, state=state)
     torch.cuda.synchronize()
     assert torch.equal(y3, y1) and torch.equal(hbuf, h1)
 
