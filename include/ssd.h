@@ -143,6 +143,28 @@ int ssd_scan_prefill(const void *x, const float *dt, const float *A, const void 
                      size_t workspace_bytes, void *stream);
 
 /*
+ * ssd_scan_prefill() without a workspace argument, for callers that cannot
+ * allocate device memory (code under stream capture, serving loops, harnesses
+ * that forbid hipMalloc): the workspace is a device array inside the library,
+ * SSD_NOALLOC_SCRATCH_BYTES bytes per device, held from library load until
+ * the process ends.  Arguments, results and errors as ssd_scan_prefill(), with
+ * every stage and the library's kernel choice; shapes whose
+ * ssd_scan_prefill_workspace() exceeds SSD_NOALLOC_SCRATCH_BYTES are refused
+ * with SSD_ERR_WORKSPACE before anything touches the device.  Nothing is
+ * allocated: the first call on a device only looks up the array's address.
+ * Every call on one device shares that device's array and leaves its contents
+ * behind (no stage reads what an earlier call left there): calls that overlap
+ * on one device -- on different streams, or from different threads -- race,
+ * so serialise them.
+ */
+#define SSD_NOALLOC_SCRATCH_BYTES (32u << 20)
+int ssd_scan_prefill_noalloc(const void *x, const float *dt, const float *A, const void *B,
+                             const void *C, const float *D, const float *h0, float *y,
+                             float *h_out, const int32_t *cu_seqlens, int nseq,
+                             int64_t total_tokens, int H, int P, int N, int G, int chunk,
+                             ssd_dtype_t dtype, void *stream);
+
+/*
  * The same computation as ssd_scan_prefill(), running only the stages in the
  * bitmask `stages` (SSD_STAGE_*, optionally with SSD_VARIANT_* bits).  Stages
  * communicate through the workspace, so running CHUNK_CUMSUM, CHUNK_STATE,

@@ -9,6 +9,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
 #include <new>
 
 #include "ssd.h"
@@ -81,6 +83,42 @@ int prefill_impl(unsigned stages, const void *x, const float *dt, const float *A
   return SSD_OK;
 }
 
+// Scratch of ssd_scan_prefill_noalloc(): the prefill workspace in a
+// file-scope device array instead of caller memory, for callers that cannot
+// allocate.  Each device holds its own copy from library load until the
+// process ends.  Host code never passes the array's name to a kernel (on the
+// host it is only a stand-in for the symbol): its device address is looked up
+// once per device with hipGetSymbolAddress and kept in g_scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[SSD_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's scratch address in *out; SSD_OK or an error code.
+int scratch_ptr(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SSD_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SSD_ERR_UNSUPPORTED, "device %d beyond the %d the scratch table holds", dev,
+                kMaxDevices);
+  void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !p)
+        return fail(SSD_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                    hipGetErrorString(e));
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return SSD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -112,6 +150,31 @@ int ssd_scan_prefill(const void *x, const float *dt, const float *A, const void 
                      void *stream) {
   return prefill_impl(SSD_STAGE_ALL, x, dt, A, B, C, D, h0, y, h_out, cu_seqlens, nseq,
                       total_tokens, H, P, N, G, chunk, dtype, workspace, workspace_bytes, stream);
+}
+
+int ssd_scan_prefill_noalloc(const void *x, const float *dt, const float *A, const void *B,
+                             const void *C, const float *D, const float *h0, float *y,
+                             float *h_out, const int32_t *cu_seqlens, int nseq,
+                             int64_t total_tokens, int H, int P, int N, int G, int chunk,
+                             ssd_dtype_t dtype, void *stream) {
+  g_err[0] = 0;
+  int rc = check_prefill(x, dt, A, B, C, D, y, nseq, total_tokens, H, P, N, G, chunk, dtype,
+                         cu_seqlens);
+  if (rc) return rc;
+  // the limit is checked before anything touches the device
+  const size_t need =
+      ssd::prefill_layout(total_tokens, nseq, H, P, N, G, chunk, dtype == SSD_BF16 ? 2 : 4).total;
+  if (need > (size_t)SSD_NOALLOC_SCRATCH_BYTES)
+    return fail(SSD_ERR_WORKSPACE,
+                "these shapes need %zu bytes of workspace; the built-in scratch holds %zu "
+                "(pass a workspace to ssd_scan_prefill instead)",
+                need, (size_t)SSD_NOALLOC_SCRATCH_BYTES);
+  void *ws = nullptr;
+  rc = scratch_ptr(&ws);
+  if (rc) return rc;
+  return prefill_impl(SSD_STAGE_ALL, x, dt, A, B, C, D, h0, y, h_out, cu_seqlens, nseq,
+                      total_tokens, H, P, N, G, chunk, dtype, ws, SSD_NOALLOC_SCRATCH_BYTES,
+                      stream);
 }
 
 int ssd_scan_prefill_stages(unsigned stages, const void *x, const float *dt, const float *A,

@@ -18,12 +18,13 @@ STAGE_CHUNK_CUMSUM, STAGE_CHUNK_STATE, STAGE_STATE_PASS, STAGE_CHUNK_SCAN = 1, 2
 STAGE_ALL = 15
 VARIANT_SCAN_ROWS, VARIANT_SCAN_HEADS = 0x100, 0x200
 VARIANT_STATE_CHUNKS, VARIANT_STATE_WALK = 0x400, 0x800
+NOALLOC_SCRATCH_BYTES = 32 << 20   # SSD_NOALLOC_SCRATCH_BYTES in ssd.h
 SCAN_VARIANTS = {"auto": 0, "rows": VARIANT_SCAN_ROWS, "heads": VARIANT_SCAN_HEADS}
 STATE_VARIANTS = {"auto": 0, "chunks": VARIANT_STATE_CHUNKS, "walk": VARIANT_STATE_WALK}
 ERRORS = {0: "SSD_OK", -1: "SSD_ERR_INVALID_ARG", -2: "SSD_ERR_UNSUPPORTED",
           -3: "SSD_ERR_WORKSPACE", -4: "SSD_ERR_HIP"}
 EXPORTS = ("ssd_scan_prefill_workspace", "ssd_scan_prefill_plan", "ssd_scan_prefill",
-           "ssd_scan_prefill_stages",
+           "ssd_scan_prefill_stages", "ssd_scan_prefill_noalloc",
            "ssd_step", "ssd_step_multi", "ssd_conv1d_step", "ssd_gated_rmsnorm",
            "ssd_decode_layer_step", "ssd_selective_scan_workspace", "ssd_selective_scan",
            "ssd_scan_prefill_backward_workspace", "ssd_scan_prefill_backward",
@@ -60,6 +61,8 @@ def load(path=LIB_PATH):
     lib.ssd_scan_prefill.restype = i32
     lib.ssd_scan_prefill_stages.argtypes = [u32] + pre
     lib.ssd_scan_prefill_stages.restype = i32
+    lib.ssd_scan_prefill_noalloc.argtypes = pre[:-3] + [vp]
+    lib.ssd_scan_prefill_noalloc.restype = i32
     lib.ssd_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
     lib.ssd_step.restype = i32
     lib.ssd_step_multi.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
@@ -169,7 +172,7 @@ def alloc_workspace(total_tokens, nseq, H, P, N, G, chunk, dtype, device):
 
 def prefill(x, dt, A, B, C, D, h0=None, chunk=256, cu_seqlens=None, *, nseq=None, y=None,
             h_out=None, workspace=None, stages=STAGE_ALL, scan="auto", state="auto",
-            prepare=False):
+            prepare=False, noalloc=False):
     """Chunked SSD prefill.
 
     x [T,H,P] (or [b,L,H,P]), dt [T,H], A [H], B/C [T,G,N], D [H], h0
@@ -180,6 +183,9 @@ def prefill(x, dt, A, B, C, D, h0=None, chunk=256, cu_seqlens=None, *, nseq=None
     "walk" forces how the states are formed (SSD_VARIANT_STATE_*).
     Returns (y [T,H,P] float32, h_out [nseq,H,N,P] float32); with
     ``prepare=True`` nothing runs and (Prepared, y, h_out) is returned.
+    ``noalloc=True`` calls ssd_scan_prefill_noalloc: the library's built-in
+    scratch replaces the workspace (every stage, the library's kernel choice;
+    shapes whose workspace exceeds NOALLOC_SCRATCH_BYTES are refused).
     """
     dense4 = x.dim() == 4
     if dense4:
@@ -219,6 +225,20 @@ def prefill(x, dt, A, B, C, D, h0=None, chunk=256, cu_seqlens=None, *, nseq=None
     _need(h_out, "h_out", torch.float32, dev)
     _shape(y, "y", (T, H, P))
     _shape(h_out, "h_out", (nseq, H, N, P))
+    if noalloc:
+        if workspace is not None or stages != STAGE_ALL or scan != "auto" or state != "auto":
+            raise ValueError("noalloc runs every stage with the library's kernel choice and "
+                             "its own scratch (no workspace, stages, scan or state)")
+        lib = load()
+        args = (_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(y),
+                _ptr(h_out), _ptr(cu_seqlens), nseq, T, H, P, N, G, chunk, code)
+        if prepare:
+            keep = (x, dt, A, B, C, D, h0, y, h_out, cu_seqlens)
+            return Prepared(lib.ssd_scan_prefill_noalloc, args, None, keep), y, h_out
+        _check(lib.ssd_scan_prefill_noalloc(*args, _stream()))
+        if dense4:
+            y = y.reshape(nseq, T // nseq, H, P)
+        return y, h_out
     if workspace is None:
         workspace = alloc_workspace(T, nseq, H, P, N, G, chunk, x.dtype, dev)
     _need(workspace, "workspace", torch.uint8, dev)

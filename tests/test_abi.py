@@ -117,6 +117,33 @@ def _prefill_rc(**kw):
     return rc, lib.ssd_last_error().decode()
 
 
+def test_noalloc_limit_matches_the_header():
+    m = re.search(r"#define\s+SSD_NOALLOC_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)",
+                  open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == ssd.NOALLOC_SCRATCH_BYTES
+
+
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(T=32768, nseq=4, H=80, P=64, N=128, chunk=256, dtype=1), -3, "scratch holds"),
+    (dict(H=6, G=4), -1, "H % G"),
+    (dict(chunk=16), -2, "use chunk 32"),
+    (dict(x=None), -1, "null"),
+])
+def test_noalloc_rejects_before_touching_the_device(kw, code, frag):
+    """The built-in-scratch prefill checks shapes and its size limit on the
+    host, before the scratch address is looked up."""
+    lib = ssd.load()
+    a = dict(x=1, dt=1, A=1, B=1, C=1, D=1, y=1, nseq=1, T=64, H=4, P=16, N=16, G=1, chunk=64,
+             dtype=0)
+    a.update(kw)
+    p = lambda v: None if v is None else ctypes.c_void_p(v)
+    rc = lib.ssd_scan_prefill_noalloc(p(a["x"]), p(a["dt"]), p(a["A"]), p(a["B"]), p(a["C"]),
+                                      p(a["D"]), None, p(a["y"]), None, None, a["nseq"], a["T"],
+                                      a["H"], a["P"], a["N"], a["G"], a["chunk"], a["dtype"], None)
+    msg = lib.ssd_last_error().decode()
+    assert rc == code and frag in msg, (rc, msg)
+
+
 @pytest.mark.parametrize("kw,code,frag", [
     (dict(H=6, G=4), -1, "H % G"),
     (dict(P=24), -2, "headdim"),
