@@ -813,6 +813,16 @@ def _kernel_key(name):
     return None
 
 
+def _template_args(name):
+    """The integer template arguments of a kernel name, mangled (Li256E) or
+    demangled (<64, 128, 256>), as a short suffix such as <64,128,256>."""
+    import re
+    vals = re.findall(r"Li(\d+)E", name)
+    if not vals and "<" in name:
+        vals = re.findall(r"\b(\d+)\b", name.split("<", 1)[1].split(">", 1)[0])
+    return "<" + ",".join(vals) + ">" if vals else ""
+
+
 def profile_commands():
     cmds = {}
     for sec, (_, a) in PROFILED.items():
@@ -884,8 +894,9 @@ def summarize(directory):
                     continue
                 b = float(np.mean(vs)) * 1024 * fac
                 traffic.setdefault(wl, {}).setdefault(k, {})[counter.lower()] = round(b)
-                lines.append(f"{k:18s} {counter:10s} {np.mean(vs):14.1f} KiB/dispatch x {fac:.4f}"
-                             f" = {b / 1e6:10.3f} MB ({len(vs)} dispatches)")
+                lab = k + _template_args(kname)
+                lines.append(f"{lab:30s} {counter:10s} {np.mean(vs):14.1f} KiB/dispatch x "
+                             f"{fac:.4f} = {b / 1e6:10.3f} MB ({len(vs)} dispatches)")
         for k, v in traffic.get(wl, {}).items():
             if "fetch_size" in v and "write_size" in v:
                 v["bytes"] = v["fetch_size"] + v["write_size"]
@@ -905,7 +916,7 @@ def summarize(directory):
                 if k is None:
                     continue
                 issued = float(np.mean(mf_flops.get(kname, [0.0])))
-                ml.append(f"{k:18s} MfmaUtil {np.mean(vs):6.2f} %   MfmaFlopsBF16 "
+                ml.append(f"{k + _template_args(kname):30s} MfmaUtil {np.mean(vs):6.2f} %   MfmaFlopsBF16 "
                           f"{issued / 1e9:10.3f} GFLOP/dispatch   ({len(vs)} dispatches)")
             with open(os.path.join(ROOT, "profiles", f"mfma_util_{sec}_{wl}.txt"), "w") as f:
                 f.write(f"MFMA utilisation per dispatch, workload {wl}: rocprofv3 derived\n"
