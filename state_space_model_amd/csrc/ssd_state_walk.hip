@@ -39,36 +39,45 @@ namespace ssd {
 // holds column n = 16 nt + l % 16 at tokens 32 ks + 4 (l / 16) + r (slots
 // 0..3) and 32 ks + 16 + 4 (l / 16) + r (slots 4..7), r = 0..3 -- the paired
 // token map of the x fragments read transposed from LDS -- and zero past the
-// chunk's end.  One workgroup per (chunk, group), a wave per fragment.
+// chunk's end.  One workgroup per (chunk, group, 32-token step): its 32 rows
+// of B (8 KB) are read whole-row into LDS, then each wave forms two n-tiles'
+// fragments with transposed LDS reads and writes them as whole 1 KB rows.
 __global__ __launch_bounds__(256) void k_bfrag(const bf16 *__restrict__ B, ChunkMap cmap, int nc,
                                                int G, int Q, bf16 *__restrict__ out) {
-  constexpr int N = 128, NTL = N / 16;
-  const int c = blockIdx.x / G, g = blockIdx.x - (blockIdx.x / G) * G;
+  constexpr int N = 128, NTL = N / 16, PITCH = N + kTrPad;
+  __shared__ __align__(16) bf16 rows[32 * PITCH];
+  const int KS = Q / 32;
+  const int u = blockIdx.x;  // (chunk, group, step), step fastest
+  const int ks = u % KS, cg = u / KS;
+  const int c = cg / G, g = cg - (cg / G) * G;
   if (c >= nc) return;
   const int4 ci = cmap(c);
   const int len = ci.z;
   if (len <= 0) return;
-  const int lane = threadIdx.x & 63, grp = lane >> 4, col = lane & 15;
-  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  const size_t bstride = (size_t)G * N;
-  // raw 16-bit patterns (the fragment is assembled with integer ops, not by
-  // element inserts into a bf16 vector)
-  const unsigned short *bg =
-      reinterpret_cast<const unsigned short *>(B) + (size_t)ci.y * bstride + (size_t)g * N;
-  const int nfr = (Q / 32) * NTL;
-  bf16 *oc = out + ((size_t)c * G + g) * (size_t)nfr * 512;
-  for (int f = wave; f < nfr; f += nw) {
-    const int ks = f / NTL, nt = f - (f / NTL) * NTL;
-    const int n = 16 * nt + col, j0 = 32 * ks + 4 * grp;
-    uint32_t v[8];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      v[r] = j0 + r < len ? bg[(size_t)(j0 + r) * bstride + n] : 0u;
-      v[4 + r] = j0 + 16 + r < len ? bg[(size_t)(j0 + 16 + r) * bstride + n] : 0u;
+  const int tid = threadIdx.x;
+  // 32 rows x 256 bytes: thread t moves 32 bytes of row t / 8 (zero past the chunk)
+  {
+    const int r = tid >> 3, q = (tid & 7) * 16;  // row, first column
+    const int j = 32 * ks + r;
+    i4v v0 = i4v{0, 0, 0, 0}, v1 = i4v{0, 0, 0, 0};
+    if (j < len) {
+      const i4v *src = reinterpret_cast<const i4v *>(B + ((size_t)ci.y + j) * G * N +
+                                                     (size_t)g * N + q);
+      v0 = src[0];
+      v1 = src[1];
     }
-    const i4v packed = i4v{(int)(v[0] | (v[1] << 16)), (int)(v[2] | (v[3] << 16)),
-                           (int)(v[4] | (v[5] << 16)), (int)(v[6] | (v[7] << 16))};
-    *reinterpret_cast<i4v *>(oc + (size_t)f * 512 + lane * 8) = packed;
+    i4v *dst = reinterpret_cast<i4v *>(rows + r * PITCH + q);
+    dst[0] = v0;
+    dst[1] = v1;
+  }
+  __syncthreads();
+  const int lane = tid & 63, grp = lane >> 4, wave = tid >> 6;
+  bf16 *oc = out + (((size_t)c * G + g) * KS + ks) * (size_t)NTL * 512;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int nt = 2 * wave + k;
+    const Frag<bf16> f = frag_kmaj(rows, PITCH, 16 * nt, 4 * grp, 16 + 4 * grp);
+    *reinterpret_cast<bf16x8 *>(oc + (size_t)nt * 512 + lane * 8) = f.v;
   }
 }
 
@@ -98,10 +107,11 @@ __device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t rs, uint32_t ld
 
 // The chunk's cumulative decay, computed by every wave from the chunk's dt
 // column in LDS (rows past its length hold 0), R consecutive rows per lane:
-// s = log2(e) A cumsum(dt), w_j = 2^(s_end - s_j) dt_j into the wave's own LDS
-// row w_l (read back by the same wave only: no barrier); with `emit`, s, dt
-// and u_j = 2^(s_r - s_j) dt_j at `off` of the output rows.  Returns s_end.
-template <int Q>
+// s = log2(e) A cumsum(dt); with W, w_j = 2^(s_end - s_j) dt_j into the
+// wave's own LDS row w_l (read back by the same wave only: no barrier); with
+// `emit`, s, dt and u_j = 2^(s_r - s_j) dt_j at `off` of the output rows.
+// Returns s_end.
+template <int Q, bool W>
 __device__ __forceinline__ float walk_decay(const float *dt_l, float *w_l, float a2, bool emit,
                                             size_t off, float *__restrict__ s_out,
                                             float *__restrict__ dt_out,
@@ -134,7 +144,7 @@ __device__ __forceinline__ float walk_decay(const float *dt_l, float *w_l, float
   for (int r = 0; r < R; ++r) {
     const int i = lane * R + r;
     if (i < Q) {
-      w_l[i] = __builtin_amdgcn_exp2f(fminf(s_end - sv[r], 0.f)) * d[r];
+      if (W) w_l[i] = __builtin_amdgcn_exp2f(fminf(s_end - sv[r], 0.f)) * d[r];
       if (emit) {
         s_out[off + i] = sv[r];
         dt_out[off + i] = d[r];
@@ -290,20 +300,10 @@ __global__ __launch_bounds__(256) void k_state_walk(
         if (c + 2 < c1) cn = cmap(c + 2);
       }
       if (ph == 0) {
-        // the state entering chunk c, in the operand type, for the chunk scan
-        const size_t hco = ((size_t)c * H + hd) * (size_t)(N * P);
-#pragma unroll
-        for (int t = 0; t < NTW; ++t)
-#pragma unroll
-          for (int pt = 0; pt < NPT; ++pt) {
-            const size_t e = hco + (size_t)(16 * (nt0 + t) + col) * P + 16 * pt + 4 * grp;
-            st4T(hin + e, Hs[t][pt]);
-            if (hin32) st4(hin32 + e, Hs[t][pt]);  // a training forward keeps them in float32
-          }
         // the chunk's decay, in every wave (wave 0 of part 0 writes s, dt, u)
-        s_end = walk_decay<Q>(reinterpret_cast<const float *>(smem + K::OFF_DT + db * K::DTN * 4),
-                              w_l, a2, part == 0 && wave == 0, ((size_t)c * H + hd) * Q, s_out,
-                              dt_out, u_out);
+        s_end = walk_decay<Q, true>(
+            reinterpret_cast<const float *>(smem + K::OFF_DT + db * K::DTN * 4), w_l, a2, false,
+            0, s_out, dt_out, u_out);
       }
       // S^T += sum over this phase's tokens of x_j (w_j B_j)^T
       const char *xt = smem + xbuf * K::XB;
@@ -331,6 +331,26 @@ __global__ __launch_bounds__(256) void k_state_walk(
       // the next phase's loads have landed and this phase's buffers are free
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
+      if (ph == 0) {
+        // the state entering chunk c, in the operand type, for the chunk scan:
+        // stored after the wait, so that the stores complete under the next
+        // phase's work instead of holding up this one's wait
+        const size_t hco = ((size_t)c * H + hd) * (size_t)(N * P);
+#pragma unroll
+        for (int t = 0; t < NTW; ++t)
+#pragma unroll
+          for (int pt = 0; pt < NPT; ++pt) {
+            const size_t e = hco + (size_t)(16 * (nt0 + t) + col) * P + 16 * pt + 4 * grp;
+            st4T(hin + e, Hs[t][pt]);
+            if (hin32) st4(hin32 + e, Hs[t][pt]);  // a training forward keeps them in float32
+          }
+        // s, dt and u for the chunk scan, likewise after the wait (wave 0 of
+        // part 0, from the chunk's dt column, which stays in LDS until the
+        // chunk after next is loaded)
+        if (part == 0 && wave == 0)
+          walk_decay<Q, false>(reinterpret_cast<const float *>(smem + K::OFF_DT + db * K::DTN * 4),
+                               w_l, a2, true, ((size_t)c * H + hd) * Q, s_out, dt_out, u_out);
+      }
 #pragma unroll
       for (int t = 0; t < NTW; ++t)
 #pragma unroll
@@ -412,7 +432,7 @@ hipError_t launch_state_walk(const PrefillArgs &a, const WorkspaceLayout &L, int
   if (nc > 0) {
     ChunkMap cm{reinterpret_cast<const int4 *>(static_cast<char *>(a.workspace) + L.info),
                 a.cu ? 0 : (int)(a.T / a.nseq), a.nseq, a.Q};
-    hipLaunchKernelGGL(k_bfrag, dim3((unsigned)nc * a.G), dim3(256), 0, st,
+    hipLaunchKernelGGL(k_bfrag, dim3((unsigned)nc * a.G * (a.Q / 32)), dim3(256), 0, st,
                        (const bf16 *)a.B, cm, nc, a.G, a.Q,
                        reinterpret_cast<bf16 *>(static_cast<char *>(a.workspace) + L.bfrag));
     hipError_t e = hipGetLastError();
