@@ -26,7 +26,10 @@
 // float32 accumulators of exact products, so the cancellation between its row
 // and column sums costs float32 rounding only; forms through y or q, whose
 // operands are rounded to bfloat16 for the MFMA, would carry that rounding
-// through the same cancellation.
+// through the same cancellation.  For the same reason the DX scan's state
+// term, from which v comes, takes dH_c as two bfloat16 operands, its rounded
+// value and what the rounding dropped: with dH_c rounded once, v alone moved
+// dA by about 1 % of its size on the 130M layer.
 //
 // Launches, all on the caller's stream:
 //   forward recompute   chunk states, state pass (H_in per chunk, final state)
@@ -119,8 +122,8 @@ __global__ __launch_bounds__(MAXT) void k_bwd_scan(
     const T *__restrict__ x, const T *__restrict__ dy, const T *__restrict__ B,
     const T *__restrict__ C, const float *__restrict__ D, const float *__restrict__ s_ws,
     const float *__restrict__ dt_ws, const float *__restrict__ u_ws,
-    const T *__restrict__ state, ChunkMap cmap, int nc, int H, int G, int Q, int JP, int hb,
-    float *__restrict__ out, int ostride, BwdRows rows) {
+    const T *__restrict__ state, const bf16 *__restrict__ state_lo, ChunkMap cmap, int nc, int H,
+    int G, int Q, int JP, int hb, float *__restrict__ out, int ostride, BwdRows rows) {
   constexpr int KD = MODE == kBwdDX ? N : P;
   constexpr int VD = MODE == kBwdDX ? P : N;
   typedef BwdScanCfg<T, MODE, KD, VD> K;
@@ -288,6 +291,17 @@ __global__ __launch_bounds__(MAXT) void k_bwd_scan(
           else
             a = frag_kmaj(Ss, K::SP, vt * 16, kk * 32 + 8 * grp, kk * 32 + 8 * grp + 4);
           mma(st, a, qf[kk]);
+          if constexpr (MODE == kBwdDX && sizeof(T) == 2) {
+            // the part of dH_c that its bfloat16 copy rounds away, in fragment
+            // order [N/8][P][8] (one 16-byte read per lane)
+            const int n8 = kk * 4 + grp;
+            if (state_lo && 8 * n8 < KD) {
+              Frag<T> lo;
+              lo.v = *reinterpret_cast<const bf16x8 *>(
+                  state_lo + csh * (size_t)(N * P) + ((size_t)n8 * P + vt * 16 + col) * 8);
+              mma(st, lo, qf[kk]);
+            }
+          }
         }
         f4 w4 = zero4();
         if (MODE != kBwdDB && i < len) w4 = ld4f(row + vt * 16 + 4 * grp);
@@ -521,8 +535,8 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_state_pass_bwd(
     const float *__restrict__ Sb, const float *__restrict__ s_ws, const int *__restrict__ seq_off,
     ChunkMap cmap, const float *__restrict__ dh_out, const float *__restrict__ hfin,
-    const float *__restrict__ hin32, T *__restrict__ dHc, float *__restrict__ epart,
-    float *__restrict__ dh0, int H, int NP, int Q) {
+    const float *__restrict__ hin32, T *__restrict__ dHc, bf16 *__restrict__ dHlo,
+    float *__restrict__ epart, float *__restrict__ dh0, int H, int NP, int Q, int P) {
   constexpr int BATCH = 8;
   const int s = blockIdx.z, hd = blockIdx.y;
   const int tid = blockIdx.x * blockDim.x + threadIdx.x;
@@ -564,6 +578,14 @@ __global__ __launch_bounds__(256) void k_state_pass_bwd(
         d += dpp_mov<0x140>(d);  // lane i with 15 - i
         if (lane16 == 0) epart[ch * npr + rid] = d;
         st4T(dHc + ch * NP + e, gv);
+        if (dHlo) {  // bfloat16: what the rounding to dHc dropped, in fragment order
+          const f4 hi = __builtin_convertvector(__builtin_convertvector(gv, bf16x4), f4);
+          const f4 lo = gv - hi;
+          const int n = e / P, p = e - (e / P) * P;
+          bf16 *dst = dHlo + ch * NP + ((size_t)(n >> 3) * P + p) * 8 + (n & 7);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) dst[8 * q] = (bf16)lo[q];
+        }
         const float a = __builtin_amdgcn_exp2f(fminf(sl[u], 0.f));
 #pragma unroll
         for (int q = 0; q < 4; ++q) gv[q] = a * gv[q] + Sv[u][q];
@@ -722,6 +744,8 @@ BwdLayout bwd_layout(int64_t T, int nseq, int H, int P, int N, int G, int Q, int
   off = align_up(off + 4 * nc * H * NP, 256);
   L.dHc = off;
   off = align_up(off + (size_t)elem * nc * H * NP, 256);
+  L.dHlo = off;  // bfloat16 only
+  off = align_up(off + (elem == 2 ? 2 * nc * H * NP : 0), 256);
   L.epart = off;
   off = align_up(off + 4 * nc * H * (NP / 64), 256);
   L.rows = off;  // q, cv, r, dyx, then rs for two parts
@@ -748,7 +772,8 @@ static BwdRows bwd_rows(char *ws, const BwdLayout &L, int nc, int H, int Q) {
 
 template <typename T, int MODE, int P, int N>
 static hipError_t launch_bwd_scan(const BwdArgs &a, const BwdLayout &L, int nc, const T *state,
-                                  float *out, int ostride, int hb, hipStream_t st) {
+                                  const bf16 *state_lo, float *out, int ostride, int hb,
+                                  hipStream_t st) {
   constexpr int KD = MODE == kBwdDX ? N : P, VD = MODE == kBwdDX ? P : N;
   typedef BwdScanCfg<T, MODE, KD, VD> K;
   const int Q = a.f.Q;
@@ -784,7 +809,7 @@ static hipError_t launch_bwd_scan(const BwdArgs &a, const BwdLayout &L, int nc, 
               a.f.cu ? 0 : (int)(a.f.T / a.f.nseq), a.f.nseq, Q};
   int nc_ = nc, H_ = a.f.H, G_ = a.f.G, Q_ = Q, jp_ = jp, hb_ = hb, os_ = ostride;
   BwdRows rows = bwd_rows(ws, L, nc, a.f.H, Q);
-  void *args[] = {&xp, &dyp, &bp, &cp, &Dp, &sp, &dtp, &up, &state, &cm, &nc_,
+  void *args[] = {&xp, &dyp, &bp, &cp, &Dp, &sp, &dtp, &up, &state, &state_lo, &cm, &nc_,
                   &H_, &G_, &Q_, &jp_, &hb_, &out, &os_, &rows};
   return hipLaunchKernel(kern, dim3(xcd_grid(nc, (a.f.H / hb) * split)), dim3(threads), args, lds,
                          st);
@@ -801,6 +826,7 @@ static hipError_t run_backward(const BwdArgs &a) {
   float *hfin = reinterpret_cast<float *>(ws + L.hfin);
   float *hin32 = reinterpret_cast<float *>(ws + L.hin32);
   T *dHc = reinterpret_cast<T *>(ws + L.dHc);
+  bf16 *dHlo = sizeof(T) == 2 ? reinterpret_cast<bf16 *>(ws + L.dHlo) : nullptr;
   T *hin = reinterpret_cast<T *>(ws + L.fwd.hin);
   float *S = reinterpret_cast<float *>(ws + L.fwd.S);
   float *epart = reinterpret_cast<float *>(ws + L.epart);
@@ -818,6 +844,7 @@ static hipError_t run_backward(const BwdArgs &a) {
     fa.h_out = hfin;
     fa.hin32 = hin32;
     fa.scan_follows = false;  // only the states are recomputed
+    fa.precise_states = true;  // as the training forward computes them
     e = launch_prefill(fa, 7u);
     if (e != hipSuccess) return e;
   }
@@ -831,7 +858,7 @@ static hipError_t run_backward(const BwdArgs &a) {
   hipLaunchKernelGGL(k_state_pass_bwd<T>, dim3((NP + 1023) / 1024, f.H, f.nseq), dim3(256), 0, st,
                      S, reinterpret_cast<const float *>(ws + L.fwd.s),
                      reinterpret_cast<const int *>(ws + L.fwd.seq_off), cmap, a.dh_out, hfin,
-                     hin32, dHc, epart, a.dh0, f.H, NP, f.Q);
+                     hin32, dHc, dHlo, epart, a.dh0, f.H, NP, f.Q, P);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int hb = bwd_heads_per_block(nc, f.H, f.G, f.Q);
@@ -840,11 +867,11 @@ static hipError_t run_backward(const BwdArgs &a) {
   float *dCo = parts == 1 ? a.dC : reinterpret_cast<float *>(ws + L.dCh);
   if (nc > 0) {
     const int os = f.H / hb;
-    e = launch_bwd_scan<T, kBwdDX, P, N>(a, L, nc, dHc, a.dx, f.H, 1, st);
+    e = launch_bwd_scan<T, kBwdDX, P, N>(a, L, nc, dHc, dHlo, a.dx, f.H, 1, st);
     if (e != hipSuccess) return e;
-    e = launch_bwd_scan<T, kBwdDB, P, N>(a, L, nc, dHc, dBo, os, hb, st);
+    e = launch_bwd_scan<T, kBwdDB, P, N>(a, L, nc, dHc, nullptr, dBo, os, hb, st);
     if (e != hipSuccess) return e;
-    e = launch_bwd_scan<T, kBwdDC, P, N>(a, L, nc, hin, dCo, os, hb, st);
+    e = launch_bwd_scan<T, kBwdDC, P, N>(a, L, nc, hin, nullptr, dCo, os, hb, st);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_bwd_ddt, dim3((unsigned)nc * f.H), dim3(f.Q < 64 ? 64 : f.Q), 0, st,
                        bwd_rows(ws, L, nc, f.H, f.Q), f.Q >= 256 ? 2 : 1,
@@ -893,6 +920,7 @@ hipError_t launch_prefill_train_forward(const PrefillArgs &f) {
   fa.h_out = hfin;  // the state pass writes the final state here and to the caller's h_out
   fa.h_out2 = f.h_out;
   fa.hin32 = reinterpret_cast<float *>(ws + L.hin32);
+  fa.precise_states = true;  // the backward reads these states (bitwise as its recompute)
   return launch_prefill(fa, 15u);
 }
 

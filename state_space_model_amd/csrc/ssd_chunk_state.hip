@@ -141,7 +141,7 @@ __device__ __forceinline__ void dma_dt(float *dt_l, const float *__restrict__ dt
   }
 }
 
-template <typename T, int P, int N, int NH, bool BWD>
+template <typename T, int P, int N, int NH, bool BWD, bool PREC>
 __global__ __launch_bounds__((StateCfg<T, P, N, NH>::THREADS)) void k_chunk_state(
     const T *__restrict__ x, const float *__restrict__ dt, const float *__restrict__ A,
     const T *__restrict__ B, ChunkMap cmap, int nc, int H, int G, int Q, int JP, int do_state,
@@ -225,11 +225,13 @@ __global__ __launch_bounds__((StateCfg<T, P, N, NH>::THREADS)) void k_chunk_stat
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
-    if constexpr (SWZ)
-      scale_rows_swz<T>(Xc, w_l, ph, min(JP, len - ph));
-    else
-      scale_rows<T, K::XP, K::XD>(Xs, w_l, ph, min(JP, len - ph));
-    __syncthreads();
+    if constexpr (!PREC) {
+      if constexpr (SWZ)
+        scale_rows_swz<T>(Xc, w_l, ph, min(JP, len - ph));
+      else
+        scale_rows<T, K::XP, K::XD>(Xs, w_l, ph, min(JP, len - ph));
+      __syncthreads();
+    }
     // swizzled transposed reads use the paired k map: rows k0 + 4 grp + col/4
     // and k0 + 16 + 4 grp + col/4 (any map works when both operands share it);
     // segment pt (or nt) by XOR with 32 pt (bits 5-6, or 5-7, of the offsets)
@@ -256,7 +258,27 @@ __global__ __launch_bounds__((StateCfg<T, P, N, NH>::THREADS)) void k_chunk_stat
             a = frag_kmaj(Xs, K::XP, pt * 16, k0 + 8 * grp, k0 + 8 * grp + 4);
             b = frag_kmaj(Bs, K::BP, nt * 16, k0 + 8 * grp, k0 + 8 * grp + 4);
           }
-          mma(acc[t], a, b);
+          if constexpr (PREC) {
+            // w x in float32 from the unscaled tile, as two bfloat16 operands:
+            // the rounded product and what the rounding dropped (rows past
+            // the chunk take weight 0)
+            const int ta = ph + k0 + (SWZ ? 4 * grp : 8 * grp);
+            const int tb = ph + k0 + (SWZ ? 16 + 4 * grp : 8 * grp + 4);
+            const f8v xv = cvt_f8(a.v);
+            f8v xw;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              xw[r] = ta + r < len ? xv[r] * w_l[ta + r] : 0.f;
+              xw[4 + r] = tb + r < len ? xv[4 + r] * w_l[tb + r] : 0.f;
+            }
+            Frag<T> hi, lo;
+            hi.v = cvt_bf8(xw);
+            lo.v = cvt_bf8(xw - cvt_f8(hi.v));
+            mma(acc[t], hi, b);
+            mma(acc[t], lo, b);
+          } else {
+            mma(acc[t], a, b);
+          }
         }
       }
     }
@@ -280,8 +302,13 @@ static hipError_t run_state(const PrefillArgs &a, const WorkspaceLayout &L, int 
   const int jp = K::jp(a.Q, jp_cap);
   const size_t lds = K::lds_bytes(jp, a.Q);
   if (lds > 160 * 1024) return hipErrorInvalidConfiguration;
-  const void *kern = bwd ? (const void *)k_chunk_state<T, P, N, NH, true>
-                        : (const void *)k_chunk_state<T, P, N, NH, false>;
+  const void *kern;
+  if (bwd)
+    kern = (const void *)k_chunk_state<T, P, N, NH, true, false>;
+  else if (sizeof(T) == 2 && a.precise_states)
+    kern = (const void *)k_chunk_state<T, P, N, NH, false, sizeof(T) == 2>;
+  else
+    kern = (const void *)k_chunk_state<T, P, N, NH, false, false>;
   hipError_t e = set_lds_limit(kern);
   if (e != hipSuccess) return e;
   char *ws = static_cast<char *>(a.workspace);

@@ -251,9 +251,9 @@ def test_backward_workspace_size():
     n1 = w(4096, 1, 24, 64, 128, 1, 256, 1)
     nc = 16
     # the forward's workspace, then: final states (f32), states entering each chunk
-    # (f32), dH per chunk (bf16), the <dH, H> partials, six per-row arrays,
-    # dA/dD partials, per-head dB and dC
-    extra = (24 * 128 * 64 * 4 + nc * 24 * 128 * 64 * (4 + 2) + nc * 24 * 128 * 4
+    # (f32), dH per chunk (bf16) and the part of it bf16 rounds away (bf16), the
+    # <dH, H> partials, six per-row arrays, dA/dD partials, per-head dB and dC
+    extra = (24 * 128 * 64 * 4 + nc * 24 * 128 * 64 * (4 + 2 + 2) + nc * 24 * 128 * 4
              + 6 * nc * 24 * 256 * 4 + 2 * nc * 24 * 4 + 2 * 4096 * 24 * 128 * 4)
     assert fwd + extra <= n1 <= fwd + extra + 16 * 256
     assert w(4096, 1, 24, 64, 128, 24, 256, 1) < n1       # H == G: no per-head dB/dC

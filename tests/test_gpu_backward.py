@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import TOL, dev_inputs, log
+from gpu_util import TOL, dev_inputs, log, maxabs
 from state_space_model_amd import inputs
 
 pytestmark = pytest.mark.gpu
@@ -47,11 +47,17 @@ def _ref_bwd(d, dy, dh, with_h0=True):
                                    d["cu_seqlens"])
 
 
-def _compare(g, r, tol):
+# dA sums dt_i dz_i over every token of a head, and dz cancels heavily, so
+# the bf16 layer workloads also hold it to a tighter bound than the others.
+DA_TOL_BF16_LAYER = 5e-3
+
+
+def _compare(g, r, tol, tight=None):
     errs = {k: scaled_err(g[k], r[k]) for k in GRADS}
     log("  " + " ".join(f"{k}={v:.2g}" for k, v in errs.items()))
-    bad = {k: v for k, v in errs.items() if not v <= tol}
-    assert not bad, f"gradients over tolerance {tol}: {bad}"
+    lim = {k: min(tol, (tight or {}).get(k, tol)) for k in GRADS}
+    bad = {k: v for k, v in errs.items() if not v <= lim[k]}
+    assert not bad, f"gradients over tolerance {lim}: {bad}"
 
 
 SMALL = [  # (lengths, H, P, N, G, chunk, h0, dh_out)
@@ -100,7 +106,7 @@ def test_backward_130m_layer_workload():
     dy, dh = inputs.cotangents(T, nseq, w.H, w.P, w.N, 701, "bf16")
     r = _ref_bwd(d, dy, dh)
     g = _gpu_bwd(d, dy, dh, "bf16", w.chunk)
-    _compare(g, r, TOL["bf16"])
+    _compare(g, r, TOL["bf16"], {"dA": DA_TOL_BF16_LAYER})
 
 
 def test_backward_2p7b_layer_workload():
@@ -114,7 +120,7 @@ def test_backward_2p7b_layer_workload():
     dy, dh = inputs.cotangents(T, nseq, w.H, w.P, w.N, 702, "bf16")
     g = _gpu_bwd(d, dy, dh, "bf16", w.chunk)
     r = _ref_bwd(d, dy, dh)
-    _compare(g, r, TOL["bf16"])
+    _compare(g, r, TOL["bf16"], {"dA": DA_TOL_BF16_LAYER})
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -247,10 +253,13 @@ TRAIN_CASES = [  # (lengths, H, P, N, G, chunk, h0, dh_out, dtype)
 
 @pytest.mark.parametrize("case", range(len(TRAIN_CASES)))
 def test_train_forward_and_saved_backward_bitwise(case):
-    """The training forward gives y and h_out bitwise as the plain prefill, and
-    the backward that takes its saved states gives every gradient bitwise as
-    the backward that recomputes them -- twice in a row on the same saved
-    states (the backward leaves them intact)."""
+    """The backward that takes the training forward's saved states gives every
+    gradient bitwise as the backward that recomputes them -- twice in a row on
+    the same saved states (the backward leaves them intact).  In float32 the
+    training forward's y and h_out are bitwise the plain prefill's; in
+    bfloat16 it forms the chunk states from a two-part (rounded value and
+    remainder) weighted x, so its y and h_out are checked against the oracle
+    and must be at least as close to it as the plain prefill's."""
     import torch
     from state_space_model_amd import ssd
     lengths, H, P, N, G, chunk, h0, dh, dtype = TRAIN_CASES[case]
@@ -271,7 +280,18 @@ def test_train_forward_and_saved_backward_bitwise(case):
     g3 = ssd.prefill_backward(*fwd, dyt, t["h0"], dht, chunk=chunk, cu_seqlens=t["cu_seqlens"],
                               saved=saved)
     torch.cuda.synchronize()
-    assert torch.equal(y1, y2) and torch.equal(h1, h2)
+    if dtype == "f32":
+        assert torch.equal(y1, y2) and torch.equal(h1, h2)
+    else:
+        ry, rh = oracle.prefill(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"],
+                                None if d.get("h0") is None else d["h0"].astype(np.float64),
+                                d["cu_seqlens"])
+        e1 = (maxabs(y1.cpu().numpy(), ry), maxabs(h1.cpu().numpy(), rh))
+        e2 = (maxabs(y2.cpu().numpy(), ry), maxabs(h2.cpu().numpy(), rh))
+        log(f"  vs oracle: prefill y {e1[0]:.3g} h {e1[1]:.3g}; training forward y {e2[0]:.3g}"
+            f" h {e2[1]:.3g}")
+        assert max(e2) <= TOL["bf16"]
+        assert e2[1] <= 1.25 * e1[1] + 1e-6, (e1, e2)
     for k in GRADS:
         assert torch.equal(g1[k], g2[k]), k
         assert torch.equal(g1[k], g3[k]), k
