@@ -81,9 +81,24 @@ __global__ __launch_bounds__(256) void k_bfrag(const bf16 *__restrict__ B, Chunk
   }
 }
 
-template <int Q, int NH, int JP_> struct WalkCfg {
+// Chunk c's map entry.  For a dense batch it is arithmetic only: a value
+// loaded from memory here would make the compiler drain every outstanding
+// memory operation (the previous chunk's stores included) before the loads it
+// feeds could issue.
+template <bool DENSE>
+__device__ __forceinline__ int4 walk_map(const ChunkMap &m, int c) {
+  if constexpr (DENSE) {
+    const int cps = (m.L + m.Q - 1) / m.Q;
+    const int seq = c / cps, k = c - seq * cps;
+    return make_int4(seq, seq * m.L + k * m.Q, min(m.Q, m.L - k * m.Q), k);
+  } else {
+    return m(c);
+  }
+}
+
+template <int Q, int NH, int JP_, int NW_> struct WalkCfg {
   static constexpr int P = 64, N = 128;
-  static constexpr int NW = 4;                  // waves
+  static constexpr int NW = NW_;                // waves
   static constexpr int NT = N / 16 / NH;        // n-tiles of the chain's state block
   static constexpr int NTW = NT / NW;           // n-tiles per wave
   static constexpr int JP = JP_ < Q ? JP_ : Q;  // rows per phase
@@ -202,14 +217,14 @@ __device__ __forceinline__ void walk_load_b(const bf16 *bc, int ph,
           bc + (size_t)((ph * K::KSP + k) * NTL + t) * 512);
 }
 
-template <int Q, int NH, int JP_>
-__global__ __launch_bounds__(256) void k_state_walk(
+template <int Q, int NH, int JP_, int NW_, bool DENSE>
+__global__ __launch_bounds__(64 * NW_) void k_state_walk(
     const bf16 *__restrict__ x, const float *__restrict__ dt, const float *__restrict__ A,
     const bf16 *__restrict__ bfr, const int *__restrict__ seq_off, ChunkMap cmap, int H, int G,
     int nchain, const float *h0, float *h_out, float *__restrict__ s_out,
     float *__restrict__ dt_out, float *__restrict__ u_out, bf16 *__restrict__ hin,
     float *__restrict__ hin32, float *h_out2) {
-  typedef WalkCfg<Q, NH, JP_> K;
+  typedef WalkCfg<Q, NH, JP_, NW_> K;
   constexpr int P = K::P, N = K::N, NTW = K::NTW, NPT = P / 16, KSP = K::KSP, NPH = K::NPH;
   constexpr int NTL = N / 16, JP = K::JP;
   // chains in contiguous blocks per XCD (workgroup L runs on XCD L % 8), so the
@@ -220,7 +235,7 @@ __global__ __launch_bounds__(256) void k_state_walk(
   const int part = chn % NH, sh = chn / NH;
   const int hd = __builtin_amdgcn_readfirstlane(sh % H), s = __builtin_amdgcn_readfirstlane(sh / H);
   int c0, c1;  // chunks of sequence s
-  if (cmap.L > 0) {
+  if constexpr (DENSE) {
     const int cps = (cmap.L + Q - 1) / Q;
     c0 = s * cps;
     c1 = c0 + cps;
@@ -264,18 +279,18 @@ __global__ __launch_bounds__(256) void k_state_walk(
   BF bcur;
   int4 cn = make_int4(0, 0, 0, 0);  // the next chunk's map entry, read a chunk ahead
   if (c0 < c1) {
-    const int4 ci = cmap(c0);
+    const int4 ci = walk_map<DENSE>(cmap, c0);
     walk_issue_dt<K>(dt, ci, H, hd, lds0 + K::OFF_DT, wave);
     walk_issue_x<K>(x, ci, 0, xstride, hd, xl, smem, wave);
     walk_load_b<K>(bfw + (size_t)c0 * bfc, 0, bcur);
-    if (c0 + 1 < c1) cn = cmap(c0 + 1);
+    if (c0 + 1 < c1) cn = walk_map<DENSE>(cmap, c0 + 1);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   int xbuf = 0;
   for (int c = c0; c < c1; ++c) {
-    const int4 ci = cmap(c);
+    const int4 ci = walk_map<DENSE>(cmap, c);
     const int db = (c - c0) & 1;
     const int4 cnow = cn;  // chunk c + 1
     float s_end = 0.f;
@@ -297,7 +312,7 @@ __global__ __launch_bounds__(256) void k_state_walk(
         walk_issue_x<K>(x, cnow, 0, xstride, hd, xl, smem + (xbuf ^ 1) * K::XB, wave);
         walk_issue_dt<K>(dt, cnow, H, hd, lds0 + K::OFF_DT + (db ^ 1) * K::DTN * 4, wave);
         walk_load_b<K>(bfw + (size_t)(c + 1) * bfc, 0, bnext);
-        if (c + 2 < c1) cn = cmap(c + 2);
+        if (c + 2 < c1) cn = walk_map<DENSE>(cmap, c + 2);
       }
       if (ph == 0) {
         // the chunk's decay, in every wave (wave 0 of part 0 writes s, dt, u)
@@ -399,12 +414,16 @@ bool walk_choice(int P, int N, int Q, bool bf16, int nseq, int H, bool packed, u
 #ifndef SSD_WALK_JP
 #define SSD_WALK_JP 128
 #endif
+#ifndef SSD_WALK_NW
+#define SSD_WALK_NW 4
+#endif
 
-template <int Q, int NH, int JP>
+template <int Q, int NH, int JP, int NW>
 static hipError_t run_walk(const PrefillArgs &a, const WorkspaceLayout &L, bool write_hout,
                            hipStream_t st) {
-  typedef WalkCfg<Q, NH, JP> K;
-  const void *kern = (const void *)k_state_walk<Q, NH, JP>;
+  typedef WalkCfg<Q, NH, JP, NW> K;
+  const void *kern = a.cu ? (const void *)k_state_walk<Q, NH, JP, NW, false>
+                          : (const void *)k_state_walk<Q, NH, JP, NW, true>;
   hipError_t e = set_lds_limit(kern);
   if (e != hipSuccess) return e;
   char *ws = static_cast<char *>(a.workspace);
@@ -439,10 +458,10 @@ hipError_t launch_state_walk(const PrefillArgs &a, const WorkspaceLayout &L, int
     if (e != hipSuccess) return e;
   }
   switch (a.Q) {
-    case 32: return run_walk<32, SSD_WALK_NH, SSD_WALK_JP>(a, L, write_hout, st);
-    case 64: return run_walk<64, SSD_WALK_NH, SSD_WALK_JP>(a, L, write_hout, st);
-    case 128: return run_walk<128, SSD_WALK_NH, SSD_WALK_JP>(a, L, write_hout, st);
-    case 256: return run_walk<256, SSD_WALK_NH, SSD_WALK_JP>(a, L, write_hout, st);
+    case 32: return run_walk<32, SSD_WALK_NH, SSD_WALK_JP, SSD_WALK_NW>(a, L, write_hout, st);
+    case 64: return run_walk<64, SSD_WALK_NH, SSD_WALK_JP, SSD_WALK_NW>(a, L, write_hout, st);
+    case 128: return run_walk<128, SSD_WALK_NH, SSD_WALK_JP, SSD_WALK_NW>(a, L, write_hout, st);
+    case 256: return run_walk<256, SSD_WALK_NH, SSD_WALK_JP, SSD_WALK_NW>(a, L, write_hout, st);
   }
   return hipErrorInvalidValue;
 }
