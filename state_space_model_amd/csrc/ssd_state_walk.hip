@@ -120,54 +120,86 @@ __device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t rs, uint32_t ld
                : "memory");
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave in registers: shifts of 1,
+// 2, 4 and 8 lanes within each 16-lane row (lanes shifted in from outside the
+// row add 0), then the last lane of row 0 and of row 2 added to rows 1 and 3
+// (row broadcast 15) and that of row 1 to rows 2 and 3 (row broadcast 31).
+__device__ __forceinline__ float wave_incl_scan(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                              0x111, 0xF, 0xF, true));  // row_shr:1
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                              0x112, 0xF, 0xF, true));  // row_shr:2
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                              0x114, 0xF, 0xF, true));  // row_shr:4
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                              0x118, 0xF, 0xF, true));  // row_shr:8
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                              0x142, 0xA, 0xF, false));  // row_bcast:15
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                              0x143, 0xC, 0xF, false));  // row_bcast:31
+  return v;
+}
+
+// The chunk's s, dt and u rows for the chunk scan, R consecutive rows per lane,
+// held in registers from the decay until they are stored.
+template <int Q> struct WalkRows {
+  static constexpr int R = Q >= 64 ? Q / 64 : 1;
+  float s[R], dt[R], u[R];
+};
+
 // The chunk's cumulative decay, computed by every wave from the chunk's dt
 // column in LDS (rows past its length hold 0), R consecutive rows per lane:
-// s = log2(e) A cumsum(dt); with W, w_j = 2^(s_end - s_j) dt_j into the
-// wave's own LDS row w_l (read back by the same wave only: no barrier); with
-// `emit`, s, dt and u_j = 2^(s_r - s_j) dt_j at `off` of the output rows.
+// s = log2(e) A cumsum(dt), w_j = 2^(s_end - s_j) dt_j into the wave's own LDS
+// row w_l (read back by the same wave only: no barrier), and s, dt and
+// u_j = 2^(s_r - s_j) dt_j (r the last row of j's 32-row block) into `rows`.
 // Returns s_end.
-template <int Q, bool W>
-__device__ __forceinline__ float walk_decay(const float *dt_l, float *w_l, float a2, bool emit,
-                                            size_t off, float *__restrict__ s_out,
-                                            float *__restrict__ dt_out,
-                                            float *__restrict__ u_out) {
-  constexpr int R = Q >= 64 ? Q / 64 : 1;
+template <int Q>
+__device__ __forceinline__ float walk_decay(const float *dt_l, float *w_l, float a2,
+                                            WalkRows<Q> &rows) {
+  constexpr int R = WalkRows<Q>::R;
   const int lane = threadIdx.x & 63;
-  float d[R], sv[R];
   float run = 0.f;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int i = lane * R + r;
-    d[r] = i < Q ? dt_l[i] : 0.f;
-    run += d[r] * a2;
-    sv[r] = run;
+    rows.dt[r] = i < Q ? dt_l[i] : 0.f;
+    run += rows.dt[r] * a2;
+    rows.s[r] = run;
   }
-  float incl = run;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const float t = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += t;
-  }
+  const float incl = wave_incl_scan(run);
   const float excl = incl - run;
 #pragma unroll
-  for (int r = 0; r < R; ++r) sv[r] += excl;
+  for (int r = 0; r < R; ++r) rows.s[r] += excl;
   // row Q - 1 sits in slot R - 1 of lane (Q - 1) / R; the last row of a lane's
   // 32-row block in slot R - 1 of the block's last lane
-  const float s_end = __shfl(sv[R - 1], (Q - 1) / R, 64);
-  const float s_ref = __shfl(sv[R - 1], lane | (32 / R - 1), 64);
+  const float s_end = __builtin_bit_cast(
+      float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rows.s[R - 1]), (Q - 1) / R));
+  const float s_ref = __shfl(rows.s[R - 1], lane | (32 / R - 1), 64);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int i = lane * R + r;
+    if (i < Q) w_l[i] = __builtin_amdgcn_exp2f(fminf(s_end - rows.s[r], 0.f)) * rows.dt[r];
+    rows.u[r] = __builtin_amdgcn_exp2f(fminf(s_ref - rows.s[r], 0.f)) * rows.dt[r];
+  }
+  return s_end;
+}
+
+template <int Q>
+__device__ __forceinline__ void walk_store_rows(const WalkRows<Q> &rows, size_t off,
+                                                float *__restrict__ s_out,
+                                                float *__restrict__ dt_out,
+                                                float *__restrict__ u_out) {
+  constexpr int R = WalkRows<Q>::R;
+  const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int i = lane * R + r;
     if (i < Q) {
-      if (W) w_l[i] = __builtin_amdgcn_exp2f(fminf(s_end - sv[r], 0.f)) * d[r];
-      if (emit) {
-        s_out[off + i] = sv[r];
-        dt_out[off + i] = d[r];
-        u_out[off + i] = __builtin_amdgcn_exp2f(fminf(s_ref - sv[r], 0.f)) * d[r];
-      }
+      s_out[off + i] = rows.s[r];
+      dt_out[off + i] = rows.dt[r];
+      u_out[off + i] = rows.u[r];
     }
   }
-  return s_end;
 }
 
 // The x rows of phase ph of chunk ci -> a block-swizzled LDS tile (rows past
@@ -294,6 +326,7 @@ __global__ __launch_bounds__(64 * NW_) void k_state_walk(
     const int db = (c - c0) & 1;
     const int4 cnow = cn;  // chunk c + 1
     float s_end = 0.f;
+    WalkRows<Q> rows;
     f4 S[NTW][NPT];
 #pragma unroll
     for (int t = 0; t < NTW; ++t)
@@ -316,9 +349,8 @@ __global__ __launch_bounds__(64 * NW_) void k_state_walk(
       }
       if (ph == 0) {
         // the chunk's decay, in every wave (wave 0 of part 0 writes s, dt, u)
-        s_end = walk_decay<Q, true>(
-            reinterpret_cast<const float *>(smem + K::OFF_DT + db * K::DTN * 4), w_l, a2, false,
-            0, s_out, dt_out, u_out);
+        s_end = walk_decay<Q>(
+            reinterpret_cast<const float *>(smem + K::OFF_DT + db * K::DTN * 4), w_l, a2, rows);
       }
       // S^T += sum over this phase's tokens of x_j (w_j B_j)^T
       const char *xt = smem + xbuf * K::XB;
@@ -360,11 +392,10 @@ __global__ __launch_bounds__(64 * NW_) void k_state_walk(
             if (hin32) st4(hin32 + e, Hs[t][pt]);  // a training forward keeps them in float32
           }
         // s, dt and u for the chunk scan, likewise after the wait (wave 0 of
-        // part 0, from the chunk's dt column, which stays in LDS until the
-        // chunk after next is loaded)
+        // part 0, from the registers the decay left them in: the chunk's dt
+        // column in LDS may already be taking the next chunk's)
         if (part == 0 && wave == 0)
-          walk_decay<Q, false>(reinterpret_cast<const float *>(smem + K::OFF_DT + db * K::DTN * 4),
-                               w_l, a2, true, ((size_t)c * H + hd) * Q, s_out, dt_out, u_out);
+          walk_store_rows<Q>(rows, ((size_t)c * H + hd) * Q, s_out, dt_out, u_out);
       }
 #pragma unroll
       for (int t = 0; t < NTW; ++t)
