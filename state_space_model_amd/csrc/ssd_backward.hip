@@ -85,6 +85,9 @@ template <typename T, int MODE, int KD, int VD> struct BwdScanCfg {
   static constexpr bool SWZ = sizeof(T) == 2 && (MODE == kBwdDX ? (KD == 128 && VD == 64)
                                                                 : (KD == 64 && VD == 128));
   static constexpr size_t s_bytes() { return SWZ ? 16 * kBlk128 : tile_slots(SR, SS) * 16; }
+  // DX in bf16 also stages what the bf16 state dropped (same layout)
+  static constexpr bool LO = MODE == kBwdDX && sizeof(T) == 2;
+  static constexpr size_t lo_bytes() { return LO ? s_bytes() : 0; }
   static constexpr size_t k_bytes(int jp) {
     return SWZ ? (KD == 128 ? (size_t)(jp / 4) * kBlk256 : (size_t)(jp / 8) * kBlk128)
                : (size_t)tile_slots(jp, KSL) * 16;
@@ -95,7 +98,7 @@ template <typename T, int MODE, int KD, int VD> struct BwdScanCfg {
   }
   // + s, dt, u rows; DX also keeps one row of W row sums per wave
   static constexpr size_t lds_bytes(int jp, int q, int nw) {
-    return s_bytes() + k_bytes(jp) + v_bytes(jp) + 12 * (size_t)q +
+    return s_bytes() + lo_bytes() + k_bytes(jp) + v_bytes(jp) + 12 * (size_t)q +
            (MODE == kBwdDX ? 4 * (size_t)nw * q : 0);
   }
   // rows per phase: up to 64 in blocks of at most 512 threads (under 61 KB),
@@ -122,7 +125,7 @@ __global__ __launch_bounds__(MAXT) void k_bwd_scan(
     const T *__restrict__ x, const T *__restrict__ dy, const T *__restrict__ B,
     const T *__restrict__ C, const float *__restrict__ D, const float *__restrict__ s_ws,
     const float *__restrict__ dt_ws, const float *__restrict__ u_ws,
-    const T *__restrict__ state, const bf16 *__restrict__ state_lo, ChunkMap cmap, int nc, int H,
+    const T *__restrict__ state, const T *__restrict__ state_lo, ChunkMap cmap, int nc, int H,
     int G, int Q, int JP, int hb, float *__restrict__ out, int ostride, BwdRows rows) {
   constexpr int KD = MODE == kBwdDX ? N : P;
   constexpr int VD = MODE == kBwdDX ? P : N;
@@ -153,7 +156,8 @@ __global__ __launch_bounds__(MAXT) void k_bwd_scan(
 
   constexpr bool SWZ = K::SWZ;
   extern __shared__ __align__(16) char smem[];
-  char *Sc = smem, *Kc = Sc + K::s_bytes(), *Vc = Kc + K::k_bytes(JP);
+  char *Sc = smem, *Slo = Sc + K::s_bytes(), *Kc = Slo + K::lo_bytes(),
+       *Vc = Kc + K::k_bytes(JP);
   T *Ss = reinterpret_cast<T *>(Sc);  // padded: state [SR][SP]
   T *Ks = reinterpret_cast<T *>(Kc);  //         K rows [JP][KP]
   T *Vs = reinterpret_cast<T *>(Vc);  //         V rows [JP][VP]
@@ -224,11 +228,17 @@ __global__ __launch_bounds__(MAXT) void k_bwd_scan(
       const int v0 = min(len, JP);
       dma_swz<kBlk128>(Sc, state + csh * (size_t)(N * P), N * P * 2, sl, 1024, N * P * 2 / 1024,
                        wave, nw);
+      if constexpr (K::LO)
+        dma_swz<kBlk128>(Slo, state_lo + csh * (size_t)(N * P), N * P * 2, sl, 1024,
+                         N * P * 2 / 1024, wave, nw);
       load_k(kg, v0);
       load_v(vg, v0);
     } else {
       dma_tile<T, K::SS, K::SD>(Ss, state + csh * (size_t)(N * P), (size_t)P, K::SR,
                                 K::ST_ROWS ? VD : KD, wave, nw);
+      if constexpr (K::LO)
+        dma_tile<T, K::SS, K::SD>(reinterpret_cast<T *>(Slo), state_lo + csh * (size_t)(N * P),
+                                  (size_t)P, K::SR, KD, wave, nw);
       dma_tile<T, K::KSL, K::KDS>(Ks, kg, ks_, JP, len, wave, nw);
       dma_tile<T, K::VSL, K::VDS>(Vs, vg, vs, JP, len, wave, nw);
     }
@@ -291,16 +301,15 @@ __global__ __launch_bounds__(MAXT) void k_bwd_scan(
           else
             a = frag_kmaj(Ss, K::SP, vt * 16, kk * 32 + 8 * grp, kk * 32 + 8 * grp + 4);
           mma(st, a, qf[kk]);
-          if constexpr (MODE == kBwdDX && sizeof(T) == 2) {
-            // the part of dH_c that its bfloat16 copy rounds away, in fragment
-            // order [N/8][P][8] (one 16-byte read per lane)
-            const int n8 = kk * 4 + grp;
-            if (state_lo && 8 * n8 < KD) {
-              Frag<T> lo;
-              lo.v = *reinterpret_cast<const bf16x8 *>(
-                  state_lo + csh * (size_t)(N * P) + ((size_t)n8 * P + vt * 16 + col) * 8);
-              mma(st, lo, qf[kk]);
-            }
+          if constexpr (K::LO) {
+            // what the bf16 copy of dH_c rounded away, from its own tile
+            Frag<T> lo;
+            if constexpr (SWZ)
+              lo = frag_kmaj_at(Slo + kk * 4 * kBlk128, so_lo ^ (32 * vt), so_hi ^ (32 * vt));
+            else
+              lo = frag_kmaj(reinterpret_cast<const T *>(Slo), K::SP, vt * 16,
+                             kk * 32 + 8 * grp, kk * 32 + 8 * grp + 4);
+            mma(st, lo, qf[kk]);
           }
         }
         f4 w4 = zero4();
@@ -535,8 +544,8 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_state_pass_bwd(
     const float *__restrict__ Sb, const float *__restrict__ s_ws, const int *__restrict__ seq_off,
     ChunkMap cmap, const float *__restrict__ dh_out, const float *__restrict__ hfin,
-    const float *__restrict__ hin32, T *__restrict__ dHc, bf16 *__restrict__ dHlo,
-    float *__restrict__ epart, float *__restrict__ dh0, int H, int NP, int Q, int P) {
+    const float *__restrict__ hin32, T *__restrict__ dHc, T *__restrict__ dHlo,
+    float *__restrict__ epart, float *__restrict__ dh0, int H, int NP, int Q) {
   constexpr int BATCH = 8;
   const int s = blockIdx.z, hd = blockIdx.y;
   const int tid = blockIdx.x * blockDim.x + threadIdx.x;
@@ -578,13 +587,9 @@ __global__ __launch_bounds__(256) void k_state_pass_bwd(
         d += dpp_mov<0x140>(d);  // lane i with 15 - i
         if (lane16 == 0) epart[ch * npr + rid] = d;
         st4T(dHc + ch * NP + e, gv);
-        if (dHlo) {  // bfloat16: what the rounding to dHc dropped, in fragment order
+        if (dHlo) {  // bfloat16: what the rounding to dHc dropped, in dHc's layout
           const f4 hi = __builtin_convertvector(__builtin_convertvector(gv, bf16x4), f4);
-          const f4 lo = gv - hi;
-          const int n = e / P, p = e - (e / P) * P;
-          bf16 *dst = dHlo + ch * NP + ((size_t)(n >> 3) * P + p) * 8 + (n & 7);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) dst[8 * q] = (bf16)lo[q];
+          st4T(dHlo + ch * NP + e, gv - hi);
         }
         const float a = __builtin_amdgcn_exp2f(fminf(sl[u], 0.f));
 #pragma unroll
@@ -772,7 +777,7 @@ static BwdRows bwd_rows(char *ws, const BwdLayout &L, int nc, int H, int Q) {
 
 template <typename T, int MODE, int P, int N>
 static hipError_t launch_bwd_scan(const BwdArgs &a, const BwdLayout &L, int nc, const T *state,
-                                  const bf16 *state_lo, float *out, int ostride, int hb,
+                                  const T *state_lo, float *out, int ostride, int hb,
                                   hipStream_t st) {
   constexpr int KD = MODE == kBwdDX ? N : P, VD = MODE == kBwdDX ? P : N;
   typedef BwdScanCfg<T, MODE, KD, VD> K;
@@ -826,7 +831,7 @@ static hipError_t run_backward(const BwdArgs &a) {
   float *hfin = reinterpret_cast<float *>(ws + L.hfin);
   float *hin32 = reinterpret_cast<float *>(ws + L.hin32);
   T *dHc = reinterpret_cast<T *>(ws + L.dHc);
-  bf16 *dHlo = sizeof(T) == 2 ? reinterpret_cast<bf16 *>(ws + L.dHlo) : nullptr;
+  T *dHlo = sizeof(T) == 2 ? reinterpret_cast<T *>(ws + L.dHlo) : nullptr;
   T *hin = reinterpret_cast<T *>(ws + L.fwd.hin);
   float *S = reinterpret_cast<float *>(ws + L.fwd.S);
   float *epart = reinterpret_cast<float *>(ws + L.epart);
@@ -858,7 +863,7 @@ static hipError_t run_backward(const BwdArgs &a) {
   hipLaunchKernelGGL(k_state_pass_bwd<T>, dim3((NP + 1023) / 1024, f.H, f.nseq), dim3(256), 0, st,
                      S, reinterpret_cast<const float *>(ws + L.fwd.s),
                      reinterpret_cast<const int *>(ws + L.fwd.seq_off), cmap, a.dh_out, hfin,
-                     hin32, dHc, dHlo, epart, a.dh0, f.H, NP, f.Q, P);
+                     hin32, dHc, dHlo, epart, a.dh0, f.H, NP, f.Q);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int hb = bwd_heads_per_block(nc, f.H, f.G, f.Q);

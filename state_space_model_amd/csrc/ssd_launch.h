@@ -23,9 +23,9 @@ struct PrefillArgs {
   float *h_out2 = nullptr;  // optional second destination of the final state
   unsigned variant = 0;     // SSD_VARIANT_* bits (0: the library's choice by size)
   bool scan_follows = true; // false: no chunk scan reads this workspace (skip C.B^T)
-  // bf16: chunk states from the decay-weighted x split into two bf16 operands
-  // (its rounded value and the rounding's remainder), on the chunk-state path;
-  // the training forward and the backward's recompute, whose gradients
+  // bf16: chunk states from the decay-weighted operand split into two bf16
+  // operands (its rounded value and the rounding's remainder), in either state
+  // kernel; the training forward and the backward's recompute, whose gradients
   // amplify the states' rounding
   bool precise_states = false;
 };
@@ -100,7 +100,7 @@ struct BwdLayout {
   size_t hfin;    // f32 [nseq][H][N][P]  final states (the forward recompute)
   size_t hin32;   // f32 [nc][H][N][P]    state entering each chunk, float32
   size_t dHc;     // T   [nc][H][N][P]    dL/d(state leaving chunk c)
-  size_t dHlo;    // bf16 [nc][H][N/8][P][8]  dL/d(state) - dHc, bfloat16 only (DX scan)
+  size_t dHlo;    // bf16 [nc][H][N][P]    dL/d(state) - dHc, bfloat16 only (DX scan)
   size_t epart;   // f32 [nc][H][NP/64]   16-lane-row partials of <dH_c, H_c>
   size_t rows;             // f32 6 x [nc][H][Q]  per-row terms of dz (q, cv, r, dyx, rs x 2)
   size_t dApart, dDpart;   // f32 [nc][H]

@@ -610,8 +610,8 @@ static hipError_t run_prefill(const PrefillArgs &a, unsigned stages) {
   hipStream_t st = static_cast<hipStream_t>(a.stream);
 
   // the state walk does stages 1, 2 and 4 in one kernel
-  const bool walk = nc > 0 && !a.precise_states &&
-                    walk_choice(P, N, a.Q, a.bf16, a.nseq, a.H, a.cu != nullptr, a.variant);
+  const bool walk =
+      nc > 0 && walk_choice(P, N, a.Q, a.bf16, a.nseq, a.H, a.cu != nullptr, a.variant);
   if ((stages & (walk ? 7u : 3u)) && (a.cu || L_dense == 0)) {
     // packed (or empty) batch: chunk map first.  Block 0 also writes the first
     // chunk of every sequence, which the state pass reads even when there are

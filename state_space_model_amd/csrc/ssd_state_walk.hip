@@ -249,7 +249,7 @@ __device__ __forceinline__ void walk_load_b(const bf16 *bc, int ph,
           bc + (size_t)((ph * K::KSP + k) * NTL + t) * 512);
 }
 
-template <int Q, int NH, int JP_, int NW_, bool DENSE>
+template <int Q, int NH, int JP_, int NW_, bool DENSE, bool PREC>
 __global__ __launch_bounds__(64 * NW_) void k_state_walk(
     const bf16 *__restrict__ x, const float *__restrict__ dt, const float *__restrict__ A,
     const bf16 *__restrict__ bfr, const int *__restrict__ seq_off, ChunkMap cmap, int H, int G,
@@ -363,17 +363,23 @@ __global__ __launch_bounds__(64 * NW_) void k_state_walk(
         for (int pt = 0; pt < NPT; ++pt)
           xa[pt] = frag_kmaj_at(xk, xo ^ (32 * pt), (xo ^ (32 * pt)) + 2 * kBlk128);
         const f4 w0 = ld4(w_l + j0 + 4 * grp), w1 = ld4(w_l + j0 + 16 + 4 * grp);
-        Frag<bf16> bw[NTW];
+        Frag<bf16> bw[NTW], bl[NTW];
 #pragma unroll
         for (int t = 0; t < NTW; ++t) {
           const f8v bv = cvt_f8(bcur[t][k]);
-          bw[t].v = cvt_bf8(f8v{bv[0] * w0[0], bv[1] * w0[1], bv[2] * w0[2], bv[3] * w0[3],
-                                bv[4] * w1[0], bv[5] * w1[1], bv[6] * w1[2], bv[7] * w1[3]});
+          const f8v wb = f8v{bv[0] * w0[0], bv[1] * w0[1], bv[2] * w0[2], bv[3] * w0[3],
+                             bv[4] * w1[0], bv[5] * w1[1], bv[6] * w1[2], bv[7] * w1[3]};
+          bw[t].v = cvt_bf8(wb);
+          // PREC: also what the rounding dropped, as a second operand
+          if constexpr (PREC) bl[t].v = cvt_bf8(wb - cvt_f8(bw[t].v));
         }
 #pragma unroll
         for (int pt = 0; pt < NPT; ++pt)
 #pragma unroll
-          for (int t = 0; t < NTW; ++t) mma(S[t][pt], xa[pt], bw[t]);
+          for (int t = 0; t < NTW; ++t) {
+            mma(S[t][pt], xa[pt], bw[t]);
+            if constexpr (PREC) mma(S[t][pt], xa[pt], bl[t]);
+          }
       }
       // the next phase's loads have landed and this phase's buffers are free
       __builtin_amdgcn_s_waitcnt(0);
@@ -453,8 +459,12 @@ template <int Q, int NH, int JP, int NW>
 static hipError_t run_walk(const PrefillArgs &a, const WorkspaceLayout &L, bool write_hout,
                            hipStream_t st) {
   typedef WalkCfg<Q, NH, JP, NW> K;
-  const void *kern = a.cu ? (const void *)k_state_walk<Q, NH, JP, NW, false>
-                          : (const void *)k_state_walk<Q, NH, JP, NW, true>;
+  const void *kern =
+      a.precise_states
+          ? (a.cu ? (const void *)k_state_walk<Q, NH, JP, NW, false, true>
+                  : (const void *)k_state_walk<Q, NH, JP, NW, true, true>)
+          : (a.cu ? (const void *)k_state_walk<Q, NH, JP, NW, false, false>
+                  : (const void *)k_state_walk<Q, NH, JP, NW, true, false>);
   hipError_t e = set_lds_limit(kern);
   if (e != hipSuccess) return e;
   char *ws = static_cast<char *>(a.workspace);

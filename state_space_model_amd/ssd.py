@@ -302,7 +302,9 @@ class TrainSaved:
 
 def prefill_train(x, dt, A, B, C, D, h0=None, chunk=256, cu_seqlens=None, *, nseq=None,
                   y=None, h_out=None, prepare=False):
-    """The forward of a training step: (y, h_out) bitwise as ``prefill``, plus
+    """The forward of a training step: (y, h_out) as ``prefill`` computes them
+    (bitwise in float32; in bfloat16 the chunk states are formed in split
+    precision for the backward, so they are closer to the exact values), plus
     a ``TrainSaved`` that lets ``prefill_backward`` skip its forward
     recompute.  Packed [T,...] layout as ``prefill_backward``.  With
     ``prepare=True`` nothing runs and (Prepared, y, h_out, saved) is returned."""
