@@ -785,7 +785,7 @@ KERNEL_NAMES = {  # kernel symbol fragment -> bench kernel name (first match win
     "k_gdn_walk": "gdn_chunk_walk", "k_gdn": "gated_delta_rule",
     "k_chunk_state": "chunk_state", "k_state_pass": "state_pass", "k_chunk_scan": "chunk_scan",
     "k_chunk_map": "chunk_map", "k_step": "decode_step", "k_state_walk": "state_walk",
-    "k_bfrag": "b_frag",
+    "k_bfrag": "b_frag", "k_walk_fixup": "walk_fixup",
 }
 BWD_SCAN_MODES = {"0": "bwd_scan_dx", "1": "bwd_scan_db", "2": "bwd_scan_dc"}
 # one profiled bench run per section: its workload name and its command's bench arguments

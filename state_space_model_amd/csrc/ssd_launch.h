@@ -50,6 +50,9 @@ struct WorkspaceLayout {
   // [nc_max][G][Q/32][N/16][64 lanes][8] bf16 (bf16 with P 64, N 128)
   size_t bfrag;
   bool has_bfrag;
+  // the state walk writes no chunk states; walking a sequence in segments, it
+  // keeps each segment's end state f32 [nseq][nseg][H][N][P] in the S region
+  size_t segend;
   size_t total;
 };
 

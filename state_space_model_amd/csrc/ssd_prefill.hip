@@ -576,6 +576,7 @@ WorkspaceLayout prefill_layout(int64_t T, int nseq, int H, int P, int N, int G, 
   L.bfrag = off;
   L.has_bfrag = walk_supported(P, N, Q, elem == 2);
   if (L.has_bfrag) off = align_up(off + (size_t)nc * G * Q * N * 2, 256);
+  L.segend = L.S;  // at most 2 segments of sequences of at least 8 chunks: fits
   L.total = off;
   return L;
 }

@@ -255,7 +255,7 @@ __global__ __launch_bounds__(64 * NW_) void k_state_walk(
     const bf16 *__restrict__ bfr, const int *__restrict__ seq_off, ChunkMap cmap, int H, int G,
     int nchain, const float *h0, float *h_out, float *__restrict__ s_out,
     float *__restrict__ dt_out, float *__restrict__ u_out, bf16 *__restrict__ hin,
-    float *__restrict__ hin32, float *h_out2) {
+    float *__restrict__ hin32, float *h_out2, int nseg, float *__restrict__ seg_end) {
   typedef WalkCfg<Q, NH, JP_, NW_> K;
   constexpr int P = K::P, N = K::N, NTW = K::NTW, NPT = P / 16, KSP = K::KSP, NPH = K::NPH;
   constexpr int NTL = N / 16, JP = K::JP;
@@ -264,8 +264,11 @@ __global__ __launch_bounds__(64 * NW_) void k_state_walk(
   const int per = (nchain + 7) >> 3;
   const int chn = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
   if (chn >= nchain) return;
-  const int part = chn % NH, sh = chn / NH;
-  const int hd = __builtin_amdgcn_readfirstlane(sh % H), s = __builtin_amdgcn_readfirstlane(sh / H);
+  // chain = (sequence, segment, head, part), part fastest
+  const int part = chn % NH, sgh = chn / NH;
+  const int hd = __builtin_amdgcn_readfirstlane(sgh % H);
+  const int seg = __builtin_amdgcn_readfirstlane((sgh / H) % nseg);
+  const int s = __builtin_amdgcn_readfirstlane(sgh / H / nseg);
   int c0, c1;  // chunks of sequence s
   if constexpr (DENSE) {
     const int cps = (cmap.L + Q - 1) / Q;
@@ -274,6 +277,12 @@ __global__ __launch_bounds__(64 * NW_) void k_state_walk(
   } else {
     c0 = __builtin_amdgcn_readfirstlane(seq_off[s]);
     c1 = __builtin_amdgcn_readfirstlane(seq_off[s + 1]);
+  }
+  {  // this chain's segment of them: segments after the first start from zero
+    const int nchk = c1 - c0;
+    const int a0 = c0 + (seg * nchk) / nseg, a1 = c0 + ((seg + 1) * nchk) / nseg;
+    c0 = a0;
+    c1 = a1;
   }
   const int g = (hd * G) / H;
   const int lane = threadIdx.x & 63, grp = lane >> 4, col = lane & 15;
@@ -291,8 +300,9 @@ __global__ __launch_bounds__(64 * NW_) void k_state_walk(
   for (int t = 0; t < NTW; ++t)
 #pragma unroll
     for (int pt = 0; pt < NPT; ++pt)
-      Hs[t][pt] = h0 ? ld4(h0 + hofs + (size_t)(16 * (nt0 + t) + col) * P + 16 * pt + 4 * grp)
-                     : zero4();
+      Hs[t][pt] = (h0 && seg == 0)
+                      ? ld4(h0 + hofs + (size_t)(16 * (nt0 + t) + col) * P + 16 * pt + 4 * grp)
+                      : zero4();
 
   const size_t xstride = (size_t)H * P;
   const int lb8 = lane >> 3;
@@ -418,14 +428,66 @@ __global__ __launch_bounds__(64 * NW_) void k_state_walk(
 #pragma unroll
         for (int q = 0; q < 4; ++q) Hs[t][pt][q] = a * Hs[t][pt][q] + S[t][pt][q];
   }
+  // the state leaving the chain: the final state, or with several segments the
+  // segment's own end state (from its own entering state) for k_walk_fixup
 #pragma unroll
   for (int t = 0; t < NTW; ++t)
 #pragma unroll
     for (int pt = 0; pt < NPT; ++pt) {
-      const size_t e = hofs + (size_t)(16 * (nt0 + t) + col) * P + 16 * pt + 4 * grp;
-      if (h_out) st4(h_out + e, Hs[t][pt]);
-      if (h_out2) st4(h_out2 + e, Hs[t][pt]);
+      const size_t e = (size_t)(16 * (nt0 + t) + col) * P + 16 * pt + 4 * grp;
+      if (nseg > 1) {
+        st4(seg_end + (((size_t)s * nseg + seg) * H + hd) * (size_t)(N * P) + e, Hs[t][pt]);
+      } else {
+        if (h_out) st4(h_out + hofs + e, Hs[t][pt]);
+        if (h_out2) st4(h_out2 + hofs + e, Hs[t][pt]);
+      }
     }
+}
+
+// The entering states of a sequence walked in nseg segments, each after the
+// first walked from a zero state: the recurrence is linear in the entering
+// state, so segment k's true entering states are those walked plus
+// (product of the decays of its chunks so far) E_k, with E_1 = the first
+// segment's end state (walked from h0) and E_(k+1) = (segment k's total decay)
+// E_k + segment k's own end state.  One thread per 4 state elements of a
+// (sequence, head), walking the segments and their chunks in order; the last
+// E is the final state.  The corrected H_in is rounded to bf16 again.
+__global__ __launch_bounds__(256) void k_walk_fixup(const float *__restrict__ s_ws,
+                                                    const int *__restrict__ seq_off, ChunkMap cmap,
+                                                    int H, int NP, int Q, int nseg,
+                                                    const float *__restrict__ seg_end,
+                                                    bf16 *__restrict__ hin, float *h_out,
+                                                    float *h_out2) {
+  const int s = blockIdx.z, hd = blockIdx.y;
+  const int e = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (e >= NP) return;
+  int c0, c1;
+  if (cmap.L > 0) {
+    const int cps = (cmap.L + Q - 1) / Q;
+    c0 = s * cps;
+    c1 = c0 + cps;
+  } else {
+    c0 = seq_off[s];
+    c1 = seq_off[s + 1];
+  }
+  const int nchk = c1 - c0;
+  f4 E = ld4(seg_end + ((size_t)s * nseg * H + hd) * (size_t)NP + e);  // segment 0, from h0
+  for (int k = 1; k < nseg; ++k) {
+    const int a0 = c0 + (k * nchk) / nseg, a1 = c0 + ((k + 1) * nchk) / nseg;
+    float dec = 1.f;  // 2^(sum of s_end over the segment's chunks so far)
+    for (int c = a0; c < a1; ++c) {
+      const size_t ch = (size_t)c * H + hd;
+      bf16 *hp = hin + ch * (size_t)NP + e;
+      const f4 hv = ld4f(hp);
+      st4T(hp, hv + dec * E);
+      dec *= __builtin_amdgcn_exp2f(fminf(s_ws[ch * Q + Q - 1], 0.f));
+    }
+    const f4 own = ld4(seg_end + (((size_t)s * nseg + k) * H + hd) * (size_t)NP + e);
+    E = dec * E + own;
+  }
+  const size_t hofs = ((size_t)s * H + hd) * (size_t)NP + e;
+  if (h_out) st4(h_out + hofs, E);
+  if (h_out2) st4(h_out2 + hofs, E);
 }
 
 // ------------------------------------------------------------------ launch
@@ -457,7 +519,7 @@ bool walk_choice(int P, int N, int Q, bool bf16, int nseq, int H, bool packed, u
 
 template <int Q, int NH, int JP, int NW>
 static hipError_t run_walk(const PrefillArgs &a, const WorkspaceLayout &L, bool write_hout,
-                           hipStream_t st) {
+                           int nseg, hipStream_t st) {
   typedef WalkCfg<Q, NH, JP, NW> K;
   const void *kern =
       a.precise_states
@@ -474,7 +536,8 @@ static hipError_t run_walk(const PrefillArgs &a, const WorkspaceLayout &L, bool 
   const int *so = reinterpret_cast<const int *>(ws + L.seq_off);
   ChunkMap cm{reinterpret_cast<const int4 *>(ws + L.info), a.cu ? 0 : (int)(a.T / a.nseq), a.nseq,
               a.Q};
-  int H_ = a.H, G_ = a.G, nch = a.nseq * a.H * NH;
+  int H_ = a.H, G_ = a.G, nch = a.nseq * a.H * NH * nseg, nseg_ = nseg;
+  float *se = reinterpret_cast<float *>(ws + L.segend);
   const float *h0p = a.h0;
   float *hop = write_hout ? a.h_out : nullptr, *hop2 = write_hout ? a.h_out2 : nullptr;
   float *sp = reinterpret_cast<float *>(ws + L.s), *dp = reinterpret_cast<float *>(ws + L.dt);
@@ -482,29 +545,66 @@ static hipError_t run_walk(const PrefillArgs &a, const WorkspaceLayout &L, bool 
   bf16 *hp = reinterpret_cast<bf16 *>(ws + L.hin);
   float *h32 = a.hin32;
   void *args[] = {&xp, &dtp, &Ap, &bp, &so, &cm, &H_, &G_, &nch, &h0p, &hop, &sp, &dp, &up, &hp,
-                  &h32, &hop2};
+                  &h32, &hop2, &nseg_, &se};
   const unsigned grid = 8u * (unsigned)((nch + 7) / 8);
   return hipLaunchKernel(kern, dim3(grid), dim3(64 * K::NW), args, K::LDS, st);
 }
 
+// Segments per sequence: two when the doubled chain count still runs in one
+// round of the 8-wave shape (three 47 KB workgroups per CU) and sequences
+// average at least 8 chunks, so that halving the chain outweighs the fix-up's
+// pass over the second segments' entering states; one for the training
+// forward, whose float32 entering states would need the fix-up too.
+int walk_segments(int nseq, int H, int64_t T, int Q, int nc, bool packed, bool training) {
+  if (training || nseq <= 0) return 1;
+  if (2L * nseq * H > 3L * 256) return 1;
+  const int64_t cps = packed ? nc / nseq : (T / nseq + Q - 1) / Q;
+  return cps >= 8 ? 2 : 1;
+}
+
+#ifndef SSD_WALK_SEG_NW
+#define SSD_WALK_SEG_NW 8
+#endif
+#ifndef SSD_WALK_SEG_JP
+#define SSD_WALK_SEG_JP 128
+#endif
+
+template <int Q>
+static hipError_t run_walk_q(const PrefillArgs &a, const WorkspaceLayout &L, bool write_hout,
+                             int nseg, hipStream_t st) {
+  if (nseg > 1) return run_walk<Q, 1, SSD_WALK_SEG_JP, SSD_WALK_SEG_NW>(a, L, write_hout, nseg, st);
+  return run_walk<Q, SSD_WALK_NH, SSD_WALK_JP, SSD_WALK_NW>(a, L, write_hout, 1, st);
+}
+
 hipError_t launch_state_walk(const PrefillArgs &a, const WorkspaceLayout &L, int nc,
                              bool write_hout, hipStream_t st) {
+  char *ws = static_cast<char *>(a.workspace);
+  const ChunkMap cm{reinterpret_cast<const int4 *>(ws + L.info), a.cu ? 0 : (int)(a.T / a.nseq),
+                    a.nseq, a.Q};
   if (nc > 0) {
-    ChunkMap cm{reinterpret_cast<const int4 *>(static_cast<char *>(a.workspace) + L.info),
-                a.cu ? 0 : (int)(a.T / a.nseq), a.nseq, a.Q};
     hipLaunchKernelGGL(k_bfrag, dim3((unsigned)nc * a.G * (a.Q / 32)), dim3(256), 0, st,
-                       (const bf16 *)a.B, cm, nc, a.G, a.Q,
-                       reinterpret_cast<bf16 *>(static_cast<char *>(a.workspace) + L.bfrag));
+                       (const bf16 *)a.B, cm, nc, a.G, a.Q, reinterpret_cast<bf16 *>(ws + L.bfrag));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  const int nseg =
+      walk_segments(a.nseq, a.H, a.T, a.Q, nc, a.cu != nullptr, a.hin32 != nullptr);
+  hipError_t e = hipErrorInvalidValue;
   switch (a.Q) {
-    case 32: return run_walk<32, SSD_WALK_NH, SSD_WALK_JP, SSD_WALK_NW>(a, L, write_hout, st);
-    case 64: return run_walk<64, SSD_WALK_NH, SSD_WALK_JP, SSD_WALK_NW>(a, L, write_hout, st);
-    case 128: return run_walk<128, SSD_WALK_NH, SSD_WALK_JP, SSD_WALK_NW>(a, L, write_hout, st);
-    case 256: return run_walk<256, SSD_WALK_NH, SSD_WALK_JP, SSD_WALK_NW>(a, L, write_hout, st);
+    case 32: e = run_walk_q<32>(a, L, write_hout, nseg, st); break;
+    case 64: e = run_walk_q<64>(a, L, write_hout, nseg, st); break;
+    case 128: e = run_walk_q<128>(a, L, write_hout, nseg, st); break;
+    case 256: e = run_walk_q<256>(a, L, write_hout, nseg, st); break;
   }
-  return hipErrorInvalidValue;
+  if (e != hipSuccess || nseg == 1) return e;
+  const int NP = 128 * 64;
+  hipLaunchKernelGGL(k_walk_fixup, dim3((NP + 1023) / 1024, a.H, a.nseq), dim3(256), 0, st,
+                     reinterpret_cast<const float *>(ws + L.s),
+                     reinterpret_cast<const int *>(ws + L.seq_off), cm, a.H, NP, a.Q, nseg,
+                     reinterpret_cast<const float *>(ws + L.segend),
+                     reinterpret_cast<bf16 *>(ws + L.hin), write_hout ? a.h_out : nullptr,
+                     write_hout ? a.h_out2 : nullptr);
+  return hipGetLastError();
 }
 
 }  // namespace ssd
