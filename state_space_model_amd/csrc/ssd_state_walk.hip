@@ -318,13 +318,16 @@ __global__ __launch_bounds__(64 * NW_) void k_state_walk(
   const float a2 = A[hd] * kLog2e;
 
   typedef bf16x8 BF[NTW][KSP];
-  BF bcur;
+  // B fragments of the current phase and of the next one, in alternating
+  // register sets (phase ph computes from bq[ph & 1]), so none are copied
+  // when a chunk has an even number of phases
+  BF bq[2];
   int4 cn = make_int4(0, 0, 0, 0);  // the next chunk's map entry, read a chunk ahead
   if (c0 < c1) {
     const int4 ci = walk_map<DENSE>(cmap, c0);
     walk_issue_dt<K>(dt, ci, H, hd, lds0 + K::OFF_DT, wave);
     walk_issue_x<K>(x, ci, 0, xstride, hd, xl, smem, wave);
-    walk_load_b<K>(bfw + (size_t)c0 * bfc, 0, bcur);
+    walk_load_b<K>(bfw + (size_t)c0 * bfc, 0, bq[0]);
     if (c0 + 1 < c1) cn = walk_map<DENSE>(cmap, c0 + 1);
   }
   __builtin_amdgcn_s_waitcnt(0);
@@ -347,14 +350,13 @@ __global__ __launch_bounds__(64 * NW_) void k_state_walk(
       // the next phase's loads first (this chunk's next rows, or the next
       // chunk's first rows and its dt column), so nothing issued later in the
       // phase stands before them
-      BF bnext;
       if (ph + 1 < NPH) {
         walk_issue_x<K>(x, ci, ph + 1, xstride, hd, xl, smem + (xbuf ^ 1) * K::XB, wave);
-        walk_load_b<K>(bfw + (size_t)(c) * bfc, ph + 1, bnext);
+        walk_load_b<K>(bfw + (size_t)(c) * bfc, ph + 1, bq[(ph + 1) & 1]);
       } else if (c + 1 < c1) {
         walk_issue_x<K>(x, cnow, 0, xstride, hd, xl, smem + (xbuf ^ 1) * K::XB, wave);
         walk_issue_dt<K>(dt, cnow, H, hd, lds0 + K::OFF_DT + (db ^ 1) * K::DTN * 4, wave);
-        walk_load_b<K>(bfw + (size_t)(c + 1) * bfc, 0, bnext);
+        walk_load_b<K>(bfw + (size_t)(c + 1) * bfc, 0, bq[(ph + 1) & 1]);
         if (c + 2 < c1) cn = walk_map<DENSE>(cmap, c + 2);
       }
       if (ph == 0) {
@@ -376,7 +378,7 @@ __global__ __launch_bounds__(64 * NW_) void k_state_walk(
         Frag<bf16> bw[NTW], bl[NTW];
 #pragma unroll
         for (int t = 0; t < NTW; ++t) {
-          const f8v bv = cvt_f8(bcur[t][k]);
+          const f8v bv = cvt_f8(bq[ph & 1][t][k]);
           const f8v wb = f8v{bv[0] * w0[0], bv[1] * w0[1], bv[2] * w0[2], bv[3] * w0[3],
                              bv[4] * w1[0], bv[5] * w1[1], bv[6] * w1[2], bv[7] * w1[3]};
           bw[t].v = cvt_bf8(wb);
@@ -413,10 +415,14 @@ __global__ __launch_bounds__(64 * NW_) void k_state_walk(
         if (part == 0 && wave == 0)
           walk_store_rows<Q>(rows, ((size_t)c * H + hd) * Q, s_out, dt_out, u_out);
       }
+      if constexpr (NPH % 2 == 1) {  // the next chunk's first phase starts from bq[0]
+        if (ph == NPH - 1) {
 #pragma unroll
-      for (int t = 0; t < NTW; ++t)
+          for (int t = 0; t < NTW; ++t)
 #pragma unroll
-        for (int k = 0; k < KSP; ++k) bcur[t][k] = bnext[t][k];
+            for (int k = 0; k < KSP; ++k) bq[0][t][k] = bq[1][t][k];
+        }
+      }
       xbuf ^= 1;
     }
     // carry: H = 2^(s_end) H + S
