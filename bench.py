@@ -801,6 +801,16 @@ PROFILED = {
 }
 
 
+PIPE_COUNTERS = (
+    ("SQ_WAVE_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY",
+     "SQ_ACTIVE_INST_VALU", "SQ_VMEM_TA_ADDR_FIFO_FULL", "SQ_VALU_MFMA_BUSY_CYCLES"),
+    ("TA_BUSY_avr", "TA_ADDR_STALLED_BY_TC_CYCLES_sum", "TCP_PENDING_STALL_CYCLES_sum",
+     "TCP_TCC_READ_REQ_LATENCY_sum", "TCP_TCC_READ_REQ_sum", "GRBM_GUI_ACTIVE"),
+    ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_VMEM_RD", "SQ_INSTS_VMEM_WR",
+     "SQ_WAVES", "TCC_HIT_sum", "TCC_MISS_sum"),
+)
+
+
 def _kernel_key(name):
     for frag, k in KERNEL_NAMES.items():
         if frag in name:
@@ -833,6 +843,12 @@ def profile_commands():
         cmds[f"{sec}_write"] = f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/{sec}_write -o run {base}"
         cmds[f"{sec}_mfma"] = ("rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 --output-format csv "
                                f"-d DIR/{sec}_mfma -o run {base}")
+    # where the headline's kernels wait: SQ issue and wait states, the vector
+    # memory path (TA address FIFO, L1 pending on L2, L2 read latency), L2 hits
+    hb = f"-- python bench.py {PROFILED['headline'][1]}"
+    for i, cs in enumerate(PIPE_COUNTERS):
+        cmds[f"headline_pipe{i + 1}"] = (f"rocprofv3 --pmc {' '.join(cs)} --output-format csv "
+                                         f"-d DIR/headline_pipe{i + 1} -o run {hb}")
     cmds["train_trace"] = ("rocprofv3 --kernel-trace --stats --output-format csv -d DIR/train_trace "
                            "-o run -- python bench.py --train-only --steps 50 --warmup 5 --quiet")
     cmds["cfetch"] = ("rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/cfetch -o run -- "
@@ -929,6 +945,7 @@ def summarize(directory):
                        os.path.join(ROOT, "profiles", f"kernel_trace_{sec}_{wl}.txt"),
                        f"rocprofv3 kernel trace, workload {wl}\n{stamp}command (cwd = repository "
                        f"root):\n  {cmds[sec + '_trace']}\n")
+    _pipeline_summary(directory, cmds, pmc, stamp)
     _trace_summary(glob.glob(os.path.join(directory, "train_trace", "**", "*kernel_stats.csv"),
                              recursive=True),
                    os.path.join(ROOT, "profiles", "kernel_trace_train_mamba2-130m-layer.txt"),
@@ -938,6 +955,50 @@ def summarize(directory):
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(traffic, f, indent=1)
     print(json.dumps(traffic, indent=1))
+
+
+def _pipeline_summary(directory, cmds, pmc, stamp):
+    """profiles/memory_pipeline_headline_<workload>.txt from the headline_pipe*
+    counter runs: per kernel, fractions of wave time and of the kernel's
+    duration per XCD, and the L1's average wait for L2 reads."""
+    wl = PROFILED["headline"][0]
+    vals = {}
+    for i, cs in enumerate(PIPE_COUNTERS):
+        for c in cs:
+            for kname, vs in pmc(f"headline_pipe{i + 1}", c).items():
+                k = _kernel_key(kname)
+                if k is not None:
+                    vals.setdefault(k, {})[c] = float(np.mean(vs))
+    if not vals:
+        return
+    lines = []
+    for k, v in sorted(vals.items()):
+        wc = v.get("SQ_WAVE_CYCLES") or 0.0
+        xcd_cycles = (v.get("GRBM_GUI_ACTIVE") or 0.0) / 8.0  # summed over the 8 XCDs
+        f = lambda c: v.get(c, 0.0) / wc if wc else float("nan")
+        per_cu = lambda c: v.get(c, 0.0) / 256.0 / xcd_cycles if xcd_cycles else float("nan")
+        lat = (v.get("TCP_TCC_READ_REQ_LATENCY_sum", 0.0) / v["TCP_TCC_READ_REQ_sum"]
+               if v.get("TCP_TCC_READ_REQ_sum") else float("nan"))
+        hit = v.get("TCC_HIT_sum", 0.0) / max(1.0, v.get("TCC_HIT_sum", 0.0) + v.get("TCC_MISS_sum", 0.0))
+        waves = max(1.0, v.get("SQ_WAVES", 1.0))
+        lines.append(
+            f"{k:14s} wave time: waiting {f('SQ_WAIT_ANY'):.2f}  issue-blocked {f('SQ_WAIT_INST_ANY'):.2f}"
+            f"  issuing {f('SQ_ACTIVE_INST_ANY'):.2f} (VALU {f('SQ_ACTIVE_INST_VALU'):.2f}, MFMA busy "
+            f"{f('SQ_VALU_MFMA_BUSY_CYCLES'):.2f})\n"
+            f"{'':14s} per CU, of the kernel's time: L1 waiting on L2 data "
+            f"{per_cu('TCP_PENDING_STALL_CYCLES_sum'):.2f}, TA stalled by L1 "
+            f"{per_cu('TA_ADDR_STALLED_BY_TC_CYCLES_sum'):.2f}, TA busy "
+            f"{v.get('TA_BUSY_avr', 0.0) / xcd_cycles if xcd_cycles else float('nan'):.2f}\n"
+            f"{'':14s} L2 read latency seen by L1 {lat:.0f} cycles, L2 hit rate {hit:.2f}; per wave: "
+            f"VALU {v.get('SQ_INSTS_VALU', 0) / waves:.0f}, MFMA {v.get('SQ_INSTS_MFMA', 0) / waves:.0f}, "
+            f"LDS {v.get('SQ_INSTS_LDS', 0) / waves:.0f}, loads {v.get('SQ_INSTS_VMEM_RD', 0) / waves:.0f}, "
+            f"stores {v.get('SQ_INSTS_VMEM_WR', 0) / waves:.0f} instructions")
+    with open(os.path.join(ROOT, "profiles", f"memory_pipeline_headline_{wl}.txt"), "w") as fh:
+        fh.write(f"Where the kernels of workload {wl} wait: rocprofv3 counters per dispatch\n"
+                 "(SQ_* summed over the waves, TA/TCP summed over the 256 CUs, GRBM_GUI_ACTIVE over\n"
+                 f"the 8 XCDs).\n{stamp}commands (cwd = repository root, DIR = output directory):\n"
+                 + "".join(f"  {cmds[f'headline_pipe{i + 1}']}\n" for i in range(len(PIPE_COUNTERS)))
+                 + "\n" + "\n".join(lines) + "\n")
 
 
 def _trace_summary(stats, out, head):
