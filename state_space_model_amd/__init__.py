@@ -1,47 +1,19 @@
-"""MI355X-native Mamba-2 SSD selective scan (chunked prefill + decode step).
+"""MI355X-native Mamba-2 SSD selective scan (chunked prefill, decode step,
+their gradients, and the related Mamba-1 and gated delta-rule scans).
 
 The compute runs in the HIP library ``libssd.so`` (built from ``csrc/``);
 ``ssd.py`` is the thin ctypes binding over its C ABI (``include/ssd.h``).
-Importing this package does not load the library; ``prefill``/``step``/``step_multi``
-load it on first use and raise if it is missing.
+Importing this package loads no library: the binding's entry points are
+resolved on first attribute access, and the library on first call (which
+raises if it has not been built).
 """
 
-
-def prefill(*args, **kwargs):
-    from . import ssd
-    return ssd.prefill(*args, **kwargs)
+_API = ("prefill", "prefill_train", "prefill_backward", "step", "step_multi",
+         "decode_layer_step", "selective_scan", "gated_delta_rule", "plan", "workspace_bytes")
 
 
-def step(*args, **kwargs):
-    from . import ssd
-    return ssd.step(*args, **kwargs)
-
-
-def step_multi(*args, **kwargs):
-    from . import ssd
-    return ssd.step_multi(*args, **kwargs)
-
-
-def decode_layer_step(*args, **kwargs):
-    from . import ssd
-    return ssd.decode_layer_step(*args, **kwargs)
-
-
-def selective_scan(*args, **kwargs):
-    from . import ssd
-    return ssd.selective_scan(*args, **kwargs)
-
-
-def prefill_backward(*args, **kwargs):
-    from . import ssd
-    return ssd.prefill_backward(*args, **kwargs)
-
-
-def gated_delta_rule(*args, **kwargs):
-    from . import ssd
-    return ssd.gated_delta_rule(*args, **kwargs)
-
-
-def prefill_train(*args, **kwargs):
-    from . import ssd
-    return ssd.prefill_train(*args, **kwargs)
+def __getattr__(name):
+    if name in _API:
+        from . import ssd
+        return getattr(ssd, name)
+    raise AttributeError(f"module {__name__!r} has no attribute {name!r}")
