@@ -83,6 +83,50 @@ def test_prefill_small(dtype, scan, state, case):
     _check(f"{dtype} {scan} {state}", y, ho, ry, rh, TOL[dtype])
 
 
+WALK_SEGMENT_CASES = [  # (lengths, dense, H, G, chunk): each walks in two segments
+    ([3000, 0, 40, 1500, 64], False, 8, 2, 64),  # empty, one-chunk, exactly one-chunk sequences
+    ([571, 571], True, 8, 1, 64),                # 9 chunks a sequence: segments of 4 and 5
+    ([2100, 700, 1], False, 6, 3, 128),          # one token alone in its segment pair
+]
+
+
+@pytest.mark.parametrize("case", range(len(WALK_SEGMENT_CASES)))
+def test_prefill_walk_segments(case):
+    """The state walk splits each sequence into two segments walked at once
+    (the second from a zero state) and corrects the second segment's entering
+    states and the final state afterwards: packed batches with empty, one-chunk
+    and one-token sequences, and a dense batch with an odd chunk count, every
+    element against the oracle, as are the chunk-parallel states on the same
+    batch and each packed sequence run alone (which may walk unsegmented)."""
+    import torch
+    from state_space_model_amd import ssd
+    lengths, dense, H, G, chunk = WALK_SEGMENT_CASES[case]
+    log(f"prefill walk segments: lengths={lengths} dense={dense} H={H} G={G} Q={chunk}")
+    d = inputs.prefill_inputs(H, 64, 128, G, lengths, 5100 + case, dtype="bf16", h0=True)
+    ry, rh = _ref(d)
+    t = dev_inputs(d, "bf16")
+    kw = dict(nseq=len(lengths)) if dense else dict(cu_seqlens=t["cu_seqlens"])
+    y, ho = ssd.prefill(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["h0"], chunk=chunk,
+                        state="walk", **kw)
+    yc, hc = ssd.prefill(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["h0"], chunk=chunk,
+                         state="chunks", **kw)
+    torch.cuda.synchronize()
+    _check("walk, two segments", y.cpu().numpy(), ho.cpu().numpy(), ry, rh, TOL["bf16"])
+    _check("chunk states", yc.cpu().numpy(), hc.cpu().numpy(), ry, rh, TOL["bf16"])
+    if not dense:  # each sequence alone (one sequence: its own two segments)
+        cu = d["cu_seqlens"]
+        for k in range(len(lengths)):
+            a, b = int(cu[k]), int(cu[k + 1])
+            one = torch.tensor([0, b - a], dtype=torch.int32, device="cuda")
+            ys, hs = ssd.prefill(t["x"][a:b].contiguous(), t["dt"][a:b].contiguous(), t["A"],
+                                 t["B"][a:b].contiguous(), t["C"][a:b].contiguous(), t["D"],
+                                 t["h0"][k:k + 1].contiguous(), chunk=chunk, state="walk",
+                                 cu_seqlens=one)
+            torch.cuda.synchronize()
+            err = (maxabs(ys.cpu().numpy(), ry[a:b]), maxabs(hs.cpu().numpy(), rh[k:k + 1]))
+            assert max(err) <= TOL["bf16"], (k, err)
+
+
 def test_prefill_heads_streamed_several_heads_per_workgroup():
     """80 heads in 2 groups at chunk 256 over a packed pair of ragged
     sequences (17 chunks x 80 heads): on the heads-streamed scan the head-count
