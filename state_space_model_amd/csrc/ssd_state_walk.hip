@@ -20,14 +20,22 @@
 //
 // The chunk states do not depend on one another, only their sum does, so the
 // walk's serial part is one multiply-add per state element per chunk; what a
-// chain waits for is its loads.  A workgroup (4 waves) owns one chain -- a
-// (sequence, head) -- and streams its chunks with the next chunk's loads in
-// flight: the x rows go straight to LDS (block-swizzled, read transposed as the
-// MFMA A operand), the decay-scaled B rows come from a copy of B already in
-// MFMA fragment order (k_bfrag) straight into registers, so B, which every head
-// of a group shares, is never staged per head.  Every wave computes the
-// chunk's decay itself (a scan of 64 lanes), so no barrier waits for it.  A
-// wave owns two n-tiles and all four p-tiles of the chain's P x N state.
+// chain waits for is its loads.  A chain -- a (sequence, head), or a segment
+// of its chunks -- is walked by one or two workgroups (each owning a share of
+// the state's n columns) that stream its chunks with the next phase's loads in
+// flight: the x rows go straight to LDS (block-swizzled, read transposed as
+// the MFMA A operand), the B rows come from a copy of B already in MFMA
+// fragment order (k_bfrag) straight into registers and are weighted there, so
+// B, which every head of a group shares, is never staged per head.  Every
+// wave computes the chunk's decay itself (a DPP scan over the wave), so no
+// barrier waits for it; a wave owns one n-tile and the four p-tiles of the
+// chain's P x N state.
+//
+// Segments: with enough room on the chip, each sequence is walked in two
+// segments at once, the second from a zero state, and k_walk_fixup then adds
+// the first segment's decayed end state to the second segment's entering
+// states and forms the final state (the recurrence is linear in the entering
+// state).
 #include "ssd.h"
 #include "ssd_launch.h"
 #include "ssd_prefill_util.h"
@@ -511,8 +519,9 @@ bool walk_choice(int P, int N, int Q, bool bf16, int nseq, int H, bool packed, u
   return !packed && (long)nseq * H >= kWalkMinChains;
 }
 
-// Launch shape: NH workgroups per (sequence, head) chain (each owns N/NH of
-// the state's n columns) and JP rows per pipeline phase.
+// Launch shape (compile-time constants): NH workgroups of NW waves per chain
+// walked whole (each owns N/NH of the state's n columns), JP rows per pipeline
+// phase; one workgroup of SEG_NW waves and SEG_JP-row phases per chain segment.
 #ifndef SSD_WALK_NH
 #define SSD_WALK_NH 2
 #endif
