@@ -801,6 +801,7 @@ PROFILED = {
 }
 
 
+PIPE_SECTIONS = ("headline", "small")
 PIPE_COUNTERS = (
     ("SQ_WAVE_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY",
      "SQ_ACTIVE_INST_VALU", "SQ_VMEM_TA_ADDR_FIFO_FULL", "SQ_VALU_MFMA_BUSY_CYCLES"),
@@ -845,10 +846,11 @@ def profile_commands():
                                f"-d DIR/{sec}_mfma -o run {base}")
     # where the headline's kernels wait: SQ issue and wait states, the vector
     # memory path (TA address FIFO, L1 pending on L2, L2 read latency), L2 hits
-    hb = f"-- python bench.py {PROFILED['headline'][1]}"
-    for i, cs in enumerate(PIPE_COUNTERS):
-        cmds[f"headline_pipe{i + 1}"] = (f"rocprofv3 --pmc {' '.join(cs)} --output-format csv "
-                                         f"-d DIR/headline_pipe{i + 1} -o run {hb}")
+    for sec in PIPE_SECTIONS:
+        hb = f"-- python bench.py {PROFILED[sec][1]}"
+        for i, cs in enumerate(PIPE_COUNTERS):
+            cmds[f"{sec}_pipe{i + 1}"] = (f"rocprofv3 --pmc {' '.join(cs)} --output-format csv "
+                                          f"-d DIR/{sec}_pipe{i + 1} -o run {hb}")
     cmds["train_trace"] = ("rocprofv3 --kernel-trace --stats --output-format csv -d DIR/train_trace "
                            "-o run -- python bench.py --train-only --steps 50 --warmup 5 --quiet")
     cmds["cfetch"] = ("rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/cfetch -o run -- "
@@ -945,7 +947,8 @@ def summarize(directory):
                        os.path.join(ROOT, "profiles", f"kernel_trace_{sec}_{wl}.txt"),
                        f"rocprofv3 kernel trace, workload {wl}\n{stamp}command (cwd = repository "
                        f"root):\n  {cmds[sec + '_trace']}\n")
-    _pipeline_summary(directory, cmds, pmc, stamp)
+    for sec in PIPE_SECTIONS:
+        _pipeline_summary(directory, cmds, pmc, stamp, sec)
     _trace_summary(glob.glob(os.path.join(directory, "train_trace", "**", "*kernel_stats.csv"),
                              recursive=True),
                    os.path.join(ROOT, "profiles", "kernel_trace_train_mamba2-130m-layer.txt"),
@@ -957,15 +960,15 @@ def summarize(directory):
     print(json.dumps(traffic, indent=1))
 
 
-def _pipeline_summary(directory, cmds, pmc, stamp):
-    """profiles/memory_pipeline_headline_<workload>.txt from the headline_pipe*
+def _pipeline_summary(directory, cmds, pmc, stamp, sec):
+    """profiles/memory_pipeline_<sec>_<workload>.txt from the <sec>_pipe*
     counter runs: per kernel, fractions of wave time and of the kernel's
     duration per XCD, and the L1's average wait for L2 reads."""
-    wl = PROFILED["headline"][0]
+    wl = PROFILED[sec][0]
     vals = {}
     for i, cs in enumerate(PIPE_COUNTERS):
         for c in cs:
-            for kname, vs in pmc(f"headline_pipe{i + 1}", c).items():
+            for kname, vs in pmc(f"{sec}_pipe{i + 1}", c).items():
                 k = _kernel_key(kname)
                 if k is not None:
                     vals.setdefault(k, {})[c] = float(np.mean(vs))
@@ -993,11 +996,11 @@ def _pipeline_summary(directory, cmds, pmc, stamp):
             f"VALU {v.get('SQ_INSTS_VALU', 0) / waves:.0f}, MFMA {v.get('SQ_INSTS_MFMA', 0) / waves:.0f}, "
             f"LDS {v.get('SQ_INSTS_LDS', 0) / waves:.0f}, loads {v.get('SQ_INSTS_VMEM_RD', 0) / waves:.0f}, "
             f"stores {v.get('SQ_INSTS_VMEM_WR', 0) / waves:.0f} instructions")
-    with open(os.path.join(ROOT, "profiles", f"memory_pipeline_headline_{wl}.txt"), "w") as fh:
+    with open(os.path.join(ROOT, "profiles", f"memory_pipeline_{sec}_{wl}.txt"), "w") as fh:
         fh.write(f"Where the kernels of workload {wl} wait: rocprofv3 counters per dispatch\n"
                  "(SQ_* summed over the waves, TA/TCP summed over the 256 CUs, GRBM_GUI_ACTIVE over\n"
                  f"the 8 XCDs).\n{stamp}commands (cwd = repository root, DIR = output directory):\n"
-                 + "".join(f"  {cmds[f'headline_pipe{i + 1}']}\n" for i in range(len(PIPE_COUNTERS)))
+                 + "".join(f"  {cmds[f'{sec}_pipe{i + 1}']}\n" for i in range(len(PIPE_COUNTERS)))
                  + "\n" + "\n".join(lines) + "\n")
 
 
