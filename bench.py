@@ -894,7 +894,19 @@ def summarize(directory):
     f_fac = copy_factor("cfetch", "FETCH_SIZE", 1024 << 20)
     w_fac = copy_factor("cwrite", "WRITE_SIZE", 1024 << 20)
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    traffic = {"source_hash": source_hash(), "fetch_factor": f_fac, "write_factor": w_fac}
+    # the kernel sources the profiled runs were built from, as each run printed
+    # them (bench.py prints the hash on every run); all runs must agree
+    import re
+    seen = set()
+    for log_path in glob.glob(os.path.join(directory, "*.log")):
+        with open(log_path, errors="replace") as fh:
+            seen.update(re.findall(r"bench: kernel sources hash ([0-9a-f]{16})", fh.read()))
+    if len(seen) > 1:
+        raise SystemExit(f"profiled runs disagree on the kernel sources: {sorted(seen)}")
+    if not seen:
+        raise SystemExit(f"no 'bench: kernel sources hash' line in {directory}/*.log: the "
+                         "profiled runs' output must be kept beside their results")
+    traffic = {"source_hash": seen.pop(), "fetch_factor": f_fac, "write_factor": w_fac}
     try:  # keep the figures of sections not profiled this time, if taken on the same sources
         with open(TRAFFIC_FILE) as f:
             old = json.load(f)
@@ -1023,6 +1035,7 @@ def main():
     if args.summarize:
         summarize(args.summarize)
         return
+    print(f"bench: kernel sources hash {source_hash()}", file=sys.stderr, flush=True)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this library runs on "
               "one GPU and has no multi-GPU path; run it with --gpus 1", file=sys.stderr)
