@@ -116,7 +116,12 @@ template <int Q, int NH, int JP_, int NW_> struct WalkCfg {
   static constexpr int DTN = Q < 64 ? 64 : Q;   // floats of a dt column buffer (whole-wave loads)
   static constexpr int OFF_DT = 2 * XB;
   static constexpr int OFF_W = OFF_DT + 2 * DTN * 4;  // a w row per wave
-  static constexpr int LDS = OFF_W + NW * DTN * 4;
+  // each wave's bf16 rows of the entering state, staged for whole-line stores
+  // (row pitch padded by 16 bytes against bank conflicts)
+  static constexpr int HST_PITCH = P * 2 + 16;
+  static constexpr int HST_WAVE = NTW * 16 * HST_PITCH;
+  static constexpr int OFF_HST = OFF_W + NW * DTN * 4;
+  static constexpr int LDS = OFF_HST + NW * HST_WAVE;
   static_assert(NTW >= 1 && NT % NW == 0 && Q <= 256, "walk shape");
 };
 
@@ -408,15 +413,29 @@ __global__ __launch_bounds__(64 * NW_) void k_state_walk(
         // the state entering chunk c, in the operand type, for the chunk scan:
         // stored after the wait, so that the stores complete under the next
         // phase's work instead of holding up this one's wait
+        // The wave's rows 16 nt0 .. 16 (nt0 + NTW) - 1 of the N x P block are
+        // contiguous; the accumulator layout gives each lane 8-byte pieces of
+        // 16 rows, so the rows go through the wave's own LDS rows first and
+        // leave as 16 bytes per lane, 8 whole 128-byte rows per store (one
+        // wave writes and reads its rows: no barrier)
         const size_t hco = ((size_t)c * H + hd) * (size_t)(N * P);
+        char *hst = smem + K::OFF_HST + wave * K::HST_WAVE;
 #pragma unroll
         for (int t = 0; t < NTW; ++t)
 #pragma unroll
           for (int pt = 0; pt < NPT; ++pt) {
-            const size_t e = hco + (size_t)(16 * (nt0 + t) + col) * P + 16 * pt + 4 * grp;
-            st4T(hin + e, Hs[t][pt]);
-            if (hin32) st4(hin32 + e, Hs[t][pt]);  // a training forward keeps them in float32
+            *reinterpret_cast<bf16x4 *>(hst + (16 * t + col) * K::HST_PITCH + 32 * pt + 8 * grp) =
+                __builtin_convertvector(Hs[t][pt], bf16x4);
+            if (hin32)  // a training forward keeps them in float32 as well
+              st4(hin32 + hco + (size_t)(16 * (nt0 + t) + col) * P + 16 * pt + 4 * grp, Hs[t][pt]);
           }
+        bf16 *hrow = hin + hco + (size_t)(16 * nt0) * P;
+#pragma unroll
+        for (int k = 0; k < 2 * NTW; ++k) {
+          const int r = 8 * k + (lane >> 3);
+          *reinterpret_cast<bf16x8 *>(hrow + (size_t)r * P + 8 * (lane & 7)) =
+              *reinterpret_cast<const bf16x8 *>(hst + r * K::HST_PITCH + 16 * (lane & 7));
+        }
         // s, dt and u for the chunk scan, likewise after the wait (wave 0 of
         // part 0, from the registers the decay left them in: the chunk's dt
         // column in LDS may already be taking the next chunk's)
@@ -565,11 +584,13 @@ static hipError_t run_walk(const PrefillArgs &a, const WorkspaceLayout &L, bool 
   return hipLaunchKernel(kern, dim3(grid), dim3(64 * K::NW), args, K::LDS, st);
 }
 
-// Segments per sequence: two when the doubled chain count still runs in one
-// round of the 8-wave shape (three 47 KB workgroups per CU) and sequences
-// average at least 8 chunks, so that halving the chain outweighs the fix-up's
-// pass over the second segments' entering states; one for the training
-// forward, whose float32 entering states would need the fix-up too.
+// Segments per sequence: two when the doubled chain count stays within three
+// per compute unit (two 8-wave workgroups are resident per CU, so at most a
+// short second round) and sequences average at least 8 chunks, so that
+// halving the chain outweighs the fix-up's pass over the second segments'
+// entering states (three or more segments measured no faster: the fix-up
+// grows with them); one for the training forward, whose float32 entering
+// states would need the fix-up too.
 int walk_segments(int nseq, int H, int64_t T, int Q, int nc, bool packed, bool training) {
   if (training || nseq <= 0) return 1;
   if (2L * nseq * H > 3L * 256) return 1;
