@@ -87,32 +87,45 @@ WALK_SEGMENT_CASES = [  # (lengths, dense, H, G, chunk): each walks in two segme
     ([3000, 0, 40, 1500, 64], False, 8, 2, 64),  # empty, one-chunk, exactly one-chunk sequences
     ([571, 571], True, 8, 1, 64),                # 9 chunks a sequence: segments of 4 and 5
     ([2100, 700, 1], False, 6, 3, 128),          # one token alone in its segment pair
+    # chunk 256, the layer shapes' chunk
+    ([4000, 0, 300, 3500], False, 8, 1, 256),    # empty sequence, one-chunk segments
+    ([2400, 2400], True, 8, 2, 256),             # 10 chunks a sequence, two groups
 ]
 
 
+@pytest.mark.parametrize("scan", ["rows", "heads"])
 @pytest.mark.parametrize("case", range(len(WALK_SEGMENT_CASES)))
-def test_prefill_walk_segments(case):
+def test_prefill_walk_segments(case, scan):
     """The state walk splits each sequence into two segments walked at once
     (the second from a zero state) and corrects the second segment's entering
-    states and the final state afterwards: packed batches with empty, one-chunk
-    and one-token sequences, and a dense batch with an odd chunk count, every
-    element against the oracle, as are the chunk-parallel states on the same
-    batch and each packed sequence run alone (which may walk unsegmented)."""
+    states and the final state afterwards: packed batches with empty,
+    one-chunk and one-token sequences, and dense batches with odd and even
+    chunk counts, through both chunk-scan kernels, every element against the
+    oracle, as are the chunk-parallel states on the same batch and each packed
+    sequence run alone (which may walk unsegmented); the stages run one by one
+    equal one call, bitwise."""
     import torch
     from state_space_model_amd import ssd
     lengths, dense, H, G, chunk = WALK_SEGMENT_CASES[case]
-    log(f"prefill walk segments: lengths={lengths} dense={dense} H={H} G={G} Q={chunk}")
+    log(f"prefill walk segments: lengths={lengths} dense={dense} H={H} G={G} Q={chunk}"
+        f" scan={scan}")
     d = inputs.prefill_inputs(H, 64, 128, G, lengths, 5100 + case, dtype="bf16", h0=True)
     ry, rh = _ref(d)
     t = dev_inputs(d, "bf16")
     kw = dict(nseq=len(lengths)) if dense else dict(cu_seqlens=t["cu_seqlens"])
-    y, ho = ssd.prefill(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["h0"], chunk=chunk,
-                        state="walk", **kw)
-    yc, hc = ssd.prefill(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["h0"], chunk=chunk,
-                         state="chunks", **kw)
+    kw.update(chunk=chunk, scan=scan)
+    args = (t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["h0"])
+    y, ho = ssd.prefill(*args, state="walk", **kw)
+    yc, hc = ssd.prefill(*args, state="chunks", **kw)
+    ws = ssd.alloc_workspace(sum(lengths), len(lengths), H, 64, 128, G, chunk, torch.bfloat16,
+                             "cuda")
+    y2, h2 = torch.empty_like(y), torch.empty_like(ho)
+    for st in (1, 2, 4, 8):
+        ssd.prefill(*args, y=y2, h_out=h2, workspace=ws, stages=st, state="walk", **kw)
     torch.cuda.synchronize()
     _check("walk, two segments", y.cpu().numpy(), ho.cpu().numpy(), ry, rh, TOL["bf16"])
     _check("chunk states", yc.cpu().numpy(), hc.cpu().numpy(), ry, rh, TOL["bf16"])
+    assert torch.equal(y, y2) and torch.equal(ho, h2)
     if not dense:  # each sequence alone (one sequence: its own two segments)
         cu = d["cu_seqlens"]
         for k in range(len(lengths)):
@@ -121,7 +134,7 @@ def test_prefill_walk_segments(case):
             ys, hs = ssd.prefill(t["x"][a:b].contiguous(), t["dt"][a:b].contiguous(), t["A"],
                                  t["B"][a:b].contiguous(), t["C"][a:b].contiguous(), t["D"],
                                  t["h0"][k:k + 1].contiguous(), chunk=chunk, state="walk",
-                                 cu_seqlens=one)
+                                 scan=scan, cu_seqlens=one)
             torch.cuda.synchronize()
             err = (maxabs(ys.cpu().numpy(), ry[a:b]), maxabs(hs.cpu().numpy(), rh[k:k + 1]))
             assert max(err) <= TOL["bf16"], (k, err)
