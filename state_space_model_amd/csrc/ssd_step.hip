@@ -11,26 +11,30 @@
 // the work is one independent lane per (head, head_dim) channel folding over
 // d_state; here a 256-thread block owns one head and splits both p and n.)
 //
-// Block = 256 threads per (b, h): TPR = P/4 threads cover one state row with
-// float4 vectors, RPP = 256/TPR rows per pass, eight passes in flight; the partial
-// y sums over rows are reduced through LDS at the end.
+// Block = 256 threads per (b, h) -- or per (b, h, half of p) when the batch
+// is too small to give every CU several blocks (PS = 2): TPR = P/PS/4 threads
+// cover the block's columns of one state row with float4 vectors, RPP =
+// 256/TPR rows per pass, U passes in flight; the partial y sums over rows are
+// reduced through LDS at the end (y[p] sums over n only, so the halves of p
+// need nothing from each other).
 #include "ssd_device.h"
 #include "ssd_launch.h"
 
 namespace ssd {
 
-template <typename T, int P>
+template <typename T, int P, int PS>
 __global__ __launch_bounds__(256) void k_step(const T *__restrict__ x, const float *__restrict__ dt,
                                               const float *__restrict__ A,
                                               const T *__restrict__ B, const T *__restrict__ C,
                                               const float *__restrict__ D, float *__restrict__ h,
                                               float *__restrict__ y, int H, int N, int G,
                                               size_t xbs, size_t bcs) {
-  constexpr int TPR = P / 4;
+  constexpr int PB = P / PS;  // the block's columns
+  constexpr int TPR = PB / 4;
   constexpr int RPP = 256 / TPR;
   __shared__ float Bsh[1024], Csh[1024];
   __shared__ f4 red[256];
-  const int hd = blockIdx.x, b = blockIdx.y;
+  const int hd = blockIdx.x / PS, pc = (blockIdx.x % PS) * PB, b = blockIdx.y;
   const int g = (hd * G) / H;
   const int tid = threadIdx.x, q = tid % TPR, r0 = tid / TPR;
   const T *Bp = B + (size_t)b * bcs + (size_t)g * N;  // x, B, C rows are xbs / bcs apart
@@ -42,17 +46,17 @@ __global__ __launch_bounds__(256) void k_step(const T *__restrict__ x, const flo
   const size_t bh = (size_t)b * H + hd;
   const float dtv = dt[bh];
   const float a = expf(fminf(dtv * A[hd], 0.f));
-  const f4 xv = ld4f(x + (size_t)b * xbs + (size_t)hd * P + 4 * q);
+  const f4 xv = ld4f(x + (size_t)b * xbs + (size_t)hd * P + pc + 4 * q);
   f4 dx;
 #pragma unroll
   for (int e = 0; e < 4; ++e) dx[e] = dtv * xv[e];
   __syncthreads();
 
-  float *hp = h + bh * (size_t)N * P + 4 * q;
+  float *hp = h + bh * (size_t)N * P + pc + 4 * q;
   f4 yacc = zero4();
   int n = r0;
-  // eight rows per thread in flight
-  constexpr int U = 8;
+  // U rows per thread in flight (all of them at N = 128 with the halves of p)
+  constexpr int U = PS == 1 ? 8 : 4;
   for (; n + (U - 1) * RPP < N; n += U * RPP) {
     f4 v[U];
 #pragma unroll
@@ -91,25 +95,32 @@ __global__ __launch_bounds__(256) void k_step(const T *__restrict__ x, const flo
     const float dv = D[hd];
 #pragma unroll
     for (int e = 0; e < 4; ++e) s[e] += dv * xv[e];
-    st4(y + bh * P + 4 * q, s);
+    st4(y + bh * P + pc + 4 * q, s);
   }
 }
+
+// Fewer (b, h) blocks than this (four per CU) and P >= 32: each head's
+// columns in two blocks.
+constexpr long kStepSplitBelow = 4L * 256;
 
 template <typename T>
 static hipError_t run_step(const StepArgs &a) {
   hipStream_t st = static_cast<hipStream_t>(a.stream);
-  dim3 grid(a.H, a.batch);
+  const int ps = (long)a.batch * a.H < kStepSplitBelow && a.P >= 32 ? 2 : 1;
+  dim3 grid(a.H * ps, a.batch);
   const size_t xbs = a.x_bstride ? a.x_bstride : (size_t)a.H * a.P;
   const size_t bcs = a.bc_bstride ? a.bc_bstride : (size_t)a.G * a.N;
-#define SSD_LAUNCH(p)                                                                          \
-  hipLaunchKernelGGL((k_step<T, p>), grid, dim3(256), 0, st, (const T *)a.x, a.dt, a.A,        \
-                     (const T *)a.B, (const T *)a.C, a.D, a.h, a.y, a.H, a.N, a.G, xbs, bcs); \
-  break;
-  switch (a.P) {
-    case 16: SSD_LAUNCH(16)
-    case 32: SSD_LAUNCH(32)
-    case 64: SSD_LAUNCH(64)
-    case 128: SSD_LAUNCH(128)
+#define SSD_LAUNCH(p, s)                                                                       \
+  hipLaunchKernelGGL((k_step<T, p, s>), grid, dim3(256), 0, st, (const T *)a.x, a.dt, a.A,     \
+                     (const T *)a.B, (const T *)a.C, a.D, a.h, a.y, a.H, a.N, a.G, xbs, bcs);
+  switch (a.P * 10 + ps) {
+    case 161: SSD_LAUNCH(16, 1) break;
+    case 321: SSD_LAUNCH(32, 1) break;
+    case 322: SSD_LAUNCH(32, 2) break;
+    case 641: SSD_LAUNCH(64, 1) break;
+    case 642: SSD_LAUNCH(64, 2) break;
+    case 1281: SSD_LAUNCH(128, 1) break;
+    case 1282: SSD_LAUNCH(128, 2) break;
     default: return hipErrorInvalidValue;
   }
 #undef SSD_LAUNCH
