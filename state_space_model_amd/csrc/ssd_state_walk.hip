@@ -31,11 +31,14 @@
 // barrier waits for it; a wave owns one n-tile and the four p-tiles of the
 // chain's P x N state.
 //
-// Segments: with enough room on the chip, each sequence is walked in two
-// segments at once, the second from a zero state, and k_walk_fixup then adds
-// the first segment's decayed end state to the second segment's entering
-// states and forms the final state (the recurrence is linear in the entering
-// state).
+// Segments: with enough room on the chip, each chain is walked in segments at
+// once, each after the first from a zero state, and k_walk_fixup then adds
+// the earlier segments' decayed contribution to their entering states and
+// forms the final state (the recurrence is linear in the entering state).
+// Some heads' chains in two segments fill the chip's slots; the rest, in
+// shorter segments, fill the slots those free (SegPlan).
+#include <algorithm>
+
 #include "ssd.h"
 #include "ssd_launch.h"
 #include "ssd_prefill_util.h"
@@ -103,6 +106,19 @@ __device__ __forceinline__ int4 walk_map(const ChunkMap &m, int c) {
     return m(c);
   }
 }
+
+// How a walk cuts its chains into segments: the chains of heads below hsplit
+// in nlo segments, those of the others in nhi (nlo = nhi = 1: whole chains).
+// The first kind comes first in the launch order, the second fills the slots
+// they free.
+struct SegPlan {
+  int nlo, nhi, hsplit;
+  __host__ __device__ int nseg(int hd) const { return hd < hsplit ? nlo : nhi; }
+  __host__ __device__ int maxseg() const { return nlo > nhi ? nlo : nhi; }
+  __host__ __device__ long chains(int nseq, int H) const {
+    return (long)nseq * (hsplit * nlo + (H - hsplit) * nhi);
+  }
+};
 
 template <int Q, int NH, int JP_, int NW_> struct WalkCfg {
   static constexpr int P = 64, N = 128;
@@ -268,20 +284,48 @@ __global__ __launch_bounds__(64 * NW_) void k_state_walk(
     const bf16 *__restrict__ bfr, const int *__restrict__ seq_off, ChunkMap cmap, int H, int G,
     int nchain, const float *h0, float *h_out, float *__restrict__ s_out,
     float *__restrict__ dt_out, float *__restrict__ u_out, bf16 *__restrict__ hin,
-    float *__restrict__ hin32, float *h_out2, int nseg, float *__restrict__ seg_end) {
+    float *__restrict__ hin32, float *h_out2, SegPlan sp, float *__restrict__ seg_end) {
   typedef WalkCfg<Q, NH, JP_, NW_> K;
   constexpr int P = K::P, N = K::N, NTW = K::NTW, NPT = P / 16, KSP = K::KSP, NPH = K::NPH;
   constexpr int NTL = N / 16, JP = K::JP;
   // chains in contiguous blocks per XCD (workgroup L runs on XCD L % 8), so the
   // chains of one sequence, which read the same B fragments, share an L2
-  const int per = (nchain + 7) >> 3;
-  const int chn = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
-  if (chn >= nchain) return;
-  // chain = (sequence, segment, head, part), part fastest
-  const int part = chn % NH, sgh = chn / NH;
-  const int hd = __builtin_amdgcn_readfirstlane(sgh % H);
-  const int seg = __builtin_amdgcn_readfirstlane((sgh / H) % nseg);
-  const int s = __builtin_amdgcn_readfirstlane(sgh / H / nseg);
+  int part, hd, seg, s;
+  const int xcd = (int)(blockIdx.x & 7), slot = (int)(blockIdx.x >> 3);
+  if (sp.maxseg() == 1) {
+    const int per = (nchain + 7) >> 3;
+    const int chn = xcd * per + slot;
+    if (chn >= nchain) return;
+    // chain = (sequence, head, part), part fastest
+    part = chn % NH;
+    hd = (chn / NH) % H;
+    seg = 0;
+    s = chn / NH / H;
+  } else {
+    // segments (NH = 1): each XCD's block of first-kind chains, then its block
+    // of second-kind ones; each kind ordered (sequence, segment, head)
+    const int nseq = cmap.nseq, hs = sp.hsplit, hr = H - hs;
+    const int nlong = nseq * hs * sp.nlo, nshort = nseq * hr * sp.nhi;
+    const int lp = (nlong + 7) >> 3, spg = (nshort + 7) >> 3;
+    part = 0;
+    if (slot < lp) {
+      const int i = xcd * lp + slot;
+      if (i >= nlong) return;
+      hd = i % hs;
+      seg = (i / hs) % sp.nlo;
+      s = i / hs / sp.nlo;
+    } else {
+      const int j = xcd * spg + (slot - lp);
+      if (slot - lp >= spg || j >= nshort) return;
+      hd = hs + j % hr;
+      seg = (j / hr) % sp.nhi;
+      s = j / hr / sp.nhi;
+    }
+  }
+  hd = __builtin_amdgcn_readfirstlane(hd);
+  seg = __builtin_amdgcn_readfirstlane(seg);
+  s = __builtin_amdgcn_readfirstlane(s);
+  const int nseg = sp.nseg(hd);
   int c0, c1;  // chunks of sequence s
   if constexpr (DENSE) {
     const int cps = (cmap.L + Q - 1) / Q;
@@ -468,8 +512,9 @@ __global__ __launch_bounds__(64 * NW_) void k_state_walk(
 #pragma unroll
     for (int pt = 0; pt < NPT; ++pt) {
       const size_t e = (size_t)(16 * (nt0 + t) + col) * P + 16 * pt + 4 * grp;
-      if (nseg > 1) {
-        st4(seg_end + (((size_t)s * nseg + seg) * H + hd) * (size_t)(N * P) + e, Hs[t][pt]);
+      if (sp.maxseg() > 1) {
+        st4(seg_end + (((size_t)s * H + hd) * sp.maxseg() + seg) * (size_t)(N * P) + e,
+            Hs[t][pt]);
       } else {
         if (h_out) st4(h_out + hofs + e, Hs[t][pt]);
         if (h_out2) st4(h_out2 + hofs + e, Hs[t][pt]);
@@ -477,8 +522,9 @@ __global__ __launch_bounds__(64 * NW_) void k_state_walk(
     }
 }
 
-// The entering states of a sequence walked in nseg segments, each after the
-// first walked from a zero state: the recurrence is linear in the entering
+// The entering states of a sequence whose chains were walked in segments
+// (the counts per head as the plan says), each after the first walked from a
+// zero state: the recurrence is linear in the entering
 // state, so segment k's true entering states are those walked plus
 // (product of the decays of its chunks so far) E_k, with E_1 = the first
 // segment's end state (walked from h0) and E_(k+1) = (segment k's total decay)
@@ -487,7 +533,7 @@ __global__ __launch_bounds__(64 * NW_) void k_state_walk(
 // E is the final state.  The corrected H_in is rounded to bf16 again.
 __global__ __launch_bounds__(256) void k_walk_fixup(const float *__restrict__ s_ws,
                                                     const int *__restrict__ seq_off, ChunkMap cmap,
-                                                    int H, int NP, int Q, int nseg,
+                                                    int H, int NP, int Q, SegPlan sp,
                                                     const float *__restrict__ seg_end,
                                                     bf16 *__restrict__ hin, float *h_out,
                                                     float *h_out2) {
@@ -504,7 +550,9 @@ __global__ __launch_bounds__(256) void k_walk_fixup(const float *__restrict__ s_
     c1 = seq_off[s + 1];
   }
   const int nchk = c1 - c0;
-  f4 E = ld4(seg_end + ((size_t)s * nseg * H + hd) * (size_t)NP + e);  // segment 0, from h0
+  const int nseg = sp.nseg(hd);
+  const size_t sb = ((size_t)s * H + hd) * sp.maxseg();  // the chain's segment end states
+  f4 E = ld4(seg_end + sb * NP + e);  // segment 0, from h0
   for (int k = 1; k < nseg; ++k) {
     const int a0 = c0 + (k * nchk) / nseg, a1 = c0 + ((k + 1) * nchk) / nseg;
     float dec = 1.f;  // 2^(sum of s_end over the segment's chunks so far)
@@ -515,7 +563,7 @@ __global__ __launch_bounds__(256) void k_walk_fixup(const float *__restrict__ s_
       st4T(hp, hv + dec * E);
       dec *= __builtin_amdgcn_exp2f(fminf(s_ws[ch * Q + Q - 1], 0.f));
     }
-    const f4 own = ld4(seg_end + (((size_t)s * nseg + k) * H + hd) * (size_t)NP + e);
+    const f4 own = ld4(seg_end + (sb + k) * NP + e);
     E = dec * E + own;
   }
   const size_t hofs = ((size_t)s * H + hd) * (size_t)NP + e;
@@ -553,7 +601,7 @@ bool walk_choice(int P, int N, int Q, bool bf16, int nseq, int H, bool packed, u
 
 template <int Q, int NH, int JP, int NW>
 static hipError_t run_walk(const PrefillArgs &a, const WorkspaceLayout &L, bool write_hout,
-                           int nseg, hipStream_t st) {
+                           SegPlan plan, hipStream_t st) {
   typedef WalkCfg<Q, NH, JP, NW> K;
   const void *kern =
       a.precise_states
@@ -570,7 +618,8 @@ static hipError_t run_walk(const PrefillArgs &a, const WorkspaceLayout &L, bool 
   const int *so = reinterpret_cast<const int *>(ws + L.seq_off);
   ChunkMap cm{reinterpret_cast<const int4 *>(ws + L.info), a.cu ? 0 : (int)(a.T / a.nseq), a.nseq,
               a.Q};
-  int H_ = a.H, G_ = a.G, nch = a.nseq * a.H * NH * nseg, nseg_ = nseg;
+  int H_ = a.H, G_ = a.G, nch = a.nseq * a.H * NH;
+  SegPlan sp_ = plan;
   float *se = reinterpret_cast<float *>(ws + L.segend);
   const float *h0p = a.h0;
   float *hop = write_hout ? a.h_out : nullptr, *hop2 = write_hout ? a.h_out2 : nullptr;
@@ -579,23 +628,37 @@ static hipError_t run_walk(const PrefillArgs &a, const WorkspaceLayout &L, bool 
   bf16 *hp = reinterpret_cast<bf16 *>(ws + L.hin);
   float *h32 = a.hin32;
   void *args[] = {&xp, &dtp, &Ap, &bp, &so, &cm, &H_, &G_, &nch, &h0p, &hop, &sp, &dp, &up, &hp,
-                  &h32, &hop2, &nseg_, &se};
-  const unsigned grid = 8u * (unsigned)((nch + 7) / 8);
+                  &h32, &hop2, &sp_, &se};
+  unsigned grid = 8u * (unsigned)((nch + 7) / 8);
+  if (plan.maxseg() > 1) {  // each XCD's block of each kind of chain
+    const long nlong = (long)a.nseq * plan.hsplit * plan.nlo;
+    const long nshort = (long)a.nseq * (a.H - plan.hsplit) * plan.nhi;
+    grid = 8u * (unsigned)((nlong + 7) / 8 + (nshort + 7) / 8);
+  }
   return hipLaunchKernel(kern, dim3(grid), dim3(64 * K::NW), args, K::LDS, st);
 }
 
-// Segments per sequence: two when the doubled chain count stays within three
-// per compute unit (two 8-wave workgroups are resident per CU, so at most a
-// short second round) and sequences average at least 8 chunks, so that
-// halving the chain outweighs the fix-up's pass over the second segments'
-// entering states (three or more segments measured no faster: the fix-up
-// grows with them); one for the training forward, whose float32 entering
-// states would need the fix-up too.
-int walk_segments(int nseq, int H, int64_t T, int Q, int nc, bool packed, bool training) {
-  if (training || nseq <= 0) return 1;
-  if (2L * nseq * H > 3L * 256) return 1;
+// How the chains are cut (see SegPlan).  Whole chains for a training forward
+// (its float32 entering states would need the fix-up too), for sequences of
+// fewer than 8 chunks on average, and when twice the chains would exceed three
+// per compute unit.  Otherwise the heads' chains in two segments while those
+// fill the slots the chip holds at once (`slots` workgroups of the segment
+// walk), and the remaining heads' chains in more, shorter segments, so that
+// they fill the slots the first free instead of leaving a tail of long chains
+// running alone (with nhi segments of at least two chunks).
+static SegPlan walk_seg_plan(int nseq, int H, int64_t T, int Q, int nc, bool packed,
+                             bool training, long slots) {
+  const SegPlan whole{1, 1, H};
+  if (training || nseq <= 0) return whole;
+  if (2L * nseq * H > 3L * 256) return whole;
   const int64_t cps = packed ? nc / nseq : (T / nseq + Q - 1) / Q;
-  return cps >= 8 ? 2 : 1;
+  if (cps < 8) return whole;
+  const long hs = slots / (2L * nseq);
+  if (hs <= 0 || hs >= H) return SegPlan{2, 2, H};
+  const long hr = H - hs;
+  long nhi = (slots + nseq * hr / 2) / (nseq * hr);
+  nhi = std::max(2L, std::min<long>(nhi, cps / 2));
+  return SegPlan{2, (int)nhi, (int)hs};
 }
 
 #ifndef SSD_WALK_SEG_NW
@@ -605,11 +668,31 @@ int walk_segments(int nseq, int H, int64_t T, int Q, int nc, bool packed, bool t
 #define SSD_WALK_SEG_JP 128
 #endif
 
+// Workgroups of the segment walk's instance the chip holds at once.
+template <int Q> static long walk_seg_slots(bool dense) {
+  typedef WalkCfg<Q, 1, SSD_WALK_SEG_JP, SSD_WALK_SEG_NW> K;
+  const void *kern =
+      dense ? (const void *)k_state_walk<Q, 1, SSD_WALK_SEG_JP, SSD_WALK_SEG_NW, true, false>
+            : (const void *)k_state_walk<Q, 1, SSD_WALK_SEG_JP, SSD_WALK_SEG_NW, false, false>;
+  int dev = 0, ncu = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      set_lds_limit(kern) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * K::NW, K::LDS) !=
+          hipSuccess)
+    return 2L * 256;  // the instance's two per CU on 256 CUs
+  return (long)std::max(1, ncu) * std::max(1, per_cu);
+}
+
 template <int Q>
-static hipError_t run_walk_q(const PrefillArgs &a, const WorkspaceLayout &L, bool write_hout,
-                             int nseg, hipStream_t st) {
-  if (nseg > 1) return run_walk<Q, 1, SSD_WALK_SEG_JP, SSD_WALK_SEG_NW>(a, L, write_hout, nseg, st);
-  return run_walk<Q, SSD_WALK_NH, SSD_WALK_JP, SSD_WALK_NW>(a, L, write_hout, 1, st);
+static hipError_t run_walk_q(const PrefillArgs &a, const WorkspaceLayout &L, int nc,
+                             bool write_hout, SegPlan *used, hipStream_t st) {
+  const SegPlan sp = walk_seg_plan(a.nseq, a.H, a.T, a.Q, nc, a.cu != nullptr,
+                                   a.hin32 != nullptr, walk_seg_slots<Q>(a.cu == nullptr));
+  *used = sp;
+  if (sp.maxseg() > 1)
+    return run_walk<Q, 1, SSD_WALK_SEG_JP, SSD_WALK_SEG_NW>(a, L, write_hout, sp, st);
+  return run_walk<Q, SSD_WALK_NH, SSD_WALK_JP, SSD_WALK_NW>(a, L, write_hout, sp, st);
 }
 
 hipError_t launch_state_walk(const PrefillArgs &a, const WorkspaceLayout &L, int nc,
@@ -623,20 +706,19 @@ hipError_t launch_state_walk(const PrefillArgs &a, const WorkspaceLayout &L, int
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int nseg =
-      walk_segments(a.nseq, a.H, a.T, a.Q, nc, a.cu != nullptr, a.hin32 != nullptr);
+  SegPlan sp{1, 1, a.H};
   hipError_t e = hipErrorInvalidValue;
   switch (a.Q) {
-    case 32: e = run_walk_q<32>(a, L, write_hout, nseg, st); break;
-    case 64: e = run_walk_q<64>(a, L, write_hout, nseg, st); break;
-    case 128: e = run_walk_q<128>(a, L, write_hout, nseg, st); break;
-    case 256: e = run_walk_q<256>(a, L, write_hout, nseg, st); break;
+    case 32: e = run_walk_q<32>(a, L, nc, write_hout, &sp, st); break;
+    case 64: e = run_walk_q<64>(a, L, nc, write_hout, &sp, st); break;
+    case 128: e = run_walk_q<128>(a, L, nc, write_hout, &sp, st); break;
+    case 256: e = run_walk_q<256>(a, L, nc, write_hout, &sp, st); break;
   }
-  if (e != hipSuccess || nseg == 1) return e;
+  if (e != hipSuccess || sp.maxseg() == 1) return e;
   const int NP = 128 * 64;
   hipLaunchKernelGGL(k_walk_fixup, dim3((NP + 1023) / 1024, a.H, a.nseq), dim3(256), 0, st,
                      reinterpret_cast<const float *>(ws + L.s),
-                     reinterpret_cast<const int *>(ws + L.seq_off), cm, a.H, NP, a.Q, nseg,
+                     reinterpret_cast<const int *>(ws + L.seq_off), cm, a.H, NP, a.Q, sp,
                      reinterpret_cast<const float *>(ws + L.segend),
                      reinterpret_cast<bf16 *>(ws + L.hin), write_hout ? a.h_out : nullptr,
                      write_hout ? a.h_out2 : nullptr);

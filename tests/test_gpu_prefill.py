@@ -90,6 +90,10 @@ WALK_SEGMENT_CASES = [  # (lengths, dense, H, G, chunk): each walks in two segme
     # chunk 256, the layer shapes' chunk
     ([4000, 0, 300, 3500], False, 8, 1, 256),    # empty sequence, one-chunk segments
     ([2400, 2400], True, 8, 2, 256),             # 10 chunks a sequence, two groups
+    # more chains than the chip holds at once with two segments each: the
+    # first heads in two segments, the rest in shorter ones
+    ([2048, 2048], True, 160, 1, 256),
+    ([3000, 1, 2600], False, 100, 2, 256),
 ]
 
 
