@@ -576,7 +576,10 @@ WorkspaceLayout prefill_layout(int64_t T, int nseq, int H, int P, int N, int G, 
   L.bfrag = off;
   L.has_bfrag = walk_supported(P, N, Q, elem == 2);
   if (L.has_bfrag) off = align_up(off + (size_t)nc * G * Q * N * 2, 256);
-  L.segend = L.S;  // at most 2 segments of sequences of at least 8 chunks: fits
+  // the walk's piece end states: one per segment of a chain, or per run piece
+  // (a packed batch walked by lists), at most one per (chunk, head): fits in S,
+  // which the walk leaves unused
+  L.segend = L.S;
   L.total = off;
   return L;
 }
@@ -612,7 +615,8 @@ static hipError_t run_prefill(const PrefillArgs &a, unsigned stages) {
 
   // the state walk does stages 1, 2 and 4 in one kernel
   const bool walk =
-      nc > 0 && walk_choice(P, N, a.Q, a.bf16, a.nseq, a.H, a.cu != nullptr, a.variant);
+      nc > 0 && walk_choice(P, N, a.Q, a.bf16, a.nseq, a.H, a.cu != nullptr, a.variant,
+                            a.hin32 != nullptr);
   if ((stages & (walk ? 7u : 3u)) && (a.cu || L_dense == 0)) {
     // packed (or empty) batch: chunk map first.  Block 0 also writes the first
     // chunk of every sequence, which the state pass reads even when there are

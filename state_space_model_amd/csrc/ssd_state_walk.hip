@@ -522,6 +522,306 @@ __global__ __launch_bounds__(64 * NW_) void k_state_walk(
     }
 }
 
+// ------------------------------------------------------------------ walk by lists
+// The walk of a packed batch, whose sequences' chunk counts differ and are
+// known on the device only: the work cut evenly over the workgroups the chip
+// holds at once.  The chunks of all chains in one order (sequence by
+// sequence, head by head, each chain's chunks in order), position f = (the
+// chain's first position) + k, and workgroup l walks positions
+// [l W, (l + 1) W).  Where its run begins inside a chain it starts from a zero
+// state; where a piece of a run ends (its chain's end or the run's) it leaves
+// the piece's state at seg_end[the piece's first position], and
+// k_walk_fixup_list then adds each piece's share of the pieces before it (the
+// recurrence is linear in the entering state).  Whole chains would leave the
+// longest sequence's chains running alone long after the rest; here every
+// workgroup has the same number of chunks.  (For a dense batch the chains
+// are cut at the same chunk in every head instead -- SegPlan -- which keeps
+// the heads' chunk positions aligned and reads x rows and B fragments
+// together.)
+
+struct WalkPos {
+  int s, hd, k, nchk, cs;  // sequence, head, chunk in the chain, chunks in it, first chunk
+};
+
+// The chain and chunk at position f (f below the total count).
+template <bool DENSE>
+__device__ __forceinline__ WalkPos walk_locate(int f, const int *__restrict__ seq_off,
+                                               ChunkMap cmap, int H, int nseq, int Q) {
+  WalkPos w;
+  if constexpr (DENSE) {
+    const int cps = (cmap.L + Q - 1) / Q;
+    const int p = f / cps;
+    w.k = f - p * cps;
+    w.s = p / H;
+    w.hd = p - w.s * H;
+    w.nchk = cps;
+    w.cs = w.s * cps;
+  } else {
+    // the last sequence whose positions start at or before f (an empty
+    // sequence shares its start with the next one, so it is never the last)
+    int lo = 0, hi = nseq - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (H * seq_off[mid] <= f) lo = mid;
+      else hi = mid - 1;
+    }
+    w.s = lo;
+    w.cs = seq_off[lo];
+    w.nchk = seq_off[lo + 1] - w.cs;
+    const int r = f - H * w.cs;
+    w.hd = r / w.nchk;
+    w.k = r - w.hd * w.nchk;
+  }
+  w.s = __builtin_amdgcn_readfirstlane(w.s);
+  w.hd = __builtin_amdgcn_readfirstlane(w.hd);
+  w.k = __builtin_amdgcn_readfirstlane(w.k);
+  w.nchk = __builtin_amdgcn_readfirstlane(w.nchk);
+  w.cs = __builtin_amdgcn_readfirstlane(w.cs);
+  return w;
+}
+
+// A chunk-map entry made wave-uniform (scalar registers).
+__device__ __forceinline__ int4 uniform4(int4 v) {
+  return make_int4(__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y),
+                   __builtin_amdgcn_readfirstlane(v.z), __builtin_amdgcn_readfirstlane(v.w));
+}
+
+template <int Q, int JP_, int NW_, bool DENSE>
+__global__ __launch_bounds__(64 * NW_) void k_state_walk_list(
+    const bf16 *__restrict__ x, const float *__restrict__ dt, const float *__restrict__ A,
+    const bf16 *__restrict__ bfr, const int *__restrict__ seq_off, ChunkMap cmap, int H, int G,
+    int nseq, int F, int W, int nlist, const float *__restrict__ h0, float *__restrict__ s_out,
+    float *__restrict__ dt_out, float *__restrict__ u_out, bf16 *__restrict__ hin,
+    float *__restrict__ seg_end) {
+  typedef WalkCfg<Q, 1, JP_, NW_> K;
+  constexpr int P = K::P, N = K::N, NTW = K::NTW, NPT = P / 16, KSP = K::KSP, NPH = K::NPH;
+  constexpr int NTL = N / 16, JP = K::JP;
+  // runs in contiguous blocks per XCD (workgroup L runs on XCD L % 8), so the
+  // runs of one sequence, which read the same B fragments, share an L2
+  const int per = (nlist + 7) >> 3;
+  const int li = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+  if (li >= nlist) return;
+  const int Fr = DENSE ? F : min(F, H * __builtin_amdgcn_readfirstlane(seq_off[nseq]));
+  const int f0 = li * W, f1 = min(Fr, f0 + W);
+  if (f0 >= f1) return;
+  const int lane = threadIdx.x & 63, grp = lane >> 4, col = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  extern __shared__ __align__(16) char smem[];
+  float *w_l = reinterpret_cast<float *>(smem + K::OFF_W) + wave * K::DTN;  // this wave's row
+  const uint32_t lds0 = (uint32_t)(size_t)(__attribute__((address_space(3))) char *)smem;
+  const int nt0 = wave * NTW;
+  const size_t xstride = (size_t)H * P;
+  const int lb8 = lane >> 3;
+  const uint32_t xl = lb8 * (uint32_t)(xstride * 2) + 16 * ((lane & 7) ^ (2 * swz8(lb8)));
+  const size_t bfc = (size_t)G * ((Q / 32) * NTL) * 512;
+  auto bfw_of = [&](int hd) {  // the B fragments of head hd's group, this wave's n-tiles
+    return bfr + (size_t)((hd * G) / H) * ((Q / 32) * NTL) * 512 + (size_t)nt0 * 512 + lane * 8;
+  };
+  const int c4 = col >> 2, cq = 8 * (col & 3);
+  const int xbk = 4 * (grp & 1) + c4;
+  const int xo = (grp >> 1) * kBlk128 + xbk * 128 + cq + 32 * swz8(xbk);
+
+  WalkPos cur = walk_locate<DENSE>(f0, seq_off, cmap, H, nseq, Q);
+  const bf16 *bfw = bfw_of(cur.hd);
+  float a2 = A[cur.hd] * kLog2e;
+  f4 Hs[NTW][NPT];
+  auto reset_state = [&]() {  // a chain's first chunk: h0; a piece after a run's start: zero
+    const size_t hofs = ((size_t)cur.s * H + cur.hd) * (size_t)(N * P);
+#pragma unroll
+    for (int t = 0; t < NTW; ++t)
+#pragma unroll
+      for (int pt = 0; pt < NPT; ++pt)
+        Hs[t][pt] = (h0 && cur.k == 0)
+                        ? ld4(h0 + hofs + (size_t)(16 * (nt0 + t) + col) * P + 16 * pt + 4 * grp)
+                        : zero4();
+  };
+  reset_state();
+  int fp = f0;  // the current piece's first position
+
+  typedef bf16x8 BF[NTW][KSP];
+  BF bq[2];
+  {
+    const int4 ci = walk_map<DENSE>(cmap, cur.cs + cur.k);
+    walk_issue_dt<K>(dt, ci, H, cur.hd, lds0 + K::OFF_DT, wave);
+    walk_issue_x<K>(x, ci, 0, xstride, cur.hd, xl, smem, wave);
+    walk_load_b<K>(bfw + (size_t)(cur.cs + cur.k) * bfc, 0, bq[0]);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  int xbuf = 0;
+  for (int f = f0; f < f1; ++f) {
+    const int c = cur.cs + cur.k;
+    const int4 ci = uniform4(walk_map<DENSE>(cmap, c));
+    const int db = (f - f0) & 1;
+    const bool more = f + 1 < f1;
+    // the next position: this chain's next chunk, or the next chain's first
+    WalkPos nx = cur;
+    if (more) {
+      if (cur.k + 1 < cur.nchk) nx.k = cur.k + 1;
+      else nx = walk_locate<DENSE>(f + 1, seq_off, cmap, H, nseq, Q);
+    }
+    const int cnx = nx.cs + nx.k;
+    const int4 cin = uniform4(walk_map<DENSE>(cmap, cnx));
+    const bf16 *bfn = nx.hd == cur.hd ? bfw : bfw_of(nx.hd);
+    float s_end = 0.f;
+    WalkRows<Q> rows;
+    f4 S[NTW][NPT];
+#pragma unroll
+    for (int t = 0; t < NTW; ++t)
+#pragma unroll
+      for (int pt = 0; pt < NPT; ++pt) S[t][pt] = zero4();
+#pragma unroll
+    for (int ph = 0; ph < NPH; ++ph) {
+      // the next phase's loads first (this chunk's next rows, or the next
+      // position's first rows and its dt column)
+      if (ph + 1 < NPH) {
+        walk_issue_x<K>(x, ci, ph + 1, xstride, cur.hd, xl, smem + (xbuf ^ 1) * K::XB, wave);
+        walk_load_b<K>(bfw + (size_t)c * bfc, ph + 1, bq[(ph + 1) & 1]);
+      } else if (more) {
+        walk_issue_x<K>(x, cin, 0, xstride, nx.hd, xl, smem + (xbuf ^ 1) * K::XB, wave);
+        walk_issue_dt<K>(dt, cin, H, nx.hd, lds0 + K::OFF_DT + (db ^ 1) * K::DTN * 4, wave);
+        walk_load_b<K>(bfn + (size_t)cnx * bfc, 0, bq[(ph + 1) & 1]);
+      }
+      if (ph == 0)
+        s_end = walk_decay<Q>(
+            reinterpret_cast<const float *>(smem + K::OFF_DT + db * K::DTN * 4), w_l, a2, rows);
+      // S^T += sum over this phase's tokens of x_j (w_j B_j)^T
+      const char *xt = smem + xbuf * K::XB;
+#pragma unroll
+      for (int kk = 0; kk < KSP; ++kk) {
+        const int j0 = ph * JP + 32 * kk;
+        Frag<bf16> xa[NPT];
+        const char *xk = xt + 4 * kk * kBlk128;
+#pragma unroll
+        for (int pt = 0; pt < NPT; ++pt)
+          xa[pt] = frag_kmaj_at(xk, xo ^ (32 * pt), (xo ^ (32 * pt)) + 2 * kBlk128);
+        const f4 w0 = ld4(w_l + j0 + 4 * grp), w1 = ld4(w_l + j0 + 16 + 4 * grp);
+        Frag<bf16> bw[NTW];
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) {
+          const f8v bv = cvt_f8(bq[ph & 1][t][kk]);
+          bw[t].v = cvt_bf8(f8v{bv[0] * w0[0], bv[1] * w0[1], bv[2] * w0[2], bv[3] * w0[3],
+                                bv[4] * w1[0], bv[5] * w1[1], bv[6] * w1[2], bv[7] * w1[3]});
+        }
+#pragma unroll
+        for (int pt = 0; pt < NPT; ++pt)
+#pragma unroll
+          for (int t = 0; t < NTW; ++t) mma(S[t][pt], xa[pt], bw[t]);
+      }
+      // the next phase's loads have landed and this phase's buffers are free
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (ph == 0) {
+        // the state entering chunk c (from the piece's start), staged per wave
+        // for whole-row stores as in k_state_walk, and the s, dt, u rows
+        const size_t hco = ((size_t)c * H + cur.hd) * (size_t)(N * P);
+        char *hst = smem + K::OFF_HST + wave * K::HST_WAVE;
+#pragma unroll
+        for (int t = 0; t < NTW; ++t)
+#pragma unroll
+          for (int pt = 0; pt < NPT; ++pt)
+            *reinterpret_cast<bf16x4 *>(hst + (16 * t + col) * K::HST_PITCH + 32 * pt + 8 * grp) =
+                __builtin_convertvector(Hs[t][pt], bf16x4);
+        bf16 *hrow = hin + hco + (size_t)(16 * nt0) * P;
+#pragma unroll
+        for (int kk = 0; kk < 2 * NTW; ++kk) {
+          const int r = 8 * kk + (lane >> 3);
+          *reinterpret_cast<bf16x8 *>(hrow + (size_t)r * P + 8 * (lane & 7)) =
+              *reinterpret_cast<const bf16x8 *>(hst + r * K::HST_PITCH + 16 * (lane & 7));
+        }
+        if (wave == 0) walk_store_rows<Q>(rows, ((size_t)c * H + cur.hd) * Q, s_out, dt_out, u_out);
+      }
+      if constexpr (NPH % 2 == 1) {  // the next chunk's first phase starts from bq[0]
+        if (ph == NPH - 1) {
+#pragma unroll
+          for (int t = 0; t < NTW; ++t)
+#pragma unroll
+            for (int kk = 0; kk < KSP; ++kk) bq[0][t][kk] = bq[1][t][kk];
+        }
+      }
+      xbuf ^= 1;
+    }
+    // carry: H = 2^(s_end) H + S
+    const float a = __builtin_amdgcn_exp2f(fminf(s_end, 0.f));
+#pragma unroll
+    for (int t = 0; t < NTW; ++t)
+#pragma unroll
+      for (int pt = 0; pt < NPT; ++pt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) Hs[t][pt][q] = a * Hs[t][pt][q] + S[t][pt][q];
+    // the piece ends at its chain's last chunk or at the run's end: its state
+    // goes to seg_end at the piece's first position
+    if (!more || nx.k == 0) {
+#pragma unroll
+      for (int t = 0; t < NTW; ++t)
+#pragma unroll
+        for (int pt = 0; pt < NPT; ++pt)
+          st4(seg_end + (size_t)fp * (N * P) + (size_t)(16 * (nt0 + t) + col) * P + 16 * pt +
+                  4 * grp,
+              Hs[t][pt]);
+    }
+    if (more) {
+      if (nx.k == 0) {  // the next chain
+        cur = nx;
+        bfw = bfn;
+        a2 = A[cur.hd] * kLog2e;
+        reset_state();
+        fp = f + 1;
+      } else {
+        cur.k = nx.k;
+      }
+    }
+  }
+}
+
+// The entering states and the final state of walks by lists: per (sequence,
+// head), E = the state leaving the chain's first piece (walked from h0); for
+// each later piece (it starts at a run boundary, a multiple of W) the stored
+// entering states of its chunks get (decay since the piece's start) E added,
+// and E = (the piece's decay) E + the piece's own end state.  The last E is
+// the final state.  The corrected entering states are rounded to bf16 again.
+template <bool DENSE>
+__global__ __launch_bounds__(256) void k_walk_fixup_list(
+    const float *__restrict__ s_ws, const int *__restrict__ seq_off, ChunkMap cmap, int H, int NP,
+    int Q, int W, const float *__restrict__ seg_end, const float *__restrict__ h0,
+    bf16 *__restrict__ hin, float *h_out, float *h_out2) {
+  const int s = blockIdx.z, hd = blockIdx.y;
+  const int e = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (e >= NP) return;
+  int cs, nchk, cf0;
+  if constexpr (DENSE) {
+    nchk = (cmap.L + Q - 1) / Q;
+    cs = s * nchk;
+    cf0 = (s * H + hd) * nchk;
+  } else {
+    cs = seq_off[s];
+    nchk = seq_off[s + 1] - cs;
+    cf0 = H * cs + hd * nchk;
+  }
+  const size_t hofs = ((size_t)s * H + hd) * (size_t)NP + e;
+  f4 E;
+  if (nchk == 0) {  // an empty sequence keeps its state
+    E = h0 ? ld4(h0 + hofs) : zero4();
+  } else {
+    E = ld4(seg_end + (size_t)cf0 * NP + e);
+    for (int b = (cf0 / W + 1) * W; b < cf0 + nchk; b += W) {
+      const int b1 = min(b + W, cf0 + nchk);
+      float dec = 1.f;  // 2^(sum of s_end over the piece's chunks so far)
+      for (int f = b; f < b1; ++f) {
+        const size_t ch = (size_t)(cs + f - cf0) * H + hd;
+        bf16 *hp = hin + ch * (size_t)NP + e;
+        const f4 hv = ld4f(hp);
+        st4T(hp, hv + dec * E);
+        dec *= __builtin_amdgcn_exp2f(fminf(s_ws[ch * Q + Q - 1], 0.f));
+      }
+      E = dec * E + ld4(seg_end + (size_t)b * NP + e);
+    }
+  }
+  if (h_out) st4(h_out + hofs, E);
+  if (h_out2) st4(h_out2 + hofs, E);
+}
+
 // The entering states of a sequence whose chains were walked in segments
 // (the counts per head as the plan says), each after the first walked from a
 // zero state: the recurrence is linear in the entering
@@ -576,14 +876,16 @@ bool walk_supported(int P, int N, int Q, bool bf16) {
   return bf16 && P == 64 && N == 128 && Q >= 32 && Q <= 256;
 }
 
-// The walk pays when there are enough chains to fill the chip and each chain
-// is short: a chain is one workgroup streaming its sequence's chunks, so a
-// packed batch whose longest sequence is unknown on the host keeps the chunk
-// states (the variant bits force either way).
-bool walk_choice(int P, int N, int Q, bool bf16, int nseq, int H, bool packed, unsigned variant) {
+// The walk pays when there are enough chains to fill the chip (a packed batch
+// walks by lists, which even out its sequences' lengths).  A packed batch's
+// training forward keeps the chunk states: the list walk keeps no float32
+// entering states.  The variant bits force either way.
+bool walk_choice(int P, int N, int Q, bool bf16, int nseq, int H, bool packed, unsigned variant,
+                 bool training) {
   if (!walk_supported(P, N, Q, bf16) || (variant & SSD_VARIANT_STATE_CHUNKS)) return false;
   if (variant & SSD_VARIANT_STATE_WALK) return true;
-  return !packed && (long)nseq * H >= kWalkMinChains;
+  if (packed && training) return false;
+  return (long)nseq * H >= kWalkMinChains;
 }
 
 // Launch shape (compile-time constants): NH workgroups of NW waves per chain
@@ -695,6 +997,55 @@ static hipError_t run_walk_q(const PrefillArgs &a, const WorkspaceLayout &L, int
   return run_walk<Q, SSD_WALK_NH, SSD_WALK_JP, SSD_WALK_NW>(a, L, write_hout, sp, st);
 }
 
+// The walk by lists of a packed batch: as many runs as the chip holds
+// workgroups of the list kernel at once (at least 8 chunks a run), then the
+// fix-up.
+template <int Q>
+static hipError_t run_walk_list(const PrefillArgs &a, const WorkspaceLayout &L, int nc,
+                                bool write_hout, hipStream_t st) {
+  typedef WalkCfg<Q, 1, SSD_WALK_SEG_JP, SSD_WALK_SEG_NW> K;
+  constexpr bool dense = false;
+  const void *kern = (const void *)k_state_walk_list<Q, SSD_WALK_SEG_JP, SSD_WALK_SEG_NW, false>;
+  hipError_t e = set_lds_limit(kern);
+  if (e != hipSuccess) return e;
+  int dev = 0, ncu = 0, per_cu = 0;
+  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+  if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+    return e;
+  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * K::NW, K::LDS)) !=
+      hipSuccess)
+    return e;
+  const int slots = std::max(1, ncu * std::max(1, per_cu));
+  // positions: every chunk of every head (a packed batch: an upper bound, the
+  // kernel takes the exact count from the chunk offsets)
+  const long F = (long)a.H * nc;
+  if (F <= 0 || F >= (1L << 31) / 2) return hipErrorInvalidValue;
+  const int W = (int)std::max<long>(8, (F + slots - 1) / slots);
+  const int nlist = (int)((F + W - 1) / W);
+  char *ws = static_cast<char *>(a.workspace);
+  const bf16 *xp = (const bf16 *)a.x;
+  const float *dtp = a.dt, *Ap = a.A;
+  const bf16 *bp = reinterpret_cast<const bf16 *>(ws + L.bfrag);
+  const int *so = reinterpret_cast<const int *>(ws + L.seq_off);
+  ChunkMap cm{reinterpret_cast<const int4 *>(ws + L.info), 0, a.nseq, a.Q};
+  int H_ = a.H, G_ = a.G, nseq_ = a.nseq, F_ = (int)F, W_ = W, nl_ = nlist;
+  const float *h0p = a.h0;
+  float *sp = reinterpret_cast<float *>(ws + L.s), *dp = reinterpret_cast<float *>(ws + L.dt);
+  float *up = reinterpret_cast<float *>(ws + L.u);
+  bf16 *hp = reinterpret_cast<bf16 *>(ws + L.hin);
+  float *se = reinterpret_cast<float *>(ws + L.segend);
+  void *args[] = {&xp, &dtp, &Ap, &bp, &so, &cm, &H_, &G_, &nseq_, &F_, &W_, &nl_, &h0p,
+                  &sp, &dp, &up, &hp, &se};
+  e = hipLaunchKernel(kern, dim3(8u * (unsigned)((nlist + 7) / 8)), dim3(64 * K::NW), args, K::LDS,
+                      st);
+  if (e != hipSuccess) return e;
+  const int NP = K::N * K::P;
+  hipLaunchKernelGGL(k_walk_fixup_list<dense>, dim3((NP + 1023) / 1024, a.H, a.nseq), dim3(256), 0,
+                     st, (const float *)sp, so, cm, a.H, NP, a.Q, W, (const float *)se, a.h0, hp,
+                     write_hout ? a.h_out : nullptr, write_hout ? a.h_out2 : nullptr);
+  return hipGetLastError();
+}
+
 hipError_t launch_state_walk(const PrefillArgs &a, const WorkspaceLayout &L, int nc,
                              bool write_hout, hipStream_t st) {
   char *ws = static_cast<char *>(a.workspace);
@@ -705,6 +1056,15 @@ hipError_t launch_state_walk(const PrefillArgs &a, const WorkspaceLayout &L, int
                        (const bf16 *)a.B, cm, nc, a.G, a.Q, reinterpret_cast<bf16 *>(ws + L.bfrag));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+  }
+  if (a.cu != nullptr && a.hin32 == nullptr && nc > 0) {  // a packed batch, not training
+    switch (a.Q) {
+      case 32: return run_walk_list<32>(a, L, nc, write_hout, st);
+      case 64: return run_walk_list<64>(a, L, nc, write_hout, st);
+      case 128: return run_walk_list<128>(a, L, nc, write_hout, st);
+      case 256: return run_walk_list<256>(a, L, nc, write_hout, st);
+    }
+    return hipErrorInvalidValue;
   }
   SegPlan sp{1, 1, a.H};
   hipError_t e = hipErrorInvalidValue;

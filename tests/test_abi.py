@@ -86,16 +86,21 @@ def test_cbg_region_sized_by_groups():
 
 def test_plan_query():
     """The planning query names the kernels a call runs: the state walk for a
-    dense batch of at least 128 (sequence, head) chains (bf16, P 64, N 128,
-    chunk <= 256), the heads-streamed scan from 2048 (chunk, head) units."""
+    batch of at least 128 (sequence, head) chains (bf16, P 64, N 128,
+    chunk <= 256; a packed batch by lists), the heads-streamed scan from 2048
+    (chunk, head) units."""
     plan = ssd.plan
     assert plan(32768, 4, 80, 64, 128, 1, 256) == {"state": "walk", "scan": "heads"}
     assert plan(4096, 1, 24, 64, 128, 1, 256) == {"state": "chunks", "scan": "rows"}
     assert plan(32768, 4, 80, 64, 128, 1, 256, torch_f32()) == {"state": "chunks",
                                                                  "scan": "rows"}
     assert plan(32768, 4, 80, 64, 128, 1, 512) == {"state": "chunks", "scan": "rows"}
-    assert plan(85952, 8, 80, 64, 128, 1, 64, packed=True) == {"state": "chunks",
+    assert plan(85952, 8, 80, 64, 128, 1, 64, packed=True) == {"state": "walk",
                                                                 "scan": "heads"}
+    assert plan(85952, 8, 80, 64, 128, 1, 512, packed=True) == {"state": "chunks",
+                                                                 "scan": "rows"}
+    assert plan(4000, 1, 80, 64, 128, 1, 256, packed=True) == {"state": "chunks",
+                                                               "scan": "rows"}
     assert plan(4096, 1, 24, 64, 100, 1, 256) is None
 
 

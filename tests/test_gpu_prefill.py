@@ -83,7 +83,9 @@ def test_prefill_small(dtype, scan, state, case):
     _check(f"{dtype} {scan} {state}", y, ho, ry, rh, TOL[dtype])
 
 
-WALK_SEGMENT_CASES = [  # (lengths, dense, H, G, chunk): each walks in two segments
+# (lengths, dense, H, G, chunk): dense batches walk in segments, packed ones by
+# lists (runs of 8 or more chunk positions, cutting chains where they end)
+WALK_SEGMENT_CASES = [
     ([3000, 0, 40, 1500, 64], False, 8, 2, 64),  # empty, one-chunk, exactly one-chunk sequences
     ([571, 571], True, 8, 1, 64),                # 9 chunks a sequence: segments of 4 and 5
     ([2100, 700, 1], False, 6, 3, 128),          # one token alone in its segment pair
@@ -94,20 +96,24 @@ WALK_SEGMENT_CASES = [  # (lengths, dense, H, G, chunk): each walks in two segme
     # first heads in two segments, the rest in shorter ones
     ([2048, 2048], True, 160, 1, 256),
     ([3000, 1, 2600], False, 100, 2, 256),
+    # more chunk positions than 8 per resident workgroup: longer runs, a
+    # one-chunk chain between two cut ones
+    ([2000, 1500, 37], False, 80, 1, 64),
 ]
 
 
 @pytest.mark.parametrize("scan", ["rows", "heads"])
 @pytest.mark.parametrize("case", range(len(WALK_SEGMENT_CASES)))
 def test_prefill_walk_segments(case, scan):
-    """The state walk splits each sequence into two segments walked at once
-    (the second from a zero state) and corrects the second segment's entering
-    states and the final state afterwards: packed batches with empty,
-    one-chunk and one-token sequences, and dense batches with odd and even
-    chunk counts, through both chunk-scan kernels, every element against the
-    oracle, as are the chunk-parallel states on the same batch and each packed
-    sequence run alone (which may walk unsegmented); the stages run one by one
-    equal one call, bitwise."""
+    """The state walk cuts chains into pieces walked at once (each after a
+    chain's first from a zero state) and corrects the later pieces' entering
+    states and the final state afterwards -- dense batches in segments per
+    head, packed batches by runs of chunk positions: packed batches with
+    empty, one-chunk and one-token sequences, and dense batches with odd and
+    even chunk counts, through both chunk-scan kernels, every element against
+    the oracle, as are the chunk-parallel states on the same batch and each
+    packed sequence run alone (which may walk unsegmented); the stages run
+    one by one equal one call, bitwise."""
     import torch
     from state_space_model_amd import ssd
     lengths, dense, H, G, chunk = WALK_SEGMENT_CASES[case]
@@ -127,10 +133,10 @@ def test_prefill_walk_segments(case, scan):
     for st in (1, 2, 4, 8):
         ssd.prefill(*args, y=y2, h_out=h2, workspace=ws, stages=st, state="walk", **kw)
     torch.cuda.synchronize()
-    _check("walk, two segments", y.cpu().numpy(), ho.cpu().numpy(), ry, rh, TOL["bf16"])
+    _check("walk, cut chains", y.cpu().numpy(), ho.cpu().numpy(), ry, rh, TOL["bf16"])
     _check("chunk states", yc.cpu().numpy(), hc.cpu().numpy(), ry, rh, TOL["bf16"])
     assert torch.equal(y, y2) and torch.equal(ho, h2)
-    if not dense:  # each sequence alone (one sequence: its own two segments)
+    if not dense:  # each sequence alone (one sequence: cut by its own runs)
         cu = d["cu_seqlens"]
         for k in range(len(lengths)):
             a, b = int(cu[k]), int(cu[k + 1])
@@ -313,7 +319,10 @@ def test_stages_separately_equal_one_call():
 @pytest.mark.parametrize("scan", ["rows", "heads"])
 def test_deterministic_and_varlen_equals_solo(scan, state):
     """Run-to-run bitwise determinism; a packed batch equals each sequence run
-    alone, bitwise; h_out may be the h0 buffer itself."""
+    alone, bitwise; h_out may be the h0 buffer itself.  (The walk by lists
+    cuts a packed batch's chains where its runs of 8 chunk positions end;
+    here each run holds whole chains -- 4 heads x 2, 1 + 1, and 2 x 4 chunks
+    -- so nothing is rounded twice and the equality is exact.)"""
     import torch
     from state_space_model_amd import ssd
     lengths = [333, 64, 1, 900]
