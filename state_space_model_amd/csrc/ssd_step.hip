@@ -39,11 +39,23 @@ __global__ __launch_bounds__(256) void k_step(const T *__restrict__ x, const flo
   const int tid = threadIdx.x, q = tid % TPR, r0 = tid / TPR;
   const T *Bp = B + (size_t)b * bcs + (size_t)g * N;  // x, B, C rows are xbs / bcs apart
   const T *Cp = C + (size_t)b * bcs + (size_t)g * N;
+  const size_t bh = (size_t)b * H + hd;
+  float *hp = h + bh * (size_t)N * P + pc + 4 * q;
+  // U rows per thread in flight (all of them at N = 128 with the halves of p);
+  // the first U are loaded before B and C are staged, so that the two
+  // round trips overlap
+  constexpr int U = PS == 1 ? 8 : 4;
+  const bool first = r0 + (U - 1) * RPP < N;
+  f4 v0[U];
+  if (first) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      v0[u] = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(hp + (size_t)(r0 + u * RPP) * P));
+  }
   for (int n = tid; n < N; n += 256) {
     Bsh[n] = to_f32(Bp[n]);
     Csh[n] = to_f32(Cp[n]);
   }
-  const size_t bh = (size_t)b * H + hd;
   const float dtv = dt[bh];
   const float a = expf(fminf(dtv * A[hd], 0.f));
   const f4 xv = ld4f(x + (size_t)b * xbs + (size_t)hd * P + pc + 4 * q);
@@ -52,11 +64,21 @@ __global__ __launch_bounds__(256) void k_step(const T *__restrict__ x, const flo
   for (int e = 0; e < 4; ++e) dx[e] = dtv * xv[e];
   __syncthreads();
 
-  float *hp = h + bh * (size_t)N * P + pc + 4 * q;
   f4 yacc = zero4();
   int n = r0;
-  // U rows per thread in flight (all of them at N = 128 with the halves of p)
-  constexpr int U = PS == 1 ? 8 : 4;
+  if (first) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float bn = Bsh[n + u * RPP], cn = Csh[n + u * RPP];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v0[u][e] = a * v0[u][e] + dx[e] * bn;
+        yacc[e] += cn * v0[u][e];
+      }
+      __builtin_nontemporal_store(v0[u], reinterpret_cast<f4 *>(hp + (size_t)(n + u * RPP) * P));
+    }
+    n += U * RPP;
+  }
   for (; n + (U - 1) * RPP < N; n += U * RPP) {
     f4 v[U];
 #pragma unroll
