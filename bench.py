@@ -7,7 +7,10 @@ heads, headdim 64, d_state 128, 1 group, chunk 256, bf16 operands, an
 initial state per sequence) through the prefill kernels, then one decode
 token for the 4 sequences from the prefill's final states through the
 decode kernel.  `value` is prefill tokens/s over whole steps, the inputs
-resident in device memory.  Inside the timed region every kernel of the step
+resident in device memory.  Before its W warm-up steps the step runs for
+--preheat seconds (1.5 by default; the count is reported), so that the K
+timed steps see the clocks the GPU holds under sustained load rather than
+the swing that follows idle time.  Inside the timed region every kernel of the step
 is bracketed by HIP events on the stream it runs on, which gives each
 kernel's average duration; the roofline object is the longest one's
 algorithmic bytes (or flops) per launch over that duration.  After timing, the
@@ -21,8 +24,8 @@ every chunk size (`prefill_long_context_varlen`), the Codestral-7B decode
 (`decode`, `decode_multi_step`, `decode_layer_step`), the Mamba-1 selective
 scan, the gated delta rule and forward + backward training steps.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--sections a,b,...]
-       [--no-cpu-baseline] [--no-parity]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--preheat S]
+       [--sections a,b,...] [--no-cpu-baseline] [--no-parity]
 """
 import argparse
 import json
@@ -51,6 +54,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--preheat", type=float, default=1.5, metavar="SECONDS",
+                    help="run the headline step for this long before its warm-up steps, so "
+                         "that the timed steps see the GPU's sustained-load clocks")
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--sections", default=",".join(SECTIONS),
                     help="comma-separated subset of " + ",".join(SECTIONS))
@@ -357,6 +363,15 @@ def headline(args, torch, inputs, ssd, dev):
             run_decode()
 
         log(args, f"headline: {wl.name} T={T} nseq={nseq} H={wl.H} P={wl.P} N={wl.N} Q={wl.chunk}")
+        # sustained load first: from idle, and for a few ms after other work,
+        # the clocks swing (the chunk scan takes 290 -> 360 -> 285 us over the
+        # first ~40 steps) before settling
+        pre, t_end = 0, time.perf_counter() + args.preheat
+        while time.perf_counter() < t_end:
+            for _ in range(8):
+                step()
+            torch.cuda.synchronize()
+            pre += 8
         for _ in range(args.warmup):
             step()
         torch.cuda.synchronize()
@@ -390,7 +405,9 @@ def headline(args, torch, inputs, ssd, dev):
                   "headdim": wl.P, "d_state": wl.N, "groups": wl.G, "chunk": wl.chunk,
                   "h0": "given", "step": "prefill + next-token decode of every sequence"}
         config["kernels"] = plan
+        preheat = {"seconds": args.preheat, "steps": pre}
         return dict(value=value, ms_step=ms_step, ms_step_graph=ms_step_graph, config=config,
+                    preheat=preheat,
                     dominant=dominant, kernels=kernels, prefill=prefill, parity=parity, cpu=cpu)
 
     return go
@@ -1105,6 +1122,7 @@ def main():
                                              "traffic")} | {"kernel": dom["kernel"],
                                                             "avg_us": dom["avg_us"]},
             "ms_per_step_graph": round(hl["ms_step_graph"], 5),
+            "preheat": hl["preheat"],
             "prefill": hl["prefill"],
             "prefill_mfma_util": hl["prefill"]["mfma_frac"],
             "kernels": hl["kernels"],
