@@ -41,11 +41,12 @@ __global__ __launch_bounds__(256) void k_step(const T *__restrict__ x, const flo
   const T *Cp = C + (size_t)b * bcs + (size_t)g * N;
   const size_t bh = (size_t)b * H + hd;
   float *hp = h + bh * (size_t)N * P + pc + 4 * q;
-  // U rows per thread in flight (all of them at N = 128 with the halves of p);
-  // the first U are loaded before B and C are staged, so that the two
-  // round trips overlap
+  // U rows per thread in flight (all of them at N = 128 with the halves of p).
+  // With the columns split (few blocks, latency-bound) the first U are loaded
+  // before B and C are staged, so that the two round trips overlap; with many
+  // blocks that only holds registers longer (the Codestral step: 1 % slower)
   constexpr int U = PS == 1 ? 8 : 4;
-  const bool first = r0 + (U - 1) * RPP < N;
+  const bool first = PS > 1 && r0 + (U - 1) * RPP < N;
   f4 v0[U];
   if (first) {
 #pragma unroll
