@@ -534,44 +534,32 @@ __global__ __launch_bounds__(64 * NW_) void k_state_walk(
 // k_walk_fixup_list then adds each piece's share of the pieces before it (the
 // recurrence is linear in the entering state).  Whole chains would leave the
 // longest sequence's chains running alone long after the rest; here every
-// workgroup has the same number of chunks.  (For a dense batch the chains
-// are cut at the same chunk in every head instead -- SegPlan -- which keeps
-// the heads' chunk positions aligned and reads x rows and B fragments
-// together.)
+// workgroup has the same number of chunks.  (A dense batch's chains are cut
+// at the same chunk in every head instead -- SegPlan -- which keeps the
+// heads' chunk positions aligned and reads x rows and B fragments together.)
 
 struct WalkPos {
   int s, hd, k, nchk, cs;  // sequence, head, chunk in the chain, chunks in it, first chunk
 };
 
-// The chain and chunk at position f (f below the total count).
-template <bool DENSE>
-__device__ __forceinline__ WalkPos walk_locate(int f, const int *__restrict__ seq_off,
-                                               ChunkMap cmap, int H, int nseq, int Q) {
+// The chain and chunk at position f (f below the total count): the last
+// sequence whose positions start at or before f (an empty sequence shares its
+// start with the next one, so it is never the last), then head and chunk.
+__device__ __forceinline__ WalkPos walk_locate(int f, const int *__restrict__ seq_off, int H,
+                                               int nseq) {
   WalkPos w;
-  if constexpr (DENSE) {
-    const int cps = (cmap.L + Q - 1) / Q;
-    const int p = f / cps;
-    w.k = f - p * cps;
-    w.s = p / H;
-    w.hd = p - w.s * H;
-    w.nchk = cps;
-    w.cs = w.s * cps;
-  } else {
-    // the last sequence whose positions start at or before f (an empty
-    // sequence shares its start with the next one, so it is never the last)
-    int lo = 0, hi = nseq - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (H * seq_off[mid] <= f) lo = mid;
-      else hi = mid - 1;
-    }
-    w.s = lo;
-    w.cs = seq_off[lo];
-    w.nchk = seq_off[lo + 1] - w.cs;
-    const int r = f - H * w.cs;
-    w.hd = r / w.nchk;
-    w.k = r - w.hd * w.nchk;
+  int lo = 0, hi = nseq - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (H * seq_off[mid] <= f) lo = mid;
+    else hi = mid - 1;
   }
+  w.s = lo;
+  w.cs = seq_off[lo];
+  w.nchk = seq_off[lo + 1] - w.cs;
+  const int r = f - H * w.cs;
+  w.hd = r / w.nchk;
+  w.k = r - w.hd * w.nchk;
   w.s = __builtin_amdgcn_readfirstlane(w.s);
   w.hd = __builtin_amdgcn_readfirstlane(w.hd);
   w.k = __builtin_amdgcn_readfirstlane(w.k);
@@ -586,7 +574,7 @@ __device__ __forceinline__ int4 uniform4(int4 v) {
                    __builtin_amdgcn_readfirstlane(v.z), __builtin_amdgcn_readfirstlane(v.w));
 }
 
-template <int Q, int JP_, int NW_, bool DENSE>
+template <int Q, int JP_, int NW_>
 __global__ __launch_bounds__(64 * NW_) void k_state_walk_list(
     const bf16 *__restrict__ x, const float *__restrict__ dt, const float *__restrict__ A,
     const bf16 *__restrict__ bfr, const int *__restrict__ seq_off, ChunkMap cmap, int H, int G,
@@ -601,7 +589,7 @@ __global__ __launch_bounds__(64 * NW_) void k_state_walk_list(
   const int per = (nlist + 7) >> 3;
   const int li = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
   if (li >= nlist) return;
-  const int Fr = DENSE ? F : min(F, H * __builtin_amdgcn_readfirstlane(seq_off[nseq]));
+  const int Fr = min(F, H * __builtin_amdgcn_readfirstlane(seq_off[nseq]));
   const int f0 = li * W, f1 = min(Fr, f0 + W);
   if (f0 >= f1) return;
   const int lane = threadIdx.x & 63, grp = lane >> 4, col = lane & 15;
@@ -621,7 +609,7 @@ __global__ __launch_bounds__(64 * NW_) void k_state_walk_list(
   const int xbk = 4 * (grp & 1) + c4;
   const int xo = (grp >> 1) * kBlk128 + xbk * 128 + cq + 32 * swz8(xbk);
 
-  WalkPos cur = walk_locate<DENSE>(f0, seq_off, cmap, H, nseq, Q);
+  WalkPos cur = walk_locate(f0, seq_off, H, nseq);
   const bf16 *bfw = bfw_of(cur.hd);
   float a2 = A[cur.hd] * kLog2e;
   f4 Hs[NTW][NPT];
@@ -641,7 +629,7 @@ __global__ __launch_bounds__(64 * NW_) void k_state_walk_list(
   typedef bf16x8 BF[NTW][KSP];
   BF bq[2];
   {
-    const int4 ci = walk_map<DENSE>(cmap, cur.cs + cur.k);
+    const int4 ci = walk_map<false>(cmap, cur.cs + cur.k);
     walk_issue_dt<K>(dt, ci, H, cur.hd, lds0 + K::OFF_DT, wave);
     walk_issue_x<K>(x, ci, 0, xstride, cur.hd, xl, smem, wave);
     walk_load_b<K>(bfw + (size_t)(cur.cs + cur.k) * bfc, 0, bq[0]);
@@ -652,17 +640,17 @@ __global__ __launch_bounds__(64 * NW_) void k_state_walk_list(
   int xbuf = 0;
   for (int f = f0; f < f1; ++f) {
     const int c = cur.cs + cur.k;
-    const int4 ci = uniform4(walk_map<DENSE>(cmap, c));
+    const int4 ci = uniform4(walk_map<false>(cmap, c));
     const int db = (f - f0) & 1;
     const bool more = f + 1 < f1;
     // the next position: this chain's next chunk, or the next chain's first
     WalkPos nx = cur;
     if (more) {
       if (cur.k + 1 < cur.nchk) nx.k = cur.k + 1;
-      else nx = walk_locate<DENSE>(f + 1, seq_off, cmap, H, nseq, Q);
+      else nx = walk_locate(f + 1, seq_off, H, nseq);
     }
     const int cnx = nx.cs + nx.k;
-    const int4 cin = uniform4(walk_map<DENSE>(cmap, cnx));
+    const int4 cin = uniform4(walk_map<false>(cmap, cnx));
     const bf16 *bfn = nx.hd == cur.hd ? bfw : bfw_of(nx.hd);
     float s_end = 0.f;
     WalkRows<Q> rows;
@@ -781,24 +769,15 @@ __global__ __launch_bounds__(64 * NW_) void k_state_walk_list(
 // entering states of its chunks get (decay since the piece's start) E added,
 // and E = (the piece's decay) E + the piece's own end state.  The last E is
 // the final state.  The corrected entering states are rounded to bf16 again.
-template <bool DENSE>
 __global__ __launch_bounds__(256) void k_walk_fixup_list(
-    const float *__restrict__ s_ws, const int *__restrict__ seq_off, ChunkMap cmap, int H, int NP,
-    int Q, int W, const float *__restrict__ seg_end, const float *__restrict__ h0,
-    bf16 *__restrict__ hin, float *h_out, float *h_out2) {
+    const float *__restrict__ s_ws, const int *__restrict__ seq_off, int H, int NP, int Q, int W,
+    const float *__restrict__ seg_end, const float *__restrict__ h0, bf16 *__restrict__ hin,
+    float *h_out, float *h_out2) {
   const int s = blockIdx.z, hd = blockIdx.y;
   const int e = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (e >= NP) return;
-  int cs, nchk, cf0;
-  if constexpr (DENSE) {
-    nchk = (cmap.L + Q - 1) / Q;
-    cs = s * nchk;
-    cf0 = (s * H + hd) * nchk;
-  } else {
-    cs = seq_off[s];
-    nchk = seq_off[s + 1] - cs;
-    cf0 = H * cs + hd * nchk;
-  }
+  const int cs = seq_off[s], nchk = seq_off[s + 1] - cs;
+  const int cf0 = H * cs + hd * nchk;  // the chain's first position
   const size_t hofs = ((size_t)s * H + hd) * (size_t)NP + e;
   f4 E;
   if (nchk == 0) {  // an empty sequence keeps its state
@@ -1004,8 +983,7 @@ template <int Q>
 static hipError_t run_walk_list(const PrefillArgs &a, const WorkspaceLayout &L, int nc,
                                 bool write_hout, hipStream_t st) {
   typedef WalkCfg<Q, 1, SSD_WALK_SEG_JP, SSD_WALK_SEG_NW> K;
-  constexpr bool dense = false;
-  const void *kern = (const void *)k_state_walk_list<Q, SSD_WALK_SEG_JP, SSD_WALK_SEG_NW, false>;
+  const void *kern = (const void *)k_state_walk_list<Q, SSD_WALK_SEG_JP, SSD_WALK_SEG_NW>;
   hipError_t e = set_lds_limit(kern);
   if (e != hipSuccess) return e;
   int dev = 0, ncu = 0, per_cu = 0;
@@ -1040,8 +1018,8 @@ static hipError_t run_walk_list(const PrefillArgs &a, const WorkspaceLayout &L, 
                       st);
   if (e != hipSuccess) return e;
   const int NP = K::N * K::P;
-  hipLaunchKernelGGL(k_walk_fixup_list<dense>, dim3((NP + 1023) / 1024, a.H, a.nseq), dim3(256), 0,
-                     st, (const float *)sp, so, cm, a.H, NP, a.Q, W, (const float *)se, a.h0, hp,
+  hipLaunchKernelGGL(k_walk_fixup_list, dim3((NP + 1023) / 1024, a.H, a.nseq), dim3(256), 0, st,
+                     (const float *)sp, so, a.H, NP, a.Q, W, (const float *)se, a.h0, hp,
                      write_hout ? a.h_out : nullptr, write_hout ? a.h_out2 : nullptr);
   return hipGetLastError();
 }
