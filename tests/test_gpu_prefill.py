@@ -60,6 +60,7 @@ SMALL = [  # (lengths, H, P, N, G, chunk, h0)
     ([130, 45], 4, 64, 128, 2, 32, True),   # block-swizzled tiles at chunk 32 (two waves)
     ([300, 129, 77], 4, 64, 128, 2, 128, True),  # C.B^T per (chunk, group) at chunk 128
     ([700, 1, 300], 6, 64, 128, 3, 256, True),   # ... and at chunk 256, three groups
+    ([900, 0, 350, 1], 4, 64, 128, 1, 64, False),  # no h0: the walk's cut chains from zero
 ]
 
 
