@@ -540,13 +540,14 @@ __global__ __launch_bounds__(64 * NW_) void k_state_walk(
 
 struct WalkPos {
   int s, hd, k, nchk, cs;  // sequence, head, chunk in the chain, chunks in it, first chunk
+  int t0, t1;              // the sequence's tokens t0 .. t1 - 1
 };
 
 // The chain and chunk at position f (f below the total count): the last
 // sequence whose positions start at or before f (an empty sequence shares its
 // start with the next one, so it is never the last), then head and chunk.
-__device__ __forceinline__ WalkPos walk_locate(int f, const int *__restrict__ seq_off, int H,
-                                               int nseq) {
+__device__ __forceinline__ WalkPos walk_locate(int f, const int *__restrict__ seq_off,
+                                               const int *__restrict__ cu, int H, int nseq) {
   WalkPos w;
   int lo = 0, hi = nseq - 1;
   while (lo < hi) {
@@ -565,22 +566,26 @@ __device__ __forceinline__ WalkPos walk_locate(int f, const int *__restrict__ se
   w.k = __builtin_amdgcn_readfirstlane(w.k);
   w.nchk = __builtin_amdgcn_readfirstlane(w.nchk);
   w.cs = __builtin_amdgcn_readfirstlane(w.cs);
+  w.t0 = __builtin_amdgcn_readfirstlane(cu[w.s]);
+  w.t1 = __builtin_amdgcn_readfirstlane(cu[w.s + 1]);
   return w;
 }
 
-// A chunk-map entry made wave-uniform (scalar registers).
-__device__ __forceinline__ int4 uniform4(int4 v) {
-  return make_int4(__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y),
-                   __builtin_amdgcn_readfirstlane(v.z), __builtin_amdgcn_readfirstlane(v.w));
+// The chunk-map entry {sequence, first token, length, chunk in the sequence}
+// of a position, by arithmetic (a map entry loaded inside the walk's loop
+// would be waited for with nothing else in flight: a round trip per chunk).
+template <int Q> __device__ __forceinline__ int4 walk_entry(const WalkPos &p) {
+  const int t = p.t0 + p.k * Q;
+  return make_int4(p.s, t, min(Q, p.t1 - t), p.k);
 }
 
 template <int Q, int JP_, int NW_>
 __global__ __launch_bounds__(64 * NW_) void k_state_walk_list(
     const bf16 *__restrict__ x, const float *__restrict__ dt, const float *__restrict__ A,
-    const bf16 *__restrict__ bfr, const int *__restrict__ seq_off, ChunkMap cmap, int H, int G,
-    int nseq, int F, int W, int nlist, const float *__restrict__ h0, float *__restrict__ s_out,
-    float *__restrict__ dt_out, float *__restrict__ u_out, bf16 *__restrict__ hin,
-    float *__restrict__ seg_end) {
+    const bf16 *__restrict__ bfr, const int *__restrict__ seq_off, const int *__restrict__ cu,
+    int H, int G, int nseq, int F, int W, int nlist, const float *__restrict__ h0,
+    float *__restrict__ s_out, float *__restrict__ dt_out, float *__restrict__ u_out,
+    bf16 *__restrict__ hin, float *__restrict__ seg_end) {
   typedef WalkCfg<Q, 1, JP_, NW_> K;
   constexpr int P = K::P, N = K::N, NTW = K::NTW, NPT = P / 16, KSP = K::KSP, NPH = K::NPH;
   constexpr int NTL = N / 16, JP = K::JP;
@@ -609,7 +614,7 @@ __global__ __launch_bounds__(64 * NW_) void k_state_walk_list(
   const int xbk = 4 * (grp & 1) + c4;
   const int xo = (grp >> 1) * kBlk128 + xbk * 128 + cq + 32 * swz8(xbk);
 
-  WalkPos cur = walk_locate(f0, seq_off, H, nseq);
+  WalkPos cur = walk_locate(f0, seq_off, cu, H, nseq);
   const bf16 *bfw = bfw_of(cur.hd);
   float a2 = A[cur.hd] * kLog2e;
   f4 Hs[NTW][NPT];
@@ -629,7 +634,7 @@ __global__ __launch_bounds__(64 * NW_) void k_state_walk_list(
   typedef bf16x8 BF[NTW][KSP];
   BF bq[2];
   {
-    const int4 ci = walk_map<false>(cmap, cur.cs + cur.k);
+    const int4 ci = walk_entry<Q>(cur);
     walk_issue_dt<K>(dt, ci, H, cur.hd, lds0 + K::OFF_DT, wave);
     walk_issue_x<K>(x, ci, 0, xstride, cur.hd, xl, smem, wave);
     walk_load_b<K>(bfw + (size_t)(cur.cs + cur.k) * bfc, 0, bq[0]);
@@ -640,17 +645,24 @@ __global__ __launch_bounds__(64 * NW_) void k_state_walk_list(
   int xbuf = 0;
   for (int f = f0; f < f1; ++f) {
     const int c = cur.cs + cur.k;
-    const int4 ci = uniform4(walk_map<false>(cmap, c));
+    const int4 ci = walk_entry<Q>(cur);
     const int db = (f - f0) & 1;
     const bool more = f + 1 < f1;
-    // the next position: this chain's next chunk, or the next chain's first
+    // the next position: this chain's next chunk, the next head's first, or
+    // (searched for, once per sequence) the next sequence's
     WalkPos nx = cur;
     if (more) {
-      if (cur.k + 1 < cur.nchk) nx.k = cur.k + 1;
-      else nx = walk_locate(f + 1, seq_off, H, nseq);
+      if (cur.k + 1 < cur.nchk) {
+        nx.k = cur.k + 1;
+      } else if (cur.hd + 1 < H) {
+        nx.hd = cur.hd + 1;
+        nx.k = 0;
+      } else {
+        nx = walk_locate(f + 1, seq_off, cu, H, nseq);
+      }
     }
     const int cnx = nx.cs + nx.k;
-    const int4 cin = uniform4(walk_map<false>(cmap, cnx));
+    const int4 cin = walk_entry<Q>(nx);
     const bf16 *bfn = nx.hd == cur.hd ? bfw : bfw_of(nx.hd);
     float s_end = 0.f;
     WalkRows<Q> rows;
@@ -1005,14 +1017,14 @@ static hipError_t run_walk_list(const PrefillArgs &a, const WorkspaceLayout &L, 
   const float *dtp = a.dt, *Ap = a.A;
   const bf16 *bp = reinterpret_cast<const bf16 *>(ws + L.bfrag);
   const int *so = reinterpret_cast<const int *>(ws + L.seq_off);
-  ChunkMap cm{reinterpret_cast<const int4 *>(ws + L.info), 0, a.nseq, a.Q};
+  const int *cup = a.cu;
   int H_ = a.H, G_ = a.G, nseq_ = a.nseq, F_ = (int)F, W_ = W, nl_ = nlist;
   const float *h0p = a.h0;
   float *sp = reinterpret_cast<float *>(ws + L.s), *dp = reinterpret_cast<float *>(ws + L.dt);
   float *up = reinterpret_cast<float *>(ws + L.u);
   bf16 *hp = reinterpret_cast<bf16 *>(ws + L.hin);
   float *se = reinterpret_cast<float *>(ws + L.segend);
-  void *args[] = {&xp, &dtp, &Ap, &bp, &so, &cm, &H_, &G_, &nseq_, &F_, &W_, &nl_, &h0p,
+  void *args[] = {&xp, &dtp, &Ap, &bp, &so, &cup, &H_, &G_, &nseq_, &F_, &W_, &nl_, &h0p,
                   &sp, &dp, &up, &hp, &se};
   e = hipLaunchKernel(kern, dim3(8u * (unsigned)((nlist + 7) / 8)), dim3(64 * K::NW), args, K::LDS,
                       st);
