@@ -179,14 +179,19 @@ def graph_ms(torch, fn, reps, per_graph):
     torch.cuda.synchronize()
     # the first graph timed in a process replays about 10 % slower than later
     # ones of the same launches (measured: 545, then 502, 497, 494 us a step at
-    # the 2.7B layer): one is captured, timed and dropped first
+    # the 2.7B layer): one is captured, timed and dropped first; and each is
+    # replayed for 0.2 s before it is timed (capture leaves the GPU idle, and
+    # the clocks swing for a few ms after idle time)
     for _ in range(2):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for _ in range(per_graph):
                 fn()
-        g.replay()
-        torch.cuda.synchronize()
+        t_end = time.perf_counter() + 0.2
+        while time.perf_counter() < t_end:
+            for _ in range(4):
+                g.replay()
+            torch.cuda.synchronize()
         ms = time_loop(torch, g.replay, reps) / per_graph
         del g
     return ms
@@ -195,23 +200,23 @@ def graph_ms(torch, fn, reps, per_graph):
 def timed_steps(torch, parts, steps):
     """Run `steps` steps of the launches in `parts` ((name, fn) in order) on the
     current stream, an event recorded before the first launch and after each
-    one.  Returns (ms per whole step, {name: average ms of that launch})."""
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)]
-           for _ in range(steps)]
+    one (the event that ends a step also starts the next).  Returns (ms per
+    whole step, {name: average ms of that launch})."""
+    n = len(parts)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps * n + 1)]
     # each event recorded once before the timed region: a first record costs
     # the host more than later ones, which would leave gaps between launches
-    for row in evs:
-        for e in row:
-            e.record()
+    for e in evs:
+        e.record()
     torch.cuda.synchronize()
+    evs[0].record()
     for k in range(steps):
-        evs[k][0].record()
         for i, (_, fn) in enumerate(parts):
             fn()
-            evs[k][i + 1].record()
+            evs[k * n + i + 1].record()
     torch.cuda.synchronize()
-    total = evs[0][0].elapsed_time(evs[-1][-1]) / steps
-    per = {name: sum(evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(steps)) / steps
+    total = evs[0].elapsed_time(evs[-1]) / steps
+    per = {name: sum(evs[k * n + i].elapsed_time(evs[k * n + i + 1]) for k in range(steps)) / steps
            for i, (name, _) in enumerate(parts)}
     return total, per
 
@@ -379,11 +384,14 @@ def headline(args, torch, inputs, ssd, dev):
         ms_step, kern_ms = timed_steps(torch, parts, args.steps)
         ms_prefill = sum(kern_ms[n] for n, _ in stages)
         value = T / (ms_step * 1e-3)
-        # outputs of the last timed step, for the parity check below
+        # the same step replayed from a HIP graph (no host launch cost), before
+        # the host copies below leave the GPU idle; every step computes the
+        # same outputs from the same inputs, so the replays leave them as the
+        # timed steps did
+        ms_step_graph = graph_ms(torch, step, reps=5, per_graph=2)
+        # outputs of the last step, for the parity check below
         y_h = y.cpu().numpy()
         yd_h, h_h = yd.cpu().numpy(), h_out.cpu().numpy()
-        # the same step replayed from a HIP graph (no host launch cost)
-        ms_step_graph = graph_ms(torch, step, reps=5, per_graph=2)
 
         work = prefill_work(wl, T, nseq, h0=True, plan=plan)
         work["decode_step"] = step_work(nseq, wl.H, wl.P, wl.N, wl.G, 2)
