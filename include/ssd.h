@@ -121,7 +121,11 @@ unsigned ssd_scan_prefill_plan(int64_t total_tokens, int nseq, int H, int P, int
  *   h_out    [nseq][H][N][P] float32    final states, or NULL to skip; may be
  *                                        the same pointer as h0 (read first)
  *   cu_seqlens  device int32 [nseq+1], cu[0] = 0, non-decreasing, cu[nseq] = T;
- *            or NULL for a dense batch of nseq sequences of T/nseq tokens each
+ *            or NULL for a dense batch of nseq sequences of T/nseq tokens each.
+ *            The values are not checked on the host (they live on the device);
+ *            the kernels give a sequence that starts below 0 or ends past T no
+ *            chunks and never index past the buffers the other arguments size,
+ *            but the outputs of a malformed array are unspecified
  *   chunk    chunk length Q; the result is the same for every supported Q up
  *            to floating-point reassociation
  *   workspace / workspace_bytes   device scratch of at least

@@ -68,7 +68,8 @@ __device__ int block_incl_scan(int v, int *sh, int &total) {
 // Resolve chunk c of the packed batch into {seq, t0, len, index} (block-wide;
 // O(nseq / blockDim) block scans).  Block (0, 0) also writes seq_off.
 __device__ int4 locate_chunk(const int32_t *__restrict__ cu, int nseq, int L_dense, int64_t T,
-                             int Q, int c, int *__restrict__ seq_off, bool write_off) {
+                             int Q, int c, int nc_max, int *__restrict__ seq_off,
+                             bool write_off) {
   __shared__ int sh_scan[16];
   __shared__ int4 sh_info;
   const int tid = threadIdx.x;
@@ -100,10 +101,13 @@ __device__ int4 locate_chunk(const int32_t *__restrict__ cu, int nseq, int L_den
         const int k = c - running - excl;
         sh_info = make_int4(s, start + k * Q, min(Q, len - k * Q), k);
       }
-      if (write_off && s < nseq) seq_off[s] = running + excl;
+      // chunk offsets clamped to the workspace's chunk count: overlapping
+      // sequences (cu decreasing somewhere) could otherwise ask for more
+      // chunks than the buffers hold
+      if (write_off && s < nseq) seq_off[s] = min(running + excl, nc_max);
       running += total;
     }
-    if (write_off && tid == 0) seq_off[nseq] = running;
+    if (write_off && tid == 0) seq_off[nseq] = min(running, nc_max);
   }
   __syncthreads();
   return sh_info;
@@ -117,7 +121,7 @@ __global__ __launch_bounds__(256) void k_chunk_map(const int32_t *__restrict__ c
                                                    int4 *__restrict__ info_out,
                                                    int *__restrict__ seq_off) {
   const int c = blockIdx.x;
-  const int4 ci = locate_chunk(cu, nseq, 0, T, Q, c, seq_off, blockIdx.x == 0);
+  const int4 ci = locate_chunk(cu, nseq, 0, T, Q, c, nc_max, seq_off, blockIdx.x == 0);
   if (c < nc_max && threadIdx.x == 0) info_out[c] = ci.x < 0 ? make_int4(0, 0, 0, 0) : ci;
 }
 
