@@ -391,7 +391,10 @@ int ssd_scan_prefill_backward_saved(const void *x, const float *dt, const float 
  *   h0       [nseq][H][V][K] float32  initial states, or NULL for zeros
  *   o        [T][H][V]       float32  output (must not alias any input)
  *   h_out    [nseq][H][V][K] float32  final states, or NULL; may be h0
- *   cu_seqlens  device int32 [nseq+1] or NULL (dense: nseq sequences of T/nseq)
+ *   cu_seqlens  device int32 [nseq+1] or NULL (dense: nseq sequences of T/nseq);
+ *            as for the prefill (non-decreasing, cu[nseq] = T); values outside
+ *            0 .. T are clamped into it, so no access leaves the buffers, but
+ *            the outputs of a malformed array are unspecified
  * Supported: K in {64,128,256}, V a multiple of 16 up to 1024, H % G == 0.
  * Arithmetic and the state are float32.  No workspace.  Splitting a sequence
  * and passing h_out on as h0 gives the same result as one call.

@@ -43,8 +43,8 @@ __global__ __launch_bounds__(256) void k_gdn(const T *__restrict__ q, const T *_
                                              const float *__restrict__ g,
                                              const float *__restrict__ beta, const float *h0,
                                              float *__restrict__ o, float *h_out,
-                                             const int32_t *__restrict__ cu, int L_dense, int H,
-                                             int G, int V) {
+                                             const int32_t *__restrict__ cu, int L_dense,
+                                             int T_all, int H, int G, int V) {
   constexpr int KE = K / kGdnSplit;               // columns per lane (a multiple of 4)
   static_assert(KE % 4 == 0, "K must be a multiple of 64");
   constexpr int RB = kGdnRows;
@@ -66,9 +66,9 @@ __global__ __launch_bounds__(256) void k_gdn(const T *__restrict__ q, const T *_
   const int tid = threadIdx.x, part = tid % kGdnSplit, r = tid / kGdnSplit;
   const int i = rb * RB + r;  // this lane's state row
   int t0, t1;
-  if (cu) {
-    t0 = cu[s];
-    t1 = cu[s + 1];
+  if (cu) {  // kept inside 0 .. T_all whatever the array holds
+    t0 = min(max(cu[s], 0), T_all);
+    t1 = min(max(cu[s + 1], t0), T_all);
   } else {
     t0 = s * L_dense;
     t1 = t0 + L_dense;
@@ -219,7 +219,7 @@ static hipError_t gdn_K(const GdnArgs &a) {
   case KK:                                                                                     \
     hipLaunchKernelGGL((k_gdn<T, KK>), grid, dim3(256), 0, static_cast<hipStream_t>(a.stream), \
                        (const T *)a.q, (const T *)a.k, (const T *)a.v, a.g, a.beta, a.h0, a.o,  \
-                       a.h_out, a.cu, L_dense, a.H, a.G, a.V);                                 \
+                       a.h_out, a.cu, L_dense, (int)a.T, a.H, a.G, a.V);                       \
     break;
   switch (a.K) {
     SSD_GDN(64) SSD_GDN(128) SSD_GDN(256)

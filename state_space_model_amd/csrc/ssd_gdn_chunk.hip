@@ -243,8 +243,8 @@ template <typename T, int K, int VB>
 __global__ __launch_bounds__(VB * 16) void k_gdn_walk(
     const T *__restrict__ q, const T *__restrict__ k, const float *__restrict__ E,
     const T *__restrict__ U, const T *__restrict__ W, const T *__restrict__ Pm, const float *h0,
-    float *__restrict__ o, float *h_out, const int32_t *__restrict__ cu, int L_dense, int nseq,
-    int H, int G, int V) {
+    float *__restrict__ o, float *h_out, const int32_t *__restrict__ cu, int L_dense, int T_all,
+    int nseq, int H, int G, int V) {
   typedef GdnWalkCfg<T, K, VB> F;
   constexpr int VN = F::VN, KP = F::KP, UP = F::UP, PP = F::PP, DP = F::DP, SP = F::SP;
   constexpr bool SPL = F::SPL;
@@ -264,9 +264,9 @@ __global__ __launch_bounds__(VB * 16) void k_gdn_walk(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tt = wave & 3, vt = wave >> 2;  // this wave's t tile and v tile
   int t0, t1;
-  if (cu) {
-    t0 = cu[s];
-    t1 = cu[s + 1];
+  if (cu) {  // kept inside 0 .. T_all whatever the array holds
+    t0 = min(max(cu[s], 0), T_all);
+    t1 = min(max(cu[s + 1], t0), T_all);
   } else {
     t0 = s * L_dense;
     t1 = t0 + L_dense;
@@ -502,8 +502,8 @@ static hipError_t gdn_walk_launch(const GdnArgs &a, int L_dense, const float *Ec
   const float *h0p = a.h0;
   float *op = a.o, *hop = a.h_out;
   const int32_t *cup = a.cu;
-  int Ld = L_dense, ns = a.nseq, H_ = a.H, G_ = a.G, V_ = a.V;
-  void *args[] = {&qp, &kkp, &Ec, &Uc, &Wc, &Pc, &h0p, &op, &hop, &cup, &Ld, &ns, &H_, &G_, &V_};
+  int Ld = L_dense, Ta = (int)a.T, ns = a.nseq, H_ = a.H, G_ = a.G, V_ = a.V;
+  void *args[] = {&qp, &kkp, &Ec, &Uc, &Wc, &Pc, &h0p, &op, &hop, &cup, &Ld, &Ta, &ns, &H_, &G_, &V_};
   const int heads = a.nseq * a.H;
   const unsigned grid = (unsigned)((heads + 7) / 8) * 8u * (unsigned)(a.V / VB);
   return hipLaunchKernel(kw, dim3(grid), dim3(FW::NT), args, FW::LDS, st);
