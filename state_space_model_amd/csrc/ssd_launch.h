@@ -76,8 +76,8 @@ hipError_t launch_chunk_state(const PrefillArgs &a, const WorkspaceLayout &L, in
 // packed batch), writing h_out only when write_hout.
 constexpr long kWalkMinChains = 128;
 bool walk_supported(int P, int N, int Q, bool bf16);
-bool walk_choice(int P, int N, int Q, bool bf16, int nseq, int H, bool packed, unsigned variant,
-                 bool training = false);
+bool walk_choice(int P, int N, int Q, bool bf16, int nseq, int H, int64_t nc, bool packed,
+                 unsigned variant, bool training = false);
 hipError_t launch_state_walk(const PrefillArgs &a, const WorkspaceLayout &L, int nc,
                              bool write_hout, hipStream_t st);
 

@@ -595,7 +595,7 @@ unsigned prefill_plan(int64_t T, int nseq, int H, int P, int N, int G, int Q, bo
   const int64_t nc = (T + (int64_t)nseq * (Q - 1)) / Q;
   const int L_dense = packed ? 0 : (int)(T / nseq);
   const int nc_real = L_dense > 0 ? nseq * ((L_dense + Q - 1) / Q) : (int)nc;
-  const bool walk = nc > 0 && walk_choice(P, N, Q, bf16, nseq, H, packed, variant);
+  const bool walk = nc > 0 && walk_choice(P, N, Q, bf16, nseq, H, nc, packed, variant);
   const int HB = scan_heads_choice(P, N, Q, bf16, nc_real, H, G, variant);
   return (walk ? SSD_VARIANT_STATE_WALK : SSD_VARIANT_STATE_CHUNKS) |
          (HB > 0 ? SSD_VARIANT_SCAN_HEADS : SSD_VARIANT_SCAN_ROWS);
@@ -619,7 +619,7 @@ static hipError_t run_prefill(const PrefillArgs &a, unsigned stages) {
 
   // the state walk does stages 1, 2 and 4 in one kernel
   const bool walk =
-      nc > 0 && walk_choice(P, N, a.Q, a.bf16, a.nseq, a.H, a.cu != nullptr, a.variant,
+      nc > 0 && walk_choice(P, N, a.Q, a.bf16, a.nseq, a.H, nc, a.cu != nullptr, a.variant,
                             a.hin32 != nullptr);
   if ((stages & (walk ? 7u : 3u)) && (a.cu || L_dense == 0)) {
     // packed (or empty) batch: chunk map first.  Block 0 also writes the first

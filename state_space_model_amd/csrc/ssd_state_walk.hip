@@ -870,12 +870,14 @@ bool walk_supported(int P, int N, int Q, bool bf16) {
 // The walk pays when there are enough chains to fill the chip (a packed batch
 // walks by lists, which even out its sequences' lengths).  A packed batch's
 // training forward keeps the chunk states: the list walk keeps no float32
-// entering states.  The variant bits force either way.
-bool walk_choice(int P, int N, int Q, bool bf16, int nseq, int H, bool packed, unsigned variant,
-                 bool training) {
+// entering states; nor do the lists take 2^30 or more (chunk, head)
+// positions (32-bit position arithmetic).  The variant bits force either way.
+bool walk_choice(int P, int N, int Q, bool bf16, int nseq, int H, int64_t nc, bool packed,
+                 unsigned variant, bool training) {
   if (!walk_supported(P, N, Q, bf16) || (variant & SSD_VARIANT_STATE_CHUNKS)) return false;
   if (variant & SSD_VARIANT_STATE_WALK) return true;
   if (packed && training) return false;
+  if (packed && (int64_t)H * nc >= (int64_t(1) << 30)) return false;
   return (long)nseq * H >= kWalkMinChains;
 }
 

@@ -101,6 +101,10 @@ def test_plan_query():
                                                                  "scan": "rows"}
     assert plan(4000, 1, 80, 64, 128, 1, 256, packed=True) == {"state": "chunks",
                                                                "scan": "rows"}
+    # 2^30 or more (chunk, head) positions (here 128 x 8388615): too many for
+    # the walk by lists
+    assert plan(2**28 - 1, 8, 128, 64, 128, 1, 32, packed=True)["state"] == "chunks"
+    assert plan(2**26, 8, 128, 64, 128, 1, 32, packed=True)["state"] == "walk"
     assert plan(4096, 1, 24, 64, 100, 1, 256) is None
 
 
