@@ -36,7 +36,10 @@
 // the earlier segments' decayed contribution to their entering states and
 // forms the final state (the recurrence is linear in the entering state).
 // Some heads' chains in two segments fill the chip's slots; the rest, in
-// shorter segments, fill the slots those free (SegPlan).
+// shorter segments, fill the slots those free (SegPlan).  A packed batch,
+// whose sequence lengths only the device knows, is walked by lists instead:
+// every chunk of every chain in one order, cut into equal runs, one per
+// resident workgroup (k_state_walk_list, k_walk_fixup_list).
 #include <algorithm>
 
 #include "ssd.h"
