@@ -885,16 +885,19 @@ def profile_commands():
     cmds = {}
     for sec, (_, a) in PROFILED.items():
         base = f"-- python bench.py {a}"
+        # counters per dispatch do not depend on the clocks: no preheat (its
+        # thousands of dispatches would only swell the output)
+        pbase = base + " --preheat 0"
         cmds[f"{sec}_trace"] = ("rocprofv3 --kernel-trace --stats --output-format csv "
                                 f"-d DIR/{sec}_trace -o run {base}")
-        cmds[f"{sec}_fetch"] = f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/{sec}_fetch -o run {base}"
-        cmds[f"{sec}_write"] = f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/{sec}_write -o run {base}"
+        cmds[f"{sec}_fetch"] = f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/{sec}_fetch -o run {pbase}"
+        cmds[f"{sec}_write"] = f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/{sec}_write -o run {pbase}"
         cmds[f"{sec}_mfma"] = ("rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 --output-format csv "
-                               f"-d DIR/{sec}_mfma -o run {base}")
+                               f"-d DIR/{sec}_mfma -o run {pbase}")
     # where the headline's kernels wait: SQ issue and wait states, the vector
     # memory path (TA address FIFO, L1 pending on L2, L2 read latency), L2 hits
     for sec in PIPE_SECTIONS:
-        hb = f"-- python bench.py {PROFILED[sec][1]}"
+        hb = f"-- python bench.py {PROFILED[sec][1]} --preheat 0"
         for i, cs in enumerate(PIPE_COUNTERS):
             cmds[f"{sec}_pipe{i + 1}"] = (f"rocprofv3 --pmc {' '.join(cs)} --output-format csv "
                                           f"-d DIR/{sec}_pipe{i + 1} -o run {hb}")
