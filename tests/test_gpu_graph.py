@@ -100,18 +100,24 @@ def test_graph_backward_and_delta_rule_replays_equal_eager():
 def test_graph_walk_and_noalloc_replays_equal_eager():
     """A dense batch large enough for the two-segment state walk (2 x 2048
     tokens, 64 heads, chunk 256: B fragments, walk, fix-up, heads-streamed or
-    row-split scan) through the workspace entry point, and a smaller packed
-    batch through the no-allocation entry point, captured in one HIP graph:
-    every replay equals the eager run bit for bit, with eager work between
+    row-split scan) and a packed one walked by lists (3 ragged sequences, 64
+    heads) through the workspace entry point, and a smaller packed batch
+    through the no-allocation entry point, captured in one HIP graph: every
+    replay equals the eager run bit for bit, with eager work between
     replays."""
     import torch
     from state_space_model_amd import ssd
-    log("graph: two-segment walk prefill + no-allocation prefill, 4 replays")
+    log("graph: two-segment walk, list walk and no-allocation prefills, 4 replays")
     d = inputs.prefill_inputs(64, 64, 128, 1, [2048, 2048], 77, dtype="bf16", h0=True)
     t = dev_inputs(d, "bf16")
     assert ssd.plan(4096, 2, 64, 64, 128, 1, 256)["state"] == "walk"
     run_w, y, h = ssd.prefill(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["h0"],
                               chunk=256, nseq=2, prepare=True)
+    d3 = inputs.prefill_inputs(64, 64, 128, 1, [1500, 700, 2100], 79, dtype="bf16", h0=True)
+    t3 = dev_inputs(d3, "bf16")
+    assert ssd.plan(4300, 3, 64, 64, 128, 1, 256, packed=True)["state"] == "walk"
+    run_l, y3, h3 = ssd.prefill(t3["x"], t3["dt"], t3["A"], t3["B"], t3["C"], t3["D"], t3["h0"],
+                                chunk=256, cu_seqlens=t3["cu_seqlens"], prepare=True)
     d2 = inputs.prefill_inputs(4, 64, 128, 2, [300, 77], 78, dtype="bf16", h0=True)
     t2 = dev_inputs(d2, "bf16")
     run_n, y2, h2 = ssd.prefill(t2["x"], t2["dt"], t2["A"], t2["B"], t2["C"], t2["D"], t2["h0"],
@@ -120,23 +126,25 @@ def test_graph_walk_and_noalloc_replays_equal_eager():
 
     def once():
         run_w()
+        run_l()
         run_n()
 
     once()  # the first no-allocation call looks up the scratch address
     torch.cuda.synchronize()
-    ref = [v.clone() for v in (y, h, y2, h2)]
+    outs = (y, h, y3, h3, y2, h2)
+    ref = [v.clone() for v in outs]
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         once()
     for r in range(4):
-        for v in (y, h, y2, h2):
+        for v in outs:
             v.zero_()
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        for v, e in zip((y, h, y2, h2), ref):
+        for v, e in zip(outs, ref):
             assert torch.equal(v, e), r
         once()
         torch.cuda.synchronize()
-        for v, e in zip((y, h, y2, h2), ref):
+        for v, e in zip(outs, ref):
             assert torch.equal(v, e), r
