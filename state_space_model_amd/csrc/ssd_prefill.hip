@@ -521,12 +521,12 @@ __global__ __launch_bounds__(1024) void k_chunk_scan(
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int j0 = jb + 4 * grp + r, j1 = j0 + 16;
-          // every argument is clamped to <= 0, so each product is finite and the
-          // mask can be a multiply by 0 or 1 (no branch)
+          // every argument is clamped to <= 0, so each product is finite; the
+          // mask is a select (no branch)
           const float e0 = __builtin_amdgcn_exp2f(fminf(si - sj0[r], 0.f)) * dj0[r];
           const float e1 = __builtin_amdgcn_exp2f(fminf(si - sj1[r], 0.f)) * dj1[r];
-          m[r] = g0[r] * e0 * (j0 <= i ? 1.f : 0.f);
-          m[4 + r] = g1[r] * e1 * (j1 <= i ? 1.f : 0.f);
+          m[r] = j0 <= i ? g0[r] * e0 : 0.f;
+          m[4 + r] = j1 <= i ? g1[r] * e1 : 0.f;
         }
       }
       const Frag<T> mf = frag_from_f32(m, T());

@@ -120,8 +120,8 @@ __device__ __forceinline__ Frag<bf16> decay_block(bf16x8 gb, int jb, int t0, int
       const int j0 = jb + 4 * grp + r, j1 = j0 + 16;
       const float e0 = __builtin_amdgcn_exp2f(fminf(si - sj0[r], 0.f)) * dj0[r];
       const float e1 = __builtin_amdgcn_exp2f(fminf(si - sj1[r], 0.f)) * dj1[r];
-      m[r] = g[r] * e0 * (j0 <= i ? 1.f : 0.f);
-      m[4 + r] = g[4 + r] * e1 * (j1 <= i ? 1.f : 0.f);
+      m[r] = j0 <= i ? g[r] * e0 : 0.f;
+      m[4 + r] = j1 <= i ? g[4 + r] * e1 : 0.f;
     }
   }
   return frag_from_f32(m, bf16());
