@@ -114,7 +114,7 @@ def prefill_work(w, T, nseq, h0, plan=None):
     x is read by two launches (the chunk states and the output), so the
     per-launch bytes sum to more than the whole prefill's.  With the state
     walk (plan["state"] == "walk") stages 1, 2 and 4 are one launch group,
-    "state_walk" (the B-fragment copy and the walk)."""
+    "state_walk" (the B-fragment copy, the walk and its fix-up)."""
     H, P, N, G, Q = w.H, w.P, w.N, w.G, w.chunk
     e = 2 if w.dtype == "bf16" else 4
     state = nseq * H * N * P * 4
@@ -219,6 +219,21 @@ def timed_steps(torch, parts, steps):
     per = {name: sum(evs[k * n + i].elapsed_time(evs[k * n + i + 1]) for k in range(steps)) / steps
            for i, (name, _) in enumerate(parts)}
     return total, per
+
+
+# the profiled kernels of each launch group the bench times as one part
+GROUP_KERNELS = {"state_walk": ("b_frag", "state_walk", "walk_fixup")}
+
+
+def group_traffic(traffic):
+    """Per-kernel HBM bytes -> per launch group: a group's bytes are the sum of
+    its kernels' (None when one of them was not profiled)."""
+    out = dict(traffic)
+    for group, ks in GROUP_KERNELS.items():
+        if group in traffic:
+            vals = [traffic.get(k) for k in ks]
+            out[group] = None if any(v is None for v in vals) else sum(vals)
+    return out
 
 
 def load_traffic():
@@ -395,7 +410,7 @@ def headline(args, torch, inputs, ssd, dev):
 
         work = prefill_work(wl, T, nseq, h0=True, plan=plan)
         work["decode_step"] = step_work(nseq, wl.H, wl.P, wl.N, wl.G, 2)
-        traffic = load_traffic().get(wl.name, {})
+        traffic = group_traffic(load_traffic().get(wl.name, {}))
         kernels = [roofline(n, work[n], kern_ms[n], traffic) for n in work]
         dominant = max(kernels, key=lambda k: k["avg_us"])
         tot = prefill_totals(wl, T, nseq, h0=True)
@@ -511,7 +526,7 @@ def small_layer(args, torch, inputs, ssd, dev):
     kern_ms["decode_step"] = graph_ms(torch, run_decode, reps=10, per_graph=20)
     work = prefill_work(wl, T, nseq, h0=False, plan=plan)
     work["decode_step"] = step_work(nseq, wl.H, wl.P, wl.N, wl.G, 2)
-    traffic = load_traffic().get(wl.name, {})
+    traffic = group_traffic(load_traffic().get(wl.name, {}))
     kernels = [roofline(n, work[n], kern_ms[n], traffic) for n in work]
     # the prefill from HBM: before each repeat a 512 MB buffer is written,
     # which evicts the 256 MB last-level cache (5 untimed + 30 timed repeats)
