@@ -3,6 +3,7 @@
 #pragma once
 #include <mutex>
 #include <set>
+#include <utility>
 
 #include "ssd_device.h"
 
@@ -146,15 +147,19 @@ __device__ __forceinline__ void dma_swz(char *lds, const void *src, uint32_t val
   }
 }
 
-// Allow a kernel the full 160 KB of LDS (once per kernel; not a stream
-// operation, so calls under graph capture are unaffected after the first).
+// Allow a kernel the full 160 KB of LDS (once per kernel and device; not a
+// stream operation, so calls under graph capture are unaffected after the
+// first).
 static inline hipError_t set_lds_limit(const void *kern) {
   static std::mutex mu;
-  static std::set<const void *> done;
+  static std::set<std::pair<int, const void *>> done;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
   std::lock_guard<std::mutex> lock(mu);
-  if (done.count(kern)) return hipSuccess;
-  hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-  if (e == hipSuccess) done.insert(kern);
+  if (done.count({dev, kern})) return hipSuccess;
+  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (e == hipSuccess) done.insert({dev, kern});
   return e;
 }
 
